@@ -1,0 +1,219 @@
+"""Plain CPU oracle of the DMS decode path.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The product (the HIP library and its
+Python binding) never calls it and shares no code with it.
+
+What it computes
+----------------
+Dynamic Memory Sparsification (DMS) gives every KV head a binary eviction
+decision per token and delays its effect by a window of w steps.  Sources,
+cited by page title and section:
+
+* "Inference-Time Hyper-Scaling with KV Cache Compression", third-party
+  paper summary (bud-325.pages.dev), sections "Key claims" and "Method"
+  (attributing paper section 3.2, section 5.3 and Fig. 5): a per-head binary
+  decision alpha_t in {0, 1}; a token marked at step t remains attendable
+  through step t + w inside a sliding window of size w, then it is gone;
+  the decisions drive an additive attention mask that is never built.
+* The same page, "Method": each head may end at its own compression ratio.
+* arXiv listing of 2506.05345 (searcharxiv.org), "Abstract": eviction is
+  delayed rather than immediate.
+
+Readings taken where the pages are silent (each listed in the design notes):
+
+* alpha = 1 exactly when the token's own eviction logit is > 0 (fp32
+  compare; logit 0, -0 and NaN give alpha = 0).  At inference the
+  Gumbel-sigmoid of training is replaced by its noiseless threshold.
+* "visible until t + w" is inclusive: a marked token i is visible to the
+  queries q in [i, i + w] and to no later query.
+* Decisions are per KV head; the G = Hq / Hkv query heads of a group share
+  one visible set; query head hq reads KV head floor(hq / G).
+* Within a decode step the token at position q is appended first (retiring
+  token q - w - 1 if it was marked), then query q attends; it sees itself.
+* Attention scale 1 / sqrt(d) unless overridden.
+* Position 0 follows the same rule as every other position (no sinks).
+
+The result is exact attention restricted to a visibility set, so this
+module is that definition written out in float64: a closed form for the
+visible set and a max-subtracted softmax over the gathered rows.  A second,
+independent form (``attend_masked``) applies the rule as a dense additive
+0 / -inf mask over all causal positions.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, List, Optional
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# Decision and visibility (summary page, "Key claims" / "Method")
+# ----------------------------------------------------------------------------
+
+def eviction_decision(logit: np.ndarray) -> np.ndarray:
+    """alpha = 1 where the fp32 eviction logit is strictly positive.
+
+    NaN compares false, so a NaN logit gives alpha = 0.
+    """
+    return np.asarray(logit, dtype=np.float32) > np.float32(0.0)
+
+
+def visible(alpha_row: np.ndarray, q: int, w: int) -> np.ndarray:
+    """Sorted positions i <= q with alpha_i == 0 or q - i <= w.
+
+    ``alpha_row`` holds the decisions of one (sequence, KV head) for
+    positions 0..q (longer rows are cut at q).
+    """
+    i = np.arange(q + 1)
+    a = np.asarray(alpha_row[: q + 1], dtype=bool)
+    keep = (~a) | (q - i <= w)
+    return i[keep]
+
+
+def retired(alpha_row: np.ndarray, q: int, w: int) -> List[int]:
+    """Positions dropped by the step that appends q: q - w - 1 if marked."""
+    j = q - w - 1
+    if j >= 0 and bool(alpha_row[j]):
+        return [j]
+    return []
+
+
+def pending(alpha_row: np.ndarray, q: int, w: int) -> np.ndarray:
+    """Marked positions still visible at query q (all lie in [q - w, q])."""
+    vis = visible(alpha_row, q, w)
+    return vis[np.asarray(alpha_row, dtype=bool)[vis]]
+
+
+def compression_ratio(q: int, n_visible: int) -> float:
+    """Tokens seen over tokens kept, (q + 1) / |Vis(q)|."""
+    return (q + 1) / n_visible
+
+
+def kv_head_of(hq: int, group: int) -> int:
+    """Grouped-query mapping: query head hq reads KV head floor(hq / G)."""
+    return hq // group
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / np.sqrt(head_dim)
+
+
+# ----------------------------------------------------------------------------
+# Attention restricted to the visible set
+# ----------------------------------------------------------------------------
+
+def _softmax(s: np.ndarray) -> np.ndarray:
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attend(qv: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(scale * q k^T) v over the gathered rows, float64.
+
+    qv: [G, d]; k_rows, v_rows: [n, d]; returns [G, d].
+    """
+    qv = np.asarray(qv, dtype=np.float64)
+    k = np.asarray(k_rows, dtype=np.float64)
+    v = np.asarray(v_rows, dtype=np.float64)
+    s = scale * (qv @ k.T)
+    return _softmax(s) @ v
+
+
+def attention_weights(qv: np.ndarray, k_rows: np.ndarray, scale: float) -> np.ndarray:
+    qv = np.asarray(qv, dtype=np.float64)
+    k = np.asarray(k_rows, dtype=np.float64)
+    return _softmax(scale * (qv @ k.T))
+
+
+def attend_masked(qv: np.ndarray, k_all: np.ndarray, v_all: np.ndarray, alpha_row: np.ndarray,
+                  q: int, w: int, scale: float) -> np.ndarray:
+    """Second form: dense causal scores over positions 0..q plus an additive
+    mask that is 0 where the rule keeps a token and -inf where it drops it."""
+    qv = np.asarray(qv, dtype=np.float64)
+    k = np.asarray(k_all[: q + 1], dtype=np.float64)
+    v = np.asarray(v_all[: q + 1], dtype=np.float64)
+    s = scale * (qv @ k.T)
+    mask = np.full(q + 1, -np.inf)
+    for i in range(q + 1):
+        if (not bool(alpha_row[i])) or (q - i <= w):
+            mask[i] = 0.0
+    s = s + mask[None, :]
+    return _softmax(s) @ v
+
+
+# ----------------------------------------------------------------------------
+# Decode of one (sequence, KV head) unit
+# ----------------------------------------------------------------------------
+
+@dataclass
+class StepRecord:
+    q: int                      # position appended and queried
+    alpha: bool                 # decision of the appended token
+    visible: np.ndarray         # sorted positions in Vis(q)
+    retired: List[int]          # positions dropped by this step
+    pending: np.ndarray         # marked positions still visible
+    out: Optional[np.ndarray]   # [G, d] float64, or None when not requested
+    cr: float
+
+
+def decode_unit(q_rows: Optional[np.ndarray], k: np.ndarray, v: np.ndarray, logit: np.ndarray,
+                prompt_len: int, steps: int, w: int, scale: float) -> List[StepRecord]:
+    """Decode ``steps`` tokens after a prompt of ``prompt_len`` tokens.
+
+    q_rows: [steps, G, d] queries of the group at positions prompt_len + t
+            (None to skip attention); k, v: [T, d] rows by position;
+    logit:  [T] eviction logits by position, T >= prompt_len + steps.
+    """
+    alpha = eviction_decision(logit)
+    recs = []
+    for t in range(steps):
+        q = prompt_len + t
+        vis = visible(alpha, q, w)
+        out = None
+        if q_rows is not None:
+            out = attend(q_rows[t], k[vis], v[vis], scale)
+        recs.append(StepRecord(q=q, alpha=bool(alpha[q]), visible=vis,
+                               retired=retired(alpha, q, w), pending=pending(alpha, q, w),
+                               out=out, cr=compression_ratio(q, len(vis))))
+    return recs
+
+
+def decode_batch(Q: np.ndarray, K: np.ndarray, V: np.ndarray, logit: np.ndarray,
+                 prompt_lens, steps: int, w: int, scale: Optional[float] = None,
+                 units=None) -> Dict:
+    """Whole-batch decode.
+
+    Q: [B, Hq, T, d]; K, V: [B, Hkv, T, d]; logit: [B, Hkv, T];
+    prompt_lens: [B].  ``units``: optional list of (b, h) to compute (default
+    all).  Returns {'out': [steps, B, Hq, d] float64 (NaN where not computed),
+    'records': {(b, h): [StepRecord]}}.
+    """
+    B, Hq, _, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = default_scale(d)
+    if units is None:
+        units = [(b, h) for b in range(B) for h in range(Hkv)]
+    out = np.full((steps, B, Hq, d), np.nan)
+    records = {}
+    for (b, h) in units:
+        P = int(prompt_lens[b])
+        heads = [hq for hq in range(Hq) if kv_head_of(hq, G) == h]
+        qr = np.stack([Q[b, heads, P + t, :] for t in range(steps)])
+        recs = decode_unit(qr, K[b, h], V[b, h], logit[b, h], P, steps, w, scale)
+        records[(b, h)] = recs
+        for t, r in enumerate(recs):
+            out[t, b, heads, :] = r.out
+    return {"out": out, "records": records}
+
+
+def state_after_prefill(logit_row: np.ndarray, prompt_len: int, w: int):
+    """Visible set and pending marked tokens after a prompt of P tokens,
+    i.e. the state that P single-token appends leave (P >= 1)."""
+    alpha = eviction_decision(logit_row)
+    q = prompt_len - 1
+    return visible(alpha, q, w), pending(alpha, q, w)

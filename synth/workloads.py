@@ -1,0 +1,132 @@
+"""Synthetic workload recipes: shapes, sizes and logit distributions.
+
+Each recipe stands in for a model/dataset pair the DMS pages evaluate on
+(Qwen-R1 reasoning traces, Llama 3.2 1B tasks), which are not available
+here; only the tensor shapes and the eviction-rate structure are
+reproduced.  Values come from ``synth.synth``.
+
+The logit mean for a target marked fraction ``1 - 1/c`` ("CR c" in the
+recipes) is ``mu(c) = Phi^-1(1 - 1/c)`` for a unit-variance logit, so that
+``P(logit > 0) = 1 - 1/c``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from statistics import NormalDist
+from typing import List, Optional
+
+import numpy as np
+
+from . import synth
+
+
+def mu_for_cr(c: float) -> float:
+    """Logit mean that marks a fraction 1 - 1/c of tokens (unit variance)."""
+    if c <= 1.0:
+        return float("-inf")
+    return NormalDist().inv_cdf(1.0 - 1.0 / c)
+
+
+@dataclass
+class Workload:
+    name: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str                 # "f32" or "bf16"
+    window: int
+    decode_steps: int
+    seed: int
+    prompt_len: int = 0        # uniform prompt length (when lengths_range is None)
+    lengths_range: Optional[tuple] = None   # (lo, hi) per-sequence prompt lengths
+    num_layers: int = 1
+    # logit mean per layer: mu_before for positions < pos_threshold, mu_after beyond
+    mu_before: List[float] = field(default_factory=lambda: [0.0])
+    mu_after: Optional[List[float]] = None
+    pos_threshold: int = synth.MAX_POS
+    description: str = ""
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def prompt_lengths(self) -> np.ndarray:
+        if self.lengths_range is None:
+            return np.full(self.batch, self.prompt_len, dtype=np.int64)
+        lo, hi = self.lengths_range
+        return synth.lengths(self.seed, self.batch, lo, hi)
+
+    def max_tokens(self) -> int:
+        return int(self.prompt_lengths().max()) + self.decode_steps
+
+    def layer_mu(self, layer: int):
+        before = self.mu_before[layer if len(self.mu_before) > 1 else 0]
+        after = before if self.mu_after is None else self.mu_after[layer if len(self.mu_after) > 1 else 0]
+        return before, after
+
+    def marked_prob(self, layer: int, pos: np.ndarray) -> np.ndarray:
+        """P(logit > 0) at each position under the Gaussian model of the logit."""
+        before, after = self.layer_mu(layer)
+        nd = NormalDist()
+        pb = 1.0 - nd.cdf(-before) if np.isfinite(before) else 0.0
+        pa = 1.0 - nd.cdf(-after) if np.isfinite(after) else 0.0
+        return np.where(np.asarray(pos) < self.pos_threshold, pb, pa)
+
+    def expected_live(self, layer: int, q: int) -> float:
+        """E|Vis(q)| under independent marks: unmarked tokens plus the window."""
+        pos = np.arange(q + 1)
+        p = self.marked_prob(layer, pos)
+        in_window = pos >= q - self.window
+        return float(np.sum(1.0 - p) + np.sum(p[in_window]))
+
+
+def tiny() -> Workload:
+    return Workload(
+        name="tiny", batch=1, num_q_heads=12, num_kv_heads=2, head_dim=128, dtype="f32",
+        window=16, decode_steps=256, seed=1000, prompt_len=256, mu_before=[0.0],
+        description="1 sequence, 12 Q / 2 KV heads, head_dim 128, fp32, 256-token prompt + "
+                    "256 decode steps, w=16, logits N(0,1) (about half marked)")
+
+
+def llama_1b() -> Workload:
+    return Workload(
+        name="llama-3.2-1b-layer", batch=8, num_q_heads=32, num_kv_heads=8, head_dim=64,
+        dtype="bf16", window=256, decode_steps=512, seed=1001, prompt_len=4096,
+        mu_before=[0.67],
+        description="Llama-3.2-1B-shaped layer: 32 Q / 8 KV heads, head_dim 64, bf16, 8 sequences, "
+                    "4096-token context, w=256, logits N(0.67,1) (CR 4), 512 decode steps")
+
+
+def qwen_7b() -> Workload:
+    return Workload(
+        name="qwen-r1-7b-layer", batch=32, num_q_heads=28, num_kv_heads=4, head_dim=128,
+        dtype="bf16", window=256, decode_steps=256, seed=1002, prompt_len=16384,
+        mu_before=[1.15],
+        description="Qwen-R1-7B-shaped layer: 28 Q / 4 KV heads, head_dim 128, bf16, 32 chains, "
+                    "16384-token context, w=256, logits N(1.15,1) (CR 8), 256 decode steps")
+
+
+def qwen_32b() -> Workload:
+    return Workload(
+        name="qwen-r1-32b-layer", batch=64, num_q_heads=40, num_kv_heads=8, head_dim=128,
+        dtype="bf16", window=256, decode_steps=256, seed=1003, prompt_len=32768,
+        mu_before=[mu_for_cr(4.0)], mu_after=[mu_for_cr(12.0)], pos_threshold=10240,
+        description="Qwen-R1-32B-shaped layer: 40 Q / 8 KV heads, head_dim 128, bf16, 64 chains at "
+                    "32768 tokens, w=256, logit mean for CR 4 below position 10240 and CR 12 "
+                    "beyond (overall about 8), 256 decode steps")
+
+
+def full_32b() -> Workload:
+    layers = 64
+    crs = [4.0 + 8.0 * l / (layers - 1) for l in range(layers)]
+    return Workload(
+        name="qwen-r1-32b-64-layer-step", batch=256, num_q_heads=40, num_kv_heads=8, head_dim=128,
+        dtype="bf16", window=256, decode_steps=128, seed=1004, lengths_range=(1024, 32768),
+        num_layers=layers, mu_before=[mu_for_cr(c) for c in crs],
+        description="64 layers x (40 Q / 8 KV heads, head_dim 128, bf16), 256 chains with lengths "
+                    "uniform in [1024, 32768], w=256, per-layer CR from 4 (layer 0) to 12 "
+                    "(layer 63), 128 decode steps")
+
+
+ALL = {w().name: w for w in (tiny, llama_1b, qwen_7b, qwen_32b, full_32b)}

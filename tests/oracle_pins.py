@@ -1,0 +1,346 @@
+"""Pins of the CPU oracle: checks against what the pages and mathematics fix.
+
+Each pin takes the oracle module ``O`` and raises AssertionError on a
+mismatch.  ``test_oracle_pins.py`` runs them on the real oracle;
+``test_oracle_mutants.py`` plants single mistakes in the oracle and checks
+that at least one pin fails for each.
+
+References are independent of the oracle's code: hand-worked tables in
+``tests/golden/``, a FIFO simulation of delayed eviction, torch's
+scaled_dot_product_attention (float64, CPU) for the dense-causal and
+sliding-window special cases, scipy's softmax, and closed forms.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+import torch
+
+from synth import synth, workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# visibility and schedule
+# --------------------------------------------------------------------------
+
+def pin_golden_visibility(O):
+    g = _load("visibility_hand.json")
+    alpha = np.array(g["alpha"], dtype=bool)
+    for case in g["cases"]:
+        w = case["w"]
+        for q, (vis, ret) in enumerate(zip(case["visible"], case["retired"])):
+            got = O.visible(alpha, q, w)
+            assert list(got) == vis, (w, q, list(got), vis)
+            assert list(O.retired(alpha, q, w)) == ret, (w, q)
+
+
+def _fifo_visible_sets(alpha, w, T):
+    """Delayed eviction simulated with explicit expiry times: a marked token
+    i is scheduled to leave once the query passes i + w."""
+    live = []
+    expiry = {}
+    sets = []
+    for q in range(T):
+        live.append(q)
+        if alpha[q]:
+            expiry[q] = q + w
+        live = [i for i in live if not (i in expiry and q > expiry[i])]
+        sets.append(list(live))
+    return sets
+
+
+def pin_fifo_simulation(O):
+    rng = np.random.default_rng(7)
+    for w in (0, 1, 2, 3, 5, 16):
+        for p in (0.0, 0.3, 0.7, 1.0):
+            T = 70
+            alpha = rng.random(T) < p
+            ref = _fifo_visible_sets(alpha, w, T)
+            for q in range(T):
+                assert list(O.visible(alpha, q, w)) == ref[q], (w, p, q)
+                prev = set(ref[q - 1]) | {q} if q > 0 else {0}
+                assert sorted(prev - set(ref[q])) == list(O.retired(alpha, q, w)), (w, p, q)
+
+
+def pin_special_visibility(O):
+    T = 40
+    for w in (0, 1, 4, 100):
+        zeros = np.zeros(T, dtype=bool)
+        ones = np.ones(T, dtype=bool)
+        for q in range(T):
+            assert list(O.visible(zeros, q, w)) == list(range(q + 1))
+            assert list(O.visible(ones, q, w)) == list(range(max(0, q - w), q + 1))
+            assert O.retired(zeros, q, w) == []
+        if w >= T:
+            rng = np.random.default_rng(w)
+            a = rng.random(T) < 0.5
+            for q in range(T):
+                assert list(O.visible(a, q, w)) == list(range(q + 1))
+
+
+def pin_schedule_invariants(O):
+    rng = np.random.default_rng(11)
+    for w in (0, 2, 7, 32):
+        alpha = rng.random(200) < 0.6
+        prev = 0
+        for q in range(200):
+            vis = O.visible(alpha, q, w)
+            ret = O.retired(alpha, q, w)
+            assert len(vis) - prev == 1 - len(ret)
+            for j in ret:
+                assert alpha[j] and j == q - w - 1
+            pend = O.pending(alpha, q, w)
+            assert len(pend) <= w + 1
+            assert all(q - w <= i <= q and alpha[i] for i in pend)
+            assert abs(O.compression_ratio(q, len(vis)) - (q + 1) / len(vis)) == 0.0
+            prev = len(vis)
+
+
+def pin_decision_threshold(O):
+    tiny = np.float32(np.finfo(np.float32).smallest_subnormal)
+    logit = np.array([np.nan, 0.0, -0.0, tiny, -tiny, 1e-30, -1e30, np.inf, -np.inf],
+                     dtype=np.float32)
+    got = O.eviction_decision(logit)
+    assert list(map(bool, got)) == [False, False, False, True, False, True, False, True, False]
+
+
+def _irwin_hall_cdf(x: float, n: int = 12) -> float:
+    """CDF of the sum of n independent U(0,1) variables (closed form)."""
+    if x <= 0:
+        return 0.0
+    if x >= n:
+        return 1.0
+    return sum((-1) ** k * math.comb(n, k) * (x - k) ** n
+               for k in range(int(math.floor(x)) + 1)) / math.factorial(n)
+
+
+def pin_expected_live_count(O):
+    """|Vis(q)| on synthetic logits against its closed-form mean and variance
+    under independent marks, within 5 sigma, plus the CR identity.
+
+    The synthetic logit is mu + x with x = IH12 - 6 up to a 2**-16 lattice, so
+    P(marked) = 1 - F_IH12(6 - mu)."""
+    wl = workloads.llama_1b()
+    q = 4095
+    lg = synth.logits(wl.seed, 0, np.arange(wl.batch), wl.num_kv_heads, np.arange(q + 1),
+                      wl.mu_before[0])
+    counts = []
+    for b in range(wl.batch):
+        for h in range(wl.num_kv_heads):
+            a = O.eviction_decision(lg[b, h])
+            counts.append(len(O.visible(a, q, wl.window)))
+    counts = np.array(counts, dtype=np.float64)
+    p = 1.0 - _irwin_hall_cdf(6.0 - wl.mu_before[0])
+    n_old = q + 1 - (wl.window + 1)
+    mean = n_old * (1 - p) + (wl.window + 1)
+    var = n_old * p * (1 - p)
+    tol = 5 * math.sqrt(var / len(counts)) + 1e-3 * n_old
+    assert abs(counts.mean() - mean) < tol, (counts.mean(), mean, tol)
+    total_seen = (q + 1) * len(counts)
+    cr = total_seen / counts.sum()
+    assert abs(cr - total_seen / np.sum([len(O.visible(O.eviction_decision(lg[b, h]), q, wl.window))
+                                          for b in range(wl.batch)
+                                          for h in range(wl.num_kv_heads)])) == 0.0
+    assert 3.0 < cr < 3.8
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+
+def pin_golden_attention(O):
+    g = _load("attention_hand.json")
+    d = g["d"]
+    qv = np.array([g["q"]])
+    K = np.array(g["keys"])
+    V = np.array(g["values"])
+    scale = O.default_scale(d)
+    for case in g["cases"]:
+        alpha = np.array(case["alpha"], dtype=bool)
+        q = case["query_pos"]
+        vis = O.visible(alpha, q, case["w"])
+        assert list(vis) == case["visible"]
+        wts = O.attention_weights(qv, K[vis], scale)[0]
+        np.testing.assert_allclose(wts, case["weights"], rtol=0, atol=1e-14)
+        out = O.attend(qv, K[vis], V[vis], scale)[0]
+        np.testing.assert_allclose(out, case["out"], rtol=0, atol=1e-13)
+        outm = O.attend_masked(qv, K, V, alpha, q, case["w"], scale)[0]
+        np.testing.assert_allclose(outm, case["out"], rtol=0, atol=1e-13)
+
+
+def _sdpa(Q, K, V, allowed, Hq, Hkv):
+    """torch reference: Q [Hq, Lq, d], K/V [Hkv, Lk, d], allowed [Lq, Lk] bool."""
+    q = torch.from_numpy(Q)[None]
+    k = torch.from_numpy(K)[None]
+    v = torch.from_numpy(V)[None]
+    m = torch.from_numpy(allowed)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m,
+                                                         enable_gqa=(Hq != Hkv))
+    return o[0].numpy()
+
+
+def _random_batch(rng, B, Hq, Hkv, T, d):
+    Q = rng.standard_normal((B, Hq, T, d))
+    K = rng.standard_normal((B, Hkv, T, d))
+    V = rng.standard_normal((B, Hkv, T, d))
+    return Q, K, V
+
+
+def _special_case_vs_sdpa(O, marked: bool, w: int):
+    rng = np.random.default_rng(3 if marked else 4)
+    B, Hq, Hkv, T, d = 2, 6, 2, 48, 16
+    P, steps = 20, 28
+    Q, K, V = _random_batch(rng, B, Hq, Hkv, T, d)
+    logit = np.full((B, Hkv, T), 1.0 if marked else -1.0, dtype=np.float32)
+    res = O.decode_batch(Q, K, V, logit, [P] * B, steps, w)
+    qpos = torch.arange(P, P + steps)[:, None]
+    kpos = torch.arange(T)[None, :]
+    allowed = kpos <= qpos
+    if marked:
+        allowed = allowed & (kpos >= qpos - w)
+    for b in range(B):
+        ref = _sdpa(np.ascontiguousarray(Q[b, :, P:P + steps]), K[b], V[b], allowed.numpy(), Hq, Hkv)
+        got = res["out"][:, b].transpose(1, 0, 2)       # [Hq, steps, d]
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def pin_unmarked_is_dense_causal(O):
+    _special_case_vs_sdpa(O, marked=False, w=5)
+
+
+def pin_marked_is_sliding_window(O):
+    for w in (0, 3, 9):
+        _special_case_vs_sdpa(O, marked=True, w=w)
+
+
+def pin_gather_equals_masked(O):
+    rng = np.random.default_rng(5)
+    d, T = 8, 64
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    for w in (0, 1, 6):
+        alpha = rng.random(T) < 0.6
+        for q in (0, 5, 31, 63):
+            qv = rng.standard_normal((3, d))
+            vis = O.visible(alpha, q, w)
+            a = O.attend(qv, K[vis], V[vis], 0.37)
+            b = O.attend_masked(qv, K, V, alpha, q, w, 0.37)
+            np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def pin_single_visible_returns_value(O):
+    """w = 0 with every token marked leaves only the query's own token, so the
+    output is that token's value row exactly."""
+    rng = np.random.default_rng(6)
+    B, Hq, Hkv, T, d = 1, 4, 2, 24, 8
+    Q, K, V = _random_batch(rng, B, Hq, Hkv, T, d)
+    logit = np.ones((B, Hkv, T), dtype=np.float32)
+    res = O.decode_batch(Q, K, V, logit, [10], 14, 0)
+    for t in range(14):
+        for hq in range(Hq):
+            assert np.array_equal(res["out"][t, 0, hq], V[0, hq // 2, 10 + t])
+
+
+def pin_constant_values(O):
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, T, d = 1, 3, 1, 40, 4
+    Q, K, _ = _random_batch(rng, B, Hq, Hkv, T, d)
+    V = np.broadcast_to(np.array([1.5, -2.0, 0.25, 7.0]), (B, Hkv, T, d)).copy()
+    logit = rng.standard_normal((B, Hkv, T)).astype(np.float32)
+    res = O.decode_batch(Q, K, V, logit, [16], 24, 3)
+    np.testing.assert_allclose(res["out"][:, 0], np.broadcast_to(V[0, 0, 0], (24, Hq, d)),
+                               rtol=0, atol=1e-13)
+
+
+def pin_one_hot_values(O):
+    """V[i] = e_i makes the output equal the softmax weights, checked against
+    scipy's softmax of the scores over the hand-built visible set."""
+    rng = np.random.default_rng(9)
+    d = 40
+    T = 40
+    K = rng.standard_normal((T, d))
+    V = np.eye(T, d)
+    qv = rng.standard_normal((2, d))
+    alpha = np.array([i % 3 == 0 for i in range(T)])
+    w = 4
+    q = T - 1
+    keep = [i for i in range(q + 1) if (i % 3 != 0) or (q - i <= w)]
+    vis = O.visible(alpha, q, w)
+    assert list(vis) == keep
+    out = O.attend(qv, K[vis], V[vis], 1 / math.sqrt(d))
+    ref = np.zeros((2, d))
+    ref[:, keep] = scipy.special.softmax(qv @ K[keep].T / math.sqrt(d), axis=1)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-14)
+
+
+def pin_needles(O):
+    """A key aligned with the query and scaled by 40 dominates the softmax
+    when visible and must have no effect when evicted."""
+    rng = np.random.default_rng(10)
+    B, Hq, Hkv, T, d = 1, 2, 1, 64, 16
+    Q, K, V = _random_batch(rng, B, Hq, Hkv, T, d)
+    w = 4
+    logit = np.where(np.arange(T) % 2 == 0, 1.0, -1.0).astype(np.float32)[None, None]
+    P, steps = 40, 1
+    q = P
+    qv = Q[0, :, q]
+    base = O.decode_batch(Q, K, V, logit, [P], steps, w)["out"][0, 0]
+    # evicted position: marked (even) and older than the window
+    ev = 20
+    assert ev not in set(O.visible(O.eviction_decision(logit[0, 0]), q, w))
+    K2 = K.copy()
+    K2[0, 0, ev] = 40.0 * qv[0] / np.linalg.norm(qv[0]) * math.sqrt(d)
+    out_ev = O.decode_batch(Q, K2, V, logit, [P], steps, w)["out"][0, 0]
+    np.testing.assert_allclose(out_ev, base, rtol=0, atol=1e-13)
+    # live position: unmarked (odd) old token
+    lv = 21
+    K3 = K.copy()
+    K3[0, 0, lv] = 40.0 * qv[0] / np.linalg.norm(qv[0]) * math.sqrt(d)
+    out_lv = O.decode_batch(Q, K3, V, logit, [P], steps, w)["out"][0, 0]
+    np.testing.assert_allclose(out_lv[0], V[0, 0, lv], rtol=0, atol=1e-6)
+
+
+def pin_ragged_prompts(O):
+    """Per-sequence prompt lengths: each sequence's queries run at its own
+    positions; compared with the all-unmarked dense case per sequence."""
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, T, d = 3, 2, 1, 40, 8
+    Q, K, V = _random_batch(rng, B, Hq, Hkv, T, d)
+    logit = np.full((B, Hkv, T), -1.0, dtype=np.float32)
+    P = [3, 17, 30]
+    res = O.decode_batch(Q, K, V, logit, P, 8, 2)
+    for b in range(B):
+        qpos = torch.arange(P[b], P[b] + 8)[:, None]
+        allowed = (torch.arange(T)[None, :] <= qpos).numpy()
+        ref = _sdpa(np.ascontiguousarray(Q[b, :, P[b]:P[b] + 8]), K[b], V[b], allowed, Hq, Hkv)
+        np.testing.assert_allclose(res["out"][:, b].transpose(1, 0, 2), ref, rtol=0, atol=1e-12)
+
+
+ALL_PINS = [
+    pin_golden_visibility,
+    pin_fifo_simulation,
+    pin_special_visibility,
+    pin_schedule_invariants,
+    pin_decision_threshold,
+    pin_expected_live_count,
+    pin_golden_attention,
+    pin_unmarked_is_dense_causal,
+    pin_marked_is_sliding_window,
+    pin_gather_equals_masked,
+    pin_single_visible_returns_value,
+    pin_constant_values,
+    pin_one_hot_values,
+    pin_needles,
+    pin_ragged_prompts,
+]

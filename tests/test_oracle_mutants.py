@@ -1,0 +1,99 @@
+"""Plausible single mistakes planted in the oracle (on the CPU) must each make
+at least one pin fail: evidence that the pins constrain every part of it."""
+import numpy as np
+import pytest
+
+import oracle_pins
+from oracle import dms_oracle as real
+
+
+def _visible_exclusive(alpha_row, q, w):
+    i = np.arange(q + 1)
+    a = np.asarray(alpha_row[: q + 1], dtype=bool)
+    return i[(~a) | (q - i < w)]
+
+
+def _visible_drops_self(alpha_row, q, w):
+    i = np.arange(q + 1)
+    a = np.asarray(alpha_row[: q + 1], dtype=bool)
+    return i[((~a) | (q - i <= w)) & (i < q)] if q > 0 else i
+
+
+def _visible_inverted(alpha_row, q, w):
+    i = np.arange(q + 1)
+    a = np.asarray(alpha_row[: q + 1], dtype=bool)
+    return i[a | (q - i <= w)]
+
+
+def _visible_window_only(alpha_row, q, w):
+    i = np.arange(q + 1)
+    return i[q - i <= w]
+
+
+def _decision_ge(logit):
+    return np.asarray(logit, dtype=np.float32) >= 0
+
+
+def _decision_nan_marks(logit):
+    x = np.asarray(logit, dtype=np.float32)
+    return (x > 0) | np.isnan(x)
+
+
+def _retired_off_by_one(alpha_row, q, w):
+    j = q - w
+    return [j] if j >= 0 and bool(alpha_row[j]) else []
+
+
+def _kv_head_mod(hq, group):
+    return hq % group
+
+
+def _scale_over_d(d):
+    return 1.0 / d
+
+
+def _attend_kv_swapped(qv, k_rows, v_rows, scale):
+    return real._softmax(scale * (np.asarray(qv, float) @ np.asarray(v_rows, float).T)) @ np.asarray(k_rows, float)
+
+
+def _softmax_wrong_axis(s):
+    m = np.max(s, axis=0, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=0, keepdims=True)
+
+
+def _attend_masked_exclusive(qv, k_all, v_all, alpha_row, q, w, scale):
+    k = np.asarray(k_all[: q + 1], float)
+    v = np.asarray(v_all[: q + 1], float)
+    s = scale * (np.asarray(qv, float) @ k.T)
+    mask = np.array([0.0 if (not alpha_row[i]) or (q - i < w) else -np.inf for i in range(q + 1)])
+    return real._softmax(s + mask[None]) @ v
+
+
+MUTANTS = {
+    "window-exclusive": ("visible", _visible_exclusive),
+    "query-misses-itself": ("visible", _visible_drops_self),
+    "decision-inverted": ("visible", _visible_inverted),
+    "decision-ignored": ("visible", _visible_window_only),
+    "threshold-ge-zero": ("eviction_decision", _decision_ge),
+    "nan-marks": ("eviction_decision", _decision_nan_marks),
+    "retire-off-by-one": ("retired", _retired_off_by_one),
+    "gqa-modulo": ("kv_head_of", _kv_head_mod),
+    "scale-1-over-d": ("default_scale", _scale_over_d),
+    "k-v-swapped": ("attend", _attend_kv_swapped),
+    "softmax-axis": ("_softmax", _softmax_wrong_axis),
+    "masked-form-exclusive": ("attend_masked", _attend_masked_exclusive),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(real, attr, fn)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(real)
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
