@@ -1,0 +1,172 @@
+/*
+ * dms.h - C ABI of the Dynamic Memory Sparsification (DMS) decode path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ *   A KV cache whose tokens carry a learned, per-KV-head binary eviction
+ *   decision, with the decision's effect delayed by a window of w steps, and
+ *   the grouped-query decode attention that reads only the tokens still
+ *   visible.  Source: "Inference-Time Hyper-Scaling with KV Cache
+ *   Compression", third-party paper summary page, sections "Key claims" and
+ *   "Method" (the paper's section 3.2, section 5.3 and Fig. 5): per-head
+ *   decision alpha_t in {0,1}; a token marked at step t is still attended up
+ *   to step t + w and dropped afterwards; the decisions act as an additive
+ *   attention mask that never has to be built; the sparsified cache works
+ *   with paged attention and adds no KV read/write operations (section 3.2
+ *   "Performance Considerations", section 3.3).
+ *
+ * Readings fixed by this interface (the pages leave them open)
+ *   - alpha = 1 exactly when the fp32 eviction logit passed in is > 0.
+ *     0, -0 and NaN give alpha = 0.  A NaN logit is not an error.
+ *   - A token marked at position i is visible to the queries at positions
+ *     i .. i + w (inclusive) and to none after.  Unmarked tokens stay.
+ *   - Decisions are per KV head.  Query head hq reads KV head hq / G with
+ *     G = num_q_heads / num_kv_heads.
+ *   - dms_append_step appends position q (retiring q - w - 1 if it was
+ *     marked); dms_decode_attention then attends with the query of q, which
+ *     sees itself.
+ *   - Attention scale 1/sqrt(head_dim) unless dms_config.scale != 0.
+ *
+ * Conventions
+ *   - Pointers named d_* are device pointers, h_* host pointers.  All are
+ *     owned by the caller.  The library never allocates device memory: the
+ *     cache lives entirely in the caller's workspace (dms_workspace_bytes),
+ *     which holds offsets and indices only, no pointers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Calls marked "async" only enqueue work on `stream`; inputs must stay
+ *     valid until the stream reaches them.  One cache is used from one
+ *     stream at a time.
+ *   - Every call returns DMS_OK (0) or a negative dms_status.  Argument and
+ *     state errors are detected on the host before anything is enqueued.
+ *     Running out of pool blocks is detected on the device: it sets a sticky
+ *     error reported by dms_cache_stats and cleared by dms_cache_reset; the
+ *     token that found no block is not stored and all memory accesses stay
+ *     in bounds.
+ *   - Layouts are row-major, innermost index last.  B = batch,
+ *     Hq = num_q_heads, Hkv = num_kv_heads, d = head_dim.
+ */
+#ifndef DMS_H
+#define DMS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dms_cache dms_cache; /* opaque host handle */
+
+typedef enum { DMS_F32 = 0, DMS_BF16 = 1 } dms_dtype;
+
+typedef enum {
+  DMS_OK = 0,
+  DMS_ERR_ARG = -1,           /* invalid argument (null pointer, shape, dtype, ...) */
+  DMS_ERR_WORKSPACE = -2,     /* workspace too small or not 256-byte aligned */
+  DMS_ERR_OUT_OF_BLOCKS = -3, /* block pool exhausted (sticky, device-detected) */
+  DMS_ERR_CAPACITY = -4,      /* a sequence would exceed max_tokens */
+  DMS_ERR_STATE = -5,         /* call not valid in the cache's current state */
+  DMS_ERR_HIP = -6,           /* a HIP runtime call or kernel launch failed */
+  DMS_ERR_DEVICE = -7         /* current device is not gfx950 */
+} dms_status;
+
+typedef struct {
+  int32_t batch;        /* B >= 1 sequences (B <= 65535) */
+  int32_t num_q_heads;  /* Hq, a multiple of num_kv_heads, Hq / Hkv <= 16 */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;     /* d, 64 or 128 */
+  int32_t window;       /* w >= 0; values >= max_tokens behave like max_tokens */
+  int32_t block_tokens; /* tokens per cache block; must be 16 */
+  int32_t max_tokens;   /* per sequence, prompt plus decode steps, 1 .. 2^24 */
+  int32_t max_splits;   /* cap on attention work items per (sequence, KV head); 0 -> 32 */
+  int64_t pool_blocks;  /* blocks in the shared pool, 1 .. 2^31-1; one block holds
+                           16 tokens of K and V of one (sequence, KV head) */
+  dms_dtype dtype;      /* element type of Q, K, V; outputs are always fp32 */
+  float scale;          /* attention scale; 0 -> 1/sqrt(head_dim) */
+} dms_config;
+
+typedef struct {
+  int64_t live_tokens;      /* sum over (sequence, KV head) of visible tokens now */
+  int64_t seen_tokens;      /* sum over (sequence, KV head) of tokens appended so far */
+  int64_t allocated_blocks; /* pool blocks in use */
+  int64_t live_token_steps; /* sum, over dms_append_step calls, of live_tokens right after
+                               the call: the visible K/V rows the following attention reads */
+  int32_t sticky_error;     /* 0, or the first device-detected dms_status */
+  int32_t reserved;
+} dms_stats;
+
+/* Bytes of device workspace the cache needs for `cfg`, or 0 if cfg is invalid.
+   The caller allocates it (256-byte aligned) and keeps it alive until
+   dms_cache_destroy.  The size grows with pool_blocks (one block is
+   2*16*d*sizeof(dtype) bytes of K/V plus 68 bytes of metadata) and with
+   B*Hkv*(max_tokens/16 + window + 6) 32-bit words of per-head state. */
+size_t dms_workspace_bytes(const dms_config* cfg);
+
+/* Creates a handle over d_workspace and enqueues its initialisation (empty
+   cache) on `stream`.  The current HIP device must be a gfx950 and must stay
+   current for every later call on the handle.  *out receives the handle. */
+int dms_cache_create(const dms_config* cfg, void* d_workspace, size_t workspace_bytes,
+                     void* stream, dms_cache** out);
+
+/* Frees the host handle only; the workspace stays the caller's.  NULL is a no-op. */
+int dms_cache_destroy(dms_cache* c);
+
+/* Async.  Empties the cache (all sequences back to length 0, pool released,
+   sticky error cleared). */
+int dms_cache_reset(dms_cache* c, void* stream);
+
+/* Async.  Compresses a prompt into an empty cache: for every (b, h), the
+   tokens of positions 0 .. len_b - 1 that are visible to the query at
+   len_b - 1 are stored, and the marked ones among the last w + 1 positions
+   are scheduled for eviction, exactly as len_b calls of dms_append_step
+   would leave the cache.  Only visible rows are read from d_k / d_v.
+     d_k, d_v : [B, Hkv, max_len, d] of dtype
+     d_logit  : [B, Hkv, max_len] fp32 eviction logits
+     h_lengths: [B] host array, 0 <= len_b <= min(max_len, max_tokens)
+   Errors: DMS_ERR_STATE if any sequence is non-empty, DMS_ERR_CAPACITY if a
+   length exceeds max_tokens, DMS_ERR_ARG for other bad arguments. */
+int dms_prefill_compress(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit,
+                         const int32_t* h_lengths, int32_t max_len, void* stream);
+
+/* Async.  Appends one token to every sequence b at position q_b = len_b:
+   decides alpha from its logit, retires position q_b - w - 1 if that token
+   was marked (its slot is reused), stores the new K/V row.
+     d_k, d_v : [B, Hkv, d] of dtype
+     d_logit  : [B, Hkv] fp32
+   Errors: DMS_ERR_CAPACITY if some len_b + 1 > max_tokens. */
+int dms_append_step(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit,
+                    void* stream);
+
+/* Async.  Grouped-query decode attention of the query at each sequence's
+   last position over that sequence's visible tokens:
+     out[b, hq, :] = sum_i softmax_i(scale * <q[b,hq], k_i>) v_i,
+   i over the visible tokens of (b, hq / G).
+     d_q  : [B, Hq, d] of dtype
+     d_out: [B, Hq, d] fp32
+   Errors: DMS_ERR_STATE if some sequence has no token yet. */
+int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stream);
+
+/* Synchronises `stream`, then fills *out. */
+int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream);
+
+/* Synchronises `stream`, then copies the logical state of the units
+   u = unit_begin .. unit_begin + unit_count - 1, where u = b * Hkv + h:
+     h_slot_pos: [unit_count, max_tokens]  position stored in each slot, -1 if
+                 the slot holds no visible token
+     h_ring    : [unit_count, min(window, max_tokens) + 1]  pending-eviction
+                 ring: entry q mod (w+1) holds the slot of a marked token at
+                 position q that is still visible, else -1
+     h_n       : [unit_count]  slots in use (visible tokens)
+   Any of the three may be NULL to skip it.  For tests and checkpoints; not
+   on the hot path. */
+int dms_cache_export(dms_cache* c, int32_t unit_begin, int32_t unit_count, int32_t* h_slot_pos,
+                     int32_t* h_ring, int32_t* h_n, void* stream);
+
+/* Static string naming a status code. */
+const char* dms_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMS_H */

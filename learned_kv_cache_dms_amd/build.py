@@ -1,0 +1,71 @@
+"""Builds the HIP libraries in-tree for gfx950.
+
+* ``learned_kv_cache_dms_amd/libdms_hip.so`` - the DMS decode path (C ABI of
+  ``include/dms.h``).
+* ``synth/libdms_synth.so`` - device twin of the synthetic input generator.
+
+Run ``python -m learned_kv_cache_dms_amd.build`` (or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "learned_kv_cache_dms_amd")
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libdms_hip.so")
+SYNTH_LIB = os.path.join(ROOT, "synth", "libdms_synth.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the DMS library)")
+
+
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # packed-FP32 VALU forms are kept out of every code object
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if out.strip():
+        print(out, flush=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed ({r.returncode}): {' '.join(cmd)}")
+
+
+def build_dms(out: str = LIB, extra=()):
+    tmp = out + ".tmp"
+    _run([hipcc(), *COMMON, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+          os.path.join(CSRC, "dms_kernels.hip"), os.path.join(CSRC, "dms_runtime.cpp"), "-o", tmp])
+    os.replace(tmp, out)
+    return out
+
+
+def build_synth(out: str = SYNTH_LIB):
+    tmp = out + ".tmp"
+    _run([hipcc(), *COMMON, os.path.join(ROOT, "synth", "synth.hip"), "-o", tmp])
+    os.replace(tmp, out)
+    return out
+
+
+def build_all():
+    build_dms()
+    build_synth()
+
+
+if __name__ == "__main__":
+    build_all()
+    sys.exit(0)

@@ -1,0 +1,71 @@
+// Internal layout of the DMS cache workspace and the launch interface between
+// the host runtime (dms_runtime.cpp) and the kernels (dms_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace dms {
+
+constexpr int kBlockTokens = 16;
+constexpr int kMaxGroup = 16;      // query heads per KV head held by one MFMA tile
+constexpr int kWavesPerWG = 4;     // attention / append work-group = 4 independent waves
+
+// Device-side counters (one 64-byte line).
+struct Counters {
+  unsigned long long bump;              // next free pool block (may overshoot on exhaustion)
+  unsigned long long live_token_steps;  // sum of live tokens after each append call
+  int sticky_error;                     // first device-detected dms_status, else 0
+  int pad[11];
+};
+
+// Byte offsets of every region inside the caller's workspace.  The workspace
+// holds no pointers, so a byte copy of it is a complete checkpoint.
+struct Layout {
+  int32_t B, Hq, Hkv, G, d, esize;
+  int32_t R;           // ring entries per unit = min(window, max_tokens) + 1
+  int32_t max_tokens, max_blocks, max_splits, U;
+  int64_t pool_blocks, block_bytes;
+  int32_t item_floats;  // floats per attention partial: m[16], l[16], o[G][d]
+  int64_t max_items;    // partial slots = U * max_splits
+  int64_t off_pool, off_btab, off_blkpos, off_blkmask, off_ring, off_n, off_pos, off_arrive,
+      off_ctr, off_part, total;
+};
+
+// Device pointers derived from a Layout and the workspace base, passed by
+// value to every kernel.
+struct Dev {
+  uint8_t* pool;       // [pool_blocks][block_bytes]: K fragments then V fragments
+  int32_t* btab;       // [U][max_blocks] physical block of each logical block
+  int32_t* blk_pos;    // [pool_blocks][16] position held by each slot
+  uint32_t* blk_mask;  // [pool_blocks] live-slot bits (low 16)
+  int32_t* ring;       // [U][R] slot of a pending marked token, or -1
+  int32_t* n;          // [U] slots in use
+  int32_t* pos;        // [U] tokens appended so far (next position)
+  int32_t* arrive;     // [U] attention work items finished in the current call
+  Counters* ctr;
+  float* part;         // [max_items][item_floats] attention partials
+  int32_t B, Hq, Hkv, G, R, max_tokens, max_blocks, max_splits, U, item_floats, target_items;
+  int64_t pool_blocks, block_bytes;
+  float scale_log2e;   // attention scale times log2(e)
+};
+
+// Prompt lengths of up to kMax sequences, passed by value to the prefill kernel.
+struct PromptLens {
+  static constexpr int kMax = 256;
+  int32_t v[kMax];
+};
+
+// Status codes mirrored from dms.h for device code.
+constexpr int kErrOutOfBlocks = -3;
+
+hipError_t launch_init(const Dev& p, hipStream_t s);
+hipError_t launch_append(const Dev& p, int dtype, int d, const void* k, const void* v,
+                         const float* logit, hipStream_t s);
+hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const void* v,
+                          const float* logit, const int32_t* h_lengths, int32_t max_len, hipStream_t s);
+hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s);
+hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out,
+                            int64_t grid_waves, hipStream_t s);
+
+}  // namespace dms

@@ -1,0 +1,776 @@
+// HIP kernels of the DMS decode path for gfx950 (MI355X).
+//
+// Method: "Inference-Time Hyper-Scaling with KV Cache Compression", paper
+// summary page, "Key claims" and "Method" (paper section 3.2, section 5.3,
+// Fig. 5).  Each KV head decides per token whether to evict it (alpha = 1
+// when the eviction logit is > 0); a marked token stays attendable for w more
+// steps, then leaves the cache.  Attention reads only what is still visible,
+// so the additive mask of the paper is never built.
+//
+// Cache layout (all inside the caller's workspace, see dms_internal.h)
+//   * Per (sequence, KV head) "unit": n live slots, always the dense prefix
+//     [0, n) of the unit's slot space (an append reuses the slot of the token
+//     it retires, else takes slot n), a block table mapping logical block
+//     j = slot / 16 to a physical pool block, and a ring of R = w + 1 slots
+//     of marked tokens whose eviction is pending (entry q mod R belongs to
+//     position q).
+//   * Pool blocks hold 16 tokens of K and V in MFMA-fragment order, so the
+//     decode attention loads each operand with one 16-byte load per lane
+//     and 1 KiB contiguous per wave instruction:
+//       K half, chunk c, lane l (16 bytes):
+//         token l % 16, channels c*4*E + E*(l/16) + e  (E = 16/sizeof(T))
+//       V half, chunk c, lane l (16 bytes):
+//         tokens 4*(l/16) + e (e < 4), channel 16*(c*NJ + jj) + l % 16
+//         at byte jj*8 + e*sizeof(T)  (NJ = 2 for bf16, 1 for fp32)
+//   * Per block: 16 slot positions and a 16-bit live mask.
+//
+// Decode attention per (unit, block range) work item, one wave each:
+//   S[t][g]  = K_blk[t] . Q[g]     MFMA, A = K fragment, B = Q fragment
+//   online softmax on S in the MFMA output layout (lane l holds tokens
+//            4*(l/16)+r of head l % 16), exp2 domain
+//   O^T[c][g] += V^T[c][t] P[t][g]  MFMA, A = V fragment, B = P taken in
+//            place from the S registers (bf16: P split into hi + lo parts)
+// The last wave of a unit to finish merges the partials (log-sum-exp).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "dms_internal.h"
+
+namespace dms {
+
+typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned int))));
+typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+
+template <int ES, int D>
+struct Geo {
+  static constexpr int kE = 16 / ES;                // elements per 16-byte chunk
+  static constexpr int kChunks = D * 16 * ES / 1024;  // chunks per lane per K (or V) half
+  static constexpr int kHalf = D * 16 * ES;         // bytes of one half-block
+  static constexpr int kTiles = D / 16;             // output tiles of 16 channels
+  static constexpr int kNJ = ES == 2 ? 2 : 1;       // V channel groups per chunk
+};
+
+// ---------------------------------------------------------------------------
+// wave helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(unsigned, v);
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(unsigned x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// state initialisation (create / reset)
+// ---------------------------------------------------------------------------
+
+__global__ void init_kernel(Dev p) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t nring = (int64_t)p.U * p.R;
+  for (int64_t i = tid; i < nring; i += stride) p.ring[i] = -1;
+  for (int64_t i = tid; i < p.U; i += stride) {
+    p.n[i] = 0;
+    p.pos[i] = 0;
+    p.arrive[i] = 0;
+  }
+  if (tid == 0) {
+    p.ctr->bump = 0;
+    p.ctr->live_token_steps = 0;
+    p.ctr->sticky_error = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// append + evict: one wave per (sequence, KV head)
+// ---------------------------------------------------------------------------
+
+// Stores one token row into slot t of an existing block.
+template <int ES, int D>
+__device__ __forceinline__ void write_row(uint8_t* blkp, int t, const uint8_t* krow,
+                                          const uint8_t* vrow, int lane) {
+  using G = Geo<ES, D>;
+  if (lane < D / G::kE) {
+    const int r = lane;  // 16-byte piece of the row: channels r*E .. r*E+E-1
+    u32x4 val = *(const u32x4*)(krow + r * 16);
+    *(u32x4*)(blkp + (r >> 2) * 1024 + (t + 16 * (r & 3)) * 16) = val;
+  }
+#pragma unroll
+  for (int ch = lane; ch < D; ch += 64) {
+    const int c = ch / (16 * G::kNJ), jj = (ch >> 4) % G::kNJ, nn = ch & 15;
+    const int l = nn + 16 * (t >> 2), e = t & 3;
+    uint8_t* dst = blkp + G::kHalf + c * 1024 + l * 16 + jj * 8 + e * ES;
+    if constexpr (ES == 2)
+      *(uint16_t*)dst = *(const uint16_t*)(vrow + ch * 2);
+    else
+      *(uint32_t*)dst = *(const uint32_t*)(vrow + ch * 4);
+  }
+}
+
+// Writes a whole fresh block: the row in slot 0, zeros in slots 1..15 (the
+// attention multiplies masked slots by zero weights, so they must be finite).
+template <int ES, int D>
+__device__ __forceinline__ void write_fresh(uint8_t* blkp, const uint8_t* krow,
+                                            const uint8_t* vrow, int lane) {
+  using G = Geo<ES, D>;
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) {
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if ((lane & 15) == 0) val = *(const u32x4*)(krow + (c * 4 + (lane >> 4)) * 16);
+    *(u32x4*)(blkp + c * 1024 + lane * 16) = val;
+  }
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) {
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (lane < 16) {
+      if constexpr (ES == 2) {
+        val[0] = *(const uint16_t*)(vrow + (16 * (2 * c) + lane) * 2);
+        val[2] = *(const uint16_t*)(vrow + (16 * (2 * c + 1) + lane) * 2);
+      } else {
+        val[0] = *(const uint32_t*)(vrow + (16 * c + lane) * 4);
+      }
+    }
+    *(u32x4*)(blkp + G::kHalf + c * 1024 + lane * 16) = val;
+  }
+}
+
+template <int ES, int D>
+__global__ __launch_bounds__(256) void append_kernel(Dev p, const uint8_t* __restrict__ k,
+                                                     const uint8_t* __restrict__ v,
+                                                     const float* __restrict__ logit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x * kWavesPerWG + wave;
+  __shared__ unsigned s_live[kWavesPerWG];
+  unsigned live = 0;
+  if (u < p.U) {
+    const float lg = logit[u];
+    const bool alpha = lg > 0.0f;  // NaN compares false
+    const int q = p.pos[u];
+    const int r = q % p.R;
+    int32_t* ring = p.ring + (int64_t)u * p.R;
+    int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
+    const int s = ring[r];          // slot of position q - R if it was marked
+    const int n = p.n[u];
+    const uint8_t* krow = k + (int64_t)u * D * ES;
+    const uint8_t* vrow = v + (int64_t)u * D * ES;
+    int slot, blk = 0;
+    bool fresh = false, ok = true;
+    if (s >= 0) {  // retire position q - R, reuse its slot
+      slot = s;
+      blk = bt[slot >> 4];
+    } else {
+      slot = n;
+      if ((slot & 15) == 0) {
+        unsigned long long nb = 0;
+        if (lane == 0) nb = atomicAdd(&p.ctr->bump, 1ull);
+        nb = __shfl(nb, 0);
+        if (nb >= (unsigned long long)p.pool_blocks) {
+          ok = false;
+          if (lane == 0) atomicCAS(&p.ctr->sticky_error, 0, kErrOutOfBlocks);
+        } else {
+          blk = (int)nb;
+          fresh = true;
+          if (lane == 0) bt[slot >> 4] = blk;
+        }
+      } else {
+        blk = bt[slot >> 4];
+      }
+    }
+    const int t = slot & 15;
+    if (ok) {
+      uint8_t* dst = p.pool + (int64_t)blk * p.block_bytes;
+      if (fresh)
+        write_fresh<ES, D>(dst, krow, vrow, lane);
+      else
+        write_row<ES, D>(dst, t, krow, vrow, lane);
+      if (lane == 0) {
+        p.blk_pos[(int64_t)blk * 16 + t] = q;
+        if (fresh)
+          p.blk_mask[blk] = 1u;
+        else if (s < 0)
+          p.blk_mask[blk] |= 1u << t;
+        ring[r] = alpha ? slot : -1;
+        if (s < 0) p.n[u] = n + 1;
+      }
+      live = (s < 0) ? (unsigned)(n + 1) : (unsigned)n;
+    } else {
+      if (lane == 0) ring[r] = -1;
+      live = (unsigned)n;
+    }
+    if (lane == 0) p.pos[u] = q + 1;
+  }
+  if (lane == 0) s_live[wave] = live;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long sum = 0;
+#pragma unroll
+    for (int i = 0; i < kWavesPerWG; ++i) sum += s_live[i];
+    atomicAdd(&p.ctr->live_token_steps, sum);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prefill compress
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int block_sum_1024(int x, int* s_tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_sum_i(x);
+  __syncthreads();
+  if (lane == 0) s_tmp[wave] = x;
+  __syncthreads();
+  int t = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += s_tmp[i];
+  return t;
+}
+
+// One work-group of 1024 threads per (sequence, KV head): counts the tokens
+// visible at the last prompt position, reserves their blocks with one
+// atomic, assigns slots in position order and fills block table, slot
+// positions, masks and the pending-eviction ring.
+__global__ __launch_bounds__(1024) void prefill_scan_kernel(Dev p, const float* __restrict__ logit,
+                                                            int32_t max_len, int32_t b0, PromptLens lens) {
+  __shared__ int s_tmp[16];
+  __shared__ int s_wave_pre[16];
+  __shared__ long long s_base;
+  __shared__ int s_n;
+  const int u = b0 * p.Hkv + blockIdx.x;
+  const int P = lens.v[blockIdx.x / p.Hkv];
+  const int w = p.R - 1;
+  const float* lg = logit + (int64_t)u * max_len;
+  int32_t* ring = p.ring + (int64_t)u * p.R;
+  for (int i = threadIdx.x; i < p.R; i += blockDim.x) ring[i] = -1;
+
+  int cnt = 0;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) {
+    const bool alpha = lg[i] > 0.0f;
+    cnt += (!alpha || (P - 1 - i) <= w) ? 1 : 0;
+  }
+  int n = block_sum_1024(cnt, s_tmp);
+  if (threadIdx.x == 0) {
+    long long base = 0;
+    const int nb = (n + 15) >> 4;
+    if (nb > 0) {
+      base = (long long)atomicAdd(&p.ctr->bump, (unsigned long long)nb);
+      if (base + nb > p.pool_blocks) {
+        atomicCAS(&p.ctr->sticky_error, 0, kErrOutOfBlocks);
+        n = 0;
+      }
+    }
+    s_base = base;
+    s_n = n;
+  }
+  __syncthreads();
+  n = s_n;
+  const long long base = s_base;
+  const int nb = (n + 15) >> 4;
+  int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
+  for (int j = threadIdx.x; j < nb; j += blockDim.x) {
+    bt[j] = (int32_t)(base + j);
+    const int fill = (j < nb - 1 || (n & 15) == 0) ? 16 : (n & 15);
+    p.blk_mask[base + j] = (fill == 16) ? 0xffffu : ((1u << fill) - 1u);
+  }
+  if (n > 0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int running = 0;
+    for (int i0 = 0; i0 < P; i0 += blockDim.x) {
+      const int i = i0 + threadIdx.x;
+      bool alpha = false;
+      int vis = 0;
+      if (i < P) {
+        alpha = lg[i] > 0.0f;
+        vis = (!alpha || (P - 1 - i) <= w) ? 1 : 0;
+      }
+      const int incl = wave_incl_scan_i(vis, lane);
+      __syncthreads();
+      if (lane == 63) s_wave_pre[wave] = incl;
+      __syncthreads();
+      int before = 0, total = 0;
+      for (int x = 0; x < nw; ++x) {
+        const int y = s_wave_pre[x];
+        if (x < wave) before += y;
+        total += y;
+      }
+      if (vis) {
+        const int slot = running + before + incl - 1;
+        const int64_t blk = base + (slot >> 4);
+        p.blk_pos[blk * 16 + (slot & 15)] = i;
+        if (alpha) ring[i % p.R] = slot;  // marked and visible: eviction pending
+      }
+      running += total;
+    }
+  }
+  if (threadIdx.x == 0) {
+    p.n[u] = n;
+    p.pos[u] = P;
+  }
+}
+
+// Gathers the visible rows of the dense prompt into the unit's blocks, in
+// fragment order.  Grid (U, S); each wave handles whole blocks.
+template <int ES, int D>
+__global__ __launch_bounds__(256) void prefill_scatter_kernel(Dev p, const uint8_t* __restrict__ k,
+                                                              const uint8_t* __restrict__ v,
+                                                              int32_t max_len) {
+  using G = Geo<ES, D>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x;
+  const int n = p.n[u];
+  const int nb = (n + 15) >> 4;
+  const int64_t row0 = (int64_t)u * max_len;
+  const int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
+  for (int j = blockIdx.y * kWavesPerWG + wave; j < nb; j += gridDim.y * kWavesPerWG) {
+    const int blk = bt[j];
+    const uint32_t msk = p.blk_mask[blk];
+    uint8_t* dst = p.pool + (int64_t)blk * p.block_bytes;
+    const int32_t* bpos = p.blk_pos + (int64_t)blk * 16;
+    // K: lane l carries token l % 16
+    {
+      const int t = lane & 15;
+      const int sp = ((msk >> t) & 1u) ? bpos[t] : -1;
+      const uint8_t* src = k + (row0 + (sp < 0 ? 0 : sp)) * D * ES;
+#pragma unroll
+      for (int c = 0; c < G::kChunks; ++c) {
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (sp >= 0) val = *(const u32x4*)(src + (c * 4 * G::kE + G::kE * (lane >> 4)) * ES);
+        *(u32x4*)(dst + c * 1024 + lane * 16) = val;
+      }
+    }
+    // V: lane l carries tokens 4*(l/16) + e
+    {
+      int sp[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 4 * (lane >> 4) + e;
+        sp[e] = ((msk >> t) & 1u) ? bpos[t] : -1;
+      }
+#pragma unroll
+      for (int c = 0; c < G::kChunks; ++c) {
+        u32x4 val = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int jj = 0; jj < G::kNJ; ++jj) {
+          const int ch = 16 * (c * G::kNJ + jj) + (lane & 15);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (sp[e] < 0) continue;
+            const uint8_t* src = v + ((row0 + sp[e]) * D + ch) * ES;
+            if constexpr (ES == 2) {
+              const unsigned x = *(const uint16_t*)src;
+              val[jj * 2 + (e >> 1)] |= x << (16 * (e & 1));
+            } else {
+              val[e] = *(const uint32_t*)src;
+            }
+          }
+        }
+        *(u32x4*)(dst + G::kHalf + c * 1024 + lane * 16) = val;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode attention
+// ---------------------------------------------------------------------------
+
+struct Item {
+  int u, k, items, base, nblk;
+};
+
+// Work plan, computed redundantly by every wave from the live counts n[]:
+// C = ceil(total blocks / target) blocks per item, unit u gets
+// min(max_splits, ceil(nblk_u / C)) items holding equal shares of its
+// blocks, items are numbered unit-major.  Returns false if `item` >= total.
+__device__ __forceinline__ int plan_total(const Dev& p, int lane, int& C) {
+  int tot = 0;
+  for (int b0 = 0; b0 < p.U; b0 += 64) {
+    const int uu = b0 + lane;
+    if (uu < p.U) tot += (p.n[uu] + 15) >> 4;
+  }
+  tot = wave_sum_i(tot);
+  C = max(1, (tot + p.target_items - 1) / p.target_items);
+  int items = 0;
+  for (int b0 = 0; b0 < p.U; b0 += 64) {
+    const int uu = b0 + lane;
+    if (uu < p.U) {
+      const int nb = (p.n[uu] + 15) >> 4;
+      items += nb > 0 ? min(p.max_splits, (nb + C - 1) / C) : 0;
+    }
+  }
+  return wave_sum_i(items);
+}
+
+__device__ __forceinline__ bool plan_find(const Dev& p, int lane, int C, int item, Item& it) {
+  int running = 0;
+  for (int b0 = 0; b0 < p.U; b0 += 64) {
+    const int uu = b0 + lane;
+    int nb = 0, cnt = 0;
+    if (uu < p.U) {
+      nb = (p.n[uu] + 15) >> 4;
+      cnt = nb > 0 ? min(p.max_splits, (nb + C - 1) / C) : 0;
+    }
+    const int incl = wave_incl_scan_i(cnt, lane);
+    const int start = running + incl - cnt;
+    const unsigned long long bal = __ballot(item >= start && item < start + cnt);
+    if (bal) {
+      const int src = __ffsll((long long)bal) - 1;
+      it.u = b0 + src;
+      it.base = __shfl(start, src);
+      it.items = __shfl(cnt, src);
+      it.nblk = __shfl(nb, src);
+      it.k = item - it.base;
+      return true;
+    }
+    running += __shfl(incl, 63);
+  }
+  return false;
+}
+
+template <int ES, int D>
+struct Frag {
+  u32x4 k[Geo<ES, D>::kChunks];
+  u32x4 v[Geo<ES, D>::kChunks];
+};
+
+template <int ES, int D>
+__device__ __forceinline__ void load_frag(Frag<ES, D>& f, const uint8_t* blkp, int lane) {
+  using G = Geo<ES, D>;
+  const uint8_t* a = blkp + lane * 16;
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) f.k[c] = __builtin_nontemporal_load((const u32x4*)(a + c * 1024));
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c)
+    f.v[c] = __builtin_nontemporal_load((const u32x4*)(a + G::kHalf + c * 1024));
+}
+
+// Running softmax state of one wave: lane l tracks head l % 16.
+template <int D>
+struct Acc {
+  f32x4 o[D / 16];  // O^T tiles: lane l, reg r -> channel 16j + 4(l/16) + r of head l % 16
+  float m, l;
+};
+
+template <int ES, int D>
+__device__ __forceinline__ void attend_block(const Frag<ES, D>& f, const u32x4 (&qf)[Geo<ES, D>::kChunks],
+                                             uint32_t mask, int lane, float sl2e, Acc<D>& a) {
+  using G = Geo<ES, D>;
+  f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) {
+    if constexpr (ES == 2) {
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.k[c]),
+                                                 __builtin_bit_cast(bf16x8, qf[c]), S, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(f.k[c][e]), __uint_as_float(qf[c][e]),
+                                                 S, 0, 0, 0);
+    }
+  }
+  const int tb = 4 * (lane >> 4);
+  float s[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s[r] = ((mask >> (tb + r)) & 1u) ? S[r] * sl2e : -INFINITY;
+  float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float mn = fmaxf(a.m, bm);
+  const float mref = (mn == -INFINITY) ? 0.f : mn;
+  const float alpha = exp2_fast(a.m - mref);
+  float pr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(s[r] - mref);
+  a.l = a.l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+  a.m = mn;
+#pragma unroll
+  for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
+  if constexpr (ES == 2) {
+    const unsigned h01 = pack_bf16x2(pr[0], pr[1]), h23 = pack_bf16x2(pr[2], pr[3]);
+    const unsigned l01 = pack_bf16x2(pr[0] - bf16_lo_to_f32(h01), pr[1] - bf16_hi_to_f32(h01));
+    const unsigned l23 = pack_bf16x2(pr[2] - bf16_lo_to_f32(h23), pr[3] - bf16_hi_to_f32(h23));
+    const u32x2 hv = {h01, h23}, lv = {l01, l23};
+    const s16x4 PH = __builtin_bit_cast(s16x4, hv), PL = __builtin_bit_cast(s16x4, lv);
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const u32x2 vv = {f.v[c][2 * jj], f.v[c][2 * jj + 1]};
+        const s16x4 A = __builtin_bit_cast(s16x4, vv);
+        a.o[2 * c + jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, PH, a.o[2 * c + jj], 0, 0, 0);
+        a.o[2 * c + jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, PL, a.o[2 * c + jj], 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a.o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(f.v[c][e]), pr[e], a.o[c], 0, 0, 0);
+    }
+  }
+}
+
+template <int ES, int D>
+__global__ __launch_bounds__(256) void attention_kernel(Dev p, const uint8_t* __restrict__ q,
+                                                        float* __restrict__ out) {
+  using G = Geo<ES, D>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  int C;
+  const int T = plan_total(p, lane, C);
+  // XCD-aware numbering: work-group wg runs on XCD wg % 8; XCD x takes the
+  // contiguous item range [x*T/8, (x+1)*T/8) so a unit's items share an L2.
+  const int nwg = gridDim.x, wg = blockIdx.x;
+  const int x = wg & 7, rr = wg >> 3;
+  const int lo = (int)(((long long)x * T) >> 3), hi = (int)(((long long)(x + 1) * T) >> 3);
+  const int item = lo + rr * kWavesPerWG + wave;
+  (void)nwg;
+  if (item >= hi) return;
+  Item it;
+  if (!plan_find(p, lane, C, item, it)) return;
+
+  const int u = it.u;
+  const int b = u / p.Hkv, h = u - b * p.Hkv;
+  const int g = lane & 15;
+  const bool gvalid = g < p.G;
+  const int hq = h * p.G + g;
+
+  // Q fragment (B operand of S = K Q^T): head g, the channels this lane's
+  // K fragment elements carry.
+  u32x4 qf[G::kChunks];
+  {
+    const uint8_t* qrow = q + ((int64_t)b * p.Hq + (gvalid ? hq : 0)) * D * ES;
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qf[c] = gvalid ? *(const u32x4*)(qrow + (c * 4 * G::kE + G::kE * (lane >> 4)) * ES) : z;
+    }
+  }
+
+  const int jb = (int)(((long long)it.k * it.nblk) / it.items);
+  const int je = (int)(((long long)(it.k + 1) * it.nblk) / it.items);
+  const int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
+
+  Acc<D> acc;
+#pragma unroll
+  for (int j = 0; j < G::kTiles; ++j) acc.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  acc.m = -INFINITY;
+  acc.l = 0.f;
+
+  // block ids and masks, 64 at a time in lane-vector registers
+  int win = jb;
+  int idv = (jb + lane < je) ? bt[jb + lane] : 0;
+  uint32_t mkv = (jb + lane < je) ? p.blk_mask[idv] : 0u;
+  auto blk_of = [&](int J, int& blk, uint32_t& msk) {
+    if (J - win >= 64) {
+      win += 64;
+      idv = (win + lane < je) ? bt[win + lane] : 0;
+      mkv = (win + lane < je) ? p.blk_mask[idv] : 0u;
+    }
+    blk = __builtin_amdgcn_readlane(idv, J - win);
+    msk = (uint32_t)__builtin_amdgcn_readlane((int)mkv, J - win);
+  };
+
+  const float sl2e = p.scale_log2e;
+  Frag<ES, D> f0, f1, f2;
+  int bk0 = 0, bk1 = 0, bk2 = 0;
+  uint32_t m0 = 0, m1 = 0, m2 = 0;
+  blk_of(jb, bk0, m0);
+  load_frag<ES, D>(f0, p.pool + (int64_t)bk0 * p.block_bytes, lane);
+  if (jb + 1 < je) {
+    blk_of(jb + 1, bk1, m1);
+    load_frag<ES, D>(f1, p.pool + (int64_t)bk1 * p.block_bytes, lane);
+  }
+  for (int j = jb; j < je; j += 3) {
+    if (j + 2 < je) {
+      blk_of(j + 2, bk2, m2);
+      load_frag<ES, D>(f2, p.pool + (int64_t)bk2 * p.block_bytes, lane);
+    }
+    attend_block<ES, D>(f0, qf, m0, lane, sl2e, acc);
+    if (j + 1 >= je) break;
+    if (j + 3 < je) {
+      blk_of(j + 3, bk0, m0);
+      load_frag<ES, D>(f0, p.pool + (int64_t)bk0 * p.block_bytes, lane);
+    }
+    attend_block<ES, D>(f1, qf, m1, lane, sl2e, acc);
+    if (j + 2 >= je) break;
+    if (j + 4 < je) {
+      blk_of(j + 4, bk1, m1);
+      load_frag<ES, D>(f1, p.pool + (int64_t)bk1 * p.block_bytes, lane);
+    }
+    attend_block<ES, D>(f2, qf, m2, lane, sl2e, acc);
+  }
+
+  // lane-local l holds 4 of the 16 tokens per block; add the four groups
+  float lt = acc.l + __shfl_xor(acc.l, 16);
+  lt = lt + __shfl_xor(lt, 32);
+
+  float* orow = out + ((int64_t)b * p.Hq + hq) * D + 4 * (lane >> 4);
+  if (it.items == 1) {
+    if (gvalid) {
+      const float inv = 1.0f / lt;
+#pragma unroll
+      for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(orow + 16 * j) = acc.o[j] * inv;
+    }
+    return;
+  }
+
+  // several items: publish the partial, the last one to arrive merges
+  const int IF = p.item_floats;
+  float* mine = p.part + (int64_t)(it.base + it.k) * IF;
+  if (gvalid) {
+    if (lane < 16) {
+      mine[g] = acc.m;
+      mine[16 + g] = lt;
+    }
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(mine + 32 + g * D + 16 * j + 4 * (lane >> 4)) = acc.o[j];
+  }
+  __threadfence();
+  int old = 0;
+  if (lane == 0) old = atomicAdd(&p.arrive[u], 1);
+  old = __shfl(old, 0);
+  if (old != it.items - 1) return;
+  __threadfence();
+  if (lane == 0) p.arrive[u] = 0;
+  if (!gvalid) return;
+  const float* pb = p.part + (int64_t)it.base * IF;
+  float M = -INFINITY;
+  for (int s = 0; s < it.items; ++s) M = fmaxf(M, pb[(int64_t)s * IF + g]);
+  const float Mr = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f;
+  f32x4 O[G::kTiles];
+#pragma unroll
+  for (int j = 0; j < G::kTiles; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < it.items; ++s) {
+    const float* ps = pb + (int64_t)s * IF;
+    const float ws = exp2_fast(ps[g] - Mr);
+    L += ws * ps[16 + g];
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j)
+      O[j] += ws * *(const f32x4*)(ps + 32 + g * D + 16 * j + 4 * (lane >> 4));
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(orow + 16 * j) = O[j] * inv;
+}
+
+// ---------------------------------------------------------------------------
+// export: slot -> position of units [u0, u0 + count) into a staging area
+// ---------------------------------------------------------------------------
+
+// Flat index f = (u - u0) * max_tokens + slot, for f in [f0, f0 + len).
+__global__ void export_kernel(Dev p, int32_t u0, int64_t f0, int64_t len, int32_t* __restrict__ stage) {
+  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < len; k += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = f0 + k;
+    const int iu = (int)(i / p.max_tokens);
+    const int slot = (int)(i - (int64_t)iu * p.max_tokens);
+    const int u = u0 + iu;
+    int32_t val = -1;
+    if (slot < p.n[u]) {
+      const int blk = p.btab[(int64_t)u * p.max_blocks + (slot >> 4)];
+      if ((p.blk_mask[blk] >> (slot & 15)) & 1u) val = p.blk_pos[(int64_t)blk * 16 + (slot & 15)];
+    }
+    stage[k] = val;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_init(const Dev& p, hipStream_t s) {
+  const int64_t work = std::max<int64_t>((int64_t)p.U * p.R, p.U);
+  const int threads = 256;
+  const int blocks = (int)std::min<int64_t>((work + threads - 1) / threads, 4096);
+  hipLaunchKernelGGL(init_kernel, dim3(std::max(blocks, 1)), dim3(threads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s) {
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((len + 255) / 256, 8192));
+  hipLaunchKernelGGL(export_kernel, dim3(blocks), dim3(256), 0, s, p, u0, f0, len, stage);
+  return hipGetLastError();
+}
+
+template <int ES, int D>
+static hipError_t append_t(const Dev& p, const void* k, const void* v, const float* logit, hipStream_t s) {
+  const int blocks = (p.U + kWavesPerWG - 1) / kWavesPerWG;
+  hipLaunchKernelGGL((append_kernel<ES, D>), dim3(blocks), dim3(64 * kWavesPerWG), 0, s, p,
+                     (const uint8_t*)k, (const uint8_t*)v, logit);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Dev& p, int dtype, int d, const void* k, const void* v,
+                         const float* logit, hipStream_t s) {
+  if (dtype == 1) return d == 128 ? append_t<2, 128>(p, k, v, logit, s) : append_t<2, 64>(p, k, v, logit, s);
+  return d == 128 ? append_t<4, 128>(p, k, v, logit, s) : append_t<4, 64>(p, k, v, logit, s);
+}
+
+template <int ES, int D>
+static hipError_t prefill_t(const Dev& p, const void* k, const void* v, const float* logit,
+                            const int32_t* h_lengths, int32_t max_len, hipStream_t s) {
+  for (int b0 = 0; b0 < p.B; b0 += PromptLens::kMax) {
+    const int nb = std::min(PromptLens::kMax, p.B - b0);
+    PromptLens lens;
+    for (int i = 0; i < nb; ++i) lens.v[i] = h_lengths[b0 + i];
+    hipLaunchKernelGGL(prefill_scan_kernel, dim3(nb * p.Hkv), dim3(1024), 0, s, p, logit, max_len, b0, lens);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int ysplit = 8;
+  hipLaunchKernelGGL((prefill_scatter_kernel<ES, D>), dim3(p.U, ysplit), dim3(64 * kWavesPerWG), 0, s, p,
+                     (const uint8_t*)k, (const uint8_t*)v, max_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const void* v,
+                          const float* logit, const int32_t* h_lengths, int32_t max_len, hipStream_t s) {
+  if (dtype == 1)
+    return d == 128 ? prefill_t<2, 128>(p, k, v, logit, h_lengths, max_len, s)
+                    : prefill_t<2, 64>(p, k, v, logit, h_lengths, max_len, s);
+  return d == 128 ? prefill_t<4, 128>(p, k, v, logit, h_lengths, max_len, s)
+                  : prefill_t<4, 64>(p, k, v, logit, h_lengths, max_len, s);
+}
+
+template <int ES, int D>
+static hipError_t attention_t(const Dev& p, const void* q, float* out, int64_t grid_waves, hipStream_t s) {
+  const int64_t nwg = grid_waves / kWavesPerWG;
+  hipLaunchKernelGGL((attention_kernel<ES, D>), dim3((unsigned)nwg), dim3(64 * kWavesPerWG), 0, s, p,
+                     (const uint8_t*)q, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out, int64_t grid_waves,
+                            hipStream_t s) {
+  if (dtype == 1)
+    return d == 128 ? attention_t<2, 128>(p, q, out, grid_waves, s) : attention_t<2, 64>(p, q, out, grid_waves, s);
+  return d == 128 ? attention_t<4, 128>(p, q, out, grid_waves, s) : attention_t<4, 64>(p, q, out, grid_waves, s);
+}
+
+}  // namespace dms

@@ -1,0 +1,302 @@
+// Host runtime behind the C ABI in include/dms.h: argument and state
+// validation, workspace layout, launch geometry, status mapping, and the
+// host side of stats / export.  All device work is the kernels in
+// dms_kernels.hip; nothing here computes any part of the decode path.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "dms.h"
+#include "dms_internal.h"
+
+struct dms_cache {
+  dms_config cfg;
+  dms::Layout L;
+  uint8_t* ws;
+  int device;
+  int num_cus;
+  int target_items;
+  int64_t grid_waves;
+  std::vector<int32_t> len;  // host mirror of each sequence's length
+};
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool valid_config(const dms_config* c) {
+  if (!c) return false;
+  if (c->batch < 1 || c->batch > 65535) return false;
+  if (c->num_kv_heads < 1 || c->num_q_heads < 1) return false;
+  if (c->num_q_heads % c->num_kv_heads != 0) return false;
+  if (c->num_q_heads / c->num_kv_heads > dms::kMaxGroup) return false;
+  if ((int64_t)c->batch * c->num_kv_heads > (1 << 24)) return false;
+  if (c->head_dim != 64 && c->head_dim != 128) return false;
+  if (c->window < 0) return false;
+  if (c->block_tokens != dms::kBlockTokens) return false;
+  if (c->max_tokens < 1 || c->max_tokens > (1 << 24)) return false;
+  if (c->max_splits < 0 || c->max_splits > 1024) return false;
+  if (c->pool_blocks < 1 || c->pool_blocks > 0x7fffffffLL) return false;
+  if (c->dtype != DMS_F32 && c->dtype != DMS_BF16) return false;
+  if (!isfinite(c->scale) || c->scale < 0.0f) return false;
+  return true;
+}
+
+void make_layout(const dms_config* c, dms::Layout& L) {
+  L.B = c->batch;
+  L.Hq = c->num_q_heads;
+  L.Hkv = c->num_kv_heads;
+  L.G = c->num_q_heads / c->num_kv_heads;
+  L.d = c->head_dim;
+  L.esize = c->dtype == DMS_BF16 ? 2 : 4;
+  L.R = std::min(c->window, c->max_tokens) + 1;
+  L.max_tokens = c->max_tokens;
+  L.max_blocks = (c->max_tokens + dms::kBlockTokens - 1) / dms::kBlockTokens;
+  L.max_splits = c->max_splits == 0 ? 32 : c->max_splits;
+  L.U = c->batch * c->num_kv_heads;
+  L.pool_blocks = c->pool_blocks;
+  L.block_bytes = 2LL * dms::kBlockTokens * L.d * L.esize;
+  L.item_floats = 32 + L.G * L.d;
+  L.max_items = (int64_t)L.U * L.max_splits;
+  int64_t o = 0;
+  L.off_pool = o;
+  o = align_up(o + L.pool_blocks * L.block_bytes, kAlign);
+  L.off_btab = o;
+  o = align_up(o + (int64_t)L.U * L.max_blocks * 4, kAlign);
+  L.off_blkpos = o;
+  o = align_up(o + L.pool_blocks * dms::kBlockTokens * 4, kAlign);
+  L.off_blkmask = o;
+  o = align_up(o + L.pool_blocks * 4, kAlign);
+  L.off_ring = o;
+  o = align_up(o + (int64_t)L.U * L.R * 4, kAlign);
+  L.off_n = o;
+  o = align_up(o + (int64_t)L.U * 4, kAlign);
+  L.off_pos = o;
+  o = align_up(o + (int64_t)L.U * 4, kAlign);
+  L.off_arrive = o;
+  o = align_up(o + (int64_t)L.U * 4, kAlign);
+  L.off_ctr = o;
+  o = align_up(o + (int64_t)sizeof(dms::Counters), kAlign);
+  L.off_part = o;
+  o = align_up(o + L.max_items * L.item_floats * 4, kAlign);
+  L.total = o;
+}
+
+dms::Dev make_dev(const dms_cache* c) {
+  const dms::Layout& L = c->L;
+  dms::Dev p;
+  p.pool = c->ws + L.off_pool;
+  p.btab = (int32_t*)(c->ws + L.off_btab);
+  p.blk_pos = (int32_t*)(c->ws + L.off_blkpos);
+  p.blk_mask = (uint32_t*)(c->ws + L.off_blkmask);
+  p.ring = (int32_t*)(c->ws + L.off_ring);
+  p.n = (int32_t*)(c->ws + L.off_n);
+  p.pos = (int32_t*)(c->ws + L.off_pos);
+  p.arrive = (int32_t*)(c->ws + L.off_arrive);
+  p.ctr = (dms::Counters*)(c->ws + L.off_ctr);
+  p.part = (float*)(c->ws + L.off_part);
+  p.B = L.B;
+  p.Hq = L.Hq;
+  p.Hkv = L.Hkv;
+  p.G = L.G;
+  p.R = L.R;
+  p.max_tokens = L.max_tokens;
+  p.max_blocks = L.max_blocks;
+  p.max_splits = L.max_splits;
+  p.U = L.U;
+  p.item_floats = L.item_floats;
+  p.target_items = c->target_items;
+  p.pool_blocks = L.pool_blocks;
+  p.block_bytes = L.block_bytes;
+  const float scale = c->cfg.scale == 0.0f ? 1.0f / sqrtf((float)L.d) : c->cfg.scale;
+  p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  return p;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DMS_OK : DMS_ERR_HIP; }
+
+int check_device(const dms_cache* c) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DMS_ERR_HIP;
+  return dev == c->device ? DMS_OK : DMS_ERR_STATE;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dms_workspace_bytes(const dms_config* cfg) {
+  if (!valid_config(cfg)) return 0;
+  dms::Layout L;
+  make_layout(cfg, L);
+  return (size_t)L.total;
+}
+
+int dms_cache_create(const dms_config* cfg, void* d_workspace, size_t workspace_bytes, void* stream,
+                     dms_cache** out) {
+  if (!out) return DMS_ERR_ARG;
+  *out = nullptr;
+  if (!valid_config(cfg) || !d_workspace) return DMS_ERR_ARG;
+  dms::Layout L;
+  make_layout(cfg, L);
+  if ((uintptr_t)d_workspace % kAlign != 0 || workspace_bytes < (size_t)L.total) return DMS_ERR_WORKSPACE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DMS_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DMS_ERR_HIP;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return DMS_ERR_DEVICE;
+  dms_cache* c = new dms_cache();
+  c->cfg = *cfg;
+  c->L = L;
+  c->ws = (uint8_t*)d_workspace;
+  c->device = dev;
+  c->num_cus = prop.multiProcessorCount;
+  // About two waves per SIMD of split-K work: enough memory-level
+  // parallelism for HBM while keeping partials and merges few.
+  c->target_items = std::max(64, c->num_cus * 8);
+  c->grid_waves = align_up(std::min<int64_t>(L.max_items, (int64_t)c->target_items + L.U) + 7, 32);
+  c->len.assign(L.B, 0);
+  const int st = hip_status(dms::launch_init(make_dev(c), (hipStream_t)stream));
+  if (st != DMS_OK) {
+    delete c;
+    return st;
+  }
+  *out = c;
+  return DMS_OK;
+}
+
+int dms_cache_destroy(dms_cache* c) {
+  delete c;
+  return DMS_OK;
+}
+
+int dms_cache_reset(dms_cache* c, void* stream) {
+  if (!c) return DMS_ERR_ARG;
+  int st = check_device(c);
+  if (st != DMS_OK) return st;
+  st = hip_status(dms::launch_init(make_dev(c), (hipStream_t)stream));
+  if (st == DMS_OK) std::fill(c->len.begin(), c->len.end(), 0);
+  return st;
+}
+
+int dms_prefill_compress(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit,
+                         const int32_t* h_lengths, int32_t max_len, void* stream) {
+  if (!c || !d_k || !d_v || !d_logit || !h_lengths || max_len < 1) return DMS_ERR_ARG;
+  int st = check_device(c);
+  if (st != DMS_OK) return st;
+  for (int32_t x : c->len)
+    if (x != 0) return DMS_ERR_STATE;
+  for (int b = 0; b < c->L.B; ++b) {
+    if (h_lengths[b] < 0 || h_lengths[b] > max_len) return DMS_ERR_ARG;
+    if (h_lengths[b] > c->L.max_tokens) return DMS_ERR_CAPACITY;
+  }
+  st = hip_status(dms::launch_prefill(make_dev(c), c->cfg.dtype, c->L.d, d_k, d_v, d_logit, h_lengths,
+                                      max_len, (hipStream_t)stream));
+  if (st == DMS_OK)
+    for (int b = 0; b < c->L.B; ++b) c->len[b] = h_lengths[b];
+  return st;
+}
+
+int dms_append_step(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit, void* stream) {
+  if (!c || !d_k || !d_v || !d_logit) return DMS_ERR_ARG;
+  int st = check_device(c);
+  if (st != DMS_OK) return st;
+  for (int32_t x : c->len)
+    if (x + 1 > c->L.max_tokens) return DMS_ERR_CAPACITY;
+  st = hip_status(dms::launch_append(make_dev(c), c->cfg.dtype, c->L.d, d_k, d_v, d_logit, (hipStream_t)stream));
+  if (st == DMS_OK)
+    for (auto& x : c->len) ++x;
+  return st;
+}
+
+int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stream) {
+  if (!c || !d_q || !d_out) return DMS_ERR_ARG;
+  int st = check_device(c);
+  if (st != DMS_OK) return st;
+  for (int32_t x : c->len)
+    if (x < 1) return DMS_ERR_STATE;
+  return hip_status(dms::launch_attention(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_out, c->grid_waves,
+                                          (hipStream_t)stream));
+}
+
+int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream) {
+  if (!c || !out) return DMS_ERR_ARG;
+  int st = check_device(c);
+  if (st != DMS_OK) return st;
+  const dms::Layout& L = c->L;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DMS_ERR_HIP;
+  dms::Counters ctr;
+  std::vector<int32_t> n(L.U), pos(L.U);
+  if (hipMemcpy(&ctr, c->ws + L.off_ctr, sizeof(ctr), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(n.data(), c->ws + L.off_n, (size_t)L.U * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(pos.data(), c->ws + L.off_pos, (size_t)L.U * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return DMS_ERR_HIP;
+  memset(out, 0, sizeof(*out));
+  for (int u = 0; u < L.U; ++u) {
+    out->live_tokens += n[u];
+    out->seen_tokens += pos[u];
+  }
+  out->allocated_blocks = (int64_t)std::min<unsigned long long>(ctr.bump, (unsigned long long)L.pool_blocks);
+  out->live_token_steps = (int64_t)ctr.live_token_steps;
+  out->sticky_error = ctr.sticky_error;
+  return DMS_OK;
+}
+
+int dms_cache_export(dms_cache* c, int32_t unit_begin, int32_t unit_count, int32_t* h_slot_pos, int32_t* h_ring,
+                     int32_t* h_n, void* stream) {
+  if (!c) return DMS_ERR_ARG;
+  const dms::Layout& L = c->L;
+  if (unit_begin < 0 || unit_count < 0 || (int64_t)unit_begin + unit_count > L.U) return DMS_ERR_ARG;
+  int st = check_device(c);
+  if (st != DMS_OK) return st;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DMS_ERR_HIP;
+  if (unit_count == 0) return DMS_OK;
+  std::vector<int32_t> n(unit_count);
+  if (hipMemcpy(n.data(), c->ws + L.off_n + (int64_t)unit_begin * 4, (size_t)unit_count * 4,
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return DMS_ERR_HIP;
+  if (h_n) memcpy(h_n, n.data(), (size_t)unit_count * 4);
+  if (h_ring) {
+    if (hipMemcpy(h_ring, c->ws + L.off_ring + (int64_t)unit_begin * L.R * 4, (size_t)unit_count * L.R * 4,
+                  hipMemcpyDeviceToHost) != hipSuccess)
+      return DMS_ERR_HIP;
+  }
+  if (h_slot_pos) {
+    // Gathered on the device into the attention-partials area (idle between
+    // calls on this stream), then copied out piece by piece.
+    const int64_t stage_words = L.max_items * L.item_floats;
+    const int64_t total = (int64_t)unit_count * L.max_tokens;
+    const dms::Dev p = make_dev(c);
+    for (int64_t f0 = 0; f0 < total; f0 += stage_words) {
+      const int64_t len = std::min(stage_words, total - f0);
+      if (dms::launch_export(p, unit_begin, f0, len, (int32_t*)p.part, (hipStream_t)stream) != hipSuccess)
+        return DMS_ERR_HIP;
+      if (hipMemcpyAsync(h_slot_pos + f0, p.part, (size_t)len * 4, hipMemcpyDeviceToHost, (hipStream_t)stream) !=
+              hipSuccess ||
+          hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+        return DMS_ERR_HIP;
+    }
+  }
+  return DMS_OK;
+}
+
+const char* dms_status_str(int status) {
+  switch (status) {
+    case DMS_OK: return "DMS_OK";
+    case DMS_ERR_ARG: return "DMS_ERR_ARG: invalid argument";
+    case DMS_ERR_WORKSPACE: return "DMS_ERR_WORKSPACE: workspace too small or misaligned";
+    case DMS_ERR_OUT_OF_BLOCKS: return "DMS_ERR_OUT_OF_BLOCKS: block pool exhausted";
+    case DMS_ERR_CAPACITY: return "DMS_ERR_CAPACITY: a sequence would exceed max_tokens";
+    case DMS_ERR_STATE: return "DMS_ERR_STATE: call not valid in the cache's current state";
+    case DMS_ERR_HIP: return "DMS_ERR_HIP: HIP runtime or launch failure";
+    case DMS_ERR_DEVICE: return "DMS_ERR_DEVICE: current device is not gfx950";
+    default: return "unknown dms status";
+  }
+}
+
+}  // extern "C"

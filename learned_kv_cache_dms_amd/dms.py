@@ -1,0 +1,242 @@
+"""Python binding of the DMS C ABI (include/dms.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+library ``libdms_hip.so``.  Importing this module fails loudly if that
+library has not been built; there is no fallback.
+
+The functions keep the C names.  ``Cache`` is a convenience wrapper that
+allocates the workspace with torch and passes ``data_ptr()`` values and the
+current HIP stream; torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdms_hip.so")
+
+DMS_F32 = 0
+DMS_BF16 = 1
+
+DMS_OK = 0
+DMS_ERR_ARG = -1
+DMS_ERR_WORKSPACE = -2
+DMS_ERR_OUT_OF_BLOCKS = -3
+DMS_ERR_CAPACITY = -4
+DMS_ERR_STATE = -5
+DMS_ERR_HIP = -6
+DMS_ERR_DEVICE = -7
+
+
+class DmsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {dms_status_str(status)} ({status})")
+
+
+class dms_config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32),
+        ("max_splits", ctypes.c_int32),
+        ("pool_blocks", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class dms_stats(ctypes.Structure):
+    _fields_ = [
+        ("live_tokens", ctypes.c_int64),
+        ("seen_tokens", ctypes.c_int64),
+        ("allocated_blocks", ctypes.c_int64),
+        ("live_token_steps", ctypes.c_int64),
+        ("sticky_error", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"DMS HIP library not found at {LIB_PATH}; build it with "
+            "`python -m learned_kv_cache_dms_amd.build` (needs ROCm hipcc).")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    P = ctypes.POINTER
+    sig = {
+        "dms_workspace_bytes": (sz, [P(dms_config)]),
+        "dms_cache_create": (ctypes.c_int, [P(dms_config), vp, sz, vp, P(vp)]),
+        "dms_cache_destroy": (ctypes.c_int, [vp]),
+        "dms_cache_reset": (ctypes.c_int, [vp, vp]),
+        "dms_prefill_compress": (ctypes.c_int, [vp, vp, vp, vp, P(i32), i32, vp]),
+        "dms_append_step": (ctypes.c_int, [vp, vp, vp, vp, vp]),
+        "dms_decode_attention": (ctypes.c_int, [vp, vp, vp, vp]),
+        "dms_cache_stats": (ctypes.c_int, [vp, P(dms_stats), vp]),
+        "dms_cache_export": (ctypes.c_int, [vp, i32, i32, P(i32), P(i32), P(i32), vp]),
+        "dms_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int, where: str):
+    if status != DMS_OK:
+        raise DmsError(status, where)
+
+
+def _i32p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.dtype == np.int32 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def make_config(batch, num_q_heads, num_kv_heads, head_dim, window, max_tokens, pool_blocks,
+                dtype=DMS_BF16, max_splits=0, scale=0.0, block_tokens=16) -> dms_config:
+    return dms_config(batch, num_q_heads, num_kv_heads, head_dim, window, block_tokens, max_tokens,
+                      max_splits, pool_blocks, dtype, scale)
+
+
+def dms_status_str(status: int) -> str:
+    return lib.dms_status_str(int(status)).decode()
+
+
+def dms_workspace_bytes(cfg: dms_config) -> int:
+    return int(lib.dms_workspace_bytes(ctypes.byref(cfg)))
+
+
+def dms_cache_create(cfg: dms_config, d_workspace: int, workspace_bytes: int, stream: int = 0) -> int:
+    h = ctypes.c_void_p()
+    _check(lib.dms_cache_create(ctypes.byref(cfg), d_workspace, workspace_bytes, stream, ctypes.byref(h)),
+           "dms_cache_create")
+    return h.value
+
+
+def dms_cache_destroy(h: int):
+    _check(lib.dms_cache_destroy(h), "dms_cache_destroy")
+
+
+def dms_cache_reset(h: int, stream: int = 0):
+    _check(lib.dms_cache_reset(h, stream), "dms_cache_reset")
+
+
+def dms_prefill_compress(h: int, d_k: int, d_v: int, d_logit: int, lengths: Sequence[int], max_len: int,
+                         stream: int = 0):
+    L = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+    _check(lib.dms_prefill_compress(h, d_k, d_v, d_logit, _i32p(L), int(max_len), stream),
+           "dms_prefill_compress")
+
+
+def dms_append_step(h: int, d_k: int, d_v: int, d_logit: int, stream: int = 0):
+    _check(lib.dms_append_step(h, d_k, d_v, d_logit, stream), "dms_append_step")
+
+
+def dms_decode_attention(h: int, d_q: int, d_out: int, stream: int = 0):
+    _check(lib.dms_decode_attention(h, d_q, d_out, stream), "dms_decode_attention")
+
+
+def dms_cache_stats(h: int, stream: int = 0) -> dict:
+    s = dms_stats()
+    _check(lib.dms_cache_stats(h, ctypes.byref(s), stream), "dms_cache_stats")
+    return {k: getattr(s, k) for k, _ in dms_stats._fields_ if k != "reserved"}
+
+
+def dms_cache_export(h: int, unit_begin: int, unit_count: int, slot_pos: Optional[np.ndarray],
+                     ring: Optional[np.ndarray], n: Optional[np.ndarray], stream: int = 0):
+    _check(lib.dms_cache_export(h, unit_begin, unit_count, _i32p(slot_pos), _i32p(ring), _i32p(n), stream),
+           "dms_cache_export")
+
+
+class Cache:
+    """A DMS cache whose workspace is a torch uint8 tensor on the current
+    device.  Tensors passed in must be contiguous, on that device, with the
+    shapes and dtypes of include/dms.h; they are checked here and handed to
+    the library by pointer."""
+
+    def __init__(self, batch, num_q_heads, num_kv_heads, head_dim, window, max_tokens, pool_blocks,
+                 dtype="bf16", max_splits=0, scale=0.0):
+        import torch
+        self._torch = torch
+        self.dtype = dtype
+        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.cfg = make_config(batch, num_q_heads, num_kv_heads, head_dim, window, max_tokens, pool_blocks,
+                               DMS_BF16 if dtype == "bf16" else DMS_F32, max_splits, scale)
+        self.B, self.Hq, self.Hkv, self.d = batch, num_q_heads, num_kv_heads, head_dim
+        self.window, self.max_tokens = window, max_tokens
+        self.ring_size = min(window, max_tokens) + 1
+        nbytes = dms_workspace_bytes(self.cfg)
+        if nbytes == 0:
+            raise DmsError(DMS_ERR_ARG, "dms_workspace_bytes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.handle = dms_cache_create(self.cfg, self.workspace.data_ptr(), nbytes, self._stream())
+
+    def _stream(self) -> int:
+        return self._torch.cuda.current_stream().cuda_stream
+
+    def _chk(self, t, shape, dtype, name):
+        if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on the GPU, got "
+                             f"{t.dtype} {tuple(t.shape)} on {t.device}")
+        return t.data_ptr()
+
+    def prefill(self, k, v, logit, lengths):
+        max_len = k.shape[2]
+        pk = self._chk(k, (self.B, self.Hkv, max_len, self.d), self.tdtype, "k")
+        pv = self._chk(v, (self.B, self.Hkv, max_len, self.d), self.tdtype, "v")
+        pl = self._chk(logit, (self.B, self.Hkv, max_len), self._torch.float32, "logit")
+        dms_prefill_compress(self.handle, pk, pv, pl, lengths, max_len, self._stream())
+
+    def append(self, k, v, logit):
+        pk = self._chk(k, (self.B, self.Hkv, self.d), self.tdtype, "k")
+        pv = self._chk(v, (self.B, self.Hkv, self.d), self.tdtype, "v")
+        pl = self._chk(logit, (self.B, self.Hkv), self._torch.float32, "logit")
+        dms_append_step(self.handle, pk, pv, pl, self._stream())
+
+    def attend(self, q, out=None):
+        pq = self._chk(q, (self.B, self.Hq, self.d), self.tdtype, "q")
+        if out is None:
+            out = self._torch.empty((self.B, self.Hq, self.d), dtype=self._torch.float32, device=q.device)
+        po = self._chk(out, (self.B, self.Hq, self.d), self._torch.float32, "out")
+        dms_decode_attention(self.handle, pq, po, self._stream())
+        return out
+
+    def stats(self) -> dict:
+        return dms_cache_stats(self.handle, self._stream())
+
+    def export(self, unit_begin=0, unit_count=None):
+        if unit_count is None:
+            unit_count = self.B * self.Hkv - unit_begin
+        slot_pos = np.empty((unit_count, self.max_tokens), dtype=np.int32)
+        ring = np.empty((unit_count, self.ring_size), dtype=np.int32)
+        n = np.empty(unit_count, dtype=np.int32)
+        dms_cache_export(self.handle, unit_begin, unit_count, slot_pos, ring, n, self._stream())
+        return slot_pos, ring, n
+
+    def reset(self):
+        dms_cache_reset(self.handle, self._stream())
+
+    def close(self):
+        if getattr(self, "handle", None):
+            dms_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

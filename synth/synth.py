@@ -101,12 +101,19 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(round_bf16_bits(x))
 
 
+def _heads(heads) -> np.ndarray:
+    """An int means heads 0..heads-1; a sequence lists head indices."""
+    if np.ndim(heads) == 0:
+        return np.arange(int(heads), dtype=np.int64)
+    return np.asarray(heads, dtype=np.int64)
+
+
 def _grid(layer, b_list, heads, positions, channels):
     """Counter values for the tensor [len(b_list), heads, len(positions), channels]
     where ``positions`` may be a 1-D array shared by all b or a 2-D array
     [len(b_list), P] of per-sequence positions."""
     b = np.asarray(b_list, dtype=np.int64).reshape(-1, 1, 1, 1)
-    h = np.arange(heads, dtype=np.int64).reshape(1, -1, 1, 1)
+    h = _heads(heads).reshape(1, -1, 1, 1)
     pos = np.asarray(positions, dtype=np.int64)
     if pos.ndim == 1:
         pos = pos.reshape(1, 1, -1, 1)
@@ -118,7 +125,8 @@ def _grid(layer, b_list, heads, positions, channels):
 
 def tensor(seed: int, stream: int, layer: int, b_list, heads: int, positions, channels: int,
            dtype: str = "f32") -> np.ndarray:
-    """Values for [B', heads, P, channels] (float32; bf16-rounded if dtype == 'bf16')."""
+    """Values for [B', heads, P, channels] (float32; bf16-rounded if dtype == 'bf16').
+    ``heads`` is a count or a list of head indices."""
     x = normal_from_index(seed, stream, _grid(layer, b_list, heads, positions, channels))
     if dtype == "bf16":
         return round_bf16(x)
@@ -131,12 +139,20 @@ def logits(seed: int, layer: int, b_list, heads: int, positions, mu_before, mu_a
            pos_threshold: int = MAX_POS) -> np.ndarray:
     """Eviction logits [B', heads, P] = float32(mu + x).
 
-    ``mu_before`` / ``mu_after`` are per-head means (scalars broadcast) used for
-    positions below / at-or-above ``pos_threshold``.
+    ``heads`` is a count or a list of head indices.  ``mu_before`` /
+    ``mu_after`` are per-head means (a scalar or one value per head of the
+    full head range) used for positions below / at-or-above ``pos_threshold``.
     """
-    mu_before = np.broadcast_to(np.asarray(mu_before, dtype=np.float64), (heads,))
-    mu_after = mu_before if mu_after is None else np.broadcast_to(
-        np.asarray(mu_after, dtype=np.float64), (heads,))
+    hl = _heads(heads)
+    mu_before = np.asarray(mu_before, dtype=np.float64)
+    mu_before = mu_before[hl] if mu_before.ndim == 1 and mu_before.size > 1 else \
+        np.broadcast_to(mu_before.reshape(-1)[:1] if mu_before.ndim else mu_before, (len(hl),))
+    if mu_after is None:
+        mu_after = mu_before
+    else:
+        mu_after = np.asarray(mu_after, dtype=np.float64)
+        mu_after = mu_after[hl] if mu_after.ndim == 1 and mu_after.size > 1 else \
+            np.broadcast_to(mu_after.reshape(-1)[:1] if mu_after.ndim else mu_after, (len(hl),))
     idx = _grid(layer, b_list, heads, positions, 1)[..., 0]
     x = normal_from_index(seed, STREAM_LOGIT, idx).astype(np.float64)
     pos = np.asarray(positions, dtype=np.int64)

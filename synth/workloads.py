@@ -73,6 +73,18 @@ class Workload:
         pa = 1.0 - nd.cdf(-after) if np.isfinite(after) else 0.0
         return np.where(np.asarray(pos) < self.pos_threshold, pb, pa)
 
+    def pool_blocks(self, layer: int = 0, slack: float = 1.2) -> int:
+        """Pool size for one layer: expected live tokens at the last decode
+        position of every sequence, times `slack`, in 16-token blocks, plus
+        one partly filled block per (sequence, KV head)."""
+        total = 0
+        for P in np.unique(self.prompt_lengths()):
+            count = int(np.sum(self.prompt_lengths() == P))
+            q = int(P) + self.decode_steps - 1
+            per_unit = int(np.ceil(slack * self.expected_live(layer, q) / 16.0)) + 2
+            total += per_unit * count * self.num_kv_heads
+        return total
+
     def expected_live(self, layer: int, q: int) -> float:
         """E|Vis(q)| under independent marks: unmarked tokens plus the window."""
         pos = np.arange(q + 1)
