@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the DMS decode hot path on one MI355X.
+
+One step = one decode step of every sequence of the workload through the C
+ABI: dms_append_step (decide, retire, store) then dms_decode_attention
+(split-K attention over the visible tokens, merge in the same launch).
+Inputs are synthetic, generated in HBM before the timed region.  The default
+workload is the Qwen-R1-32B-shaped layer: 64 chains at 32768 tokens, 40 query
+/ 8 KV heads, head_dim 128, bf16, w = 256, logit mean for CR 4 below position
+10240 and CR 12 beyond (overall about 8).
+
+Prints one JSON line.  `value` is decode-attention tokens per second (batch
+sequences per step); the live-KV bandwidth of the attention launch is in
+`roofline`.  `cpu_baseline` times the CPU oracle on a bounded sample of the
+same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --calib-copy-bytes N    # plain copy kernel, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attention tokens/sec + live-KV HBM GB/s (% of peak) at CR=8, 32K ctx"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "learned_kv_cache_dms_amd", "csrc", "dms_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or was taken on another version of the kernels."""
+    path = os.path.join(ROOT, "profiles", f"attention_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def calib_copy(nbytes: int):
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": nbytes, "launches": 5}), flush=True)
+
+
+def cpu_baseline(wl, steps_per_unit: int, n_units: int):
+    """The oracle, as it is, on a sample of the workload's (sequence, KV head)
+    units: `steps_per_unit` decode steps each at full context.  Input
+    generation is outside the timed part."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import dms_oracle as O
+    from synth import synth
+
+    rng = np.random.default_rng(wl.seed + 17)
+    U = wl.batch * wl.num_kv_heads
+    units = sorted(rng.choice(U, size=min(n_units, U), replace=False).tolist())
+    lengths = wl.prompt_lengths()
+    G = wl.group
+    elapsed = 0.0
+    for u in units:
+        b, h = divmod(u, wl.num_kv_heads)
+        P = int(lengths[b])
+        pos = np.arange(P + steps_per_unit)
+        K = synth.tensor(wl.seed, synth.STREAM_K, 0, [b], [h], pos, wl.head_dim, wl.dtype)[0, 0]
+        V = synth.tensor(wl.seed, synth.STREAM_V, 0, [b], [h], pos, wl.head_dim, wl.dtype)[0, 0]
+        lg = synth.logits(wl.seed, 0, [b], [h], pos, *wl.layer_mu(0), wl.pos_threshold)[0, 0]
+        Q = synth.tensor(wl.seed, synth.STREAM_Q, 0, [b], list(range(h * G, (h + 1) * G)),
+                         np.arange(P, P + steps_per_unit), wl.head_dim, wl.dtype)[0].transpose(1, 0, 2)
+        t0 = time.perf_counter()
+        O.decode_unit(Q, K, V, lg, P, steps_per_unit, wl.window, O.default_scale(wl.head_dim))
+        elapsed += time.perf_counter() - t0
+    per_unit_step = elapsed / (len(units) * steps_per_unit)
+    step_s = per_unit_step * U                      # a full decode step of the workload
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": wl.batch / step_s,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(units)} of {U} (sequence, KV head) units x {steps_per_unit} decode steps at full "
+                  f"context ({elapsed:.1f} s of oracle time), scaled to all units",
+        "seconds_per_step": step_s,
+        "host_cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="qwen-r1-32b-layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=16)
+    ap.add_argument("--cpu-steps", type=int, default=192)
+    ap.add_argument("--calib-copy-bytes", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the DMS decode path on one GPU only; "
+              f"--gpus {args.gpus} (WORLD_SIZE {world}) is not supported.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+    if args.calib_copy_bytes:
+        calib_copy(args.calib_copy_bytes)
+        return
+
+    from learned_kv_cache_dms_amd import dms
+    from synth import device as dsynth
+    from synth import synth, workloads
+
+    wl0 = workloads.ALL[args.workload]()
+    if wl0.num_layers != 1:
+        raise SystemExit("bench.py times one layer; choose a single-layer workload")
+    W, K = args.warmup, args.steps
+    wl = dataclasses.replace(wl0, decode_steps=W + K)
+    B, Hq, Hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    esize = 2 if wl.dtype == "bf16" else 4
+    lengths = wl.prompt_lengths()
+
+    cache = dms.Cache(B, Hq, Hkv, d, wl.window, wl.max_tokens(), wl.pool_blocks(0), dtype=wl.dtype)
+    print(f"# workload {wl.name}: prompt {int(lengths.max())}, {W}+{K} steps, pool {wl.pool_blocks(0)} blocks",
+          file=sys.stderr, flush=True)
+    max_len = int(lengths.max())
+    Kd = torch.empty((B, Hkv, max_len, d), dtype=tdt, device="cuda")
+    Vd = torch.empty_like(Kd)
+    Ld = torch.empty((B, Hkv, max_len), dtype=torch.float32, device="cuda")
+    mb, ma = wl.layer_mu(0)
+    dsynth.fill(Kd, wl.seed, synth.STREAM_K, 0, 0)
+    dsynth.fill(Vd, wl.seed, synth.STREAM_V, 0, 0)
+    dsynth.logits(Ld, wl.seed, 0, 0, mb, ma, wl.pos_threshold)
+    cache.prefill(Kd, Vd, Ld, lengths)
+    torch.cuda.synchronize()
+    del Kd, Vd, Ld
+    torch.cuda.empty_cache()
+
+    S = W + K
+    qs = torch.empty((S, B, Hq, d), dtype=tdt, device="cuda")
+    ks = torch.empty((S, B, Hkv, d), dtype=tdt, device="cuda")
+    vs = torch.empty_like(ks)
+    lgs = torch.empty((S, B, Hkv), dtype=torch.float32, device="cuda")
+    base = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    for t in range(S):
+        pb = base + t
+        dsynth.fill(qs[t], wl.seed, synth.STREAM_Q, 0, 0, pos_base=pb)
+        dsynth.fill(ks[t], wl.seed, synth.STREAM_K, 0, 0, pos_base=pb)
+        dsynth.fill(vs[t], wl.seed, synth.STREAM_V, 0, 0, pos_base=pb)
+        dsynth.logits(lgs[t], wl.seed, 0, 0, mb, ma, wl.pos_threshold, pos_base=pb)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    for t in range(W):
+        cache.append(ks[t], vs[t], lgs[t])
+        cache.attend(qs[t], out)
+    st0 = cache.stats()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        t = W + i
+        cache.append(ks[t], vs[t], lgs[t])
+        ev[i][0].record()
+        cache.attend(qs[t], out)
+        ev[i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st1 = cache.stats()
+    if st1["sticky_error"] != 0:
+        raise SystemExit(f"device error during the run: {st1}")
+
+    total_ms = start.elapsed_time(end)
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_avg_s = sum(attn_ms) / K / 1e3
+    live_tokens = (st1["live_token_steps"] - st0["live_token_steps"]) / K   # per step, all units
+    live_bytes = live_tokens * 2 * d * esize
+    step_s = total_ms / K / 1e3
+    tokens_per_s = B / step_s
+    achieved = live_bytes / attn_avg_s / 1e9
+    traffic = measured_traffic(wl.name)
+    seen = st1["seen_tokens"] / (B * Hkv)
+
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(total_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+            "context": int(lengths.max()), "window": wl.window, "block_tokens": 16,
+            "decode_steps": S, "logit_mean": [round(mb, 4), round(ma, 4)], "logit_mean_switch": wl.pos_threshold,
+        },
+        "live_kv_gbps": round(achieved, 1),
+        "live_kv_gbps_per_step": round(live_bytes / step_s / 1e9, 1),
+        "pct_peak_hbm": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "attention_ms": round(attn_avg_s * 1e3, 5),
+        "live_tokens_per_step": round(live_tokens, 1),
+        "realized_cr": round(seen * B * Hkv / st1["live_tokens"], 3),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "kernel": "attention_kernel<2,128>" if (esize == 2 and d == 128) else "attention_kernel",
+            "algorithmic_bytes_per_launch": round(live_bytes),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps, args.cpu_units)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,6 +51,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#if defined(__GNUC__) || defined(__clang__)
+#define DMS_API __attribute__((visibility("default")))
+#else
+#define DMS_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -100,20 +106,20 @@ typedef struct {
    dms_cache_destroy.  The size grows with pool_blocks (one block is
    2*16*d*sizeof(dtype) bytes of K/V plus 68 bytes of metadata) and with
    B*Hkv*(max_tokens/16 + window + 6) 32-bit words of per-head state. */
-size_t dms_workspace_bytes(const dms_config* cfg);
+DMS_API size_t dms_workspace_bytes(const dms_config* cfg);
 
 /* Creates a handle over d_workspace and enqueues its initialisation (empty
    cache) on `stream`.  The current HIP device must be a gfx950 and must stay
    current for every later call on the handle.  *out receives the handle. */
-int dms_cache_create(const dms_config* cfg, void* d_workspace, size_t workspace_bytes,
+DMS_API int dms_cache_create(const dms_config* cfg, void* d_workspace, size_t workspace_bytes,
                      void* stream, dms_cache** out);
 
 /* Frees the host handle only; the workspace stays the caller's.  NULL is a no-op. */
-int dms_cache_destroy(dms_cache* c);
+DMS_API int dms_cache_destroy(dms_cache* c);
 
 /* Async.  Empties the cache (all sequences back to length 0, pool released,
    sticky error cleared). */
-int dms_cache_reset(dms_cache* c, void* stream);
+DMS_API int dms_cache_reset(dms_cache* c, void* stream);
 
 /* Async.  Compresses a prompt into an empty cache: for every (b, h), the
    tokens of positions 0 .. len_b - 1 that are visible to the query at
@@ -125,7 +131,7 @@ int dms_cache_reset(dms_cache* c, void* stream);
      h_lengths: [B] host array, 0 <= len_b <= min(max_len, max_tokens)
    Errors: DMS_ERR_STATE if any sequence is non-empty, DMS_ERR_CAPACITY if a
    length exceeds max_tokens, DMS_ERR_ARG for other bad arguments. */
-int dms_prefill_compress(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit,
+DMS_API int dms_prefill_compress(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit,
                          const int32_t* h_lengths, int32_t max_len, void* stream);
 
 /* Async.  Appends one token to every sequence b at position q_b = len_b:
@@ -134,7 +140,7 @@ int dms_prefill_compress(dms_cache* c, const void* d_k, const void* d_v, const f
      d_k, d_v : [B, Hkv, d] of dtype
      d_logit  : [B, Hkv] fp32
    Errors: DMS_ERR_CAPACITY if some len_b + 1 > max_tokens. */
-int dms_append_step(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit,
+DMS_API int dms_append_step(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit,
                     void* stream);
 
 /* Async.  Grouped-query decode attention of the query at each sequence's
@@ -144,10 +150,10 @@ int dms_append_step(dms_cache* c, const void* d_k, const void* d_v, const float*
      d_q  : [B, Hq, d] of dtype
      d_out: [B, Hq, d] fp32
    Errors: DMS_ERR_STATE if some sequence has no token yet. */
-int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stream);
+DMS_API int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stream);
 
 /* Synchronises `stream`, then fills *out. */
-int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream);
+DMS_API int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream);
 
 /* Synchronises `stream`, then copies the logical state of the units
    u = unit_begin .. unit_begin + unit_count - 1, where u = b * Hkv + h:
@@ -159,11 +165,11 @@ int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream);
      h_n       : [unit_count]  slots in use (visible tokens)
    Any of the three may be NULL to skip it.  For tests and checkpoints; not
    on the hot path. */
-int dms_cache_export(dms_cache* c, int32_t unit_begin, int32_t unit_count, int32_t* h_slot_pos,
+DMS_API int dms_cache_export(dms_cache* c, int32_t unit_begin, int32_t unit_count, int32_t* h_slot_pos,
                      int32_t* h_ring, int32_t* h_n, void* stream);
 
 /* Static string naming a status code. */
-const char* dms_status_str(int status);
+DMS_API const char* dms_status_str(int status);
 
 #ifdef __cplusplus
 }

@@ -33,6 +33,8 @@ COMMON = [
     # packed-FP32 VALU forms are kept out of every code object
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # only the C ABI is exported; internal C++ symbols stay private
+    "-fvisibility=hidden",
 ]
 
 

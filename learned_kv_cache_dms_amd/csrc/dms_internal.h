@@ -9,7 +9,8 @@ namespace dms {
 
 constexpr int kBlockTokens = 16;
 constexpr int kMaxGroup = 16;      // query heads per KV head held by one MFMA tile
-constexpr int kWavesPerWG = 4;     // attention / append work-group = 4 independent waves
+constexpr int kMaxItemBlocks = 512;  // blocks per attention work item (128 per wave)
+constexpr int kWavesPerWG = 4;     // waves per work-group (attention work item, append, reduce)
 
 // Device-side counters (one 64-byte line).
 struct Counters {
@@ -28,7 +29,7 @@ struct Layout {
   int64_t pool_blocks, block_bytes;
   int32_t item_floats;  // floats per attention partial: m[16], l[16], o[G][d]
   int64_t max_items;    // partial slots = U * max_splits
-  int64_t off_pool, off_btab, off_blkpos, off_blkmask, off_ring, off_n, off_pos, off_arrive,
+  int64_t off_pool, off_btab, off_blkpos, off_blkmask, off_ring, off_n, off_pos, off_plan,
       off_ctr, off_part, total;
 };
 
@@ -42,7 +43,7 @@ struct Dev {
   int32_t* ring;       // [U][R] slot of a pending marked token, or -1
   int32_t* n;          // [U] slots in use
   int32_t* pos;        // [U] tokens appended so far (next position)
-  int32_t* arrive;     // [U] attention work items finished in the current call
+  int32_t* plan;       // [U][2] first work item and item count of the last attention call
   Counters* ctr;
   float* part;         // [max_items][item_floats] attention partials
   int32_t B, Hq, Hkv, G, R, max_tokens, max_blocks, max_splits, U, item_floats, target_items;
@@ -66,6 +67,6 @@ hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const v
                           const float* logit, const int32_t* h_lengths, int32_t max_len, hipStream_t s);
 hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s);
 hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out,
-                            int64_t grid_waves, hipStream_t s);
+                            int64_t grid_wgs, hipStream_t s);
 
 }  // namespace dms

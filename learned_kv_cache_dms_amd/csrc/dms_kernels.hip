@@ -24,22 +24,39 @@
 //         at byte jj*8 + e*sizeof(T)  (NJ = 2 for bf16, 1 for fp32)
 //   * Per block: 16 slot positions and a 16-bit live mask.
 //
-// Decode attention per (unit, block range) work item, one wave each:
+// Decode attention per (unit, block range) work item, one work-group of four
+// waves each (waves take every fourth block and merge through LDS):
 //   S[t][g]  = K_blk[t] . Q[g]     MFMA, A = K fragment, B = Q fragment
 //   online softmax on S in the MFMA output layout (lane l holds tokens
 //            4*(l/16)+r of head l % 16), exp2 domain
 //   O^T[c][g] += V^T[c][t] P[t][g]  MFMA, A = V fragment, B = P taken in
 //            place from the S registers (bf16: P split into hi + lo parts)
-// The last wave of a unit to finish merges the partials (log-sum-exp).
+// A unit whose blocks were split over several work items gets its partials
+// merged by reduce_kernel in a second launch (log-sum-exp).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <tuple>
+#include <utility>
 
 #include "dms_internal.h"
 
 namespace dms {
+
+// Launches `kernel` and returns the status of this launch alone (a stale
+// error left in the thread by an unrelated earlier HIP call is not reported).
+template <typename... KArgs, typename... Args>
+static hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Args&&... args) {
+  auto tup = [](auto&&... a) { return std::tuple<KArgs...>(a...); }(std::forward<Args>(args)...);
+  void* ptrs[sizeof...(KArgs)];
+  std::apply([&](auto&... a) {
+    int i = 0;
+    ((ptrs[i++] = (void*)&a), ...);
+  }, tup);
+  return hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, s);
+}
 
 typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -98,7 +115,8 @@ __global__ void init_kernel(Dev p) {
   for (int64_t i = tid; i < p.U; i += stride) {
     p.n[i] = 0;
     p.pos[i] = 0;
-    p.arrive[i] = 0;
+    p.plan[2 * i] = 0;
+    p.plan[2 * i + 1] = 0;
   }
   if (tid == 0) {
     p.ctr->bump = 0;
@@ -403,50 +421,52 @@ struct Item {
 };
 
 // Work plan, computed redundantly by every wave from the live counts n[]:
-// C = ceil(total blocks / target) blocks per item, unit u gets
-// min(max_splits, ceil(nblk_u / C)) items holding equal shares of its
-// blocks, items are numbered unit-major.  Returns false if `item` >= total.
-__device__ __forceinline__ int plan_total(const Dev& p, int lane, int& C) {
-  int tot = 0;
+// unit u (nblk_u blocks) gets items_u = round(nblk_u * target / total blocks)
+// work items, at least ceil(nblk_u / kMaxItemBlocks) and at most max_splits
+// (which the host keeps >= ceil(max_blocks / kMaxItemBlocks)); each item
+// holds an equal share of the unit's blocks, so the items of a launch have
+// about the same size.  Items are numbered unit-major.
+__device__ __forceinline__ int unit_items(int nb, long long tot, int target, int max_splits) {
+  if (nb <= 0) return 0;
+  const long long want = ((long long)nb * target * 2 + tot) / (2 * tot);  // round(nb * target / tot)
+  const int lo = (nb + kMaxItemBlocks - 1) / kMaxItemBlocks;
+  return (int)min((long long)max_splits, max((long long)lo, want));
+}
+
+__device__ __forceinline__ long long plan_blocks(const Dev& p, int lane) {
+  long long tot = 0;
   for (int b0 = 0; b0 < p.U; b0 += 64) {
     const int uu = b0 + lane;
     if (uu < p.U) tot += (p.n[uu] + 15) >> 4;
   }
-  tot = wave_sum_i(tot);
-  C = max(1, (tot + p.target_items - 1) / p.target_items);
-  int items = 0;
-  for (int b0 = 0; b0 < p.U; b0 += 64) {
-    const int uu = b0 + lane;
-    if (uu < p.U) {
-      const int nb = (p.n[uu] + 15) >> 4;
-      items += nb > 0 ? min(p.max_splits, (nb + C - 1) / C) : 0;
-    }
-  }
-  return wave_sum_i(items);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+  return max(1LL, tot);
 }
 
-__device__ __forceinline__ bool plan_find(const Dev& p, int lane, int C, int item, Item& it) {
+// Finds work item `item`; false when item >= the plan's total.
+__device__ __forceinline__ bool plan_find(const Dev& p, int lane, long long tot, int item, Item& it) {
   int running = 0;
-  for (int b0 = 0; b0 < p.U; b0 += 64) {
+  for (int b0 = 0; b0 < p.U && running <= item; b0 += 64) {
     const int uu = b0 + lane;
     int nb = 0, cnt = 0;
     if (uu < p.U) {
       nb = (p.n[uu] + 15) >> 4;
-      cnt = nb > 0 ? min(p.max_splits, (nb + C - 1) / C) : 0;
+      cnt = unit_items(nb, tot, p.target_items, p.max_splits);
     }
     const int incl = wave_incl_scan_i(cnt, lane);
     const int start = running + incl - cnt;
     const unsigned long long bal = __ballot(item >= start && item < start + cnt);
     if (bal) {
-      const int src = __ffsll((long long)bal) - 1;
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)bal) - 1);
       it.u = b0 + src;
-      it.base = __shfl(start, src);
-      it.items = __shfl(cnt, src);
-      it.nblk = __shfl(nb, src);
+      it.base = __builtin_amdgcn_readlane(start, src);
+      it.items = __builtin_amdgcn_readlane(cnt, src);
+      it.nblk = __builtin_amdgcn_readlane(nb, src);
       it.k = item - it.base;
       return true;
     }
-    running += __shfl(incl, 63);
+    running += __builtin_amdgcn_readlane(incl, 63);
   }
   return false;
 }
@@ -535,24 +555,30 @@ __device__ __forceinline__ void attend_block(const Frag<ES, D>& f, const u32x4 (
   }
 }
 
+// Split-K decode attention.  One work-group (4 waves) per work item = a
+// chunk of one (sequence, KV head)'s blocks; wave w takes the chunk's blocks
+// w, w+4, w+8, ... so the work-group streams one contiguous run.  The waves'
+// softmax states are merged through LDS; a unit held by a single work item
+// writes its output here, otherwise the merged partial goes to reduce_kernel.
 template <int ES, int D>
-__global__ __launch_bounds__(256) void attention_kernel(Dev p, const uint8_t* __restrict__ q,
-                                                        float* __restrict__ out) {
+__global__ __launch_bounds__(256) void attention_kernel(Dev p, const int32_t* __restrict__ btab,
+                                                        const uint32_t* __restrict__ bmask,
+                                                        const uint8_t* __restrict__ q, float* __restrict__ out) {
   using G = Geo<ES, D>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kW = kWavesPerWG;
+  constexpr int kTilesPerWave = (G::kTiles + kW - 1) / kW;
+  __shared__ f32x4 s_o[kW][G::kTiles][64];
+  __shared__ float s_m[kW][16], s_l[kW][16];
 
-  int C;
-  const int T = plan_total(p, lane, C);
-  // XCD-aware numbering: work-group wg runs on XCD wg % 8; XCD x takes the
-  // contiguous item range [x*T/8, (x+1)*T/8) so a unit's items share an L2.
-  const int nwg = gridDim.x, wg = blockIdx.x;
-  const int x = wg & 7, rr = wg >> 3;
-  const int lo = (int)(((long long)x * T) >> 3), hi = (int)(((long long)(x + 1) * T) >> 3);
-  const int item = lo + rr * kWavesPerWG + wave;
-  (void)nwg;
-  if (item >= hi) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // Work item = work-group id.  Consecutive ids are consecutive units, and
+  // the dispatcher deals work-groups round-robin over the XCDs, so every XCD
+  // gets an even share of units.
+  const long long tot = plan_blocks(p, lane);
   Item it;
-  if (!plan_find(p, lane, C, item, it)) return;
+  if (!plan_find(p, lane, tot, (int)blockIdx.x, it)) return;  // uniform over the work-group
 
   const int u = it.u;
   const int b = u / p.Hkv, h = u - b * p.Hkv;
@@ -574,7 +600,8 @@ __global__ __launch_bounds__(256) void attention_kernel(Dev p, const uint8_t* __
 
   const int jb = (int)(((long long)it.k * it.nblk) / it.items);
   const int je = (int)(((long long)(it.k + 1) * it.nblk) / it.items);
-  const int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
+  // this wave's blocks: jb + wave + kW * i, i < cnt
+  const int cnt = max(0, (je - jb - wave + kW - 1) / kW);
 
   Acc<D> acc;
 #pragma unroll
@@ -582,102 +609,145 @@ __global__ __launch_bounds__(256) void attention_kernel(Dev p, const uint8_t* __
   acc.m = -INFINITY;
   acc.l = 0.f;
 
-  // block ids and masks, 64 at a time in lane-vector registers
-  int win = jb;
-  int idv = (jb + lane < je) ? bt[jb + lane] : 0;
-  uint32_t mkv = (jb + lane < je) ? p.blk_mask[idv] : 0u;
-  auto blk_of = [&](int J, int& blk, uint32_t& msk) {
-    if (J - win >= 64) {
-      win += 64;
-      idv = (win + lane < je) ? bt[win + lane] : 0;
-      mkv = (win + lane < je) ? p.blk_mask[idv] : 0u;
+  if (cnt > 0) {
+    // This wave's block ids and live masks (at most 2 x 64, the plan keeps
+    // items within kMaxItemBlocks) are loaded once into lane vectors and read
+    // with readlane, so the K/V pipeline never waits on a dependent load.
+    const int32_t* bt = btab + (int64_t)u * p.max_blocks + jb + wave;
+    int id0 = 0, id1 = 0;
+    uint32_t mk0 = 0u, mk1 = 0u;
+    if (lane < cnt) id0 = bt[(int64_t)lane * kW];
+    if (lane + 64 < cnt) id1 = bt[(int64_t)(lane + 64) * kW];
+    if (lane < cnt) mk0 = bmask[id0];
+    if (lane + 64 < cnt) mk1 = bmask[id1];
+    const float sl2e = p.scale_log2e;
+    const uint8_t* pool = p.pool;
+    const int64_t BB = p.block_bytes;
+    // Three-block rotation: two blocks load while one is computed.  Loads
+    // are unconditional (indices past the end are clamped to the last block,
+    // just read) so the load counter analysis stays exact in the loop.
+    Frag<ES, D> f0, f1, f2;
+    uint32_t m0, m1, m2;
+    const int last = cnt - 1;
+    auto fetch = [&](Frag<ES, D>& f, uint32_t& m, int i) {
+      const int ic = min(i, last);
+      const int blk = ic < 64 ? __builtin_amdgcn_readlane(id0, ic) : __builtin_amdgcn_readlane(id1, ic - 64);
+      const uint32_t mm = (uint32_t)(ic < 64 ? __builtin_amdgcn_readlane((int)mk0, ic)
+                                             : __builtin_amdgcn_readlane((int)mk1, ic - 64));
+      m = i <= last ? mm : 0u;
+      load_frag<ES, D>(f, pool + (int64_t)blk * BB, lane);
+    };
+    fetch(f0, m0, 0);
+    fetch(f1, m1, 1);
+    int i = 0;
+    for (; i + 2 < cnt; i += 3) {
+      fetch(f2, m2, i + 2);
+      attend_block<ES, D>(f0, qf, m0, lane, sl2e, acc);
+      fetch(f0, m0, i + 3);
+      attend_block<ES, D>(f1, qf, m1, lane, sl2e, acc);
+      fetch(f1, m1, i + 4);
+      attend_block<ES, D>(f2, qf, m2, lane, sl2e, acc);
     }
-    blk = __builtin_amdgcn_readlane(idv, J - win);
-    msk = (uint32_t)__builtin_amdgcn_readlane((int)mkv, J - win);
-  };
-
-  const float sl2e = p.scale_log2e;
-  Frag<ES, D> f0, f1, f2;
-  int bk0 = 0, bk1 = 0, bk2 = 0;
-  uint32_t m0 = 0, m1 = 0, m2 = 0;
-  blk_of(jb, bk0, m0);
-  load_frag<ES, D>(f0, p.pool + (int64_t)bk0 * p.block_bytes, lane);
-  if (jb + 1 < je) {
-    blk_of(jb + 1, bk1, m1);
-    load_frag<ES, D>(f1, p.pool + (int64_t)bk1 * p.block_bytes, lane);
-  }
-  for (int j = jb; j < je; j += 3) {
-    if (j + 2 < je) {
-      blk_of(j + 2, bk2, m2);
-      load_frag<ES, D>(f2, p.pool + (int64_t)bk2 * p.block_bytes, lane);
-    }
-    attend_block<ES, D>(f0, qf, m0, lane, sl2e, acc);
-    if (j + 1 >= je) break;
-    if (j + 3 < je) {
-      blk_of(j + 3, bk0, m0);
-      load_frag<ES, D>(f0, p.pool + (int64_t)bk0 * p.block_bytes, lane);
-    }
-    attend_block<ES, D>(f1, qf, m1, lane, sl2e, acc);
-    if (j + 2 >= je) break;
-    if (j + 4 < je) {
-      blk_of(j + 4, bk1, m1);
-      load_frag<ES, D>(f1, p.pool + (int64_t)bk1 * p.block_bytes, lane);
-    }
-    attend_block<ES, D>(f2, qf, m2, lane, sl2e, acc);
+    // 0, 1 or 2 blocks remain, already loaded in f0 and f1
+    if (i < cnt) attend_block<ES, D>(f0, qf, m0, lane, sl2e, acc);
+    if (i + 1 < cnt) attend_block<ES, D>(f1, qf, m1, lane, sl2e, acc);
   }
 
   // lane-local l holds 4 of the 16 tokens per block; add the four groups
   float lt = acc.l + __shfl_xor(acc.l, 16);
   lt = lt + __shfl_xor(lt, 32);
 
-  float* orow = out + ((int64_t)b * p.Hq + hq) * D + 4 * (lane >> 4);
+  // merge the waves' states through LDS; wave w finishes tiles w*TPW...
+  if (lane < 16) {
+    s_m[wave][lane] = acc.m;
+    s_l[wave][lane] = lt;
+  }
+#pragma unroll
+  for (int j = 0; j < G::kTiles; ++j) s_o[wave][j][lane] = acc.o[j];
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) M = fmaxf(M, s_m[w][g]);
+  const float Mr = (M == -INFINITY) ? 0.f : M;
+  float wt[kW];
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    wt[w] = exp2_fast(s_m[w][g] - Mr);
+    L += wt[w] * s_l[w][g];
+  }
+  const int j0 = wave * kTilesPerWave;
+  f32x4 O[kTilesPerWave];
+#pragma unroll
+  for (int t = 0; t < kTilesPerWave; ++t) {
+    O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (j0 + t < G::kTiles) {
+#pragma unroll
+      for (int w = 0; w < kW; ++w) O[t] += wt[w] * s_o[w][j0 + t][lane];
+    }
+  }
+  if (it.k == 0 && wave == 0 && lane == 0) {  // read by reduce_kernel, for every unit
+    p.plan[2 * u] = it.base;
+    p.plan[2 * u + 1] = it.items;
+  }
   if (it.items == 1) {
     if (gvalid) {
-      const float inv = 1.0f / lt;
+      float* orow = out + ((int64_t)b * p.Hq + hq) * D + 4 * (lane >> 4);
+      const float inv = 1.0f / L;
 #pragma unroll
-      for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(orow + 16 * j) = acc.o[j] * inv;
+      for (int t = 0; t < kTilesPerWave; ++t)
+        if (j0 + t < G::kTiles) *(f32x4*)(orow + 16 * (j0 + t)) = O[t] * inv;
     }
     return;
   }
-
-  // several items: publish the partial, the last one to arrive merges
+  // several items: publish the merged partial; reduce_kernel combines them
   const int IF = p.item_floats;
   float* mine = p.part + (int64_t)(it.base + it.k) * IF;
   if (gvalid) {
-    if (lane < 16) {
-      mine[g] = acc.m;
-      mine[16 + g] = lt;
+    if (wave == 0 && lane < 16) {
+      mine[g] = M;
+      mine[16 + g] = L;
     }
 #pragma unroll
-    for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(mine + 32 + g * D + 16 * j + 4 * (lane >> 4)) = acc.o[j];
+    for (int t = 0; t < kTilesPerWave; ++t)
+      if (j0 + t < G::kTiles) *(f32x4*)(mine + 32 + g * D + 16 * (j0 + t) + 4 * (lane >> 4)) = O[t];
   }
-  __threadfence();
-  int old = 0;
-  if (lane == 0) old = atomicAdd(&p.arrive[u], 1);
-  old = __shfl(old, 0);
-  if (old != it.items - 1) return;
-  __threadfence();
-  if (lane == 0) p.arrive[u] = 0;
-  if (!gvalid) return;
-  const float* pb = p.part + (int64_t)it.base * IF;
+}
+
+// Split reduce: one wave per (sequence, KV head) whose attention was split
+// into several work items; merges their (m, l, o) partials by log-sum-exp:
+//   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  o = sum_s 2^(m_s - M) o_s / L.
+// Lane l handles head l % 16 and the channels 16j + 4(l/16) + r.
+template <int D>
+__global__ __launch_bounds__(256) void reduce_kernel(Dev p, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int u = blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
+  if (u >= p.U) return;
+  const int n = p.n[u], base = p.plan[2 * u], items = p.plan[2 * u + 1];
+  if (n == 0) return;
+  const int g = lane & 15;
+  if (items <= 1 || g >= p.G) return;
+  const int b = u / p.Hkv, h = u - b * p.Hkv;
+  const int IF = p.item_floats;
+  const float* pb = p.part + (int64_t)base * IF;
   float M = -INFINITY;
-  for (int s = 0; s < it.items; ++s) M = fmaxf(M, pb[(int64_t)s * IF + g]);
+  for (int s = 0; s < items; ++s) M = fmaxf(M, pb[(int64_t)s * IF + g]);
   const float Mr = (M == -INFINITY) ? 0.f : M;
   float L = 0.f;
-  f32x4 O[G::kTiles];
+  f32x4 O[D / 16];
 #pragma unroll
-  for (int j = 0; j < G::kTiles; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < it.items; ++s) {
+  for (int j = 0; j < D / 16; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < items; ++s) {
     const float* ps = pb + (int64_t)s * IF;
     const float ws = exp2_fast(ps[g] - Mr);
     L += ws * ps[16 + g];
 #pragma unroll
-    for (int j = 0; j < G::kTiles; ++j)
-      O[j] += ws * *(const f32x4*)(ps + 32 + g * D + 16 * j + 4 * (lane >> 4));
+    for (int j = 0; j < D / 16; ++j) O[j] += ws * *(const f32x4*)(ps + 32 + g * D + 16 * j + 4 * (lane >> 4));
   }
   const float inv = 1.0f / L;
+  float* orow = out + ((int64_t)b * p.Hq + h * p.G + g) * D + 4 * (lane >> 4);
 #pragma unroll
-  for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(orow + 16 * j) = O[j] * inv;
+  for (int j = 0; j < D / 16; ++j) *(f32x4*)(orow + 16 * j) = O[j] * inv;
 }
 
 // ---------------------------------------------------------------------------
@@ -708,22 +778,19 @@ hipError_t launch_init(const Dev& p, hipStream_t s) {
   const int64_t work = std::max<int64_t>((int64_t)p.U * p.R, p.U);
   const int threads = 256;
   const int blocks = (int)std::min<int64_t>((work + threads - 1) / threads, 4096);
-  hipLaunchKernelGGL(init_kernel, dim3(std::max(blocks, 1)), dim3(threads), 0, s, p);
-  return hipGetLastError();
+  return launch(init_kernel, dim3(std::max(blocks, 1)), dim3(threads), s, p);
 }
 
 hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s) {
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((len + 255) / 256, 8192));
-  hipLaunchKernelGGL(export_kernel, dim3(blocks), dim3(256), 0, s, p, u0, f0, len, stage);
-  return hipGetLastError();
+  return launch(export_kernel, dim3(blocks), dim3(256), s, p, u0, f0, len, stage);
 }
 
 template <int ES, int D>
 static hipError_t append_t(const Dev& p, const void* k, const void* v, const float* logit, hipStream_t s) {
   const int blocks = (p.U + kWavesPerWG - 1) / kWavesPerWG;
-  hipLaunchKernelGGL((append_kernel<ES, D>), dim3(blocks), dim3(64 * kWavesPerWG), 0, s, p,
-                     (const uint8_t*)k, (const uint8_t*)v, logit);
-  return hipGetLastError();
+  return launch(append_kernel<ES, D>, dim3(blocks), dim3(64 * kWavesPerWG), s, p, (const uint8_t*)k,
+                (const uint8_t*)v, logit);
 }
 
 hipError_t launch_append(const Dev& p, int dtype, int d, const void* k, const void* v,
@@ -739,14 +806,12 @@ static hipError_t prefill_t(const Dev& p, const void* k, const void* v, const fl
     const int nb = std::min(PromptLens::kMax, p.B - b0);
     PromptLens lens;
     for (int i = 0; i < nb; ++i) lens.v[i] = h_lengths[b0 + i];
-    hipLaunchKernelGGL(prefill_scan_kernel, dim3(nb * p.Hkv), dim3(1024), 0, s, p, logit, max_len, b0, lens);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = launch(prefill_scan_kernel, dim3(nb * p.Hkv), dim3(1024), s, p, logit, max_len, b0, lens);
     if (e != hipSuccess) return e;
   }
   const int ysplit = 8;
-  hipLaunchKernelGGL((prefill_scatter_kernel<ES, D>), dim3(p.U, ysplit), dim3(64 * kWavesPerWG), 0, s, p,
-                     (const uint8_t*)k, (const uint8_t*)v, max_len);
-  return hipGetLastError();
+  return launch(prefill_scatter_kernel<ES, D>, dim3(p.U, ysplit), dim3(64 * kWavesPerWG), s, p,
+                (const uint8_t*)k, (const uint8_t*)v, max_len);
 }
 
 hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const void* v,
@@ -759,18 +824,19 @@ hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const v
 }
 
 template <int ES, int D>
-static hipError_t attention_t(const Dev& p, const void* q, float* out, int64_t grid_waves, hipStream_t s) {
-  const int64_t nwg = grid_waves / kWavesPerWG;
-  hipLaunchKernelGGL((attention_kernel<ES, D>), dim3((unsigned)nwg), dim3(64 * kWavesPerWG), 0, s, p,
-                     (const uint8_t*)q, out);
-  return hipGetLastError();
+static hipError_t attention_t(const Dev& p, const void* q, float* out, int64_t grid_wgs, hipStream_t s) {
+  const int64_t nwg = grid_wgs;
+  const hipError_t e = launch(attention_kernel<ES, D>, dim3((unsigned)nwg), dim3(64 * kWavesPerWG), s, p,
+                              (const int32_t*)p.btab, (const uint32_t*)p.blk_mask, (const uint8_t*)q, out);
+  if (e != hipSuccess) return e;
+  return launch(reduce_kernel<D>, dim3((p.U + kWavesPerWG - 1) / kWavesPerWG), dim3(64 * kWavesPerWG), s, p, out);
 }
 
-hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out, int64_t grid_waves,
+hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out, int64_t grid_wgs,
                             hipStream_t s) {
   if (dtype == 1)
-    return d == 128 ? attention_t<2, 128>(p, q, out, grid_waves, s) : attention_t<2, 64>(p, q, out, grid_waves, s);
-  return d == 128 ? attention_t<4, 128>(p, q, out, grid_waves, s) : attention_t<4, 64>(p, q, out, grid_waves, s);
+    return d == 128 ? attention_t<2, 128>(p, q, out, grid_wgs, s) : attention_t<2, 64>(p, q, out, grid_wgs, s);
+  return d == 128 ? attention_t<4, 128>(p, q, out, grid_wgs, s) : attention_t<4, 64>(p, q, out, grid_wgs, s);
 }
 
 }  // namespace dms

@@ -19,9 +19,13 @@ struct dms_cache {
   int device;
   int num_cus;
   int target_items;
-  int64_t grid_waves;
+  int64_t grid_wgs;
   std::vector<int32_t> len;  // host mirror of each sequence's length
 };
+
+#ifndef DMS_SPLIT_ITEMS_PER_CU
+#define DMS_SPLIT_ITEMS_PER_CU 2
+#endif
 
 namespace {
 
@@ -57,7 +61,9 @@ void make_layout(const dms_config* c, dms::Layout& L) {
   L.R = std::min(c->window, c->max_tokens) + 1;
   L.max_tokens = c->max_tokens;
   L.max_blocks = (c->max_tokens + dms::kBlockTokens - 1) / dms::kBlockTokens;
-  L.max_splits = c->max_splits == 0 ? 32 : c->max_splits;
+  // at least enough work items per unit to keep each within kMaxItemBlocks
+  L.max_splits = std::max(c->max_splits == 0 ? 32 : c->max_splits,
+                          (L.max_blocks + dms::kMaxItemBlocks - 1) / dms::kMaxItemBlocks);
   L.U = c->batch * c->num_kv_heads;
   L.pool_blocks = c->pool_blocks;
   L.block_bytes = 2LL * dms::kBlockTokens * L.d * L.esize;
@@ -78,8 +84,8 @@ void make_layout(const dms_config* c, dms::Layout& L) {
   o = align_up(o + (int64_t)L.U * 4, kAlign);
   L.off_pos = o;
   o = align_up(o + (int64_t)L.U * 4, kAlign);
-  L.off_arrive = o;
-  o = align_up(o + (int64_t)L.U * 4, kAlign);
+  L.off_plan = o;
+  o = align_up(o + (int64_t)L.U * 8, kAlign);
   L.off_ctr = o;
   o = align_up(o + (int64_t)sizeof(dms::Counters), kAlign);
   L.off_part = o;
@@ -97,7 +103,7 @@ dms::Dev make_dev(const dms_cache* c) {
   p.ring = (int32_t*)(c->ws + L.off_ring);
   p.n = (int32_t*)(c->ws + L.off_n);
   p.pos = (int32_t*)(c->ws + L.off_pos);
-  p.arrive = (int32_t*)(c->ws + L.off_arrive);
+  p.plan = (int32_t*)(c->ws + L.off_plan);
   p.ctr = (dms::Counters*)(c->ws + L.off_ctr);
   p.part = (float*)(c->ws + L.off_part);
   p.B = L.B;
@@ -156,10 +162,14 @@ int dms_cache_create(const dms_config* cfg, void* d_workspace, size_t workspace_
   c->ws = (uint8_t*)d_workspace;
   c->device = dev;
   c->num_cus = prop.multiProcessorCount;
-  // About two waves per SIMD of split-K work: enough memory-level
-  // parallelism for HBM while keeping partials and merges few.
-  c->target_items = std::max(64, c->num_cus * 8);
-  c->grid_waves = align_up(std::min<int64_t>(L.max_items, (int64_t)c->target_items + L.U) + 7, 32);
+  // Split-K work items (4-wave work-groups) per launch: about two per CU.
+  // Fewer, longer streams keep HBM efficient; the pipeline in each wave
+  // supplies the memory-level parallelism.  Each unit gets at most
+  // round(share) + ceil(nblk / kMaxItemBlocks) items, so the plan never
+  // exceeds target + U + U + pool_blocks / kMaxItemBlocks items.
+  c->target_items = std::max(8, c->num_cus * DMS_SPLIT_ITEMS_PER_CU);
+  c->grid_wgs = std::min<int64_t>(L.max_items, (int64_t)c->target_items + 2LL * L.U +
+                                                   L.pool_blocks / dms::kMaxItemBlocks);
   c->len.assign(L.B, 0);
   const int st = hip_status(dms::launch_init(make_dev(c), (hipStream_t)stream));
   if (st != DMS_OK) {
@@ -220,7 +230,7 @@ int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stre
   if (st != DMS_OK) return st;
   for (int32_t x : c->len)
     if (x < 1) return DMS_ERR_STATE;
-  return hip_status(dms::launch_attention(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_out, c->grid_waves,
+  return hip_status(dms::launch_attention(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_out, c->grid_wgs,
                                           (hipStream_t)stream));
 }
 

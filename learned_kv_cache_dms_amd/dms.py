@@ -64,7 +64,19 @@ class dms_stats(ctypes.Structure):
     ]
 
 
+def _bind_hip_runtime():
+    """torch ships its own HIP runtime.  Loading it before the library makes
+    the library bind to that same runtime, so device pointers and streams
+    from torch are valid here; loaded the other way round a process can end
+    up with two HIP runtimes that do not share state."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
 def _load():
+    _bind_hip_runtime()
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"DMS HIP library not found at {LIB_PATH}; build it with "

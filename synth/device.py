@@ -13,7 +13,19 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdms_synth.so")
 
 
+def _bind_hip_runtime():
+    """torch ships its own HIP runtime.  Loading it before the library makes
+    the library bind to that same runtime, so device pointers and streams
+    from torch are valid here; loaded the other way round a process can end
+    up with two HIP runtimes that do not share state."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
 def _load():
+    _bind_hip_runtime()
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} missing; build with `python -m learned_kv_cache_dms_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)

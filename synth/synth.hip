@@ -89,6 +89,7 @@ int grid_for(int64_t total) {
 
 extern "C" {
 
+__attribute__((visibility("default")))
 // Fills out[nb][heads][npos][channels] (fp32, or bf16 when bf16 != 0) with
 // the values of (seed, stream) at layer, sequences b0.., positions
 // pos_base[bi] (device array, may be null -> pos0) + 0..npos-1.
@@ -98,11 +99,12 @@ int synth_fill(void* d_out, int bf16, uint64_t seed, int stream, int layer, int 
   Shape s{seed, stream, layer, b0, nb, heads, pos0, npos, channels, d_pos_base};
   const int64_t total = (int64_t)nb * heads * npos * channels;
   if (total == 0) return 0;
-  hipLaunchKernelGGL(fill_kernel, dim3(grid_for(total)), dim3(256), 0, (hipStream_t)hip_stream, s, d_out, bf16,
-                     total);
-  return hipGetLastError() == hipSuccess ? 0 : -6;
+  void* args[] = {&s, &d_out, &bf16, (void*)&total};
+  return hipLaunchKernel((const void*)fill_kernel, dim3(grid_for(total)), dim3(256), args, 0,
+                         (hipStream_t)hip_stream) == hipSuccess ? 0 : -6;
 }
 
+__attribute__((visibility("default")))
 // Eviction logits out[nb][heads][npos] = float32(mu + x), mu per head from
 // mu_before (positions < pos_threshold) or mu_after.
 int synth_logits(float* d_out, uint64_t seed, int layer, int b0, int nb, int heads, const int32_t* d_pos_base,
@@ -117,9 +119,9 @@ int synth_logits(float* d_out, uint64_t seed, int layer, int b0, int nb, int hea
   }
   const int64_t total = (int64_t)nb * heads * npos;
   if (total == 0) return 0;
-  hipLaunchKernelGGL(logit_kernel, dim3(grid_for(total)), dim3(256), 0, (hipStream_t)hip_stream, s, d_out, mu,
-                     pos_threshold, total);
-  return hipGetLastError() == hipSuccess ? 0 : -6;
+  void* args[] = {&s, &d_out, &mu, &pos_threshold, (void*)&total};
+  return hipLaunchKernel((const void*)logit_kernel, dim3(grid_for(total)), dim3(256), args, 0,
+                         (hipStream_t)hip_stream) == hipSuccess ? 0 : -6;
 }
 
 }  // extern "C"
