@@ -17,7 +17,8 @@ struct Counters {
   unsigned long long bump;              // next free pool block (may overshoot on exhaustion)
   unsigned long long live_token_steps;  // sum of live tokens after each append call
   int sticky_error;                     // first device-detected dms_status, else 0
-  int pad[11];
+  int next_item;                        // attention work items handed out past the grid
+  int pad[10];
 };
 
 // Byte offsets of every region inside the caller's workspace.  The workspace
@@ -66,6 +67,8 @@ hipError_t launch_append(const Dev& p, int dtype, int d, const void* k, const vo
 hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const void* v,
                           const float* logit, const int32_t* h_lengths, int32_t max_len, hipStream_t s);
 hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s);
+// Work-groups of the attention kernel that fit on the device at once.
+int attention_resident_wgs(int dtype, int d, int num_cus);
 hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out,
                             int64_t grid_wgs, hipStream_t s);
 

@@ -122,6 +122,7 @@ __global__ void init_kernel(Dev p) {
     p.ctr->bump = 0;
     p.ctr->live_token_steps = 0;
     p.ctr->sticky_error = 0;
+    p.ctr->next_item = 0;
   }
 }
 
@@ -444,29 +445,36 @@ __device__ __forceinline__ long long plan_blocks(const Dev& p, int lane) {
   return max(1LL, tot);
 }
 
-// Finds work item `item`; false when item >= the plan's total.
-__device__ __forceinline__ bool plan_find(const Dev& p, int lane, long long tot, int item, Item& it) {
-  int running = 0;
-  for (int b0 = 0; b0 < p.U && running <= item; b0 += 64) {
-    const int uu = b0 + lane;
+// Position of a search through the plan: units before b0 hold `running` items.
+struct PlanCursor {
+  int b0 = 0, running = 0;
+};
+
+// Finds work item `item`; false when item >= the plan's total.  The cursor
+// resumes the search where the previous one stopped, so a work-group that
+// visits increasing items scans n[] once in total.
+__device__ __forceinline__ bool plan_find(const Dev& p, int lane, long long tot, int item, Item& it,
+                                          PlanCursor& cur) {
+  for (; cur.b0 < p.U && cur.running <= item; cur.b0 += 64) {
+    const int uu = cur.b0 + lane;
     int nb = 0, cnt = 0;
     if (uu < p.U) {
       nb = (p.n[uu] + 15) >> 4;
       cnt = unit_items(nb, tot, p.target_items, p.max_splits);
     }
     const int incl = wave_incl_scan_i(cnt, lane);
-    const int start = running + incl - cnt;
+    const int start = cur.running + incl - cnt;
     const unsigned long long bal = __ballot(item >= start && item < start + cnt);
     if (bal) {
       const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)bal) - 1);
-      it.u = b0 + src;
+      it.u = cur.b0 + src;
       it.base = __builtin_amdgcn_readlane(start, src);
       it.items = __builtin_amdgcn_readlane(cnt, src);
       it.nblk = __builtin_amdgcn_readlane(nb, src);
       it.k = item - it.base;
-      return true;
+      return true;  // the cursor stays on this group: later items may fall in it
     }
-    running += __builtin_amdgcn_readlane(incl, 63);
+    cur.running += __builtin_amdgcn_readlane(incl, 63);
   }
   return false;
 }
@@ -555,31 +563,27 @@ __device__ __forceinline__ void attend_block(const Frag<ES, D>& f, const u32x4 (
   }
 }
 
-// Split-K decode attention.  One work-group (4 waves) per work item = a
-// chunk of one (sequence, KV head)'s blocks; wave w takes the chunk's blocks
-// w, w+4, w+8, ... so the work-group streams one contiguous run.  The waves'
-// softmax states are merged through LDS; a unit held by a single work item
-// writes its output here, otherwise the merged partial goes to reduce_kernel.
+// Split-K decode attention.  A work item is a chunk of one (sequence, KV
+// head)'s blocks, processed by one work-group of 4 waves: wave w takes the
+// chunk's blocks w, w+4, w+8, ... so the work-group streams one contiguous
+// run.  The waves' softmax states are merged through LDS; a unit held by a
+// single work item writes its output here, otherwise the merged partial goes
+// to reduce_kernel.
 template <int ES, int D>
-__global__ __launch_bounds__(256) void attention_kernel(Dev p, const int32_t* __restrict__ btab,
-                                                        const uint32_t* __restrict__ bmask,
-                                                        const uint8_t* __restrict__ q, float* __restrict__ out) {
+struct AttnShared {
+  f32x4 o[kWavesPerWG][Geo<ES, D>::kTiles][64];
+  float m[kWavesPerWG][16], l[kWavesPerWG][16];
+  int next;
+};
+
+template <int ES, int D>
+__device__ __forceinline__ void attention_item(const Dev& p, const int32_t* __restrict__ btab,
+                                               const uint32_t* __restrict__ bmask, const uint8_t* __restrict__ q,
+                                               float* __restrict__ out, const Item& it, int lane, int wave,
+                                               AttnShared<ES, D>& sh) {
   using G = Geo<ES, D>;
   constexpr int kW = kWavesPerWG;
   constexpr int kTilesPerWave = (G::kTiles + kW - 1) / kW;
-  __shared__ f32x4 s_o[kW][G::kTiles][64];
-  __shared__ float s_m[kW][16], s_l[kW][16];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  // Work item = work-group id.  Consecutive ids are consecutive units, and
-  // the dispatcher deals work-groups round-robin over the XCDs, so every XCD
-  // gets an even share of units.
-  const long long tot = plan_blocks(p, lane);
-  Item it;
-  if (!plan_find(p, lane, tot, (int)blockIdx.x, it)) return;  // uniform over the work-group
-
   const int u = it.u;
   const int b = u / p.Hkv, h = u - b * p.Hkv;
   const int g = lane & 15;
@@ -625,32 +629,33 @@ __global__ __launch_bounds__(256) void attention_kernel(Dev p, const int32_t* __
     const int64_t BB = p.block_bytes;
     // Three-block rotation: two blocks load while one is computed.  Loads
     // are unconditional (indices past the end are clamped to the last block,
-    // just read) so the load counter analysis stays exact in the loop.
+    // just read) so the load counter analysis stays exact in the loop.  The
+    // live mask of block i is read only when the block is computed, so the
+    // K/V loads never wait for the mask loads.
     Frag<ES, D> f0, f1, f2;
-    uint32_t m0, m1, m2;
     const int last = cnt - 1;
-    auto fetch = [&](Frag<ES, D>& f, uint32_t& m, int i) {
+    auto fetch = [&](Frag<ES, D>& f, int i) {
       const int ic = min(i, last);
       const int blk = ic < 64 ? __builtin_amdgcn_readlane(id0, ic) : __builtin_amdgcn_readlane(id1, ic - 64);
-      const uint32_t mm = (uint32_t)(ic < 64 ? __builtin_amdgcn_readlane((int)mk0, ic)
-                                             : __builtin_amdgcn_readlane((int)mk1, ic - 64));
-      m = i <= last ? mm : 0u;
       load_frag<ES, D>(f, pool + (int64_t)blk * BB, lane);
     };
-    fetch(f0, m0, 0);
-    fetch(f1, m1, 1);
+    auto mask_of = [&](int i) -> uint32_t {
+      return (uint32_t)(i < 64 ? __builtin_amdgcn_readlane((int)mk0, i) : __builtin_amdgcn_readlane((int)mk1, i - 64));
+    };
+    fetch(f0, 0);
+    fetch(f1, 1);
     int i = 0;
     for (; i + 2 < cnt; i += 3) {
-      fetch(f2, m2, i + 2);
-      attend_block<ES, D>(f0, qf, m0, lane, sl2e, acc);
-      fetch(f0, m0, i + 3);
-      attend_block<ES, D>(f1, qf, m1, lane, sl2e, acc);
-      fetch(f1, m1, i + 4);
-      attend_block<ES, D>(f2, qf, m2, lane, sl2e, acc);
+      fetch(f2, i + 2);
+      attend_block<ES, D>(f0, qf, mask_of(i), lane, sl2e, acc);
+      fetch(f0, i + 3);
+      attend_block<ES, D>(f1, qf, mask_of(i + 1), lane, sl2e, acc);
+      fetch(f1, i + 4);
+      attend_block<ES, D>(f2, qf, mask_of(i + 2), lane, sl2e, acc);
     }
     // 0, 1 or 2 blocks remain, already loaded in f0 and f1
-    if (i < cnt) attend_block<ES, D>(f0, qf, m0, lane, sl2e, acc);
-    if (i + 1 < cnt) attend_block<ES, D>(f1, qf, m1, lane, sl2e, acc);
+    if (i < cnt) attend_block<ES, D>(f0, qf, mask_of(i), lane, sl2e, acc);
+    if (i + 1 < cnt) attend_block<ES, D>(f1, qf, mask_of(i + 1), lane, sl2e, acc);
   }
 
   // lane-local l holds 4 of the 16 tokens per block; add the four groups
@@ -659,22 +664,22 @@ __global__ __launch_bounds__(256) void attention_kernel(Dev p, const int32_t* __
 
   // merge the waves' states through LDS; wave w finishes tiles w*TPW...
   if (lane < 16) {
-    s_m[wave][lane] = acc.m;
-    s_l[wave][lane] = lt;
+    sh.m[wave][lane] = acc.m;
+    sh.l[wave][lane] = lt;
   }
 #pragma unroll
-  for (int j = 0; j < G::kTiles; ++j) s_o[wave][j][lane] = acc.o[j];
+  for (int j = 0; j < G::kTiles; ++j) sh.o[wave][j][lane] = acc.o[j];
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kW; ++w) M = fmaxf(M, s_m[w][g]);
+  for (int w = 0; w < kW; ++w) M = fmaxf(M, sh.m[w][g]);
   const float Mr = (M == -INFINITY) ? 0.f : M;
   float wt[kW];
   float L = 0.f;
 #pragma unroll
   for (int w = 0; w < kW; ++w) {
-    wt[w] = exp2_fast(s_m[w][g] - Mr);
-    L += wt[w] * s_l[w][g];
+    wt[w] = exp2_fast(sh.m[w][g] - Mr);
+    L += wt[w] * sh.l[w][g];
   }
   const int j0 = wave * kTilesPerWave;
   f32x4 O[kTilesPerWave];
@@ -683,7 +688,7 @@ __global__ __launch_bounds__(256) void attention_kernel(Dev p, const int32_t* __
     O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (j0 + t < G::kTiles) {
 #pragma unroll
-      for (int w = 0; w < kW; ++w) O[t] += wt[w] * s_o[w][j0 + t][lane];
+      for (int w = 0; w < kW; ++w) O[t] += wt[w] * sh.o[w][j0 + t][lane];
     }
   }
   if (it.k == 0 && wave == 0 && lane == 0) {  // read by reduce_kernel, for every unit
@@ -698,7 +703,7 @@ __global__ __launch_bounds__(256) void attention_kernel(Dev p, const int32_t* __
       for (int t = 0; t < kTilesPerWave; ++t)
         if (j0 + t < G::kTiles) *(f32x4*)(orow + 16 * (j0 + t)) = O[t] * inv;
     }
-    return;
+    return;  // returns from this item only
   }
   // several items: publish the merged partial; reduce_kernel combines them
   const int IF = p.item_floats;
@@ -714,12 +719,38 @@ __global__ __launch_bounds__(256) void attention_kernel(Dev p, const int32_t* __
   }
 }
 
+// Persistent launch: one work-group per resident slot.  Its first item is its
+// id; further items come from an atomic counter (reset by reduce_kernel, which
+// runs after this kernel on the same stream), so no work-group is launched
+// only to find it has nothing to do.
+template <int ES, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2 : 1))) void attention_kernel(
+    Dev p, const int32_t* __restrict__ btab,
+                                                        const uint32_t* __restrict__ bmask,
+                                                        const uint8_t* __restrict__ q, float* __restrict__ out) {
+  __shared__ AttnShared<ES, D> sh;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long tot = plan_blocks(p, lane);
+  PlanCursor cur;
+  int item = blockIdx.x;
+  for (;;) {
+    Item it;
+    if (!plan_find(p, lane, tot, item, it, cur)) break;  // uniform over the work-group
+    attention_item<ES, D>(p, btab, bmask, q, out, it, lane, wave, sh);
+    if (threadIdx.x == 0) sh.next = (int)gridDim.x + atomicAdd(&p.ctr->next_item, 1);
+    __syncthreads();  // publishes sh.next; the LDS of this item is free again
+    item = sh.next;
+  }
+}
+
 // Split reduce: one wave per (sequence, KV head) whose attention was split
 // into several work items; merges their (m, l, o) partials by log-sum-exp:
 //   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  o = sum_s 2^(m_s - M) o_s / L.
 // Lane l handles head l % 16 and the channels 16j + 4(l/16) + r.
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(Dev p, float* __restrict__ out) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.ctr->next_item = 0;  // attention_kernel has finished
   const int lane = threadIdx.x & 63;
   const int u = blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
   if (u >= p.U) return;
@@ -830,6 +861,21 @@ static hipError_t attention_t(const Dev& p, const void* q, float* out, int64_t g
                               (const int32_t*)p.btab, (const uint32_t*)p.blk_mask, (const uint8_t*)q, out);
   if (e != hipSuccess) return e;
   return launch(reduce_kernel<D>, dim3((p.U + kWavesPerWG - 1) / kWavesPerWG), dim3(64 * kWavesPerWG), s, p, out);
+}
+
+template <int ES, int D>
+static int resident_t(int num_cus) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attention_kernel<ES, D>, 64 * kWavesPerWG, 0) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  return per_cu * num_cus;
+}
+
+int attention_resident_wgs(int dtype, int d, int num_cus) {
+  if (dtype == 1) return d == 128 ? resident_t<2, 128>(num_cus) : resident_t<2, 64>(num_cus);
+  return d == 128 ? resident_t<4, 128>(num_cus) : resident_t<4, 64>(num_cus);
 }
 
 hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out, int64_t grid_wgs,

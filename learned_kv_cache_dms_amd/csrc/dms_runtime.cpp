@@ -23,8 +23,9 @@ struct dms_cache {
   std::vector<int32_t> len;  // host mirror of each sequence's length
 };
 
-#ifndef DMS_SPLIT_ITEMS_PER_CU
-#define DMS_SPLIT_ITEMS_PER_CU 2
+// Split-plan target in quarters of the resident work-group count.
+#ifndef DMS_SPLIT_ITEMS_PER_RESIDENT
+#define DMS_SPLIT_ITEMS_PER_RESIDENT 8
 #endif
 
 namespace {
@@ -162,14 +163,15 @@ int dms_cache_create(const dms_config* cfg, void* d_workspace, size_t workspace_
   c->ws = (uint8_t*)d_workspace;
   c->device = dev;
   c->num_cus = prop.multiProcessorCount;
-  // Split-K work items (4-wave work-groups) per launch: about two per CU.
-  // Fewer, longer streams keep HBM efficient; the pipeline in each wave
-  // supplies the memory-level parallelism.  Each unit gets at most
-  // round(share) + ceil(nblk / kMaxItemBlocks) items, so the plan never
-  // exceeds target + U + U + pool_blocks / kMaxItemBlocks items.
-  c->target_items = std::max(8, c->num_cus * DMS_SPLIT_ITEMS_PER_CU);
-  c->grid_wgs = std::min<int64_t>(L.max_items, (int64_t)c->target_items + 2LL * L.U +
-                                                   L.pool_blocks / dms::kMaxItemBlocks);
+  // Persistent attention grid: as many 4-wave work-groups as fit at once.
+  // The split plan aims at two work items per resident work-group: long
+  // streams keep HBM efficient (the pipeline in each wave supplies the
+  // memory-level parallelism), and the second round, handed out dynamically,
+  // evens out the work-groups' finishing times.
+  const int resident = dms::attention_resident_wgs(cfg->dtype, L.d, c->num_cus);
+  c->target_items = std::max(8, resident * DMS_SPLIT_ITEMS_PER_RESIDENT / 4);
+  c->grid_wgs = std::min<int64_t>(resident, std::min<int64_t>(L.max_items, (int64_t)c->target_items + 2LL * L.U +
+                                                                              L.pool_blocks / dms::kMaxItemBlocks));
   c->len.assign(L.B, 0);
   const int st = hip_status(dms::launch_init(make_dev(c), (hipStream_t)stream));
   if (st != DMS_OK) {
