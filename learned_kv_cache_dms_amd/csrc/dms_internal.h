@@ -10,6 +10,7 @@ namespace dms {
 constexpr int kBlockTokens = 16;
 constexpr int kMaxGroup = 16;      // query heads per KV head held by one MFMA tile
 constexpr int kMaxItemBlocks = 512;  // blocks per attention work item (128 per wave)
+constexpr int kMaxTargetItems = 4096;  // cap on the split plan's target item count
 constexpr int kWavesPerWG = 4;     // waves per work-group (attention work item, append, reduce)
 
 // Device-side counters (one 64-byte line).
@@ -29,7 +30,7 @@ struct Layout {
   int32_t max_tokens, max_blocks, max_splits, U;
   int64_t pool_blocks, block_bytes;
   int32_t item_floats;  // floats per attention partial: m[16], l[16], o[G][d]
-  int64_t max_items;    // partial slots = U * max_splits
+  int64_t max_items;    // partial slots: the most items a plan can have
   int64_t off_pool, off_btab, off_blkpos, off_blkmask, off_ring, off_n, off_pos, off_plan,
       off_ctr, off_part, total;
 };

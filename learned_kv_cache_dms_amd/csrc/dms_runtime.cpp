@@ -69,7 +69,10 @@ void make_layout(const dms_config* c, dms::Layout& L) {
   L.pool_blocks = c->pool_blocks;
   L.block_bytes = 2LL * dms::kBlockTokens * L.d * L.esize;
   L.item_floats = 32 + L.G * L.d;
-  L.max_items = (int64_t)L.U * L.max_splits;
+  // A plan never has more than target + 2U + pool_blocks / kMaxItemBlocks
+  // items (target <= kMaxTargetItems), nor more than max_splits per unit.
+  L.max_items = std::min<int64_t>((int64_t)L.U * L.max_splits,
+                                  dms::kMaxTargetItems + 2LL * L.U + L.pool_blocks / dms::kMaxItemBlocks);
   int64_t o = 0;
   L.off_pool = o;
   o = align_up(o + L.pool_blocks * L.block_bytes, kAlign);
@@ -169,7 +172,7 @@ int dms_cache_create(const dms_config* cfg, void* d_workspace, size_t workspace_
   // memory-level parallelism), and the second round, handed out dynamically,
   // evens out the work-groups' finishing times.
   const int resident = dms::attention_resident_wgs(cfg->dtype, L.d, c->num_cus);
-  c->target_items = std::max(8, resident * DMS_SPLIT_ITEMS_PER_RESIDENT / 4);
+  c->target_items = std::min(dms::kMaxTargetItems, std::max(8, resident * DMS_SPLIT_ITEMS_PER_RESIDENT / 4));
   c->grid_wgs = std::min<int64_t>(resident, std::min<int64_t>(L.max_items, (int64_t)c->target_items + 2LL * L.U +
                                                                               L.pool_blocks / dms::kMaxItemBlocks));
   c->len.assign(L.B, 0);

@@ -87,6 +87,9 @@ class Workload:
 
     def expected_live(self, layer: int, q: int) -> float:
         """E|Vis(q)| under independent marks: unmarked tokens plus the window."""
+        if q < self.pos_threshold:  # one marking rate over positions 0..q: closed form
+            p = float(self.marked_prob(layer, np.array([0]))[0])
+            return (q + 1) * (1.0 - p) + min(self.window + 1, q + 1) * p
         pos = np.arange(q + 1)
         p = self.marked_prob(layer, pos)
         in_window = pos >= q - self.window

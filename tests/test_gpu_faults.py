@@ -1,0 +1,188 @@
+"""Failure handling, forced from the host; every kernel still exits normally.
+
+- an undersized block pool raises the sticky DMS_ERR_OUT_OF_BLOCKS on the
+  device (reported by stats, cleared by reset) while all accesses stay in
+  bounds;
+- argument, state and capacity errors are returned before anything is
+  enqueued;
+- a NaN logit means "not marked";
+- reset returns the cache to a state equal to a fresh one.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from synth import workloads as W
+
+gpu = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _wl(**kw):
+    base = dict(name="fault", batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16", window=4,
+                decode_steps=8, seed=31, prompt_len=64, mu_before=[0.0])
+    base.update(kw)
+    return W.Workload(**base)
+
+
+def _prompt(wl, lengths):
+    import gpu_util as U
+    return U.device_prompt(wl, 0, np.asarray(lengths))
+
+
+@gpu
+def test_pool_exhaustion_in_prefill_is_sticky_and_reset_clears_it():
+    import gpu_util as U
+    from learned_kv_cache_dms_amd import dms
+    wl = _wl(prompt_len=200, mu_before=[-5.0])          # nothing marked: 200 visible tokens per unit
+    c = U.make_cache(wl, pool_blocks=20)                 # 4 units x 13 blocks needed
+    K, V, Lg = _prompt(wl, [200, 200])
+    c.prefill(K, V, Lg, [200, 200])
+    st = c.stats()
+    assert st["sticky_error"] == dms.DMS_ERR_OUT_OF_BLOCKS
+    assert st["allocated_blocks"] <= 20
+    # appends and attention still run, in bounds
+    pos = torch.tensor([200, 200], dtype=torch.int32, device="cuda")
+    q, k, v, lg = U.device_step(wl, 0, pos)
+    c.append(k, v, lg)
+    c.attend(q)
+    torch.cuda.synchronize()
+    assert c.stats()["sticky_error"] == dms.DMS_ERR_OUT_OF_BLOCKS
+    c.reset()
+    st = c.stats()
+    assert st["sticky_error"] == 0 and st["live_tokens"] == 0 and st["allocated_blocks"] == 0
+    # after reset a prompt that fits works and matches the oracle
+    K2, V2, Lg2 = _prompt(wl, [40, 40])
+    c.prefill(K2, V2, Lg2, [40, 40])
+    _, _, n = c.export()
+    assert list(n) == [40, 40, 40, 40]
+
+
+@gpu
+def test_pool_exhaustion_during_decode():
+    import gpu_util as U
+    from learned_kv_cache_dms_amd import dms
+    wl = _wl(prompt_len=32, mu_before=[-5.0], decode_steps=40)
+    c = U.make_cache(wl, pool_blocks=8)                  # prompt uses exactly 2 blocks per unit
+    K, V, Lg = _prompt(wl, [32, 32])
+    c.prefill(K, V, Lg, [32, 32])
+    assert c.stats()["sticky_error"] == 0
+    pos = torch.tensor([32, 32], dtype=torch.int32, device="cuda")
+    for t in range(20):
+        q, k, v, lg = U.device_step(wl, 0, pos + t)
+        c.append(k, v, lg)
+        c.attend(q)
+    torch.cuda.synchronize()
+    st = c.stats()
+    assert st["sticky_error"] == dms.DMS_ERR_OUT_OF_BLOCKS
+    assert st["allocated_blocks"] == 8
+    _, _, n = c.export()
+    assert all(32 <= x <= 48 for x in n)
+
+
+@gpu
+def test_capacity_state_and_argument_errors():
+    import gpu_util as U
+    from learned_kv_cache_dms_amd import dms
+    wl = _wl(prompt_len=10, decode_steps=2)
+    c = U.make_cache(wl, max_tokens=12)
+    pos = torch.tensor([0, 0], dtype=torch.int32, device="cuda")
+    q, k, v, lg = U.device_step(wl, 0, pos)
+    with pytest.raises(dms.DmsError) as e:
+        c.attend(q)                                      # no token yet
+    assert e.value.status == dms.DMS_ERR_STATE
+    K, V, Lg = _prompt(wl, [10, 10])
+    with pytest.raises(dms.DmsError) as e:
+        c.prefill(K, V, Lg, [13, 10])                     # longer than the prompt tensor
+    assert e.value.status == dms.DMS_ERR_ARG
+    c.prefill(K, V, Lg, [10, 10])
+    with pytest.raises(dms.DmsError) as e:
+        c.prefill(K, V, Lg, [10, 10])                     # not empty
+    assert e.value.status == dms.DMS_ERR_STATE
+    c.append(k, v, lg)
+    c.append(k, v, lg)
+    with pytest.raises(dms.DmsError) as e:
+        c.append(k, v, lg)                                # 13 > max_tokens
+    assert e.value.status == dms.DMS_ERR_CAPACITY
+    assert c.stats()["seen_tokens"] == 4 * 12
+    with pytest.raises(ValueError):
+        c.append(k.float(), v, lg)                        # dtype checked by the binding
+    with pytest.raises(ValueError):
+        c.attend(q[:, :4].contiguous())                   # shape checked by the binding
+    L = dms.lib
+    assert L.dms_append_step(c.handle, None, v.data_ptr(), lg.data_ptr(), None) == dms.DMS_ERR_ARG
+    assert L.dms_decode_attention(c.handle, q.data_ptr(), None, None) == dms.DMS_ERR_ARG
+    assert L.dms_cache_export(c.handle, 3, 2, None, None, None, None) == dms.DMS_ERR_ARG
+
+
+@gpu
+def test_nan_and_zero_logits_are_not_marked():
+    import gpu_util as U
+    wl = _wl(prompt_len=30, window=100)
+    c = U.make_cache(wl)
+    K, V, Lg = _prompt(wl, [30, 30])
+    special = torch.tensor([float("nan"), 0.0, -0.0, 1e-30, -1e-30, float("inf"), float("-inf")],
+                           device="cuda")
+    Lg[:, :, :7] = special
+    c.prefill(K, V, Lg, [30, 30])
+    slot_pos, ring, n = c.export()
+    for u in range(4):
+        pend = set(slot_pos[u][ring[u][ring[u] >= 0]].tolist())
+        assert 0 not in pend and 1 not in pend and 2 not in pend and 4 not in pend and 6 not in pend
+        assert 3 in pend and 5 in pend                   # 1e-30 and +inf are > 0
+        assert n[u] == 30
+
+
+@gpu
+def test_reset_equals_fresh_cache():
+    import gpu_util as U
+    wl = _wl(prompt_len=50, decode_steps=5, mu_before=[0.4])
+    a = U.make_cache(wl)
+    K, V, Lg = _prompt(wl, [50, 33])
+    a.prefill(K, V, Lg, [50, 33])
+    pos = torch.tensor([50, 33], dtype=torch.int32, device="cuda")
+    for t in range(5):
+        q, k, v, lg = U.device_step(wl, 0, pos + t)
+        a.append(k, v, lg)
+    a.reset()
+    b = U.make_cache(wl)
+    outs = []
+    for c in (a, b):
+        c.prefill(K, V, Lg, [50, 33])
+        for t in range(5):
+            q, k, v, lg = U.device_step(wl, 0, pos + t)
+            c.append(k, v, lg)
+            o = c.attend(q)
+        outs.append((o.clone(), c.export()))
+    assert torch.equal(outs[0][0], outs[1][0])
+    for x, y in zip(outs[0][1], outs[1][1]):
+        assert np.array_equal(x, y)
+
+
+@gpu
+def test_runs_on_a_non_default_stream():
+    import gpu_util as U
+    wl = _wl(prompt_len=60, decode_steps=3)
+    K, V, Lg = _prompt(wl, [60, 60])
+    pos = torch.tensor([60, 60], dtype=torch.int32, device="cuda")
+    q, k, v, lg = U.device_step(wl, 0, pos)
+    ref = U.make_cache(wl)
+    ref.prefill(K, V, Lg, [60, 60])
+    ref.append(k, v, lg)
+    o_ref = ref.attend(q)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = U.make_cache(wl)
+        c.prefill(K, V, Lg, [60, 60])
+        c.append(k, v, lg)
+        o = c.attend(q)
+    s.synchronize()
+    assert torch.equal(o, o_ref)
