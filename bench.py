@@ -3,7 +3,7 @@
 
 One step = one decode step of every sequence of the workload through the C
 ABI: dms_append_step (decide, retire, store) then dms_decode_attention
-(split-K attention over the visible tokens, merge in the same launch).
+(split-K attention over the visible tokens, then the split merge).
 Inputs are synthetic, generated in HBM before the timed region.  The default
 workload is the Qwen-R1-32B-shaped layer: 64 chains at 32768 tokens, 40 query
 / 8 KV heads, head_dim 128, bf16, w = 256, logit mean for CR 4 below position
@@ -11,8 +11,9 @@ workload is the Qwen-R1-32B-shaped layer: 64 chains at 32768 tokens, 40 query
 
 Prints one JSON line.  `value` is decode-attention tokens per second (batch
 sequences per step); the live-KV bandwidth of the attention launch is in
-`roofline`.  `cpu_baseline` times the CPU oracle on a bounded sample of the
-same workload.
+`roofline`, timed with HIP events around each dms_decode_attention call (its
+two kernels: attention_kernel and reduce_kernel).  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --calib-copy-bytes N    # plain copy kernel, for counter scaling
@@ -160,8 +161,10 @@ def main():
     dsynth.logits(Ld, wl.seed, 0, 0, mb, ma, wl.pos_threshold)
     cache.prefill(Kd, Vd, Ld, lengths)
     torch.cuda.synchronize()
+    # The dense prompt stays in torch's cache: returning 17 GB to the driver
+    # (empty_cache) was measured to lower HBM streaming rates by 4-5% for the
+    # rest of the process on this platform.
     del Kd, Vd, Ld
-    torch.cuda.empty_cache()
 
     S = W + K
     qs = torch.empty((S, B, Hq, d), dtype=tdt, device="cuda")
@@ -244,7 +247,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None if traffic is None else round(traffic),
-            "kernel": "attention_kernel<2,128>" if (esize == 2 and d == 128) else "attention_kernel",
+            "kernel": "dms_decode_attention = attention_kernel + reduce_kernel",
             "algorithmic_bytes_per_launch": round(live_bytes),
         },
         "cpu_baseline": None,
