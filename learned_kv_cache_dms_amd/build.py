@@ -37,6 +37,12 @@ COMMON = [
     "-fvisibility=hidden",
 ]
 
+# Device code only: the atomic optimizer rewrites a one-lane atomicAdd into a
+# wave-wide one whose result is read at once, which makes the wave wait for
+# every load it has in flight; the attention takes its next work item that
+# way while its prefetched blocks are loading.
+DMS_DEVICE = ["-Xarch_device", "-mllvm=-amdgpu-atomic-optimizer-strategy=None"]
+
 
 def _run(cmd):
     print("+", " ".join(cmd), flush=True)
@@ -50,7 +56,7 @@ def _run(cmd):
 
 def build_dms(out: str = LIB, extra=()):
     tmp = out + ".tmp"
-    _run([hipcc(), *COMMON, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    _run([hipcc(), *COMMON, *DMS_DEVICE, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
           os.path.join(CSRC, "dms_kernels.hip"), os.path.join(CSRC, "dms_runtime.cpp"), "-o", tmp])
     os.replace(tmp, out)
     return out

@@ -12,14 +12,14 @@ constexpr int kMaxGroup = 16;      // query heads per KV head held by one MFMA t
 constexpr int kMaxItemBlocks = 512;  // blocks per attention work item (128 per wave)
 constexpr int kMaxTargetItems = 4096;  // cap on the split plan's target item count
 constexpr int kWavesPerWG = 4;     // waves per work-group (attention work item, append, reduce)
+constexpr int kPlanLdsUnits = 4096;  // units up to which the attention keeps its plan in LDS
 
 // Device-side counters (one 64-byte line).
 struct Counters {
   unsigned long long bump;              // next free pool block (may overshoot on exhaustion)
   unsigned long long live_token_steps;  // sum of live tokens after each append call
   int sticky_error;                     // first device-detected dms_status, else 0
-  int next_item;                        // attention work items handed out past the grid
-  int pad[10];
+  int pad[11];
 };
 
 // Byte offsets of every region inside the caller's workspace.  The workspace

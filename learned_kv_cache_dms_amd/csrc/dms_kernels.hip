@@ -83,6 +83,12 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
+__device__ __forceinline__ long long wave_sum_ll(long long x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -122,7 +128,6 @@ __global__ void init_kernel(Dev p) {
     p.ctr->bump = 0;
     p.ctr->live_token_steps = 0;
     p.ctr->sticky_error = 0;
-    p.ctr->next_item = 0;
   }
 }
 
@@ -269,45 +274,93 @@ __device__ __forceinline__ int block_sum_1024(int x, int* s_tmp) {
   return t;
 }
 
-// One work-group of 1024 threads per (sequence, KV head): counts the tokens
-// visible at the last prompt position, reserves their blocks with one
-// atomic, assigns slots in position order and fills block table, slot
-// positions, masks and the pending-eviction ring.
-__global__ __launch_bounds__(1024) void prefill_scan_kernel(Dev p, const float* __restrict__ logit,
-                                                            int32_t max_len, int32_t b0, PromptLens lens) {
+// Prefill allocates in three launches, so that each unit's blocks are one
+// contiguous run of the pool and the runs follow unit order: the attention
+// streams many units at once, and runs at regularly spaced addresses spread
+// its concurrent reads evenly over the memory channels (runs placed in
+// arbitrary order were measured about 4 % slower).
+
+// One work-group of 1024 threads per (sequence, KV head): n[u] = the tokens
+// visible at the last prompt position.
+__global__ __launch_bounds__(1024) void prefill_count_kernel(Dev p, const float* __restrict__ logit,
+                                                             int32_t max_len, int32_t b0, PromptLens lens) {
   __shared__ int s_tmp[16];
+  const int u = b0 * p.Hkv + blockIdx.x;
+  const int P = lens.v[blockIdx.x / p.Hkv];
+  const int w = p.R - 1;
+  const float* lg = logit + (int64_t)u * max_len;
+  int cnt = 0;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) {
+    const bool alpha = lg[i] > 0.0f;
+    cnt += (!alpha || (P - 1 - i) <= w) ? 1 : 0;
+  }
+  const int n = block_sum_1024(cnt, s_tmp);
+  if (threadIdx.x == 0) p.n[u] = n;
+}
+
+// One work-group of 1024 threads: base[u] = first pool block of unit u, an
+// exclusive scan of the units' block counts in unit order after one atomic
+// reservation of them all.  A unit whose run does not fit in the pool gets
+// no blocks and no tokens, and sets the sticky error.
+__global__ __launch_bounds__(1024) void prefill_alloc_kernel(Dev p, int32_t* __restrict__ base) {
+  __shared__ long long s_sum[16];
+  __shared__ int s_wave[16];
+  __shared__ long long s_b0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  long long t = 0;
+  for (int u = tid; u < p.U; u += blockDim.x) t += (p.n[u] + 15) >> 4;
+  t = wave_sum_ll(t);
+  if (lane == 0) s_sum[wave] = t;
+  __syncthreads();
+  if (tid == 0) {
+    long long tot = 0;
+    for (int i = 0; i < nw; ++i) tot += s_sum[i];
+    s_b0 = tot > 0 ? (long long)atomicAdd(&p.ctr->bump, (unsigned long long)tot) : 0;
+  }
+  __syncthreads();
+  long long running = s_b0;
+  for (int c0 = 0; c0 < p.U; c0 += blockDim.x) {
+    const int u = c0 + tid;
+    const int nb = u < p.U ? (p.n[u] + 15) >> 4 : 0;
+    const int incl = wave_incl_scan_i(nb, lane);
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int i = 0; i < nw; ++i) {
+      const int y = s_wave[i];
+      if (i < wave) before += y;
+      total += y;
+    }
+    const long long start = running + before + incl - nb;
+    if (u < p.U) {
+      if (start + nb > p.pool_blocks) {
+        p.n[u] = 0;
+        base[u] = 0;
+        atomicCAS(&p.ctr->sticky_error, 0, kErrOutOfBlocks);
+      } else {
+        base[u] = (int32_t)start;
+      }
+    }
+    running += total;
+    __syncthreads();  // s_wave is reused by the next chunk
+  }
+}
+
+// One work-group of 1024 threads per (sequence, KV head): assigns the
+// visible tokens slots 0 .. n-1 in position order and fills block table,
+// slot positions, masks and the pending-eviction ring.
+__global__ __launch_bounds__(1024) void prefill_scan_kernel(Dev p, const float* __restrict__ logit,
+                                                            int32_t max_len, int32_t b0, PromptLens lens,
+                                                            const int32_t* __restrict__ bases) {
   __shared__ int s_wave_pre[16];
-  __shared__ long long s_base;
-  __shared__ int s_n;
   const int u = b0 * p.Hkv + blockIdx.x;
   const int P = lens.v[blockIdx.x / p.Hkv];
   const int w = p.R - 1;
   const float* lg = logit + (int64_t)u * max_len;
   int32_t* ring = p.ring + (int64_t)u * p.R;
   for (int i = threadIdx.x; i < p.R; i += blockDim.x) ring[i] = -1;
-
-  int cnt = 0;
-  for (int i = threadIdx.x; i < P; i += blockDim.x) {
-    const bool alpha = lg[i] > 0.0f;
-    cnt += (!alpha || (P - 1 - i) <= w) ? 1 : 0;
-  }
-  int n = block_sum_1024(cnt, s_tmp);
-  if (threadIdx.x == 0) {
-    long long base = 0;
-    const int nb = (n + 15) >> 4;
-    if (nb > 0) {
-      base = (long long)atomicAdd(&p.ctr->bump, (unsigned long long)nb);
-      if (base + nb > p.pool_blocks) {
-        atomicCAS(&p.ctr->sticky_error, 0, kErrOutOfBlocks);
-        n = 0;
-      }
-    }
-    s_base = base;
-    s_n = n;
-  }
-  __syncthreads();
-  n = s_n;
-  const long long base = s_base;
+  const int n = p.n[u];
+  const long long base = bases[u];
   const int nb = (n + 15) >> 4;
   int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
   for (int j = threadIdx.x; j < nb; j += blockDim.x) {
@@ -345,10 +398,7 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(Dev p, const float* 
       running += total;
     }
   }
-  if (threadIdx.x == 0) {
-    p.n[u] = n;
-    p.pos[u] = P;
-  }
+  if (threadIdx.x == 0) p.pos[u] = P;
 }
 
 // Gathers the visible rows of the dense prompt into the unit's blocks, in
@@ -419,6 +469,7 @@ __global__ __launch_bounds__(256) void prefill_scatter_kernel(Dev p, const uint8
 
 struct Item {
   int u, k, items, base, nblk;
+  int tail;  // live slots of the unit's last block, 0 when it is full
 };
 
 // Work plan, computed redundantly by every wave from the live counts n[]:
@@ -429,9 +480,12 @@ struct Item {
 // about the same size.  Items are numbered unit-major.
 __device__ __forceinline__ int unit_items(int nb, long long tot, int target, int max_splits) {
   if (nb <= 0) return 0;
-  const long long want = ((long long)nb * target * 2 + tot) / (2 * tot);  // round(nb * target / tot)
+  // round(nb * target / tot) in double: nb <= tot and target <= kMaxTargetItems keep
+  // the quotient below 2^13, where a double quotient of these integers (exact
+  // below 2^53) is never rounded across an integer, so the floor is exact.
+  const double want = floor(((double)nb * target * 2.0 + (double)tot) / (2.0 * (double)tot));
   const int lo = (nb + kMaxItemBlocks - 1) / kMaxItemBlocks;
-  return (int)min((long long)max_splits, max((long long)lo, want));
+  return min(max_splits, max(lo, (int)want));
 }
 
 __device__ __forceinline__ long long plan_blocks(const Dev& p, int lane) {
@@ -443,6 +497,102 @@ __device__ __forceinline__ long long plan_blocks(const Dev& p, int lane) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
   return max(1LL, tot);
+}
+
+// The plan in LDS (units <= kPlanLdsUnits): n[u] = live slots of unit u and
+// start[u] = items of the units before u (start[U] = all items).  Built once
+// per work-group from n[], which is read in one round of loads.
+struct PlanLds {
+  int start[kPlanLdsUnits + 1];
+  int n[kPlanLdsUnits];
+  long long wsum[kWavesPerWG];
+  int wtot[kWavesPerWG];
+};
+
+// Work-group-wide (256 threads); ends with a barrier.  n[] is read with
+// coalesced loads (unit u by thread u % 256); thread t then scans the
+// ceil(U / 256) units from t * ceil(U / 256) on.
+__device__ void plan_build_lds(const Dev& p, PlanLds& pl) {
+  constexpr int kThreads = 64 * kWavesPerWG;
+  constexpr int kPer = kPlanLdsUnits / kThreads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int U = p.U;
+  // Unconditional loads with clamped indices, so that they all issue before
+  // the first wait.
+  int x[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) x[k] = p.n[min(tid + kThreads * k, U - 1)];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int u = tid + kThreads * k;
+    if (u < U) pl.n[u] = x[k];
+  }
+  __syncthreads();
+  const int per = (U + kThreads - 1) / kThreads;  // <= kPer
+  const int u0 = tid * per;
+  int nb[kPer];
+  int s = 0;  // <= 16 units x 2^20 blocks
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    nb[k] = (k < per && u0 + k < U) ? (pl.n[u0 + k] + 15) >> 4 : 0;
+    s += nb[k];
+  }
+  const long long sw = wave_sum_ll((long long)s);
+  if (lane == 0) pl.wsum[wave] = sw;
+  __syncthreads();
+  long long tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerWG; ++w) tot += pl.wsum[w];
+  tot = max(1LL, tot);
+  int cnt[kPer];
+  int c = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    cnt[k] = unit_items(nb[k], tot, p.target_items, p.max_splits);
+    c += cnt[k];
+  }
+  const int incl = wave_incl_scan_i(c, lane);
+  if (lane == 63) pl.wtot[wave] = incl;
+  __syncthreads();
+  int run = incl - c;
+  for (int w = 0; w < wave; ++w) run += pl.wtot[w];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    if (k < per && u0 + k < U) pl.start[u0 + k] = run;
+    run += cnt[k];
+  }
+  if (tid == kThreads - 1) pl.start[U] = run;  // the last thread's running sum is the total
+  __syncthreads();
+}
+
+// Finds work item `item` in the LDS plan; false when item >= the total.  The
+// unit is the last u with start[u] <= item, found by a 64-way search (two
+// rounds for 4096 units).
+__device__ __forceinline__ bool plan_lookup_lds(const PlanLds& pl, int U, int item, int lane, Item& it) {
+  // readfirstlane: the compiler does not know an LDS value is uniform, and a
+  // branch on it would make every item value a per-lane (vector) value
+  if (item >= __builtin_amdgcn_readfirstlane(pl.start[U])) return false;
+  int lo = 0, len = U;
+  while (len > 64) {
+    const int step = (len + 63) >> 6;
+    const int off = lane * step;
+    const int v = off < len ? pl.start[lo + off] : 0x7fffffff;
+    const unsigned long long bal = __ballot(v <= item);  // non-empty: start[lo] <= item
+    const int k = 63 - __clzll((long long)bal);
+    lo += k * step;
+    len = min(step, len - k * step);
+  }
+  const int v = lane < len ? pl.start[lo + lane] : 0x7fffffff;
+  const unsigned long long bal = __ballot(v <= item);
+  const int u = __builtin_amdgcn_readfirstlane(lo + 63 - __clzll((long long)bal));
+  it.u = u;
+  it.base = __builtin_amdgcn_readfirstlane(pl.start[u]);
+  it.items = __builtin_amdgcn_readfirstlane(pl.start[u + 1]) - it.base;
+  const int n = __builtin_amdgcn_readfirstlane(pl.n[u]);
+  it.nblk = (n + 15) >> 4;
+  it.tail = n & 15;
+  it.k = item - it.base;
+  return true;
 }
 
 // Position of a search through the plan: units before b0 hold `running` items.
@@ -457,9 +607,10 @@ __device__ __forceinline__ bool plan_find(const Dev& p, int lane, long long tot,
                                           PlanCursor& cur) {
   for (; cur.b0 < p.U && cur.running <= item; cur.b0 += 64) {
     const int uu = cur.b0 + lane;
-    int nb = 0, cnt = 0;
+    int nb = 0, cnt = 0, nn = 0;
     if (uu < p.U) {
-      nb = (p.n[uu] + 15) >> 4;
+      nn = p.n[uu];
+      nb = (nn + 15) >> 4;
       cnt = unit_items(nb, tot, p.target_items, p.max_splits);
     }
     const int incl = wave_incl_scan_i(cnt, lane);
@@ -471,6 +622,7 @@ __device__ __forceinline__ bool plan_find(const Dev& p, int lane, long long tot,
       it.base = __builtin_amdgcn_readlane(start, src);
       it.items = __builtin_amdgcn_readlane(cnt, src);
       it.nblk = __builtin_amdgcn_readlane(nb, src);
+      it.tail = __builtin_amdgcn_readlane(nn, src) & 15;
       it.k = item - it.base;
       return true;  // the cursor stays on this group: later items may fall in it
     }
@@ -563,24 +715,247 @@ __device__ __forceinline__ void attend_block(const Frag<ES, D>& f, const u32x4 (
   }
 }
 
-// Split-K decode attention.  A work item is a chunk of one (sequence, KV
+// Split-K decode attention.  A work item is a run of one (sequence, KV
 // head)'s blocks, processed by one work-group of 4 waves: wave w takes the
-// chunk's blocks w, w+4, w+8, ... so the work-group streams one contiguous
-// run.  The waves' softmax states are merged through LDS; a unit held by a
-// single work item writes its output here, otherwise the merged partial goes
-// to reduce_kernel.
+// run's blocks w, w+4, w+8, ... so the work-group streams one contiguous run.
+// The waves' softmax states are merged through LDS; a unit held by a single
+// work item writes its output there, otherwise the merged partial goes to
+// reduce_kernel.
+//
+// The loads do not stop at item boundaries.  While a wave computes item A it
+// already holds the block ids of its next item B, and the loads that run past
+// A's last block fetch B's first two blocks; the LDS merge of A overlaps
+// them.
 template <int ES, int D>
 struct AttnShared {
   f32x4 o[kWavesPerWG][Geo<ES, D>::kTiles][64];
   float m[kWavesPerWG][16], l[kWavesPerWG][16];
-  int next;
+  u32x4 q[2][Geo<ES, D>::kChunks][64];  // Q fragments of the current and the next item
+};
+
+// One work item as one wave sees it.  Block ids are read through the scalar
+// cache (waiting for a scalar load never waits for the vector loads in
+// flight): the first two when the item is set up, one item ahead, and the
+// rest inside the block loop, one iteration ahead.
+struct WaveItem {
+  int u;         // (sequence, KV head) unit
+  int nblk;      // the unit's blocks
+  int tail;      // live slots of the unit's last block, 0 when it is full
+  int pidx;      // partial slot of the item, or -1 when it is the unit's only item
+  int j0;        // the unit's logical block of this wave's block 0 (jb + wave)
+  int cnt;       // this wave's blocks: the unit's blocks j0 + 4i, i < cnt
+  int vs;        // visit stride: the wave's i-th load is its block (i * vs) mod cnt
+  int pf0, pf1;  // pool ids of the first two blocks visited (pool block 0 if absent)
+};
+
+// A load of a uniform address that no kernel writes while this one runs, read
+// through the scalar cache (constant address space).
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ __forceinline__ int scalar_load(const int32_t* a) { return *(const_i32*)(uintptr_t)a; }
+
+__device__ __forceinline__ int padded3(int c) { return (c + 2) / 3 * 3; }
+
+// Visit order.  Every work-group streams its runs at the same pace, so if
+// the waves walked their blocks in address order, the addresses read at any
+// moment would be the runs' start addresses shifted by a common offset: how
+// evenly they spread over the memory channels would be fixed by where the
+// runs happen to start, for the whole launch.  Walking each wave's blocks at
+// a stride coprime to their count keeps those offsets changing (measured:
+// about 4 % faster on prefilled caches, as fast as the best start layouts).
+__device__ __forceinline__ int visit_stride(int cnt) {
+  if (cnt <= 1) return 0;
+  const int a = (cnt % 7) ? 7 : ((cnt % 11) ? 11 : 13);  // cnt <= 128 < 7 * 11 * 13
+  return a % cnt;
+}
+
+// Position in the wave's block list of its i-th visit (i < cnt).
+__device__ __forceinline__ int visit_pos(const WaveItem& w, int i) {
+  return (int)((unsigned)(i * w.vs) % (unsigned)w.cnt);
+}
+
+// Pool id of this wave's i-th visited block, i clamped to cnt - 1 (cnt >= 1).
+__device__ __forceinline__ int wave_item_id(const int32_t* __restrict__ btab, int max_blocks, const WaveItem& w,
+                                            int i) {
+  const int j = __builtin_amdgcn_readfirstlane(w.j0 + kWavesPerWG * visit_pos(w, min(i, w.cnt - 1)));
+  return scalar_load(btab + (int64_t)w.u * max_blocks + j);
+}
+
+// Sets up item `it` for this wave; the first wave of the unit's first item
+// also records the unit's item range for reduce_kernel.
+__device__ __forceinline__ void wave_item_setup(const Dev& p, const int32_t* __restrict__ btab, int wave, int lane,
+                                                const Item& it, WaveItem& w) {
+  // k < items <= max_splits <= 2^11 and nblk <= 2^20: the products fit 32 bits unsigned
+  const int jb = (int)((unsigned)it.k * (unsigned)it.nblk / (unsigned)it.items);
+  const int je = (int)((unsigned)(it.k + 1) * (unsigned)it.nblk / (unsigned)it.items);
+  // readfirstlane: all of these are uniform, and must live in scalar
+  // registers (the division is expanded with vector instructions), or the
+  // block-id loads computed from them would be vector loads
+  w.u = __builtin_amdgcn_readfirstlane(it.u);
+  w.nblk = __builtin_amdgcn_readfirstlane(it.nblk);
+  w.tail = __builtin_amdgcn_readfirstlane(it.tail);
+  w.pidx = __builtin_amdgcn_readfirstlane(it.items == 1 ? -1 : it.base + it.k);
+  w.j0 = __builtin_amdgcn_readfirstlane(jb + wave);
+  w.cnt = __builtin_amdgcn_readfirstlane(max(0, (je - jb - wave + kWavesPerWG - 1) / kWavesPerWG));
+  w.vs = visit_stride(w.cnt);
+  w.pf0 = w.cnt > 0 ? wave_item_id(btab, p.max_blocks, w, 0) : 0;
+  w.pf1 = w.cnt > 1 ? wave_item_id(btab, p.max_blocks, w, 1) : 0;
+  if (it.k == 0 && it.nblk > 0 && wave == 0 && lane == 0) {
+    p.plan[2 * it.u] = it.base;
+    p.plan[2 * it.u + 1] = it.items;
+  }
+}
+
+// An empty item on unit 0: stands for "no next item", so that the loads that
+// would start the next item stay unconditional.
+__device__ __forceinline__ void wave_item_none(WaveItem& w) {
+  w.u = 0;
+  w.nblk = 0;
+  w.tail = 0;
+  w.pidx = -1;
+  w.j0 = 0;
+  w.cnt = 0;
+  w.vs = 0;
+  w.pf0 = 0;
+  w.pf1 = 0;
+}
+
+// Live-slot mask of this wave's i-th visited block of item w.  Live slots are
+// always the dense prefix [0, n) of the unit's slots (an append reuses the
+// slot it retires or takes slot n; prefill assigns 0 .. n-1), so only the
+// unit's last block can be partly filled.
+__device__ __forceinline__ uint32_t wave_item_mask(const WaveItem& w, int i) {
+  const int j = w.j0 + kWavesPerWG * visit_pos(w, i);
+  return (j == w.nblk - 1 && w.tail != 0) ? ((1u << w.tail) - 1u) : 0xffffu;
+}
+
+// Q fragment (B operand of S = K Q^T): head g = lane % 16 of the item's
+// group, the channels this lane's K fragment elements carry.  It goes through
+// LDS: wave w loads chunks w, w+4, ... of the next item's fragment while the
+// current item streams, stores them before the merge, and every wave reads
+// the whole fragment after it.  No wait for a K/V load is ever also a wait
+// for Q, nor the other way round.
+template <int ES, int D>
+struct QPart {
+  static constexpr int kN = (Geo<ES, D>::kChunks + kWavesPerWG - 1) / kWavesPerWG;
+  u32x4 v[kN];
 };
 
 template <int ES, int D>
-__device__ __forceinline__ void attention_item(const Dev& p, const int32_t* __restrict__ btab,
-                                               const uint32_t* __restrict__ bmask, const uint8_t* __restrict__ q,
-                                               float* __restrict__ out, const Item& it, int lane, int wave,
-                                               AttnShared<ES, D>& sh) {
+__device__ __forceinline__ void load_q_part(const Dev& p, const uint8_t* __restrict__ q, int u, int lane,
+                                            int wave, QPart<ES, D>& part) {
+  using G = Geo<ES, D>;
+  const int b = u / p.Hkv, h = u - b * p.Hkv;
+  const int g = lane & 15;
+  // Columns g >= G (unused heads) load head 0 of the group: every column is
+  // an independent softmax, and those columns are never written out.
+  const uint8_t* qrow = q + ((int64_t)b * p.Hq + h * p.G + (g < p.G ? g : 0)) * D * ES;
+#pragma unroll
+  for (int j = 0; j < QPart<ES, D>::kN; ++j) {
+    const int c = min(wave + kWavesPerWG * j, G::kChunks - 1);
+    part.v[j] = *(const u32x4*)(qrow + (c * 4 * G::kE + G::kE * (lane >> 4)) * ES);
+  }
+}
+
+template <int ES, int D>
+__device__ __forceinline__ void store_q_part(AttnShared<ES, D>& sh, int buf, int lane, int wave,
+                                             const QPart<ES, D>& part) {
+  // Clamped like the load: waves past the last chunk store that chunk again,
+  // with the same values (an unconditional store keeps the load waits exact).
+#pragma unroll
+  for (int j = 0; j < QPart<ES, D>::kN; ++j)
+    sh.q[buf][min(wave + kWavesPerWG * j, Geo<ES, D>::kChunks - 1)][lane] = part.v[j];
+}
+
+template <int ES, int D>
+__device__ __forceinline__ void read_q(const AttnShared<ES, D>& sh, int buf, int lane,
+                                       u32x4 (&qf)[Geo<ES, D>::kChunks]) {
+#pragma unroll
+  for (int c = 0; c < Geo<ES, D>::kChunks; ++c) qf[c] = sh.q[buf][c][lane];
+}
+
+// The item lookup: the LDS plan, or for very many units a scan of n[].
+struct Planner {
+  bool lds;
+  long long tot;
+  PlanCursor cur;
+};
+
+__device__ __forceinline__ bool find_item(const Dev& p, const PlanLds& pl, Planner& pn, int item, int lane,
+                                          Item& it) {
+  return pn.lds ? plan_lookup_lds(pl, p.U, item, lane, it) : plan_find(p, lane, pn.tot, item, it, pn.cur);
+}
+
+// Computes this wave's blocks of item A.  The wave reads one stream of
+// blocks: A's, each item padded to a multiple of three blocks, then B's.
+// The three buffers rotate, so with the padding every item starts with its
+// blocks 0 and 1 in buffers 0 and 1, and ends with B's blocks 0 and 1 loading
+// there.  Padding slots, and stream positions past B, load pool block 0 (any
+// valid address does) and are not computed.  When A has no blocks, buffers 0
+// and 1 were filled before B was known and are loaded again here.
+template <int ES, int D, typename Early>
+__device__ __forceinline__ void run_item(const Dev& p, Frag<ES, D>& f0, Frag<ES, D>& f1, Frag<ES, D>& f2,
+                                         const WaveItem& A, const WaveItem& B,
+                                         const u32x4 (&qf)[Geo<ES, D>::kChunks], int lane, Acc<D>& acc,
+                                         Early&& early) {
+#pragma unroll
+  for (int j = 0; j < Geo<ES, D>::kTiles; ++j) acc.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  acc.m = -INFINITY;
+  acc.l = 0.f;
+  const uint8_t* pool = p.pool;
+  const int64_t BB = p.block_bytes;
+  const float sl2e = p.scale_log2e;
+  const int cnt = A.cnt, cpad = padded3(A.cnt);
+  // Pool id of stream position s, given the id `own` of A's block s when s < cnt.
+  auto stream_id = [&](int s, int own) { return s < cnt ? own : (s == cpad ? B.pf0 : (s == cpad + 1 ? B.pf1 : 0)); };
+  const int32_t* __restrict__ btab = p.btab;
+  auto fetch = [&](Frag<ES, D>& fr, int blk) { load_frag<ES, D>(fr, pool + (int64_t)blk * BB, lane); };
+  // A's ids of the blocks fetched next (scalar-cache hits: the same lines as
+  // blocks 0 and 1)
+  int n2 = 0, n3 = 0, n4 = 0;
+  if (cnt > 0) {
+    n2 = wave_item_id(btab, p.max_blocks, A, 2);
+    n3 = wave_item_id(btab, p.max_blocks, A, 3);
+    n4 = wave_item_id(btab, p.max_blocks, A, 4);
+  }
+  // Blocks i, i+1, i+2 (i a multiple of 3 below cpad, so block i is one of A's).
+  auto body = [&](int i) {
+    const int b2 = stream_id(i + 2, n2), b3 = stream_id(i + 3, n3), b4 = stream_id(i + 4, n4);
+    if (i + 5 < cnt) {  // the next iteration's ids
+      n2 = wave_item_id(btab, p.max_blocks, A, i + 5);
+      n3 = wave_item_id(btab, p.max_blocks, A, i + 6);
+      n4 = wave_item_id(btab, p.max_blocks, A, i + 7);
+    }
+    fetch(f2, b2);
+    attend_block<ES, D>(f0, qf, wave_item_mask(A, i), lane, sl2e, acc);
+    fetch(f0, b3);
+    if (i + 1 < cnt) attend_block<ES, D>(f1, qf, wave_item_mask(A, i + 1), lane, sl2e, acc);
+    fetch(f1, b4);
+    if (i + 2 < cnt) attend_block<ES, D>(f2, qf, wave_item_mask(A, i + 2), lane, sl2e, acc);
+  };
+  // The first group is peeled: it is the one that waits for the item's Q
+  // (loaded after blocks 0 and 1), and keeping that wait out of the loop
+  // keeps the loop's own load waits exact.
+  // `early` consumes values loaded before this function: it runs right after
+  // the first group of loads, where the compiler counts the loads issued
+  // since exactly (after a loop it would assume none and wait for all).
+  if (cpad == 0) {
+    fetch(f0, B.pf0);
+    fetch(f1, B.pf1);
+    early();
+  } else {
+    body(0);
+    early();
+    for (int i = 3; i < cpad; i += 3) body(i);
+  }
+}
+
+// Merges the four waves' states of item `it` through LDS and writes the
+// output (single-item unit) or the item's partial.  Contains two work-group
+// barriers; LDS stores made before the call (the next item's Q) are visible to
+// every wave on return.
+template <int ES, int D>
+__device__ __forceinline__ void merge_item(const Dev& p, float* __restrict__ out, const WaveItem& it,
+                                           const Acc<D>& acc, int lane, int wave, AttnShared<ES, D>& sh) {
   using G = Geo<ES, D>;
   constexpr int kW = kWavesPerWG;
   constexpr int kTilesPerWave = (G::kTiles + kW - 1) / kW;
@@ -590,79 +965,9 @@ __device__ __forceinline__ void attention_item(const Dev& p, const int32_t* __re
   const bool gvalid = g < p.G;
   const int hq = h * p.G + g;
 
-  // Q fragment (B operand of S = K Q^T): head g, the channels this lane's
-  // K fragment elements carry.
-  u32x4 qf[G::kChunks];
-  {
-    const uint8_t* qrow = q + ((int64_t)b * p.Hq + (gvalid ? hq : 0)) * D * ES;
-#pragma unroll
-    for (int c = 0; c < G::kChunks; ++c) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qf[c] = gvalid ? *(const u32x4*)(qrow + (c * 4 * G::kE + G::kE * (lane >> 4)) * ES) : z;
-    }
-  }
-
-  const int jb = (int)(((long long)it.k * it.nblk) / it.items);
-  const int je = (int)(((long long)(it.k + 1) * it.nblk) / it.items);
-  // this wave's blocks: jb + wave + kW * i, i < cnt
-  const int cnt = max(0, (je - jb - wave + kW - 1) / kW);
-
-  Acc<D> acc;
-#pragma unroll
-  for (int j = 0; j < G::kTiles; ++j) acc.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  acc.m = -INFINITY;
-  acc.l = 0.f;
-
-  if (cnt > 0) {
-    // This wave's block ids and live masks (at most 2 x 64, the plan keeps
-    // items within kMaxItemBlocks) are loaded once into lane vectors and read
-    // with readlane, so the K/V pipeline never waits on a dependent load.
-    const int32_t* bt = btab + (int64_t)u * p.max_blocks + jb + wave;
-    int id0 = 0, id1 = 0;
-    uint32_t mk0 = 0u, mk1 = 0u;
-    if (lane < cnt) id0 = bt[(int64_t)lane * kW];
-    if (lane + 64 < cnt) id1 = bt[(int64_t)(lane + 64) * kW];
-    if (lane < cnt) mk0 = bmask[id0];
-    if (lane + 64 < cnt) mk1 = bmask[id1];
-    const float sl2e = p.scale_log2e;
-    const uint8_t* pool = p.pool;
-    const int64_t BB = p.block_bytes;
-    // Three-block rotation: two blocks load while one is computed.  Loads
-    // are unconditional (indices past the end are clamped to the last block,
-    // just read) so the load counter analysis stays exact in the loop.  The
-    // live mask of block i is read only when the block is computed, so the
-    // K/V loads never wait for the mask loads.
-    Frag<ES, D> f0, f1, f2;
-    const int last = cnt - 1;
-    auto fetch = [&](Frag<ES, D>& f, int i) {
-      const int ic = min(i, last);
-      const int blk = ic < 64 ? __builtin_amdgcn_readlane(id0, ic) : __builtin_amdgcn_readlane(id1, ic - 64);
-      load_frag<ES, D>(f, pool + (int64_t)blk * BB, lane);
-    };
-    auto mask_of = [&](int i) -> uint32_t {
-      return (uint32_t)(i < 64 ? __builtin_amdgcn_readlane((int)mk0, i) : __builtin_amdgcn_readlane((int)mk1, i - 64));
-    };
-    fetch(f0, 0);
-    fetch(f1, 1);
-    int i = 0;
-    for (; i + 2 < cnt; i += 3) {
-      fetch(f2, i + 2);
-      attend_block<ES, D>(f0, qf, mask_of(i), lane, sl2e, acc);
-      fetch(f0, i + 3);
-      attend_block<ES, D>(f1, qf, mask_of(i + 1), lane, sl2e, acc);
-      fetch(f1, i + 4);
-      attend_block<ES, D>(f2, qf, mask_of(i + 2), lane, sl2e, acc);
-    }
-    // 0, 1 or 2 blocks remain, already loaded in f0 and f1
-    if (i < cnt) attend_block<ES, D>(f0, qf, mask_of(i), lane, sl2e, acc);
-    if (i + 1 < cnt) attend_block<ES, D>(f1, qf, mask_of(i + 1), lane, sl2e, acc);
-  }
-
   // lane-local l holds 4 of the 16 tokens per block; add the four groups
   float lt = acc.l + __shfl_xor(acc.l, 16);
   lt = lt + __shfl_xor(lt, 32);
-
-  // merge the waves' states through LDS; wave w finishes tiles w*TPW...
   if (lane < 16) {
     sh.m[wave][lane] = acc.m;
     sh.l[wave][lane] = lt;
@@ -681,6 +986,7 @@ __device__ __forceinline__ void attention_item(const Dev& p, const int32_t* __re
     wt[w] = exp2_fast(sh.m[w][g] - Mr);
     L += wt[w] * sh.l[w][g];
   }
+  // wave w finishes tiles w * kTilesPerWave ...
   const int j0 = wave * kTilesPerWave;
   f32x4 O[kTilesPerWave];
 #pragma unroll
@@ -691,11 +997,8 @@ __device__ __forceinline__ void attention_item(const Dev& p, const int32_t* __re
       for (int w = 0; w < kW; ++w) O[t] += wt[w] * sh.o[w][j0 + t][lane];
     }
   }
-  if (it.k == 0 && wave == 0 && lane == 0) {  // read by reduce_kernel, for every unit
-    p.plan[2 * u] = it.base;
-    p.plan[2 * u + 1] = it.items;
-  }
-  if (it.items == 1) {
+  __syncthreads();  // the LDS of this item may be overwritten after this
+  if (it.pidx < 0) {
     if (gvalid) {
       float* orow = out + ((int64_t)b * p.Hq + hq) * D + 4 * (lane >> 4);
       const float inv = 1.0f / L;
@@ -703,11 +1006,11 @@ __device__ __forceinline__ void attention_item(const Dev& p, const int32_t* __re
       for (int t = 0; t < kTilesPerWave; ++t)
         if (j0 + t < G::kTiles) *(f32x4*)(orow + 16 * (j0 + t)) = O[t] * inv;
     }
-    return;  // returns from this item only
+    return;
   }
   // several items: publish the merged partial; reduce_kernel combines them
   const int IF = p.item_floats;
-  float* mine = p.part + (int64_t)(it.base + it.k) * IF;
+  float* mine = p.part + (int64_t)it.pidx * IF;
   if (gvalid) {
     if (wave == 0 && lane < 16) {
       mine[g] = M;
@@ -719,28 +1022,83 @@ __device__ __forceinline__ void attention_item(const Dev& p, const int32_t* __re
   }
 }
 
-// Persistent launch: one work-group per resident slot.  Its first item is its
-// id; further items come from an atomic counter (reset by reduce_kernel, which
-// runs after this kernel on the same stream), so no work-group is launched
-// only to find it has nothing to do.
+// Persistent launch: one work-group per resident slot; work-group b takes
+// items b, b + G, b + 2G, ... (G = grid size).  The plan makes items of about
+// equal size, so the static assignment is balanced, and the next item is
+// known in advance: its block ids are read while the item before it is
+// computed.
+//
+// The loop is written so that the compiler's load-counter waits stay exact:
+// every load is unconditional (an absent next item is an empty one on unit
+// 0), block ids come through the scalar cache, and values loaded before an
+// item's block loop are consumed right after its first group of loads.  A
+// wait for one value then never drains the K/V blocks in flight behind it.
 template <int ES, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2 : 1))) void attention_kernel(
-    Dev p, const int32_t* __restrict__ btab,
-                                                        const uint32_t* __restrict__ bmask,
-                                                        const uint8_t* __restrict__ q, float* __restrict__ out) {
+    Dev p, const int32_t* __restrict__ btab, const uint8_t* __restrict__ q, float* __restrict__ out) {
+  using G = Geo<ES, D>;
   __shared__ AttnShared<ES, D> sh;
+  __shared__ PlanLds pl;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const long long tot = plan_blocks(p, lane);
-  PlanCursor cur;
+  Planner pn;
+  pn.lds = p.U <= kPlanLdsUnits;
+  pn.tot = 0;
+  if (pn.lds)
+    plan_build_lds(p, pl);
+  else
+    pn.tot = plan_blocks(p, lane);
+
+  const int grid = (int)gridDim.x;
   int item = blockIdx.x;
-  for (;;) {
+  WaveItem W0, W1;
+  {
     Item it;
-    if (!plan_find(p, lane, tot, item, it, cur)) break;  // uniform over the work-group
-    attention_item<ES, D>(p, btab, bmask, q, out, it, lane, wave, sh);
-    if (threadIdx.x == 0) sh.next = (int)gridDim.x + atomicAdd(&p.ctr->next_item, 1);
-    __syncthreads();  // publishes sh.next; the LDS of this item is free again
-    item = sh.next;
+    if (!find_item(p, pl, pn, item, lane, it)) return;  // uniform over the work-group
+    wave_item_setup(p, btab, wave, lane, it, W0);
+  }
+  bool has_next;
+  {
+    Item it;
+    has_next = find_item(p, pl, pn, item + grid, lane, it);
+    if (has_next)
+      wave_item_setup(p, btab, wave, lane, it, W1);
+    else
+      wave_item_none(W1);
+  }
+  Frag<ES, D> f0, f1, f2;
+  load_frag<ES, D>(f0, p.pool + (int64_t)W0.pf0 * p.block_bytes, lane);
+  load_frag<ES, D>(f1, p.pool + (int64_t)W0.pf1 * p.block_bytes, lane);
+  {
+    QPart<ES, D> q0;
+    load_q_part<ES, D>(p, q, W0.u, lane, wave, q0);
+    store_q_part<ES, D>(sh, 0, lane, wave, q0);
+  }
+  __syncthreads();
+  u32x4 qf[G::kChunks];
+  read_q<ES, D>(sh, 0, lane, qf);
+  int qbuf = 0;
+
+  // W0 is the item being computed, W1 the next one (both held in scalar
+  // registers, so moving W1 into W0 waits for no load).
+  for (;;) {
+    QPart<ES, D> qn;
+    load_q_part<ES, D>(p, q, W1.u, lane, wave, qn);  // W1's Q, stored to LDS early in W0's block loop
+    Acc<D> acc;  // set by run_item
+    run_item<ES, D>(p, f0, f1, f2, W0, W1, qf, lane, acc,
+                    [&]() { store_q_part<ES, D>(sh, qbuf ^ 1, lane, wave, qn); });
+    merge_item<ES, D>(p, out, W0, acc, lane, wave, sh);
+    if (!has_next) break;
+    qbuf ^= 1;
+    read_q<ES, D>(sh, qbuf, lane, qf);
+    W0 = W1;
+    item += grid;
+    Item it;
+    has_next = find_item(p, pl, pn, item + grid, lane, it);
+    if (has_next)
+      wave_item_setup(p, btab, wave, lane, it, W1);
+    else
+      wave_item_none(W1);
   }
 }
 
@@ -750,7 +1108,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
 // Lane l handles head l % 16 and the channels 16j + 4(l/16) + r.
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(Dev p, float* __restrict__ out) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) p.ctr->next_item = 0;  // attention_kernel has finished
   const int lane = threadIdx.x & 63;
   const int u = blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
   if (u >= p.U) return;
@@ -833,12 +1190,23 @@ hipError_t launch_append(const Dev& p, int dtype, int d, const void* k, const vo
 template <int ES, int D>
 static hipError_t prefill_t(const Dev& p, const void* k, const void* v, const float* logit,
                             const int32_t* h_lengths, int32_t max_len, hipStream_t s) {
-  for (int b0 = 0; b0 < p.B; b0 += PromptLens::kMax) {
-    const int nb = std::min(PromptLens::kMax, p.B - b0);
-    PromptLens lens;
-    for (int i = 0; i < nb; ++i) lens.v[i] = h_lengths[b0 + i];
-    const hipError_t e = launch(prefill_scan_kernel, dim3(nb * p.Hkv), dim3(1024), s, p, logit, max_len, b0, lens);
-    if (e != hipSuccess) return e;
+  // The partial area is free between attention calls: it holds the bases.
+  int32_t* bases = (int32_t*)p.part;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int b0 = 0; b0 < p.B; b0 += PromptLens::kMax) {
+      const int nb = std::min(PromptLens::kMax, p.B - b0);
+      PromptLens lens;
+      for (int i = 0; i < nb; ++i) lens.v[i] = h_lengths[b0 + i];
+      const hipError_t e =
+          pass == 0 ? launch(prefill_count_kernel, dim3(nb * p.Hkv), dim3(1024), s, p, logit, max_len, b0, lens)
+                    : launch(prefill_scan_kernel, dim3(nb * p.Hkv), dim3(1024), s, p, logit, max_len, b0, lens,
+                             (const int32_t*)bases);
+      if (e != hipSuccess) return e;
+    }
+    if (pass == 0) {
+      const hipError_t e = launch(prefill_alloc_kernel, dim3(1), dim3(1024), s, p, bases);
+      if (e != hipSuccess) return e;
+    }
   }
   const int ysplit = 8;
   return launch(prefill_scatter_kernel<ES, D>, dim3(p.U, ysplit), dim3(64 * kWavesPerWG), s, p,
@@ -858,7 +1226,7 @@ template <int ES, int D>
 static hipError_t attention_t(const Dev& p, const void* q, float* out, int64_t grid_wgs, hipStream_t s) {
   const int64_t nwg = grid_wgs;
   const hipError_t e = launch(attention_kernel<ES, D>, dim3((unsigned)nwg), dim3(64 * kWavesPerWG), s, p,
-                              (const int32_t*)p.btab, (const uint32_t*)p.blk_mask, (const uint8_t*)q, out);
+                              (const int32_t*)p.btab, (const uint8_t*)q, out);
   if (e != hipSuccess) return e;
   return launch(reduce_kernel<D>, dim3((p.U + kWavesPerWG - 1) / kWavesPerWG), dim3(64 * kWavesPerWG), s, p, out);
 }
