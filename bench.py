@@ -35,12 +35,17 @@ if ROOT not in sys.path:
 
 METRIC = "decode attention tokens/sec + live-KV HBM GB/s (% of peak) at CR=8, 32K ctx"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "learned_kv_cache_dms_amd", "csrc", "dms_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "learned_kv_cache_dms_amd", "csrc", f) for f in ("dms_kernels.hip", "dms_runtime.cpp")]
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the kernels and of the runtime
+    that plans their launches (both decide the traffic of a call)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
