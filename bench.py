@@ -11,8 +11,9 @@ workload is the Qwen-R1-32B-shaped layer: 64 chains at 32768 tokens, 40 query
 
 Prints one JSON line.  `value` is decode-attention tokens per second (batch
 sequences per step); the live-KV bandwidth of the attention launch is in
-`roofline`, timed with HIP events around each dms_decode_attention call (its
-two kernels: attention_kernel and reduce_kernel).  `cpu_baseline` times the
+`roofline`, timed with HIP events around each dms_decode_attention call
+(attention_kernel; reduce_kernel too when some unit is split, which never
+happens at 512 units on 512 resident work-groups).  `cpu_baseline` times the
 CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -252,7 +253,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None if traffic is None else round(traffic),
-            "kernel": "dms_decode_attention = attention_kernel + reduce_kernel",
+            "kernel": "dms_decode_attention = attention_kernel (+ reduce_kernel when a unit is split)",
             "algorithmic_bytes_per_launch": round(live_bytes),
         },
         "cpu_baseline": None,

@@ -9,7 +9,7 @@ namespace dms {
 
 constexpr int kBlockTokens = 16;
 constexpr int kMaxGroup = 16;      // query heads per KV head held by one MFMA tile
-constexpr int kMaxItemBlocks = 512;  // blocks per attention work item (128 per wave)
+constexpr int kMaxItemBlocks = 512;  // blocks per split attention work item (128 per wave)
 constexpr int kMaxTargetItems = 4096;  // cap on the split plan's target item count
 constexpr int kWavesPerWG = 4;     // waves per work-group (attention work item, append, reduce)
 constexpr int kPlanLdsUnits = 4096;  // units up to which the attention keeps its plan in LDS
@@ -49,6 +49,7 @@ struct Dev {
   Counters* ctr;
   float* part;         // [max_items][item_floats] attention partials
   int32_t B, Hq, Hkv, G, R, max_tokens, max_blocks, max_splits, U, item_floats, target_items;
+  int32_t whole_units;  // 1: one work item per unit (never split); no split merge
   int64_t pool_blocks, block_bytes;
   float scale_log2e;   // attention scale times log2(e)
 };

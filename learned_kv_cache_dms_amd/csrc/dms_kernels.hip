@@ -478,8 +478,9 @@ struct Item {
 // (which the host keeps >= ceil(max_blocks / kMaxItemBlocks)); each item
 // holds an equal share of the unit's blocks, so the items of a launch have
 // about the same size.  Items are numbered unit-major.
-__device__ __forceinline__ int unit_items(int nb, long long tot, int target, int max_splits) {
+__device__ __forceinline__ int unit_items(int nb, long long tot, int target, int max_splits, bool whole) {
   if (nb <= 0) return 0;
+  if (whole) return 1;  // at least as many units as work-groups: no split
   // round(nb * target / tot) in double: nb <= tot and target <= kMaxTargetItems keep
   // the quotient below 2^13, where a double quotient of these integers (exact
   // below 2^53) is never rounded across an integer, so the floor is exact.
@@ -548,7 +549,7 @@ __device__ void plan_build_lds(const Dev& p, PlanLds& pl) {
   int c = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    cnt[k] = unit_items(nb[k], tot, p.target_items, p.max_splits);
+    cnt[k] = unit_items(nb[k], tot, p.target_items, p.max_splits, p.whole_units != 0);
     c += cnt[k];
   }
   const int incl = wave_incl_scan_i(c, lane);
@@ -611,7 +612,7 @@ __device__ __forceinline__ bool plan_find(const Dev& p, int lane, long long tot,
     if (uu < p.U) {
       nn = p.n[uu];
       nb = (nn + 15) >> 4;
-      cnt = unit_items(nb, tot, p.target_items, p.max_splits);
+      cnt = unit_items(nb, tot, p.target_items, p.max_splits, p.whole_units != 0);
     }
     const int incl = wave_incl_scan_i(cnt, lane);
     const int start = cur.running + incl - cnt;
@@ -764,13 +765,20 @@ __device__ __forceinline__ int padded3(int c) { return (c + 2) / 3 * 3; }
 // about 4 % faster on prefilled caches, as fast as the best start layouts).
 __device__ __forceinline__ int visit_stride(int cnt) {
   if (cnt <= 1) return 0;
-  const int a = (cnt % 7) ? 7 : ((cnt % 11) ? 11 : 13);  // cnt <= 128 < 7 * 11 * 13
+  // the first of these primes that does not divide cnt (their product exceeds
+  // any block count, so one always qualifies)
+  constexpr int kPrimes[8] = {7, 11, 13, 17, 19, 23, 29, 31};
+  int a = 37;
+  for (int i = 7; i >= 0; --i)
+    if (cnt % kPrimes[i]) a = kPrimes[i];
   return a % cnt;
 }
 
-// Position in the wave's block list of its i-th visit (i < cnt).
+// Position in the wave's block list of its i-th visit (i < cnt).  A unit
+// holds at most 2^31 / 16 blocks (token counts are int32), a wave at most a
+// quarter of them, so i * vs < 2^25 * 37 stays within 32 unsigned bits.
 __device__ __forceinline__ int visit_pos(const WaveItem& w, int i) {
-  return (int)((unsigned)(i * w.vs) % (unsigned)w.cnt);
+  return (int)((unsigned)i * (unsigned)w.vs % (unsigned)w.cnt);
 }
 
 // Pool id of this wave's i-th visited block, i clamped to cnt - 1 (cnt >= 1).
@@ -1052,9 +1060,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
   const int grid = (int)gridDim.x;
   int item = blockIdx.x;
   WaveItem W0, W1;
+  QPart<ES, D> q0;
   {
     Item it;
     if (!find_item(p, pl, pn, item, lane, it)) return;  // uniform over the work-group
+    // Q first: it is stored to LDS below, and a wait for it must not also
+    // wait for the first blocks (loads complete in issue order)
+    load_q_part<ES, D>(p, q, it.u, lane, wave, q0);
     wave_item_setup(p, btab, wave, lane, it, W0);
   }
   bool has_next;
@@ -1069,11 +1081,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
   Frag<ES, D> f0, f1, f2;
   load_frag<ES, D>(f0, p.pool + (int64_t)W0.pf0 * p.block_bytes, lane);
   load_frag<ES, D>(f1, p.pool + (int64_t)W0.pf1 * p.block_bytes, lane);
-  {
-    QPart<ES, D> q0;
-    load_q_part<ES, D>(p, q, W0.u, lane, wave, q0);
-    store_q_part<ES, D>(sh, 0, lane, wave, q0);
-  }
+  store_q_part<ES, D>(sh, 0, lane, wave, q0);
   __syncthreads();
   u32x4 qf[G::kChunks];
   read_q<ES, D>(sh, 0, lane, qf);
@@ -1224,10 +1232,11 @@ hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const v
 
 template <int ES, int D>
 static hipError_t attention_t(const Dev& p, const void* q, float* out, int64_t grid_wgs, hipStream_t s) {
+  // whole_units: no unit is split, so there is nothing for reduce_kernel
   const int64_t nwg = grid_wgs;
   const hipError_t e = launch(attention_kernel<ES, D>, dim3((unsigned)nwg), dim3(64 * kWavesPerWG), s, p,
                               (const int32_t*)p.btab, (const uint8_t*)q, out);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.whole_units) return e;
   return launch(reduce_kernel<D>, dim3((p.U + kWavesPerWG - 1) / kWavesPerWG), dim3(64 * kWavesPerWG), s, p, out);
 }
 

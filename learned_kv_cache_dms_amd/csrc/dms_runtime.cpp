@@ -121,6 +121,7 @@ dms::Dev make_dev(const dms_cache* c) {
   p.U = L.U;
   p.item_floats = L.item_floats;
   p.target_items = c->target_items;
+  p.whole_units = c->L.U >= c->target_items ? 1 : 0;
   p.pool_blocks = L.pool_blocks;
   p.block_bytes = L.block_bytes;
   const float scale = c->cfg.scale == 0.0f ? 1.0f / sqrtf((float)L.d) : c->cfg.scale;
@@ -167,12 +168,12 @@ int dms_cache_create(const dms_config* cfg, void* d_workspace, size_t workspace_
   c->device = dev;
   c->num_cus = prop.multiProcessorCount;
   // Persistent attention grid: as many 4-wave work-groups as fit at once.
-  // The split plan aims at one work item per resident work-group: units are
-  // split only when there are fewer of them than work-groups (or one is much
-  // larger than the average item), so that a call over many similar units
-  // writes no partials and leaves the split merge nothing to do.  (Measured on
-  // 512 equal units and 512 work-groups: one item per unit 193.5 us per
-  // call, two 199 us.)
+  // The split plan aims at one work item per resident work-group.  With at
+  // least as many units as that, every unit is one item (whole-unit mode):
+  // no partials are written and the split-merge launch is skipped.  With
+  // fewer, units are split in proportion to their blocks.  (Measured on 512
+  // equal units and 512 work-groups: one item per unit 193.5 us per call,
+  // two 199 us.)
   const int resident = dms::attention_resident_wgs(cfg->dtype, L.d, c->num_cus);
   c->target_items = std::min(dms::kMaxTargetItems, std::max(8, resident * DMS_SPLIT_ITEMS_PER_RESIDENT / 4));
   c->grid_wgs = std::min<int64_t>(resident, std::min<int64_t>(L.max_items, (int64_t)c->target_items + 2LL * L.U +

@@ -109,6 +109,21 @@ def test_visit_order_strides(blocks):
 
 
 @gpu
+def test_whole_units_long_runs():
+    """512 units (at least one per resident work-group): each unit is one work
+    item, never split, and no split merge runs.  Nothing is evicted (logits
+    far below 0), so each unit holds 8320 tokens = 520 blocks and every wave
+    walks 130 of them (more than 128, with the visit stride of its count).
+    Sampled units at every step against the oracle."""
+    import gpu_util as U
+    wl = _small("bf16-d64-512-units-520-blocks", head_dim=64, batch=64, num_q_heads=8, num_kv_heads=8,
+                window=16, decode_steps=2, prompt_len=520 * 16 - 1, mu_before=[-8.0])
+    units = [(0, 0), (17, 3), (40, 5), (63, 7)]
+    st = U.run_decode(wl, wl.decode_steps, units, _tol(wl))
+    assert st.checks == len(units) * wl.decode_steps
+
+
+@gpu
 @pytest.mark.parametrize("batch", [512, 520], ids=["4096-units", "4160-units"])
 def test_many_units(batch):
     """As many (sequence, KV head) units as the attention's work-group-wide
