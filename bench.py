@@ -3,7 +3,7 @@
 
 One step = one decode step of every sequence of the workload through the C
 ABI: dms_append_step (decide, retire, store) then dms_decode_attention
-(split-K attention over the visible tokens, then the split merge).
+(attention over the visible tokens; a split merge when a unit is split).
 Inputs are synthetic, generated in HBM before the timed region.  The default
 workload is the Qwen-R1-32B-shaped layer: 64 chains at 32768 tokens, 40 query
 / 8 KV heads, head_dim 128, bf16, w = 256, logit mean for CR 4 below position
@@ -17,6 +17,8 @@ happens at 512 units on 512 resident work-groups).  `cpu_baseline` times the
 CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --workload qwen-r1-32b-layer-dense --no-cpu-baseline
+        # the dense baseline (nothing evicted, CR 1) through the same kernels
     python bench.py --calib-copy-bytes N    # plain copy kernel, for counter scaling
 """
 from __future__ import annotations
@@ -27,6 +29,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -36,6 +39,9 @@ if ROOT not in sys.path:
 
 METRIC = "decode attention tokens/sec + live-KV HBM GB/s (% of peak) at CR=8, 32K ctx"
 HBM_PEAK_GBPS = 8000.0
+# MI355X Infinity Cache (MALL): a step whose live KV fits in it is reported as
+# cache-resident, its rate is not an HBM rate
+MALL_BYTES = 256 * 2**20
 KERNEL_SRCS = [os.path.join(ROOT, "learned_kv_cache_dms_amd", "csrc", f) for f in ("dms_kernels.hip", "dms_runtime.cpp")]
 
 
@@ -213,6 +219,8 @@ def main():
     total_ms = start.elapsed_time(end)
     attn_ms = [a.elapsed_time(b) for a, b in ev]
     attn_avg_s = sum(attn_ms) / K / 1e3
+    # step period from one attention end to the next (append + attention + gaps)
+    period_ms = [ev[i][1].elapsed_time(ev[i + 1][1]) for i in range(K - 1)]
     live_tokens = (st1["live_token_steps"] - st0["live_token_steps"]) / K   # per step, all units
     live_bytes = live_tokens * 2 * d * esize
     step_s = total_ms / K / 1e3
@@ -243,6 +251,9 @@ def main():
         "live_kv_gbps_per_step": round(live_bytes / step_s / 1e9, 1),
         "pct_peak_hbm": round(100 * achieved / HBM_PEAK_GBPS, 2),
         "attention_ms": round(attn_avg_s * 1e3, 5),
+        "attention_ms_median": round(statistics.median(attn_ms), 5),
+        "ms_per_step_median": round(statistics.median(period_ms), 5) if period_ms else None,
+        "cache_resident": bool(live_bytes < MALL_BYTES),
         "live_tokens_per_step": round(live_tokens, 1),
         "realized_cr": round(seen * B * Hkv / st1["live_tokens"], 3),
         "wall_s_timed": round(wall, 4),

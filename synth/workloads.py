@@ -132,6 +132,19 @@ def qwen_32b() -> Workload:
                     "beyond (overall about 8), 256 decode steps")
 
 
+def qwen_32b_dense() -> Workload:
+    """The Qwen-R1-32B-shaped layer with nothing marked (CR 1): the dense
+    baseline through the same kernels.  The logits are N(-8, 1)-like values
+    of the Irwin-Hall generator, which never exceed -8 + 6 = -2."""
+    w = qwen_32b()
+    w.name = "qwen-r1-32b-layer-dense"
+    w.seed = 1003
+    w.mu_before, w.mu_after, w.pos_threshold = [-8.0], None, synth.MAX_POS
+    w.description = ("Qwen-R1-32B-shaped layer as above with every eviction logit below 0: nothing is "
+                     "evicted (CR 1), 64 chains x 32768 tokens of dense KV")
+    return w
+
+
 def full_32b() -> Workload:
     layers = 64
     crs = [4.0 + 8.0 * l / (layers - 1) for l in range(layers)]
@@ -144,4 +157,4 @@ def full_32b() -> Workload:
                     "(layer 63), 128 decode steps")
 
 
-ALL = {w().name: w for w in (tiny, llama_1b, qwen_7b, qwen_32b, full_32b)}
+ALL = {w().name: w for w in (tiny, llama_1b, qwen_7b, qwen_32b, qwen_32b_dense, full_32b)}

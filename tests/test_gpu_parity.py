@@ -243,3 +243,23 @@ def test_full_size_sampled_units(wl_fn):
     ref = np.array([len(O.visible(O.eviction_decision(lg[b, h]), q, wl.window))
                     for b in range(wl.batch) for h in range(wl.num_kv_heads)])
     assert np.array_equal(n, ref)
+
+
+@gpu
+def test_dense_full_size_sampled_units():
+    """The dense baseline shape (Qwen-R1-32B-shaped layer with every logit
+    below 0): nothing is evicted, every unit holds all 32768 + t tokens (2064
+    blocks, 516 per wave in one work item) and the output is plain causal
+    attention.  Sampled units against the oracle at every one of 32 steps,
+    and every unit's live count = its position + 1."""
+    import dataclasses
+    import gpu_util as U
+    wl = dataclasses.replace(W.qwen_32b_dense(), decode_steps=32)
+    U_ = wl.batch * wl.num_kv_heads
+    units = [(0, 0), (21, 5), (63, 7)]
+    cache = U.make_cache(wl)
+    st = U.run_decode(wl, wl.decode_steps, units, _tol(wl), cache=cache)
+    assert st.checks == len(units) * wl.decode_steps
+    _, _, n = cache.export(0, U_)
+    assert np.all(n == wl.prompt_len + wl.decode_steps)
+
