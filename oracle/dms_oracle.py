@@ -33,6 +33,9 @@ Readings taken where the pages are silent (each listed in the design notes):
   token q - w - 1 if it was marked), then query q attends; it sees itself.
 * Attention scale 1 / sqrt(d) unless overridden.
 * Position 0 follows the same rule as every other position (no sinks).
+* When the logit comes from a repurposed projection channel: for keys, KV
+  head h's own channel; for queries, that channel of the group's first query
+  head; the channel may be zeroed in the stored keys (``without_channel``).
 
 The result is exact attention restricted to a visibility set, so this
 module is that definition written out in float64: a closed form for the
@@ -209,6 +212,61 @@ def decode_batch(Q: np.ndarray, K: np.ndarray, V: np.ndarray, logit: np.ndarray,
         for t, r in enumerate(recs):
             out[t, b, heads, :] = r.out
     return {"out": out, "records": records}
+
+
+# ----------------------------------------------------------------------------
+# Eviction logit read from a repurposed projection channel (summary page,
+# "Key claims" and "Method": no parameters are added; one neuron of the K or
+# Q projection of each head is repurposed to produce the eviction logit)
+# ----------------------------------------------------------------------------
+
+def logits_from_channel(X: np.ndarray, channel: int, group: int = 1) -> np.ndarray:
+    """Eviction logits [B, H // group, T] (float32) read from one channel of a
+    projection output X [B, H, T, d].
+
+    Keys (group = 1): the logit of KV head h at position i is
+    K[b, h, i, channel].  Queries (H = Hq, group = G): it is
+    Q[b, h * G, i, channel].  Reading: the pages do not say which query head
+    of a group drives the group's shared decision; the group's first query
+    head carries the neuron.
+    """
+    X = np.asarray(X)
+    B, H, T, _ = X.shape
+    out = np.empty((B, H // group, T), dtype=np.float32)
+    for h in range(H // group):
+        out[:, h, :] = X[:, h * group, :, channel]
+    return out
+
+
+def without_channel(X: np.ndarray, channel: int) -> np.ndarray:
+    """X (float64 copy) with ``channel`` set to 0 in every row.
+
+    Reading: when the caller asks for it, the neuron that now carries the
+    eviction logit no longer takes part in q . k (its key entry is stored as
+    0); the pages leave open whether the repurposed neuron stays a feature.
+    """
+    Y = np.array(X, dtype=np.float64, copy=True)
+    Y[..., channel] = 0.0
+    return Y
+
+
+def decode_batch_channel(Q: np.ndarray, K: np.ndarray, V: np.ndarray, prompt_lens, steps: int, w: int,
+                         source: str, channel: int, zero: bool, scale: Optional[float] = None,
+                         units=None) -> Dict:
+    """``decode_batch`` with the logits read from channel ``channel`` of the
+    keys (source "k") or of the queries (source "q"), and, for source "k"
+    with ``zero``, that channel of the keys set to 0 before attention."""
+    G = Q.shape[1] // K.shape[1]
+    if source == "k":
+        logit = logits_from_channel(K, channel, 1)
+    elif source == "q":
+        logit = logits_from_channel(Q, channel, G)
+    else:
+        raise ValueError(source)
+    Kc = without_channel(K, channel) if zero else K
+    if scale is None:
+        scale = default_scale(Q.shape[-1])
+    return decode_batch(Q, Kc, V, logit, prompt_lens, steps, w, scale, units)
 
 
 def state_after_prefill(logit_row: np.ndarray, prompt_len: int, w: int):

@@ -327,6 +327,68 @@ def pin_ragged_prompts(O):
         np.testing.assert_allclose(res["out"][:, b].transpose(1, 0, 2), ref, rtol=0, atol=1e-12)
 
 
+def pin_channel_logit_location(O):
+    """The logit of KV head h at position i sits at channel c of key head h,
+    or of query head h * G: a tensor that is zero except there (plus noise
+    in every other channel and in the group's other query heads) gives back
+    exactly the values planted."""
+    rng = np.random.default_rng(21)
+    B, Hkv, G, T, d, c = 2, 3, 4, 7, 6, 2
+    for group, H in ((1, Hkv), (G, Hkv * G)):
+        X = rng.standard_normal((B, H, T, d)).astype(np.float32) * 50
+        planted = np.empty((B, Hkv, T), dtype=np.float32)
+        for b in range(B):
+            for h in range(Hkv):
+                for i in range(T):
+                    val = np.float32(100 * b + 10 * h + i + 0.25)
+                    X[b, h * group, i, c] = val
+                    planted[b, h, i] = val
+        got = O.logits_from_channel(X, c, group)
+        assert got.dtype == np.float32 and got.shape == (B, Hkv, T)
+        assert np.array_equal(got, planted)
+
+
+def pin_zeroed_channel_is_dropped_feature(O):
+    """Keys with channel c zeroed give the attention of queries and keys with
+    that channel deleted (d - 1 features), at the same scale 1/sqrt(d)."""
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, T, d, c = 2, 4, 2, 30, 8, 5
+    Q, K, V = _random_batch(rng, B, Hq, Hkv, T, d)
+    logit = rng.standard_normal((B, Hkv, T)).astype(np.float32)
+    P, steps, w = [10, 17], 9, 3
+    a = O.decode_batch(Q, O.without_channel(K, c), V, logit, P, steps, w, 1 / math.sqrt(d))
+    # V loses the same column so that every array has d - 1 channels; the
+    # outputs' other columns must agree
+    b = O.decode_batch(np.delete(Q, c, axis=-1), np.delete(K, c, axis=-1), np.delete(V, c, axis=-1),
+                       logit, P, steps, w, 1 / math.sqrt(d))
+    np.testing.assert_allclose(np.delete(a["out"], c, axis=-1), b["out"], rtol=0, atol=1e-12)
+
+
+def pin_channel_logit_special_cases(O):
+    """Key channel c forced below 0 everywhere: nothing is marked, so the
+    decode is dense causal attention (torch SDPA with the channel deleted);
+    forced above 0: everything is marked, so it is the sliding window."""
+    rng = np.random.default_rng(23)
+    B, Hq, Hkv, T, d, c, w = 2, 6, 2, 40, 8, 3, 4
+    P, steps = 12, 28
+    for marked in (False, True):
+        Q, K, V = _random_batch(rng, B, Hq, Hkv, T, d)
+        K[..., c] = (np.abs(K[..., c]) + 0.1) * (1.0 if marked else -1.0)
+        res = O.decode_batch_channel(Q, K, V, [P] * B, steps, w, "k", c, True)
+        qpos = torch.arange(P, P + steps)[:, None]
+        kpos = torch.arange(T)[None, :]
+        allowed = kpos <= qpos
+        if marked:
+            allowed = allowed & (kpos >= qpos - w)
+        Qd, Kd = np.delete(Q, c, axis=-1), np.delete(K, c, axis=-1)
+        for b in range(B):
+            # SDPA scales by 1/sqrt(d - 1): rescale the queries to keep 1/sqrt(d)
+            qs = np.ascontiguousarray(Qd[b, :, P:P + steps]) * math.sqrt((d - 1) / d)
+            ref = _sdpa(qs, np.ascontiguousarray(Kd[b]), V[b], allowed.numpy(), Hq, Hkv)
+            got = res["out"][:, b].transpose(1, 0, 2)
+            np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_golden_visibility,
     pin_fifo_simulation,
@@ -343,4 +405,7 @@ ALL_PINS = [
     pin_one_hot_values,
     pin_needles,
     pin_ragged_prompts,
+    pin_channel_logit_location,
+    pin_zeroed_channel_is_dropped_feature,
+    pin_channel_logit_special_cases,
 ]

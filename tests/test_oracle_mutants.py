@@ -70,6 +70,28 @@ def _attend_masked_exclusive(qv, k_all, v_all, alpha_row, q, w, scale):
     return real._softmax(s + mask[None]) @ v
 
 
+def _channel_off_by_one(X, channel, group=1):
+    X = np.asarray(X)
+    B, H, T, d = X.shape
+    return np.stack([X[:, h * group, :, (channel + 1) % d] for h in range(H // group)], axis=1).astype(np.float32)
+
+
+def _channel_last_query_head(X, channel, group=1):
+    X = np.asarray(X)
+    B, H, T, d = X.shape
+    return np.stack([X[:, h * group + group - 1, :, channel] for h in range(H // group)], axis=1).astype(np.float32)
+
+
+def _zero_next_channel(X, channel):
+    Y = np.array(X, dtype=np.float64, copy=True)
+    Y[..., (channel + 1) % Y.shape[-1]] = 0.0
+    return Y
+
+
+def _zero_nothing(X, channel):
+    return np.array(X, dtype=np.float64, copy=True)
+
+
 MUTANTS = {
     "window-exclusive": ("visible", _visible_exclusive),
     "query-misses-itself": ("visible", _visible_drops_self),
@@ -83,6 +105,10 @@ MUTANTS = {
     "k-v-swapped": ("attend", _attend_kv_swapped),
     "softmax-axis": ("_softmax", _softmax_wrong_axis),
     "masked-form-exclusive": ("attend_masked", _attend_masked_exclusive),
+    "logit-channel-off-by-one": ("logits_from_channel", _channel_off_by_one),
+    "logit-last-query-head": ("logits_from_channel", _channel_last_query_head),
+    "zero-next-channel": ("without_channel", _zero_next_channel),
+    "zero-nothing": ("without_channel", _zero_nothing),
 }
 
 
