@@ -132,6 +132,11 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=16)
     ap.add_argument("--cpu-steps", type=int, default=192)
     ap.add_argument("--calib-copy-bytes", type=int, default=0)
+    ap.add_argument("--logit-source", choices=("array", "k", "q"), default="array",
+                    help="where the append reads the eviction logit: the logit array, or the workload's "
+                         "logits (bf16-rounded) planted in channel --logit-channel of the keys (stored "
+                         "zeroed) or of each group's first query head")
+    ap.add_argument("--logit-channel", type=int, default=0)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -171,7 +176,18 @@ def main():
     dsynth.fill(Kd, wl.seed, synth.STREAM_K, 0, 0)
     dsynth.fill(Vd, wl.seed, synth.STREAM_V, 0, 0)
     dsynth.logits(Ld, wl.seed, 0, 0, mb, ma, wl.pos_threshold)
-    cache.prefill(Kd, Vd, Ld, lengths)
+    src, ch = args.logit_source, args.logit_channel
+    G = Hq // Hkv
+    if src == "array":
+        cache.prefill(Kd, Vd, Ld, lengths)
+    elif src == "k":
+        Kd[..., ch] = Ld.to(tdt)
+        cache.prefill_channel(Kd, Vd, lengths, source="k", channel=ch, zero=True)
+    else:
+        Qp = torch.zeros((B, Hq, max_len, d), dtype=tdt, device="cuda")
+        Qp[:, ::G, :, ch] = Ld.to(tdt)
+        cache.prefill_channel(Kd, Vd, lengths, source="q", channel=ch, q=Qp)
+        del Qp
     torch.cuda.synchronize()
     # The dense prompt stays in torch's cache: returning 17 GB to the driver
     # (empty_cache) was measured to lower HBM streaming rates by 4-5% for the
@@ -190,11 +206,23 @@ def main():
         dsynth.fill(ks[t], wl.seed, synth.STREAM_K, 0, 0, pos_base=pb)
         dsynth.fill(vs[t], wl.seed, synth.STREAM_V, 0, 0, pos_base=pb)
         dsynth.logits(lgs[t], wl.seed, 0, 0, mb, ma, wl.pos_threshold, pos_base=pb)
+    if src == "k":
+        ks[..., ch] = lgs.to(tdt)
+    elif src == "q":
+        qs[:, :, ::G, ch] = lgs.to(tdt)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
 
+    if src == "array":
+        def append(t):
+            cache.append(ks[t], vs[t], lgs[t])
+    else:
+        def append(t):
+            cache.append_channel(ks[t], vs[t], source=src, channel=ch, zero=(src == "k"),
+                                 q=qs[t] if src == "q" else None)
+
     for t in range(W):
-        cache.append(ks[t], vs[t], lgs[t])
+        append(t)
         cache.attend(qs[t], out)
     st0 = cache.stats()
 
@@ -205,7 +233,7 @@ def main():
     start.record()
     for i in range(K):
         t = W + i
-        cache.append(ks[t], vs[t], lgs[t])
+        append(t)
         ev[i][0].record()
         cache.attend(qs[t], out)
         ev[i][1].record()
@@ -246,6 +274,8 @@ def main():
             "workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
             "context": int(lengths.max()), "window": wl.window, "block_tokens": 16,
             "decode_steps": S, "logit_mean": [round(mb, 4), round(ma, 4)], "logit_mean_switch": wl.pos_threshold,
+            "logit_source": {"array": "array", "k": f"key channel {ch} (stored zeroed)",
+                             "q": f"query channel {ch} of each group's first head"}[src],
         },
         "live_kv_gbps": round(achieved, 1),
         "live_kv_gbps_per_step": round(live_bytes / step_s / 1e9, 1),
@@ -269,7 +299,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and src == "array":
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps, args.cpu_units)
     print(json.dumps(res), flush=True)
 

@@ -143,6 +143,44 @@ DMS_API int dms_prefill_compress(dms_cache* c, const void* d_k, const void* d_v,
 DMS_API int dms_append_step(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit,
                     void* stream);
 
+/* Where the _channel variants read the eviction logit.  Source: "Inference-
+   Time Hyper-Scaling with KV Cache Compression", third-party paper summary
+   page, sections "Key claims" and "Method": no parameters are added; one
+   neuron of each head's K or Q projection is repurposed to produce the
+   eviction logit. */
+typedef enum {
+  DMS_LOGIT_FROM_K = 0, /* KV head h's logit is channel `channel` of its own key row */
+  DMS_LOGIT_FROM_Q = 1  /* it is channel `channel` of query head h * G, the group's first
+                           query head (the pages do not say which query head of a group
+                           drives the group's shared decision) */
+} dms_logit_source;
+
+/* Async.  dms_append_step with the eviction logit read from a projection
+   channel instead of a separate array:
+     logit[b, h] = fp32(d_k[b, h, channel])      for DMS_LOGIT_FROM_K
+     logit[b, h] = fp32(d_q[b, h * G, channel])  for DMS_LOGIT_FROM_Q
+   (bf16 values are upcast exactly), then the same decision, retirement and
+   store.  d_q: [B, Hq, d] of dtype, read only for DMS_LOGIT_FROM_Q (may be
+   NULL otherwise).  zero_channel != 0 (DMS_LOGIT_FROM_K only) stores the key
+   row with that channel set to 0, so that the repurposed neuron takes no part
+   in the attention scores; d_k itself is not modified.
+   Errors: DMS_ERR_ARG for a bad source or channel (not in 0 .. d-1), a NULL
+   d_q with DMS_LOGIT_FROM_Q, or zero_channel with DMS_LOGIT_FROM_Q;
+   DMS_ERR_CAPACITY as dms_append_step. */
+DMS_API int dms_append_step_channel(dms_cache* c, const void* d_k, const void* d_v, const void* d_q,
+                                    int32_t source, int32_t channel, int32_t zero_channel, void* stream);
+
+/* Async.  dms_prefill_compress with the eviction logits read from a
+   projection channel (as dms_append_step_channel, at every prompt position):
+     logit[b, h, i] = fp32(d_k[b, h, i, channel])      for DMS_LOGIT_FROM_K
+     logit[b, h, i] = fp32(d_q[b, h * G, i, channel])  for DMS_LOGIT_FROM_Q
+   d_q: [B, Hq, max_len, d] of dtype, read only for DMS_LOGIT_FROM_Q.
+   zero_channel as in dms_append_step_channel.  Errors: those of
+   dms_prefill_compress and of dms_append_step_channel's arguments. */
+DMS_API int dms_prefill_compress_channel(dms_cache* c, const void* d_k, const void* d_v, const void* d_q,
+                                         int32_t source, int32_t channel, int32_t zero_channel,
+                                         const int32_t* h_lengths, int32_t max_len, void* stream);
+
 /* Async.  Grouped-query decode attention of the query at each sequence's
    last position over that sequence's visible tokens:
      out[b, hq, :] = sum_i softmax_i(scale * <q[b,hq], k_i>) v_i,

@@ -60,14 +60,28 @@ struct PromptLens {
   int32_t v[kMax];
 };
 
+// Where the eviction logit of unit (b, h) at position i is read: element
+// b * sb + h * sh + i * si + off of an fp32 or bf16 array.  It covers the
+// logit arrays ([B, Hkv] per step, [B, Hkv, max_len] for a prompt) and a
+// channel of the keys ([B, Hkv, (max_len,) d]) or of the group's first query
+// head ([B, Hq, (max_len,) d], sh = G * row stride).
+struct LogitSrc {
+  const void* base;
+  int64_t sb, sh, si;
+  int32_t off;
+  int32_t bf16;  // 1: bf16 elements (upcast exactly), 0: fp32
+};
+
 // Status codes mirrored from dms.h for device code.
 constexpr int kErrOutOfBlocks = -3;
 
 hipError_t launch_init(const Dev& p, hipStream_t s);
+// zero_ch >= 0: that key channel is stored as 0; -1: keys are stored as given.
 hipError_t launch_append(const Dev& p, int dtype, int d, const void* k, const void* v,
-                         const float* logit, hipStream_t s);
+                         const LogitSrc& logit, int zero_ch, hipStream_t s);
 hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const void* v,
-                          const float* logit, const int32_t* h_lengths, int32_t max_len, hipStream_t s);
+                          const LogitSrc& logit, int zero_ch, const int32_t* h_lengths, int32_t max_len,
+                          hipStream_t s);
 hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s);
 // Work-groups of the attention kernel that fit on the device at once.
 int attention_resident_wgs(int dtype, int d, int num_cus);

@@ -109,6 +109,26 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo_to_f32(unsigned x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
+// Eviction logit of unit (b, h) at position i (an exact upcast for bf16).
+__device__ __forceinline__ float load_logit(const LogitSrc& ls, int b, int h, int64_t i) {
+  const int64_t e = (int64_t)b * ls.sb + (int64_t)h * ls.sh + i * ls.si + ls.off;
+  if (ls.bf16) return __uint_as_float((unsigned)((const uint16_t*)ls.base)[e] << 16);
+  return ((const float*)ls.base)[e];
+}
+
+// Clears key channel zc (none when zc < 0) if it lies in 16-byte piece r of
+// a row (channels r * 16 / ES .. (r + 1) * 16 / ES - 1).
+template <int ES>
+__device__ __forceinline__ void clear_channel(u32x4& val, int r, int zc) {
+  constexpr int kE = 16 / ES;
+  if (zc < 0 || zc / kE != r) return;
+  const int byte = (zc % kE) * ES;
+  const unsigned keep = ES == 4 ? 0u : ((byte & 2) ? 0x0000ffffu : 0xffff0000u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i == (byte >> 2)) val[i] &= keep;
+}
+
 // ---------------------------------------------------------------------------
 // state initialisation (create / reset)
 // ---------------------------------------------------------------------------
@@ -138,11 +158,12 @@ __global__ void init_kernel(Dev p) {
 // Stores one token row into slot t of an existing block.
 template <int ES, int D>
 __device__ __forceinline__ void write_row(uint8_t* blkp, int t, const uint8_t* krow,
-                                          const uint8_t* vrow, int lane) {
+                                          const uint8_t* vrow, int lane, int zero_ch) {
   using G = Geo<ES, D>;
   if (lane < D / G::kE) {
     const int r = lane;  // 16-byte piece of the row: channels r*E .. r*E+E-1
     u32x4 val = *(const u32x4*)(krow + r * 16);
+    clear_channel<ES>(val, r, zero_ch);
     *(u32x4*)(blkp + (r >> 2) * 1024 + (t + 16 * (r & 3)) * 16) = val;
   }
 #pragma unroll
@@ -161,12 +182,15 @@ __device__ __forceinline__ void write_row(uint8_t* blkp, int t, const uint8_t* k
 // attention multiplies masked slots by zero weights, so they must be finite).
 template <int ES, int D>
 __device__ __forceinline__ void write_fresh(uint8_t* blkp, const uint8_t* krow,
-                                            const uint8_t* vrow, int lane) {
+                                            const uint8_t* vrow, int lane, int zero_ch) {
   using G = Geo<ES, D>;
 #pragma unroll
   for (int c = 0; c < G::kChunks; ++c) {
     u32x4 val = {0u, 0u, 0u, 0u};
-    if ((lane & 15) == 0) val = *(const u32x4*)(krow + (c * 4 + (lane >> 4)) * 16);
+    if ((lane & 15) == 0) {
+      val = *(const u32x4*)(krow + (c * 4 + (lane >> 4)) * 16);
+      clear_channel<ES>(val, c * 4 + (lane >> 4), zero_ch);
+    }
     *(u32x4*)(blkp + c * 1024 + lane * 16) = val;
   }
 #pragma unroll
@@ -186,14 +210,14 @@ __device__ __forceinline__ void write_fresh(uint8_t* blkp, const uint8_t* krow,
 
 template <int ES, int D>
 __global__ __launch_bounds__(256) void append_kernel(Dev p, const uint8_t* __restrict__ k,
-                                                     const uint8_t* __restrict__ v,
-                                                     const float* __restrict__ logit) {
+                                                     const uint8_t* __restrict__ v, LogitSrc logit,
+                                                     int zero_ch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int u = blockIdx.x * kWavesPerWG + wave;
   __shared__ unsigned s_live[kWavesPerWG];
   unsigned live = 0;
   if (u < p.U) {
-    const float lg = logit[u];
+    const float lg = load_logit(logit, u / p.Hkv, u % p.Hkv, 0);
     const bool alpha = lg > 0.0f;  // NaN compares false
     const int q = p.pos[u];
     const int r = q % p.R;
@@ -230,9 +254,9 @@ __global__ __launch_bounds__(256) void append_kernel(Dev p, const uint8_t* __res
     if (ok) {
       uint8_t* dst = p.pool + (int64_t)blk * p.block_bytes;
       if (fresh)
-        write_fresh<ES, D>(dst, krow, vrow, lane);
+        write_fresh<ES, D>(dst, krow, vrow, lane, zero_ch);
       else
-        write_row<ES, D>(dst, t, krow, vrow, lane);
+        write_row<ES, D>(dst, t, krow, vrow, lane, zero_ch);
       if (lane == 0) {
         p.blk_pos[(int64_t)blk * 16 + t] = q;
         if (fresh)
@@ -282,16 +306,16 @@ __device__ __forceinline__ int block_sum_1024(int x, int* s_tmp) {
 
 // One work-group of 1024 threads per (sequence, KV head): n[u] = the tokens
 // visible at the last prompt position.
-__global__ __launch_bounds__(1024) void prefill_count_kernel(Dev p, const float* __restrict__ logit,
-                                                             int32_t max_len, int32_t b0, PromptLens lens) {
+__global__ __launch_bounds__(1024) void prefill_count_kernel(Dev p, LogitSrc logit, int32_t b0,
+                                                             PromptLens lens) {
   __shared__ int s_tmp[16];
   const int u = b0 * p.Hkv + blockIdx.x;
+  const int b = u / p.Hkv, h = u % p.Hkv;
   const int P = lens.v[blockIdx.x / p.Hkv];
   const int w = p.R - 1;
-  const float* lg = logit + (int64_t)u * max_len;
   int cnt = 0;
   for (int i = threadIdx.x; i < P; i += blockDim.x) {
-    const bool alpha = lg[i] > 0.0f;
+    const bool alpha = load_logit(logit, b, h, i) > 0.0f;
     cnt += (!alpha || (P - 1 - i) <= w) ? 1 : 0;
   }
   const int n = block_sum_1024(cnt, s_tmp);
@@ -349,14 +373,13 @@ __global__ __launch_bounds__(1024) void prefill_alloc_kernel(Dev p, int32_t* __r
 // One work-group of 1024 threads per (sequence, KV head): assigns the
 // visible tokens slots 0 .. n-1 in position order and fills block table,
 // slot positions, masks and the pending-eviction ring.
-__global__ __launch_bounds__(1024) void prefill_scan_kernel(Dev p, const float* __restrict__ logit,
-                                                            int32_t max_len, int32_t b0, PromptLens lens,
-                                                            const int32_t* __restrict__ bases) {
+__global__ __launch_bounds__(1024) void prefill_scan_kernel(Dev p, LogitSrc logit, int32_t b0,
+                                                            PromptLens lens, const int32_t* __restrict__ bases) {
   __shared__ int s_wave_pre[16];
   const int u = b0 * p.Hkv + blockIdx.x;
+  const int b = u / p.Hkv, h = u % p.Hkv;
   const int P = lens.v[blockIdx.x / p.Hkv];
   const int w = p.R - 1;
-  const float* lg = logit + (int64_t)u * max_len;
   int32_t* ring = p.ring + (int64_t)u * p.R;
   for (int i = threadIdx.x; i < p.R; i += blockDim.x) ring[i] = -1;
   const int n = p.n[u];
@@ -376,7 +399,7 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(Dev p, const float* 
       bool alpha = false;
       int vis = 0;
       if (i < P) {
-        alpha = lg[i] > 0.0f;
+        alpha = load_logit(logit, b, h, i) > 0.0f;
         vis = (!alpha || (P - 1 - i) <= w) ? 1 : 0;
       }
       const int incl = wave_incl_scan_i(vis, lane);
@@ -406,7 +429,7 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(Dev p, const float* 
 template <int ES, int D>
 __global__ __launch_bounds__(256) void prefill_scatter_kernel(Dev p, const uint8_t* __restrict__ k,
                                                               const uint8_t* __restrict__ v,
-                                                              int32_t max_len) {
+                                                              int32_t max_len, int zero_ch) {
   using G = Geo<ES, D>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int u = blockIdx.x;
@@ -427,7 +450,10 @@ __global__ __launch_bounds__(256) void prefill_scatter_kernel(Dev p, const uint8
 #pragma unroll
       for (int c = 0; c < G::kChunks; ++c) {
         u32x4 val = {0u, 0u, 0u, 0u};
-        if (sp >= 0) val = *(const u32x4*)(src + (c * 4 * G::kE + G::kE * (lane >> 4)) * ES);
+        if (sp >= 0) {
+          val = *(const u32x4*)(src + (c * 4 * G::kE + G::kE * (lane >> 4)) * ES);
+          clear_channel<ES>(val, c * 4 + (lane >> 4), zero_ch);
+        }
         *(u32x4*)(dst + c * 1024 + lane * 16) = val;
       }
     }
@@ -1183,20 +1209,22 @@ hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int3
 }
 
 template <int ES, int D>
-static hipError_t append_t(const Dev& p, const void* k, const void* v, const float* logit, hipStream_t s) {
+static hipError_t append_t(const Dev& p, const void* k, const void* v, const LogitSrc& logit, int zero_ch,
+                           hipStream_t s) {
   const int blocks = (p.U + kWavesPerWG - 1) / kWavesPerWG;
   return launch(append_kernel<ES, D>, dim3(blocks), dim3(64 * kWavesPerWG), s, p, (const uint8_t*)k,
-                (const uint8_t*)v, logit);
+                (const uint8_t*)v, logit, zero_ch);
 }
 
 hipError_t launch_append(const Dev& p, int dtype, int d, const void* k, const void* v,
-                         const float* logit, hipStream_t s) {
-  if (dtype == 1) return d == 128 ? append_t<2, 128>(p, k, v, logit, s) : append_t<2, 64>(p, k, v, logit, s);
-  return d == 128 ? append_t<4, 128>(p, k, v, logit, s) : append_t<4, 64>(p, k, v, logit, s);
+                         const LogitSrc& logit, int zero_ch, hipStream_t s) {
+  if (dtype == 1)
+    return d == 128 ? append_t<2, 128>(p, k, v, logit, zero_ch, s) : append_t<2, 64>(p, k, v, logit, zero_ch, s);
+  return d == 128 ? append_t<4, 128>(p, k, v, logit, zero_ch, s) : append_t<4, 64>(p, k, v, logit, zero_ch, s);
 }
 
 template <int ES, int D>
-static hipError_t prefill_t(const Dev& p, const void* k, const void* v, const float* logit,
+static hipError_t prefill_t(const Dev& p, const void* k, const void* v, const LogitSrc& logit, int zero_ch,
                             const int32_t* h_lengths, int32_t max_len, hipStream_t s) {
   // The partial area is free between attention calls: it holds the bases.
   int32_t* bases = (int32_t*)p.part;
@@ -1206,8 +1234,8 @@ static hipError_t prefill_t(const Dev& p, const void* k, const void* v, const fl
       PromptLens lens;
       for (int i = 0; i < nb; ++i) lens.v[i] = h_lengths[b0 + i];
       const hipError_t e =
-          pass == 0 ? launch(prefill_count_kernel, dim3(nb * p.Hkv), dim3(1024), s, p, logit, max_len, b0, lens)
-                    : launch(prefill_scan_kernel, dim3(nb * p.Hkv), dim3(1024), s, p, logit, max_len, b0, lens,
+          pass == 0 ? launch(prefill_count_kernel, dim3(nb * p.Hkv), dim3(1024), s, p, logit, b0, lens)
+                    : launch(prefill_scan_kernel, dim3(nb * p.Hkv), dim3(1024), s, p, logit, b0, lens,
                              (const int32_t*)bases);
       if (e != hipSuccess) return e;
     }
@@ -1218,16 +1246,17 @@ static hipError_t prefill_t(const Dev& p, const void* k, const void* v, const fl
   }
   const int ysplit = 8;
   return launch(prefill_scatter_kernel<ES, D>, dim3(p.U, ysplit), dim3(64 * kWavesPerWG), s, p,
-                (const uint8_t*)k, (const uint8_t*)v, max_len);
+                (const uint8_t*)k, (const uint8_t*)v, max_len, zero_ch);
 }
 
 hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const void* v,
-                          const float* logit, const int32_t* h_lengths, int32_t max_len, hipStream_t s) {
+                          const LogitSrc& logit, int zero_ch, const int32_t* h_lengths, int32_t max_len,
+                          hipStream_t s) {
   if (dtype == 1)
-    return d == 128 ? prefill_t<2, 128>(p, k, v, logit, h_lengths, max_len, s)
-                    : prefill_t<2, 64>(p, k, v, logit, h_lengths, max_len, s);
-  return d == 128 ? prefill_t<4, 128>(p, k, v, logit, h_lengths, max_len, s)
-                  : prefill_t<4, 64>(p, k, v, logit, h_lengths, max_len, s);
+    return d == 128 ? prefill_t<2, 128>(p, k, v, logit, zero_ch, h_lengths, max_len, s)
+                    : prefill_t<2, 64>(p, k, v, logit, zero_ch, h_lengths, max_len, s);
+  return d == 128 ? prefill_t<4, 128>(p, k, v, logit, zero_ch, h_lengths, max_len, s)
+                  : prefill_t<4, 64>(p, k, v, logit, zero_ch, h_lengths, max_len, s);
 }
 
 template <int ES, int D>

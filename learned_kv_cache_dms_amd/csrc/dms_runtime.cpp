@@ -202,9 +202,45 @@ int dms_cache_reset(dms_cache* c, void* stream) {
   return st;
 }
 
-int dms_prefill_compress(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit,
-                         const int32_t* h_lengths, int32_t max_len, void* stream) {
-  if (!c || !d_k || !d_v || !d_logit || !h_lengths || max_len < 1) return DMS_ERR_ARG;
+// Logit source of the plain fp32 arrays: [B, Hkv] per step (positions = 1),
+// [B, Hkv, max_len] for a prompt.
+static dms::LogitSrc array_logits(const dms_cache* c, const float* d_logit, int64_t positions) {
+  dms::LogitSrc ls{};
+  ls.base = d_logit;
+  ls.sh = positions;
+  ls.sb = (int64_t)c->L.Hkv * positions;
+  ls.si = 1;
+  ls.off = 0;
+  ls.bf16 = 0;
+  return ls;
+}
+
+// Logit source of a projection channel; rows of d elements, `positions` rows
+// per head ([B, H, positions, d]).  Returns DMS_ERR_ARG for bad arguments.
+static int channel_logits(const dms_cache* c, const void* d_k, const void* d_q, int32_t source,
+                          int32_t channel, int32_t zero_channel, int64_t positions, dms::LogitSrc* ls) {
+  const int d = c->L.d;
+  if (channel < 0 || channel >= d) return DMS_ERR_ARG;
+  if (source == DMS_LOGIT_FROM_K) {
+    ls->base = d_k;
+    ls->sh = positions * d;
+    ls->sb = (int64_t)c->L.Hkv * positions * d;
+  } else if (source == DMS_LOGIT_FROM_Q) {
+    if (!d_q || zero_channel) return DMS_ERR_ARG;
+    ls->base = d_q;
+    ls->sh = (int64_t)c->L.G * positions * d;  // query head h * G
+    ls->sb = (int64_t)c->L.Hq * positions * d;
+  } else {
+    return DMS_ERR_ARG;
+  }
+  ls->si = d;
+  ls->off = channel;
+  ls->bf16 = c->cfg.dtype == DMS_BF16 ? 1 : 0;
+  return DMS_OK;
+}
+
+static int prefill_common(dms_cache* c, const void* d_k, const void* d_v, const dms::LogitSrc& ls, int zero_ch,
+                          const int32_t* h_lengths, int32_t max_len, void* stream) {
   int st = check_device(c);
   if (st != DMS_OK) return st;
   for (int32_t x : c->len)
@@ -213,23 +249,54 @@ int dms_prefill_compress(dms_cache* c, const void* d_k, const void* d_v, const f
     if (h_lengths[b] < 0 || h_lengths[b] > max_len) return DMS_ERR_ARG;
     if (h_lengths[b] > c->L.max_tokens) return DMS_ERR_CAPACITY;
   }
-  st = hip_status(dms::launch_prefill(make_dev(c), c->cfg.dtype, c->L.d, d_k, d_v, d_logit, h_lengths,
+  st = hip_status(dms::launch_prefill(make_dev(c), c->cfg.dtype, c->L.d, d_k, d_v, ls, zero_ch, h_lengths,
                                       max_len, (hipStream_t)stream));
   if (st == DMS_OK)
     for (int b = 0; b < c->L.B; ++b) c->len[b] = h_lengths[b];
   return st;
 }
 
-int dms_append_step(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit, void* stream) {
-  if (!c || !d_k || !d_v || !d_logit) return DMS_ERR_ARG;
+static int append_common(dms_cache* c, const void* d_k, const void* d_v, const dms::LogitSrc& ls, int zero_ch,
+                         void* stream) {
   int st = check_device(c);
   if (st != DMS_OK) return st;
   for (int32_t x : c->len)
     if (x + 1 > c->L.max_tokens) return DMS_ERR_CAPACITY;
-  st = hip_status(dms::launch_append(make_dev(c), c->cfg.dtype, c->L.d, d_k, d_v, d_logit, (hipStream_t)stream));
+  st = hip_status(
+      dms::launch_append(make_dev(c), c->cfg.dtype, c->L.d, d_k, d_v, ls, zero_ch, (hipStream_t)stream));
   if (st == DMS_OK)
     for (auto& x : c->len) ++x;
   return st;
+}
+
+int dms_prefill_compress(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit,
+                         const int32_t* h_lengths, int32_t max_len, void* stream) {
+  if (!c || !d_k || !d_v || !d_logit || !h_lengths || max_len < 1) return DMS_ERR_ARG;
+  return prefill_common(c, d_k, d_v, array_logits(c, d_logit, max_len), -1, h_lengths, max_len, stream);
+}
+
+int dms_prefill_compress_channel(dms_cache* c, const void* d_k, const void* d_v, const void* d_q, int32_t source,
+                                 int32_t channel, int32_t zero_channel, const int32_t* h_lengths, int32_t max_len,
+                                 void* stream) {
+  if (!c || !d_k || !d_v || !h_lengths || max_len < 1) return DMS_ERR_ARG;
+  dms::LogitSrc ls{};
+  const int st = channel_logits(c, d_k, d_q, source, channel, zero_channel, max_len, &ls);
+  if (st != DMS_OK) return st;
+  return prefill_common(c, d_k, d_v, ls, zero_channel ? channel : -1, h_lengths, max_len, stream);
+}
+
+int dms_append_step(dms_cache* c, const void* d_k, const void* d_v, const float* d_logit, void* stream) {
+  if (!c || !d_k || !d_v || !d_logit) return DMS_ERR_ARG;
+  return append_common(c, d_k, d_v, array_logits(c, d_logit, 1), -1, stream);
+}
+
+int dms_append_step_channel(dms_cache* c, const void* d_k, const void* d_v, const void* d_q, int32_t source,
+                            int32_t channel, int32_t zero_channel, void* stream) {
+  if (!c || !d_k || !d_v) return DMS_ERR_ARG;
+  dms::LogitSrc ls{};
+  const int st = channel_logits(c, d_k, d_q, source, channel, zero_channel, 1, &ls);
+  if (st != DMS_OK) return st;
+  return append_common(c, d_k, d_v, ls, zero_channel ? channel : -1, stream);
 }
 
 int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stream) {

@@ -30,6 +30,9 @@ DMS_ERR_STATE = -5
 DMS_ERR_HIP = -6
 DMS_ERR_DEVICE = -7
 
+DMS_LOGIT_FROM_K = 0
+DMS_LOGIT_FROM_Q = 1
+
 
 class DmsError(RuntimeError):
     def __init__(self, status: int, where: str):
@@ -91,6 +94,8 @@ def _load():
         "dms_cache_reset": (ctypes.c_int, [vp, vp]),
         "dms_prefill_compress": (ctypes.c_int, [vp, vp, vp, vp, P(i32), i32, vp]),
         "dms_append_step": (ctypes.c_int, [vp, vp, vp, vp, vp]),
+        "dms_append_step_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp]),
+        "dms_prefill_compress_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, P(i32), i32, vp]),
         "dms_decode_attention": (ctypes.c_int, [vp, vp, vp, vp]),
         "dms_cache_stats": (ctypes.c_int, [vp, P(dms_stats), vp]),
         "dms_cache_export": (ctypes.c_int, [vp, i32, i32, P(i32), P(i32), P(i32), vp]),
@@ -158,6 +163,20 @@ def dms_append_step(h: int, d_k: int, d_v: int, d_logit: int, stream: int = 0):
     _check(lib.dms_append_step(h, d_k, d_v, d_logit, stream), "dms_append_step")
 
 
+def dms_append_step_channel(h: int, d_k: int, d_v: int, d_q: Optional[int], source: int, channel: int,
+                            zero_channel: bool, stream: int = 0):
+    _check(lib.dms_append_step_channel(h, d_k, d_v, d_q, int(source), int(channel), int(bool(zero_channel)),
+                                       stream), "dms_append_step_channel")
+
+
+def dms_prefill_compress_channel(h: int, d_k: int, d_v: int, d_q: Optional[int], source: int, channel: int,
+                                 zero_channel: bool, lengths: Sequence[int], max_len: int, stream: int = 0):
+    L = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+    _check(lib.dms_prefill_compress_channel(h, d_k, d_v, d_q, int(source), int(channel),
+                                            int(bool(zero_channel)), _i32p(L), int(max_len), stream),
+           "dms_prefill_compress_channel")
+
+
 def dms_decode_attention(h: int, d_q: int, d_out: int, stream: int = 0):
     _check(lib.dms_decode_attention(h, d_q, d_out, stream), "dms_decode_attention")
 
@@ -218,6 +237,28 @@ class Cache:
         pv = self._chk(v, (self.B, self.Hkv, self.d), self.tdtype, "v")
         pl = self._chk(logit, (self.B, self.Hkv), self._torch.float32, "logit")
         dms_append_step(self.handle, pk, pv, pl, self._stream())
+
+    _SOURCES = {"k": DMS_LOGIT_FROM_K, "q": DMS_LOGIT_FROM_Q}
+
+    def prefill_channel(self, k, v, lengths, source="k", channel=0, zero=False, q=None):
+        """prefill with the eviction logits read from channel `channel` of the
+        keys (source "k") or of each group's first query head (source "q";
+        q: [B, Hq, max_len, d])."""
+        max_len = k.shape[2]
+        pk = self._chk(k, (self.B, self.Hkv, max_len, self.d), self.tdtype, "k")
+        pv = self._chk(v, (self.B, self.Hkv, max_len, self.d), self.tdtype, "v")
+        pq = None if q is None else self._chk(q, (self.B, self.Hq, max_len, self.d), self.tdtype, "q")
+        dms_prefill_compress_channel(self.handle, pk, pv, pq, self._SOURCES[source], channel, zero, lengths,
+                                     max_len, self._stream())
+
+    def append_channel(self, k, v, source="k", channel=0, zero=False, q=None):
+        """append with the eviction logit read from channel `channel` of the
+        key row (source "k") or of the group's first query head (source "q";
+        q: [B, Hq, d])."""
+        pk = self._chk(k, (self.B, self.Hkv, self.d), self.tdtype, "k")
+        pv = self._chk(v, (self.B, self.Hkv, self.d), self.tdtype, "v")
+        pq = None if q is None else self._chk(q, (self.B, self.Hq, self.d), self.tdtype, "q")
+        dms_append_step_channel(self.handle, pk, pv, pq, self._SOURCES[source], channel, zero, self._stream())
 
     def attend(self, q, out=None):
         pq = self._chk(q, (self.B, self.Hq, self.d), self.tdtype, "q")
