@@ -215,6 +215,38 @@ def decode_batch(Q: np.ndarray, K: np.ndarray, V: np.ndarray, logit: np.ndarray,
 
 
 # ----------------------------------------------------------------------------
+# Attention of the prompt's own queries under the same rule (summary page,
+# "Method": the decisions act as an additive attention mask, the same one at
+# every position, that never has to be built)
+# ----------------------------------------------------------------------------
+
+def prefill_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, logit: np.ndarray, prompt_lens,
+                      w: int, scale: Optional[float] = None) -> np.ndarray:
+    """Output of every prompt query: query position q of sequence b and
+    query head hq attends the visible set Vis(b, h, q) of KV head
+    h = floor(hq / G), exactly as a decode query at q would.
+
+    Q: [B, Hq, T, d]; K, V: [B, Hkv, T, d]; logit: [B, Hkv, T];
+    prompt_lens: [B] (<= T).  Returns [B, Hq, T, d] float64, NaN at
+    positions q >= prompt_lens[b].
+    """
+    B, Hq, T, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = default_scale(d)
+    out = np.full((B, Hq, T, d), np.nan)
+    for b in range(B):
+        for h in range(Hkv):
+            alpha = eviction_decision(logit[b, h])
+            heads = [hq for hq in range(Hq) if kv_head_of(hq, G) == h]
+            for q in range(int(prompt_lens[b])):
+                vis = visible(alpha, q, w)
+                out[b, heads, q, :] = attend(Q[b, heads, q, :], K[b, h][vis], V[b, h][vis], scale)
+    return out
+
+
+# ----------------------------------------------------------------------------
 # Eviction logit read from a repurposed projection channel (summary page,
 # "Key claims" and "Method": no parameters are added; one neuron of the K or
 # Q projection of each head is repurposed to produce the eviction logit)

@@ -389,6 +389,52 @@ def pin_channel_logit_special_cases(O):
             np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
+def _prefill_special_case(O, marked: bool, w: int):
+    rng = np.random.default_rng(31 if marked else 32)
+    B, Hq, Hkv, T, d = 2, 6, 3, 45, 8
+    Q, K, V = _random_batch(rng, B, Hq, Hkv, T, d)
+    logit = np.full((B, Hkv, T), 1.0 if marked else -1.0, dtype=np.float32)
+    P = [45, 29]
+    out = O.prefill_attention(Q, K, V, logit, P, w)
+    for b in range(B):
+        pos = torch.arange(P[b])
+        allowed = pos[None, :] <= pos[:, None]
+        if marked:
+            allowed = allowed & (pos[None, :] >= pos[:, None] - w)
+        ref = _sdpa(np.ascontiguousarray(Q[b, :, :P[b]]), np.ascontiguousarray(K[b, :, :P[b]]),
+                    np.ascontiguousarray(V[b, :, :P[b]]), allowed.numpy(), Hq, Hkv)
+        np.testing.assert_allclose(out[b, :, :P[b]], ref, rtol=0, atol=1e-12)
+        assert np.all(np.isnan(out[b, :, P[b]:]))
+
+
+def pin_prefill_unmarked_is_causal_attention(O):
+    """No token marked: every prompt query attends all earlier positions
+    (torch SDPA, causal mask)."""
+    _prefill_special_case(O, marked=False, w=4)
+
+
+def pin_prefill_marked_is_sliding_window(O):
+    """Every token marked: query q attends positions q - w .. q."""
+    for w in (0, 5):
+        _prefill_special_case(O, marked=True, w=w)
+
+
+def pin_prefill_equals_masked_form(O):
+    """Random decisions: each prompt query's output equals the dense
+    additive-mask form over its causal positions."""
+    rng = np.random.default_rng(33)
+    B, Hq, Hkv, T, d, w = 1, 4, 2, 40, 8, 3
+    Q, K, V = _random_batch(rng, B, Hq, Hkv, T, d)
+    logit = rng.standard_normal((B, Hkv, T)).astype(np.float32) + 0.5
+    out = O.prefill_attention(Q, K, V, logit, [T], w, 0.3)
+    for h in range(Hkv):
+        alpha = logit[0, h] > 0
+        for hq in (2 * h, 2 * h + 1):
+            for q in range(T):
+                ref = O.attend_masked(Q[0, hq, q][None], K[0, h], V[0, h], alpha, q, w, 0.3)[0]
+                np.testing.assert_allclose(out[0, hq, q], ref, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_golden_visibility,
     pin_fifo_simulation,
@@ -408,4 +454,7 @@ ALL_PINS = [
     pin_channel_logit_location,
     pin_zeroed_channel_is_dropped_feature,
     pin_channel_logit_special_cases,
+    pin_prefill_unmarked_is_causal_attention,
+    pin_prefill_marked_is_sliding_window,
+    pin_prefill_equals_masked_form,
 ]

@@ -92,6 +92,42 @@ def _zero_nothing(X, channel):
     return np.array(X, dtype=np.float64, copy=True)
 
 
+def _prefill_final_state(Q, K, V, logit, prompt_lens, w, scale=None):
+    """Every prompt query attends the visible set of the prompt's last position."""
+    B, Hq, T, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    scale = real.default_scale(d) if scale is None else scale
+    out = np.full((B, Hq, T, d), np.nan)
+    for b in range(B):
+        for h in range(Hkv):
+            alpha = real.eviction_decision(logit[b, h])
+            P = int(prompt_lens[b])
+            vis = real.visible(alpha, P - 1, w)
+            for hq in range(h * G, (h + 1) * G):
+                for q in range(P):
+                    vq = vis[vis <= q]
+                    out[b, hq, q] = real.attend(Q[b, hq, q][None], K[b, h][vq], V[b, h][vq], scale)[0]
+    return out
+
+
+def _prefill_shifted_query(Q, K, V, logit, prompt_lens, w, scale=None):
+    """Query q takes the visible set of q - 1 (the step before its own append)."""
+    B, Hq, T, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    scale = real.default_scale(d) if scale is None else scale
+    out = np.full((B, Hq, T, d), np.nan)
+    for b in range(B):
+        for h in range(Hkv):
+            alpha = real.eviction_decision(logit[b, h])
+            for q in range(int(prompt_lens[b])):
+                vis = real.visible(alpha, max(q - 1, 0), w)
+                for hq in range(h * G, (h + 1) * G):
+                    out[b, hq, q] = real.attend(Q[b, hq, q][None], K[b, h][vis], V[b, h][vis], scale)[0]
+    return out
+
+
 MUTANTS = {
     "window-exclusive": ("visible", _visible_exclusive),
     "query-misses-itself": ("visible", _visible_drops_self),
@@ -109,6 +145,8 @@ MUTANTS = {
     "logit-last-query-head": ("logits_from_channel", _channel_last_query_head),
     "zero-next-channel": ("without_channel", _zero_next_channel),
     "zero-nothing": ("without_channel", _zero_nothing),
+    "prefill-final-state": ("prefill_attention", _prefill_final_state),
+    "prefill-query-misses-itself": ("prefill_attention", _prefill_shifted_query),
 }
 
 
