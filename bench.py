@@ -19,6 +19,8 @@ CPU oracle on a bounded sample of the same workload.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --workload qwen-r1-32b-layer-dense --no-cpu-baseline
         # the dense baseline (nothing evicted, CR 1) through the same kernels
+    python bench.py --prefill-attention --steps 5 --warmup 1
+        # attention of every prompt query (after the prompt's compression)
     python bench.py --calib-copy-bytes N    # plain copy kernel, for counter scaling
 """
 from __future__ import annotations
@@ -42,6 +44,8 @@ HBM_PEAK_GBPS = 8000.0
 # MI355X Infinity Cache (MALL): a step whose live KV fits in it is reported as
 # cache-resident, its rate is not an HBM rate
 MALL_BYTES = 256 * 2**20
+# MI355X dense bf16 matrix-core peak (no sparsity)
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 KERNEL_SRCS = [os.path.join(ROOT, "learned_kv_cache_dms_amd", "csrc", f) for f in ("dms_kernels.hip", "dms_runtime.cpp")]
 
 
@@ -122,6 +126,86 @@ def cpu_baseline(wl, steps_per_unit: int, n_units: int):
     }
 
 
+def visible_pairs(Ld, lengths, w: int, G: int) -> int:
+    """Visible (query, key) pairs of every prompt query of every query head:
+    for query q, the unmarked positions below q - w plus the min(q + 1, w + 1)
+    positions of its window (counted from the logits on the device)."""
+    import torch
+    B, Hkv, T = Ld.shape
+    L = torch.as_tensor(lengths, device=Ld.device).view(B, 1, 1)
+    pos = torch.arange(T, device=Ld.device).view(1, 1, T)
+    unmarked = ((Ld <= 0) | torch.isnan(Ld)) & (pos < L)
+    cu = torch.cumsum(unmarked.to(torch.int64), dim=-1)            # unmarked in [0, i]
+    # far part of query q: cu[q - w - 1]; summed over q < P: sum of cu[i], i <= P - w - 2
+    far = torch.where(pos <= L - w - 2, cu, torch.zeros_like(cu)).sum()
+    near = torch.where(pos < L, torch.clamp(pos + 1, max=w + 1), torch.zeros_like(pos)).sum() * Hkv
+    return int((far + near).item()) * G
+
+
+def bench_prefill_attention(args):
+    """dms_prefill_attention on the workload's prompt (after its compression):
+    algorithmic TFLOP/s = 4 d flops per visible (query, key) pair (q.k and
+    p.v, 2 d each) over the mean event time of the call."""
+    import numpy as np
+    import torch
+    from learned_kv_cache_dms_amd import dms
+    from synth import device as dsynth
+    from synth import synth, workloads
+
+    torch.cuda.set_device(0)
+    wl = workloads.ALL[args.workload]()
+    B, Hq, Hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    lengths = wl.prompt_lengths()
+    max_len = int(lengths.max())
+    cache = dms.Cache(B, Hq, Hkv, d, wl.window, wl.max_tokens(), wl.pool_blocks(0), dtype=wl.dtype)
+    Kd = torch.empty((B, Hkv, max_len, d), dtype=tdt, device="cuda")
+    Vd = torch.empty_like(Kd)
+    Ld = torch.empty((B, Hkv, max_len), dtype=torch.float32, device="cuda")
+    Qd = torch.empty((B, Hq, max_len, d), dtype=tdt, device="cuda")
+    mb, ma = wl.layer_mu(0)
+    dsynth.fill(Kd, wl.seed, synth.STREAM_K, 0, 0)
+    dsynth.fill(Vd, wl.seed, synth.STREAM_V, 0, 0)
+    dsynth.fill(Qd, wl.seed, synth.STREAM_Q, 0, 0)
+    dsynth.logits(Ld, wl.seed, 0, 0, mb, ma, wl.pos_threshold)
+    cache.prefill(Kd, Vd, Ld, lengths)
+    out = torch.empty((B, Hq, max_len, d), dtype=torch.float32, device="cuda")
+    pairs = visible_pairs(Ld, lengths, wl.window, Hq // Hkv)
+    causal = int(sum(int(P) * (int(P) + 1) // 2 for P in lengths)) * Hq
+    flops = 4.0 * d * pairs
+    torch.cuda.synchronize()
+    W, K = args.warmup, args.steps
+    for _ in range(W):
+        cache.prefill_attention(Qd, Kd, Vd, out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        cache.prefill_attention(Qd, Kd, Vd, out)
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    mean_s = sum(ms) / K / 1e3
+    tflops = flops / mean_s / 1e12
+    res = {
+        "metric": "DMS-masked prompt attention, algorithmic TFLOP/s (every prompt query over its visible set)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(mean_s * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "prompt": max_len, "window": wl.window},
+        "visible_pairs": pairs, "causal_pairs": causal, "visible_fraction": round(pairs / causal, 4),
+        "prompt_tokens_per_s": round(float(np.sum(lengths)) / mean_s, 1),
+        "ms_median": round(statistics.median(ms), 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "dms_prefill_attention = prefill_attention_kernel",
+                     "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +221,9 @@ def main():
                          "logits (bf16-rounded) planted in channel --logit-channel of the keys (stored "
                          "zeroed) or of each group's first query head")
     ap.add_argument("--logit-channel", type=int, default=0)
+    ap.add_argument("--prefill-attention", action="store_true",
+                    help="time dms_prefill_attention on the workload's prompt instead of the decode step "
+                         "(use small --steps / --warmup: one call is a whole prompt)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -149,6 +236,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calib_copy_bytes:
         calib_copy(args.calib_copy_bytes)
+        return
+    if args.prefill_attention:
+        bench_prefill_attention(args)
         return
 
     from learned_kv_cache_dms_amd import dms

@@ -181,6 +181,27 @@ DMS_API int dms_prefill_compress_channel(dms_cache* c, const void* d_k, const vo
                                          int32_t source, int32_t channel, int32_t zero_channel,
                                          const int32_t* h_lengths, int32_t max_len, void* stream);
 
+/* Async.  Attention of every prompt query under the same visibility rule,
+   for the prompt that dms_prefill_compress (or _channel) has just stored:
+     out[b, hq, i, :] = sum_j softmax_j(scale * <q[b,hq,i], k_j>) v_j,
+   j over the tokens of (b, hq / G) visible to position i, for every
+   0 <= i < len_b: the unmarked positions below i - w and every position of
+   i - w .. i.  Sources: "Inference-Time Hyper-Scaling with KV Cache
+   Compression", third-party paper summary page, section "Method" (the
+   decisions act as an additive attention mask that is never built, the same
+   at every position, and it suits FlashAttention-style kernels).  The
+   positions below i - w are read from the cache (right after the prompt's
+   compression it holds exactly the unmarked ones among them), the window from
+   d_k / d_v; the decisions are not needed again.
+     d_q         : [B, Hq, max_len, d] of dtype, the prompt's queries
+     d_k, d_v    : [B, Hkv, max_len, d], the tensors the compression read
+     d_out       : [B, Hq, max_len, d] fp32; rows i >= len_b are not written
+   Errors: DMS_ERR_STATE unless the last call that changed the cache was a
+   successful prefill (an append or a reset in between makes it invalid);
+   DMS_ERR_ARG for NULL pointers or a max_len shorter than some prompt. */
+DMS_API int dms_prefill_attention(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, int32_t max_len,
+                                  float* d_out, void* stream);
+
 /* Async.  Grouped-query decode attention of the query at each sequence's
    last position over that sequence's visible tokens:
      out[b, hq, :] = sum_i softmax_i(scale * <q[b,hq], k_i>) v_i,

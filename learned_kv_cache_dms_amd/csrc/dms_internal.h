@@ -82,6 +82,10 @@ hipError_t launch_append(const Dev& p, int dtype, int d, const void* k, const vo
 hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const void* v,
                           const LogitSrc& logit, int zero_ch, const int32_t* h_lengths, int32_t max_len,
                           hipStream_t s);
+// Attention of every prompt query (q, k, v: the dense prompt tensors the
+// compression read); max_prompt = the longest prompt (grid size).
+hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,
+                                    int32_t max_len, int32_t max_prompt, float* out, hipStream_t s);
 hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s);
 // Work-groups of the attention kernel that fit on the device at once.
 int attention_resident_wgs(int dtype, int d, int num_cus);

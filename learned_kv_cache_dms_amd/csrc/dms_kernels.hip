@@ -1173,6 +1173,157 @@ __global__ __launch_bounds__(256) void reduce_kernel(Dev p, float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// attention of the prompt's own queries, after the prompt's compression
+// ---------------------------------------------------------------------------
+
+// Query q attends Vis(q) = { j < q - w : j unmarked } + [q - w, q] (every
+// token of the last w + 1 positions is visible, marked or not).  The first
+// part is exactly the cache slots whose position is below q - w: right after
+// the compression the cache holds every unmarked prompt token, and the marked
+// tokens it still holds sit at positions >= P - 1 - w >= q - w; its slots are
+// in position order.  The second part is read from the dense prompt.  The two
+// parts are disjoint and the decisions themselves are never needed.
+//
+// Work-group = 4 waves = kPfTile consecutive queries of one query head; wave
+// w owns kPfCols tiles of 16 queries, one query per MFMA column (where the
+// decode packs the group's heads), and streams the same key blocks as the
+// other waves.
+constexpr int kPfCols = 2;
+constexpr int kPfTile = 16 * kPfCols * kWavesPerWG;
+
+// Fragment (the cache block order) of 16 consecutive dense rows row0 ..
+// row0 + 15 of one (sequence, KV head), rows clamped to `last` (the clamped
+// rows are masked out by the caller; they only have to be finite).
+template <int ES, int D>
+__device__ __forceinline__ void load_frag_dense(Frag<ES, D>& f, const uint8_t* __restrict__ K,
+                                                const uint8_t* __restrict__ V, int row0, int last, int lane) {
+  using G = Geo<ES, D>;
+  // K: lane l carries row l % 16, 16-byte piece 4c + l / 16 of the row
+  const uint8_t* krow = K + (int64_t)min(row0 + (lane & 15), last) * D * ES;
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) f.k[c] = *(const u32x4*)(krow + c * 64 + 16 * (lane >> 4));
+  // V: lane l carries rows 4 (l / 16) + e, channel 16 (c kNJ + jj) + l % 16
+  const uint8_t* vrow[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vrow[e] = V + (int64_t)min(row0 + 4 * (lane >> 4) + e, last) * D * ES;
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) {
+    u32x4 val = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int jj = 0; jj < G::kNJ; ++jj) {
+      const int ch = 16 * (c * G::kNJ + jj) + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (ES == 2) {
+          const unsigned x = *(const uint16_t*)(vrow[e] + ch * 2);
+          val[jj * 2 + (e >> 1)] |= x << (16 * (e & 1));
+        } else {
+          val[e] = *(const uint32_t*)(vrow[e] + ch * 4);
+        }
+      }
+    }
+    f.v[c] = val;
+  }
+}
+
+// Grid (ceil(max_len_used / kPfTile), Hq, B).
+template <int ES, int D>
+__global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uint8_t* __restrict__ q,
+                                                                const uint8_t* __restrict__ k,
+                                                                const uint8_t* __restrict__ v, int32_t max_len,
+                                                                float* __restrict__ out) {
+  using G = Geo<ES, D>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.z, hq = blockIdx.y;
+  const int h = hq / p.G, u = b * p.Hkv + h;
+  const int P = __builtin_amdgcn_readfirstlane(p.pos[u]);
+  const int q0 = blockIdx.x * kPfTile;
+  if (q0 >= P) return;
+  const int w = p.R - 1;
+  const int qmax = min(q0 + kPfTile, P) - 1;
+  const int64_t unit_rows = ((int64_t)b * p.Hkv + h) * max_len;
+  const uint8_t* Ku = k + unit_rows * D * ES;
+  const uint8_t* Vu = v + unit_rows * D * ES;
+  const uint8_t* Qh = q + ((int64_t)b * p.Hq + hq) * max_len * D * ES;
+
+  int qc[kPfCols];
+  u32x4 qf[kPfCols][G::kChunks];
+  Acc<D> acc[kPfCols];
+#pragma unroll
+  for (int t = 0; t < kPfCols; ++t) {
+    qc[t] = q0 + 16 * (kPfCols * wave + t) + (lane & 15);
+    const uint8_t* qrow = Qh + (int64_t)min(qc[t], P - 1) * D * ES;
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) qf[t][c] = *(const u32x4*)(qrow + c * 64 + 16 * (lane >> 4));
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) acc[t].o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[t].m = -INFINITY;
+    acc[t].l = 0.f;
+  }
+  const int tb = 4 * (lane >> 4);
+
+  // Far part: the cache blocks whose first slot lies below qmax - w (slot
+  // positions increase, so they are a prefix); counted with one round of
+  // independent loads of the blocks' first positions.
+  const int n = __builtin_amdgcn_readfirstlane(p.n[u]);
+  const int nb = (n + 15) >> 4;
+  const int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
+  const int lim = qmax - w;
+  int nfar = 0;
+  for (int j0 = 0; j0 < nb; j0 += 64) {
+    const int j = j0 + lane;
+    int c = 0;
+    if (j < nb) c = p.blk_pos[(int64_t)bt[j] * 16] < lim ? 1 : 0;
+    nfar += wave_sum_i(c);
+  }
+  nfar = __builtin_amdgcn_readfirstlane(nfar);
+  for (int j = 0; j < nfar; ++j) {
+    const int blk = __builtin_amdgcn_readfirstlane(bt[j]);
+    Frag<ES, D> f;
+    load_frag<ES, D>(f, p.pool + (int64_t)blk * p.block_bytes, lane);
+    const int32_t* bp = p.blk_pos + (int64_t)blk * 16 + tb;
+    const int live = n - 16 * j;  // live slots of this block (>= 1)
+#pragma unroll
+    for (int t = 0; t < kPfCols; ++t) {
+      uint32_t mask = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (tb + r < live && bp[r] < qc[t] - w) mask |= 1u << (tb + r);
+      attend_block<ES, D>(f, qf[t], mask, lane, p.scale_log2e, acc[t]);
+    }
+  }
+
+  // Near part: dense rows max(0, q0 - w) .. qmax, all visible within the window.
+  for (int r0 = max(0, q0 - w); r0 <= qmax; r0 += 16) {
+    Frag<ES, D> f;
+    load_frag_dense<ES, D>(f, Ku, Vu, r0, P - 1, lane);
+#pragma unroll
+    for (int t = 0; t < kPfCols; ++t) {
+      uint32_t mask = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pos = r0 + tb + r;
+        if (pos <= qc[t] && pos >= qc[t] - w && pos < P) mask |= 1u << (tb + r);
+      }
+      attend_block<ES, D>(f, qf[t], mask, lane, p.scale_log2e, acc[t]);
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < kPfCols; ++t) {
+    // each lane's l sums its own 4 keys of every block: add the 4 lane groups
+    // of the column (all share the column's running max)
+    float lt = acc[t].l + __shfl_xor(acc[t].l, 16);
+    lt = lt + __shfl_xor(lt, 32);
+    if (qc[t] >= P) continue;
+    const float inv = 1.0f / lt;
+    float* orow = out + (((int64_t)b * p.Hq + hq) * max_len + qc[t]) * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(orow + 16 * j) = acc[t].o[j] * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // export: slot -> position of units [u0, u0 + count) into a staging area
 // ---------------------------------------------------------------------------
 
@@ -1267,6 +1418,24 @@ static hipError_t attention_t(const Dev& p, const void* q, float* out, int64_t g
                               (const int32_t*)p.btab, (const uint8_t*)q, out);
   if (e != hipSuccess || p.whole_units) return e;
   return launch(reduce_kernel<D>, dim3((p.U + kWavesPerWG - 1) / kWavesPerWG), dim3(64 * kWavesPerWG), s, p, out);
+}
+
+template <int ES, int D>
+static hipError_t prefill_attention_t(const Dev& p, const void* q, const void* k, const void* v, int32_t max_len,
+                                      int32_t max_prompt, float* out, hipStream_t s) {
+  const dim3 grid((unsigned)((max_prompt + kPfTile - 1) / kPfTile), (unsigned)p.Hq, (unsigned)p.B);
+  return launch(prefill_attention_kernel<ES, D>, grid, dim3(64 * kWavesPerWG), s, p, (const uint8_t*)q,
+                (const uint8_t*)k, (const uint8_t*)v, max_len, out);
+}
+
+hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,
+                                    int32_t max_len, int32_t max_prompt, float* out, hipStream_t s) {
+  if (max_prompt < 1) return hipSuccess;
+  if (dtype == 1)
+    return d == 128 ? prefill_attention_t<2, 128>(p, q, k, v, max_len, max_prompt, out, s)
+                    : prefill_attention_t<2, 64>(p, q, k, v, max_len, max_prompt, out, s);
+  return d == 128 ? prefill_attention_t<4, 128>(p, q, k, v, max_len, max_prompt, out, s)
+                  : prefill_attention_t<4, 64>(p, q, k, v, max_len, max_prompt, out, s);
 }
 
 template <int ES, int D>

@@ -21,6 +21,10 @@ struct dms_cache {
   int target_items;
   int64_t grid_wgs;
   std::vector<int32_t> len;  // host mirror of each sequence's length
+  // True from a successful prefill until the next append or reset: the cache
+  // then holds the prompt's visible tokens with slots in position order, which
+  // dms_prefill_attention relies on.
+  bool prompt_fresh = false;
 };
 
 // Split-plan target in quarters of the resident work-group count.
@@ -198,7 +202,10 @@ int dms_cache_reset(dms_cache* c, void* stream) {
   int st = check_device(c);
   if (st != DMS_OK) return st;
   st = hip_status(dms::launch_init(make_dev(c), (hipStream_t)stream));
-  if (st == DMS_OK) std::fill(c->len.begin(), c->len.end(), 0);
+  if (st == DMS_OK) {
+    std::fill(c->len.begin(), c->len.end(), 0);
+    c->prompt_fresh = false;
+  }
   return st;
 }
 
@@ -251,8 +258,10 @@ static int prefill_common(dms_cache* c, const void* d_k, const void* d_v, const 
   }
   st = hip_status(dms::launch_prefill(make_dev(c), c->cfg.dtype, c->L.d, d_k, d_v, ls, zero_ch, h_lengths,
                                       max_len, (hipStream_t)stream));
-  if (st == DMS_OK)
+  if (st == DMS_OK) {
     for (int b = 0; b < c->L.B; ++b) c->len[b] = h_lengths[b];
+    c->prompt_fresh = true;
+  }
   return st;
 }
 
@@ -264,8 +273,10 @@ static int append_common(dms_cache* c, const void* d_k, const void* d_v, const d
     if (x + 1 > c->L.max_tokens) return DMS_ERR_CAPACITY;
   st = hip_status(
       dms::launch_append(make_dev(c), c->cfg.dtype, c->L.d, d_k, d_v, ls, zero_ch, (hipStream_t)stream));
-  if (st == DMS_OK)
+  if (st == DMS_OK) {
     for (auto& x : c->len) ++x;
+    c->prompt_fresh = false;
+  }
   return st;
 }
 
@@ -297,6 +308,21 @@ int dms_append_step_channel(dms_cache* c, const void* d_k, const void* d_v, cons
   const int st = channel_logits(c, d_k, d_q, source, channel, zero_channel, 1, &ls);
   if (st != DMS_OK) return st;
   return append_common(c, d_k, d_v, ls, zero_channel ? channel : -1, stream);
+}
+
+int dms_prefill_attention(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, int32_t max_len,
+                          float* d_out, void* stream) {
+  if (!c || !d_q || !d_k || !d_v || !d_out || max_len < 1) return DMS_ERR_ARG;
+  int st = check_device(c);
+  if (st != DMS_OK) return st;
+  if (!c->prompt_fresh) return DMS_ERR_STATE;
+  int32_t longest = 0;
+  for (int32_t x : c->len) {
+    if (x > max_len) return DMS_ERR_ARG;
+    longest = std::max(longest, x);
+  }
+  return hip_status(dms::launch_prefill_attention(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_k, d_v, max_len,
+                                                  longest, d_out, (hipStream_t)stream));
 }
 
 int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stream) {

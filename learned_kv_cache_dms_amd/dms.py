@@ -97,6 +97,7 @@ def _load():
         "dms_append_step_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp]),
         "dms_prefill_compress_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, P(i32), i32, vp]),
         "dms_decode_attention": (ctypes.c_int, [vp, vp, vp, vp]),
+        "dms_prefill_attention": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, vp]),
         "dms_cache_stats": (ctypes.c_int, [vp, P(dms_stats), vp]),
         "dms_cache_export": (ctypes.c_int, [vp, i32, i32, P(i32), P(i32), P(i32), vp]),
         "dms_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -175,6 +176,10 @@ def dms_prefill_compress_channel(h: int, d_k: int, d_v: int, d_q: Optional[int],
     _check(lib.dms_prefill_compress_channel(h, d_k, d_v, d_q, int(source), int(channel),
                                             int(bool(zero_channel)), _i32p(L), int(max_len), stream),
            "dms_prefill_compress_channel")
+
+
+def dms_prefill_attention(h: int, d_q: int, d_k: int, d_v: int, max_len: int, d_out: int, stream: int = 0):
+    _check(lib.dms_prefill_attention(h, d_q, d_k, d_v, int(max_len), d_out, stream), "dms_prefill_attention")
 
 
 def dms_decode_attention(h: int, d_q: int, d_out: int, stream: int = 0):
@@ -259,6 +264,20 @@ class Cache:
         pv = self._chk(v, (self.B, self.Hkv, self.d), self.tdtype, "v")
         pq = None if q is None else self._chk(q, (self.B, self.Hq, self.d), self.tdtype, "q")
         dms_append_step_channel(self.handle, pk, pv, pq, self._SOURCES[source], channel, zero, self._stream())
+
+    def prefill_attention(self, q, k, v, out=None):
+        """Attention of every prompt query, right after prefill(k, v, ...):
+        q [B, Hq, max_len, d]; returns (or fills) out [B, Hq, max_len, d]
+        fp32, rows past each prompt's length left untouched."""
+        max_len = k.shape[2]
+        pq = self._chk(q, (self.B, self.Hq, max_len, self.d), self.tdtype, "q")
+        pk = self._chk(k, (self.B, self.Hkv, max_len, self.d), self.tdtype, "k")
+        pv = self._chk(v, (self.B, self.Hkv, max_len, self.d), self.tdtype, "v")
+        if out is None:
+            out = self._torch.zeros((self.B, self.Hq, max_len, self.d), dtype=self._torch.float32, device=q.device)
+        po = self._chk(out, (self.B, self.Hq, max_len, self.d), self._torch.float32, "out")
+        dms_prefill_attention(self.handle, pq, pk, pv, max_len, po, self._stream())
+        return out
 
     def attend(self, q, out=None):
         pq = self._chk(q, (self.B, self.Hq, self.d), self.tdtype, "q")
