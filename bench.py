@@ -21,6 +21,8 @@ CPU oracle on a bounded sample of the same workload.
         # the dense baseline (nothing evicted, CR 1) through the same kernels
     python bench.py --prefill-attention --steps 5 --warmup 1
         # attention of every prompt query (after the prompt's compression)
+    python bench.py --hyper-scaling
+        # KV budgets of a vanilla generation spent on longer / more DMS chains
     python bench.py --calib-copy-bytes N    # plain copy kernel, for counter scaling
 """
 from __future__ import annotations
@@ -206,6 +208,73 @@ def bench_prefill_attention(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_hyper_scaling(args):
+    """The hyper-scaling harness: the vanilla generation (8 chains x 16384
+    tokens after a 1024-token prompt, nothing evicted) sets a KV memory-read
+    budget and a peak-token budget; the DMS budget model picks the longest
+    generation per chain count within each; the vanilla run and three DMS
+    frontier points run end to end on the GPU, and their device-counted reads
+    are checked against the count implied by their decisions."""
+    import numpy as np
+    import torch
+    from learned_kv_cache_dms_amd import hyperscale as H
+    from synth import workloads
+
+    torch.cuda.set_device(0)
+    wl = workloads.ALL["qwen-r1-32b-hyperscale"]()
+    P, L0, W0 = wl.prompt_len, wl.decode_steps, wl.batch
+    max_len = 4 * L0
+    vanilla_model = H.BudgetModel(lambda pos: np.zeros(len(pos)), wl.window, P, max_len)
+    dms_model = H.BudgetModel(lambda pos: wl.marked_prob(0, pos), wl.window, P, max_len)
+    base = vanilla_model.config(W0, L0)
+    widths = [8, 16, 32, 64, 128, 256]
+    fr = {kind: H.frontier(dms_model, budget, kind, widths)
+          for kind, budget in (("reads", base.reads), ("peak", base.peak))}
+    picks = [("reads", 8), ("reads", 64), ("peak", 32)]
+    dense = dataclasses.replace(wl, mu_before=[-8.0], mu_after=None, pos_threshold=wl.pos_threshold)
+    runs = []
+    r = H.run_config(dense, W0, L0)
+    runs.append(("vanilla", W0, L0, r))
+    print(f"# vanilla {W0} x {L0}: {r.seconds:.3f} s, reads {r.reads_device} (exact {r.reads_exact})",
+          file=sys.stderr, flush=True)
+    for kind, wd in picks:
+        c = next(x for x in fr[kind] if x.width == wd)
+        r = H.run_config(wl, c.width, c.length)
+        runs.append((f"dms-{kind}-budget", c.width, c.length, r))
+        print(f"# dms {kind} {c.width} x {c.length}: {r.seconds:.3f} s, reads {r.reads_device} "
+              f"(exact {r.reads_exact})", file=sys.stderr, flush=True)
+    Hkv = wl.num_kv_heads
+    van = runs[0][3]
+    out_runs = []
+    for name, wd, ln, rr in runs:
+        out_runs.append({
+            "run": name, "chains": wd, "tokens_per_chain": ln, "tokens": wd * ln,
+            "decode_s": round(rr.seconds, 4), "tokens_per_s": round(rr.tokens_per_s, 1),
+            "reads_per_kv_head": rr.reads_device / Hkv, "reads_exact_match": rr.reads_device == rr.reads_exact,
+            "peak_per_kv_head": rr.peak_device / Hkv, "peak_exact_match": rr.peak_device == rr.peak_exact,
+            "reads_vs_budget": round(rr.reads_device / Hkv / base.reads, 4),
+            "peak_vs_budget": round(rr.peak_device / Hkv / base.peak, 4),
+            "kv_gbps": round(rr.kv_bytes_read / rr.seconds / 1e9, 1),
+            "tokens_vs_vanilla": round(wd * ln / (W0 * L0), 3),
+            "time_vs_vanilla": round(rr.seconds / van.seconds, 3),
+        })
+    best = out_runs[2]   # 64 chains within the vanilla read budget
+    res = {
+        "metric": "hyper-scaling: tokens generated within the vanilla KV memory-read budget, DMS / vanilla",
+        "value": best["tokens_vs_vanilla"], "unit": "x", "n_gpus": 1, "steps": int(sum(x["tokens_per_chain"] for x in out_runs)),
+        "warmup": 0, "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "prompt": P, "vanilla_chains": W0, "vanilla_tokens_per_chain": L0,
+                   "q_heads": wl.num_q_heads, "kv_heads": Hkv, "head_dim": wl.head_dim, "window": wl.window},
+        "budget_reads_per_kv_head": base.reads, "budget_peak_per_kv_head": base.peak,
+        "frontier": {k: [{"chains": c.width, "tokens_per_chain": c.length, "tokens": c.tokens,
+                          "tokens_vs_vanilla": round(c.tokens / base.tokens, 3)} for c in v] for k, v in fr.items()},
+        "runs": out_runs,
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +290,8 @@ def main():
                          "logits (bf16-rounded) planted in channel --logit-channel of the keys (stored "
                          "zeroed) or of each group's first query head")
     ap.add_argument("--logit-channel", type=int, default=0)
+    ap.add_argument("--hyper-scaling", action="store_true",
+                    help="run the hyper-scaling harness (vanilla budget, DMS frontier, end-to-end runs)")
     ap.add_argument("--prefill-attention", action="store_true",
                     help="time dms_prefill_attention on the workload's prompt instead of the decode step "
                          "(use small --steps / --warmup: one call is a whole prompt)")
@@ -239,6 +310,9 @@ def main():
         return
     if args.prefill_attention:
         bench_prefill_attention(args)
+        return
+    if args.hyper_scaling:
+        bench_hyper_scaling(args)
         return
 
     from learned_kv_cache_dms_amd import dms

@@ -145,6 +145,19 @@ def qwen_32b_dense() -> Workload:
     return w
 
 
+def qwen_32b_hyperscale() -> Workload:
+    """Base of the hyper-scaling harness: the Qwen-R1-32B-shaped layer with
+    a 1024-token prompt and the vanilla generation that sets the budget
+    (8 chains x 16384 tokens); the harness varies the chain count and length."""
+    w = qwen_32b()
+    w.name = "qwen-r1-32b-hyperscale"
+    w.batch, w.prompt_len, w.decode_steps = 8, 1024, 16384
+    w.seed = 1005
+    w.description = ("Qwen-R1-32B-shaped layer (40 Q / 8 KV heads, d 128, bf16, w 256, CR 4 below position "
+                     "10240 and 12 beyond), 1024-token prompt; the vanilla budget is 8 chains x 16384 tokens")
+    return w
+
+
 def full_32b() -> Workload:
     layers = 64
     crs = [4.0 + 8.0 * l / (layers - 1) for l in range(layers)]
@@ -157,4 +170,4 @@ def full_32b() -> Workload:
                     "(layer 63), 128 decode steps")
 
 
-ALL = {w().name: w for w in (tiny, llama_1b, qwen_7b, qwen_32b, qwen_32b_dense, full_32b)}
+ALL = {w().name: w for w in (tiny, llama_1b, qwen_7b, qwen_32b, qwen_32b_dense, qwen_32b_hyperscale, full_32b)}
