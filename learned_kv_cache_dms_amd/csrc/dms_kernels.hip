@@ -742,6 +742,122 @@ __device__ __forceinline__ void attend_block(const Frag<ES, D>& f, const u32x4 (
   }
 }
 
+// Two blocks (32 keys) per softmax step.  For bf16, S of both blocks, one
+// running-max update and rescale, then O^T += V^T P^T with 16x16x32 MFMAs.
+// Their k index runs over the lane group's 4 keys of block A, then the same 4
+// keys of block B, for both operands alike (a permutation of the sum).  The V
+// operand of channel tile j is therefore 8 bytes of block A next to 8 bytes
+// of block B, and it is loaded straight into that order.  For fp32 the pair
+// is two blocks computed one after the other.
+template <int ES, int D>
+struct PairFrag {
+  Frag<ES, D> a, b;
+};
+
+template <int D>
+struct PairFrag<2, D> {
+  u32x4 ka[Geo<2, D>::kChunks], kb[Geo<2, D>::kChunks];
+  u32x4 v[Geo<2, D>::kTiles];  // tile 2c + jj: {A keys tb..tb+3, B keys tb..tb+3} of channel 16(2c+jj) + l%16
+};
+
+// Loads blocks A and B of the pool (fragment order) as a pair.
+template <int ES, int D>
+__device__ __forceinline__ void load_pair(PairFrag<ES, D>& f, const uint8_t* blka, const uint8_t* blkb, int lane) {
+  using G = Geo<ES, D>;
+  if constexpr (ES == 2) {
+    const uint8_t* a = blka + lane * 16;
+    const uint8_t* b = blkb + lane * 16;
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) f.ka[c] = __builtin_nontemporal_load((const u32x4*)(a + c * 1024));
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) f.kb[c] = __builtin_nontemporal_load((const u32x4*)(b + c * 1024));
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const u32x2 x = __builtin_nontemporal_load((const u32x2*)(a + G::kHalf + c * 1024 + jj * 8));
+        const u32x2 y = __builtin_nontemporal_load((const u32x2*)(b + G::kHalf + c * 1024 + jj * 8));
+        f.v[2 * c + jj] = u32x4{x[0], x[1], y[0], y[1]};
+      }
+    }
+  } else {
+    load_frag<ES, D>(f.a, blka, lane);
+    load_frag<ES, D>(f.b, blkb, lane);
+  }
+}
+
+// The same pair order from two fragments already in registers.
+template <int ES, int D>
+__device__ __forceinline__ void make_pair(PairFrag<ES, D>& f, const Frag<ES, D>& fa, const Frag<ES, D>& fb) {
+  using G = Geo<ES, D>;
+  if constexpr (ES == 2) {
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) {
+      f.ka[c] = fa.k[c];
+      f.kb[c] = fb.k[c];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        f.v[2 * c + jj] = u32x4{fa.v[c][2 * jj], fa.v[c][2 * jj + 1], fb.v[c][2 * jj], fb.v[c][2 * jj + 1]};
+    }
+  } else {
+    f.a = fa;
+    f.b = fb;
+  }
+}
+
+template <int ES, int D>
+__device__ __forceinline__ void attend_pair(const PairFrag<ES, D>& f, const u32x4 (&qf)[Geo<ES, D>::kChunks],
+                                            uint32_t ma, uint32_t mb, int lane, float sl2e, Acc<D>& a) {
+  using G = Geo<ES, D>;
+  if constexpr (ES != 2) {
+    attend_block<ES, D>(f.a, qf, ma, lane, sl2e, a);
+    attend_block<ES, D>(f.b, qf, mb, lane, sl2e, a);
+  } else {
+    f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) {
+      SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.ka[c]),
+                                                    __builtin_bit_cast(bf16x8, qf[c]), SA, 0, 0, 0);
+      SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.kb[c]),
+                                                    __builtin_bit_cast(bf16x8, qf[c]), SB, 0, 0, 0);
+    }
+    const int tb = 4 * (lane >> 4);
+    float s[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s[r] = ((ma >> (tb + r)) & 1u) ? SA[r] * sl2e : -INFINITY;
+      s[4 + r] = ((mb >> (tb + r)) & 1u) ? SB[r] * sl2e : -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(a.m, bm);
+    const float mref = (mn == -INFINITY) ? 0.f : mn;
+    const float alpha = exp2_fast(a.m - mref);
+    float pr[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pr[r] = exp2_fast(s[r] - mref);
+    a.l = a.l * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+    a.m = mn;
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
+    unsigned hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hi[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
+      lo[i] = pack_bf16x2(pr[2 * i] - bf16_lo_to_f32(hi[i]), pr[2 * i + 1] - bf16_hi_to_f32(hi[i]));
+    }
+    const u32x4 hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
+    const bf16x8 PH = __builtin_bit_cast(bf16x8, hv), PL = __builtin_bit_cast(bf16x8, lv);
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) {
+      const bf16x8 A = __builtin_bit_cast(bf16x8, f.v[j]);
+      a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PH, a.o[j], 0, 0, 0);
+      a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PL, a.o[j], 0, 0, 0);
+    }
+  }
+}
+
 // Split-K decode attention.  A work item is a run of one (sequence, KV
 // head)'s blocks, processed by one work-group of 4 waves: wave w takes the
 // run's blocks w, w+4, w+8, ... so the work-group streams one contiguous run.
@@ -1269,44 +1385,97 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
   const int nb = (n + 15) >> 4;
   const int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
   const int lim = qmax - w;
-  int nfar = 0;
+  // nfar: blocks whose first slot lies below qmax - w.  nfull: blocks j whose
+  // next block starts at or below q0 - w; all 16 slots of such a block lie
+  // below q0 - w, so every key in it is far for every query of the tile.
+  // Slot positions increase, so both are prefixes; one round of independent
+  // loads of the blocks' first positions counts them.
+  int nfar = 0, nlow = 0;
   for (int j0 = 0; j0 < nb; j0 += 64) {
     const int j = j0 + lane;
-    int c = 0;
-    if (j < nb) c = p.blk_pos[(int64_t)bt[j] * 16] < lim ? 1 : 0;
+    int c = 0, d2 = 0;
+    if (j < nb) {
+      const int first = p.blk_pos[(int64_t)bt[j] * 16];
+      c = first < lim ? 1 : 0;
+      d2 = first <= q0 - w ? 1 : 0;
+    }
     nfar += wave_sum_i(c);
+    nlow += wave_sum_i(d2);
   }
   nfar = __builtin_amdgcn_readfirstlane(nfar);
-  for (int j = 0; j < nfar; ++j) {
-    const int blk = __builtin_amdgcn_readfirstlane(bt[j]);
-    Frag<ES, D> f;
-    load_frag<ES, D>(f, p.pool + (int64_t)blk * p.block_bytes, lane);
-    const int32_t* bp = p.blk_pos + (int64_t)blk * 16 + tb;
-    const int live = n - 16 * j;  // live slots of this block (>= 1)
+  const int nfull = min(max(__builtin_amdgcn_readfirstlane(nlow) - 1, 0), nfar);
+  auto blk_at = [&](int j, int jmax) { return __builtin_amdgcn_readfirstlane(bt[min(j, jmax)]); };
+  if (nfull > 0) {
+    // Whole blocks, in pairs, one pair loaded ahead of the one computed.
+    // Loads are unconditional: an index past the last whole block re-reads
+    // it, and its keys are masked out.  The scheduling barriers keep each
+    // pair's loads issued ahead of the previous pair's arithmetic (left alone,
+    // the scheduler sinks them next to their use, exposing their latency).
+    const int npair = (nfull + 1) >> 1;
+    auto fetch = [&](PairFrag<ES, D>& f, int i) {
+      const int ba = blk_at(2 * i, nfull - 1), bb = blk_at(2 * i + 1, nfull - 1);
+      load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
+    };
+    auto compute = [&](const PairFrag<ES, D>& f, int i) {
+      const uint32_t mb = 2 * i + 1 < nfull ? 0xffffu : 0u;
+#pragma unroll
+      for (int t = 0; t < kPfCols; ++t) attend_pair<ES, D>(f, qf[t], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
+    };
+    PairFrag<ES, D> f0, f1;
+    fetch(f0, 0);
+    for (int i = 0; i < npair; i += 2) {
+      fetch(f1, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f0, i);
+      if (i + 1 >= npair) break;
+      fetch(f0, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f1, i + 1);
+    }
+  }
+  // The far blocks that straddle q - w for some query of the tile: masked
+  // per slot position (a key is far for query q when its position is < q - w).
+  for (int j = nfull; j < nfar; j += 2) {
+    const int ba = blk_at(j, nfar - 1), bb = blk_at(j + 1, nfar - 1);
+    PairFrag<ES, D> f;
+    load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
+    const int4 pa = *(const int4*)(p.blk_pos + (int64_t)ba * 16 + tb);
+    const int4 pb = *(const int4*)(p.blk_pos + (int64_t)bb * 16 + tb);
+    const int lva = n - 16 * j, lvb = j + 1 < nfar ? n - 16 * (j + 1) : 0;  // live slots
 #pragma unroll
     for (int t = 0; t < kPfCols; ++t) {
-      uint32_t mask = 0;
+      const int lt = qc[t] - w;
+      uint32_t ma = 0, mb = 0;
+      const int xa[4] = {pa.x, pa.y, pa.z, pa.w}, xb[4] = {pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (tb + r < live && bp[r] < qc[t] - w) mask |= 1u << (tb + r);
-      attend_block<ES, D>(f, qf[t], mask, lane, p.scale_log2e, acc[t]);
+      for (int r = 0; r < 4; ++r) {
+        if (tb + r < lva && xa[r] < lt) ma |= 1u << (tb + r);
+        if (tb + r < lvb && xb[r] < lt) mb |= 1u << (tb + r);
+      }
+      attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
     }
   }
 
-  // Near part: dense rows max(0, q0 - w) .. qmax, all visible within the window.
-  for (int r0 = max(0, q0 - w); r0 <= qmax; r0 += 16) {
-    Frag<ES, D> f;
-    load_frag_dense<ES, D>(f, Ku, Vu, r0, P - 1, lane);
+  // Near part: dense rows max(0, q0 - w) .. qmax, all visible within the
+  // window, 32 rows per softmax step.
+  auto near_mask = [&](int r0, int t) -> uint32_t {
+    uint32_t m = 0;
 #pragma unroll
-    for (int t = 0; t < kPfCols; ++t) {
-      uint32_t mask = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = r0 + tb + r;
-        if (pos <= qc[t] && pos >= qc[t] - w && pos < P) mask |= 1u << (tb + r);
-      }
-      attend_block<ES, D>(f, qf[t], mask, lane, p.scale_log2e, acc[t]);
+    for (int r = 0; r < 4; ++r) {
+      const int pos = r0 + tb + r;
+      if (pos <= qc[t] && pos >= qc[t] - w && pos < P) m |= 1u << (tb + r);
     }
+    return m;
+  };
+  for (int r0 = max(0, q0 - w); r0 <= qmax; r0 += 32) {
+    Frag<ES, D> fa, fb;
+    load_frag_dense<ES, D>(fa, Ku, Vu, r0, P - 1, lane);
+    load_frag_dense<ES, D>(fb, Ku, Vu, r0 + 16, P - 1, lane);
+    PairFrag<ES, D> f;
+    make_pair<ES, D>(f, fa, fb);
+#pragma unroll
+    for (int t = 0; t < kPfCols; ++t)
+      attend_pair<ES, D>(f, qf[t], near_mask(r0, t), near_mask(r0 + 16, t), lane, p.scale_log2e, acc[t]);
   }
 
 #pragma unroll
