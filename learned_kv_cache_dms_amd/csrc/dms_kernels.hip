@@ -749,6 +749,10 @@ __device__ __forceinline__ void attend_block(const Frag<ES, D>& f, const u32x4 (
 // operand of channel tile j is therefore 8 bytes of block A next to 8 bytes
 // of block B, and it is loaded straight into that order.  For fp32 the pair
 // is two blocks computed one after the other.
+#ifndef DMS_PF_LAZY
+#define DMS_PF_LAZY 1
+#endif
+
 template <int ES, int D>
 struct PairFrag {
   Frag<ES, D> a, b;
@@ -822,25 +826,41 @@ __device__ __forceinline__ void attend_pair(const PairFrag<ES, D>& f, const u32x
                                                     __builtin_bit_cast(bf16x8, qf[c]), SB, 0, 0, 0);
     }
     const int tb = 4 * (lane >> 4);
+    // Raw scores, masked to -inf; the scale (> 0) is applied to the max and
+    // inside the exponent's fma, which keeps the max exact.
     float s[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      s[r] = ((ma >> (tb + r)) & 1u) ? SA[r] * sl2e : -INFINITY;
-      s[4 + r] = ((mb >> (tb + r)) & 1u) ? SB[r] * sl2e : -INFINITY;
+      s[r] = ((ma >> (tb + r)) & 1u) ? SA[r] : -INFINITY;
+      s[4 + r] = ((mb >> (tb + r)) & 1u) ? SB[r] : -INFINITY;
     }
     float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(a.m, bm);
+    const float mn = fmaxf(a.m, bm * sl2e);
     const float mref = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = exp2_fast(a.m - mref);
     float pr[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) pr[r] = exp2_fast(s[r] - mref);
-    a.l = a.l * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
-    a.m = mn;
+    for (int r = 0; r < 8; ++r) pr[r] = exp2_fast(fmaf(s[r], sl2e, -mref));
+    const float psum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+#if DMS_PF_LAZY
+    // Rescale only when some column's running max moved (after the first
+    // blocks it rarely does).  An unmoved max gives alpha = 1 exactly; a
+    // column with no key yet has o = l = 0, which any alpha leaves at 0.
+    if (__builtin_amdgcn_ballot_w64(mn != a.m) != 0) {
+      const float alpha = exp2_fast(a.m - mref);
+      a.l *= alpha;
+#pragma unroll
+      for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
+    }
+    a.l += psum;
+#else
+    const float alpha = exp2_fast(a.m - mref);
+    a.l = a.l * alpha + psum;
 #pragma unroll
     for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
+#endif
+    a.m = mn;
     unsigned hi[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1304,7 +1324,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(Dev p, float* __restrict__ 
 // w owns kPfCols tiles of 16 queries, one query per MFMA column (where the
 // decode packs the group's heads), and streams the same key blocks as the
 // other waves.
-constexpr int kPfCols = 2;
+#ifndef DMS_PF_COLS
+#define DMS_PF_COLS 3
+#endif
+constexpr int kPfCols = DMS_PF_COLS;
 constexpr int kPfTile = 16 * kPfCols * kWavesPerWG;
 
 // Fragment (the cache block order) of 16 consecutive dense rows row0 ..
