@@ -21,6 +21,8 @@ CPU oracle on a bounded sample of the same workload.
         # the dense baseline (nothing evicted, CR 1) through the same kernels
     python bench.py --prefill-attention --steps 5 --warmup 1
         # attention of every prompt query (after the prompt's compression)
+    python bench.py --chunk 16 --steps 30 --warmup 3
+        # several decode steps per call (dms_decode_chunk)
     python bench.py --hyper-scaling
         # KV budgets of a vanilla generation spent on longer / more DMS chains
     python bench.py --calib-copy-bytes N    # plain copy kernel, for counter scaling
@@ -275,6 +277,82 @@ def bench_hyper_scaling(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_chunk(args):
+    """dms_decode_chunk on the workload: after the prompt, chunks of C
+    tokens per sequence, each call timed with HIP events.  Live-KV bytes of a
+    call = the cached tokens it reads (the live count before the chunk) plus
+    the chunk's own rows, 2 d sizeof(dtype) each."""
+    import torch
+    from learned_kv_cache_dms_amd import dms
+    from synth import device as dsynth
+    from synth import synth, workloads
+
+    torch.cuda.set_device(0)
+    wl0 = workloads.ALL[args.workload]()
+    C, W, K = args.chunk, args.warmup, args.steps
+    wl = dataclasses.replace(wl0, decode_steps=C * (W + K))
+    B, Hq, Hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    esize = 2 if wl.dtype == "bf16" else 4
+    lengths = wl.prompt_lengths()
+    max_len = int(lengths.max())
+    cache = dms.Cache(B, Hq, Hkv, d, wl.window, wl.max_tokens(), wl.pool_blocks(0), dtype=wl.dtype)
+    Kd = torch.empty((B, Hkv, max_len, d), dtype=tdt, device="cuda")
+    Vd = torch.empty_like(Kd)
+    Ld = torch.empty((B, Hkv, max_len), dtype=torch.float32, device="cuda")
+    mb, ma = wl.layer_mu(0)
+    dsynth.fill(Kd, wl.seed, synth.STREAM_K, 0, 0)
+    dsynth.fill(Vd, wl.seed, synth.STREAM_V, 0, 0)
+    dsynth.logits(Ld, wl.seed, 0, 0, mb, ma, wl.pos_threshold)
+    cache.prefill(Kd, Vd, Ld, lengths)
+    torch.cuda.synchronize()
+    del Kd, Vd, Ld
+    n_calls = W + K
+    base = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    qs = torch.empty((n_calls, B, Hq, C, d), dtype=tdt, device="cuda")
+    ks = torch.empty((n_calls, B, Hkv, C, d), dtype=tdt, device="cuda")
+    vs = torch.empty_like(ks)
+    lgs = torch.empty((n_calls, B, Hkv, C), dtype=torch.float32, device="cuda")
+    for i in range(n_calls):
+        dsynth.fill(qs[i], wl.seed, synth.STREAM_Q, 0, 0, pos_base=base + i * C)
+        dsynth.fill(ks[i], wl.seed, synth.STREAM_K, 0, 0, pos_base=base + i * C)
+        dsynth.fill(vs[i], wl.seed, synth.STREAM_V, 0, 0, pos_base=base + i * C)
+        dsynth.logits(lgs[i], wl.seed, 0, 0, mb, ma, wl.pos_threshold, pos_base=base + i * C)
+    out = torch.empty((B, Hq, C, d), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for i in range(W):
+        cache.decode_chunk(qs[i], ks[i], vs[i], lgs[i], out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    live_before = []
+    torch.cuda.synchronize()
+    for i in range(K):
+        live_before.append(cache.stats()["live_tokens"])
+        ev[i][0].record()
+        cache.decode_chunk(qs[W + i], ks[W + i], vs[W + i], lgs[W + i], out)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    mean_s = sum(ms) / K / 1e3
+    kv_bytes = (sum(live_before) / K + B * Hkv * C) * 2 * d * esize
+    gbps = kv_bytes / mean_s / 1e9
+    res = {
+        "metric": "chunked decode tokens/sec (dms_decode_chunk, C tokens per sequence per call)",
+        "value": round(B * C / mean_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(mean_s * 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "context": max_len, "window": wl.window, "chunk": C},
+        "ms_median": round(statistics.median(ms), 5),
+        "live_kv_gbps": round(gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "dms_decode_chunk = chunk_attention_kernel + append_chunk_kernel",
+                     "algorithmic_bytes_per_launch": round(kv_bytes)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +368,8 @@ def main():
                          "logits (bf16-rounded) planted in channel --logit-channel of the keys (stored "
                          "zeroed) or of each group's first query head")
     ap.add_argument("--logit-channel", type=int, default=0)
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="time dms_decode_chunk with this many tokens per sequence per call")
     ap.add_argument("--hyper-scaling", action="store_true",
                     help="run the hyper-scaling harness (vanilla budget, DMS frontier, end-to-end runs)")
     ap.add_argument("--prefill-attention", action="store_true",
@@ -313,6 +393,9 @@ def main():
         return
     if args.hyper_scaling:
         bench_hyper_scaling(args)
+        return
+    if args.chunk:
+        bench_chunk(args)
         return
 
     from learned_kv_cache_dms_amd import dms

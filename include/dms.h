@@ -211,6 +211,27 @@ DMS_API int dms_prefill_attention(dms_cache* c, const void* d_q, const void* d_k
    Errors: DMS_ERR_STATE if some sequence has no token yet. */
 DMS_API int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stream);
 
+/* Async.  `chunk` decode steps at once: for every sequence b and every
+   0 <= j < chunk, position q_j = len_b + j is appended (decision,
+   retirement, store, as dms_append_step does, in order) and its query
+   attends the tokens visible to q_j:
+     out[b, hq, j, :] = attention of q[b, hq, j] over Vis(b, hq / G, q_j).
+   The same results as `chunk` calls of dms_append_step + dms_decode_attention
+   with the j-th slices (up to the order of floating-point sums), and the same
+   final cache.  Sources: as dms_append_step and dms_decode_attention; the
+   rule gives every position its own visible set whatever the order of work.
+   Every cached block is read once for all the chunk's queries.
+     d_q   : [B, Hq, chunk, d] of dtype
+     d_k, d_v: [B, Hkv, chunk, d] of dtype
+     d_logit: [B, Hkv, chunk] fp32
+     d_out : [B, Hq, chunk, d] fp32
+   Errors: DMS_ERR_ARG for NULL pointers, chunk < 1, or a cache whose
+   max_tokens exceeds 131072 (the pending-eviction bitmap of a sequence is
+   kept in on-chip memory); DMS_ERR_CAPACITY if some len_b + chunk >
+   max_tokens. */
+DMS_API int dms_decode_chunk(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, const float* d_logit,
+                             int32_t chunk, float* d_out, void* stream);
+
 /* Synchronises `stream`, then fills *out. */
 DMS_API int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream);
 

@@ -86,6 +86,12 @@ hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const v
 // compression read); max_prompt = the longest prompt (grid size).
 hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,
                                     int32_t max_len, int32_t max_prompt, float* out, hipStream_t s);
+// Decode of `chunk` consecutive tokens per sequence: attention of the chunk's
+// queries over the current cache and the chunk's rows, then the appends.
+hipError_t launch_decode_chunk(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,
+                               const float* logit, int chunk, float* out, hipStream_t s);
+// Longest block table (blocks per unit) the chunk decode supports.
+int chunk_max_blocks();
 hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s);
 // Work-groups of the attention kernel that fit on the device at once.
 int attention_resident_wgs(int dtype, int d, int num_cus);

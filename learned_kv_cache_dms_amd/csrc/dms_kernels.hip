@@ -208,71 +208,74 @@ __device__ __forceinline__ void write_fresh(uint8_t* blkp, const uint8_t* krow,
   }
 }
 
+// Appends the token at unit u's next position (one wave): decides alpha,
+// retires position q - R if it was marked (its slot is reused), stores the
+// row.  Returns the unit's live count afterwards.  Every per-unit value is
+// read through lane 0, the lane that writes it, so that consecutive calls of
+// one wave (a chunk) see their own updates in program order.
 template <int ES, int D>
-__global__ __launch_bounds__(256) void append_kernel(Dev p, const uint8_t* __restrict__ k,
-                                                     const uint8_t* __restrict__ v, LogitSrc logit,
-                                                     int zero_ch) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int u = blockIdx.x * kWavesPerWG + wave;
-  __shared__ unsigned s_live[kWavesPerWG];
-  unsigned live = 0;
-  if (u < p.U) {
-    const float lg = load_logit(logit, u / p.Hkv, u % p.Hkv, 0);
-    const bool alpha = lg > 0.0f;  // NaN compares false
-    const int q = p.pos[u];
-    const int r = q % p.R;
-    int32_t* ring = p.ring + (int64_t)u * p.R;
-    int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
-    const int s = ring[r];          // slot of position q - R if it was marked
-    const int n = p.n[u];
-    const uint8_t* krow = k + (int64_t)u * D * ES;
-    const uint8_t* vrow = v + (int64_t)u * D * ES;
-    int slot, blk = 0;
-    bool fresh = false, ok = true;
-    if (s >= 0) {  // retire position q - R, reuse its slot
-      slot = s;
-      blk = bt[slot >> 4];
-    } else {
-      slot = n;
-      if ((slot & 15) == 0) {
-        unsigned long long nb = 0;
-        if (lane == 0) nb = atomicAdd(&p.ctr->bump, 1ull);
-        nb = __shfl(nb, 0);
-        if (nb >= (unsigned long long)p.pool_blocks) {
-          ok = false;
-          if (lane == 0) atomicCAS(&p.ctr->sticky_error, 0, kErrOutOfBlocks);
-        } else {
-          blk = (int)nb;
-          fresh = true;
-          if (lane == 0) bt[slot >> 4] = blk;
-        }
+__device__ __forceinline__ unsigned append_token(const Dev& p, int u, int lane, const uint8_t* krow,
+                                                 const uint8_t* vrow, float lg, int zero_ch) {
+  const bool alpha = lg > 0.0f;  // NaN compares false
+  const int q = __builtin_amdgcn_readfirstlane(p.pos[u]);
+  const int r = q % p.R;
+  int32_t* ring = p.ring + (int64_t)u * p.R;
+  int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
+  const int s = __builtin_amdgcn_readfirstlane(ring[r]);  // slot of position q - R if it was marked
+  const int n = __builtin_amdgcn_readfirstlane(p.n[u]);
+  int slot, blk = 0;
+  bool fresh = false, ok = true;
+  if (s >= 0) {  // retire position q - R, reuse its slot
+    slot = s;
+    blk = __builtin_amdgcn_readfirstlane(bt[slot >> 4]);
+  } else {
+    slot = n;
+    if ((slot & 15) == 0) {
+      unsigned long long nb = 0;
+      if (lane == 0) nb = atomicAdd(&p.ctr->bump, 1ull);
+      nb = __shfl(nb, 0);
+      if (nb >= (unsigned long long)p.pool_blocks) {
+        ok = false;
+        if (lane == 0) atomicCAS(&p.ctr->sticky_error, 0, kErrOutOfBlocks);
       } else {
-        blk = bt[slot >> 4];
+        blk = (int)nb;
+        fresh = true;
+        if (lane == 0) bt[slot >> 4] = blk;
       }
-    }
-    const int t = slot & 15;
-    if (ok) {
-      uint8_t* dst = p.pool + (int64_t)blk * p.block_bytes;
-      if (fresh)
-        write_fresh<ES, D>(dst, krow, vrow, lane, zero_ch);
-      else
-        write_row<ES, D>(dst, t, krow, vrow, lane, zero_ch);
-      if (lane == 0) {
-        p.blk_pos[(int64_t)blk * 16 + t] = q;
-        if (fresh)
-          p.blk_mask[blk] = 1u;
-        else if (s < 0)
-          p.blk_mask[blk] |= 1u << t;
-        ring[r] = alpha ? slot : -1;
-        if (s < 0) p.n[u] = n + 1;
-      }
-      live = (s < 0) ? (unsigned)(n + 1) : (unsigned)n;
     } else {
-      if (lane == 0) ring[r] = -1;
-      live = (unsigned)n;
+      blk = __builtin_amdgcn_readfirstlane(bt[slot >> 4]);
     }
-    if (lane == 0) p.pos[u] = q + 1;
   }
+  const int t = slot & 15;
+  unsigned live;
+  if (ok) {
+    uint8_t* dst = p.pool + (int64_t)blk * p.block_bytes;
+    if (fresh)
+      write_fresh<ES, D>(dst, krow, vrow, lane, zero_ch);
+    else
+      write_row<ES, D>(dst, t, krow, vrow, lane, zero_ch);
+    if (lane == 0) {
+      p.blk_pos[(int64_t)blk * 16 + t] = q;
+      if (fresh)
+        p.blk_mask[blk] = 1u;
+      else if (s < 0)
+        p.blk_mask[blk] |= 1u << t;
+      ring[r] = alpha ? slot : -1;
+      if (s < 0) p.n[u] = n + 1;
+    }
+    live = (s < 0) ? (unsigned)(n + 1) : (unsigned)n;
+  } else {
+    if (lane == 0) ring[r] = -1;
+    live = (unsigned)n;
+  }
+  if (lane == 0) p.pos[u] = q + 1;
+  return live;
+}
+
+// Adds each work-group's live counts to live_token_steps (one atomic).
+__device__ __forceinline__ void add_live_token_steps(const Dev& p, unsigned long long live) {
+  __shared__ unsigned long long s_live[kWavesPerWG];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) s_live[wave] = live;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -281,6 +284,38 @@ __global__ __launch_bounds__(256) void append_kernel(Dev p, const uint8_t* __res
     for (int i = 0; i < kWavesPerWG; ++i) sum += s_live[i];
     atomicAdd(&p.ctr->live_token_steps, sum);
   }
+}
+
+// One token per (sequence, KV head): one wave per unit, 4 units per work-group.
+template <int ES, int D>
+__global__ __launch_bounds__(256) void append_kernel(Dev p, const uint8_t* __restrict__ k,
+                                                     const uint8_t* __restrict__ v, LogitSrc logit,
+                                                     int zero_ch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x * kWavesPerWG + wave;
+  unsigned live = 0;
+  if (u < p.U)
+    live = append_token<ES, D>(p, u, lane, k + (int64_t)u * D * ES, v + (int64_t)u * D * ES,
+                               load_logit(logit, u / p.Hkv, u % p.Hkv, 0), zero_ch);
+  add_live_token_steps(p, live);
+}
+
+// `chunk` consecutive tokens per unit, in order, as that many append_kernel
+// launches would: k, v [U, chunk, d], logit [U, chunk].
+template <int ES, int D>
+__global__ __launch_bounds__(256) void append_chunk_kernel(Dev p, const uint8_t* __restrict__ k,
+                                                           const uint8_t* __restrict__ v,
+                                                           const float* __restrict__ logit, int chunk) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x * kWavesPerWG + wave;
+  unsigned long long live = 0;
+  if (u < p.U) {
+    for (int j = 0; j < chunk; ++j) {
+      const int64_t row = (int64_t)u * chunk + j;
+      live += append_token<ES, D>(p, u, lane, k + row * D * ES, v + row * D * ES, logit[row], -1);
+    }
+  }
+  add_live_token_steps(p, live);
 }
 
 // ---------------------------------------------------------------------------
@@ -1516,6 +1551,213 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
 }
 
 // ---------------------------------------------------------------------------
+// decode of a chunk of consecutive tokens: attention, then the appends
+// ---------------------------------------------------------------------------
+
+// Chunk query j (position q0 + j, q0 = the unit's length before the chunk)
+// attends Vis(q0 + j), read before any token of the chunk is appended:
+//  - every cached token that is not a pending marked one (an unmarked token
+//    stays visible for good);
+//  - a pending marked token (a slot held by the ring) while its position is
+//    >= q0 + j - w;
+//  - chunk row i <= j when it is unmarked or i >= j - w.
+// Marked tokens that left the cache before the chunk are invisible to every
+// chunk query too, so this is exactly the visible set of each step.  The
+// pending slots come from the ring into a per-block bitmap in LDS.
+//
+// Work-group = 4 waves = one (sequence, KV head) unit and kPfTile columns;
+// column c = j G + g carries query head h G + g of chunk position j, so the
+// group's heads share every loaded block as in the decode kernel.
+constexpr int kChunkMaxBlocks = 8192;
+
+// NC tiles of 16 columns per wave.  Grid (U, ceil(chunk G / (64 NC))).
+// q [B, Hq, chunk, d]; k, v [B, Hkv,
+// chunk, d]; logit [B, Hkv, chunk]; out [B, Hq, chunk, d].
+//
+// The work-group's columns need 1 to 4 waves of NC tiles each.  When
+// they fit in one or two waves, the idle waves split the key stream instead
+// (4 or 2 ways: wave w takes every nsplit-th pair of blocks and of chunk
+// rows), and the waves of one tile group merge their softmax states through
+// LDS at the end, tile by tile.
+template <int ES, int D, int NC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && ES == 2 ? 2 : 1))) void chunk_attention_kernel(Dev p, const uint8_t* __restrict__ q,
+                                                              const uint8_t* __restrict__ k,
+                                                              const uint8_t* __restrict__ v,
+                                                              const float* __restrict__ logit, int chunk,
+                                                              float* __restrict__ out) {
+  using G = Geo<ES, D>;
+  __shared__ uint32_t pend[kChunkMaxBlocks];
+  __shared__ f32x4 mo[kWavesPerWG - 1][G::kTiles][64];
+  __shared__ float mm[kWavesPerWG - 1][64], ml[kWavesPerWG - 1][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x;
+  const int b = u / p.Hkv, h = u - b * p.Hkv;
+  const int n = __builtin_amdgcn_readfirstlane(p.n[u]);
+  const int nb = (n + 15) >> 4;
+  const int q0 = __builtin_amdgcn_readfirstlane(p.pos[u]);
+  const int w = p.R - 1;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) pend[i] = 0u;
+  __syncthreads();
+  const int32_t* ring = p.ring + (int64_t)u * p.R;
+  for (int r = threadIdx.x; r < p.R; r += blockDim.x) {
+    const int sl = ring[r];
+    if (sl >= 0 && sl < n) atomicOr(&pend[sl >> 4], 1u << (sl & 15));
+  }
+  __syncthreads();
+
+  const int ncol = chunk * p.G;
+  const int cwg = blockIdx.y * (16 * NC * kWavesPerWG);
+  const int wg_cols = min((16 * NC * kWavesPerWG), ncol - cwg);
+  const int need = (wg_cols + 16 * NC - 1) / (16 * NC);  // waves with columns
+  const int nsplit = need == 1 ? 4 : (need == 2 ? 2 : 1);
+  const int tg = wave / nsplit, sp = wave - tg * nsplit;
+  if (tg >= need) return;  // only when nsplit == 1: no barrier follows for this work-group
+  const int c0 = cwg + 16 * NC * tg;
+  const int tb = 4 * (lane >> 4);
+  int qj[NC], qg[NC];
+  u32x4 qf[NC][G::kChunks];
+  Acc<D> acc[NC];
+#pragma unroll
+  for (int t = 0; t < NC; ++t) {
+    const int col = min(c0 + 16 * t + (lane & 15), ncol - 1);
+    qj[t] = col / p.G;
+    qg[t] = col - qj[t] * p.G;
+    const uint8_t* qrow = q + (((int64_t)b * p.Hq + h * p.G + qg[t]) * chunk + qj[t]) * D * ES;
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) qf[t][c] = *(const u32x4*)(qrow + c * 64 + 16 * (lane >> 4));
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) acc[t].o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[t].m = -INFINITY;
+    acc[t].l = 0.f;
+  }
+
+  // Cached tokens: this wave's pairs of blocks i = sp, sp + nsplit, ...,
+  // one pair loaded ahead of the one computed.  Loads are unconditional
+  // (clamped indices; a pair past the wave's last is masked out).
+  const int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
+  const int npair = (nb + 1) >> 1;
+  const int cnt = sp < npair ? (npair - sp + nsplit - 1) / nsplit : 0;
+  if (cnt > 0) {
+    struct Meta {
+      int4 pa, pb;
+      uint32_t wa, wb;
+    };
+    auto fetch = [&](PairFrag<ES, D>& f, Meta& m, int kk) {
+      const int i = min(sp + nsplit * kk, npair - 1);
+      const int ja = 2 * i, jb = min(2 * i + 1, nb - 1);
+      const int ba = __builtin_amdgcn_readfirstlane(bt[ja]), bb = __builtin_amdgcn_readfirstlane(bt[jb]);
+      load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
+      m.pa = *(const int4*)(p.blk_pos + (int64_t)ba * 16 + tb);
+      m.pb = *(const int4*)(p.blk_pos + (int64_t)bb * 16 + tb);
+      m.wa = pend[ja];
+      m.wb = pend[jb];
+    };
+    auto compute = [&](const PairFrag<ES, D>& f, const Meta& m, int kk) {
+      const int i = sp + nsplit * kk;
+      const bool ok = i < npair;
+      const int ja = 2 * i;
+      const int lva = ok ? n - 16 * ja : 0, lvb = ok && ja + 1 < nb ? n - 16 * (ja + 1) : 0;
+      const int xa[4] = {m.pa.x, m.pa.y, m.pa.z, m.pa.w}, xb[4] = {m.pb.x, m.pb.y, m.pb.z, m.pb.w};
+#pragma unroll
+      for (int t = 0; t < NC; ++t) {
+        const int lt = q0 + qj[t] - w;  // a pending token is visible from position >= lt
+        uint32_t ma = 0, mb = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int bit = tb + r;
+          if (bit < lva && (!((m.wa >> bit) & 1u) || xa[r] >= lt)) ma |= 1u << bit;
+          if (bit < lvb && (!((m.wb >> bit) & 1u) || xb[r] >= lt)) mb |= 1u << bit;
+        }
+        attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
+      }
+    };
+    PairFrag<ES, D> f0, f1;
+    Meta m0, m1;
+    fetch(f0, m0, 0);
+    for (int kk = 0; kk < cnt; kk += 2) {
+      fetch(f1, m1, kk + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f0, m0, kk);
+      if (kk + 1 >= cnt) break;
+      fetch(f0, m0, kk + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f1, m1, kk + 1);
+    }
+  }
+
+  // The chunk's own rows, 32 per step, every nsplit-th step for this wave.
+  const uint8_t* Ku = k + (int64_t)u * chunk * D * ES;
+  const uint8_t* Vu = v + (int64_t)u * chunk * D * ES;
+  const float* lgu = logit + (int64_t)u * chunk;
+  for (int r0 = 32 * sp; r0 < chunk; r0 += 32 * nsplit) {
+    Frag<ES, D> fa, fb;
+    load_frag_dense<ES, D>(fa, Ku, Vu, r0, chunk - 1, lane);
+    load_frag_dense<ES, D>(fb, Ku, Vu, r0 + 16, chunk - 1, lane);
+    PairFrag<ES, D> f;
+    make_pair<ES, D>(f, fa, fb);
+    bool unmarked_a[4], unmarked_b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      unmarked_a[r] = !(lgu[min(r0 + tb + r, chunk - 1)] > 0.0f);
+      unmarked_b[r] = !(lgu[min(r0 + 16 + tb + r, chunk - 1)] > 0.0f);
+    }
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+      uint32_t ma = 0, mb = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ia = r0 + tb + r, ib = r0 + 16 + tb + r;
+        if (ia <= qj[t] && (unmarked_a[r] || ia >= qj[t] - w)) ma |= 1u << (tb + r);
+        if (ib <= qj[t] && (unmarked_b[r] || ib >= qj[t] - w)) mb |= 1u << (tb + r);
+      }
+      attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
+    }
+  }
+
+  // Merge the split waves' states (per lane: same column, same lane group),
+  // then normalise and write.  nsplit is uniform over the work-group, so every
+  // wave takes the same barriers.
+#pragma unroll
+  for (int t = 0; t < NC; ++t) {
+    if (nsplit > 1) {
+      if (sp > 0) {
+        const int slot = (tg * nsplit + sp) - tg - 1;  // the split waves' LDS slots: 0 .. 4 - need - 1
+#pragma unroll
+        for (int j = 0; j < G::kTiles; ++j) mo[slot][j][lane] = acc[t].o[j];
+        mm[slot][lane] = acc[t].m;
+        ml[slot][lane] = acc[t].l;
+      }
+      __syncthreads();
+      if (sp == 0) {
+        float M = acc[t].m;
+        for (int x = 1; x < nsplit; ++x) M = fmaxf(M, mm[tg * (nsplit - 1) + x - 1][lane]);
+        const float Mr = M == -INFINITY ? 0.f : M;
+        const float w0 = exp2_fast(acc[t].m - Mr);
+        float L = acc[t].l * w0;
+#pragma unroll
+        for (int j = 0; j < G::kTiles; ++j) acc[t].o[j] *= w0;
+        for (int x = 1; x < nsplit; ++x) {
+          const int slot = tg * (nsplit - 1) + x - 1;
+          const float wx = exp2_fast(mm[slot][lane] - Mr);
+          L += ml[slot][lane] * wx;
+#pragma unroll
+          for (int j = 0; j < G::kTiles; ++j) acc[t].o[j] += mo[slot][j][lane] * wx;
+        }
+        acc[t].l = L;
+      }
+      __syncthreads();
+    }
+    float lt = acc[t].l + __shfl_xor(acc[t].l, 16);
+    lt = lt + __shfl_xor(lt, 32);
+    if (sp != 0 || c0 + 16 * t + (lane & 15) >= ncol) continue;
+    const float inv = 1.0f / lt;
+    float* orow = out + (((int64_t)b * p.Hq + h * p.G + qg[t]) * chunk + qj[t]) * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(orow + 16 * j) = acc[t].o[j] * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // export: slot -> position of units [u0, u0 + count) into a staging area
 // ---------------------------------------------------------------------------
 
@@ -1629,6 +1871,46 @@ hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* 
   return d == 128 ? prefill_attention_t<4, 128>(p, q, k, v, max_len, max_prompt, out, s)
                   : prefill_attention_t<4, 64>(p, q, k, v, max_len, max_prompt, out, s);
 }
+
+// Columns per wave of the chunk attention: one tile when the chunk's columns
+// (chunk x G) fit in it; every wave then streams a quarter of the keys, and
+// two work-groups stay resident per CU.  Three tiles beyond, so that more
+// columns share every loaded block.  (Measured on the 32B-shaped layer, G =
+// 5: one tile was faster for chunks of 1, three tiles for 4 and 12.)
+#ifndef DMS_CHUNK_SMALL_COLS
+#define DMS_CHUNK_SMALL_COLS 16
+#endif
+
+template <int ES, int D, int NC>
+static hipError_t chunk_attention_t(const Dev& p, const void* q, const void* k, const void* v, const float* logit,
+                                    int chunk, float* out, hipStream_t s) {
+  const int ytiles = (chunk * p.G + 64 * NC - 1) / (64 * NC);
+  return launch(chunk_attention_kernel<ES, D, NC>, dim3((unsigned)p.U, (unsigned)ytiles), dim3(64 * kWavesPerWG), s,
+                p, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, logit, chunk, out);
+}
+
+template <int ES, int D>
+static hipError_t decode_chunk_t(const Dev& p, const void* q, const void* k, const void* v, const float* logit,
+                                 int chunk, float* out, hipStream_t s) {
+  const hipError_t e = chunk * p.G <= DMS_CHUNK_SMALL_COLS
+                           ? chunk_attention_t<ES, D, 1>(p, q, k, v, logit, chunk, out, s)
+                           : chunk_attention_t<ES, D, 3>(p, q, k, v, logit, chunk, out, s);
+  if (e != hipSuccess) return e;
+  const int blocks = (p.U + kWavesPerWG - 1) / kWavesPerWG;
+  return launch(append_chunk_kernel<ES, D>, dim3(blocks), dim3(64 * kWavesPerWG), s, p, (const uint8_t*)k,
+                (const uint8_t*)v, logit, chunk);
+}
+
+hipError_t launch_decode_chunk(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,
+                               const float* logit, int chunk, float* out, hipStream_t s) {
+  if (dtype == 1)
+    return d == 128 ? decode_chunk_t<2, 128>(p, q, k, v, logit, chunk, out, s)
+                    : decode_chunk_t<2, 64>(p, q, k, v, logit, chunk, out, s);
+  return d == 128 ? decode_chunk_t<4, 128>(p, q, k, v, logit, chunk, out, s)
+                  : decode_chunk_t<4, 64>(p, q, k, v, logit, chunk, out, s);
+}
+
+int chunk_max_blocks() { return kChunkMaxBlocks; }
 
 template <int ES, int D>
 static int resident_t(int num_cus) {

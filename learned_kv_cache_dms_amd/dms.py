@@ -98,6 +98,7 @@ def _load():
         "dms_prefill_compress_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, P(i32), i32, vp]),
         "dms_decode_attention": (ctypes.c_int, [vp, vp, vp, vp]),
         "dms_prefill_attention": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, vp]),
+        "dms_decode_chunk": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, vp]),
         "dms_cache_stats": (ctypes.c_int, [vp, P(dms_stats), vp]),
         "dms_cache_export": (ctypes.c_int, [vp, i32, i32, P(i32), P(i32), P(i32), vp]),
         "dms_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -180,6 +181,10 @@ def dms_prefill_compress_channel(h: int, d_k: int, d_v: int, d_q: Optional[int],
 
 def dms_prefill_attention(h: int, d_q: int, d_k: int, d_v: int, max_len: int, d_out: int, stream: int = 0):
     _check(lib.dms_prefill_attention(h, d_q, d_k, d_v, int(max_len), d_out, stream), "dms_prefill_attention")
+
+
+def dms_decode_chunk(h: int, d_q: int, d_k: int, d_v: int, d_logit: int, chunk: int, d_out: int, stream: int = 0):
+    _check(lib.dms_decode_chunk(h, d_q, d_k, d_v, d_logit, int(chunk), d_out, stream), "dms_decode_chunk")
 
 
 def dms_decode_attention(h: int, d_q: int, d_out: int, stream: int = 0):
@@ -277,6 +282,20 @@ class Cache:
             out = self._torch.zeros((self.B, self.Hq, max_len, self.d), dtype=self._torch.float32, device=q.device)
         po = self._chk(out, (self.B, self.Hq, max_len, self.d), self._torch.float32, "out")
         dms_prefill_attention(self.handle, pq, pk, pv, max_len, po, self._stream())
+        return out
+
+    def decode_chunk(self, q, k, v, logit, out=None):
+        """`chunk` decode steps at once: q [B, Hq, C, d], k, v [B, Hkv, C, d],
+        logit [B, Hkv, C] fp32; returns (or fills) out [B, Hq, C, d] fp32."""
+        C = k.shape[2]
+        pq = self._chk(q, (self.B, self.Hq, C, self.d), self.tdtype, "q")
+        pk = self._chk(k, (self.B, self.Hkv, C, self.d), self.tdtype, "k")
+        pv = self._chk(v, (self.B, self.Hkv, C, self.d), self.tdtype, "v")
+        pl = self._chk(logit, (self.B, self.Hkv, C), self._torch.float32, "logit")
+        if out is None:
+            out = self._torch.empty((self.B, self.Hq, C, self.d), dtype=self._torch.float32, device=q.device)
+        po = self._chk(out, (self.B, self.Hq, C, self.d), self._torch.float32, "out")
+        dms_decode_chunk(self.handle, pq, pk, pv, pl, C, po, self._stream())
         return out
 
     def attend(self, q, out=None):
