@@ -23,6 +23,8 @@ CPU oracle on a bounded sample of the same workload.
         # attention of every prompt query (after the prompt's compression)
     python bench.py --chunk 16 --steps 30 --warmup 3
         # several decode steps per call (dms_decode_chunk)
+    python bench.py --workload qwen-r1-32b-64-layer-step --steps 16 --warmup 4
+        # the whole 64-layer step (256 chains, prompts of 1K-32K tokens)
     python bench.py --hyper-scaling
         # KV budgets of a vanilla generation spent on longer / more DMS chains
     python bench.py --calib-copy-bytes N    # plain copy kernel, for counter scaling
@@ -353,6 +355,107 @@ def bench_chunk(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_full_step(args):
+    """A multi-layer decode step: one cache per layer, every timed step runs
+    dms_append_step + dms_decode_attention for every layer in order (as a
+    model would).  Tokens/s = batch / (time of one step over all layers)."""
+    import torch
+    from learned_kv_cache_dms_amd import dms
+    from synth import device as dsynth
+    from synth import synth, workloads
+
+    torch.cuda.set_device(0)
+    wl0 = workloads.ALL[args.workload]()
+    W, K = args.warmup, args.steps
+    wl = dataclasses.replace(wl0, decode_steps=W + K)
+    B, Hq, Hkv, d, NL = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_layers
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    esize = 2 if wl.dtype == "bf16" else 4
+    lengths = wl.prompt_lengths()
+    max_len = int(lengths.max())
+    caches = []
+    for l in range(NL):
+        c = dms.Cache(B, Hq, Hkv, d, wl.window, wl.max_tokens(), wl.pool_blocks(l, slack=1.1), dtype=wl.dtype)
+        Kd = torch.empty((B, Hkv, max_len, d), dtype=tdt, device="cuda")
+        Vd = torch.empty_like(Kd)
+        Ld = torch.empty((B, Hkv, max_len), dtype=torch.float32, device="cuda")
+        mb, ma = wl.layer_mu(l)
+        dsynth.fill(Kd, wl.seed, synth.STREAM_K, l, 0)
+        dsynth.fill(Vd, wl.seed, synth.STREAM_V, l, 0)
+        dsynth.logits(Ld, wl.seed, l, 0, mb, ma, wl.pos_threshold)
+        c.prefill(Kd, Vd, Ld, lengths)
+        del Kd, Vd, Ld
+        caches.append(c)
+        if l % 16 == 15:
+            torch.cuda.synchronize()
+            print(f"# {l + 1} layers prefilled", file=sys.stderr, flush=True)
+    S = W + K
+    base = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    qs = torch.empty((S, NL, B, Hq, d), dtype=tdt, device="cuda")
+    ks = torch.empty((S, NL, B, Hkv, d), dtype=tdt, device="cuda")
+    vs = torch.empty_like(ks)
+    lgs = torch.empty((S, NL, B, Hkv), dtype=torch.float32, device="cuda")
+    for t in range(S):
+        for l in range(NL):
+            mb, ma = wl.layer_mu(l)
+            dsynth.fill(qs[t, l], wl.seed, synth.STREAM_Q, l, 0, pos_base=base + t)
+            dsynth.fill(ks[t, l], wl.seed, synth.STREAM_K, l, 0, pos_base=base + t)
+            dsynth.fill(vs[t, l], wl.seed, synth.STREAM_V, l, 0, pos_base=base + t)
+            dsynth.logits(lgs[t, l], wl.seed, l, 0, mb, ma, wl.pos_threshold, pos_base=base + t)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for t in range(W):
+        for l in range(NL):
+            caches[l].append(ks[t, l], vs[t, l], lgs[t, l])
+            caches[l].attend(qs[t, l], out)
+    st0 = [c.stats() for c in caches]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K * NL)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        t = W + i
+        for l in range(NL):
+            caches[l].append(ks[t, l], vs[t, l], lgs[t, l])
+            ev[i * NL + l][0].record()
+            caches[l].attend(qs[t, l], out)
+            ev[i * NL + l][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st1 = [c.stats() for c in caches]
+    if any(x["sticky_error"] for x in st1):
+        raise SystemExit("device error during the run")
+    total_ms = start.elapsed_time(end)
+    attn_s = sum(a.elapsed_time(b) for a, b in ev) / 1e3          # all attention calls
+    live_tokens = sum(b["live_token_steps"] - a["live_token_steps"] for a, b in zip(st0, st1)) / K
+    live_bytes = live_tokens * 2 * d * esize                        # per step, all layers
+    step_s = total_ms / K / 1e3
+    achieved = live_bytes * K / attn_s / 1e9
+    seen = sum(x["seen_tokens"] for x in st1)
+    live_now = sum(x["live_tokens"] for x in st1)
+    res = {
+        "metric": METRIC, "value": round(B / step_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(total_ms / K, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "layers": NL, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "prompt_lengths": [int(lengths.min()), int(lengths.max())], "window": wl.window,
+                   "decode_steps": S},
+        "live_kv_gbps": round(achieved, 1), "live_kv_gbps_per_step": round(live_bytes / step_s / 1e9, 1),
+        "pct_peak_hbm": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "attention_ms_per_layer": round(attn_s / (K * NL) * 1e3, 5),
+        "live_bytes_per_step": round(live_bytes), "realized_cr": round(seen / live_now, 3),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "dms_decode_attention = attention_kernel (+ reduce_kernel when a unit is split)",
+                     "algorithmic_bytes_per_launch": round(live_bytes / NL)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -404,7 +507,8 @@ def main():
 
     wl0 = workloads.ALL[args.workload]()
     if wl0.num_layers != 1:
-        raise SystemExit("bench.py times one layer; choose a single-layer workload")
+        bench_full_step(args)
+        return
     W, K = args.warmup, args.steps
     wl = dataclasses.replace(wl0, decode_steps=W + K)
     B, Hq, Hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
