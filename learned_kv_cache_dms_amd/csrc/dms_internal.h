@@ -31,7 +31,7 @@ struct Layout {
   int64_t pool_blocks, block_bytes;
   int32_t item_floats;  // floats per attention partial: m[16], l[16], o[G][d]
   int64_t max_items;    // partial slots: the most items a plan can have
-  int64_t off_pool, off_btab, off_blkpos, off_blkmask, off_ring, off_n, off_pos, off_plan,
+  int64_t off_pool, off_btab, off_blkpos, off_blkmask, off_ring, off_n, off_pos, off_plan, off_order,
       off_ctr, off_part, total;
 };
 
@@ -46,10 +46,12 @@ struct Dev {
   int32_t* n;          // [U] slots in use
   int32_t* pos;        // [U] tokens appended so far (next position)
   int32_t* plan;       // [U][2] first work item and item count of the last attention call
+  int32_t* order;      // [U] the attention's unit order: position v holds unit order[v]
   Counters* ctr;
   float* part;         // [max_items][item_floats] attention partials
   int32_t B, Hq, Hkv, G, R, max_tokens, max_blocks, max_splits, U, item_floats, target_items;
   int32_t whole_units;  // 1: one work item per unit (never split); no split merge
+  int32_t ordered;      // 1: the attention visits units in `order`, 0: in index order
   int64_t pool_blocks, block_bytes;
   float scale_log2e;   // attention scale times log2(e)
 };

@@ -143,6 +143,7 @@ __global__ void init_kernel(Dev p) {
     p.pos[i] = 0;
     p.plan[2 * i] = 0;
     p.plan[2 * i + 1] = 0;
+    p.order[i] = (int32_t)i;
   }
   if (tid == 0) {
     p.ctr->bump = 0;
@@ -550,6 +551,9 @@ __device__ __forceinline__ int unit_items(int nb, long long tot, int target, int
   return min(max_splits, max(lo, (int)want));
 }
 
+// The unit at position v of the attention's unit order (vector form, any v < U).
+__device__ __forceinline__ int unit_at(const Dev& p, int v) { return p.ordered ? p.order[v] : v; }
+
 __device__ __forceinline__ long long plan_blocks(const Dev& p, int lane) {
   long long tot = 0;
   for (int b0 = 0; b0 < p.U; b0 += 64) {
@@ -561,9 +565,10 @@ __device__ __forceinline__ long long plan_blocks(const Dev& p, int lane) {
   return max(1LL, tot);
 }
 
-// The plan in LDS (units <= kPlanLdsUnits): n[u] = live slots of unit u and
-// start[u] = items of the units before u (start[U] = all items).  Built once
-// per work-group from n[], which is read in one round of loads.
+// The plan in LDS (units <= kPlanLdsUnits), over positions v of the unit
+// order: n[v] = live slots of unit unit_at(v) and start[v] = items of the
+// positions before v (start[U] = all items).  Built once per work-group from
+// n[], which is read in one round of loads.
 struct PlanLds {
   int start[kPlanLdsUnits + 1];
   int n[kPlanLdsUnits];
@@ -583,7 +588,7 @@ __device__ void plan_build_lds(const Dev& p, PlanLds& pl) {
   // the first wait.
   int x[kPer];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) x[k] = p.n[min(tid + kThreads * k, U - 1)];
+  for (int k = 0; k < kPer; ++k) x[k] = p.n[unit_at(p, min(tid + kThreads * k, U - 1))];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int u = tid + kThreads * k;
@@ -630,7 +635,8 @@ __device__ void plan_build_lds(const Dev& p, PlanLds& pl) {
 // Finds work item `item` in the LDS plan; false when item >= the total.  The
 // unit is the last u with start[u] <= item, found by a 64-way search (two
 // rounds for 4096 units).
-__device__ __forceinline__ bool plan_lookup_lds(const PlanLds& pl, int U, int item, int lane, Item& it) {
+__device__ __forceinline__ bool plan_lookup_lds(const Dev& p, const PlanLds& pl, int U, int item, int lane,
+                                                Item& it) {
   // readfirstlane: the compiler does not know an LDS value is uniform, and a
   // branch on it would make every item value a per-lane (vector) value
   if (item >= __builtin_amdgcn_readfirstlane(pl.start[U])) return false;
@@ -647,7 +653,7 @@ __device__ __forceinline__ bool plan_lookup_lds(const PlanLds& pl, int U, int it
   const int v = lane < len ? pl.start[lo + lane] : 0x7fffffff;
   const unsigned long long bal = __ballot(v <= item);
   const int u = __builtin_amdgcn_readfirstlane(lo + 63 - __clzll((long long)bal));
-  it.u = u;
+  it.u = p.ordered ? __builtin_amdgcn_readfirstlane(p.order[u]) : u;
   it.base = __builtin_amdgcn_readfirstlane(pl.start[u]);
   it.items = __builtin_amdgcn_readfirstlane(pl.start[u + 1]) - it.base;
   const int n = __builtin_amdgcn_readfirstlane(pl.n[u]);
@@ -671,7 +677,7 @@ __device__ __forceinline__ bool plan_find(const Dev& p, int lane, long long tot,
     const int uu = cur.b0 + lane;
     int nb = 0, cnt = 0, nn = 0;
     if (uu < p.U) {
-      nn = p.n[uu];
+      nn = p.n[unit_at(p, uu)];
       nb = (nn + 15) >> 4;
       cnt = unit_items(nb, tot, p.target_items, p.max_splits, p.whole_units != 0);
     }
@@ -680,7 +686,7 @@ __device__ __forceinline__ bool plan_find(const Dev& p, int lane, long long tot,
     const unsigned long long bal = __ballot(item >= start && item < start + cnt);
     if (bal) {
       const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)bal) - 1);
-      it.u = cur.b0 + src;
+      it.u = unit_at(p, cur.b0 + src);
       it.base = __builtin_amdgcn_readlane(start, src);
       it.items = __builtin_amdgcn_readlane(cnt, src);
       it.nblk = __builtin_amdgcn_readlane(nb, src);
@@ -1087,7 +1093,7 @@ struct Planner {
 
 __device__ __forceinline__ bool find_item(const Dev& p, const PlanLds& pl, Planner& pn, int item, int lane,
                                           Item& it) {
-  return pn.lds ? plan_lookup_lds(pl, p.U, item, lane, it) : plan_find(p, lane, pn.tot, item, it, pn.cur);
+  return pn.lds ? plan_lookup_lds(p, pl, p.U, item, lane, it) : plan_find(p, lane, pn.tot, item, it, pn.cur);
 }
 
 // Computes this wave's blocks of item A.  The wave reads one stream of

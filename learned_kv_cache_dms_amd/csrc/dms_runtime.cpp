@@ -25,6 +25,10 @@ struct dms_cache {
   // then holds the prompt's visible tokens with slots in position order, which
   // dms_prefill_attention relies on.
   bool prompt_fresh = false;
+  // The attention's unit order (in the workspace; identity after create and
+  // reset).  Set after a prefill with unequal prompt lengths, see balance_units.
+  bool ordered = false;
+  std::vector<int32_t> order;  // host copy, alive while the upload may still read it
 };
 
 // Split-plan target in quarters of the resident work-group count.
@@ -94,6 +98,8 @@ void make_layout(const dms_config* c, dms::Layout& L) {
   o = align_up(o + (int64_t)L.U * 4, kAlign);
   L.off_plan = o;
   o = align_up(o + (int64_t)L.U * 8, kAlign);
+  L.off_order = o;
+  o = align_up(o + (int64_t)L.U * 4, kAlign);
   L.off_ctr = o;
   o = align_up(o + (int64_t)sizeof(dms::Counters), kAlign);
   L.off_part = o;
@@ -112,6 +118,7 @@ dms::Dev make_dev(const dms_cache* c) {
   p.n = (int32_t*)(c->ws + L.off_n);
   p.pos = (int32_t*)(c->ws + L.off_pos);
   p.plan = (int32_t*)(c->ws + L.off_plan);
+  p.order = (int32_t*)(c->ws + L.off_order);
   p.ctr = (dms::Counters*)(c->ws + L.off_ctr);
   p.part = (float*)(c->ws + L.off_part);
   p.B = L.B;
@@ -126,6 +133,7 @@ dms::Dev make_dev(const dms_cache* c) {
   p.item_floats = L.item_floats;
   p.target_items = c->target_items;
   p.whole_units = c->L.U >= c->target_items ? 1 : 0;
+  p.ordered = c->ordered ? 1 : 0;
   p.pool_blocks = L.pool_blocks;
   p.block_bytes = L.block_bytes;
   const float scale = c->cfg.scale == 0.0f ? 1.0f / sqrtf((float)L.d) : c->cfg.scale;
@@ -205,6 +213,7 @@ int dms_cache_reset(dms_cache* c, void* stream) {
   if (st == DMS_OK) {
     std::fill(c->len.begin(), c->len.end(), 0);
     c->prompt_fresh = false;
+    c->ordered = false;
   }
   return st;
 }
@@ -246,6 +255,39 @@ static int channel_logits(const dms_cache* c, const void* d_k, const void* d_q, 
   return DMS_OK;
 }
 
+// With one work item per unit, work-group g of the G resident ones takes
+// units order[g], order[g + G], order[g + 2G], ...  After a prefill with
+// unequal prompt lengths the host orders the units by their sequence's
+// length, longest first, and deals them out in alternating directions (round
+// k: slot g gets the (kG + g)-th largest unit for even k, the (kG + G-1-g)-th
+// for odd k), so that every work-group's sum of lengths is about the mean.
+// The live counts of a sequence's heads follow its length, so this balances
+// the attention's load.  Appends keep the order valid (all lengths grow by
+// one).  Equal lengths keep the index order.
+static int balance_units(dms_cache* c, void* stream) {
+  const dms::Layout& L = c->L;
+  c->ordered = false;
+  if (L.U < c->target_items) return DMS_OK;  // units are split and balanced by blocks instead
+  const auto mm = std::minmax_element(c->len.begin(), c->len.end());
+  if (*mm.first == *mm.second) return DMS_OK;
+  std::vector<int32_t> s(L.U);
+  for (int u = 0; u < L.U; ++u) s[u] = u;
+  std::stable_sort(s.begin(), s.end(),
+                   [&](int32_t a, int32_t b) { return c->len[a / L.Hkv] > c->len[b / L.Hkv]; });
+  const int64_t G = c->grid_wgs;
+  c->order.assign(L.U, 0);
+  for (int64_t k0 = 0; k0 < L.U; k0 += G) {
+    const int64_t r = std::min<int64_t>(G, L.U - k0);
+    const bool rev = ((k0 / G) & 1) != 0;
+    for (int64_t g = 0; g < r; ++g) c->order[k0 + g] = s[k0 + (rev ? r - 1 - g : g)];
+  }
+  if (hipMemcpyAsync(c->ws + L.off_order, c->order.data(), (size_t)L.U * 4, hipMemcpyHostToDevice,
+                     (hipStream_t)stream) != hipSuccess)
+    return DMS_ERR_HIP;
+  c->ordered = true;
+  return DMS_OK;
+}
+
 static int prefill_common(dms_cache* c, const void* d_k, const void* d_v, const dms::LogitSrc& ls, int zero_ch,
                           const int32_t* h_lengths, int32_t max_len, void* stream) {
   int st = check_device(c);
@@ -261,6 +303,7 @@ static int prefill_common(dms_cache* c, const void* d_k, const void* d_v, const 
   if (st == DMS_OK) {
     for (int b = 0; b < c->L.B; ++b) c->len[b] = h_lengths[b];
     c->prompt_fresh = true;
+    st = balance_units(c, stream);
   }
   return st;
 }
