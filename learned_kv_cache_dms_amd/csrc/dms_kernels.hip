@@ -32,7 +32,20 @@
 //   O^T[c][g] += V^T[c][t] P[t][g]  MFMA, A = V fragment, B = P taken in
 //            place from the S registers (bf16: P split into hi + lo parts)
 // A unit whose blocks were split over several work items gets its partials
-// merged by reduce_kernel in a second launch (log-sum-exp).
+// merged by reduce_kernel in a second launch (log-sum-exp).  With at least as
+// many units as resident work-groups no unit is split and that launch is
+// skipped.
+//
+// The other kernels, in file order:
+//   * append_kernel / append_chunk_kernel: one token (or a chunk of tokens, in
+//     order) per unit: decision, retirement of position q - w - 1, store.
+//   * prefill_{count,alloc,scan,scatter}_kernel: a dense prompt compressed to
+//     the state of one append per token.
+//   * prefill_attention_kernel: every prompt query over its own visible set,
+//     from the compressed cache (positions below q - w) and the dense prompt
+//     (the window).
+//   * chunk_attention_kernel: the queries of a chunk of tokens over the cache
+//     as it stands plus the chunk's own rows, before the chunk's appends.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
