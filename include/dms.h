@@ -192,7 +192,9 @@ DMS_API int dms_prefill_compress_channel(dms_cache* c, const void* d_k, const vo
    at every position, and it suits FlashAttention-style kernels).  The
    positions below i - w are read from the cache (right after the prompt's
    compression it holds exactly the unmarked ones among them), the window from
-   d_k / d_v; the decisions are not needed again.
+   d_k / d_v; the decisions are not needed again.  After
+   dms_prefill_compress_channel with zero_channel, that key channel is read
+   as 0 from d_k as well, as the cache stores it.
      d_q         : [B, Hq, max_len, d] of dtype, the prompt's queries
      d_k, d_v    : [B, Hkv, max_len, d], the tensors the compression read
      d_out       : [B, Hq, max_len, d] fp32; rows i >= len_b are not written

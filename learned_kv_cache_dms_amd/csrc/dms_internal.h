@@ -85,9 +85,10 @@ hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const v
                           const LogitSrc& logit, int zero_ch, const int32_t* h_lengths, int32_t max_len,
                           hipStream_t s);
 // Attention of every prompt query (q, k, v: the dense prompt tensors the
-// compression read); max_prompt = the longest prompt (grid size).
+// compression read); max_prompt = the longest prompt (grid size); zero_ch >= 0:
+// the key channel the compression stored as 0 (read as 0 from k too).
 hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,
-                                    int32_t max_len, int32_t max_prompt, float* out, hipStream_t s);
+                                    int32_t max_len, int32_t max_prompt, int zero_ch, float* out, hipStream_t s);
 // Decode of `chunk` consecutive tokens per sequence: attention of the chunk's
 // queries over the current cache and the chunk's rows, then the appends.
 hipError_t launch_decode_chunk(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,

@@ -1389,12 +1389,17 @@ constexpr int kPfTile = 16 * kPfCols * kWavesPerWG;
 // rows are masked out by the caller; they only have to be finite).
 template <int ES, int D>
 __device__ __forceinline__ void load_frag_dense(Frag<ES, D>& f, const uint8_t* __restrict__ K,
-                                                const uint8_t* __restrict__ V, int row0, int last, int lane) {
+                                                const uint8_t* __restrict__ V, int row0, int last, int lane,
+                                                int zero_ch = -1) {
   using G = Geo<ES, D>;
   // K: lane l carries row l % 16, 16-byte piece 4c + l / 16 of the row
+  // (key channel zero_ch, when >= 0, is read as 0, as the cache stores it)
   const uint8_t* krow = K + (int64_t)min(row0 + (lane & 15), last) * D * ES;
 #pragma unroll
-  for (int c = 0; c < G::kChunks; ++c) f.k[c] = *(const u32x4*)(krow + c * 64 + 16 * (lane >> 4));
+  for (int c = 0; c < G::kChunks; ++c) {
+    f.k[c] = *(const u32x4*)(krow + c * 64 + 16 * (lane >> 4));
+    clear_channel<ES>(f.k[c], 4 * c + (lane >> 4), zero_ch);
+  }
   // V: lane l carries rows 4 (l / 16) + e, channel 16 (c kNJ + jj) + l % 16
   const uint8_t* vrow[4];
 #pragma unroll
@@ -1424,7 +1429,7 @@ template <int ES, int D>
 __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uint8_t* __restrict__ q,
                                                                 const uint8_t* __restrict__ k,
                                                                 const uint8_t* __restrict__ v, int32_t max_len,
-                                                                float* __restrict__ out) {
+                                                                int zero_ch, float* __restrict__ out) {
   using G = Geo<ES, D>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.z, hq = blockIdx.y;
@@ -1546,8 +1551,8 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
   };
   for (int r0 = max(0, q0 - w); r0 <= qmax; r0 += 32) {
     Frag<ES, D> fa, fb;
-    load_frag_dense<ES, D>(fa, Ku, Vu, r0, P - 1, lane);
-    load_frag_dense<ES, D>(fb, Ku, Vu, r0 + 16, P - 1, lane);
+    load_frag_dense<ES, D>(fa, Ku, Vu, r0, P - 1, lane, zero_ch);
+    load_frag_dense<ES, D>(fb, Ku, Vu, r0 + 16, P - 1, lane, zero_ch);
     PairFrag<ES, D> f;
     make_pair<ES, D>(f, fa, fb);
 #pragma unroll
@@ -1875,20 +1880,20 @@ static hipError_t attention_t(const Dev& p, const void* q, float* out, int64_t g
 
 template <int ES, int D>
 static hipError_t prefill_attention_t(const Dev& p, const void* q, const void* k, const void* v, int32_t max_len,
-                                      int32_t max_prompt, float* out, hipStream_t s) {
+                                      int32_t max_prompt, int zero_ch, float* out, hipStream_t s) {
   const dim3 grid((unsigned)((max_prompt + kPfTile - 1) / kPfTile), (unsigned)p.Hq, (unsigned)p.B);
   return launch(prefill_attention_kernel<ES, D>, grid, dim3(64 * kWavesPerWG), s, p, (const uint8_t*)q,
-                (const uint8_t*)k, (const uint8_t*)v, max_len, out);
+                (const uint8_t*)k, (const uint8_t*)v, max_len, zero_ch, out);
 }
 
 hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,
-                                    int32_t max_len, int32_t max_prompt, float* out, hipStream_t s) {
+                                    int32_t max_len, int32_t max_prompt, int zero_ch, float* out, hipStream_t s) {
   if (max_prompt < 1) return hipSuccess;
   if (dtype == 1)
-    return d == 128 ? prefill_attention_t<2, 128>(p, q, k, v, max_len, max_prompt, out, s)
-                    : prefill_attention_t<2, 64>(p, q, k, v, max_len, max_prompt, out, s);
-  return d == 128 ? prefill_attention_t<4, 128>(p, q, k, v, max_len, max_prompt, out, s)
-                  : prefill_attention_t<4, 64>(p, q, k, v, max_len, max_prompt, out, s);
+    return d == 128 ? prefill_attention_t<2, 128>(p, q, k, v, max_len, max_prompt, zero_ch, out, s)
+                    : prefill_attention_t<2, 64>(p, q, k, v, max_len, max_prompt, zero_ch, out, s);
+  return d == 128 ? prefill_attention_t<4, 128>(p, q, k, v, max_len, max_prompt, zero_ch, out, s)
+                  : prefill_attention_t<4, 64>(p, q, k, v, max_len, max_prompt, zero_ch, out, s);
 }
 
 // Columns per wave of the chunk attention: one tile when the chunk's columns

@@ -25,6 +25,7 @@ struct dms_cache {
   // then holds the prompt's visible tokens with slots in position order, which
   // dms_prefill_attention relies on.
   bool prompt_fresh = false;
+  int prompt_zero_ch = -1;  // the key channel that prefill stored as 0, or -1
   // The attention's unit order (in the workspace; identity after create and
   // reset).  Set after a prefill with unequal prompt lengths, see balance_units.
   bool ordered = false;
@@ -303,6 +304,7 @@ static int prefill_common(dms_cache* c, const void* d_k, const void* d_v, const 
   if (st == DMS_OK) {
     for (int b = 0; b < c->L.B; ++b) c->len[b] = h_lengths[b];
     c->prompt_fresh = true;
+    c->prompt_zero_ch = zero_ch;
     st = balance_units(c, stream);
   }
   return st;
@@ -365,7 +367,7 @@ int dms_prefill_attention(dms_cache* c, const void* d_q, const void* d_k, const 
     longest = std::max(longest, x);
   }
   return hip_status(dms::launch_prefill_attention(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_k, d_v, max_len,
-                                                  longest, d_out, (hipStream_t)stream));
+                                                  longest, c->prompt_zero_ch, d_out, (hipStream_t)stream));
 }
 
 int dms_decode_chunk(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, const float* d_logit,

@@ -78,6 +78,34 @@ def test_prefill_attention_every_row(case):
 
 
 @gpu
+@pytest.mark.parametrize("source,zero", [("k", True), ("q", False)], ids=["key-channel-zeroed", "query-channel"])
+def test_prefill_attention_after_channel_prefill(source, zero):
+    """A prompt compressed with the eviction logit read from a projection
+    channel (for keys, stored with that channel at 0): the prompt attention
+    reads the window's keys with the same channel at 0, and every row equals
+    the oracle on the channel-zeroed keys with the channel's logits."""
+    from learned_kv_cache_dms_amd import dms
+    from oracle import dms_oracle as O
+    B, Hq, Hkv, d, w, ch, dtype = 2, 8, 2, 128, 24, 37, "bf16"
+    P = np.array([260, 141])
+    T = int(P.max())
+    Q, K, V, _ = _host_prompt(5300, B, Hq, Hkv, T, d, dtype, 0.0)
+    G = Hq // Hkv
+    lg = O.logits_from_channel(K if source == "k" else Q, ch, 1 if source == "k" else G)
+    Kc = O.without_channel(K, ch) if zero else K
+    ref = O.prefill_attention(Q, Kc, V, lg, P, w)
+    cache = dms.Cache(B, Hq, Hkv, d, w, T + 1, B * Hkv * (T // 16 + 2), dtype=dtype)
+    Qd, Kd, Vd = _dev(Q, dtype), _dev(K, dtype), _dev(V, dtype)
+    cache.prefill_channel(Kd, Vd, P, source=source, channel=ch, zero=zero, q=Qd if source == "q" else None)
+    out = torch.full((B, Hq, T, d), 7.0, dtype=torch.float32, device="cuda")
+    cache.prefill_attention(Qd, Kd, Vd, out)
+    got = out.double().cpu().numpy()
+    for b in range(B):
+        err = float(np.max(np.abs(got[b, :, :P[b]] - ref[b, :, :P[b]])))
+        assert err <= TOL[dtype], (source, b, err)
+
+
+@gpu
 def test_prefill_attention_full_size_sampled_rows():
     """The Qwen-R1-32B-shaped layer (64 x 32768 tokens, 40 Q / 8 KV heads,
     d = 128, w = 256, CR 4 below position 10240 and 12 beyond): all rows on
