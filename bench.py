@@ -463,8 +463,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="qwen-r1-32b-layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=16)
-    ap.add_argument("--cpu-steps", type=int, default=192)
+    ap.add_argument("--cpu-units", type=int, default=24)
+    ap.add_argument("--cpu-steps", type=int, default=256)
     ap.add_argument("--calib-copy-bytes", type=int, default=0)
     ap.add_argument("--logit-source", choices=("array", "k", "q"), default="array",
                     help="where the append reads the eviction logit: the logit array, or the workload's "
