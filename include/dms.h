@@ -234,6 +234,17 @@ DMS_API int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, vo
 DMS_API int dms_decode_chunk(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, const float* d_logit,
                              int32_t chunk, float* d_out, void* stream);
 
+/* Async.  dms_decode_chunk with the eviction logits read from a projection
+   channel (as dms_append_step_channel, at every chunk position j):
+     logit[b, h, j] = fp32(d_k[b, h, j, channel])      for DMS_LOGIT_FROM_K
+     logit[b, h, j] = fp32(d_q[b, h * G, j, channel])  for DMS_LOGIT_FROM_Q
+   zero_channel (DMS_LOGIT_FROM_K only): the chunk's keys are stored with that
+   channel at 0 and attended that way.  Errors: those of dms_decode_chunk and
+   of dms_append_step_channel's arguments. */
+DMS_API int dms_decode_chunk_channel(dms_cache* c, const void* d_q, const void* d_k, const void* d_v,
+                                     int32_t source, int32_t channel, int32_t zero_channel, int32_t chunk,
+                                     float* d_out, void* stream);
+
 /* Synchronises `stream`, then fills *out. */
 DMS_API int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream);
 

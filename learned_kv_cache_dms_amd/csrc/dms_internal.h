@@ -92,7 +92,7 @@ hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* 
 // Decode of `chunk` consecutive tokens per sequence: attention of the chunk's
 // queries over the current cache and the chunk's rows, then the appends.
 hipError_t launch_decode_chunk(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,
-                               const float* logit, int chunk, float* out, hipStream_t s);
+                               const LogitSrc& logit, int zero_ch, int chunk, float* out, hipStream_t s);
 // Longest block table (blocks per unit) the chunk decode supports.
 int chunk_max_blocks();
 hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s);

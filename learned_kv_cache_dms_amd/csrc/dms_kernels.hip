@@ -315,18 +315,21 @@ __global__ __launch_bounds__(256) void append_kernel(Dev p, const uint8_t* __res
 }
 
 // `chunk` consecutive tokens per unit, in order, as that many append_kernel
-// launches would: k, v [U, chunk, d], logit [U, chunk].
+// launches would: k, v [U, chunk, d]; the logit of token j from `logit` at
+// position j.
 template <int ES, int D>
 __global__ __launch_bounds__(256) void append_chunk_kernel(Dev p, const uint8_t* __restrict__ k,
-                                                           const uint8_t* __restrict__ v,
-                                                           const float* __restrict__ logit, int chunk) {
+                                                           const uint8_t* __restrict__ v, LogitSrc logit,
+                                                           int zero_ch, int chunk) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int u = blockIdx.x * kWavesPerWG + wave;
   unsigned long long live = 0;
   if (u < p.U) {
+    const int b = u / p.Hkv, h = u - b * p.Hkv;
     for (int j = 0; j < chunk; ++j) {
       const int64_t row = (int64_t)u * chunk + j;
-      live += append_token<ES, D>(p, u, lane, k + row * D * ES, v + row * D * ES, logit[row], -1);
+      live += append_token<ES, D>(p, u, lane, k + row * D * ES, v + row * D * ES, load_logit(logit, b, h, j),
+                                  zero_ch);
     }
   }
   add_live_token_steps(p, live);
@@ -1606,9 +1609,8 @@ constexpr int kChunkMaxBlocks = 8192;
 template <int ES, int D, int NC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && ES == 2 ? 2 : 1))) void chunk_attention_kernel(Dev p, const uint8_t* __restrict__ q,
                                                               const uint8_t* __restrict__ k,
-                                                              const uint8_t* __restrict__ v,
-                                                              const float* __restrict__ logit, int chunk,
-                                                              float* __restrict__ out) {
+                                                              const uint8_t* __restrict__ v, LogitSrc logit,
+                                                              int zero_ch, int chunk, float* __restrict__ out) {
   using G = Geo<ES, D>;
   __shared__ uint32_t pend[kChunkMaxBlocks];
   __shared__ f32x4 mo[kWavesPerWG - 1][G::kTiles][64];
@@ -1712,18 +1714,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
   // The chunk's own rows, 32 per step, every nsplit-th step for this wave.
   const uint8_t* Ku = k + (int64_t)u * chunk * D * ES;
   const uint8_t* Vu = v + (int64_t)u * chunk * D * ES;
-  const float* lgu = logit + (int64_t)u * chunk;
   for (int r0 = 32 * sp; r0 < chunk; r0 += 32 * nsplit) {
     Frag<ES, D> fa, fb;
-    load_frag_dense<ES, D>(fa, Ku, Vu, r0, chunk - 1, lane);
-    load_frag_dense<ES, D>(fb, Ku, Vu, r0 + 16, chunk - 1, lane);
+    load_frag_dense<ES, D>(fa, Ku, Vu, r0, chunk - 1, lane, zero_ch);
+    load_frag_dense<ES, D>(fb, Ku, Vu, r0 + 16, chunk - 1, lane, zero_ch);
     PairFrag<ES, D> f;
     make_pair<ES, D>(f, fa, fb);
     bool unmarked_a[4], unmarked_b[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      unmarked_a[r] = !(lgu[min(r0 + tb + r, chunk - 1)] > 0.0f);
-      unmarked_b[r] = !(lgu[min(r0 + 16 + tb + r, chunk - 1)] > 0.0f);
+      unmarked_a[r] = !(load_logit(logit, b, h, min(r0 + tb + r, chunk - 1)) > 0.0f);
+      unmarked_b[r] = !(load_logit(logit, b, h, min(r0 + 16 + tb + r, chunk - 1)) > 0.0f);
     }
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
@@ -1906,32 +1907,32 @@ hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* 
 #endif
 
 template <int ES, int D, int NC>
-static hipError_t chunk_attention_t(const Dev& p, const void* q, const void* k, const void* v, const float* logit,
-                                    int chunk, float* out, hipStream_t s) {
+static hipError_t chunk_attention_t(const Dev& p, const void* q, const void* k, const void* v, const LogitSrc& logit,
+                                    int zero_ch, int chunk, float* out, hipStream_t s) {
   const int ytiles = (chunk * p.G + 64 * NC - 1) / (64 * NC);
   return launch(chunk_attention_kernel<ES, D, NC>, dim3((unsigned)p.U, (unsigned)ytiles), dim3(64 * kWavesPerWG), s,
-                p, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, logit, chunk, out);
+                p, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, logit, zero_ch, chunk, out);
 }
 
 template <int ES, int D>
-static hipError_t decode_chunk_t(const Dev& p, const void* q, const void* k, const void* v, const float* logit,
-                                 int chunk, float* out, hipStream_t s) {
+static hipError_t decode_chunk_t(const Dev& p, const void* q, const void* k, const void* v, const LogitSrc& logit,
+                                 int zero_ch, int chunk, float* out, hipStream_t s) {
   const hipError_t e = chunk * p.G <= DMS_CHUNK_SMALL_COLS
-                           ? chunk_attention_t<ES, D, 1>(p, q, k, v, logit, chunk, out, s)
-                           : chunk_attention_t<ES, D, 3>(p, q, k, v, logit, chunk, out, s);
+                           ? chunk_attention_t<ES, D, 1>(p, q, k, v, logit, zero_ch, chunk, out, s)
+                           : chunk_attention_t<ES, D, 3>(p, q, k, v, logit, zero_ch, chunk, out, s);
   if (e != hipSuccess) return e;
   const int blocks = (p.U + kWavesPerWG - 1) / kWavesPerWG;
   return launch(append_chunk_kernel<ES, D>, dim3(blocks), dim3(64 * kWavesPerWG), s, p, (const uint8_t*)k,
-                (const uint8_t*)v, logit, chunk);
+                (const uint8_t*)v, logit, zero_ch, chunk);
 }
 
 hipError_t launch_decode_chunk(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,
-                               const float* logit, int chunk, float* out, hipStream_t s) {
+                               const LogitSrc& logit, int zero_ch, int chunk, float* out, hipStream_t s) {
   if (dtype == 1)
-    return d == 128 ? decode_chunk_t<2, 128>(p, q, k, v, logit, chunk, out, s)
-                    : decode_chunk_t<2, 64>(p, q, k, v, logit, chunk, out, s);
-  return d == 128 ? decode_chunk_t<4, 128>(p, q, k, v, logit, chunk, out, s)
-                  : decode_chunk_t<4, 64>(p, q, k, v, logit, chunk, out, s);
+    return d == 128 ? decode_chunk_t<2, 128>(p, q, k, v, logit, zero_ch, chunk, out, s)
+                    : decode_chunk_t<2, 64>(p, q, k, v, logit, zero_ch, chunk, out, s);
+  return d == 128 ? decode_chunk_t<4, 128>(p, q, k, v, logit, zero_ch, chunk, out, s)
+                  : decode_chunk_t<4, 64>(p, q, k, v, logit, zero_ch, chunk, out, s);
 }
 
 int chunk_max_blocks() { return kChunkMaxBlocks; }

@@ -370,21 +370,35 @@ int dms_prefill_attention(dms_cache* c, const void* d_q, const void* d_k, const 
                                                   longest, c->prompt_zero_ch, d_out, (hipStream_t)stream));
 }
 
-int dms_decode_chunk(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, const float* d_logit,
-                     int32_t chunk, float* d_out, void* stream) {
-  if (!c || !d_q || !d_k || !d_v || !d_logit || !d_out || chunk < 1) return DMS_ERR_ARG;
+static int chunk_common(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, const dms::LogitSrc& ls,
+                        int zero_ch, int32_t chunk, float* d_out, void* stream) {
   if (c->L.max_blocks > dms::chunk_max_blocks()) return DMS_ERR_ARG;
   int st = check_device(c);
   if (st != DMS_OK) return st;
   for (int32_t x : c->len)
     if ((int64_t)x + chunk > c->L.max_tokens) return DMS_ERR_CAPACITY;
-  st = hip_status(dms::launch_decode_chunk(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_k, d_v, d_logit, chunk, d_out,
-                                           (hipStream_t)stream));
+  st = hip_status(dms::launch_decode_chunk(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_k, d_v, ls, zero_ch, chunk,
+                                           d_out, (hipStream_t)stream));
   if (st == DMS_OK) {
     for (auto& x : c->len) x += chunk;
     c->prompt_fresh = false;
   }
   return st;
+}
+
+int dms_decode_chunk(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, const float* d_logit,
+                     int32_t chunk, float* d_out, void* stream) {
+  if (!c || !d_q || !d_k || !d_v || !d_logit || !d_out || chunk < 1) return DMS_ERR_ARG;
+  return chunk_common(c, d_q, d_k, d_v, array_logits(c, d_logit, chunk), -1, chunk, d_out, stream);
+}
+
+int dms_decode_chunk_channel(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, int32_t source,
+                             int32_t channel, int32_t zero_channel, int32_t chunk, float* d_out, void* stream) {
+  if (!c || !d_q || !d_k || !d_v || !d_out || chunk < 1) return DMS_ERR_ARG;
+  dms::LogitSrc ls{};
+  const int st = channel_logits(c, d_k, d_q, source, channel, zero_channel, chunk, &ls);
+  if (st != DMS_OK) return st;
+  return chunk_common(c, d_q, d_k, d_v, ls, zero_channel ? channel : -1, chunk, d_out, stream);
 }
 
 int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stream) {

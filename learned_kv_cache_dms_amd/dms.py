@@ -99,6 +99,7 @@ def _load():
         "dms_decode_attention": (ctypes.c_int, [vp, vp, vp, vp]),
         "dms_prefill_attention": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, vp]),
         "dms_decode_chunk": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, vp]),
+        "dms_decode_chunk_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]),
         "dms_cache_stats": (ctypes.c_int, [vp, P(dms_stats), vp]),
         "dms_cache_export": (ctypes.c_int, [vp, i32, i32, P(i32), P(i32), P(i32), vp]),
         "dms_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -185,6 +186,12 @@ def dms_prefill_attention(h: int, d_q: int, d_k: int, d_v: int, max_len: int, d_
 
 def dms_decode_chunk(h: int, d_q: int, d_k: int, d_v: int, d_logit: int, chunk: int, d_out: int, stream: int = 0):
     _check(lib.dms_decode_chunk(h, d_q, d_k, d_v, d_logit, int(chunk), d_out, stream), "dms_decode_chunk")
+
+
+def dms_decode_chunk_channel(h: int, d_q: int, d_k: int, d_v: int, source: int, channel: int, zero_channel: bool,
+                             chunk: int, d_out: int, stream: int = 0):
+    _check(lib.dms_decode_chunk_channel(h, d_q, d_k, d_v, int(source), int(channel), int(bool(zero_channel)),
+                                        int(chunk), d_out, stream), "dms_decode_chunk_channel")
 
 
 def dms_decode_attention(h: int, d_q: int, d_out: int, stream: int = 0):
@@ -296,6 +303,19 @@ class Cache:
             out = self._torch.empty((self.B, self.Hq, C, self.d), dtype=self._torch.float32, device=q.device)
         po = self._chk(out, (self.B, self.Hq, C, self.d), self._torch.float32, "out")
         dms_decode_chunk(self.handle, pq, pk, pv, pl, C, po, self._stream())
+        return out
+
+    def decode_chunk_channel(self, q, k, v, source="k", channel=0, zero=False, out=None):
+        """decode_chunk with the eviction logits read from channel `channel`
+        of the keys (source "k") or of each group's first query head ("q")."""
+        C = k.shape[2]
+        pq = self._chk(q, (self.B, self.Hq, C, self.d), self.tdtype, "q")
+        pk = self._chk(k, (self.B, self.Hkv, C, self.d), self.tdtype, "k")
+        pv = self._chk(v, (self.B, self.Hkv, C, self.d), self.tdtype, "v")
+        if out is None:
+            out = self._torch.empty((self.B, self.Hq, C, self.d), dtype=self._torch.float32, device=q.device)
+        po = self._chk(out, (self.B, self.Hq, C, self.d), self._torch.float32, "out")
+        dms_decode_chunk_channel(self.handle, pq, pk, pv, self._SOURCES[source], channel, zero, C, po, self._stream())
         return out
 
     def attend(self, q, out=None):

@@ -82,6 +82,7 @@ def test_null_handle_calls_are_argument_errors():
     assert L.dms_decode_attention(None, 1, 1, None) == dms.DMS_ERR_ARG
     assert L.dms_prefill_attention(None, 1, 1, 1, 1, 1, None) == dms.DMS_ERR_ARG
     assert L.dms_decode_chunk(None, 1, 1, 1, 1, 1, 1, None) == dms.DMS_ERR_ARG
+    assert L.dms_decode_chunk_channel(None, 1, 1, 1, 0, 0, 0, 1, 1, None) == dms.DMS_ERR_ARG
     assert L.dms_prefill_compress(None, 1, 1, 1, None, 1, None) == dms.DMS_ERR_ARG
     assert L.dms_append_step_channel(None, 1, 1, None, 0, 0, 0, None) == dms.DMS_ERR_ARG
     assert L.dms_prefill_compress_channel(None, 1, 1, None, 0, 0, 0, None, 1, None) == dms.DMS_ERR_ARG

@@ -98,6 +98,46 @@ def test_chunks_match_oracle(case):
 
 
 @gpu
+@pytest.mark.parametrize("source,zero,ch", [("k", True, 0), ("k", False, 91), ("q", False, 5)],
+                         ids=["key-channel-zeroed", "key-channel", "query-channel"])
+def test_chunks_with_channel_logits(source, zero, ch):
+    """Prompt and chunks with the eviction logit read from a projection
+    channel (dms_prefill_compress_channel, dms_decode_chunk_channel): every
+    output row and the state after every chunk against the oracle's
+    step-by-step decode with the same logits and, when zeroed, keys."""
+    from learned_kv_cache_dms_amd import dms
+    from oracle import dms_oracle as O
+    B, Hq, Hkv, d, w, dtype = 2, 8, 2, 128, 10, "bf16"
+    P = np.array([90, 33])
+    chunks = [5, 19, 1]
+    steps = sum(chunks)
+    T = int(P.max()) + steps
+    Q, K, V, _ = _host(6200 + ch, B, Hq, Hkv, T, d, dtype, 0.0)
+    ref = O.decode_batch_channel(Q, K, V, P, steps, w, source, ch, zero)
+    cache = dms.Cache(B, Hq, Hkv, d, w, T, B * Hkv * (T // 16 + 2), dtype=dtype)
+    pmax = int(P.max())
+    Kp, Vp, Qp = (_dev(np.ascontiguousarray(X[:, :, :pmax]), dtype) for X in (K, V, Q))
+    cache.prefill_channel(Kp, Vp, P, source=source, channel=ch, zero=zero, q=Qp if source == "q" else None)
+    t0 = 0
+    for C in chunks:
+        q = _dev(_slices(Q, P, t0, C), dtype)
+        k = _dev(_slices(K, P, t0, C), dtype)
+        v = _dev(_slices(V, P, t0, C), dtype)
+        out = cache.decode_chunk_channel(q, k, v, source=source, channel=ch, zero=zero)
+        torch.cuda.synchronize()
+        err = float(np.max(np.abs(out.double().cpu().numpy() - ref["out"][t0:t0 + C].transpose(1, 2, 0, 3))))
+        assert err <= TOL[dtype], (source, zero, t0, C, err)
+        sp, rg, n = cache.export()
+        for b in range(B):
+            for h in range(Hkv):
+                rec = ref["records"][(b, h)][t0 + C - 1]
+                u = b * Hkv + h
+                assert np.array_equal(np.sort(sp[u][sp[u] >= 0]), rec.visible), (source, t0, b, h)
+                assert np.array_equal(np.sort(sp[u][rg[u][rg[u] >= 0]]), rec.pending), (source, t0, b, h)
+        t0 += C
+
+
+@gpu
 def test_chunk_equals_token_steps():
     """The same tokens through dms_decode_chunk and through one
     dms_append_step + dms_decode_attention per token: identical logical
