@@ -247,6 +247,103 @@ def prefill_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, logit: np.nda
 
 
 # ----------------------------------------------------------------------------
+# Training-time relaxation (summary page, "Method": the binary decision is
+# trained through a Gumbel-sigmoid reparametrisation at low temperature with a
+# logit offset gamma; the decisions enter attention as an additive mask).
+# Readings: alpha_i = sigmoid((logit_i + gamma + g_i) / tau) with logistic
+# noise g_i supplied by the caller; for query q and key i <= q the additive
+# bias is 0 while q - i <= w and log(1 - alpha_i) after, which is the hard rule
+# exactly when alpha is 0 or 1.
+# ----------------------------------------------------------------------------
+
+def soft_decision_arg(logit, noise, gamma: float, tau: float) -> np.ndarray:
+    """x_i = (logit_i + gamma + g_i) / tau, so that alpha_i = sigmoid(x_i)."""
+    return (np.asarray(logit, np.float64) + gamma + np.asarray(noise, np.float64)) / tau
+
+
+def soft_bias(x: np.ndarray) -> np.ndarray:
+    """log(1 - sigmoid(x)) = -softplus(x), evaluated without overflow."""
+    return -np.logaddexp(0.0, x)
+
+
+def soft_attention(Q, K, V, logit, noise, w: int, gamma: float, tau: float,
+                   scale: Optional[float] = None) -> Dict:
+    """Causal attention of every position with the relaxed mask.
+
+    Q: [B, Hq, T, d]; K, V: [B, Hkv, T, d]; logit, noise: [B, Hkv, T].
+    Returns {'out': [B, Hq, T, d], 'lse': [B, Hq, T]} in float64 (lse: the
+    natural log of each row's softmax denominator, for the backward).
+    """
+    B, Hq, T, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = default_scale(d)
+    out = np.zeros((B, Hq, T, d))
+    lse = np.zeros((B, Hq, T))
+    pos = np.arange(T)
+    far = (pos[:, None] - pos[None, :]) > w            # [q, i]
+    causal = pos[None, :] <= pos[:, None]
+    for b in range(B):
+        for h in range(Hkv):
+            bias = soft_bias(soft_decision_arg(logit[b, h], noise[b, h], gamma, tau))   # [T]
+            add = np.where(causal, np.where(far, bias[None, :], 0.0), -np.inf)
+            for hq in range(h * G, (h + 1) * G):
+                s = scale * (np.asarray(Q[b, hq], np.float64) @ np.asarray(K[b, h], np.float64).T) + add
+                m = np.max(s, axis=1, keepdims=True)
+                e = np.exp(s - m)
+                z = np.sum(e, axis=1, keepdims=True)
+                out[b, hq] = (e / z) @ np.asarray(V[b, h], np.float64)
+                lse[b, hq] = (m + np.log(z))[:, 0]
+    return {"out": out, "lse": lse}
+
+
+def soft_attention_grads(Q, K, V, logit, noise, dO, w: int, gamma: float, tau: float,
+                         scale: Optional[float] = None) -> Dict:
+    """Gradients of sum(dO * out) of ``soft_attention`` with respect to Q,
+    K, V and the logits (the noise, gamma and tau are constants), written out
+    from the chain rule: P = softmax(S), dP = dO V^T, dS = P (dP - rowsum(dO
+    out)), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO, and for the bias
+    -softplus(x) of the far keys, dlogit_i = -sigmoid(x_i) / tau * sum of dS
+    over the far (query, head) pairs of key i.  All float64."""
+    B, Hq, T, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = default_scale(d)
+    dQ = np.zeros((B, Hq, T, d))
+    dK = np.zeros((B, Hkv, T, d))
+    dV = np.zeros((B, Hkv, T, d))
+    dlogit = np.zeros((B, Hkv, T))
+    pos = np.arange(T)
+    far = (pos[:, None] - pos[None, :]) > w
+    causal = pos[None, :] <= pos[:, None]
+    for b in range(B):
+        for h in range(Hkv):
+            x = soft_decision_arg(logit[b, h], noise[b, h], gamma, tau)
+            bias = soft_bias(x)
+            add = np.where(causal, np.where(far, bias[None, :], 0.0), -np.inf)
+            Kh = np.asarray(K[b, h], np.float64)
+            Vh = np.asarray(V[b, h], np.float64)
+            for hq in range(h * G, (h + 1) * G):
+                Qh = np.asarray(Q[b, hq], np.float64)
+                dOh = np.asarray(dO[b, hq], np.float64)
+                s = scale * (Qh @ Kh.T) + add
+                P = np.exp(s - np.max(s, axis=1, keepdims=True))
+                P /= np.sum(P, axis=1, keepdims=True)
+                O = P @ Vh
+                dP = dOh @ Vh.T
+                dS = P * (dP - np.sum(dOh * O, axis=1, keepdims=True))
+                dQ[b, hq] = scale * (dS @ Kh)
+                dK[b, h] += scale * (dS.T @ Qh)
+                dV[b, h] += P.T @ dOh
+                dlogit[b, h] += np.sum(np.where(far & causal, dS, 0.0), axis=0)
+            sig = 1.0 / (1.0 + np.exp(-x))
+            dlogit[b, h] *= -sig / tau
+    return {"dq": dQ, "dk": dK, "dv": dV, "dlogit": dlogit}
+
+
+# ----------------------------------------------------------------------------
 # Eviction logit read from a repurposed projection channel (summary page,
 # "Key claims" and "Method": no parameters are added; one neuron of the K or
 # Q projection of each head is repurposed to produce the eviction logit)

@@ -435,6 +435,93 @@ def pin_prefill_equals_masked_form(O):
                 np.testing.assert_allclose(out[0, hq, q], ref, rtol=0, atol=1e-12)
 
 
+def _soft_inputs(seed, B=2, Hq=4, Hkv=2, T=37, d=8):
+    rng = np.random.default_rng(seed)
+    Q, K, V = _random_batch(rng, B, Hq, Hkv, T, d)
+    logit = rng.standard_normal((B, Hkv, T))
+    u = rng.random((B, Hkv, T))
+    noise = np.log(u) - np.log1p(-u)          # logistic noise
+    dO = rng.standard_normal((B, Hq, T, d))
+    return Q, K, V, logit, noise, dO
+
+
+def _soft_torch(Q, K, V, logit, noise, w, gamma, tau, requires_grad=False):
+    """torch SDPA (float64, CPU) with the relaxed mask as a float attn_mask."""
+    Hq, Hkv = Q.shape[1], K.shape[1]
+    t = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=requires_grad)
+    q, k, v, lg = t(Q), t(K), t(V), t(logit)
+    T = Q.shape[2]
+    pos = torch.arange(T)
+    far = (pos[:, None] - pos[None, :]) > w
+    causal = pos[None, :] <= pos[:, None]
+    x = (lg + gamma + torch.tensor(noise, dtype=torch.float64)) / tau
+    bias = torch.log(1.0 - torch.sigmoid(x))                               # [B, Hkv, T]
+    bias = bias.repeat_interleave(Hq // Hkv, dim=1)[:, :, None, :]          # [B, Hq, 1, T]
+    mask = torch.where(causal, torch.where(far, bias, torch.zeros(())), torch.tensor(-float("inf")))
+    o = torch.nn.functional.scaled_dot_product_attention(q, k.repeat_interleave(Hq // Hkv, 1),
+                                                         v.repeat_interleave(Hq // Hkv, 1), attn_mask=mask)
+    return o, (q, k, v, lg)
+
+
+def pin_soft_attention_is_sdpa_with_float_mask(O):
+    """The relaxed attention equals torch SDPA given the additive mask."""
+    Q, K, V, logit, noise, _ = _soft_inputs(51)
+    for w, gamma, tau in ((3, 0.0, 1.0), (0, -2.0, 0.3), (10, 1.5, 2.0)):
+        got = O.soft_attention(Q, K, V, logit, noise, w, gamma, tau)["out"]
+        ref, _ = _soft_torch(Q, K, V, logit, noise, w, gamma, tau)
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def pin_soft_attention_hard_limit(O):
+    """Decisions pushed to 0 or 1 (|logit| = 60 at tau = 1) give the hard DMS
+    attention of every prompt query (itself pinned above)."""
+    Q, K, V, logit, noise, _ = _soft_inputs(52)
+    marked = logit > 0
+    hard = np.where(marked, 60.0, -60.0)
+    zero = np.zeros_like(noise)
+    for w in (0, 4):
+        got = O.soft_attention(Q, K, V, hard, zero, w, 0.0, 1.0)["out"]
+        ref = O.prefill_attention(Q, K, V, marked.astype(np.float32) * 2 - 1, [Q.shape[2]] * Q.shape[0], w)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def pin_soft_attention_lse(O):
+    """lse is the log of each row's denominator: exp(s - lse) sums to 1,
+    checked through out = sum_i exp(s_i - lse) v_i with V = ones."""
+    Q, K, V, logit, noise, _ = _soft_inputs(53)
+    res = O.soft_attention(Q, K, np.ones_like(V), logit, noise, 2, 0.5, 0.7)
+    np.testing.assert_allclose(res["out"], 1.0, rtol=0, atol=1e-12)
+    ref_lse = []
+    B, Hq, T, d = Q.shape
+    G = Hq // K.shape[1]
+    pos = np.arange(T)
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // G
+            x = (logit[b, h] + 0.5 + noise[b, h]) / 0.7
+            bias = np.log1p(-1.0 / (1.0 + np.exp(-x)))
+            row = []
+            for q in range(T):
+                s = [Q[b, hq, q] @ K[b, h, i] / math.sqrt(d) + (bias[i] if q - i > 2 else 0.0) for i in range(q + 1)]
+                row.append(scipy.special.logsumexp(s))
+            ref_lse.append(row)
+    np.testing.assert_allclose(res["lse"].reshape(B * Hq, T), np.array(ref_lse), rtol=0, atol=1e-11)
+
+
+def pin_soft_attention_grads_are_autograd(O):
+    """Gradients equal torch autograd (float64) through SDPA with the float
+    mask, for Q, K, V and the logits."""
+    Q, K, V, logit, noise, dO = _soft_inputs(54)
+    for w, gamma, tau in ((3, 0.0, 1.0), (1, -1.0, 0.4)):
+        g = O.soft_attention_grads(Q, K, V, logit, noise, dO, w, gamma, tau)
+        o, (q, k, v, lg) = _soft_torch(Q, K, V, logit, noise, w, gamma, tau, requires_grad=True)
+        (o * torch.tensor(dO)).sum().backward()
+        np.testing.assert_allclose(g["dq"], q.grad.numpy(), rtol=0, atol=1e-11)
+        np.testing.assert_allclose(g["dk"], k.grad.numpy(), rtol=0, atol=1e-11)
+        np.testing.assert_allclose(g["dv"], v.grad.numpy(), rtol=0, atol=1e-11)
+        np.testing.assert_allclose(g["dlogit"], lg.grad.numpy(), rtol=0, atol=1e-11)
+
+
 ALL_PINS = [
     pin_golden_visibility,
     pin_fifo_simulation,
@@ -457,4 +544,8 @@ ALL_PINS = [
     pin_prefill_unmarked_is_causal_attention,
     pin_prefill_marked_is_sliding_window,
     pin_prefill_equals_masked_form,
+    pin_soft_attention_is_sdpa_with_float_mask,
+    pin_soft_attention_hard_limit,
+    pin_soft_attention_lse,
+    pin_soft_attention_grads_are_autograd,
 ]

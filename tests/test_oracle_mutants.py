@@ -128,6 +128,20 @@ def _prefill_shifted_query(Q, K, V, logit, prompt_lens, w, scale=None):
     return out
 
 
+def _soft_bias_positive(x):
+    return np.logaddexp(0.0, x)
+
+
+def _soft_arg_without_noise(logit, noise, gamma, tau):
+    return (np.asarray(logit, np.float64) + gamma) / tau
+
+
+def _soft_grads_dlogit_sign(Q, K, V, logit, noise, dO, w, gamma, tau, scale=None):
+    g = real.__dict__["_orig_soft_attention_grads"](Q, K, V, logit, noise, dO, w, gamma, tau, scale)
+    g["dlogit"] = -g["dlogit"]
+    return g
+
+
 MUTANTS = {
     "window-exclusive": ("visible", _visible_exclusive),
     "query-misses-itself": ("visible", _visible_drops_self),
@@ -147,12 +161,16 @@ MUTANTS = {
     "zero-nothing": ("without_channel", _zero_nothing),
     "prefill-final-state": ("prefill_attention", _prefill_final_state),
     "prefill-query-misses-itself": ("prefill_attention", _prefill_shifted_query),
+    "soft-bias-positive": ("soft_bias", _soft_bias_positive),
+    "soft-noise-ignored": ("soft_decision_arg", _soft_arg_without_noise),
+    "soft-dlogit-sign": ("soft_attention_grads", _soft_grads_dlogit_sign),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
+    monkeypatch.setattr(real, "_orig_" + attr, getattr(real, attr), raising=False)
     monkeypatch.setattr(real, attr, fn)
     failed = []
     for pin in oracle_pins.ALL_PINS:
