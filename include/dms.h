@@ -245,6 +245,55 @@ DMS_API int dms_decode_chunk_channel(dms_cache* c, const void* d_q, const void* 
                                      int32_t source, int32_t channel, int32_t zero_channel, int32_t chunk,
                                      float* d_out, void* stream);
 
+/* Training-time relaxed DMS attention: the decisions as a differentiable
+   soft mask (Gumbel-sigmoid), for learning the eviction logits.  Source:
+   "Inference-Time Hyper-Scaling with KV Cache Compression", third-party
+   paper summary page, section "Method" (the paper's section 3.2, Eq. 5-6):
+   during training alpha_i is sampled from a Gumbel-sigmoid, and log(1 -
+   alpha_i) is added to the attention score of key i for the queries that
+   are more than the window past it.  Readings fixed here:
+     x_i     = (logit_i + gamma + noise_i) / tau, alpha_i = sigmoid(x_i), with
+               noise_i the Gumbel (logistic) sample, supplied by the caller
+     bias    = log(1 - alpha_i) = -softplus(x_i) for queries q with q - i > w,
+               0 for i <= q <= i + w (the window), -inf for i > q (causal)
+     out     = softmax(scale * q k^T + bias) v per query head (GQA: query head
+               hq reads KV head hq / G), scale = 1/sqrt(d) when 0 is passed
+     lse     = natural log of each row's softmax denominator (for backward)
+   As tau -> 0 with the logit's sign fixed this is the hard rule of the
+   decode path (alpha in {0, 1}).
+   Layouts: d_q [B, Hq, T, d], d_k, d_v [B, Hkv, T, d] bf16; d_logit,
+   d_noise [B, Hkv, T] fp32; d_out [B, Hq, T, d] and d_lse [B, Hq, T] fp32.
+   d = 64 or 128; 1 <= T <= 2^20; window >= 0; tau > 0.  Async.  Errors:
+   DMS_ERR_ARG for NULL pointers or bad shapes or parameters, DMS_ERR_DEVICE
+   if the current device is not gfx950. */
+DMS_API int dms_soft_attention_forward(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d, int32_t window,
+                                       float gamma, float tau, float scale, const void* d_q, const void* d_k,
+                                       const void* d_v, const float* d_logit, const float* d_noise, float* d_out,
+                                       float* d_lse, void* stream);
+
+/* Bytes of device workspace dms_soft_attention_backward needs (0 for bad
+   shapes): copies of q, dout and k in a transposed operand layout, and the
+   row dot products sum(dout * out). */
+DMS_API size_t dms_soft_attention_backward_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
+                                                           int32_t d);
+
+/* Gradients of sum(dout * out) of dms_soft_attention_forward with respect to
+   q, k, v and the logits (noise, gamma, tau and scale are constants), from
+   the forward's d_out and d_lse (recomputation of the scores, no stored
+   probabilities).  d_dout bf16 [B, Hq, T, d]; d_dq fp32 [B, Hq, T, d]; d_dk,
+   d_dv fp32 [B, Hkv, T, d]; d_dlogit fp32 [B, Hkv, T] (all written, not
+   accumulated).  dK, dV and dlogit sum over the G query heads of each KV
+   head; dlogit_i = -sigmoid(x_i) / tau * (sum of dS over the far queries),
+   dS = P (dP - rowsum(dout * out)).  d_workspace: 256-byte aligned, at least
+   dms_soft_attention_backward_workspace_bytes.  Async.  Errors: as the
+   forward, and DMS_ERR_WORKSPACE for a small or unaligned workspace. */
+DMS_API int dms_soft_attention_backward(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d, int32_t window,
+                                        float gamma, float tau, float scale, const void* d_q, const void* d_k,
+                                        const void* d_v, const float* d_logit, const float* d_noise,
+                                        const float* d_out, const float* d_lse, const void* d_dout, float* d_dq,
+                                        float* d_dk, float* d_dv, float* d_dlogit, void* d_workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* Synchronises `stream`, then fills *out. */
 DMS_API int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream);
 

@@ -74,6 +74,13 @@ struct LogitSrc {
   int32_t bf16;  // 1: bf16 elements (upcast exactly), 0: fp32
 };
 
+// Relaxed (training-time) attention of T positions: shapes, window w, and
+// the decision argument x = (logit + gamma + noise) * inv_tau of each key.
+struct SoftArgs {
+  int32_t B, Hq, Hkv, G, T, w;
+  float gamma, inv_tau, scale_log2e, scale;
+};
+
 // Status codes mirrored from dms.h for device code.
 constexpr int kErrOutOfBlocks = -3;
 
@@ -95,6 +102,17 @@ hipError_t launch_decode_chunk(const Dev& p, int dtype, int d, const void* q, co
                                const LogitSrc& logit, int zero_ch, int chunk, float* out, hipStream_t s);
 // Longest block table (blocks per unit) the chunk decode supports.
 int chunk_max_blocks();
+// Relaxed attention, bf16 q [B, Hq, T, d], k, v [B, Hkv, T, d]; logit, noise
+// [B, Hkv, T] fp32.  Forward: out [B, Hq, T, d] and lse [B, Hq, T] fp32.
+hipError_t launch_soft_forward(const SoftArgs& a, int d, const void* q, const void* k, const void* v,
+                               const float* logit, const float* noise, float* out, float* lse, hipStream_t s);
+// Backward from dout (bf16, like out): dq, dk, dv (fp32, like q, k, v) and
+// dlogit (fp32, like logit); ws holds soft_backward_workspace_bytes.
+int64_t soft_backward_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
+hipError_t launch_soft_backward(const SoftArgs& a, int d, const void* q, const void* k, const void* v,
+                                const float* logit, const float* noise, const float* out, const float* lse,
+                                const void* dout, float* dq, float* dk, float* dv, float* dlogit, void* ws,
+                                hipStream_t s);
 hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s);
 // Work-groups of the attention kernel that fit on the device at once.
 int attention_resident_wgs(int dtype, int d, int num_cus);

@@ -1578,6 +1578,444 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
 }
 
 // ---------------------------------------------------------------------------
+// training-time relaxed attention (Gumbel-sigmoid decisions as a soft mask)
+// ---------------------------------------------------------------------------
+
+// Soft decision of key i: x = (logit + gamma + noise) / tau, alpha = sigmoid(x).
+// Query q >= i adds log(1 - alpha) = -softplus(x) to the score of key i when
+// q - i > w, nothing inside the window (the hard rule when alpha is 0 or 1).
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+
+// The x of key i of unit (b, h).
+__device__ __forceinline__ float soft_x(const SoftArgs& a, const float* __restrict__ logit,
+                                        const float* __restrict__ noise, int64_t unit_row0, int i) {
+  return (logit[unit_row0 + i] + a.gamma + noise[unit_row0 + i]) * a.inv_tau;
+}
+
+// attend_pair (bf16) with an additive score per key and column, in the exp2
+// domain: badd[0..3] for this lane's keys of block A, badd[4..7] of block B
+// (-inf for keys the column may not see).
+template <int D>
+__device__ __forceinline__ void attend_pair_biased(const PairFrag<2, D>& f, const u32x4 (&qf)[Geo<2, D>::kChunks],
+                                                   const float (&badd)[8], float sl2e, Acc<D>& a) {
+  using G = Geo<2, D>;
+  f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) {
+    SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.ka[c]),
+                                                  __builtin_bit_cast(bf16x8, qf[c]), SA, 0, 0, 0);
+    SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.kb[c]),
+                                                  __builtin_bit_cast(bf16x8, qf[c]), SB, 0, 0, 0);
+  }
+  float s[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s[r] = fmaf(SA[r], sl2e, badd[r]);
+    s[4 + r] = fmaf(SB[r], sl2e, badd[4 + r]);
+  }
+  float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float mn = fmaxf(a.m, bm);
+  const float mref = (mn == -INFINITY) ? 0.f : mn;
+  float pr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) pr[r] = exp2_fast(s[r] - mref);
+  const float psum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+  if (__builtin_amdgcn_ballot_w64(mn != a.m) != 0) {
+    const float alpha = exp2_fast(a.m - mref);
+    a.l *= alpha;
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
+  }
+  a.l += psum;
+  a.m = mn;
+  unsigned hi[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
+    lo[i] = pack_bf16x2(pr[2 * i] - bf16_lo_to_f32(hi[i]), pr[2 * i + 1] - bf16_hi_to_f32(hi[i]));
+  }
+  const u32x4 hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
+  const bf16x8 PH = __builtin_bit_cast(bf16x8, hv), PL = __builtin_bit_cast(bf16x8, lv);
+#pragma unroll
+  for (int j = 0; j < G::kTiles; ++j) {
+    const bf16x8 A = __builtin_bit_cast(bf16x8, f.v[j]);
+    a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PH, a.o[j], 0, 0, 0);
+    a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PL, a.o[j], 0, 0, 0);
+  }
+}
+
+// Forward: out = softmax(scale q k^T + bias) v and lse (natural log of each
+// row's softmax denominator) for every position.  q [B, Hq, T, d], k, v [B,
+// Hkv, T, d] bf16; logit, noise [B, Hkv, T] fp32; out [B, Hq, T, d], lse [B,
+// Hq, T] fp32.  Grid (ceil(T / kPfTile), Hq, B), as the prompt attention.
+template <int D>
+__global__ __launch_bounds__(256) void soft_forward_kernel(SoftArgs a, const uint8_t* __restrict__ q,
+                                                           const uint8_t* __restrict__ k,
+                                                           const uint8_t* __restrict__ v,
+                                                           const float* __restrict__ logit,
+                                                           const float* __restrict__ noise, float* __restrict__ out,
+                                                           float* __restrict__ lse) {
+  using G = Geo<2, D>;
+  constexpr int ES = 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.z, hq = blockIdx.y, h = hq / a.G;
+  const int T = a.T, w = a.w;
+  const int q0 = blockIdx.x * kPfTile;
+  const int qmax = min(q0 + kPfTile, T) - 1;
+  const int64_t urow = ((int64_t)b * a.Hkv + h) * T;
+  const uint8_t* Ku = k + urow * D * ES;
+  const uint8_t* Vu = v + urow * D * ES;
+  const uint8_t* Qh = q + ((int64_t)b * a.Hq + hq) * T * D * ES;
+  const int tb = 4 * (lane >> 4);
+  int qc[kPfCols];
+  u32x4 qf[kPfCols][G::kChunks];
+  Acc<D> acc[kPfCols];
+#pragma unroll
+  for (int t = 0; t < kPfCols; ++t) {
+    qc[t] = q0 + 16 * (kPfCols * wave + t) + (lane & 15);
+    const uint8_t* qrow = Qh + (int64_t)min(qc[t], T - 1) * D * ES;
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) qf[t][c] = *(const u32x4*)(qrow + c * 64 + 16 * (lane >> 4));
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) acc[t].o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[t].m = -INFINITY;
+    acc[t].l = 0.f;
+  }
+  constexpr float kLog2e = 1.4426950408889634f;
+  for (int r0 = 0; r0 <= qmax; r0 += 32) {
+    Frag<ES, D> fa, fb;
+    load_frag_dense<ES, D>(fa, Ku, Vu, r0, T - 1, lane);
+    load_frag_dense<ES, D>(fb, Ku, Vu, r0 + 16, T - 1, lane);
+    PairFrag<ES, D> f;
+    make_pair<ES, D>(f, fa, fb);
+    float kb2[8];  // this lane's keys' far bias, exp2 domain
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = min(r0 + (r >> 2) * 16 + tb + (r & 3), T - 1);
+      kb2[r] = -softplus_f(soft_x(a, logit, noise, urow, i)) * kLog2e;
+    }
+#pragma unroll
+    for (int t = 0; t < kPfCols; ++t) {
+      float badd[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int i = r0 + (r >> 2) * 16 + tb + (r & 3);
+        badd[r] = i > qc[t] ? -INFINITY : (qc[t] - i > w ? kb2[r] : 0.f);
+      }
+      attend_pair_biased<D>(f, qf[t], badd, a.scale_log2e, acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kPfCols; ++t) {
+    float lt = acc[t].l + __shfl_xor(acc[t].l, 16);
+    lt = lt + __shfl_xor(lt, 32);
+    if (qc[t] >= T) continue;
+    const float inv = 1.0f / lt;
+    const int64_t row = ((int64_t)b * a.Hq + hq) * T + qc[t];
+    float* orow = out + row * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(orow + 16 * j) = acc[t].o[j] * inv;
+    if (lane < 16) lse[row] = (acc[t].m + log2f(lt)) / kLog2e;
+  }
+}
+
+// Bias of key i in the exp2 domain, log2e * log(1 - sigmoid(x)) =
+// -(max(x, 0) log2e + log2(1 + 2^(-|x| log2e))).  It is added to a score, so
+// its absolute error (a few 1e-7) is what matters, not a relative one.
+__device__ __forceinline__ float soft_bias2(float x) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  return -(fmaxf(x, 0.f) * kLog2e + __builtin_amdgcn_logf(1.f + exp2_fast(-fabsf(x) * kLog2e)));
+}
+
+// Transposed pair copy ("pairT") of a row-major [R, D] bf16 matrix, the
+// operand layout of a product that contracts over its rows: for row pair p
+// (rows 32p .. 32p + 31), channel tile j and lane l, 16 bytes at
+// ((p * D / 16 + j) * 64 + l) * 16 holding rows 32p + 4(l/16) + e, then rows
+// 32p + 16 + 4(l/16) + e (e = 0..3), of channel 16j + l % 16.  Rows >= R are
+// 0.  With `out` set, also the row dot products delta[r] = sum_c src[r][c] *
+// out[r][c] (out fp32, [R, D]).  Grid (matrices, ceil(R / 32)), 256 threads.
+template <int D>
+__global__ __launch_bounds__(256) void soft_pack_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                        int R, const float* __restrict__ out,
+                                                        float* __restrict__ delta) {
+  __shared__ uint16_t tile[32][D + 2];
+  const int p = blockIdx.y, m = blockIdx.x, tid = threadIdx.x;
+  const int64_t mrow0 = (int64_t)m * R;
+  const int npairs = (R + 31) / 32;
+  for (int e = tid; e < 32 * D / 2; e += 256) {
+    const int r = e / (D / 2), c2 = e % (D / 2);
+    const int row = 32 * p + r;
+    uint32_t x = 0u;
+    if (row < R) x = *(const uint32_t*)(src + (mrow0 + row) * D + 2 * c2);
+    tile[r][2 * c2] = (uint16_t)(x & 0xffffu);
+    tile[r][2 * c2 + 1] = (uint16_t)(x >> 16);
+  }
+  __syncthreads();
+  uint8_t* d0 = dst + ((int64_t)m * npairs + p) * (D / 16) * 64 * 16;
+  for (int o = tid; o < (D / 16) * 64; o += 256) {
+    const int j = o >> 6, l = o & 63, g = l >> 4, ch = 16 * j + (l & 15);
+    u32x4 val;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const int r = 16 * h + 4 * g + 2 * e2;
+        val[2 * h + e2] = (uint32_t)tile[r][ch] | ((uint32_t)tile[r + 1][ch] << 16);
+      }
+    *(u32x4*)(d0 + (int64_t)o * 16) = val;
+  }
+  if (out != nullptr) {
+    // 8 threads per row, D / 8 channels each
+    const int r = tid >> 3, part = tid & 7, row = 32 * p + r;
+    float acc = 0.f;
+    if (row < R) {
+      const float* orow = out + (mrow0 + row) * D;
+#pragma unroll
+      for (int c = part * (D / 8); c < (part + 1) * (D / 8); ++c)
+        acc = fmaf(__uint_as_float((uint32_t)tile[r][c] << 16), orow[c], acc);
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if (row < R && part == 0) delta[mrow0 + row] = acc;
+  }
+}
+
+// 16 consecutive rows row0 .. row0 + 15 of a row-major [*, D] bf16 matrix as
+// an MFMA operand whose rows are the matrix rows: lane l carries row l % 16
+// (clamped to `last`), 16-byte piece 4c + l / 16.
+template <int D>
+__device__ __forceinline__ void load_rows(u32x4 (&f)[D / 32], const uint8_t* __restrict__ M, int row0, int last,
+                                          int lane) {
+  const uint8_t* r = M + (int64_t)min(row0 + (lane & 15), last) * D * 2 + 16 * (lane >> 4);
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) f[c] = *(const u32x4*)(r + c * 64);
+}
+
+template <int D>
+__device__ __forceinline__ void load_pairT(u32x4 (&f)[D / 16], const uint8_t* __restrict__ Mt, int pair, int lane) {
+  const uint8_t* a = Mt + ((int64_t)pair * (D / 16) * 64 + lane) * 16;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) f[j] = *(const u32x4*)(a + j * 1024);
+}
+
+// 8 fp32 values in the pair order as bf16 hi and lo parts (x = hi + lo to
+// about 2^-17 relative), the B operand of a product over the pair's rows.
+__device__ __forceinline__ void split_pair(const float (&x)[8], bf16x8& H, bf16x8& L) {
+  unsigned hi[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    lo[i] = pack_bf16x2(x[2 * i] - bf16_lo_to_f32(hi[i]), x[2 * i + 1] - bf16_hi_to_f32(hi[i]));
+  }
+  const u32x4 hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
+  H = __builtin_bit_cast(bf16x8, hv);
+  L = __builtin_bit_cast(bf16x8, lv);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+constexpr int kSoftQCols = 2;                            // query tiles of 16 per wave (dQ)
+constexpr int kSoftQTile = 16 * kSoftQCols * kWavesPerWG;  // queries per work-group (dQ)
+constexpr int kSoftKTile = 16 * kWavesPerWG;               // keys per work-group (dK, dV)
+
+// Backward, query-stationary: dq = scale * dS k with dS = P (dP - delta), P
+// recomputed from the forward's lse, dP = dO v^T.  Each wave holds
+// kSoftQCols tiles of 16 queries (columns) and streams the causal keys in
+// pairs of 16-row blocks: S^T = k q^T and dP^T = v dO^T with the keys as rows,
+// then dq^T += k^T dS^T with k^T from its pairT copy.  Grid (ceil(T /
+// kSoftQTile), Hq, B).
+template <int D>
+__global__ __launch_bounds__(256) void soft_dq_kernel(SoftArgs a, const uint8_t* __restrict__ q,
+                                                      const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+                                                      const uint8_t* __restrict__ kt, const uint8_t* __restrict__ dO,
+                                                      const float* __restrict__ logit,
+                                                      const float* __restrict__ noise, const float* __restrict__ lse,
+                                                      const float* __restrict__ delta, float* __restrict__ dq) {
+  constexpr int NCH = D / 32, NT = D / 16;
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.z, hq = blockIdx.y, h = hq / a.G;
+  const int T = a.T, w = a.w;
+  const int q0 = blockIdx.x * kSoftQTile;
+  const int qmax = min(q0 + kSoftQTile, T) - 1;
+  const int64_t urow = ((int64_t)b * a.Hkv + h) * T;
+  const int64_t hrow = ((int64_t)b * a.Hq + hq) * T;
+  const uint8_t* Ku = k + urow * D * 2;
+  const uint8_t* Vu = v + urow * D * 2;
+  const uint8_t* Kt = kt + ((int64_t)b * a.Hkv + h) * ((T + 31) / 32) * 32 * D * 2;
+  const int tb = 4 * (lane >> 4);
+  int qc[kSoftQCols];
+  float lse2[kSoftQCols], dl[kSoftQCols];
+  u32x4 qf[kSoftQCols][NCH], of[kSoftQCols][NCH];
+  f32x4 acc[kSoftQCols][NT];
+#pragma unroll
+  for (int t = 0; t < kSoftQCols; ++t) {
+    const int c0 = q0 + 16 * (kSoftQCols * wave + t);
+    qc[t] = c0 + (lane & 15);
+    load_rows<D>(qf[t], q + hrow * D * 2, c0, T - 1, lane);
+    load_rows<D>(of[t], dO + hrow * D * 2, c0, T - 1, lane);
+    const int64_t r = hrow + min(qc[t], T - 1);
+    lse2[t] = lse[r] * kLog2e;
+    dl[t] = delta[r];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int r0 = 0; r0 <= qmax; r0 += 32) {
+    u32x4 ka[NCH], kb[NCH], va[NCH], vb[NCH], ktp[NT];
+    load_rows<D>(ka, Ku, r0, T - 1, lane);
+    load_rows<D>(kb, Ku, r0 + 16, T - 1, lane);
+    load_rows<D>(va, Vu, r0, T - 1, lane);
+    load_rows<D>(vb, Vu, r0 + 16, T - 1, lane);
+    load_pairT<D>(ktp, Kt, r0 / 32, lane);
+    float kb2[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = min(r0 + (r >> 2) * 16 + tb + (r & 3), T - 1);
+      kb2[r] = soft_bias2(soft_x(a, logit, noise, urow, i));
+    }
+#pragma unroll
+    for (int t = 0; t < kSoftQCols; ++t) {
+      f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = SA, PA = SA, PB = SA;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        SA = mfma_bf16(ka[c], qf[t][c], SA);
+        SB = mfma_bf16(kb[c], qf[t][c], SB);
+        PA = mfma_bf16(va[c], of[t][c], PA);
+        PB = mfma_bf16(vb[c], of[t][c], PB);
+      }
+      float ds[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int i = r0 + (r >> 2) * 16 + tb + (r & 3);
+        const float badd = i > qc[t] ? -INFINITY : (qc[t] - i > w ? kb2[r] : 0.f);
+        const float sv = r < 4 ? SA[r] : SB[r - 4];
+        const float dp = r < 4 ? PA[r] : PB[r - 4];
+        const float pr = exp2_fast(fmaf(sv, a.scale_log2e, badd) - lse2[t]);
+        ds[r] = pr * (dp - dl[t]);
+      }
+      bf16x8 DH, DL;
+      split_pair(ds, DH, DL);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ktp[j]), DH, acc[t][j], 0, 0, 0);
+        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ktp[j]), DL, acc[t][j], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kSoftQCols; ++t) {
+    if (qc[t] >= T) continue;
+    float* orow = dq + (hrow + qc[t]) * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) *(f32x4*)(orow + 16 * j) = acc[t][j] * a.scale;
+  }
+}
+
+// Backward, key-stationary: for 16 keys per wave, over the G query heads of
+// its KV head and every query at or after them, dv = P^T dO, dk = scale dS^T
+// q and dlogit = -sigmoid(x) / tau * (sum of dS over the far queries).  S =
+// q k^T and dP = dO v^T with the queries as rows (k, v rows stay in
+// registers); dv^T += dO^T P and dk^T += q^T dS with dO^T, q^T from their
+// pairT copies.  No atomics: every key has one owner.  Grid (ceil(T /
+// kSoftKTile), Hkv, B); the work-groups with the most queries start first.
+template <int D>
+__global__ __launch_bounds__(256) void soft_dkv_kernel(SoftArgs a, const uint8_t* __restrict__ q,
+                                                       const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+                                                       const uint8_t* __restrict__ qt, const uint8_t* __restrict__ dO,
+                                                       const uint8_t* __restrict__ dOt,
+                                                       const float* __restrict__ logit,
+                                                       const float* __restrict__ noise, const float* __restrict__ lse,
+                                                       const float* __restrict__ delta, float* __restrict__ dk,
+                                                       float* __restrict__ dv, float* __restrict__ dlogit) {
+  constexpr int NCH = D / 32, NT = D / 16;
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int T = a.T, w = a.w;
+  const int nkt = (T + kSoftKTile - 1) / kSoftKTile;
+  const int kbase = (nkt - 1 - (int)blockIdx.x) * kSoftKTile;
+  const int k0 = kbase + 16 * wave;
+  const int key = k0 + (lane & 15);
+  const int64_t urow = ((int64_t)b * a.Hkv + h) * T;
+  const int npairs = (T + 31) / 32;
+  const int tb = 4 * (lane >> 4);
+  u32x4 kf[NCH], vf[NCH];
+  load_rows<D>(kf, k + urow * D * 2, k0, T - 1, lane);
+  load_rows<D>(vf, v + urow * D * 2, k0, T - 1, lane);
+  const float x = soft_x(a, logit, noise, urow, min(key, T - 1));
+  const float kb2 = soft_bias2(x);
+  f32x4 ak[NT], av[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) ak[j] = av[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float far_ds = 0.f;
+  for (int hq = h * a.G; hq < (h + 1) * a.G; ++hq) {
+    const int64_t hrow = ((int64_t)b * a.Hq + hq) * T;
+    const uint8_t* Qh = q + hrow * D * 2;
+    const uint8_t* Oh = dO + hrow * D * 2;
+    const uint8_t* Qt = qt + ((int64_t)b * a.Hq + hq) * npairs * 32 * D * 2;
+    const uint8_t* Ot = dOt + ((int64_t)b * a.Hq + hq) * npairs * 32 * D * 2;
+    for (int q0 = kbase; q0 < T; q0 += 32) {
+      u32x4 qa[NCH], qb[NCH], oa[NCH], ob[NCH], qtp[NT], otp[NT];
+      load_rows<D>(qa, Qh, q0, T - 1, lane);
+      load_rows<D>(qb, Qh, q0 + 16, T - 1, lane);
+      load_rows<D>(oa, Oh, q0, T - 1, lane);
+      load_rows<D>(ob, Oh, q0 + 16, T - 1, lane);
+      load_pairT<D>(qtp, Qt, q0 / 32, lane);
+      load_pairT<D>(otp, Ot, q0 / 32, lane);
+      f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = SA, PA = SA, PB = SA;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        SA = mfma_bf16(qa[c], kf[c], SA);
+        SB = mfma_bf16(qb[c], kf[c], SB);
+        PA = mfma_bf16(oa[c], vf[c], PA);
+        PB = mfma_bf16(ob[c], vf[c], PB);
+      }
+      float pr[8], ds[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int qi = q0 + (r >> 2) * 16 + tb + (r & 3);
+        const int64_t row = hrow + min(qi, T - 1);
+        const float badd = (qi < key || qi >= T) ? -INFINITY : (qi - key > w ? kb2 : 0.f);
+        const float sv = r < 4 ? SA[r] : SB[r - 4];
+        const float dp = r < 4 ? PA[r] : PB[r - 4];
+        pr[r] = exp2_fast(fmaf(sv, a.scale_log2e, badd) - lse[row] * kLog2e);
+        ds[r] = pr[r] * (dp - delta[row]);
+        if (qi - key > w) far_ds += ds[r];
+      }
+      bf16x8 PH, PL, DH, DL;
+      split_pair(pr, PH, PL);
+      split_pair(ds, DH, DL);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const bf16x8 OT = __builtin_bit_cast(bf16x8, otp[j]), QT = __builtin_bit_cast(bf16x8, qtp[j]);
+        av[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PH, av[j], 0, 0, 0);
+        av[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PL, av[j], 0, 0, 0);
+        ak[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DH, ak[j], 0, 0, 0);
+        ak[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DL, ak[j], 0, 0, 0);
+      }
+    }
+  }
+  far_ds += __shfl_xor(far_ds, 16);
+  far_ds += __shfl_xor(far_ds, 32);
+  if (key >= T) return;
+  float* krow = dk + (urow + key) * D + 4 * (lane >> 4);
+  float* vrow = dv + (urow + key) * D + 4 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    *(f32x4*)(krow + 16 * j) = ak[j] * a.scale;
+    *(f32x4*)(vrow + 16 * j) = av[j];
+  }
+  if (lane < 16) dlogit[urow + key] = -sigmoid_f(x) * a.inv_tau * far_ds;
+}
+
+// ---------------------------------------------------------------------------
 // decode of a chunk of consecutive tokens: attention, then the appends
 // ---------------------------------------------------------------------------
 
@@ -1936,6 +2374,71 @@ hipError_t launch_decode_chunk(const Dev& p, int dtype, int d, const void* q, co
 }
 
 int chunk_max_blocks() { return kChunkMaxBlocks; }
+
+static int64_t soft_pairT_bytes(int T, int d) { return (int64_t)((T + 31) / 32) * 32 * d * 2; }
+
+int64_t soft_backward_workspace_bytes(int B, int Hq, int Hkv, int T, int d) {
+  // pairT copies of q and dO (per query head) and of k (per KV head), then delta
+  const int64_t pt = soft_pairT_bytes(T, d);
+  const int64_t copies = ((int64_t)B * Hq * 2 + (int64_t)B * Hkv) * pt;
+  return copies + (int64_t)B * Hq * T * 4;
+}
+
+template <int D>
+static hipError_t soft_forward_t(const SoftArgs& a, const void* q, const void* k, const void* v, const float* logit,
+                                 const float* noise, float* out, float* lse, hipStream_t s) {
+  const dim3 grid((unsigned)((a.T + kPfTile - 1) / kPfTile), (unsigned)a.Hq, (unsigned)a.B);
+  return launch(soft_forward_kernel<D>, grid, dim3(64 * kWavesPerWG), s, a, (const uint8_t*)q, (const uint8_t*)k,
+                (const uint8_t*)v, logit, noise, out, lse);
+}
+
+hipError_t launch_soft_forward(const SoftArgs& a, int d, const void* q, const void* k, const void* v,
+                               const float* logit, const float* noise, float* out, float* lse, hipStream_t s) {
+  return d == 128 ? soft_forward_t<128>(a, q, k, v, logit, noise, out, lse, s)
+                  : soft_forward_t<64>(a, q, k, v, logit, noise, out, lse, s);
+}
+
+template <int D>
+static hipError_t soft_backward_t(const SoftArgs& a, const void* q, const void* k, const void* v,
+                                  const float* logit, const float* noise, const float* out, const float* lse,
+                                  const void* dout, float* dq, float* dk, float* dv, float* dlogit, uint8_t* ws,
+                                  hipStream_t s) {
+  const int64_t pt = soft_pairT_bytes(a.T, D);
+  uint8_t* qt = ws;
+  uint8_t* ot = qt + (int64_t)a.B * a.Hq * pt;
+  uint8_t* kt = ot + (int64_t)a.B * a.Hq * pt;
+  float* delta = (float*)(kt + (int64_t)a.B * a.Hkv * pt);
+  const unsigned npairs = (unsigned)((a.T + 31) / 32);
+  hipError_t e = launch(soft_pack_kernel<D>, dim3((unsigned)(a.B * a.Hq), npairs), dim3(256), s,
+                        (const uint16_t*)q, qt, a.T, (const float*)nullptr, (float*)nullptr);
+  if (e == hipSuccess)
+    e = launch(soft_pack_kernel<D>, dim3((unsigned)(a.B * a.Hq), npairs), dim3(256), s, (const uint16_t*)dout, ot,
+               a.T, out, delta);
+  if (e == hipSuccess)
+    e = launch(soft_pack_kernel<D>, dim3((unsigned)(a.B * a.Hkv), npairs), dim3(256), s, (const uint16_t*)k, kt,
+               a.T, (const float*)nullptr, (float*)nullptr);
+  if (e == hipSuccess)
+    e = launch(soft_dq_kernel<D>, dim3((unsigned)((a.T + kSoftQTile - 1) / kSoftQTile), (unsigned)a.Hq, (unsigned)a.B),
+               dim3(64 * kWavesPerWG), s, a, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v,
+               (const uint8_t*)kt, (const uint8_t*)dout, logit, noise, lse, (const float*)delta, dq);
+  if (e == hipSuccess)
+    e = launch(soft_dkv_kernel<D>, dim3((unsigned)((a.T + kSoftKTile - 1) / kSoftKTile), (unsigned)a.Hkv,
+                                        (unsigned)a.B),
+               dim3(64 * kWavesPerWG), s, a, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v,
+               (const uint8_t*)qt, (const uint8_t*)dout, (const uint8_t*)ot, logit, noise, lse, (const float*)delta,
+               dk, dv, dlogit);
+  return e;
+}
+
+hipError_t launch_soft_backward(const SoftArgs& a, int d, const void* q, const void* k, const void* v,
+                                const float* logit, const float* noise, const float* out, const float* lse,
+                                const void* dout, float* dq, float* dk, float* dv, float* dlogit, void* ws,
+                                hipStream_t s) {
+  return d == 128 ? soft_backward_t<128>(a, q, k, v, logit, noise, out, lse, dout, dq, dk, dv, dlogit,
+                                         (uint8_t*)ws, s)
+                  : soft_backward_t<64>(a, q, k, v, logit, noise, out, lse, dout, dq, dk, dv, dlogit,
+                                        (uint8_t*)ws, s);
+}
 
 template <int ES, int D>
 static int resident_t(int num_cus) {

@@ -4,9 +4,11 @@
 // dms_kernels.hip; nothing here computes any part of the decode path.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdint.h>
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "dms.h"
@@ -148,6 +150,39 @@ int check_device(const dms_cache* c) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return DMS_ERR_HIP;
   return dev == c->device ? DMS_OK : DMS_ERR_STATE;
+}
+
+// The current device, if it is a gfx950 (property query cached per device).
+int current_gfx950_device(int* dev) {
+  static int8_t known[256];  // 0 unknown, 1 gfx950, -1 other
+  if (hipGetDevice(dev) != hipSuccess) return DMS_ERR_HIP;
+  if (*dev < 0 || *dev >= 256) return DMS_ERR_DEVICE;
+  int8_t k = __atomic_load_n(&known[*dev], __ATOMIC_RELAXED);
+  if (k == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, *dev) != hipSuccess) return DMS_ERR_HIP;
+    k = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    __atomic_store_n(&known[*dev], k, __ATOMIC_RELAXED);
+  }
+  return k == 1 ? DMS_OK : DMS_ERR_DEVICE;
+}
+
+constexpr int32_t kSoftMaxT = 1 << 20;
+
+bool soft_shapes_ok(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d) {
+  return B >= 1 && B <= 65535 && Hkv >= 1 && Hq >= Hkv && Hq <= 65535 && Hq % Hkv == 0 && T >= 1 &&
+         T <= kSoftMaxT && (d == 64 || d == 128) && (int64_t)B * Hq <= INT32_MAX;
+}
+
+int soft_args(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d, int32_t window, float gamma, float tau,
+              float scale, dms::SoftArgs* a) {
+  if (!soft_shapes_ok(B, Hq, Hkv, T, d) || window < 0 || !(tau > 0.0f) || !std::isfinite(tau) ||
+      !std::isfinite(gamma) || !std::isfinite(scale) || scale < 0.0f)
+    return DMS_ERR_ARG;
+  const float sc = scale == 0.0f ? 1.0f / sqrtf((float)d) : scale;
+  *a = dms::SoftArgs{B, Hq, Hkv, Hq / Hkv, T, window, gamma, 1.0f / tau,
+                     (float)((double)sc * 1.4426950408889634), sc};
+  return DMS_OK;
 }
 
 }  // namespace
@@ -470,6 +505,47 @@ int dms_cache_export(dms_cache* c, int32_t unit_begin, int32_t unit_count, int32
     }
   }
   return DMS_OK;
+}
+
+int dms_soft_attention_forward(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d, int32_t window,
+                               float gamma, float tau, float scale, const void* d_q, const void* d_k,
+                               const void* d_v, const float* d_logit, const float* d_noise, float* d_out,
+                               float* d_lse, void* stream) {
+  if (!d_q || !d_k || !d_v || !d_logit || !d_noise || !d_out || !d_lse) return DMS_ERR_ARG;
+  dms::SoftArgs a;
+  int st = soft_args(B, Hq, Hkv, T, d, window, gamma, tau, scale, &a);
+  if (st != DMS_OK) return st;
+  int dev;
+  st = current_gfx950_device(&dev);
+  if (st != DMS_OK) return st;
+  return hip_status(dms::launch_soft_forward(a, d, d_q, d_k, d_v, d_logit, d_noise, d_out, d_lse,
+                                             (hipStream_t)stream));
+}
+
+size_t dms_soft_attention_backward_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d) {
+  if (!soft_shapes_ok(B, Hq, Hkv, T, d)) return 0;
+  return (size_t)dms::soft_backward_workspace_bytes(B, Hq, Hkv, T, d);
+}
+
+int dms_soft_attention_backward(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d, int32_t window,
+                                float gamma, float tau, float scale, const void* d_q, const void* d_k,
+                                const void* d_v, const float* d_logit, const float* d_noise, const float* d_out,
+                                const float* d_lse, const void* d_dout, float* d_dq, float* d_dk, float* d_dv,
+                                float* d_dlogit, void* d_workspace, size_t workspace_bytes, void* stream) {
+  if (!d_q || !d_k || !d_v || !d_logit || !d_noise || !d_out || !d_lse || !d_dout || !d_dq || !d_dk || !d_dv ||
+      !d_dlogit || !d_workspace)
+    return DMS_ERR_ARG;
+  dms::SoftArgs a;
+  int st = soft_args(B, Hq, Hkv, T, d, window, gamma, tau, scale, &a);
+  if (st != DMS_OK) return st;
+  if ((uintptr_t)d_workspace % kAlign != 0 ||
+      workspace_bytes < (size_t)dms::soft_backward_workspace_bytes(B, Hq, Hkv, T, d))
+    return DMS_ERR_WORKSPACE;
+  int dev;
+  st = current_gfx950_device(&dev);
+  if (st != DMS_OK) return st;
+  return hip_status(dms::launch_soft_backward(a, d, d_q, d_k, d_v, d_logit, d_noise, d_out, d_lse, d_dout, d_dq,
+                                              d_dk, d_dv, d_dlogit, d_workspace, (hipStream_t)stream));
 }
 
 const char* dms_status_str(int status) {

@@ -103,6 +103,11 @@ def _load():
         "dms_cache_stats": (ctypes.c_int, [vp, P(dms_stats), vp]),
         "dms_cache_export": (ctypes.c_int, [vp, i32, i32, P(i32), P(i32), P(i32), vp]),
         "dms_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "dms_soft_attention_forward": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, ctypes.c_float,
+                                                      ctypes.c_float, ctypes.c_float] + [vp] * 8),
+        "dms_soft_attention_backward_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "dms_soft_attention_backward": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, ctypes.c_float,
+                                                       ctypes.c_float, ctypes.c_float] + [vp] * 13 + [sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -208,6 +213,76 @@ def dms_cache_export(h: int, unit_begin: int, unit_count: int, slot_pos: Optiona
                      ring: Optional[np.ndarray], n: Optional[np.ndarray], stream: int = 0):
     _check(lib.dms_cache_export(h, unit_begin, unit_count, _i32p(slot_pos), _i32p(ring), _i32p(n), stream),
            "dms_cache_export")
+
+
+def dms_soft_attention_forward(B, Hq, Hkv, T, d, window, gamma, tau, scale, d_q, d_k, d_v, d_logit, d_noise,
+                               d_out, d_lse, stream: int = 0):
+    _check(lib.dms_soft_attention_forward(int(B), int(Hq), int(Hkv), int(T), int(d), int(window), float(gamma),
+                                          float(tau), float(scale), d_q, d_k, d_v, d_logit, d_noise, d_out, d_lse,
+                                          stream), "dms_soft_attention_forward")
+
+
+def dms_soft_attention_backward_workspace_bytes(B, Hq, Hkv, T, d) -> int:
+    return int(lib.dms_soft_attention_backward_workspace_bytes(int(B), int(Hq), int(Hkv), int(T), int(d)))
+
+
+def dms_soft_attention_backward(B, Hq, Hkv, T, d, window, gamma, tau, scale, d_q, d_k, d_v, d_logit, d_noise,
+                                d_out, d_lse, d_dout, d_dq, d_dk, d_dv, d_dlogit, d_workspace, workspace_bytes,
+                                stream: int = 0):
+    _check(lib.dms_soft_attention_backward(int(B), int(Hq), int(Hkv), int(T), int(d), int(window), float(gamma),
+                                           float(tau), float(scale), d_q, d_k, d_v, d_logit, d_noise, d_out, d_lse,
+                                           d_dout, d_dq, d_dk, d_dv, d_dlogit, d_workspace, int(workspace_bytes),
+                                           stream), "dms_soft_attention_backward")
+
+
+def _soft_check(q, k, v, logit, noise):
+    import torch
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    for t, shape, dt, name in ((q, (B, Hq, T, d), torch.bfloat16, "q"), (k, (B, Hkv, T, d), torch.bfloat16, "k"),
+                               (v, (B, Hkv, T, d), torch.bfloat16, "v"), (logit, (B, Hkv, T), torch.float32, "logit"),
+                               (noise, (B, Hkv, T), torch.float32, "noise")):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name}: expected contiguous {dt} {shape} on the GPU, got "
+                             f"{t.dtype} {tuple(t.shape)}")
+    return B, Hq, Hkv, T, d
+
+
+def soft_attention_forward(q, k, v, logit, noise, window, gamma=0.0, tau=1.0, scale=0.0, out=None, lse=None):
+    """Relaxed DMS attention forward (dms_soft_attention_forward) on torch
+    tensors: returns (out, lse), fp32, allocated here unless given."""
+    import torch
+    B, Hq, Hkv, T, d = _soft_check(q, k, v, logit, noise)
+    if out is None:
+        out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    dms_soft_attention_forward(B, Hq, Hkv, T, d, window, gamma, tau, scale, q.data_ptr(), k.data_ptr(),
+                               v.data_ptr(), logit.data_ptr(), noise.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream)
+    return out, lse
+
+
+def soft_attention_backward(q, k, v, logit, noise, out, lse, dout, window, gamma=0.0, tau=1.0, scale=0.0,
+                            workspace=None):
+    """Gradients (dms_soft_attention_backward) on torch tensors: returns
+    {'dq', 'dk', 'dv', 'dlogit'} in fp32.  dout is bf16 like q."""
+    import torch
+    B, Hq, Hkv, T, d = _soft_check(q, k, v, logit, noise)
+    if tuple(dout.shape) != (B, Hq, T, d) or dout.dtype != torch.bfloat16 or not dout.is_contiguous():
+        raise ValueError("dout: expected contiguous bf16 of q's shape")
+    nbytes = dms_soft_attention_backward_workspace_bytes(B, Hq, Hkv, T, d)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, Hkv, T, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
+    dlogit = torch.empty((B, Hkv, T), dtype=torch.float32, device=q.device)
+    dms_soft_attention_backward(B, Hq, Hkv, T, d, window, gamma, tau, scale, q.data_ptr(), k.data_ptr(),
+                                v.data_ptr(), logit.data_ptr(), noise.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dlogit.data_ptr(),
+                                workspace.data_ptr(), workspace.numel(), torch.cuda.current_stream().cuda_stream)
+    return {"dq": dq, "dk": dk, "dv": dv, "dlogit": dlogit}
 
 
 class Cache:

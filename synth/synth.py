@@ -30,7 +30,12 @@ Every value is addressed by ``(seed, stream, idx)``:
   fp32 bit pattern.
 * Eviction logits are ``float32(float64(mu) + float64(x))``, one rounding.
 
-Streams: Q = 0, K = 1, V = 2, logit = 3, lengths = 4.
+* Logistic noise (the relaxed decisions' random draw) takes the first word z
+  of each counter (channel 0) on stream 5: u = ((z >> 11) + 0.5) * 2**-53,
+  in (0, 1), and g = float32(log(u) - log(1 - u)), a Logistic(0, 1) sample
+  (the difference of two independent Gumbel(0, 1) samples).
+
+Streams: Q = 0, K = 1, V = 2, logit = 3, lengths = 4, noise = 5.
 """
 from __future__ import annotations
 
@@ -41,6 +46,7 @@ STREAM_K = 1
 STREAM_V = 2
 STREAM_LOGIT = 3
 STREAM_LEN = 4
+STREAM_NOISE = 5
 
 _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
@@ -171,3 +177,12 @@ def lengths(seed: int, batch: int, lo: int, hi: int) -> np.ndarray:
     z = splitmix64(base ^ (np.uint64(3) * idx))
     span = np.uint64(hi - lo + 1)
     return (np.uint64(lo) + z % span).astype(np.int64)
+
+
+def logistic_noise(seed: int, layer: int, b_list, heads: int, positions) -> np.ndarray:
+    """Logistic(0, 1) samples [B', heads, P] (float32), stream 5."""
+    idx = _grid(layer, b_list, heads, positions, 1)[..., 0]
+    base = np.uint64(seed) ^ (np.uint64(STREAM_NOISE) << np.uint64(56))
+    z = splitmix64(base ^ (np.uint64(3) * idx.astype(np.uint64)))
+    u = ((z >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
+    return (np.log(u) - np.log1p(-u)).astype(np.float32)

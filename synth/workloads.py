@@ -170,4 +170,73 @@ def full_32b() -> Workload:
                     "(layer 63), 128 decode steps")
 
 
+@dataclass
+class TrainWorkload:
+    """A layer of the relaxed (training-time) attention: every position of
+    `batch` sequences of `seq_len` tokens attends causally, with the soft mask
+    of logits ~ mu + N(0, 1) (Irwin-Hall), offset gamma, temperature tau and
+    Logistic(0, 1) noise.  dO is a query-shaped draw of seed + 1."""
+    name: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    seq_len: int
+    window: int
+    gamma: float
+    tau: float
+    mu: float
+    seed: int
+    description: str = ""
+
+    def host_slice(self, b_list, kv_heads):
+        """Host tensors of sequences b_list and KV heads kv_heads (with their
+        query heads): Q, K, V, dO (bf16-exact float32), logits, noise."""
+        G = self.num_q_heads // self.num_kv_heads
+        qh = [h * G + j for h in kv_heads for j in range(G)]
+        pos = np.arange(self.seq_len)
+        d = self.head_dim
+        Q = synth.tensor(self.seed, synth.STREAM_Q, 0, b_list, qh, pos, d, "bf16")
+        K = synth.tensor(self.seed, synth.STREAM_K, 0, b_list, kv_heads, pos, d, "bf16")
+        V = synth.tensor(self.seed, synth.STREAM_V, 0, b_list, kv_heads, pos, d, "bf16")
+        dO = synth.tensor(self.seed + 1, synth.STREAM_Q, 0, b_list, qh, pos, d, "bf16")
+        lg = synth.logits(self.seed, 0, b_list, kv_heads, pos, self.mu)
+        g = synth.logistic_noise(self.seed, 0, b_list, kv_heads, pos)
+        return Q, K, V, dO, lg, g
+
+    def device_inputs(self):
+        """The same values for the whole layer on the current GPU (the device
+        twin of the generator; the noise is drawn on the host)."""
+        import torch
+        from synth import device as dsynth
+        B, Hq, Hkv, T, d = self.batch, self.num_q_heads, self.num_kv_heads, self.seq_len, self.head_dim
+        q = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device="cuda")
+        do = torch.empty_like(q)
+        k = torch.empty((B, Hkv, T, d), dtype=torch.bfloat16, device="cuda")
+        v = torch.empty_like(k)
+        dsynth.fill(q, self.seed, synth.STREAM_Q, 0, 0)
+        dsynth.fill(do, self.seed + 1, synth.STREAM_Q, 0, 0)
+        dsynth.fill(k, self.seed, synth.STREAM_K, 0, 0)
+        dsynth.fill(v, self.seed, synth.STREAM_V, 0, 0)
+        lg = torch.empty((B, Hkv, T), dtype=torch.float32, device="cuda")
+        dsynth.logits(lg, self.seed, 0, 0, self.mu)
+        g = torch.from_numpy(synth.logistic_noise(self.seed, 0, np.arange(B), np.arange(Hkv),
+                                                  np.arange(T))).cuda()
+        return q, k, v, do, lg, g
+
+    def causal_pairs(self) -> int:
+        """(query, key) pairs with key <= query, all heads."""
+        T = self.seq_len
+        return self.batch * self.num_q_heads * T * (T + 1) // 2
+
+
+def qwen_32b_train() -> TrainWorkload:
+    return TrainWorkload(
+        name="qwen-r1-32b-train-layer", batch=4, num_q_heads=40, num_kv_heads=8, head_dim=128, seq_len=4096,
+        window=256, gamma=-5.0, tau=0.1, mu=5.0, seed=1006,
+        description="Qwen-R1-32B-shaped layer (40 Q / 8 KV heads, d 128, bf16, w 256) at training time: 4 "
+                    "sequences x 4096 tokens, relaxed decisions with tau 0.1, gamma -5, logits 5 + N(0, 1), "
+                    "Logistic noise")
+
+
 ALL = {w().name: w for w in (tiny, llama_1b, qwen_7b, qwen_32b, qwen_32b_dense, qwen_32b_hyperscale, full_32b)}

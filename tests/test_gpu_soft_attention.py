@@ -1,0 +1,183 @@
+"""GPU parity of the training-time relaxed attention (dms_soft_attention_forward
+and dms_soft_attention_backward) against the oracle's ``soft_attention`` and
+``soft_attention_grads``: every output, lse and gradient element at small and
+medium sizes (several tiles of every kernel and a ragged tail), sampled KV
+heads at the Qwen-R1-32B-shaped training layer, and the hard-decision limit
+against the GPU's own prompt attention.
+
+Tolerances: inputs are bf16-exact on both sides, so the differences are the
+GPU's fp32 arithmetic alone.  Probabilities and dS enter the MFMA products as
+bf16 hi + lo pairs (about 2^-17 relative), accumulation is fp32 over at most
+a few thousand terms, and exp2 / log2 are the hardware approximations (about
+1 ulp).  Each output is compared as max |got - want| / max(1, max |want|)
+against 1e-4 (out, dq, dk, dv, dlogit) and 1e-5 absolute for lse."""
+import numpy as np
+import pytest
+import torch
+
+from synth import synth
+
+gpu = pytest.mark.gpu
+
+TOL = 1e-4
+TOL_LSE = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gpu_util  # noqa: F401  (imports the HIP libraries; fails loudly if unbuilt)
+
+
+def _inputs(seed, B, Hq, Hkv, T, d, mu):
+    pos = np.arange(T)
+    Q = synth.tensor(seed, synth.STREAM_Q, 0, np.arange(B), np.arange(Hq), pos, d, "bf16")
+    K = synth.tensor(seed, synth.STREAM_K, 0, np.arange(B), np.arange(Hkv), pos, d, "bf16")
+    V = synth.tensor(seed, synth.STREAM_V, 0, np.arange(B), np.arange(Hkv), pos, d, "bf16")
+    # dO drawn as a query-shaped tensor of another seed (bf16-exact)
+    dO = synth.tensor(seed + 1, synth.STREAM_Q, 0, np.arange(B), np.arange(Hq), pos, d, "bf16")
+    lg = synth.logits(seed, 0, np.arange(B), np.arange(Hkv), pos, mu)
+    g = synth.logistic_noise(seed, 0, np.arange(B), np.arange(Hkv), pos)
+    return Q, K, V, dO, lg, g
+
+
+def _bf(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=torch.bfloat16)
+
+
+def _f(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def _nerr(got, want):
+    return float(np.max(np.abs(got - want))) / max(1.0, float(np.max(np.abs(want))))
+
+
+CASES = [
+    # id, B, Hq, Hkv, T, d, w, gamma, tau, mu
+    ("d128-g4-w8-ragged", 2, 8, 2, 150, 128, 8, 0.0, 1.0, 0.0),
+    ("d64-g8-w0", 1, 16, 2, 97, 64, 0, -2.0, 0.5, 1.0),
+    ("d128-g1-w-ge-T-no-far-keys", 1, 2, 2, 70, 128, 100, 0.0, 1.0, 0.0),
+    ("d128-g5-low-tau", 1, 10, 2, 333, 128, 16, -5.0, 0.1, 5.0),
+    ("d128-g5-one-token", 2, 10, 2, 1, 128, 4, 0.0, 1.0, 0.0),
+    ("d64-g4-many-tiles", 1, 4, 1, 1100, 64, 64, 0.0, 1.0, -1.0),
+    ("d128-g5-w32", 2, 10, 2, 417, 128, 32, 1.0, 2.0, -0.5),
+]
+
+
+def _run(case):
+    from learned_kv_cache_dms_amd import dms
+    from oracle import dms_oracle as O
+    name, B, Hq, Hkv, T, d, w, gamma, tau, mu = case
+    Q, K, V, dO, lg, g = _inputs(7000 + T + d, B, Hq, Hkv, T, d, mu)
+    print(f"[{name}] B={B} Hq={Hq} Hkv={Hkv} T={T} d={d} w={w} gamma={gamma} tau={tau}", flush=True)
+    q, k, v, do = _bf(Q), _bf(K), _bf(V), _bf(dO)
+    logit, noise = _f(lg), _f(g)
+    out, lse = dms.soft_attention_forward(q, k, v, logit, noise, w, gamma, tau)
+    grads = dms.soft_attention_backward(q, k, v, logit, noise, out, lse, do, w, gamma, tau)
+    torch.cuda.synchronize()
+    ref = O.soft_attention(Q, K, V, lg, g, w, gamma, tau)
+    refg = O.soft_attention_grads(Q, K, V, lg, g, dO, w, gamma, tau)
+    errs = {
+        "out": _nerr(out.double().cpu().numpy(), ref["out"]),
+        "lse": float(np.max(np.abs(lse.double().cpu().numpy() - ref["lse"]))),
+    }
+    for key in ("dq", "dk", "dv", "dlogit"):
+        errs[key] = _nerr(grads[key].double().cpu().numpy(), refg[key])
+    print(f"[{name}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    return errs, grads, refg
+
+
+@gpu
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_soft_attention_every_element(case):
+    errs, grads, refg = _run(case)
+    assert errs["lse"] <= TOL_LSE, (case[0], errs)
+    for key in ("out", "dq", "dk", "dv", "dlogit"):
+        assert errs[key] <= TOL, (case[0], key, errs)
+    if case[6] >= case[4] - 1:
+        # no query is more than w past any key: no key gets a logit gradient
+        assert float(grads["dlogit"].abs().max()) == 0.0
+
+
+@gpu
+def test_soft_attention_hard_limit_equals_prompt_attention():
+    """With |x| huge (tau tiny) the relaxed mask is the hard rule: the
+    forward equals dms_prefill_attention (the inference path) after a
+    prefill with the same logits, and no gradient reaches the logits."""
+    from learned_kv_cache_dms_amd import dms
+    B, Hq, Hkv, T, d, w = 2, 10, 2, 300, 128, 24
+    Q, K, V, dO, lg, _ = _inputs(7500, B, Hq, Hkv, T, d, 0.3)
+    lg = np.where(lg > 0, 40.0, -40.0).astype(np.float32)
+    zero = np.zeros_like(lg)
+    q, k, v = _bf(Q), _bf(K), _bf(V)
+    out, _ = dms.soft_attention_forward(q, k, v, _f(lg), _f(zero), w, 0.0, 1e-3)
+    cache = dms.Cache(B, Hq, Hkv, d, w, T + 1, B * Hkv * (T // 16 + 2), dtype="bf16")
+    cache.prefill(k, v, _f(lg), [T] * B)
+    hard = torch.empty((B, Hq, T, d), dtype=torch.float32, device="cuda")
+    cache.prefill_attention(q, k, v, hard)
+    grads = dms.soft_attention_backward(q, k, v, _f(lg), _f(zero), out, _, _bf(dO), w, 0.0, 1e-3)
+    torch.cuda.synchronize()
+    err = float((out - hard).abs().max())
+    print(f"[hard limit] max |soft - prompt attention| = {err:.2e}", flush=True)
+    assert err <= TOL
+    assert float(grads["dlogit"].abs().max()) == 0.0
+
+
+@gpu
+def test_soft_attention_full_size_sampled_heads():
+    """The Qwen-R1-32B-shaped training layer (40 Q / 8 KV heads, d = 128,
+    w = 256, T = 4096, tau = 0.1, gamma = -5): all heads on the GPU, two KV
+    heads (with their 5 query heads each) of two sequences against the
+    oracle."""
+    from learned_kv_cache_dms_amd import dms
+    from oracle import dms_oracle as O
+    from synth import workloads as W
+    wl = W.qwen_32b_train()
+    B, Hq, Hkv, T, d, w = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.seq_len, wl.head_dim, wl.window
+    G = Hq // Hkv
+    q, k, v, do, logit, noise = wl.device_inputs()
+    print(f"[qwen-32b training layer] B={B} Hq={Hq} T={T}", flush=True)
+    out, lse = dms.soft_attention_forward(q, k, v, logit, noise, w, wl.gamma, wl.tau)
+    grads = dms.soft_attention_backward(q, k, v, logit, noise, out, lse, do, w, wl.gamma, wl.tau)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (B - 1, Hkv - 1)]:
+        hs = slice(h * G, (h + 1) * G)
+        Q, K, V, dO, lg, g = wl.host_slice([b], [h])
+        ref = O.soft_attention(Q, K, V, lg, g, w, wl.gamma, wl.tau)
+        refg = O.soft_attention_grads(Q, K, V, lg, g, dO, w, wl.gamma, wl.tau)
+        errs = {
+            "out": _nerr(out[b:b + 1, hs].double().cpu().numpy(), ref["out"]),
+            "lse": float(np.max(np.abs(lse[b:b + 1, hs].double().cpu().numpy() - ref["lse"]))),
+            "dq": _nerr(grads["dq"][b:b + 1, hs].double().cpu().numpy(), refg["dq"]),
+            "dk": _nerr(grads["dk"][b:b + 1, h:h + 1].double().cpu().numpy(), refg["dk"]),
+            "dv": _nerr(grads["dv"][b:b + 1, h:h + 1].double().cpu().numpy(), refg["dv"]),
+            "dlogit": _nerr(grads["dlogit"][b:b + 1, h:h + 1].double().cpu().numpy(), refg["dlogit"]),
+        }
+        print(f"  (b={b}, h={h}) " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+        assert errs["lse"] <= TOL_LSE, errs
+        for key in ("out", "dq", "dk", "dv", "dlogit"):
+            assert errs[key] <= TOL, (b, h, key, errs)
+
+
+@gpu
+def test_soft_attention_errors():
+    from learned_kv_cache_dms_amd import dms
+    x = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16, device="cuda")
+    f = torch.zeros((1, 1, 8), dtype=torch.float32, device="cuda")
+    o = torch.zeros((1, 2, 8, 64), dtype=torch.float32, device="cuda")
+    l = torch.zeros((1, 2, 8), dtype=torch.float32, device="cuda")
+    p = lambda t: t.data_ptr()
+    with pytest.raises(dms.DmsError) as e:
+        dms.dms_soft_attention_forward(1, 2, 1, 8, 64, 4, 0.0, 0.0, 0.0, p(x), p(x), p(x), p(f), p(f), p(o), p(l))
+    assert e.value.status == dms.DMS_ERR_ARG
+    with pytest.raises(dms.DmsError) as e:
+        dms.dms_soft_attention_forward(1, 2, 1, 8, 96, 4, 0.0, 1.0, 0.0, p(x), p(x), p(x), p(f), p(f), p(o), p(l))
+    assert e.value.status == dms.DMS_ERR_ARG
+    need = dms.dms_soft_attention_backward_workspace_bytes(1, 2, 1, 8, 64)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dms.DmsError) as e:
+        dms.dms_soft_attention_backward(1, 2, 1, 8, 64, 4, 0.0, 1.0, 0.0, p(x), p(x), p(x), p(f), p(f), p(o), p(l),
+                                        p(x), p(o), p(o), p(o), p(f), p(ws), need - 1)
+    assert e.value.status == dms.DMS_ERR_WORKSPACE

@@ -75,3 +75,19 @@ def test_workload_recipes():
     assert 4500 < n < 4900
     f = workloads.full_32b()
     assert len(f.mu_before) == 64
+
+
+def test_logistic_noise_distribution_and_addressing():
+    """Logistic(0, 1): CDF 1 / (1 + e^-g) at a few points and variance pi^2 / 3
+    (within 5 standard errors for 400K samples); values addressed by counter,
+    not by the shape of the draw."""
+    g = synth.logistic_noise(11, 0, np.arange(4), 4, np.arange(25000)).astype(np.float64).ravel()
+    n = g.size
+    for x in (-np.log(3.0), 0.0, np.log(3.0), 3.0):
+        p = 1.0 / (1.0 + np.exp(-x))
+        assert abs(np.mean(g <= x) - p) < 5 * np.sqrt(p * (1 - p) / n), x
+    assert abs(np.var(g) - np.pi ** 2 / 3) < 0.05
+    part = synth.logistic_noise(11, 0, [2], [3], np.arange(100, 200))
+    full = synth.logistic_noise(11, 0, np.arange(4), 4, np.arange(25000))
+    assert np.array_equal(part[0, 0], full[2, 3, 100:200])
+    assert np.all(np.isfinite(g))
