@@ -212,6 +212,94 @@ def bench_prefill_attention(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_soft_attention(args):
+    """Training-time relaxed attention (dms_soft_attention_forward, then
+    dms_soft_attention_backward) on the Qwen-R1-32B-shaped training layer.
+    Algorithmic flops per causal (query, key) pair and head: 4 d forward (q.k,
+    p.v) and 8 d backward (dP = dO v^T, dq, dk, dv; the recomputed scores are
+    not counted).  Forward and backward are timed with HIP events on the
+    stream the library launches on; the step is one of each."""
+    import numpy as np
+    import torch
+    from learned_kv_cache_dms_amd import dms
+    from synth import workloads
+
+    torch.cuda.set_device(0)
+    wl = workloads.qwen_32b_train()
+    B, Hq, Hkv, T, d, w = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.seq_len, wl.head_dim, wl.window
+    q, k, v, do, logit, noise = wl.device_inputs()
+    out = torch.empty((B, Hq, T, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dms.dms_soft_attention_backward_workspace_bytes(B, Hq, Hkv, T, d), dtype=torch.uint8,
+                     device="cuda")
+    fws = torch.empty(dms.dms_soft_attention_forward_workspace_bytes(B, Hq, Hkv, T, d), dtype=torch.uint8,
+                      device="cuda")
+    pairs = wl.causal_pairs()
+    f_fwd, f_bwd = 4.0 * d * pairs, 8.0 * d * pairs
+
+    def fwd():
+        dms.soft_attention_forward(q, k, v, logit, noise, w, wl.gamma, wl.tau, out=out, lse=lse, workspace=fws)
+
+    def bwd():
+        return dms.soft_attention_backward(q, k, v, logit, noise, out, lse, do, w, wl.gamma, wl.tau, workspace=ws)
+
+    W, K = args.warmup, args.steps
+    for _ in range(W):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(s)
+        fwd()
+        e[1].record(s)
+        bwd()
+        e[2].record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_f = [a.elapsed_time(b) for a, b, _ in ev]
+    ms_b = [b.elapsed_time(c) for _, b, c in ev]
+    mf, mb = sum(ms_f) / K / 1e3, sum(ms_b) / K / 1e3
+    tf_f, tf_b = f_fwd / mf / 1e12, f_bwd / mb / 1e12
+    tf_all = (f_fwd + f_bwd) / (mf + mb) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import dms_oracle as O
+        sample = [(b, h) for b in (0, B - 1) for h in range(0, Hkv, 2)]
+        t1 = time.perf_counter()
+        for (b, h) in sample:
+            Q, K_, V, dO, lg, g = wl.host_slice([b], [h])
+            O.soft_attention(Q, K_, V, lg, g, w, wl.gamma, wl.tau)
+            O.soft_attention_grads(Q, K_, V, lg, g, dO, w, wl.gamma, wl.tau)
+        secs = time.perf_counter() - t1
+        G = Hq // Hkv
+        cpu_flops = 12.0 * d * len(sample) * G * T * (T + 1) // 2
+        cpu = {"value": round(cpu_flops / secs / 1e12, 5), "unit": "TFLOP/s", "cores": torch.get_num_threads(),
+               "kind": "oracle",
+               "sample": f"forward + gradients of {len(sample)} KV heads x {G} query heads x {T} tokens "
+                         f"(float64 numpy, {secs:.1f} s incl. input generation)"}
+    res = {
+        "metric": "relaxed DMS attention forward + backward, algorithmic TFLOP/s (training layer)",
+        "value": round(tf_all, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round((mf + mb) * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "seq_len": T, "window": w, "tau": wl.tau, "gamma": wl.gamma},
+        "forward_ms": round(mf * 1e3, 4), "backward_ms": round(mb * 1e3, 4),
+        "forward_tflops": round(tf_f, 2), "backward_tflops": round(tf_b, 2),
+        "tokens_per_s": round(B * T / (mf + mb), 1), "causal_pairs": pairs, "wall_s": round(wall, 3),
+        "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf_b / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "dms_soft_attention_backward (pack, dq, dkv launches)",
+                     "algorithmic_flops_per_launch": f_bwd},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_hyper_scaling(args):
     """The hyper-scaling harness: the vanilla generation (8 chains x 16384
     tokens after a 1024-token prompt, nothing evicted) sets a KV memory-read
@@ -475,6 +563,8 @@ def main():
                     help="time dms_decode_chunk with this many tokens per sequence per call")
     ap.add_argument("--hyper-scaling", action="store_true",
                     help="run the hyper-scaling harness (vanilla budget, DMS frontier, end-to-end runs)")
+    ap.add_argument("--soft-attention", action="store_true",
+                    help="training-time relaxed attention forward + backward on the 32B-shaped training layer")
     ap.add_argument("--prefill-attention", action="store_true",
                     help="time dms_prefill_attention on the workload's prompt instead of the decode step "
                          "(use small --steps / --warmup: one call is a whole prompt)")
@@ -496,6 +586,9 @@ def main():
         return
     if args.hyper_scaling:
         bench_hyper_scaling(args)
+        return
+    if args.soft_attention:
+        bench_soft_attention(args)
         return
     if args.chunk:
         bench_chunk(args)

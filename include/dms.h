@@ -263,17 +263,25 @@ DMS_API int dms_decode_chunk_channel(dms_cache* c, const void* d_q, const void* 
    decode path (alpha in {0, 1}).
    Layouts: d_q [B, Hq, T, d], d_k, d_v [B, Hkv, T, d] bf16; d_logit,
    d_noise [B, Hkv, T] fp32; d_out [B, Hq, T, d] and d_lse [B, Hq, T] fp32.
-   d = 64 or 128; 1 <= T <= 2^20; window >= 0; tau > 0.  Async.  Errors:
-   DMS_ERR_ARG for NULL pointers or bad shapes or parameters, DMS_ERR_DEVICE
-   if the current device is not gfx950. */
+   d = 64 or 128; 1 <= T <= 2^20; window >= 0; tau > 0.  d_workspace:
+   256-byte aligned, at least dms_soft_attention_forward_workspace_bytes (a
+   copy of v in a transposed operand layout and each key's bias).  Async.
+   Errors: DMS_ERR_ARG for NULL pointers or bad shapes or parameters,
+   DMS_ERR_WORKSPACE for a small or unaligned workspace, DMS_ERR_DEVICE if
+   the current device is not gfx950. */
 DMS_API int dms_soft_attention_forward(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d, int32_t window,
                                        float gamma, float tau, float scale, const void* d_q, const void* d_k,
                                        const void* d_v, const float* d_logit, const float* d_noise, float* d_out,
-                                       float* d_lse, void* stream);
+                                       float* d_lse, void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace dms_soft_attention_forward needs (0 for bad
+   shapes). */
+DMS_API size_t dms_soft_attention_forward_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
+                                                          int32_t d);
 
 /* Bytes of device workspace dms_soft_attention_backward needs (0 for bad
-   shapes): copies of q, dout and k in a transposed operand layout, and the
-   row dot products sum(dout * out). */
+   shapes): copies of q, dout and k in a transposed operand layout, the row
+   dot products sum(dout * out) and each key's bias. */
 DMS_API size_t dms_soft_attention_backward_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
                                                            int32_t d);
 

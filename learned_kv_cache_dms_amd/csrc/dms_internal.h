@@ -104,8 +104,11 @@ hipError_t launch_decode_chunk(const Dev& p, int dtype, int d, const void* q, co
 int chunk_max_blocks();
 // Relaxed attention, bf16 q [B, Hq, T, d], k, v [B, Hkv, T, d]; logit, noise
 // [B, Hkv, T] fp32.  Forward: out [B, Hq, T, d] and lse [B, Hq, T] fp32.
+// ws holds soft_forward_workspace_bytes.
+int64_t soft_forward_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
 hipError_t launch_soft_forward(const SoftArgs& a, int d, const void* q, const void* k, const void* v,
-                               const float* logit, const float* noise, float* out, float* lse, hipStream_t s);
+                               const float* logit, const float* noise, float* out, float* lse, void* ws,
+                               hipStream_t s);
 // Backward from dout (bf16, like out): dq, dk, dv (fp32, like q, k, v) and
 // dlogit (fp32, like logit); ws holds soft_backward_workspace_bytes.
 int64_t soft_backward_workspace_bytes(int B, int Hq, int Hkv, int T, int d);

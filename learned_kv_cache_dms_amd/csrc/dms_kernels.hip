@@ -1648,79 +1648,18 @@ __device__ __forceinline__ void attend_pair_biased(const PairFrag<2, D>& f, cons
 }
 
 // Forward: out = softmax(scale q k^T + bias) v and lse (natural log of each
-// row's softmax denominator) for every position.  q [B, Hq, T, d], k, v [B,
-// Hkv, T, d] bf16; logit, noise [B, Hkv, T] fp32; out [B, Hq, T, d], lse [B,
-// Hq, T] fp32.  Grid (ceil(T / kPfTile), Hq, B), as the prompt attention.
+// row's softmax denominator) for every position.  q [B, Hq, T, d], k [B, Hkv,
+// T, d] bf16 rows; vt the pairT copy of v; bias2 the keys' far bias
+// (exp2 domain, soft_bias_kernel); out [B, Hq, T, d], lse [B, Hq, T] fp32.
+// Each wave holds kPfCols tiles of 16 queries and streams the causal keys in
+// pairs of 16-row blocks, one pair loaded ahead of the one computed.  Grid
+// (ceil(T / kPfTile), Hq, B).
 template <int D>
 __global__ __launch_bounds__(256) void soft_forward_kernel(SoftArgs a, const uint8_t* __restrict__ q,
                                                            const uint8_t* __restrict__ k,
-                                                           const uint8_t* __restrict__ v,
-                                                           const float* __restrict__ logit,
-                                                           const float* __restrict__ noise, float* __restrict__ out,
-                                                           float* __restrict__ lse) {
-  using G = Geo<2, D>;
-  constexpr int ES = 2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.z, hq = blockIdx.y, h = hq / a.G;
-  const int T = a.T, w = a.w;
-  const int q0 = blockIdx.x * kPfTile;
-  const int qmax = min(q0 + kPfTile, T) - 1;
-  const int64_t urow = ((int64_t)b * a.Hkv + h) * T;
-  const uint8_t* Ku = k + urow * D * ES;
-  const uint8_t* Vu = v + urow * D * ES;
-  const uint8_t* Qh = q + ((int64_t)b * a.Hq + hq) * T * D * ES;
-  const int tb = 4 * (lane >> 4);
-  int qc[kPfCols];
-  u32x4 qf[kPfCols][G::kChunks];
-  Acc<D> acc[kPfCols];
-#pragma unroll
-  for (int t = 0; t < kPfCols; ++t) {
-    qc[t] = q0 + 16 * (kPfCols * wave + t) + (lane & 15);
-    const uint8_t* qrow = Qh + (int64_t)min(qc[t], T - 1) * D * ES;
-#pragma unroll
-    for (int c = 0; c < G::kChunks; ++c) qf[t][c] = *(const u32x4*)(qrow + c * 64 + 16 * (lane >> 4));
-#pragma unroll
-    for (int j = 0; j < G::kTiles; ++j) acc[t].o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[t].m = -INFINITY;
-    acc[t].l = 0.f;
-  }
-  constexpr float kLog2e = 1.4426950408889634f;
-  for (int r0 = 0; r0 <= qmax; r0 += 32) {
-    Frag<ES, D> fa, fb;
-    load_frag_dense<ES, D>(fa, Ku, Vu, r0, T - 1, lane);
-    load_frag_dense<ES, D>(fb, Ku, Vu, r0 + 16, T - 1, lane);
-    PairFrag<ES, D> f;
-    make_pair<ES, D>(f, fa, fb);
-    float kb2[8];  // this lane's keys' far bias, exp2 domain
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int i = min(r0 + (r >> 2) * 16 + tb + (r & 3), T - 1);
-      kb2[r] = -softplus_f(soft_x(a, logit, noise, urow, i)) * kLog2e;
-    }
-#pragma unroll
-    for (int t = 0; t < kPfCols; ++t) {
-      float badd[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int i = r0 + (r >> 2) * 16 + tb + (r & 3);
-        badd[r] = i > qc[t] ? -INFINITY : (qc[t] - i > w ? kb2[r] : 0.f);
-      }
-      attend_pair_biased<D>(f, qf[t], badd, a.scale_log2e, acc[t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < kPfCols; ++t) {
-    float lt = acc[t].l + __shfl_xor(acc[t].l, 16);
-    lt = lt + __shfl_xor(lt, 32);
-    if (qc[t] >= T) continue;
-    const float inv = 1.0f / lt;
-    const int64_t row = ((int64_t)b * a.Hq + hq) * T + qc[t];
-    float* orow = out + row * D + 4 * (lane >> 4);
-#pragma unroll
-    for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(orow + 16 * j) = acc[t].o[j] * inv;
-    if (lane < 16) lse[row] = (acc[t].m + log2f(lt)) / kLog2e;
-  }
-}
+                                                           const uint8_t* __restrict__ vt,
+                                                           const float* __restrict__ bias2, float* __restrict__ out,
+                                                           float* __restrict__ lse);
 
 // Bias of key i in the exp2 domain, log2e * log(1 - sigmoid(x)) =
 // -(max(x, 0) log2e + log2(1 + 2^(-|x| log2e))).  It is added to a score, so
@@ -1821,36 +1760,226 @@ __device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, f32x4
                                                  0, 0);
 }
 
-constexpr int kSoftQCols = 2;                            // query tiles of 16 per wave (dQ)
-constexpr int kSoftQTile = 16 * kSoftQCols * kWavesPerWG;  // queries per work-group (dQ)
-constexpr int kSoftKTile = 16 * kWavesPerWG;               // keys per work-group (dK, dV)
+// Far bias of every key, bias2[u][i] = log2e * log(1 - sigmoid(x_i)) for
+// unit u = b * Hkv + h, rows padded to a multiple of 32 with 0.
+__global__ __launch_bounds__(256) void soft_bias_kernel(SoftArgs a, const float* __restrict__ logit,
+                                                        const float* __restrict__ noise, float* __restrict__ bias2) {
+  const int rows = (a.T + 31) / 32 * 32;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)a.B * a.Hkv * rows) return;
+  const int64_t u = e / rows;
+  const int i = (int)(e - u * rows);
+  bias2[e] = i < a.T ? soft_bias2(soft_x(a, logit, noise, u * a.T, i)) : 0.f;
+}
+
+template <int D>
+struct SoftPair {
+  PairFrag<2, D> f;
+  f32x4 ba, bb;  // far bias of this lane's keys tb..tb+3 of blocks A and B
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void soft_forward_kernel(SoftArgs a, const uint8_t* __restrict__ q,
+                                                           const uint8_t* __restrict__ k,
+                                                           const uint8_t* __restrict__ vt,
+                                                           const float* __restrict__ bias2, float* __restrict__ out,
+                                                           float* __restrict__ lse) {
+  using G = Geo<2, D>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.z, hq = blockIdx.y, h = hq / a.G;
+  const int T = a.T, w = a.w;
+  const int npairs = (T + 31) / 32;
+  const int q0 = blockIdx.x * kPfTile;
+  const int qmax = min(q0 + kPfTile, T) - 1;
+  const int64_t unit = (int64_t)b * a.Hkv + h;
+  const uint8_t* Ku = k + unit * T * D * 2;
+  const uint8_t* Vt = vt + unit * npairs * 32 * D * 2;
+  const float* bu = bias2 + unit * npairs * 32;
+  const uint8_t* Qh = q + ((int64_t)b * a.Hq + hq) * T * D * 2;
+  const int tb = 4 * (lane >> 4);
+  int qc[kPfCols];
+  u32x4 qf[kPfCols][G::kChunks];
+  Acc<D> acc[kPfCols];
+#pragma unroll
+  for (int t = 0; t < kPfCols; ++t) {
+    const int c0 = q0 + 16 * (kPfCols * wave + t);
+    qc[t] = c0 + (lane & 15);
+    load_rows<D>(qf[t], Qh, c0, T - 1, lane);
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) acc[t].o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[t].m = -INFINITY;
+    acc[t].l = 0.f;
+  }
+  const int npair = qmax / 32 + 1;
+  // Loads are unconditional: an index past the last pair re-reads it (not
+  // computed).  The scheduling barriers keep a pair's loads ahead of the
+  // previous pair's arithmetic.
+  auto fetch = [&](SoftPair<D>& x, int i) {
+    i = min(i, npair - 1);
+    load_rows<D>(x.f.ka, Ku, 32 * i, T - 1, lane);
+    load_rows<D>(x.f.kb, Ku, 32 * i + 16, T - 1, lane);
+    load_pairT<D>(x.f.v, Vt, i, lane);
+    x.ba = *(const f32x4*)(bu + 32 * i + tb);
+    x.bb = *(const f32x4*)(bu + 32 * i + 16 + tb);
+  };
+  const int cw0 = q0 + 16 * kPfCols * wave;  // the wave's first query
+  auto compute = [&](const SoftPair<D>& x, int i) {
+    if (32 * i + 31 + w < cw0) {
+      // every key of the pair is past the window of every query of the wave
+      const float badd[8] = {x.ba[0], x.ba[1], x.ba[2], x.ba[3], x.bb[0], x.bb[1], x.bb[2], x.bb[3]};
+#pragma unroll
+      for (int t = 0; t < kPfCols; ++t) attend_pair_biased<D>(x.f, qf[t], badd, a.scale_log2e, acc[t]);
+      return;
+    }
+#pragma unroll
+    for (int t = 0; t < kPfCols; ++t) {
+      float badd[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int key = 32 * i + (r >> 2) * 16 + tb + (r & 3);
+        const float fb = r < 4 ? x.ba[r] : x.bb[r - 4];
+        badd[r] = key > qc[t] ? -INFINITY : (qc[t] - key > w ? fb : 0.f);
+      }
+      attend_pair_biased<D>(x.f, qf[t], badd, a.scale_log2e, acc[t]);
+    }
+  };
+  SoftPair<D> f0, f1;
+  fetch(f0, 0);
+  for (int i = 0; i < npair; i += 2) {
+    fetch(f1, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(f0, i);
+    if (i + 1 >= npair) break;
+    fetch(f0, i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(f1, i + 1);
+  }
+  constexpr float kLog2e = 1.4426950408889634f;
+#pragma unroll
+  for (int t = 0; t < kPfCols; ++t) {
+    float lt = acc[t].l + __shfl_xor(acc[t].l, 16);
+    lt = lt + __shfl_xor(lt, 32);
+    if (qc[t] >= T) continue;
+    const float inv = 1.0f / lt;
+    const int64_t row = ((int64_t)b * a.Hq + hq) * T + qc[t];
+    float* orow = out + row * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(orow + 16 * j) = acc[t].o[j] * inv;
+    if (lane < 16) lse[row] = (acc[t].m + log2f(lt)) / kLog2e;
+  }
+}
+
+#ifndef DMS_SOFT_QCOLS
+#define DMS_SOFT_QCOLS 1
+#endif
+#ifndef DMS_SOFT_DQ_WG
+#define DMS_SOFT_DQ_WG 4
+#endif
+#ifndef DMS_SOFT_DKV_WG
+#define DMS_SOFT_DKV_WG 4
+#endif
+// Waves per work-group of the backward kernels: the waves of a work-group
+// share every staged step, so more waves means fewer re-reads of the
+// streamed operands (the dominant L2 / MALL traffic).
+constexpr int kSoftQWaves = DMS_SOFT_DQ_WG;
+constexpr int kSoftKWaves = DMS_SOFT_DKV_WG;
+constexpr int kSoftQCols = DMS_SOFT_QCOLS;               // query tiles of 16 per wave (dQ)
+constexpr int kSoftQTile = 16 * kSoftQCols * kSoftQWaves;  // queries per work-group (dQ)
+constexpr int kSoftKTile = 16 * kSoftKWaves;               // keys per work-group (dK, dV)
 
 // Backward, query-stationary: dq = scale * dS k with dS = P (dP - delta), P
 // recomputed from the forward's lse, dP = dO v^T.  Each wave holds
 // kSoftQCols tiles of 16 queries (columns) and streams the causal keys in
 // pairs of 16-row blocks: S^T = k q^T and dP^T = v dO^T with the keys as rows,
-// then dq^T += k^T dS^T with k^T from its pairT copy.  Grid (ceil(T /
+// then dq^T += k^T dS^T with k^T from its pairT copy.  The 4 waves share each
+// key pair: the work-group stages k and v rows (operand order), k^T and the
+// keys' bias in LDS, double-buffered as in soft_dkv_kernel.  Grid (ceil(T /
 // kSoftQTile), Hq, B).
+// Pieces of one staged operand this thread moves (32 rows of D bf16 = 4 D
+// pieces, NTH threads): row operands in fragment order, piece (blk * D / 32 +
+// c) * 64 + l = row 16 blk + l % 16, bytes 64 c + 16 (l / 16); pairT
+// operands are contiguous already.  Row offsets and piece slots are fixed per
+// thread.
+template <int D, int NTH>
+struct SoftStagePieces {
+  static constexpr int kN = (4 * D + NTH - 1) / NTH;  // pieces per thread per operand (slot < 4 D)
+  int slot[kN];                           // piece index in the operand
+  int row[kN];                            // row within the 32 (row operands)
+  int col_bytes[kN];                      // byte offset within the row
+  // Only when the threads outnumber the pieces does a slot fall outside.
+  static __device__ __forceinline__ bool valid(int slot) { return (4 * D) % NTH == 0 || slot < 4 * D; }
+  __device__ __forceinline__ SoftStagePieces(int tid) {
+    constexpr int NCH = D / 32;
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+      const int pc = tid + NTH * n, l = pc & 63;
+      slot[n] = pc;
+      row[n] = 16 * (pc / (NCH * 64)) + (l & 15);
+      col_bytes[n] = 64 * ((pc / 64) % NCH) + 16 * (l >> 4);
+    }
+  }
+};
+
 template <int D>
-__global__ __launch_bounds__(256) void soft_dq_kernel(SoftArgs a, const uint8_t* __restrict__ q,
-                                                      const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
-                                                      const uint8_t* __restrict__ kt, const uint8_t* __restrict__ dO,
-                                                      const float* __restrict__ logit,
-                                                      const float* __restrict__ noise, const float* __restrict__ lse,
-                                                      const float* __restrict__ delta, float* __restrict__ dq) {
-  constexpr int NCH = D / 32, NT = D / 16;
+struct SoftQStage {
+  static constexpr int kOps = 3;                       // k rows, v rows, k^T
+  static constexpr int kOpPieces = 32 * D * 2 / 16;
+  u32x4 op[kOps][kOpPieces];
+  float bias[32];
+};
+
+#ifndef DMS_SOFT_DQ_WAVES
+#define DMS_SOFT_DQ_WAVES 2
+#endif
+template <int D>
+__global__ __launch_bounds__(64 * kSoftQWaves) __attribute__((amdgpu_waves_per_eu(DMS_SOFT_DQ_WAVES))) void soft_dq_kernel(
+    SoftArgs a, const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+    const uint8_t* __restrict__ kt, const uint8_t* __restrict__ dO, const float* __restrict__ bias2,
+    const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dq) {
+  using St = SoftQStage<D>;
+  using Pc = SoftStagePieces<D, 64 * kSoftQWaves>;
+  constexpr int NCH = D / 32, NT = D / 16, NP = Pc::kN;
   constexpr float kLog2e = 1.4426950408889634f;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ St st[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.z, hq = blockIdx.y, h = hq / a.G;
   const int T = a.T, w = a.w;
+  const int npairs = (T + 31) / 32;
   const int q0 = blockIdx.x * kSoftQTile;
   const int qmax = min(q0 + kSoftQTile, T) - 1;
-  const int64_t urow = ((int64_t)b * a.Hkv + h) * T;
+  const int cw0 = q0 + 16 * kSoftQCols * wave;  // the wave's first query
+  const int64_t unit = (int64_t)b * a.Hkv + h;
+  const int64_t urow = unit * T;
   const int64_t hrow = ((int64_t)b * a.Hq + hq) * T;
   const uint8_t* Ku = k + urow * D * 2;
   const uint8_t* Vu = v + urow * D * 2;
-  const uint8_t* Kt = kt + ((int64_t)b * a.Hkv + h) * ((T + 31) / 32) * 32 * D * 2;
+  const uint8_t* Kt = kt + unit * npairs * 32 * D * 2;
+  const float* bu = bias2 + unit * npairs * 32;
   const int tb = 4 * (lane >> 4);
+  const int nsteps = qmax / 32 + 1;
+  const Pc pcs(tid);
+
+  auto gload = [&](u32x4 (&r)[3][NP], float& bx, int s) {
+    const int r0 = 32 * s;
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+      if (!Pc::valid(pcs.slot[n])) continue;
+      const int off = min(r0 + pcs.row[n], T - 1) * D * 2 + pcs.col_bytes[n];
+      r[0][n] = *(const u32x4*)(Ku + off);
+      r[1][n] = *(const u32x4*)(Vu + off);
+      r[2][n] = *(const u32x4*)(Kt + (int64_t)s * 32 * D * 2 + pcs.slot[n] * 16);
+    }
+    if (tid < 32) bx = bu[r0 + tid];
+  };
+  auto lds_store = [&](St& S, const u32x4 (&r)[3][NP], float bx) {
+#pragma unroll
+    for (int o = 0; o < 3; ++o)
+#pragma unroll
+      for (int n = 0; n < NP; ++n)
+        if (Pc::valid(pcs.slot[n])) S.op[o][pcs.slot[n]] = r[o][n];
+    if (tid < 32) S.bias[tid] = bx;
+  };
+
   int qc[kSoftQCols];
   float lse2[kSoftQCols], dl[kSoftQCols];
   u32x4 qf[kSoftQCols][NCH], of[kSoftQCols][NCH];
@@ -1867,19 +1996,26 @@ __global__ __launch_bounds__(256) void soft_dq_kernel(SoftArgs a, const uint8_t*
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  for (int r0 = 0; r0 <= qmax; r0 += 32) {
-    u32x4 ka[NCH], kb[NCH], va[NCH], vb[NCH], ktp[NT];
-    load_rows<D>(ka, Ku, r0, T - 1, lane);
-    load_rows<D>(kb, Ku, r0 + 16, T - 1, lane);
-    load_rows<D>(va, Vu, r0, T - 1, lane);
-    load_rows<D>(vb, Vu, r0 + 16, T - 1, lane);
-    load_pairT<D>(ktp, Kt, r0 / 32, lane);
-    float kb2[8];
+  u32x4 pre[3][NP];
+  float prb = 0.f;
+  gload(pre, prb, 0);
+  lds_store(st[0], pre, prb);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    if (s + 1 < nsteps) gload(pre, prb, s + 1);
+    const St& S = st[s & 1];
+    const int r0 = 32 * s;
+    // every key of the pair is past the window of every query of the wave
+    const bool far = r0 + 31 + w < cw0;
+    u32x4 ka[NCH], kb[NCH], va[NCH], vb[NCH];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int i = min(r0 + (r >> 2) * 16 + tb + (r & 3), T - 1);
-      kb2[r] = soft_bias2(soft_x(a, logit, noise, urow, i));
+    for (int c = 0; c < NCH; ++c) {
+      ka[c] = S.op[0][c * 64 + lane];
+      kb[c] = S.op[0][(NCH + c) * 64 + lane];
+      va[c] = S.op[1][c * 64 + lane];
+      vb[c] = S.op[1][(NCH + c) * 64 + lane];
     }
+    const f32x4 ba = *(const f32x4*)&S.bias[tb], bb = *(const f32x4*)&S.bias[16 + tb];
 #pragma unroll
     for (int t = 0; t < kSoftQCols; ++t) {
       f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = SA, PA = SA, PB = SA;
@@ -1891,23 +2027,36 @@ __global__ __launch_bounds__(256) void soft_dq_kernel(SoftArgs a, const uint8_t*
         PB = mfma_bf16(vb[c], of[t][c], PB);
       }
       float ds[8];
+      if (far) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int i = r0 + (r >> 2) * 16 + tb + (r & 3);
-        const float badd = i > qc[t] ? -INFINITY : (qc[t] - i > w ? kb2[r] : 0.f);
-        const float sv = r < 4 ? SA[r] : SB[r - 4];
-        const float dp = r < 4 ? PA[r] : PB[r - 4];
-        const float pr = exp2_fast(fmaf(sv, a.scale_log2e, badd) - lse2[t]);
-        ds[r] = pr * (dp - dl[t]);
+        for (int r = 0; r < 8; ++r) {
+          const float kb2 = r < 4 ? ba[r] : bb[r - 4];
+          const float sv = r < 4 ? SA[r] : SB[r - 4];
+          const float dp = r < 4 ? PA[r] : PB[r - 4];
+          ds[r] = exp2_fast(fmaf(sv, a.scale_log2e, kb2 - lse2[t])) * (dp - dl[t]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int i = r0 + (r >> 2) * 16 + tb + (r & 3);
+          const float kb2 = r < 4 ? ba[r] : bb[r - 4];
+          const float badd = i > qc[t] ? -INFINITY : (qc[t] - i > w ? kb2 : 0.f);
+          const float sv = r < 4 ? SA[r] : SB[r - 4];
+          const float dp = r < 4 ? PA[r] : PB[r - 4];
+          ds[r] = exp2_fast(fmaf(sv, a.scale_log2e, badd) - lse2[t]) * (dp - dl[t]);
+        }
       }
       bf16x8 DH, DL;
       split_pair(ds, DH, DL);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ktp[j]), DH, acc[t][j], 0, 0, 0);
-        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ktp[j]), DL, acc[t][j], 0, 0, 0);
+        const bf16x8 KT = __builtin_bit_cast(bf16x8, S.op[2][j * 64 + lane]);
+        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KT, DH, acc[t][j], 0, 0, 0);
+        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KT, DL, acc[t][j], 0, 0, 0);
       }
     }
+    if (s + 1 < nsteps) lds_store(st[(s + 1) & 1], pre, prb);
+    __syncthreads();
   }
 #pragma unroll
   for (int t = 0; t < kSoftQCols; ++t) {
@@ -1923,10 +2072,22 @@ __global__ __launch_bounds__(256) void soft_dq_kernel(SoftArgs a, const uint8_t*
 // q and dlogit = -sigmoid(x) / tau * (sum of dS over the far queries).  S =
 // q k^T and dP = dO v^T with the queries as rows (k, v rows stay in
 // registers); dv^T += dO^T P and dk^T += q^T dS with dO^T, q^T from their
-// pairT copies.  No atomics: every key has one owner.  Grid (ceil(T /
-// kSoftKTile), Hkv, B); the work-groups with the most queries start first.
+// pairT copies.  The 4 waves share each step's 32 queries: the work-group
+// stages q and dO (rows and pairT, in operand order) and the rows' lse and
+// delta in LDS, double-buffered, the next step's loads in flight during the
+// current step's products.  No atomics: every key has one owner.  Grid
+// (ceil(T / kSoftKTile), Hkv, B); the work-groups with the most queries
+// start first.
 template <int D>
-__global__ __launch_bounds__(256) void soft_dkv_kernel(SoftArgs a, const uint8_t* __restrict__ q,
+struct SoftKvStage {
+  static constexpr int kOps = 4;                       // q rows, dO rows, q^T, dO^T
+  static constexpr int kOpPieces = 32 * D * 2 / 16;    // 16-byte pieces of one operand
+  u32x4 op[kOps][kOpPieces];
+  float lse2[32], delta[32];
+};
+
+template <int D>
+__global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, const uint8_t* __restrict__ q,
                                                        const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
                                                        const uint8_t* __restrict__ qt, const uint8_t* __restrict__ dO,
                                                        const uint8_t* __restrict__ dOt,
@@ -1934,9 +2095,12 @@ __global__ __launch_bounds__(256) void soft_dkv_kernel(SoftArgs a, const uint8_t
                                                        const float* __restrict__ noise, const float* __restrict__ lse,
                                                        const float* __restrict__ delta, float* __restrict__ dk,
                                                        float* __restrict__ dv, float* __restrict__ dlogit) {
-  constexpr int NCH = D / 32, NT = D / 16;
+  using St = SoftKvStage<D>;
+  using Pc = SoftStagePieces<D, 64 * kSoftKWaves>;
+  constexpr int NCH = D / 32, NT = D / 16, NP = Pc::kN;
   constexpr float kLog2e = 1.4426950408889634f;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ St st[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.z, h = blockIdx.y;
   const int T = a.T, w = a.w;
   const int nkt = (T + kSoftKTile - 1) / kSoftKTile;
@@ -1946,6 +2110,52 @@ __global__ __launch_bounds__(256) void soft_dkv_kernel(SoftArgs a, const uint8_t
   const int64_t urow = ((int64_t)b * a.Hkv + h) * T;
   const int npairs = (T + 31) / 32;
   const int tb = 4 * (lane >> 4);
+  const int per_head = (T - kbase + 31) / 32;  // steps of 32 queries per query head
+  const int nsteps = a.G * per_head;
+  const Pc pcs(tid);
+
+  // Step state (hq, q0), advanced without divisions.
+  struct Pos {
+    int hq, q0;
+  };
+  auto next = [&](Pos p) -> Pos {
+    p.q0 += 32;
+    if (p.q0 >= T) {
+      p.q0 = kbase;
+      ++p.hq;
+    }
+    return p;
+  };
+  auto gload = [&](u32x4 (&r)[4][NP], float& x, Pos p) {
+    const int64_t head = (int64_t)b * a.Hq + p.hq;
+    const uint8_t* Qh = q + head * T * D * 2;
+    const uint8_t* Oh = dO + head * T * D * 2;
+    const uint8_t* Qt = qt + (head * npairs + p.q0 / 32) * 32 * D * 2;
+    const uint8_t* Ot = dOt + (head * npairs + p.q0 / 32) * 32 * D * 2;
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+      if (!Pc::valid(pcs.slot[n])) continue;
+      const int off = min(p.q0 + pcs.row[n], T - 1) * D * 2 + pcs.col_bytes[n];
+      r[0][n] = *(const u32x4*)(Qh + off);
+      r[1][n] = *(const u32x4*)(Oh + off);
+      r[2][n] = *(const u32x4*)(Qt + pcs.slot[n] * 16);
+      r[3][n] = *(const u32x4*)(Ot + pcs.slot[n] * 16);
+    }
+    if (tid < 64) {  // lse (0..31) and delta (32..63) of the step's rows
+      const int64_t row = head * T + min(p.q0 + (tid & 31), T - 1);
+      x = tid < 32 ? lse[row] * kLog2e : delta[row];
+    }
+  };
+  auto lds_store = [&](St& S, const u32x4 (&r)[4][NP], float x) {
+#pragma unroll
+    for (int o = 0; o < 4; ++o)
+#pragma unroll
+      for (int n = 0; n < NP; ++n)
+        if (Pc::valid(pcs.slot[n])) S.op[o][pcs.slot[n]] = r[o][n];
+    if (tid < 32) S.lse2[tid] = x;
+    else if (tid < 64) S.delta[tid - 32] = x;
+  };
+
   u32x4 kf[NCH], vf[NCH];
   load_rows<D>(kf, k + urow * D * 2, k0, T - 1, lane);
   load_rows<D>(vf, v + urow * D * 2, k0, T - 1, lane);
@@ -1955,52 +2165,78 @@ __global__ __launch_bounds__(256) void soft_dkv_kernel(SoftArgs a, const uint8_t
 #pragma unroll
   for (int j = 0; j < NT; ++j) ak[j] = av[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float far_ds = 0.f;
-  for (int hq = h * a.G; hq < (h + 1) * a.G; ++hq) {
-    const int64_t hrow = ((int64_t)b * a.Hq + hq) * T;
-    const uint8_t* Qh = q + hrow * D * 2;
-    const uint8_t* Oh = dO + hrow * D * 2;
-    const uint8_t* Qt = qt + ((int64_t)b * a.Hq + hq) * npairs * 32 * D * 2;
-    const uint8_t* Ot = dOt + ((int64_t)b * a.Hq + hq) * npairs * 32 * D * 2;
-    for (int q0 = kbase; q0 < T; q0 += 32) {
-      u32x4 qa[NCH], qb[NCH], oa[NCH], ob[NCH], qtp[NT], otp[NT];
-      load_rows<D>(qa, Qh, q0, T - 1, lane);
-      load_rows<D>(qb, Qh, q0 + 16, T - 1, lane);
-      load_rows<D>(oa, Oh, q0, T - 1, lane);
-      load_rows<D>(ob, Oh, q0 + 16, T - 1, lane);
-      load_pairT<D>(qtp, Qt, q0 / 32, lane);
-      load_pairT<D>(otp, Ot, q0 / 32, lane);
-      f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = SA, PA = SA, PB = SA;
+
+  u32x4 pre[4][NP];
+  float prx = 0.f;
+  Pos cur{h * a.G, kbase};
+  gload(pre, prx, cur);
+  lds_store(st[0], pre, prx);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const Pos nx = next(cur);
+    if (s + 1 < nsteps) gload(pre, prx, nx);
+    const St& S = st[s & 1];
+    const int q0 = cur.q0;
+    u32x4 qa[NCH], qb[NCH], oa[NCH], ob[NCH];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        SA = mfma_bf16(qa[c], kf[c], SA);
-        SB = mfma_bf16(qb[c], kf[c], SB);
-        PA = mfma_bf16(oa[c], vf[c], PA);
-        PB = mfma_bf16(ob[c], vf[c], PB);
+    for (int c = 0; c < NCH; ++c) {
+      qa[c] = S.op[0][c * 64 + lane];
+      qb[c] = S.op[0][(NCH + c) * 64 + lane];
+      oa[c] = S.op[1][c * 64 + lane];
+      ob[c] = S.op[1][(NCH + c) * 64 + lane];
+    }
+    f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = SA, PA = SA, PB = SA;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      SA = mfma_bf16(qa[c], kf[c], SA);
+      SB = mfma_bf16(qb[c], kf[c], SB);
+      PA = mfma_bf16(oa[c], vf[c], PA);
+      PB = mfma_bf16(ob[c], vf[c], PB);
+    }
+    const f32x4 la = *(const f32x4*)&S.lse2[tb], lb = *(const f32x4*)&S.lse2[16 + tb];
+    const f32x4 da = *(const f32x4*)&S.delta[tb], db = *(const f32x4*)&S.delta[16 + tb];
+    float pr[8], ds[8];
+    if (q0 >= k0 + 16 + w && q0 + 32 <= T) {
+      // every query of the step is past the window of every key of the wave
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float sv = r < 4 ? SA[r] : SB[r - 4];
+        const float dp = r < 4 ? PA[r] : PB[r - 4];
+        const float l2 = r < 4 ? la[r] : lb[r - 4];
+        const float dl = r < 4 ? da[r] : db[r - 4];
+        pr[r] = exp2_fast(fmaf(sv, a.scale_log2e, kb2 - l2));
+        ds[r] = pr[r] * (dp - dl);
       }
-      float pr[8], ds[8];
+      far_ds += ((ds[0] + ds[1]) + (ds[2] + ds[3])) + ((ds[4] + ds[5]) + (ds[6] + ds[7]));
+    } else {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int qi = q0 + (r >> 2) * 16 + tb + (r & 3);
-        const int64_t row = hrow + min(qi, T - 1);
         const float badd = (qi < key || qi >= T) ? -INFINITY : (qi - key > w ? kb2 : 0.f);
         const float sv = r < 4 ? SA[r] : SB[r - 4];
         const float dp = r < 4 ? PA[r] : PB[r - 4];
-        pr[r] = exp2_fast(fmaf(sv, a.scale_log2e, badd) - lse[row] * kLog2e);
-        ds[r] = pr[r] * (dp - delta[row]);
+        const float l2 = r < 4 ? la[r] : lb[r - 4];
+        const float dl = r < 4 ? da[r] : db[r - 4];
+        pr[r] = exp2_fast(fmaf(sv, a.scale_log2e, badd) - l2);
+        ds[r] = pr[r] * (dp - dl);
         if (qi - key > w) far_ds += ds[r];
       }
-      bf16x8 PH, PL, DH, DL;
-      split_pair(pr, PH, PL);
-      split_pair(ds, DH, DL);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const bf16x8 OT = __builtin_bit_cast(bf16x8, otp[j]), QT = __builtin_bit_cast(bf16x8, qtp[j]);
-        av[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PH, av[j], 0, 0, 0);
-        av[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PL, av[j], 0, 0, 0);
-        ak[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DH, ak[j], 0, 0, 0);
-        ak[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DL, ak[j], 0, 0, 0);
-      }
     }
+    bf16x8 PH, PL, DH, DL;
+    split_pair(pr, PH, PL);
+    split_pair(ds, DH, DL);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const bf16x8 OT = __builtin_bit_cast(bf16x8, S.op[3][j * 64 + lane]);
+      const bf16x8 QT = __builtin_bit_cast(bf16x8, S.op[2][j * 64 + lane]);
+      av[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PH, av[j], 0, 0, 0);
+      av[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PL, av[j], 0, 0, 0);
+      ak[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DH, ak[j], 0, 0, 0);
+      ak[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DL, ak[j], 0, 0, 0);
+    }
+    if (s + 1 < nsteps) lds_store(st[(s + 1) & 1], pre, prx);
+    __syncthreads();
+    cur = nx;
   }
   far_ds += __shfl_xor(far_ds, 16);
   far_ds += __shfl_xor(far_ds, 32);
@@ -2376,26 +2612,45 @@ hipError_t launch_decode_chunk(const Dev& p, int dtype, int d, const void* q, co
 int chunk_max_blocks() { return kChunkMaxBlocks; }
 
 static int64_t soft_pairT_bytes(int T, int d) { return (int64_t)((T + 31) / 32) * 32 * d * 2; }
+static int64_t soft_bias_bytes(int B, int Hkv, int T) { return (int64_t)B * Hkv * ((T + 31) / 32) * 32 * 4; }
+
+int64_t soft_forward_workspace_bytes(int B, int Hq, int Hkv, int T, int d) {
+  (void)Hq;
+  return (int64_t)B * Hkv * soft_pairT_bytes(T, d) + soft_bias_bytes(B, Hkv, T);
+}
 
 int64_t soft_backward_workspace_bytes(int B, int Hq, int Hkv, int T, int d) {
-  // pairT copies of q and dO (per query head) and of k (per KV head), then delta
+  // pairT copies of q and dO (per query head) and of k (per KV head), delta, bias
   const int64_t pt = soft_pairT_bytes(T, d);
   const int64_t copies = ((int64_t)B * Hq * 2 + (int64_t)B * Hkv) * pt;
-  return copies + (int64_t)B * Hq * T * 4;
+  return copies + (int64_t)B * Hq * T * 4 + soft_bias_bytes(B, Hkv, T);
+}
+
+static hipError_t soft_bias(const SoftArgs& a, const float* logit, const float* noise, float* bias2, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.Hkv * ((a.T + 31) / 32) * 32;
+  return launch(soft_bias_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, a, logit, noise, bias2);
 }
 
 template <int D>
 static hipError_t soft_forward_t(const SoftArgs& a, const void* q, const void* k, const void* v, const float* logit,
-                                 const float* noise, float* out, float* lse, hipStream_t s) {
+                                 const float* noise, float* out, float* lse, uint8_t* ws, hipStream_t s) {
+  uint8_t* vt = ws;
+  float* bias2 = (float*)(vt + (int64_t)a.B * a.Hkv * soft_pairT_bytes(a.T, D));
+  const unsigned npairs = (unsigned)((a.T + 31) / 32);
+  hipError_t e = launch(soft_pack_kernel<D>, dim3((unsigned)(a.B * a.Hkv), npairs), dim3(256), s,
+                        (const uint16_t*)v, vt, a.T, (const float*)nullptr, (float*)nullptr);
+  if (e == hipSuccess) e = soft_bias(a, logit, noise, bias2, s);
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((a.T + kPfTile - 1) / kPfTile), (unsigned)a.Hq, (unsigned)a.B);
   return launch(soft_forward_kernel<D>, grid, dim3(64 * kWavesPerWG), s, a, (const uint8_t*)q, (const uint8_t*)k,
-                (const uint8_t*)v, logit, noise, out, lse);
+                (const uint8_t*)vt, (const float*)bias2, out, lse);
 }
 
 hipError_t launch_soft_forward(const SoftArgs& a, int d, const void* q, const void* k, const void* v,
-                               const float* logit, const float* noise, float* out, float* lse, hipStream_t s) {
-  return d == 128 ? soft_forward_t<128>(a, q, k, v, logit, noise, out, lse, s)
-                  : soft_forward_t<64>(a, q, k, v, logit, noise, out, lse, s);
+                               const float* logit, const float* noise, float* out, float* lse, void* ws,
+                               hipStream_t s) {
+  return d == 128 ? soft_forward_t<128>(a, q, k, v, logit, noise, out, lse, (uint8_t*)ws, s)
+                  : soft_forward_t<64>(a, q, k, v, logit, noise, out, lse, (uint8_t*)ws, s);
 }
 
 template <int D>
@@ -2408,6 +2663,7 @@ static hipError_t soft_backward_t(const SoftArgs& a, const void* q, const void* 
   uint8_t* ot = qt + (int64_t)a.B * a.Hq * pt;
   uint8_t* kt = ot + (int64_t)a.B * a.Hq * pt;
   float* delta = (float*)(kt + (int64_t)a.B * a.Hkv * pt);
+  float* bias2 = delta + (int64_t)a.B * a.Hq * a.T;
   const unsigned npairs = (unsigned)((a.T + 31) / 32);
   hipError_t e = launch(soft_pack_kernel<D>, dim3((unsigned)(a.B * a.Hq), npairs), dim3(256), s,
                         (const uint16_t*)q, qt, a.T, (const float*)nullptr, (float*)nullptr);
@@ -2417,14 +2673,15 @@ static hipError_t soft_backward_t(const SoftArgs& a, const void* q, const void* 
   if (e == hipSuccess)
     e = launch(soft_pack_kernel<D>, dim3((unsigned)(a.B * a.Hkv), npairs), dim3(256), s, (const uint16_t*)k, kt,
                a.T, (const float*)nullptr, (float*)nullptr);
+  if (e == hipSuccess) e = soft_bias(a, logit, noise, bias2, s);
   if (e == hipSuccess)
     e = launch(soft_dq_kernel<D>, dim3((unsigned)((a.T + kSoftQTile - 1) / kSoftQTile), (unsigned)a.Hq, (unsigned)a.B),
-               dim3(64 * kWavesPerWG), s, a, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v,
-               (const uint8_t*)kt, (const uint8_t*)dout, logit, noise, lse, (const float*)delta, dq);
+               dim3(64 * kSoftQWaves), s, a, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v,
+               (const uint8_t*)kt, (const uint8_t*)dout, (const float*)bias2, lse, (const float*)delta, dq);
   if (e == hipSuccess)
     e = launch(soft_dkv_kernel<D>, dim3((unsigned)((a.T + kSoftKTile - 1) / kSoftKTile), (unsigned)a.Hkv,
                                         (unsigned)a.B),
-               dim3(64 * kWavesPerWG), s, a, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v,
+               dim3(64 * kSoftKWaves), s, a, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v,
                (const uint8_t*)qt, (const uint8_t*)dout, (const uint8_t*)ot, logit, noise, lse, (const float*)delta,
                dk, dv, dlogit);
   return e;

@@ -507,18 +507,26 @@ int dms_cache_export(dms_cache* c, int32_t unit_begin, int32_t unit_count, int32
   return DMS_OK;
 }
 
+size_t dms_soft_attention_forward_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d) {
+  if (!soft_shapes_ok(B, Hq, Hkv, T, d)) return 0;
+  return (size_t)dms::soft_forward_workspace_bytes(B, Hq, Hkv, T, d);
+}
+
 int dms_soft_attention_forward(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d, int32_t window,
                                float gamma, float tau, float scale, const void* d_q, const void* d_k,
                                const void* d_v, const float* d_logit, const float* d_noise, float* d_out,
-                               float* d_lse, void* stream) {
-  if (!d_q || !d_k || !d_v || !d_logit || !d_noise || !d_out || !d_lse) return DMS_ERR_ARG;
+                               float* d_lse, void* d_workspace, size_t workspace_bytes, void* stream) {
+  if (!d_q || !d_k || !d_v || !d_logit || !d_noise || !d_out || !d_lse || !d_workspace) return DMS_ERR_ARG;
   dms::SoftArgs a;
   int st = soft_args(B, Hq, Hkv, T, d, window, gamma, tau, scale, &a);
   if (st != DMS_OK) return st;
+  if ((uintptr_t)d_workspace % kAlign != 0 ||
+      workspace_bytes < (size_t)dms::soft_forward_workspace_bytes(B, Hq, Hkv, T, d))
+    return DMS_ERR_WORKSPACE;
   int dev;
   st = current_gfx950_device(&dev);
   if (st != DMS_OK) return st;
-  return hip_status(dms::launch_soft_forward(a, d, d_q, d_k, d_v, d_logit, d_noise, d_out, d_lse,
+  return hip_status(dms::launch_soft_forward(a, d, d_q, d_k, d_v, d_logit, d_noise, d_out, d_lse, d_workspace,
                                              (hipStream_t)stream));
 }
 

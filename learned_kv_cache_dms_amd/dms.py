@@ -104,7 +104,8 @@ def _load():
         "dms_cache_export": (ctypes.c_int, [vp, i32, i32, P(i32), P(i32), P(i32), vp]),
         "dms_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "dms_soft_attention_forward": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, ctypes.c_float,
-                                                      ctypes.c_float, ctypes.c_float] + [vp] * 8),
+                                                      ctypes.c_float, ctypes.c_float] + [vp] * 8 + [sz, vp]),
+        "dms_soft_attention_forward_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "dms_soft_attention_backward_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "dms_soft_attention_backward": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                                        ctypes.c_float, ctypes.c_float] + [vp] * 13 + [sz, vp]),
@@ -215,11 +216,15 @@ def dms_cache_export(h: int, unit_begin: int, unit_count: int, slot_pos: Optiona
            "dms_cache_export")
 
 
+def dms_soft_attention_forward_workspace_bytes(B, Hq, Hkv, T, d) -> int:
+    return int(lib.dms_soft_attention_forward_workspace_bytes(int(B), int(Hq), int(Hkv), int(T), int(d)))
+
+
 def dms_soft_attention_forward(B, Hq, Hkv, T, d, window, gamma, tau, scale, d_q, d_k, d_v, d_logit, d_noise,
-                               d_out, d_lse, stream: int = 0):
+                               d_out, d_lse, d_workspace, workspace_bytes, stream: int = 0):
     _check(lib.dms_soft_attention_forward(int(B), int(Hq), int(Hkv), int(T), int(d), int(window), float(gamma),
                                           float(tau), float(scale), d_q, d_k, d_v, d_logit, d_noise, d_out, d_lse,
-                                          stream), "dms_soft_attention_forward")
+                                          d_workspace, int(workspace_bytes), stream), "dms_soft_attention_forward")
 
 
 def dms_soft_attention_backward_workspace_bytes(B, Hq, Hkv, T, d) -> int:
@@ -248,18 +253,23 @@ def _soft_check(q, k, v, logit, noise):
     return B, Hq, Hkv, T, d
 
 
-def soft_attention_forward(q, k, v, logit, noise, window, gamma=0.0, tau=1.0, scale=0.0, out=None, lse=None):
+def soft_attention_forward(q, k, v, logit, noise, window, gamma=0.0, tau=1.0, scale=0.0, out=None, lse=None,
+                           workspace=None):
     """Relaxed DMS attention forward (dms_soft_attention_forward) on torch
-    tensors: returns (out, lse), fp32, allocated here unless given."""
+    tensors: returns (out, lse), fp32; outputs and workspace are allocated
+    here unless given."""
     import torch
     B, Hq, Hkv, T, d = _soft_check(q, k, v, logit, noise)
     if out is None:
         out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(dms_soft_attention_forward_workspace_bytes(B, Hq, Hkv, T, d), dtype=torch.uint8,
+                                device=q.device)
     dms_soft_attention_forward(B, Hq, Hkv, T, d, window, gamma, tau, scale, q.data_ptr(), k.data_ptr(),
                                v.data_ptr(), logit.data_ptr(), noise.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                               torch.cuda.current_stream().cuda_stream)
+                               workspace.data_ptr(), workspace.numel(), torch.cuda.current_stream().cuda_stream)
     return out, lse
 
 

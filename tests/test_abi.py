@@ -102,19 +102,30 @@ def test_soft_attention_validates_before_touching_the_device():
     from learned_kv_cache_dms_amd import dms
     L = dms.lib
     ok = (1, 4, 2, 100, 128, 8, 0.0, 1.0, 0.0)
-    ptrs = [0x1000] * 8
-    assert L.dms_soft_attention_forward(*ok[:7], 1.0, 0.0, *([None] + ptrs[1:])) == dms.DMS_ERR_ARG
+    fneed = dms.dms_soft_attention_forward_workspace_bytes(1, 4, 2, 100, 128)
+    # v in the transposed operand layout (rows padded to 32) per KV head, then the keys' bias
+    assert fneed == 2 * 128 * 128 * 2 + 2 * 128 * 4
+    data = [0x1000] * 7
+
+    def fwd(*shape_and_params, ptrs=data, ws=0x1000, nbytes=fneed):
+        return L.dms_soft_attention_forward(*shape_and_params, *ptrs, ws, nbytes, None)
+
+    assert fwd(*ok, ptrs=[None] + data[1:]) == dms.DMS_ERR_ARG
+    assert fwd(*ok, ws=None) == dms.DMS_ERR_ARG
+    assert fwd(*ok, ws=0x1001) == dms.DMS_ERR_WORKSPACE
+    assert fwd(*ok, nbytes=fneed - 1) == dms.DMS_ERR_WORKSPACE
     for bad in [(1, 3, 2, 100, 128), (1, 4, 2, 0, 128), (1, 4, 2, 100, 96), (0, 4, 2, 100, 128),
                 (1, 4, 2, (1 << 20) + 1, 128)]:
-        assert L.dms_soft_attention_forward(*bad, 8, 0.0, 1.0, 0.0, *ptrs) == dms.DMS_ERR_ARG, bad
+        assert fwd(*bad, 8, 0.0, 1.0, 0.0) == dms.DMS_ERR_ARG, bad
+        assert dms.dms_soft_attention_forward_workspace_bytes(*bad) == 0
         assert dms.dms_soft_attention_backward_workspace_bytes(*bad) == 0
     for tau in (0.0, -1.0, float("nan"), float("inf")):
-        assert L.dms_soft_attention_forward(1, 4, 2, 100, 128, 8, 0.0, tau, 0.0, *ptrs) == dms.DMS_ERR_ARG
-    assert L.dms_soft_attention_forward(1, 4, 2, 100, 128, -1, 0.0, 1.0, 0.0, *ptrs) == dms.DMS_ERR_ARG
-    assert L.dms_soft_attention_forward(1, 4, 2, 100, 128, 8, float("nan"), 1.0, 0.0, *ptrs) == dms.DMS_ERR_ARG
+        assert fwd(1, 4, 2, 100, 128, 8, 0.0, tau, 0.0) == dms.DMS_ERR_ARG
+    assert fwd(1, 4, 2, 100, 128, -1, 0.0, 1.0, 0.0) == dms.DMS_ERR_ARG
+    assert fwd(1, 4, 2, 100, 128, 8, float("nan"), 1.0, 0.0) == dms.DMS_ERR_ARG
     need = dms.dms_soft_attention_backward_workspace_bytes(1, 4, 2, 100, 128)
-    # q and dO copies per query head, k per KV head (rows padded to 32), then delta
-    assert need == (4 * 2 + 2) * 128 * 128 * 2 + 4 * 100 * 4
+    # q and dO copies per query head, k per KV head, then delta and the keys' bias
+    assert need == (4 * 2 + 2) * 128 * 128 * 2 + 4 * 100 * 4 + 2 * 128 * 4
     bptrs = [0x1000] * 12
     assert L.dms_soft_attention_backward(*ok, *bptrs, 0x1001, need, None) == dms.DMS_ERR_WORKSPACE
     assert L.dms_soft_attention_backward(*ok, *bptrs, 0x1000, need - 1, None) == dms.DMS_ERR_WORKSPACE

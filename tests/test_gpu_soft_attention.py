@@ -169,12 +169,20 @@ def test_soft_attention_errors():
     o = torch.zeros((1, 2, 8, 64), dtype=torch.float32, device="cuda")
     l = torch.zeros((1, 2, 8), dtype=torch.float32, device="cuda")
     p = lambda t: t.data_ptr()
+    fneed = dms.dms_soft_attention_forward_workspace_bytes(1, 2, 1, 8, 64)
+    fws = torch.empty(fneed, dtype=torch.uint8, device="cuda")
     with pytest.raises(dms.DmsError) as e:
-        dms.dms_soft_attention_forward(1, 2, 1, 8, 64, 4, 0.0, 0.0, 0.0, p(x), p(x), p(x), p(f), p(f), p(o), p(l))
+        dms.dms_soft_attention_forward(1, 2, 1, 8, 64, 4, 0.0, 0.0, 0.0, p(x), p(x), p(x), p(f), p(f), p(o), p(l),
+                                       p(fws), fneed)
     assert e.value.status == dms.DMS_ERR_ARG
     with pytest.raises(dms.DmsError) as e:
-        dms.dms_soft_attention_forward(1, 2, 1, 8, 96, 4, 0.0, 1.0, 0.0, p(x), p(x), p(x), p(f), p(f), p(o), p(l))
+        dms.dms_soft_attention_forward(1, 2, 1, 8, 96, 4, 0.0, 1.0, 0.0, p(x), p(x), p(x), p(f), p(f), p(o), p(l),
+                                       p(fws), fneed)
     assert e.value.status == dms.DMS_ERR_ARG
+    with pytest.raises(dms.DmsError) as e:
+        dms.dms_soft_attention_forward(1, 2, 1, 8, 64, 4, 0.0, 1.0, 0.0, p(x), p(x), p(x), p(f), p(f), p(o), p(l),
+                                       p(fws), fneed - 1)
+    assert e.value.status == dms.DMS_ERR_WORKSPACE
     need = dms.dms_soft_attention_backward_workspace_bytes(1, 2, 1, 8, 64)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     with pytest.raises(dms.DmsError) as e:
