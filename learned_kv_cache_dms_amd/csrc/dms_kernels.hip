@@ -1885,7 +1885,11 @@ constexpr int kSoftQWaves = DMS_SOFT_DQ_WG;
 constexpr int kSoftKWaves = DMS_SOFT_DKV_WG;
 constexpr int kSoftQCols = DMS_SOFT_QCOLS;               // query tiles of 16 per wave (dQ)
 constexpr int kSoftQTile = 16 * kSoftQCols * kSoftQWaves;  // queries per work-group (dQ)
-constexpr int kSoftKTile = 16 * kSoftKWaves;               // keys per work-group (dK, dV)
+#ifndef DMS_SOFT_DKV_KT
+#define DMS_SOFT_DKV_KT 1
+#endif
+constexpr int kSoftKT = DMS_SOFT_DKV_KT;                    // key tiles of 16 per wave (dK, dV)
+constexpr int kSoftKTile = 16 * kSoftKT * kSoftKWaves;      // keys per work-group (dK, dV)
 
 // Backward, query-stationary: dq = scale * dS k with dS = P (dP - delta), P
 // recomputed from the forward's lse, dP = dO v^T.  Each wave holds
@@ -2105,8 +2109,8 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
   const int T = a.T, w = a.w;
   const int nkt = (T + kSoftKTile - 1) / kSoftKTile;
   const int kbase = (nkt - 1 - (int)blockIdx.x) * kSoftKTile;
-  const int k0 = kbase + 16 * wave;
-  const int key = k0 + (lane & 15);
+  constexpr int KT = kSoftKT;
+  const int k0 = kbase + 16 * KT * wave;  // the wave's first key
   const int64_t urow = ((int64_t)b * a.Hkv + h) * T;
   const int npairs = (T + 31) / 32;
   const int tb = 4 * (lane >> 4);
@@ -2156,15 +2160,21 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
     else if (tid < 64) S.delta[tid - 32] = x;
   };
 
-  u32x4 kf[NCH], vf[NCH];
-  load_rows<D>(kf, k + urow * D * 2, k0, T - 1, lane);
-  load_rows<D>(vf, v + urow * D * 2, k0, T - 1, lane);
-  const float x = soft_x(a, logit, noise, urow, min(key, T - 1));
-  const float kb2 = soft_bias2(x);
-  f32x4 ak[NT], av[NT];
+  u32x4 kf[KT][NCH], vf[KT][NCH];
+  int key[KT];
+  float x[KT], kb2[KT], far_ds[KT];
+  f32x4 ak[KT][NT], av[KT][NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) ak[j] = av[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float far_ds = 0.f;
+  for (int kt = 0; kt < KT; ++kt) {
+    key[kt] = k0 + 16 * kt + (lane & 15);
+    load_rows<D>(kf[kt], k + urow * D * 2, k0 + 16 * kt, T - 1, lane);
+    load_rows<D>(vf[kt], v + urow * D * 2, k0 + 16 * kt, T - 1, lane);
+    x[kt] = soft_x(a, logit, noise, urow, min(key[kt], T - 1));
+    kb2[kt] = soft_bias2(x[kt]);
+    far_ds[kt] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) ak[kt][j] = av[kt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   u32x4 pre[4][NP];
   float prx = 0.f;
@@ -2185,70 +2195,79 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
       oa[c] = S.op[1][c * 64 + lane];
       ob[c] = S.op[1][(NCH + c) * 64 + lane];
     }
-    f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = SA, PA = SA, PB = SA;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      SA = mfma_bf16(qa[c], kf[c], SA);
-      SB = mfma_bf16(qb[c], kf[c], SB);
-      PA = mfma_bf16(oa[c], vf[c], PA);
-      PB = mfma_bf16(ob[c], vf[c], PB);
-    }
     const f32x4 la = *(const f32x4*)&S.lse2[tb], lb = *(const f32x4*)&S.lse2[16 + tb];
     const f32x4 da = *(const f32x4*)&S.delta[tb], db = *(const f32x4*)&S.delta[16 + tb];
-    float pr[8], ds[8];
-    if (q0 >= k0 + 16 + w && q0 + 32 <= T) {
-      // every query of the step is past the window of every key of the wave
+    bf16x8 PH[KT], PL[KT], DH[KT], DL[KT];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float sv = r < 4 ? SA[r] : SB[r - 4];
-        const float dp = r < 4 ? PA[r] : PB[r - 4];
-        const float l2 = r < 4 ? la[r] : lb[r - 4];
-        const float dl = r < 4 ? da[r] : db[r - 4];
-        pr[r] = exp2_fast(fmaf(sv, a.scale_log2e, kb2 - l2));
-        ds[r] = pr[r] * (dp - dl);
-      }
-      far_ds += ((ds[0] + ds[1]) + (ds[2] + ds[3])) + ((ds[4] + ds[5]) + (ds[6] + ds[7]));
-    } else {
+    for (int kt = 0; kt < KT; ++kt) {
+      f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = SA, PA = SA, PB = SA;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int qi = q0 + (r >> 2) * 16 + tb + (r & 3);
-        const float badd = (qi < key || qi >= T) ? -INFINITY : (qi - key > w ? kb2 : 0.f);
-        const float sv = r < 4 ? SA[r] : SB[r - 4];
-        const float dp = r < 4 ? PA[r] : PB[r - 4];
-        const float l2 = r < 4 ? la[r] : lb[r - 4];
-        const float dl = r < 4 ? da[r] : db[r - 4];
-        pr[r] = exp2_fast(fmaf(sv, a.scale_log2e, badd) - l2);
-        ds[r] = pr[r] * (dp - dl);
-        if (qi - key > w) far_ds += ds[r];
+      for (int c = 0; c < NCH; ++c) {
+        SA = mfma_bf16(qa[c], kf[kt][c], SA);
+        SB = mfma_bf16(qb[c], kf[kt][c], SB);
+        PA = mfma_bf16(oa[c], vf[kt][c], PA);
+        PB = mfma_bf16(ob[c], vf[kt][c], PB);
       }
+      float pr[8], ds[8];
+      if (q0 >= k0 + 16 * kt + 16 + w && q0 + 32 <= T) {
+        // every query of the step is past the window of every key of the tile
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float sv = r < 4 ? SA[r] : SB[r - 4];
+          const float dp = r < 4 ? PA[r] : PB[r - 4];
+          const float l2 = r < 4 ? la[r] : lb[r - 4];
+          const float dl = r < 4 ? da[r] : db[r - 4];
+          pr[r] = exp2_fast(fmaf(sv, a.scale_log2e, kb2[kt] - l2));
+          ds[r] = pr[r] * (dp - dl);
+        }
+        far_ds[kt] += ((ds[0] + ds[1]) + (ds[2] + ds[3])) + ((ds[4] + ds[5]) + (ds[6] + ds[7]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int qi = q0 + (r >> 2) * 16 + tb + (r & 3);
+          const float badd = (qi < key[kt] || qi >= T) ? -INFINITY : (qi - key[kt] > w ? kb2[kt] : 0.f);
+          const float sv = r < 4 ? SA[r] : SB[r - 4];
+          const float dp = r < 4 ? PA[r] : PB[r - 4];
+          const float l2 = r < 4 ? la[r] : lb[r - 4];
+          const float dl = r < 4 ? da[r] : db[r - 4];
+          pr[r] = exp2_fast(fmaf(sv, a.scale_log2e, badd) - l2);
+          ds[r] = pr[r] * (dp - dl);
+          if (qi - key[kt] > w) far_ds[kt] += ds[r];
+        }
+      }
+      split_pair(pr, PH[kt], PL[kt]);
+      split_pair(ds, DH[kt], DL[kt]);
     }
-    bf16x8 PH, PL, DH, DL;
-    split_pair(pr, PH, PL);
-    split_pair(ds, DH, DL);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const bf16x8 OT = __builtin_bit_cast(bf16x8, S.op[3][j * 64 + lane]);
       const bf16x8 QT = __builtin_bit_cast(bf16x8, S.op[2][j * 64 + lane]);
-      av[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PH, av[j], 0, 0, 0);
-      av[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PL, av[j], 0, 0, 0);
-      ak[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DH, ak[j], 0, 0, 0);
-      ak[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DL, ak[j], 0, 0, 0);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        av[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PH[kt], av[kt][j], 0, 0, 0);
+        av[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PL[kt], av[kt][j], 0, 0, 0);
+        ak[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DH[kt], ak[kt][j], 0, 0, 0);
+        ak[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DL[kt], ak[kt][j], 0, 0, 0);
+      }
     }
     if (s + 1 < nsteps) lds_store(st[(s + 1) & 1], pre, prx);
     __syncthreads();
     cur = nx;
   }
-  far_ds += __shfl_xor(far_ds, 16);
-  far_ds += __shfl_xor(far_ds, 32);
-  if (key >= T) return;
-  float* krow = dk + (urow + key) * D + 4 * (lane >> 4);
-  float* vrow = dv + (urow + key) * D + 4 * (lane >> 4);
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    *(f32x4*)(krow + 16 * j) = ak[j] * a.scale;
-    *(f32x4*)(vrow + 16 * j) = av[j];
+  for (int kt = 0; kt < KT; ++kt) {
+    float fd = far_ds[kt] + __shfl_xor(far_ds[kt], 16);
+    fd += __shfl_xor(fd, 32);
+    if (key[kt] >= T) continue;
+    float* krow = dk + (urow + key[kt]) * D + 4 * (lane >> 4);
+    float* vrow = dv + (urow + key[kt]) * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      *(f32x4*)(krow + 16 * j) = ak[kt][j] * a.scale;
+      *(f32x4*)(vrow + 16 * j) = av[kt][j];
+    }
+    if (lane < 16) dlogit[urow + key[kt]] = -sigmoid_f(x[kt]) * a.inv_tau * fd;
   }
-  if (lane < 16) dlogit[urow + key] = -sigmoid_f(x) * a.inv_tau * far_ds;
 }
 
 // ---------------------------------------------------------------------------
