@@ -2146,8 +2146,10 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
       r[3][n] = *(const u32x4*)(Ot + pcs.slot[n] * 16);
     }
     if (tid < 64) {  // lse (0..31) and delta (32..63) of the step's rows
+      // (scaled only when stored: arithmetic on a just-loaded value would
+      // make the wave wait here for every load of the step)
       const int64_t row = head * T + min(p.q0 + (tid & 31), T - 1);
-      x = tid < 32 ? lse[row] * kLog2e : delta[row];
+      x = (tid < 32 ? lse : delta)[row];
     }
   };
   auto lds_store = [&](St& S, const u32x4 (&r)[4][NP], float x) {
@@ -2156,7 +2158,7 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
 #pragma unroll
       for (int n = 0; n < NP; ++n)
         if (Pc::valid(pcs.slot[n])) S.op[o][pcs.slot[n]] = r[o][n];
-    if (tid < 32) S.lse2[tid] = x;
+    if (tid < 32) S.lse2[tid] = x * kLog2e;
     else if (tid < 64) S.delta[tid - 32] = x;
   };
 
