@@ -113,6 +113,24 @@ __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+#ifndef DMS_PERMLANE_MAX
+#define DMS_PERMLANE_MAX 1
+#endif
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups that hold
+// one MFMA column's rows).  The gfx950 permlane swaps exchange those lane
+// groups within the VALU; a shuffle would go through the LDS crossbar.
+__device__ __forceinline__ float max_over_groups(float v) {
+#if DMS_PERMLANE_MAX
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+#else
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+#endif
+}
+
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
   bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -891,9 +909,8 @@ __device__ __forceinline__ void attend_pair(const PairFrag<ES, D>& f, const u32x
       s[r] = ((ma >> (tb + r)) & 1u) ? SA[r] : -INFINITY;
       s[4 + r] = ((mb >> (tb + r)) & 1u) ? SB[r] : -INFINITY;
     }
-    float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float bm = max_over_groups(
+        fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))));
     const float mn = fmaxf(a.m, bm * sl2e);
     const float mref = (mn == -INFINITY) ? 0.f : mn;
     float pr[8];
@@ -1614,9 +1631,8 @@ __device__ __forceinline__ void attend_pair_biased(const PairFrag<2, D>& f, cons
     s[r] = fmaf(SA[r], sl2e, badd[r]);
     s[4 + r] = fmaf(SB[r], sl2e, badd[4 + r]);
   }
-  float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float bm = max_over_groups(
+      fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))));
   const float mn = fmaxf(a.m, bm);
   const float mref = (mn == -INFINITY) ? 0.f : mn;
   float pr[8];
