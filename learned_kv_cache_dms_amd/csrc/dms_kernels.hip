@@ -884,71 +884,88 @@ __device__ __forceinline__ void make_pair(PairFrag<ES, D>& f, const Frag<ES, D>&
   }
 }
 
+template <int D>
+__device__ __forceinline__ void score_pair(const PairFrag<2, D>& f, const u32x4 (&qf)[Geo<2, D>::kChunks], f32x4& SA,
+                                           f32x4& SB) {
+  using G = Geo<2, D>;
+  SA = f32x4{0.f, 0.f, 0.f, 0.f};
+  SB = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) {
+    SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.ka[c]),
+                                                  __builtin_bit_cast(bf16x8, qf[c]), SA, 0, 0, 0);
+    SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.kb[c]),
+                                                  __builtin_bit_cast(bf16x8, qf[c]), SB, 0, 0, 0);
+  }
+}
+
+// Softmax step and P.V of a pair of blocks from its raw scores (score_pair):
+// masks ma, mb select the live keys (bit i = key i of the block).
+template <int D>
+__device__ __forceinline__ void softmax_pv_masked(const PairFrag<2, D>& f, const f32x4& SA, const f32x4& SB,
+                                                  uint32_t ma, uint32_t mb, int lane, float sl2e, Acc<D>& a) {
+  using G = Geo<2, D>;
+  const int tb = 4 * (lane >> 4);
+  // Raw scores, masked to -inf; the scale (> 0) is applied to the max and
+  // inside the exponent's fma, which keeps the max exact.
+  float s[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s[r] = ((ma >> (tb + r)) & 1u) ? SA[r] : -INFINITY;
+    s[4 + r] = ((mb >> (tb + r)) & 1u) ? SB[r] : -INFINITY;
+  }
+  const float bm = max_over_groups(
+      fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))));
+  const float mn = fmaxf(a.m, bm * sl2e);
+  const float mref = (mn == -INFINITY) ? 0.f : mn;
+  float pr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) pr[r] = exp2_fast(fmaf(s[r], sl2e, -mref));
+  const float psum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+#if DMS_PF_LAZY
+  // Rescale only when some column's running max moved (after the first
+  // blocks it rarely does).  An unmoved max gives alpha = 1 exactly; a
+  // column with no key yet has o = l = 0, which any alpha leaves at 0.
+  if (__builtin_amdgcn_ballot_w64(mn != a.m) != 0) {
+    const float alpha = exp2_fast(a.m - mref);
+    a.l *= alpha;
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
+  }
+  a.l += psum;
+#else
+  const float alpha = exp2_fast(a.m - mref);
+  a.l = a.l * alpha + psum;
+#pragma unroll
+  for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
+#endif
+  a.m = mn;
+  unsigned hi[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
+    lo[i] = pack_bf16x2(pr[2 * i] - bf16_lo_to_f32(hi[i]), pr[2 * i + 1] - bf16_hi_to_f32(hi[i]));
+  }
+  const u32x4 hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
+  const bf16x8 PH = __builtin_bit_cast(bf16x8, hv), PL = __builtin_bit_cast(bf16x8, lv);
+#pragma unroll
+  for (int j = 0; j < G::kTiles; ++j) {
+    const bf16x8 A = __builtin_bit_cast(bf16x8, f.v[j]);
+    a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PH, a.o[j], 0, 0, 0);
+    a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PL, a.o[j], 0, 0, 0);
+  }
+}
+
 template <int ES, int D>
 __device__ __forceinline__ void attend_pair(const PairFrag<ES, D>& f, const u32x4 (&qf)[Geo<ES, D>::kChunks],
                                             uint32_t ma, uint32_t mb, int lane, float sl2e, Acc<D>& a) {
-  using G = Geo<ES, D>;
   if constexpr (ES != 2) {
     attend_block<ES, D>(f.a, qf, ma, lane, sl2e, a);
     attend_block<ES, D>(f.b, qf, mb, lane, sl2e, a);
   } else {
-    f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < G::kChunks; ++c) {
-      SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.ka[c]),
-                                                    __builtin_bit_cast(bf16x8, qf[c]), SA, 0, 0, 0);
-      SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.kb[c]),
-                                                    __builtin_bit_cast(bf16x8, qf[c]), SB, 0, 0, 0);
-    }
-    const int tb = 4 * (lane >> 4);
-    // Raw scores, masked to -inf; the scale (> 0) is applied to the max and
-    // inside the exponent's fma, which keeps the max exact.
-    float s[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s[r] = ((ma >> (tb + r)) & 1u) ? SA[r] : -INFINITY;
-      s[4 + r] = ((mb >> (tb + r)) & 1u) ? SB[r] : -INFINITY;
-    }
-    const float bm = max_over_groups(
-        fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))));
-    const float mn = fmaxf(a.m, bm * sl2e);
-    const float mref = (mn == -INFINITY) ? 0.f : mn;
-    float pr[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) pr[r] = exp2_fast(fmaf(s[r], sl2e, -mref));
-    const float psum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-#if DMS_PF_LAZY
-    // Rescale only when some column's running max moved (after the first
-    // blocks it rarely does).  An unmoved max gives alpha = 1 exactly; a
-    // column with no key yet has o = l = 0, which any alpha leaves at 0.
-    if (__builtin_amdgcn_ballot_w64(mn != a.m) != 0) {
-      const float alpha = exp2_fast(a.m - mref);
-      a.l *= alpha;
-#pragma unroll
-      for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
-    }
-    a.l += psum;
-#else
-    const float alpha = exp2_fast(a.m - mref);
-    a.l = a.l * alpha + psum;
-#pragma unroll
-    for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
-#endif
-    a.m = mn;
-    unsigned hi[4], lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hi[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
-      lo[i] = pack_bf16x2(pr[2 * i] - bf16_lo_to_f32(hi[i]), pr[2 * i + 1] - bf16_hi_to_f32(hi[i]));
-    }
-    const u32x4 hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
-    const bf16x8 PH = __builtin_bit_cast(bf16x8, hv), PL = __builtin_bit_cast(bf16x8, lv);
-#pragma unroll
-    for (int j = 0; j < G::kTiles; ++j) {
-      const bf16x8 A = __builtin_bit_cast(bf16x8, f.v[j]);
-      a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PH, a.o[j], 0, 0, 0);
-      a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PL, a.o[j], 0, 0, 0);
-    }
+    f32x4 SA, SB;
+    score_pair<D>(f, qf, SA, SB);
+    softmax_pv_masked<D>(f, SA, SB, ma, mb, lane, sl2e, a);
   }
 }
 
@@ -1520,8 +1537,19 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
     };
     auto compute = [&](const PairFrag<ES, D>& f, int i) {
       const uint32_t mb = 2 * i + 1 < nfull ? 0xffffu : 0u;
+      if constexpr (ES == 2) {
+        // column t + 1's score products issued before column t's softmax
+        f32x4 SA[2], SB[2];
+        score_pair<D>(f, qf[0], SA[0], SB[0]);
 #pragma unroll
-      for (int t = 0; t < kPfCols; ++t) attend_pair<ES, D>(f, qf[t], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
+        for (int t = 0; t < kPfCols; ++t) {
+          if (t + 1 < kPfCols) score_pair<D>(f, qf[t + 1], SA[(t + 1) & 1], SB[(t + 1) & 1]);
+          softmax_pv_masked<D>(f, SA[t & 1], SB[t & 1], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < kPfCols; ++t) attend_pair<ES, D>(f, qf[t], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
+      }
     };
     PairFrag<ES, D> f0, f1;
     fetch(f0, 0);
@@ -1613,18 +1641,14 @@ __device__ __forceinline__ float soft_x(const SoftArgs& a, const float* __restri
 // attend_pair (bf16) with an additive score per key and column, in the exp2
 // domain: badd[0..3] for this lane's keys of block A, badd[4..7] of block B
 // (-inf for keys the column may not see).
+
+// The softmax step and P.V of attend_pair_biased from the pair's scores
+// (score_pair), so that the next column's score products can be issued
+// ahead of this column's softmax.
 template <int D>
-__device__ __forceinline__ void attend_pair_biased(const PairFrag<2, D>& f, const u32x4 (&qf)[Geo<2, D>::kChunks],
-                                                   const float (&badd)[8], float sl2e, Acc<D>& a) {
+__device__ __forceinline__ void softmax_pv_biased(const PairFrag<2, D>& f, const f32x4& SA, const f32x4& SB,
+                                                  const float (&badd)[8], float sl2e, Acc<D>& a) {
   using G = Geo<2, D>;
-  f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < G::kChunks; ++c) {
-    SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.ka[c]),
-                                                  __builtin_bit_cast(bf16x8, qf[c]), SA, 0, 0, 0);
-    SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.kb[c]),
-                                                  __builtin_bit_cast(bf16x8, qf[c]), SB, 0, 0, 0);
-  }
   float s[8];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -1661,6 +1685,14 @@ __device__ __forceinline__ void attend_pair_biased(const PairFrag<2, D>& f, cons
     a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PH, a.o[j], 0, 0, 0);
     a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PL, a.o[j], 0, 0, 0);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void attend_pair_biased(const PairFrag<2, D>& f, const u32x4 (&qf)[Geo<2, D>::kChunks],
+                                                   const float (&badd)[8], float sl2e, Acc<D>& a) {
+  f32x4 SA, SB;
+  score_pair<D>(f, qf, SA, SB);
+  softmax_pv_biased<D>(f, SA, SB, badd, sl2e, a);
 }
 
 // Forward: out = softmax(scale q k^T + bias) v and lse (natural log of each
@@ -1843,8 +1875,16 @@ __global__ __launch_bounds__(256) void soft_forward_kernel(SoftArgs a, const uin
     if (32 * i + 31 + w < cw0) {
       // every key of the pair is past the window of every query of the wave
       const float badd[8] = {x.ba[0], x.ba[1], x.ba[2], x.ba[3], x.bb[0], x.bb[1], x.bb[2], x.bb[3]};
+      // column t + 1's score products are issued before column t's softmax,
+      // so they run while its VALU work does (each column's lazy-rescale
+      // test is a branch the scheduler does not move work across)
+      f32x4 SA[2], SB[2];
+      score_pair<D>(x.f, qf[0], SA[0], SB[0]);
 #pragma unroll
-      for (int t = 0; t < kPfCols; ++t) attend_pair_biased<D>(x.f, qf[t], badd, a.scale_log2e, acc[t]);
+      for (int t = 0; t < kPfCols; ++t) {
+        if (t + 1 < kPfCols) score_pair<D>(x.f, qf[t + 1], SA[(t + 1) & 1], SB[(t + 1) & 1]);
+        softmax_pv_biased<D>(x.f, SA[t & 1], SB[t & 1], badd, a.scale_log2e, acc[t]);
+      }
       return;
     }
 #pragma unroll
