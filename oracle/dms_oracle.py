@@ -266,6 +266,20 @@ def soft_bias(x: np.ndarray) -> np.ndarray:
     return -np.logaddexp(0.0, x)
 
 
+def soft_mask(bias: np.ndarray, w: int):
+    """The relaxed mask of one (sequence, KV head) over T positions.
+
+    Returns (add, far): add[q, i] is -inf for i > q (causal), 0 for
+    q - w <= i <= q (the window) and bias[i] for i < q - w; far[q, i] marks
+    the keys that carry their bias (q - i > w, i <= q)."""
+    T = len(bias)
+    pos = np.arange(T)
+    causal = pos[None, :] <= pos[:, None]                # [q, i]
+    far = ((pos[:, None] - pos[None, :]) > w) & causal
+    add = np.where(causal, np.where(far, np.asarray(bias, np.float64)[None, :], 0.0), -np.inf)
+    return add, far
+
+
 def soft_attention(Q, K, V, logit, noise, w: int, gamma: float, tau: float,
                    scale: Optional[float] = None) -> Dict:
     """Causal attention of every position with the relaxed mask.
@@ -281,13 +295,9 @@ def soft_attention(Q, K, V, logit, noise, w: int, gamma: float, tau: float,
         scale = default_scale(d)
     out = np.zeros((B, Hq, T, d))
     lse = np.zeros((B, Hq, T))
-    pos = np.arange(T)
-    far = (pos[:, None] - pos[None, :]) > w            # [q, i]
-    causal = pos[None, :] <= pos[:, None]
     for b in range(B):
         for h in range(Hkv):
-            bias = soft_bias(soft_decision_arg(logit[b, h], noise[b, h], gamma, tau))   # [T]
-            add = np.where(causal, np.where(far, bias[None, :], 0.0), -np.inf)
+            add, _ = soft_mask(soft_bias(soft_decision_arg(logit[b, h], noise[b, h], gamma, tau)), w)
             for hq in range(h * G, (h + 1) * G):
                 s = scale * (np.asarray(Q[b, hq], np.float64) @ np.asarray(K[b, h], np.float64).T) + add
                 m = np.max(s, axis=1, keepdims=True)
@@ -315,14 +325,10 @@ def soft_attention_grads(Q, K, V, logit, noise, dO, w: int, gamma: float, tau: f
     dK = np.zeros((B, Hkv, T, d))
     dV = np.zeros((B, Hkv, T, d))
     dlogit = np.zeros((B, Hkv, T))
-    pos = np.arange(T)
-    far = (pos[:, None] - pos[None, :]) > w
-    causal = pos[None, :] <= pos[:, None]
     for b in range(B):
         for h in range(Hkv):
             x = soft_decision_arg(logit[b, h], noise[b, h], gamma, tau)
-            bias = soft_bias(x)
-            add = np.where(causal, np.where(far, bias[None, :], 0.0), -np.inf)
+            add, far = soft_mask(soft_bias(x), w)
             Kh = np.asarray(K[b, h], np.float64)
             Vh = np.asarray(V[b, h], np.float64)
             for hq in range(h * G, (h + 1) * G):
@@ -337,7 +343,7 @@ def soft_attention_grads(Q, K, V, logit, noise, dO, w: int, gamma: float, tau: f
                 dQ[b, hq] = scale * (dS @ Kh)
                 dK[b, h] += scale * (dS.T @ Qh)
                 dV[b, h] += P.T @ dOh
-                dlogit[b, h] += np.sum(np.where(far & causal, dS, 0.0), axis=0)
+                dlogit[b, h] += np.sum(np.where(far, dS, 0.0), axis=0)
             sig = 1.0 / (1.0 + np.exp(-x))
             dlogit[b, h] *= -sig / tau
     return {"dq": dQ, "dk": dK, "dv": dV, "dlogit": dlogit}

@@ -142,6 +142,25 @@ def _soft_grads_dlogit_sign(Q, K, V, logit, noise, dO, w, gamma, tau, scale=None
     return g
 
 
+def _soft_mask_window_ge(bias, w):
+    """The bias already applies at q - i == w (the window one short)."""
+    T = len(bias)
+    pos = np.arange(T)
+    causal = pos[None, :] <= pos[:, None]
+    far = ((pos[:, None] - pos[None, :]) >= w) & causal
+    return np.where(causal, np.where(far, np.asarray(bias, float)[None, :], 0.0), -np.inf), far
+
+
+def _soft_mask_strict_causal(bias, w):
+    """A query does not see its own key."""
+    T = len(bias)
+    pos = np.arange(T)
+    causal = pos[None, :] < pos[:, None]
+    causal[0, 0] = True  # keep row 0 finite
+    far = ((pos[:, None] - pos[None, :]) > w) & causal
+    return np.where(causal, np.where(far, np.asarray(bias, float)[None, :], 0.0), -np.inf), far
+
+
 MUTANTS = {
     "window-exclusive": ("visible", _visible_exclusive),
     "query-misses-itself": ("visible", _visible_drops_self),
@@ -164,6 +183,8 @@ MUTANTS = {
     "soft-bias-positive": ("soft_bias", _soft_bias_positive),
     "soft-noise-ignored": ("soft_decision_arg", _soft_arg_without_noise),
     "soft-dlogit-sign": ("soft_attention_grads", _soft_grads_dlogit_sign),
+    "soft-window-one-short": ("soft_mask", _soft_mask_window_ge),
+    "soft-query-misses-itself": ("soft_mask", _soft_mask_strict_causal),
 }
 
 
