@@ -1629,7 +1629,6 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
 // Soft decision of key i: x = (logit + gamma + noise) / tau, alpha = sigmoid(x).
 // Query q >= i adds log(1 - alpha) = -softplus(x) to the score of key i when
 // q - i > w, nothing inside the window (the hard rule when alpha is 0 or 1).
-__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
 
 // The x of key i of unit (b, h).
@@ -1638,13 +1637,11 @@ __device__ __forceinline__ float soft_x(const SoftArgs& a, const float* __restri
   return (logit[unit_row0 + i] + a.gamma + noise[unit_row0 + i]) * a.inv_tau;
 }
 
-// attend_pair (bf16) with an additive score per key and column, in the exp2
-// domain: badd[0..3] for this lane's keys of block A, badd[4..7] of block B
-// (-inf for keys the column may not see).
-
-// The softmax step and P.V of attend_pair_biased from the pair's scores
-// (score_pair), so that the next column's score products can be issued
-// ahead of this column's softmax.
+// The softmax step and P.V of a pair of blocks from its raw scores
+// (score_pair), with an additive score per key and column in the exp2 domain:
+// badd[0..3] for this lane's keys of block A, badd[4..7] of block B (-inf for
+// keys the column may not see).  Split from the score products so that the
+// next column's can be issued ahead of this column's softmax.
 template <int D>
 __device__ __forceinline__ void softmax_pv_biased(const PairFrag<2, D>& f, const f32x4& SA, const f32x4& SB,
                                                   const float (&badd)[8], float sl2e, Acc<D>& a) {
@@ -1687,6 +1684,7 @@ __device__ __forceinline__ void softmax_pv_biased(const PairFrag<2, D>& f, const
   }
 }
 
+// attend_pair (bf16) with the additive scores badd (as softmax_pv_biased).
 template <int D>
 __device__ __forceinline__ void attend_pair_biased(const PairFrag<2, D>& f, const u32x4 (&qf)[Geo<2, D>::kChunks],
                                                    const float (&badd)[8], float sl2e, Acc<D>& a) {
@@ -1934,9 +1932,10 @@ __global__ __launch_bounds__(256) void soft_forward_kernel(SoftArgs a, const uin
 #ifndef DMS_SOFT_DKV_WG
 #define DMS_SOFT_DKV_WG 4
 #endif
-// Waves per work-group of the backward kernels: the waves of a work-group
-// share every staged step, so more waves means fewer re-reads of the
-// streamed operands (the dominant L2 / MALL traffic).
+// Waves per work-group of the backward kernels.  The waves of a work-group
+// share every staged step, so more waves re-read the streamed operands less
+// often; measured on the 32B-shaped training layer, 8 waves made dq slower
+// and dkv no faster than 4.
 constexpr int kSoftQWaves = DMS_SOFT_DQ_WG;
 constexpr int kSoftKWaves = DMS_SOFT_DKV_WG;
 constexpr int kSoftQCols = DMS_SOFT_QCOLS;               // query tiles of 16 per wave (dQ)
