@@ -260,7 +260,9 @@ DMS_API int dms_decode_chunk_channel(dms_cache* c, const void* d_q, const void* 
                hq reads KV head hq / G), scale = 1/sqrt(d) when 0 is passed
      lse     = natural log of each row's softmax denominator (for backward)
    As tau -> 0 with the logit's sign fixed this is the hard rule of the
-   decode path (alpha in {0, 1}).
+   decode path (alpha in {0, 1}).  Unlike that rule, a NaN logit or noise
+   value is not read as unmarked here: it propagates to the outputs and
+   gradients of the queries it reaches, as in any differentiable layer.
    Layouts: d_q [B, Hq, T, d], d_k, d_v [B, Hkv, T, d] bf16; d_logit,
    d_noise [B, Hkv, T] fp32; d_out [B, Hq, T, d] and d_lse [B, Hq, T] fp32.
    d = 64 or 128; 1 <= T <= 2^20; window >= 0; tau > 0.  d_workspace:
