@@ -189,3 +189,62 @@ def test_soft_attention_errors():
         dms.dms_soft_attention_backward(1, 2, 1, 8, 64, 4, 0.0, 1.0, 0.0, p(x), p(x), p(x), p(f), p(f), p(o), p(l),
                                         p(x), p(o), p(o), p(o), p(f), p(ws), need - 1)
     assert e.value.status == dms.DMS_ERR_WORKSPACE
+
+
+@gpu
+def test_soft_attention_long_ragged_sequence():
+    """T = 6000 (not a multiple of any tile: 64 keys per dK/dV work-group,
+    64 queries per dQ work-group, 192 per forward work-group, 32-row pairs):
+    every output and gradient of one KV head with its query heads against
+    the oracle."""
+    from learned_kv_cache_dms_amd import dms
+    from oracle import dms_oracle as O
+    B, Hq, Hkv, T, d, w, gamma, tau = 1, 8, 2, 6000, 128, 256, -3.0, 0.25
+    Q, K, V, dO, lg, g = _inputs(7700, B, Hq, Hkv, T, d, 3.0)
+    print(f"[long ragged] T={T} Hq={Hq} Hkv={Hkv}", flush=True)
+    q, k, v, do = _bf(Q), _bf(K), _bf(V), _bf(dO)
+    logit, noise = _f(lg), _f(g)
+    out, lse = dms.soft_attention_forward(q, k, v, logit, noise, w, gamma, tau)
+    grads = dms.soft_attention_backward(q, k, v, logit, noise, out, lse, do, w, gamma, tau)
+    torch.cuda.synchronize()
+    h = 1
+    G = Hq // Hkv
+    hs = slice(h * G, (h + 1) * G)
+    sl = lambda X: np.ascontiguousarray(X[:, h:h + 1])
+    ref = O.soft_attention(Q[:, hs], sl(K), sl(V), sl(lg), sl(g), w, gamma, tau)
+    refg = O.soft_attention_grads(Q[:, hs], sl(K), sl(V), sl(lg), sl(g), dO[:, hs], w, gamma, tau)
+    errs = {
+        "out": _nerr(out[:, hs].double().cpu().numpy(), ref["out"]),
+        "lse": float(np.max(np.abs(lse[:, hs].double().cpu().numpy() - ref["lse"]))),
+        "dq": _nerr(grads["dq"][:, hs].double().cpu().numpy(), refg["dq"]),
+        "dk": _nerr(grads["dk"][:, h:h + 1].double().cpu().numpy(), refg["dk"]),
+        "dv": _nerr(grads["dv"][:, h:h + 1].double().cpu().numpy(), refg["dv"]),
+        "dlogit": _nerr(grads["dlogit"][:, h:h + 1].double().cpu().numpy(), refg["dlogit"]),
+    }
+    print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    assert errs["lse"] <= TOL_LSE, errs
+    for key in ("out", "dq", "dk", "dv", "dlogit"):
+        assert errs[key] <= TOL, (key, errs)
+
+
+@gpu
+def test_soft_attention_on_a_side_stream():
+    """Both calls on a non-default stream, with the inputs written on that
+    stream just before: the results equal those of the default stream."""
+    from learned_kv_cache_dms_amd import dms
+    B, Hq, Hkv, T, d, w = 2, 8, 2, 300, 128, 16
+    Q, K, V, dO, lg, g = _inputs(7800, B, Hq, Hkv, T, d, 0.5)
+    args = [_bf(Q), _bf(K), _bf(V), _f(lg), _f(g)]
+    out0, lse0 = dms.soft_attention_forward(*args, w, 0.0, 0.5)
+    g0 = dms.soft_attention_backward(*args, out0, lse0, _bf(dO), w, 0.0, 0.5)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        a = [x.clone() for x in args]          # written on the side stream
+        do = _bf(dO).to(torch.bfloat16)
+        out1, lse1 = dms.soft_attention_forward(*a, w, 0.0, 0.5)
+        g1 = dms.soft_attention_backward(*a, out1, lse1, do, w, 0.0, 0.5)
+    side.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+    for key in g0:
+        assert torch.equal(g0[key], g1[key]), key
