@@ -575,7 +575,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs the DMS decode path on one GPU only; "
+        print("bench.py: the DMS path here runs on one GPU only; "
               f"--gpus {args.gpus} (WORLD_SIZE {world}) is not supported.", file=sys.stderr, flush=True)
         sys.exit(2)
 
@@ -636,7 +636,7 @@ def main():
         cache.prefill_channel(Kd, Vd, lengths, source="q", channel=ch, q=Qp)
         del Qp
     torch.cuda.synchronize()
-    # The dense prompt stays in torch's cache: returning 17 GB to the driver
+    # The dense prompt stays in torch's cache: returning 17 GB to the HIP runtime
     # (empty_cache) was measured to lower HBM streaming rates by 4-5% for the
     # rest of the process on this platform.
     del Kd, Vd, Ld
