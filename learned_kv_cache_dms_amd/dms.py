@@ -295,6 +295,49 @@ def soft_attention_backward(q, k, v, logit, noise, out, lse, dout, window, gamma
     return {"dq": dq, "dk": dk, "dv": dv, "dlogit": dlogit}
 
 
+def _soft_autograd():
+    import torch
+
+    class SoftAttention(torch.autograd.Function):
+        """The relaxed attention as an autograd function: the forward keeps
+        out and lse for dms_soft_attention_backward.  Gradients come back in
+        the inputs' dtypes (bf16 for q, k, v; fp32 for the logits); the
+        incoming gradient of out is rounded to bf16, the library's dout
+        operand.  The noise is a constant."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, logit, noise, window, gamma, tau, scale):
+            out, lse = soft_attention_forward(q, k, v, logit, noise, window, gamma, tau, scale)
+            ctx.save_for_backward(q, k, v, logit, noise, out, lse)
+            ctx.params = (window, gamma, tau, scale)
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, logit, noise, out, lse = ctx.saved_tensors
+            window, gamma, tau, scale = ctx.params
+            g = soft_attention_backward(q, k, v, logit, noise, out, lse,
+                                        dout.to(torch.bfloat16).contiguous(), window, gamma, tau, scale)
+            return (g["dq"].to(q.dtype), g["dk"].to(k.dtype), g["dv"].to(v.dtype), g["dlogit"],
+                    None, None, None, None, None)
+
+    return SoftAttention
+
+
+_SOFT_FN = None
+
+
+def soft_attention(q, k, v, logit, noise, window, gamma=0.0, tau=1.0, scale=0.0):
+    """Differentiable relaxed DMS attention (torch autograd over
+    dms_soft_attention_forward / dms_soft_attention_backward): returns out
+    [B, Hq, T, d] fp32; q, k, v bf16, logit and noise fp32 (see
+    soft_attention_forward for the shapes)."""
+    global _SOFT_FN
+    if _SOFT_FN is None:
+        _SOFT_FN = _soft_autograd()
+    return _SOFT_FN.apply(q, k, v, logit, noise, window, gamma, tau, scale)
+
+
 class Cache:
     """A DMS cache whose workspace is a torch uint8 tensor on the current
     device.  Tensors passed in must be contiguous, on that device, with the

@@ -248,3 +248,33 @@ def test_soft_attention_on_a_side_stream():
     assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
     for key in g0:
         assert torch.equal(g0[key], g1[key]), key
+
+
+@gpu
+def test_soft_attention_autograd_function():
+    """dms.soft_attention under torch autograd: out equals the forward call;
+    after backward of sum(out * dO) the logits' gradient equals the backward
+    call's exactly and the q, k, v gradients are its values rounded to bf16;
+    the logit gradient also matches the oracle."""
+    from learned_kv_cache_dms_amd import dms
+    from oracle import dms_oracle as O
+    B, Hq, Hkv, T, d, w, gamma, tau = 1, 8, 2, 200, 64, 12, -1.0, 0.5
+    Q, K, V, dO, lg, g = _inputs(7900, B, Hq, Hkv, T, d, 1.0)
+    q, k, v = (_bf(X).requires_grad_(True) for X in (Q, K, V))
+    logit = _f(lg).requires_grad_(True)
+    noise = _f(g)
+    out = dms.soft_attention(q, k, v, logit, noise, w, gamma, tau)
+    (out * _f(dO)).sum().backward()
+    torch.cuda.synchronize()
+    with torch.no_grad():
+        out2, lse2 = dms.soft_attention_forward(q.detach(), k.detach(), v.detach(), logit.detach(), noise, w,
+                                                gamma, tau)
+        g2 = dms.soft_attention_backward(q.detach(), k.detach(), v.detach(), logit.detach(), noise, out2, lse2,
+                                         _bf(dO), w, gamma, tau)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), out2)
+    assert torch.equal(logit.grad, g2["dlogit"])
+    for t, key in ((q, "dq"), (k, "dk"), (v, "dv")):
+        assert t.grad.dtype == torch.bfloat16 and torch.equal(t.grad, g2[key].to(torch.bfloat16)), key
+    ref = O.soft_attention_grads(Q, K, V, lg, g, dO, w, gamma, tau)
+    assert _nerr(logit.grad.double().cpu().numpy(), ref["dlogit"]) <= TOL
