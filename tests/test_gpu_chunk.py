@@ -200,3 +200,70 @@ def test_chunk_errors():
         big.decode_chunk(x, x, x, torch.zeros((1, 1, 1), dtype=torch.float32, device="cuda"))
     assert e.value.status == dms.DMS_ERR_ARG
     assert c.stats()["seen_tokens"] == 0
+
+
+@gpu
+def test_chunks_full_size_sampled_units():
+    """The Qwen-R1-32B-shaped layer at full size (64 x 32768-token prompts,
+    40 Q / 8 KV heads, d = 128, w = 256): chunks of 16, 3 and 16 tokens per
+    sequence.  For sampled units, every output row of every chunk against
+    the oracle's attention at that row's own position, and the visible and
+    pending sets after every chunk (bit-exact); every unit's live count at
+    the end."""
+    import dataclasses
+    import gpu_util as U
+    from oracle import dms_oracle as O
+    from synth import device as dsynth
+    from synth import workloads as W
+    chunks = [16, 3, 16]
+    wl = dataclasses.replace(W.qwen_32b(), decode_steps=sum(chunks))
+    B, Hq, Hkv, d, w, G = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window, wl.group
+    lengths = wl.prompt_lengths()
+    cache = U.make_cache(wl)
+    K, V, Lg = U.device_prompt(wl, 0, lengths)
+    cache.prefill(K, V, Lg, lengths)
+    del K, V, Lg
+    rng = np.random.default_rng(wl.seed + 1)
+    n_units = B * Hkv
+    picks = sorted(set([0, n_units - 1] + list(rng.choice(n_units, 2, replace=False))))
+    units = [(u // Hkv, u % Hkv) for u in picks]
+    host = {key: U.host_unit(wl, 0, key[0], key[1], int(lengths[key[0]]), wl.decode_steps) for key in units}
+    base = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    mb, ma = wl.layer_mu(0)
+    scale = O.default_scale(d)
+    st = U.CompareStats()
+    worst = 0.0
+    t0 = 0
+    for C in chunks:
+        print(f"[qwen-32b chunk] C={C} at step {t0}", flush=True)
+        q = torch.empty((B, Hq, C, d), dtype=torch.bfloat16, device="cuda")
+        k = torch.empty((B, Hkv, C, d), dtype=torch.bfloat16, device="cuda")
+        v = torch.empty_like(k)
+        lg = torch.empty((B, Hkv, C), dtype=torch.float32, device="cuda")
+        pb = base + t0  # per-sequence first position of the chunk
+        dsynth.fill(q, wl.seed, synth.STREAM_Q, 0, 0, pos_base=pb)
+        dsynth.fill(k, wl.seed, synth.STREAM_K, 0, 0, pos_base=pb)
+        dsynth.fill(v, wl.seed, synth.STREAM_V, 0, 0, pos_base=pb)
+        dsynth.logits(lg, wl.seed, 0, 0, mb, ma, wl.pos_threshold, pos_base=pb)
+        out = cache.decode_chunk(q, k, v, lg)
+        torch.cuda.synchronize()
+        for key in units:
+            ud = host[key]
+            alpha = O.eviction_decision(ud.logit)
+            for j in range(C - 1):
+                vis = O.visible(alpha, ud.prompt_len + t0 + j, w)
+                ref = O.attend(ud.Q[t0 + j], ud.K[vis], ud.V[vis], scale)
+                got = out[ud.b, ud.h * G:(ud.h + 1) * G, j].double().cpu().numpy()
+                err = float(np.max(np.abs(got - ref)))
+                worst = max(worst, err)
+                assert err <= TOL["bf16"], (key, t0 + j, err)
+            # the last row, with the cache state after the chunk
+            U.check_unit_step(cache, wl, ud, t0 + C - 1, out[:, :, C - 1], TOL["bf16"], st)
+        t0 += C
+    assert cache.stats()["sticky_error"] == 0
+    qlast = wl.prompt_len + wl.decode_steps - 1
+    lgh = synth.logits(wl.seed, 0, np.arange(B), Hkv, np.arange(qlast + 1), mb, ma, wl.pos_threshold)
+    _, _, n = cache.export(0, n_units)
+    ref_n = np.array([len(O.visible(O.eviction_decision(lgh[b, h]), qlast, w)) for b in range(B) for h in range(Hkv)])
+    assert np.array_equal(n, ref_n)
+    print(f"  max_err={max(worst, st.max_err):.2e} over {len(units)} units", flush=True)
