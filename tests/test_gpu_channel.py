@@ -145,3 +145,57 @@ def test_channel_argument_errors():
     c.append_channel(k, k, source="k", channel=3, zero=True)
     st = c.stats()
     assert st["seen_tokens"] == B * Hkv and st["sticky_error"] == 0
+
+
+@gpu
+def test_key_channel_full_size_sampled_units():
+    """The Qwen-R1-32B-shaped layer at full size (64 x 32768-token prompts):
+    the workload's logits, rounded to bf16, planted in key channel 77 and read
+    from there by the prompt compression and 8 appends, with that channel
+    stored as 0.  Sampled units at every step against the oracle on the same
+    logits and the channel-zeroed keys; every unit's live count at the end."""
+    import dataclasses
+    import gpu_util as U
+    from oracle import dms_oracle as O
+    from synth import workloads as W
+    ch = 77
+    wl = dataclasses.replace(W.qwen_32b(), decode_steps=8)
+    B, Hkv = wl.batch, wl.num_kv_heads
+    lengths = wl.prompt_lengths()
+    cache = U.make_cache(wl)
+    K, V, Lg = U.device_prompt(wl, 0, lengths)
+    K[..., ch] = Lg.to(torch.bfloat16)
+    print(f"[qwen-32b key channel {ch}] prefill", flush=True)
+    cache.prefill_channel(K, V, lengths, source="k", channel=ch, zero=True)
+    del K, V, Lg
+    rng = np.random.default_rng(wl.seed + 2)
+    n_units = B * Hkv
+    picks = sorted(set([0, n_units - 1] + list(rng.choice(n_units, 2, replace=False))))
+    units = [(u // Hkv, u % Hkv) for u in picks]
+    host = {}
+    for (b, h) in units:
+        ud = U.host_unit(wl, 0, b, h, int(lengths[b]), wl.decode_steps)
+        lg16 = synth.round_bf16(ud.logit)          # the logit as the channel holds it
+        Kz = ud.K.copy()
+        Kz[:, ch] = 0.0                            # the channel is stored as 0
+        host[(b, h)] = dataclasses.replace(ud, K=Kz, logit=lg16)
+    st = U.CompareStats()
+    pos = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    for t in range(wl.decode_steps):
+        q, k, v, lg = U.device_step(wl, 0, pos + t)
+        k[..., ch] = lg.to(torch.bfloat16)
+        cache.append_channel(k, v, source="k", channel=ch, zero=True)
+        out = cache.attend(q)
+        torch.cuda.synchronize()
+        for key in units:
+            U.check_unit_step(cache, wl, host[key], t, out, TOL["bf16"], st)
+    assert cache.stats()["sticky_error"] == 0
+    qlast = wl.prompt_len + wl.decode_steps - 1
+    mb, ma = wl.layer_mu(0)
+    lgh = synth.round_bf16(synth.logits(wl.seed, 0, np.arange(B), Hkv, np.arange(qlast + 1), mb, ma,
+                                        wl.pos_threshold))
+    _, _, n = cache.export(0, n_units)
+    ref_n = np.array([len(O.visible(O.eviction_decision(lgh[b, h]), qlast, wl.window))
+                      for b in range(B) for h in range(Hkv)])
+    assert np.array_equal(n, ref_n)
+    print(f"  checks={st.checks} max_err={st.max_err:.2e}", flush=True)
