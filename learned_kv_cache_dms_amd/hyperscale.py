@@ -30,9 +30,8 @@ decisions.  The two must agree exactly.
 from __future__ import annotations
 
 import dataclasses
-import time
 from dataclasses import dataclass
-from typing import Callable, Dict, List, Optional, Sequence
+from typing import Callable, List, Optional, Sequence
 
 import numpy as np
 

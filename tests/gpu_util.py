@@ -7,7 +7,6 @@ two twins are checked bit for bit in test_gpu_synth.py.
 """
 from __future__ import annotations
 
-import math
 import sys
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence, Tuple

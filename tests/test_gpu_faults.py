@@ -8,7 +8,6 @@
 - a NaN logit means "not marked";
 - reset returns the cache to a state equal to a fresh one.
 """
-import ctypes
 
 import numpy as np
 import pytest

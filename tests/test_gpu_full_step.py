@@ -9,7 +9,6 @@ Checked against the oracle: sampled (layer, sequence, KV head) units at
 sampled steps (visible sets, pending evictions, outputs), and the live
 counts of every unit of one layer after the last step.
 """
-import dataclasses
 import time
 
 import numpy as np
