@@ -2295,6 +2295,10 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
       split_pair(pr, PH[kt], PL[kt]);
       split_pair(ds, DH[kt], DL[kt]);
     }
+    // Raised issue priority over the gradient products, so that another
+    // wave's softmax arithmetic on the same SIMD does not delay their issue
+    // (measured: the backward pass about 3% faster than without).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const bf16x8 OT = __builtin_bit_cast(bf16x8, S.op[3][j * 64 + lane]);
@@ -2307,6 +2311,7 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
         ak[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DL[kt], ak[kt][j], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (s + 1 < nsteps) lds_store(st[(s + 1) & 1], pre, prx);
     __syncthreads();
     cur = nx;
