@@ -105,6 +105,7 @@ def cpu_baseline(wl, steps_per_unit: int, n_units: int):
     lengths = wl.prompt_lengths()
     G = wl.group
     elapsed = 0.0
+    live = 0  # live tokens attended over the sampled steps
     for u in units:
         b, h = divmod(u, wl.num_kv_heads)
         P = int(lengths[b])
@@ -115,8 +116,9 @@ def cpu_baseline(wl, steps_per_unit: int, n_units: int):
         Q = synth.tensor(wl.seed, synth.STREAM_Q, 0, [b], list(range(h * G, (h + 1) * G)),
                          np.arange(P, P + steps_per_unit), wl.head_dim, wl.dtype)[0].transpose(1, 0, 2)
         t0 = time.perf_counter()
-        O.decode_unit(Q, K, V, lg, P, steps_per_unit, wl.window, O.default_scale(wl.head_dim))
+        recs = O.decode_unit(Q, K, V, lg, P, steps_per_unit, wl.window, O.default_scale(wl.head_dim))
         elapsed += time.perf_counter() - t0
+        live += sum(len(r.visible) for r in recs)
     per_unit_step = elapsed / (len(units) * steps_per_unit)
     step_s = per_unit_step * U                      # a full decode step of the workload
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -128,8 +130,22 @@ def cpu_baseline(wl, steps_per_unit: int, n_units: int):
         "sample": f"{len(units)} of {U} (sequence, KV head) units x {steps_per_unit} decode steps at full "
                   f"context ({elapsed:.1f} s of oracle time), scaled to all units",
         "seconds_per_step": step_s,
+        # the live K/V bytes of the workload's dtype attended per second, as the metric counts them
+        "live_kv_gbps": live * 2 * wl.head_dim * (2 if wl.dtype == "bf16" else 4) / elapsed / 1e9,
         "host_cores_available": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def visible_pairs(Ld, lengths, w: int, G: int) -> int:
