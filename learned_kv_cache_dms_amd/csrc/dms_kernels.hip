@@ -1134,15 +1134,34 @@ __device__ __forceinline__ void read_q(const AttnShared<ES, D>& sh, int buf, int
   for (int c = 0; c < Geo<ES, D>::kChunks; ++c) qf[c] = sh.q[buf][c][lane];
 }
 
-// The item lookup: the LDS plan, or for very many units a scan of n[].
+// Item `item` in whole-unit mode: the unit at that position of the unit
+// order, whole.  Every unit holds at least its newest token whenever an
+// attention is allowed, so no unit is skipped and no plan is needed.  (A unit
+// left empty by an exhausted pool becomes an item with no blocks, for which
+// merge_item writes nothing.)
+__device__ __forceinline__ bool whole_item(const Dev& p, int item, Item& it) {
+  if (item >= p.U) return false;
+  it.u = p.ordered ? scalar_load(p.order + item) : item;
+  const int n = scalar_load(p.n + it.u);
+  it.nblk = (n + 15) >> 4;
+  it.tail = n & 15;
+  it.base = item;
+  it.items = 1;
+  it.k = 0;
+  return true;
+}
+
+// The item lookup: direct in whole-unit mode, else the LDS plan, or for very
+// many units a scan of n[].
 struct Planner {
-  bool lds;
+  bool whole, lds;
   long long tot;
   PlanCursor cur;
 };
 
 __device__ __forceinline__ bool find_item(const Dev& p, const PlanLds& pl, Planner& pn, int item, int lane,
                                           Item& it) {
+  if (pn.whole) return whole_item(p, item, it);
   return pn.lds ? plan_lookup_lds(p, pl, p.U, item, lane, it) : plan_find(p, lane, pn.tot, item, it, pn.cur);
 }
 
@@ -1220,6 +1239,10 @@ __device__ __forceinline__ void merge_item(const Dev& p, float* __restrict__ out
   using G = Geo<ES, D>;
   constexpr int kW = kWavesPerWG;
   constexpr int kTilesPerWave = (G::kTiles + kW - 1) / kW;
+  if (it.nblk == 0) {  // a unit with no live token (uniform): nothing to write
+    __syncthreads();    // but the next item's Q must still be visible on return
+    return;
+  }
   const int u = it.u;
   const int b = u / p.Hkv, h = u - b * p.Hkv;
   const int g = lane & 15;
@@ -1303,12 +1326,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Planner pn;
+  pn.whole = p.whole_units != 0;
   pn.lds = p.U <= kPlanLdsUnits;
   pn.tot = 0;
-  if (pn.lds)
-    plan_build_lds(p, pl);
-  else
-    pn.tot = plan_blocks(p, lane);
+  if (!pn.whole) {
+    if (pn.lds)
+      plan_build_lds(p, pl);
+    else
+      pn.tot = plan_blocks(p, lane);
+  }
 
   const int grid = (int)gridDim.x;
   int item = blockIdx.x;

@@ -87,6 +87,49 @@ def test_pool_exhaustion_during_decode():
 
 
 @gpu
+def test_whole_unit_attention_with_units_left_empty():
+    """1024 units, more than the resident work-groups (at most 2 per CU on 256
+    CUs), so each unit is one work item, found directly by its position in
+    the unit order.  An undersized pool leaves the units after the first that
+    does not fit empty (n = 0) after the prompt; the unequal prompt lengths
+    make the order length-balanced, so empty and full items alternate along
+    the work-groups' items.  Full units match the oracle, an empty unit's
+    output rows are left as they were."""
+    import gpu_util as U
+    from learned_kv_cache_dms_amd import dms
+    from oracle import dms_oracle as O
+    wl = _wl(batch=128, num_q_heads=40, num_kv_heads=8, prompt_len=80, mu_before=[-5.0])
+    lengths = np.random.default_rng(5).integers(17, 81, size=wl.batch)
+    need = int(sum((int(L) + 15) // 16 for L in lengths)) * wl.num_kv_heads
+    c = U.make_cache(wl, pool_blocks=need // 2)
+    K, V, Lg = _prompt(wl, lengths)
+    c.prefill(K, V, Lg, lengths.tolist())
+    assert c.stats()["sticky_error"] == dms.DMS_ERR_OUT_OF_BLOCKS
+    q, _, _, _ = U.device_step(wl, 0, torch.tensor(lengths, dtype=torch.int32, device="cuda"))
+    out = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), 7.0, device="cuda")
+    c.attend(q, out)
+    torch.cuda.synchronize()
+    _, _, n = c.export()
+    G = wl.group
+    full = [u for u in range(len(n)) if n[u] > 0]
+    empty = [u for u in range(len(n)) if n[u] == 0]
+    assert len(full) > 100 and len(empty) > 100, (len(full), len(empty))
+    got = out.double().cpu().numpy()
+    for u in empty:
+        b, h = divmod(u, wl.num_kv_heads)
+        assert np.all(got[b, h * G:(h + 1) * G] == 7.0), (b, h)
+    rng = np.random.default_rng(6)
+    for u in rng.choice(full, size=48, replace=False):
+        b, h = divmod(int(u), wl.num_kv_heads)
+        P = int(lengths[b])
+        assert n[u] == P  # nothing marked: the whole prompt is live
+        ud = U.host_unit(wl, 0, b, h, P, 1)
+        ref = O.attend(ud.Q[0], ud.K[:P], ud.V[:P], O.default_scale(wl.head_dim))
+        err = float(np.max(np.abs(got[b, h * G:(h + 1) * G] - ref)))
+        assert err <= 1e-4, (b, h, err)
+
+
+@gpu
 def test_capacity_state_and_argument_errors():
     import gpu_util as U
     from learned_kv_cache_dms_amd import dms
