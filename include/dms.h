@@ -209,7 +209,9 @@ DMS_API int dms_prefill_attention(dms_cache* c, const void* d_q, const void* d_k
      out[b, hq, :] = sum_i softmax_i(scale * <q[b,hq], k_i>) v_i,
    i over the visible tokens of (b, hq / G).
      d_q  : [B, Hq, d] of dtype
-     d_out: [B, Hq, d] fp32
+     d_out: [B, Hq, d] fp32; the rows of a (sequence, KV head) left with no
+            live token by an exhausted pool (sticky DMS_ERR_OUT_OF_BLOCKS)
+            are not written
    Errors: DMS_ERR_STATE if some sequence has no token yet. */
 DMS_API int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stream);
 
