@@ -1308,9 +1308,9 @@ __device__ __forceinline__ void merge_item(const Dev& p, float* __restrict__ out
 
 // Persistent launch: one work-group per resident slot; work-group b takes
 // items b, b + G, b + 2G, ... (G = grid size).  The plan makes items of about
-// equal size, so the static assignment is balanced, and the next item is
-// known in advance: its block ids are read while the item before it is
-// computed.
+// equal size (in whole-unit mode each unit is one item, found without a
+// plan), so the static assignment is balanced, and the next item is known in
+// advance: its block ids are read while the item before it is computed.
 //
 // The loop is written so that the compiler's load-counter waits stay exact:
 // every load is unconditional (an absent next item is an empty one on unit

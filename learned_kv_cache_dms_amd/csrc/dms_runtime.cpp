@@ -218,7 +218,8 @@ int dms_cache_create(const dms_config* cfg, void* d_workspace, size_t workspace_
   // Persistent attention grid: as many 4-wave work-groups as fit at once.
   // The split plan aims at one work item per resident work-group.  With at
   // least as many units as that, every unit is one item (whole-unit mode):
-  // no partials are written and the split-merge launch is skipped.  With
+  // the kernel builds no plan (item i is the unit at position i of the unit
+  // order), no partials are written and the split-merge launch is skipped.  With
   // fewer, units are split in proportion to their blocks.  (Measured on 512
   // equal units and 512 work-groups: one item per unit 193.5 us per call,
   // two 199 us.)
