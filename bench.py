@@ -689,13 +689,14 @@ def main():
         cache.attend(qs[t], out)
     st0 = cache.stats()
 
-    # Every N-th attention call of the timed region is bracketed by its own
-    # event pair (an event pair costs a few microseconds of stream time, so
-    # one around every call would slow every step); the calls in between run
-    # exactly as the sampled ones.
+    # Every N-th attention call of the timed region is timed by a pair of HIP
+    # events that the runtime stamps with the start and the end of the call's
+    # own kernels (dms_decode_attention_timed); the calls in between run
+    # exactly as the sampled ones.  (Event pairs recorded around the call
+    # instead read 1-10 us more than the kernels themselves.)
     N = max(1, args.event_every)
     sampled = list(range(0, K, N))
-    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
+    ev = {i: dms.KernelTimer() for i in sampled}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -704,9 +705,7 @@ def main():
         t = W + i
         append(t)
         if i in ev:
-            ev[i][0].record()
-            cache.attend(qs[t], out)
-            ev[i][1].record()
+            cache.attend_timed(qs[t], ev[i], out)
         else:
             cache.attend(qs[t], out)
     end.record()
@@ -717,10 +716,10 @@ def main():
         raise SystemExit(f"device error during the run: {st1}")
 
     total_ms = start.elapsed_time(end)
-    attn_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in sampled]
+    attn_ms = [ev[i].elapsed_ms() for i in sampled]
     attn_avg_s = sum(attn_ms) / len(attn_ms) / 1e3
     # step period from one sampled attention end to the next, per step
-    period_ms = [ev[a][1].elapsed_time(ev[b][1]) / (b - a) for a, b in zip(sampled, sampled[1:])]
+    period_ms = [dms.KernelTimer.between(ev[a], ev[b]) / (b - a) for a, b in zip(sampled, sampled[1:])]
     live_tokens = (st1["live_token_steps"] - st0["live_token_steps"]) / K   # per step, all units
     live_bytes = live_tokens * 2 * d * esize
     step_s = total_ms / K / 1e3

@@ -215,6 +215,17 @@ DMS_API int dms_prefill_attention(dms_cache* c, const void* d_q, const void* d_k
    Errors: DMS_ERR_STATE if some sequence has no token yet. */
 DMS_API int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stream);
 
+/* Async.  dms_decode_attention, with its kernels timed by the HIP runtime:
+   start_event and stop_event (hipEvent_t, created by the caller with timing
+   enabled) are stamped with the start of the attention kernel and the end of
+   the call's last kernel (the split merge when one runs), not at marker
+   packets around the call, so hipEventElapsedTime gives the call's own
+   device time.  For measurement; the results are those of
+   dms_decode_attention.
+   Errors: as dms_decode_attention; DMS_ERR_ARG for a NULL event. */
+DMS_API int dms_decode_attention_timed(dms_cache* c, const void* d_q, float* d_out, void* start_event,
+                                       void* stop_event, void* stream);
+
 /* Async.  `chunk` decode steps at once: for every sequence b and every
    0 <= j < chunk, position q_j = len_b + j is appended (decision,
    retirement, store, as dms_append_step does, in order) and its query

@@ -119,7 +119,9 @@ hipError_t launch_soft_backward(const SoftArgs& a, int d, const void* q, const v
 hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s);
 // Work-groups of the attention kernel that fit on the device at once.
 int attention_resident_wgs(int dtype, int d, int num_cus);
+// start / stop (may be null): events stamped with the start of the attention
+// launch and the end of the call's last launch.
 hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out,
-                            int64_t grid_wgs, hipStream_t s);
+                            int64_t grid_wgs, hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 }  // namespace dms

@@ -71,6 +71,20 @@ static hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStr
   return hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, s);
 }
 
+// As launch, through hipExtLaunchKernel with events that the runtime stamps
+// with the start and the end of this kernel (either may be null).
+template <typename... KArgs, typename... Args>
+static hipError_t launch_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, hipEvent_t start,
+                               hipEvent_t stop, Args&&... args) {
+  auto tup = [](auto&&... a) { return std::tuple<KArgs...>(a...); }(std::forward<Args>(args)...);
+  void* ptrs[sizeof...(KArgs)];
+  std::apply([&](auto&... a) {
+    int i = 0;
+    ((ptrs[i++] = (void*)&a), ...);
+  }, tup);
+  return hipExtLaunchKernel((const void*)kernel, grid, block, ptrs, 0, s, start, stop, 0);
+}
+
 typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
@@ -2651,13 +2665,22 @@ hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const v
 }
 
 template <int ES, int D>
-static hipError_t attention_t(const Dev& p, const void* q, float* out, int64_t grid_wgs, hipStream_t s) {
+static hipError_t attention_t(const Dev& p, const void* q, float* out, int64_t grid_wgs, hipStream_t s,
+                              hipEvent_t start, hipEvent_t stop) {
   // whole_units: no unit is split, so there is nothing for reduce_kernel
-  const int64_t nwg = grid_wgs;
-  const hipError_t e = launch(attention_kernel<ES, D>, dim3((unsigned)nwg), dim3(64 * kWavesPerWG), s, p,
-                              (const int32_t*)p.btab, (const uint8_t*)q, out);
+  const dim3 grid((unsigned)grid_wgs), block(64 * kWavesPerWG);
+  const dim3 rgrid((p.U + kWavesPerWG - 1) / kWavesPerWG);
+  if (!start && !stop) {
+    const hipError_t e = launch(attention_kernel<ES, D>, grid, block, s, p, (const int32_t*)p.btab,
+                                (const uint8_t*)q, out);
+    if (e != hipSuccess || p.whole_units) return e;
+    return launch(reduce_kernel<D>, rgrid, block, s, p, out);
+  }
+  // timed: start with the attention launch, stop with the call's last launch
+  const hipError_t e = launch_timed(attention_kernel<ES, D>, grid, block, s, start, p.whole_units ? stop : nullptr,
+                                    p, (const int32_t*)p.btab, (const uint8_t*)q, out);
   if (e != hipSuccess || p.whole_units) return e;
-  return launch(reduce_kernel<D>, dim3((p.U + kWavesPerWG - 1) / kWavesPerWG), dim3(64 * kWavesPerWG), s, p, out);
+  return launch_timed(reduce_kernel<D>, rgrid, block, s, nullptr, stop, p, out);
 }
 
 template <int ES, int D>
@@ -2820,10 +2843,12 @@ int attention_resident_wgs(int dtype, int d, int num_cus) {
 }
 
 hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out, int64_t grid_wgs,
-                            hipStream_t s) {
+                            hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   if (dtype == 1)
-    return d == 128 ? attention_t<2, 128>(p, q, out, grid_wgs, s) : attention_t<2, 64>(p, q, out, grid_wgs, s);
-  return d == 128 ? attention_t<4, 128>(p, q, out, grid_wgs, s) : attention_t<4, 64>(p, q, out, grid_wgs, s);
+    return d == 128 ? attention_t<2, 128>(p, q, out, grid_wgs, s, start, stop)
+                    : attention_t<2, 64>(p, q, out, grid_wgs, s, start, stop);
+  return d == 128 ? attention_t<4, 128>(p, q, out, grid_wgs, s, start, stop)
+                  : attention_t<4, 64>(p, q, out, grid_wgs, s, start, stop);
 }
 
 }  // namespace dms

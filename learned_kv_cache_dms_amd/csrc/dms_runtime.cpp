@@ -447,6 +447,17 @@ int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stre
                                           (hipStream_t)stream));
 }
 
+int dms_decode_attention_timed(dms_cache* c, const void* d_q, float* d_out, void* start_event, void* stop_event,
+                               void* stream) {
+  if (!c || !d_q || !d_out || !start_event || !stop_event) return DMS_ERR_ARG;
+  int st = check_device(c);
+  if (st != DMS_OK) return st;
+  for (int32_t x : c->len)
+    if (x < 1) return DMS_ERR_STATE;
+  return hip_status(dms::launch_attention(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_out, c->grid_wgs,
+                                          (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event));
+}
+
 int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream) {
   if (!c || !out) return DMS_ERR_ARG;
   int st = check_device(c);

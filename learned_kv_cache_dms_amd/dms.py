@@ -97,6 +97,7 @@ def _load():
         "dms_append_step_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp]),
         "dms_prefill_compress_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, P(i32), i32, vp]),
         "dms_decode_attention": (ctypes.c_int, [vp, vp, vp, vp]),
+        "dms_decode_attention_timed": (ctypes.c_int, [vp, vp, vp, vp, vp, vp]),
         "dms_prefill_attention": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, vp]),
         "dms_decode_chunk": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, vp]),
         "dms_decode_chunk_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]),
@@ -202,6 +203,80 @@ def dms_decode_chunk_channel(h: int, d_q: int, d_k: int, d_v: int, source: int, 
 
 def dms_decode_attention(h: int, d_q: int, d_out: int, stream: int = 0):
     _check(lib.dms_decode_attention(h, d_q, d_out, stream), "dms_decode_attention")
+
+
+def dms_decode_attention_timed(h: int, d_q: int, d_out: int, start_event: int, stop_event: int, stream: int = 0):
+    _check(lib.dms_decode_attention_timed(h, d_q, d_out, start_event, stop_event, stream),
+           "dms_decode_attention_timed")
+
+
+_hip = None
+
+
+def _hip_api():
+    """The process's HIP runtime (the one torch loaded; opening its soname
+    returns that same library), for the events of dms_decode_attention_timed."""
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so.7")
+        vp = ctypes.c_void_p
+        h.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+        h.hipEventDestroy.argtypes = [vp]
+        h.hipEventSynchronize.argtypes = [vp]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        for f in (h.hipEventCreate, h.hipEventDestroy, h.hipEventSynchronize, h.hipEventElapsedTime):
+            f.restype = ctypes.c_int
+        _hip = h
+    return _hip
+
+
+class KernelTimer:
+    """A start / stop pair of HIP events (timing enabled) for
+    dms_decode_attention_timed, which has the runtime stamp them with the
+    start and the end of the call's own kernels."""
+
+    def __init__(self):
+        h = _hip_api()
+        self.start, self.stop = ctypes.c_void_p(), ctypes.c_void_p()
+        for e in (self.start, self.stop):
+            rc = h.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+
+    def elapsed_ms(self) -> float:
+        h = _hip_api()
+        rc = h.hipEventSynchronize(self.stop)
+        t = ctypes.c_float()
+        if rc == 0:
+            rc = h.hipEventElapsedTime(ctypes.byref(t), self.start, self.stop)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return t.value
+
+    @staticmethod
+    def between(a: "KernelTimer", b: "KernelTimer") -> float:
+        """ms from the end of a's kernels to the end of b's."""
+        h = _hip_api()
+        t = ctypes.c_float()
+        rc = h.hipEventSynchronize(b.stop)
+        if rc == 0:
+            rc = h.hipEventElapsedTime(ctypes.byref(t), a.stop, b.stop)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return t.value
+
+    def close(self):
+        h = _hip_api()
+        for e in (self.start, self.stop):
+            if e.value:
+                h.hipEventDestroy(e)
+                e.value = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def dms_cache_stats(h: int, stream: int = 0) -> dict:
@@ -452,6 +527,15 @@ class Cache:
             out = self._torch.empty((self.B, self.Hq, self.d), dtype=self._torch.float32, device=q.device)
         po = self._chk(out, (self.B, self.Hq, self.d), self._torch.float32, "out")
         dms_decode_attention(self.handle, pq, po, self._stream())
+        return out
+
+    def attend_timed(self, q, timer: "KernelTimer", out=None):
+        """attend, with the call's kernels timed into `timer` (elapsed_ms)."""
+        pq = self._chk(q, (self.B, self.Hq, self.d), self.tdtype, "q")
+        if out is None:
+            out = self._torch.empty((self.B, self.Hq, self.d), dtype=self._torch.float32, device=q.device)
+        po = self._chk(out, (self.B, self.Hq, self.d), self._torch.float32, "out")
+        dms_decode_attention_timed(self.handle, pq, po, timer.start.value, timer.stop.value, self._stream())
         return out
 
     def stats(self) -> dict:

@@ -80,6 +80,7 @@ def test_null_handle_calls_are_argument_errors():
     assert L.dms_cache_reset(None, None) == dms.DMS_ERR_ARG
     assert L.dms_append_step(None, 1, 1, 1, None) == dms.DMS_ERR_ARG
     assert L.dms_decode_attention(None, 1, 1, None) == dms.DMS_ERR_ARG
+    assert L.dms_decode_attention_timed(None, 1, 1, 1, 1, None) == dms.DMS_ERR_ARG
     assert L.dms_prefill_attention(None, 1, 1, 1, 1, 1, None) == dms.DMS_ERR_ARG
     assert L.dms_decode_chunk(None, 1, 1, 1, 1, 1, 1, None) == dms.DMS_ERR_ARG
     assert L.dms_decode_chunk_channel(None, 1, 1, 1, 0, 0, 0, 1, 1, None) == dms.DMS_ERR_ARG

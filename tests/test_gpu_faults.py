@@ -209,6 +209,28 @@ def test_reset_equals_fresh_cache():
 
 
 @gpu
+def test_timed_attention_equals_untimed():
+    """dms_decode_attention_timed gives the untimed call's results bit for bit
+    and has the runtime stamp its events (a positive elapsed time); NULL
+    events are argument errors."""
+    import gpu_util as U
+    from learned_kv_cache_dms_amd import dms
+    wl = _wl(prompt_len=100, mu_before=[0.5])
+    c = U.make_cache(wl)
+    K, V, Lg = _prompt(wl, [100, 77])
+    c.prefill(K, V, Lg, [100, 77])
+    q, _, _, _ = U.device_step(wl, 0, torch.tensor([100, 77], dtype=torch.int32, device="cuda"))
+    a = c.attend(q)
+    timer = dms.KernelTimer()
+    b = c.attend_timed(q, timer)
+    assert timer.elapsed_ms() > 0.0
+    assert torch.equal(a, b)
+    with pytest.raises(dms.DmsError):
+        dms.dms_decode_attention_timed(c.handle, q.data_ptr(), b.data_ptr(), 0, timer.stop.value)
+    timer.close()
+
+
+@gpu
 def test_runs_on_a_non_default_stream():
     import gpu_util as U
     wl = _wl(prompt_len=60, decode_steps=3)
