@@ -11,9 +11,10 @@ workload is the Qwen-R1-32B-shaped layer: 64 chains at 32768 tokens, 40 query
 
 Prints one JSON line.  `value` is decode-attention tokens per second (batch
 sequences per step); the live-KV bandwidth of the attention launch is in
-`roofline`, timed with HIP events around each dms_decode_attention call
-(attention_kernel; reduce_kernel too when some unit is split, which never
-happens at 512 units on 512 resident work-groups).  `cpu_baseline` times the
+`roofline`, timed on every 8th attention call of the timed region with HIP
+events that the runtime stamps at the call's own kernels
+(dms_decode_attention_timed: attention_kernel; reduce_kernel too when some
+unit is split, which never happens at 512 units on 512 resident work-groups).  `cpu_baseline` times the
 CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -571,8 +572,8 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=256)
     ap.add_argument("--calib-copy-bytes", type=int, default=0)
     ap.add_argument("--event-every", type=int, default=8,
-                    help="decode bench: bracket every N-th attention call of the timed region with its own "
-                         "event pair (roofline.achieved is their mean)")
+                    help="decode bench: time every N-th attention call of the timed region with its own "
+                         "kernel-stamped event pair (roofline.achieved is their mean)")
     ap.add_argument("--logit-source", choices=("array", "k", "q"), default="array",
                     help="where the append reads the eviction logit: the logit array, or the workload's "
                          "logits (bf16-rounded) planted in channel --logit-channel of the keys (stored "
