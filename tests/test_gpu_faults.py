@@ -108,7 +108,14 @@ def test_whole_unit_attention_with_units_left_empty():
     q, _, _, _ = U.device_step(wl, 0, torch.tensor(lengths, dtype=torch.int32, device="cuda"))
     out = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), 7.0, device="cuda")
     c.attend(q, out)
+    # the timed call in whole-unit mode (its stop event on the attention launch itself)
+    out_t = torch.full_like(out, 7.0)
+    timer = dms.KernelTimer()
+    c.attend_timed(q, timer, out_t)
+    assert timer.elapsed_ms() > 0.0
+    timer.close()
     torch.cuda.synchronize()
+    assert torch.equal(out, out_t)
     _, _, n = c.export()
     G = wl.group
     full = [u for u in range(len(n)) if n[u] > 0]
@@ -212,7 +219,8 @@ def test_reset_equals_fresh_cache():
 def test_timed_attention_equals_untimed():
     """dms_decode_attention_timed gives the untimed call's results bit for bit
     and has the runtime stamp its events (a positive elapsed time); NULL
-    events are argument errors."""
+    events are argument errors.  4 units on many more work-groups: the units
+    are split, so the stop event is bound to the split-merge launch."""
     import gpu_util as U
     from learned_kv_cache_dms_amd import dms
     wl = _wl(prompt_len=100, mu_before=[0.5])
