@@ -721,6 +721,8 @@ def main():
     attn_avg_s = sum(attn_ms) / len(attn_ms) / 1e3
     # step period from one sampled attention end to the next, per step
     period_ms = [dms.KernelTimer.between(ev[a], ev[b]) / (b - a) for a, b in zip(sampled, sampled[1:])]
+    for tm in ev.values():
+        tm.close()
     live_tokens = (st1["live_token_steps"] - st0["live_token_steps"]) / K   # per step, all units
     live_bytes = live_tokens * 2 * d * esize
     step_s = total_ms / K / 1e3
