@@ -261,10 +261,13 @@ DMS_API int dms_decode_chunk_channel(dms_cache* c, const void* d_q, const void* 
 /* Training-time relaxed DMS attention: the decisions as a differentiable
    soft mask (Gumbel-sigmoid), for learning the eviction logits.  Source:
    "Inference-Time Hyper-Scaling with KV Cache Compression", third-party
-   paper summary page, section "Method" (the paper's section 3.2, Eq. 5-6):
-   during training alpha_i is sampled from a Gumbel-sigmoid, and log(1 -
-   alpha_i) is added to the attention score of key i for the queries that
-   are more than the window past it.  Readings fixed here:
+   paper summary page, section "Method": during training the binary decision
+   is relaxed through a Gumbel-sigmoid at low temperature with a logit
+   offset, its effect is delayed by the window, and the decisions enter
+   attention as an additive mask.  The page prints no formula for that mask;
+   the form below is this library's reading of it (the additive term whose
+   limits alpha -> 0 and alpha -> 1 give the hard rule's 0 and -inf).
+   Readings fixed here:
      x_i     = (logit_i + gamma + noise_i) / tau, alpha_i = sigmoid(x_i), with
                noise_i the Gumbel (logistic) sample, supplied by the caller
      bias    = log(1 - alpha_i) = -softplus(x_i) for queries q with q - i > w,

@@ -402,11 +402,3 @@ def decode_batch_channel(Q: np.ndarray, K: np.ndarray, V: np.ndarray, prompt_len
     if scale is None:
         scale = default_scale(Q.shape[-1])
     return decode_batch(Q, Kc, V, logit, prompt_lens, steps, w, scale, units)
-
-
-def state_after_prefill(logit_row: np.ndarray, prompt_len: int, w: int):
-    """Visible set and pending marked tokens after a prompt of P tokens,
-    i.e. the state that P single-token appends leave (P >= 1)."""
-    alpha = eviction_decision(logit_row)
-    q = prompt_len - 1
-    return visible(alpha, q, w), pending(alpha, q, w)

@@ -45,19 +45,26 @@ def pin_golden_visibility(O):
             assert list(O.retired(alpha, q, w)) == ret, (w, q)
 
 
-def _fifo_visible_sets(alpha, w, T):
+def _fifo_simulation(alpha, w, T):
     """Delayed eviction simulated with explicit expiry times: a marked token
-    i is scheduled to leave once the query passes i + w."""
+    i is scheduled to leave once the query passes i + w.  Returns, for every
+    query q, the live tokens and the scheduled ones among them (marked,
+    still live, their removal pending)."""
     live = []
     expiry = {}
-    sets = []
+    sets, scheduled = [], []
     for q in range(T):
         live.append(q)
         if alpha[q]:
             expiry[q] = q + w
         live = [i for i in live if not (i in expiry and q > expiry[i])]
         sets.append(list(live))
-    return sets
+        scheduled.append([i for i in live if i in expiry])
+    return sets, scheduled
+
+
+def _fifo_visible_sets(alpha, w, T):
+    return _fifo_simulation(alpha, w, T)[0]
 
 
 def pin_fifo_simulation(O):
@@ -71,6 +78,25 @@ def pin_fifo_simulation(O):
                 assert list(O.visible(alpha, q, w)) == ref[q], (w, p, q)
                 prev = set(ref[q - 1]) | {q} if q > 0 else {0}
                 assert sorted(prev - set(ref[q])) == list(O.retired(alpha, q, w)), (w, p, q)
+
+
+def pin_pending_against_fifo(O):
+    """The pending set is exactly the simulation's scheduled tokens: every
+    marked token still live, oldest included (completeness and soundness),
+    and its size is min(q, w) + 1 when every token is marked."""
+    rng = np.random.default_rng(19)
+    for w in (0, 1, 3, 8, 40):
+        for p in (0.0, 0.4, 0.9, 1.0):
+            T = 90
+            alpha = rng.random(T) < p
+            _, sched = _fifo_simulation(alpha, w, T)
+            for q in range(T):
+                got = [int(i) for i in O.pending(alpha, q, w)]
+                assert got == sched[q], (w, p, q, got, sched[q])
+    ones = np.ones(50, dtype=bool)
+    for w in (0, 5, 60):
+        for q in range(50):
+            assert len(O.pending(ones, q, w)) == min(q, w) + 1
 
 
 def pin_special_visibility(O):
@@ -525,6 +551,7 @@ def pin_soft_attention_grads_are_autograd(O):
 ALL_PINS = [
     pin_golden_visibility,
     pin_fifo_simulation,
+    pin_pending_against_fifo,
     pin_special_visibility,
     pin_schedule_invariants,
     pin_decision_threshold,

@@ -44,6 +44,15 @@ def _retired_off_by_one(alpha_row, q, w):
     return [j] if j >= 0 and bool(alpha_row[j]) else []
 
 
+def _pending_empty(alpha_row, q, w):
+    return np.zeros(0, dtype=np.int64)
+
+
+def _pending_window_one_short(alpha_row, q, w):
+    i = np.arange(max(0, q - w + 1), q + 1)
+    return i[np.asarray(alpha_row, dtype=bool)[i]]
+
+
 def _kv_head_mod(hq, group):
     return hq % group
 
@@ -169,6 +178,8 @@ MUTANTS = {
     "threshold-ge-zero": ("eviction_decision", _decision_ge),
     "nan-marks": ("eviction_decision", _decision_nan_marks),
     "retire-off-by-one": ("retired", _retired_off_by_one),
+    "pending-empty": ("pending", _pending_empty),
+    "pending-window-one-short": ("pending", _pending_window_one_short),
     "gqa-modulo": ("kv_head_of", _kv_head_mod),
     "scale-1-over-d": ("default_scale", _scale_over_d),
     "k-v-swapped": ("attend", _attend_kv_swapped),
