@@ -84,7 +84,11 @@ typedef struct {
   int32_t window;       /* w >= 0; values >= max_tokens behave like max_tokens */
   int32_t block_tokens; /* tokens per cache block; must be 16 */
   int32_t max_tokens;   /* per sequence, prompt plus decode steps, 1 .. 2^24 */
-  int32_t max_splits;   /* cap on attention work items per (sequence, KV head); 0 -> 32 */
+  int32_t split_wgs;    /* how the decode attention shares its work among work-groups:
+                           0 automatic (see dms_cache_balance); 1 every (sequence, KV
+                           head) whole to one work-group; n >= 2 always split the
+                           live blocks in equal shares over min(n, resident)
+                           work-groups (requires batch * num_kv_heads <= 4096) */
   int64_t pool_blocks;  /* blocks in the shared pool, 1 .. 2^31-1; one block holds
                            16 tokens of K and V of one (sequence, KV head) */
   dms_dtype dtype;      /* element type of Q, K, V; outputs are always fp32 */
@@ -214,6 +218,59 @@ DMS_API int dms_prefill_attention(dms_cache* c, const void* d_q, const void* d_k
             are not written
    Errors: DMS_ERR_STATE if some sequence has no token yet. */
 DMS_API int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stream);
+
+/* Async.  One decode step: dms_append_step followed by dms_decode_attention,
+   with the same arguments, results and final cache, in fewer launches.  In
+   whole-unit mode (see dms_cache_balance) it is a single kernel: the
+   work-group that attends a (sequence, KV head) also appends its token, and
+   the attention reads the cache as it stood before the step without the
+   retiring token, plus the new token from d_k / d_v, which is exactly the
+   visible set after the append.  In split mode it is the append, the
+   attention and the split merge.  Unlike the two calls, a sequence may be
+   empty before the step (its output is then the new token's value row).
+   When the pool is exhausted (sticky DMS_ERR_OUT_OF_BLOCKS) the token that
+   found no block is not stored but is still attended in this step.
+     d_q : [B, Hq, d]; d_k, d_v: [B, Hkv, d] of dtype; d_logit: [B, Hkv] fp32
+     d_out: [B, Hq, d] fp32
+   Errors: DMS_ERR_CAPACITY if some len_b + 1 > max_tokens; DMS_ERR_ARG for
+   NULL pointers. */
+DMS_API int dms_decode_step(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, const float* d_logit,
+                            float* d_out, void* stream);
+
+/* Async.  dms_decode_step with its launches timed by the HIP runtime:
+   start_event is stamped at the start of the step's first kernel and
+   stop_event at the end of its last (as dms_decode_attention_timed).  For
+   measurement.  Errors: as dms_decode_step; DMS_ERR_ARG for a NULL event. */
+DMS_API int dms_decode_step_timed(dms_cache* c, const void* d_q, const void* d_k, const void* d_v,
+                                  const float* d_logit, float* d_out, void* start_event, void* stop_event,
+                                  void* stream);
+
+/* Async.  dms_decode_step with the eviction logit read from a projection
+   channel, as dms_append_step_channel (same sources, channel and zeroing;
+   d_q is both the step's queries and, for DMS_LOGIT_FROM_Q, the logit
+   source).  Errors: those of dms_decode_step and of
+   dms_append_step_channel's arguments. */
+DMS_API int dms_decode_step_channel(dms_cache* c, const void* d_q, const void* d_k, const void* d_v,
+                                    int32_t source, int32_t channel, int32_t zero_channel, float* d_out,
+                                    void* stream);
+
+/* Synchronises `stream`, reads every (sequence, KV head)'s live count and
+   re-plans how the decode attention shares its work.  Heads reach different
+   compression ratios ("Inference-Time Hyper-Scaling with KV Cache
+   Compression", third-party paper summary page, section "Method": each head
+   can land at its own compression ratio), so the live blocks per (sequence,
+   KV head) can differ several-fold.  Whole-unit mode deals the (sequence, KV
+   head)s to the work-groups longest first by live blocks; when the heaviest
+   work-group would still carry more than 1/16 above the mean (or there are
+   fewer (sequence, KV head)s than work-groups), the attention switches to
+   split mode, which gives every work-group an equal share of the live
+   blocks and merges the pieces of a split (sequence, KV head) in a second
+   launch.  The plan stays in force until the next dms_cache_balance, reset
+   or prompt compression; calls stay correct whatever the plan, only their
+   speed depends on it.  With split_wgs != 0 the mode is fixed (1: whole
+   units, dealt as above; >= 2: split, nothing to do).  Call after a prompt's
+   compression and from time to time as the live counts drift. */
+DMS_API int dms_cache_balance(dms_cache* c, void* stream);
 
 /* Async.  dms_decode_attention, with its kernels timed by the HIP runtime:
    start_event and stop_event (hipEvent_t, created by the caller with timing

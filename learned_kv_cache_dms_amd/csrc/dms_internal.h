@@ -9,10 +9,10 @@ namespace dms {
 
 constexpr int kBlockTokens = 16;
 constexpr int kMaxGroup = 16;      // query heads per KV head held by one MFMA tile
-constexpr int kMaxItemBlocks = 512;  // blocks per split attention work item (128 per wave)
-constexpr int kMaxTargetItems = 4096;  // cap on the split plan's target item count
 constexpr int kWavesPerWG = 4;     // waves per work-group (attention work item, append, reduce)
-constexpr int kPlanLdsUnits = 4096;  // units up to which the attention keeps its plan in LDS
+constexpr int kPlanLdsUnits = 4096;  // most units the attention's split mode plans for (its plan is in LDS)
+constexpr int kMaxAttnWGs = 4096;  // most attention work-groups of a launch (the workspace is sized for it)
+constexpr int kMinSplitBlocks = 8;  // split mode: fewest blocks per work-group (2 per wave)
 
 // Device-side counters (one 64-byte line).
 struct Counters {
@@ -27,12 +27,12 @@ struct Counters {
 struct Layout {
   int32_t B, Hq, Hkv, G, d, esize;
   int32_t R;           // ring entries per unit = min(window, max_tokens) + 1
-  int32_t max_tokens, max_blocks, max_splits, U;
+  int32_t max_tokens, max_blocks, U;
   int64_t pool_blocks, block_bytes;
   int32_t item_floats;  // floats per attention partial: m[16], l[16], o[G][d]
-  int64_t max_items;    // partial slots: the most items a plan can have
+  int64_t max_items;    // partial slots: U + kMaxAttnWGs (split mode uses slots u + g)
   int64_t off_pool, off_btab, off_blkpos, off_blkmask, off_ring, off_n, off_pos, off_plan, off_order,
-      off_ctr, off_part, total;
+      off_wgrange, off_ctr, off_part, total;
 };
 
 // Device pointers derived from a Layout and the workspace base, passed by
@@ -45,13 +45,15 @@ struct Dev {
   int32_t* ring;       // [U][R] slot of a pending marked token, or -1
   int32_t* n;          // [U] slots in use
   int32_t* pos;        // [U] tokens appended so far (next position)
-  int32_t* plan;       // [U][2] first work item and item count of the last attention call
-  int32_t* order;      // [U] the attention's unit order: position v holds unit order[v]
+  int32_t* plan;       // [U][2] split mode: first partial slot and item count of each unit
+  int32_t* order;      // [U] whole-unit mode: the units, work-group by work-group
+  int32_t* wg_range;   // [grid + 1] whole-unit mode: work-group g takes order[wg_range[g] .. wg_range[g+1])
   Counters* ctr;
   float* part;         // [max_items][item_floats] attention partials
-  int32_t B, Hq, Hkv, G, R, max_tokens, max_blocks, max_splits, U, item_floats, target_items;
-  int32_t whole_units;  // 1: one work item per unit (never split); no split merge
-  int32_t ordered;      // 1: the attention visits units in `order`, 0: in index order
+  int32_t B, Hq, Hkv, G, R, max_tokens, max_blocks, U, item_floats;
+  int32_t grid;        // attention work-groups of a launch (resident at once)
+  int32_t split;       // 1: split mode (the live blocks in equal shares, then reduce_kernel), 0: whole units
+  int32_t split_wgs;   // split mode: at most this many work-groups take part (<= grid)
   int64_t pool_blocks, block_bytes;
   float scale_log2e;   // attention scale times log2(e)
 };
@@ -79,6 +81,16 @@ struct LogitSrc {
 struct SoftArgs {
   int32_t B, Hq, Hkv, G, T, w;
   float gamma, inv_tau, scale_log2e, scale;
+};
+
+// Inputs of a fused decode step (zero everywhere else): the new token's K
+// and V rows [U, d], where its eviction logit is read, and the key channel
+// stored as 0 (-1: none).
+struct StepIn {
+  const uint8_t* k;
+  const uint8_t* v;
+  LogitSrc logit;
+  int32_t zero_ch;
 };
 
 // Status codes mirrored from dms.h for device code.
@@ -117,11 +129,16 @@ hipError_t launch_soft_backward(const SoftArgs& a, int d, const void* q, const v
                                 const void* dout, float* dq, float* dk, float* dv, float* dlogit, void* ws,
                                 hipStream_t s);
 hipError_t launch_export(const Dev& p, int32_t u0, int64_t f0, int64_t len, int32_t* stage, hipStream_t s);
-// Work-groups of the attention kernel that fit on the device at once.
+// Work-groups of the attention kernels that fit on the device at once.
 int attention_resident_wgs(int dtype, int d, int num_cus);
 // start / stop (may be null): events stamped with the start of the attention
-// launch and the end of the call's last launch.
-hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out,
-                            int64_t grid_wgs, hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// launch and the end of the call's last launch.  Split mode adds reduce_kernel.
+hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out, hipStream_t s,
+                            hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// One decode step: append + attention.  Whole-unit mode: one fused launch;
+// split mode: append_kernel, the attention, reduce_kernel.  start / stop as
+// launch_attention, around the step's launches.
+hipError_t launch_decode_step(const Dev& p, int dtype, int d, const void* q, const StepIn& in, float* out,
+                              hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 }  // namespace dms

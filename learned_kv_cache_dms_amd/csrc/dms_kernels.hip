@@ -51,6 +51,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <tuple>
 #include <utility>
 
@@ -82,6 +83,7 @@ static hipError_t launch_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, 
     int i = 0;
     ((ptrs[i++] = (void*)&a), ...);
   }, tup);
+  if (!start && !stop) return hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, s);
   return hipExtLaunchKernel((const void*)kernel, grid, block, ptrs, 0, s, start, stop, 0);
 }
 
@@ -127,22 +129,14 @@ __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-#ifndef DMS_PERMLANE_MAX
-#define DMS_PERMLANE_MAX 1
-#endif
 // max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups that hold
 // one MFMA column's rows).  The gfx950 permlane swaps exchange those lane
 // groups within the VALU; a shuffle would go through the LDS crossbar.
 __device__ __forceinline__ float max_over_groups(float v) {
-#if DMS_PERMLANE_MAX
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-#else
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
-#endif
 }
 
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
@@ -183,13 +177,19 @@ __global__ void init_kernel(Dev p) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t nring = (int64_t)p.U * p.R;
   for (int64_t i = tid; i < nring; i += stride) p.ring[i] = -1;
+  // whole-unit mode's default layout: work-group g takes units g, g + grid,
+  // g + 2 grid, ... (its range of the unit order starts after the units of
+  // the work-groups before it)
+  const int per = p.U / p.grid, extra = p.U % p.grid;
   for (int64_t i = tid; i < p.U; i += stride) {
     p.n[i] = 0;
     p.pos[i] = 0;
     p.plan[2 * i] = 0;
     p.plan[2 * i + 1] = 0;
-    p.order[i] = (int32_t)i;
+    const int g = (int)(i % p.grid), k = (int)(i / p.grid);
+    p.order[g * per + min(g, extra) + k] = (int32_t)i;
   }
+  for (int64_t g = tid; g <= p.grid; g += stride) p.wg_range[g] = (int32_t)(g * per + min<int64_t>(g, extra));
   if (tid == 0) {
     p.ctr->bump = 0;
     p.ctr->live_token_steps = 0;
@@ -254,42 +254,33 @@ __device__ __forceinline__ void write_fresh(uint8_t* blkp, const uint8_t* krow,
   }
 }
 
-// Appends the token at unit u's next position (one wave): decides alpha,
-// retires position q - R if it was marked (its slot is reused), stores the
-// row.  Returns the unit's live count afterwards.  Every per-unit value is
-// read through lane 0, the lane that writes it, so that consecutive calls of
-// one wave (a chunk) see their own updates in program order.
+// Stores the token at position q of unit u (one wave), once its decision and
+// destination are known: rs = the slot of position q - R if that token was
+// marked (it retires now and the new token takes its slot), else -1 (the new
+// token takes slot n); blk = the pool block of that slot, or -1 when the
+// slot starts a new block, which is then claimed from the pool (on
+// exhaustion the sticky error is set and nothing is stored).  Writes the
+// row, the slot's position and mask bit, the ring entry of q, n and pos, all
+// from lane 0 except the row.  Returns the unit's live count afterwards.
 template <int ES, int D>
-__device__ __forceinline__ unsigned append_token(const Dev& p, int u, int lane, const uint8_t* krow,
-                                                 const uint8_t* vrow, float lg, int zero_ch) {
-  const bool alpha = lg > 0.0f;  // NaN compares false
-  const int q = __builtin_amdgcn_readfirstlane(p.pos[u]);
-  const int r = q % p.R;
+__device__ __forceinline__ unsigned store_token(const Dev& p, int u, int lane, const uint8_t* krow,
+                                                const uint8_t* vrow, bool alpha, int q, int rs, int n, int blk,
+                                                int zero_ch) {
   int32_t* ring = p.ring + (int64_t)u * p.R;
-  int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
-  const int s = __builtin_amdgcn_readfirstlane(ring[r]);  // slot of position q - R if it was marked
-  const int n = __builtin_amdgcn_readfirstlane(p.n[u]);
-  int slot, blk = 0;
+  const int r = q % p.R;
+  const int slot = rs >= 0 ? rs : n;
   bool fresh = false, ok = true;
-  if (s >= 0) {  // retire position q - R, reuse its slot
-    slot = s;
-    blk = __builtin_amdgcn_readfirstlane(bt[slot >> 4]);
-  } else {
-    slot = n;
-    if ((slot & 15) == 0) {
-      unsigned long long nb = 0;
-      if (lane == 0) nb = atomicAdd(&p.ctr->bump, 1ull);
-      nb = __shfl(nb, 0);
-      if (nb >= (unsigned long long)p.pool_blocks) {
-        ok = false;
-        if (lane == 0) atomicCAS(&p.ctr->sticky_error, 0, kErrOutOfBlocks);
-      } else {
-        blk = (int)nb;
-        fresh = true;
-        if (lane == 0) bt[slot >> 4] = blk;
-      }
+  if (blk < 0) {
+    unsigned long long nb = 0;
+    if (lane == 0) nb = atomicAdd(&p.ctr->bump, 1ull);
+    nb = __shfl(nb, 0);
+    if (nb >= (unsigned long long)p.pool_blocks) {
+      ok = false;
+      if (lane == 0) atomicCAS(&p.ctr->sticky_error, 0, kErrOutOfBlocks);
     } else {
-      blk = __builtin_amdgcn_readfirstlane(bt[slot >> 4]);
+      blk = (int)nb;
+      fresh = true;
+      if (lane == 0) p.btab[(int64_t)u * p.max_blocks + (slot >> 4)] = blk;
     }
   }
   const int t = slot & 15;
@@ -304,18 +295,38 @@ __device__ __forceinline__ unsigned append_token(const Dev& p, int u, int lane, 
       p.blk_pos[(int64_t)blk * 16 + t] = q;
       if (fresh)
         p.blk_mask[blk] = 1u;
-      else if (s < 0)
+      else if (rs < 0)
         p.blk_mask[blk] |= 1u << t;
       ring[r] = alpha ? slot : -1;
-      if (s < 0) p.n[u] = n + 1;
+      if (rs < 0) p.n[u] = n + 1;
     }
-    live = (s < 0) ? (unsigned)(n + 1) : (unsigned)n;
+    live = (rs < 0) ? (unsigned)(n + 1) : (unsigned)n;
   } else {
     if (lane == 0) ring[r] = -1;
     live = (unsigned)n;
   }
   if (lane == 0) p.pos[u] = q + 1;
   return live;
+}
+
+// Appends the token at unit u's next position (one wave): decides alpha,
+// retires position q - R if it was marked (its slot is reused), stores the
+// row.  Returns the unit's live count afterwards.  Every per-unit value is
+// read through lane 0, the lane that writes it, so that consecutive calls of
+// one wave (a chunk) see their own updates in program order.
+template <int ES, int D>
+__device__ __forceinline__ unsigned append_token(const Dev& p, int u, int lane, const uint8_t* krow,
+                                                 const uint8_t* vrow, float lg, int zero_ch) {
+  const bool alpha = lg > 0.0f;  // NaN compares false
+  const int q = __builtin_amdgcn_readfirstlane(p.pos[u]);
+  const int rs = __builtin_amdgcn_readfirstlane(p.ring[(int64_t)u * p.R + q % p.R]);  // slot of q - R if marked
+  const int n = __builtin_amdgcn_readfirstlane(p.n[u]);
+  const int slot = rs >= 0 ? rs : n;
+  // the slot's block exists unless the token starts a new one
+  const int blk = (rs >= 0 || (n & 15) != 0)
+                      ? __builtin_amdgcn_readfirstlane(p.btab[(int64_t)u * p.max_blocks + (slot >> 4)])
+                      : -1;
+  return store_token<ES, D>(p, u, lane, krow, vrow, alpha, q, rs, n, blk, zero_ch);
 }
 
 // Adds each work-group's live counts to live_token_steps (one atomic).
@@ -577,66 +588,62 @@ __global__ __launch_bounds__(256) void prefill_scatter_kernel(Dev p, const uint8
 // decode attention
 // ---------------------------------------------------------------------------
 
+// A work item: plan blocks [jb, je) of one (sequence, KV head) unit, i.e. its
+// logical blocks jb .. je - 1.  A unit with no live token counts one plan
+// block and holds no real one, so that every unit belongs to some item.
 struct Item {
-  int u, k, items, base, nblk;
-  int tail;  // live slots of the unit's last block, 0 when it is full
+  int u;          // the unit
+  int nblk;       // the unit's blocks that hold live tokens
+  int tail;       // live slots of the unit's last block, 0 when it is full
+  int jb, je;     // plan blocks of the unit covered by this item
+  int pidx;       // partial slot of the item, or -1 when it is the whole unit
+  int plan_cnt;   // split mode, the unit's first item: the unit's item count, else 0
+  // fused decode step only (whole-unit mode): the token appended to the unit
+  int q;          // its position
+  int rs;         // slot of position q - w - 1 if that token was marked (it retires now), else -1
+  int tblk;       // pool block of the slot the token goes to, -1 when a fresh block is claimed
+  int alpha;      // its eviction decision
 };
 
-// Work plan, computed redundantly by every wave from the live counts n[]:
-// unit u (nblk_u blocks) gets items_u = round(nblk_u * target / total blocks)
-// work items, at least ceil(nblk_u / kMaxItemBlocks) and at most max_splits
-// (which the host keeps >= ceil(max_blocks / kMaxItemBlocks)); each item
-// holds an equal share of the unit's blocks, so the items of a launch have
-// about the same size.  Items are numbered unit-major.
-__device__ __forceinline__ int unit_items(int nb, long long tot, int target, int max_splits, bool whole) {
-  if (nb <= 0) return 0;
-  if (whole) return 1;  // at least as many units as work-groups: no split
-  // round(nb * target / tot) in double: nb <= tot and target <= kMaxTargetItems keep
-  // the quotient below 2^13, where a double quotient of these integers (exact
-  // below 2^53) is never rounded across an integer, so the floor is exact.
-  const double want = floor(((double)nb * target * 2.0 + (double)tot) / (2.0 * (double)tot));
-  const int lo = (nb + kMaxItemBlocks - 1) / kMaxItemBlocks;
-  return min(max_splits, max(lo, (int)want));
-}
-
-// The unit at position v of the attention's unit order (vector form, any v < U).
-__device__ __forceinline__ int unit_at(const Dev& p, int v) { return p.ordered ? p.order[v] : v; }
-
-__device__ __forceinline__ long long plan_blocks(const Dev& p, int lane) {
-  long long tot = 0;
-  for (int b0 = 0; b0 < p.U; b0 += 64) {
-    const int uu = b0 + lane;
-    if (uu < p.U) tot += (p.n[uu] + 15) >> 4;
-  }
+__device__ __forceinline__ uint32_t wave_incl_scan_u(uint32_t x, int lane) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
-  return max(1LL, tot);
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
 }
 
-// The plan in LDS (units <= kPlanLdsUnits), over positions v of the unit
-// order: n[v] = live slots of unit unit_at(v) and start[v] = items of the
-// positions before v (start[U] = all items).  Built once per work-group from
-// n[], which is read in one round of loads.
-struct PlanLds {
-  int start[kPlanLdsUnits + 1];
-  int n[kPlanLdsUnits];
-  long long wsum[kWavesPerWG];
-  int wtot[kWavesPerWG];
+// Split mode.  Every work-group derives the same plan from the live counts:
+// unit u counts nb_u = max(1, ceil(n_u / 16)) plan blocks, the units' plan
+// blocks lie end to end in unit order (P[u] = plan blocks of the units before
+// u, P[U] = T), and work-group g of the R taking part takes plan blocks
+// [floor(g T / R), floor((g + 1) T / R)).  Every work-group therefore streams
+// the same number of blocks, within one, whatever compression ratio each
+// head has reached.  Its items are the pieces of that range in each unit it
+// meets.  An item that is not its whole unit leaves a partial in slot u + g:
+// distinct pieces have distinct slots, and the pieces of one unit occupy
+// consecutive slots, which reduce_kernel merges.  Every unit of a split call
+// has its item count recorded by its first item (1 when it is not cut).
+struct SplitPlan {
+  uint32_t P[kPlanLdsUnits + 1];
+  int32_t n[kPlanLdsUnits];
+  uint32_t wsum[kWavesPerWG];
 };
 
 // Work-group-wide (256 threads); ends with a barrier.  n[] is read with
 // coalesced loads (unit u by thread u % 256); thread t then scans the
-// ceil(U / 256) units from t * ceil(U / 256) on.
-__device__ void plan_build_lds(const Dev& p, PlanLds& pl) {
+// ceil(U / 256) consecutive units from t * ceil(U / 256) on.  The pool holds
+// fewer than 2^31 blocks and U <= 4096, so T < 2^32.
+__device__ void split_plan_build(const Dev& p, SplitPlan& pl) {
   constexpr int kThreads = 64 * kWavesPerWG;
   constexpr int kPer = kPlanLdsUnits / kThreads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int U = p.U;
-  // Unconditional loads with clamped indices, so that they all issue before
-  // the first wait.
+  // unconditional loads with clamped indices, so that all issue before the first wait
   int x[kPer];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) x[k] = p.n[unit_at(p, min(tid + kThreads * k, U - 1))];
+  for (int k = 0; k < kPer; ++k) x[k] = p.n[min(tid + kThreads * k, U - 1)];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int u = tid + kThreads * k;
@@ -645,106 +652,131 @@ __device__ void plan_build_lds(const Dev& p, PlanLds& pl) {
   __syncthreads();
   const int per = (U + kThreads - 1) / kThreads;  // <= kPer
   const int u0 = tid * per;
-  int nb[kPer];
-  int s = 0;  // <= 16 units x 2^20 blocks
+  uint32_t nb[kPer];
+  uint32_t s = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    nb[k] = (k < per && u0 + k < U) ? (pl.n[u0 + k] + 15) >> 4 : 0;
+    nb[k] = (k < per && u0 + k < U) ? (uint32_t)max(1, (pl.n[u0 + k] + 15) >> 4) : 0u;
     s += nb[k];
   }
-  const long long sw = wave_sum_ll((long long)s);
-  if (lane == 0) pl.wsum[wave] = sw;
+  const uint32_t incl = wave_incl_scan_u(s, lane);
+  if (lane == 63) pl.wsum[wave] = incl;
   __syncthreads();
-  long long tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWavesPerWG; ++w) tot += pl.wsum[w];
-  tot = max(1LL, tot);
-  int cnt[kPer];
-  int c = 0;
+  uint32_t run = incl - s;
+  for (int w = 0; w < wave; ++w) run += pl.wsum[w];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    cnt[k] = unit_items(nb[k], tot, p.target_items, p.max_splits, p.whole_units != 0);
-    c += cnt[k];
+    if (k < per && u0 + k < U) pl.P[u0 + k] = run;
+    run += nb[k];
   }
-  const int incl = wave_incl_scan_i(c, lane);
-  if (lane == 63) pl.wtot[wave] = incl;
-  __syncthreads();
-  int run = incl - c;
-  for (int w = 0; w < wave; ++w) run += pl.wtot[w];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    if (k < per && u0 + k < U) pl.start[u0 + k] = run;
-    run += cnt[k];
-  }
-  if (tid == kThreads - 1) pl.start[U] = run;  // the last thread's running sum is the total
+  if (tid == kThreads - 1) pl.P[U] = run;  // the last thread's running sum is the total
   __syncthreads();
 }
 
-// Finds work item `item` in the LDS plan; false when item >= the total.  The
-// unit is the last u with start[u] <= item, found by a 64-way search (two
-// rounds for 4096 units).
-__device__ __forceinline__ bool plan_lookup_lds(const Dev& p, const PlanLds& pl, int U, int item, int lane,
-                                                Item& it) {
-  // readfirstlane: the compiler does not know an LDS value is uniform, and a
-  // branch on it would make every item value a per-lane (vector) value
-  if (item >= __builtin_amdgcn_readfirstlane(pl.start[U])) return false;
+// The last unit u with P[u] <= b (b < T), by a 64-way search (two rounds for
+// 4096 units).  P is strictly increasing and P[0] = 0.
+__device__ __forceinline__ int split_unit_at(const SplitPlan& pl, int U, uint32_t b, int lane) {
   int lo = 0, len = U;
   while (len > 64) {
     const int step = (len + 63) >> 6;
     const int off = lane * step;
-    const int v = off < len ? pl.start[lo + off] : 0x7fffffff;
-    const unsigned long long bal = __ballot(v <= item);  // non-empty: start[lo] <= item
+    const unsigned long long bal = __ballot(off < len && pl.P[lo + off] <= b);  // bit 0 is always set
     const int k = 63 - __clzll((long long)bal);
     lo += k * step;
     len = min(step, len - k * step);
   }
-  const int v = lane < len ? pl.start[lo + lane] : 0x7fffffff;
-  const unsigned long long bal = __ballot(v <= item);
-  const int u = __builtin_amdgcn_readfirstlane(lo + 63 - __clzll((long long)bal));
-  it.u = p.ordered ? __builtin_amdgcn_readfirstlane(p.order[u]) : u;
-  it.base = __builtin_amdgcn_readfirstlane(pl.start[u]);
-  it.items = __builtin_amdgcn_readfirstlane(pl.start[u + 1]) - it.base;
+  const unsigned long long bal = __ballot(lane < len && pl.P[lo + lane] <= b);
+  return __builtin_amdgcn_readfirstlane(lo + 63 - __clzll((long long)bal));
+}
+
+// One work-group's share of a call: in split mode its range of plan blocks,
+// in whole-unit mode its range of the unit order.
+struct Share {
+  int g;               // work-group index
+  int R;               // split: work-groups taking part
+  uint32_t T, b0, b1;  // split: total plan blocks, this work-group's [b0, b1)
+  int u0;              // split: the unit holding plan block b0
+  int w0, w1;          // whole-unit: the units order[w0 .. w1)
+};
+
+// The k-th item of a work-group in split mode; false past its range.
+__device__ __forceinline__ bool split_item(const Dev& p, const SplitPlan& pl, const Share& s, int k, Item& it) {
+  const int u = s.u0 + k;
+  if (u >= p.U) return false;
+  // readfirstlane: the compiler does not know an LDS value is uniform, and a
+  // branch on it would make every item value a per-lane (vector) value
+  const uint32_t pu = __builtin_amdgcn_readfirstlane(pl.P[u]);
+  if (pu >= s.b1) return false;
+  const uint32_t pe = __builtin_amdgcn_readfirstlane(pl.P[u + 1]);
   const int n = __builtin_amdgcn_readfirstlane(pl.n[u]);
+  it.u = u;
   it.nblk = (n + 15) >> 4;
   it.tail = n & 15;
-  it.k = item - it.base;
+  it.jb = (int)(max(s.b0, pu) - pu);
+  it.je = (int)(min(s.b1, pe) - pu);
+  it.pidx = (it.jb == 0 && it.je == (int)(pe - pu)) ? -1 : u + s.g;
+  // the work-group holding the unit's last plan block: the largest g with
+  // floor(g T / R) <= pe - 1
+  const int glast = (int)(((uint64_t)pe * (uint64_t)s.R - 1ull) / s.T);
+  it.plan_cnt = it.jb == 0 ? glast - s.g + 1 : 0;
+  it.q = 0;
+  it.rs = -1;
+  it.tblk = -1;
+  it.alpha = 0;
   return true;
 }
 
-// Position of a search through the plan: units before b0 hold `running` items.
-struct PlanCursor {
-  int b0 = 0, running = 0;
-};
+// A load of a uniform address through the scalar cache (constant address
+// space): the address must not be written by this kernel before the load.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ __forceinline__ int scalar_load(const int32_t* a) { return *(const_i32*)(uintptr_t)a; }
 
-// Finds work item `item`; false when item >= the plan's total.  The cursor
-// resumes the search where the previous one stopped, so a work-group that
-// visits increasing items scans n[] once in total.
-__device__ __forceinline__ bool plan_find(const Dev& p, int lane, long long tot, int item, Item& it,
-                                          PlanCursor& cur) {
-  for (; cur.b0 < p.U && cur.running <= item; cur.b0 += 64) {
-    const int uu = cur.b0 + lane;
-    int nb = 0, cnt = 0, nn = 0;
-    if (uu < p.U) {
-      nn = p.n[unit_at(p, uu)];
-      nb = (nn + 15) >> 4;
-      cnt = unit_items(nb, tot, p.target_items, p.max_splits, p.whole_units != 0);
-    }
-    const int incl = wave_incl_scan_i(cnt, lane);
-    const int start = cur.running + incl - cnt;
-    const unsigned long long bal = __ballot(item >= start && item < start + cnt);
-    if (bal) {
-      const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)bal) - 1);
-      it.u = unit_at(p, cur.b0 + src);
-      it.base = __builtin_amdgcn_readlane(start, src);
-      it.items = __builtin_amdgcn_readlane(cnt, src);
-      it.nblk = __builtin_amdgcn_readlane(nb, src);
-      it.tail = __builtin_amdgcn_readlane(nn, src) & 15;
-      it.k = item - it.base;
-      return true;  // the cursor stays on this group: later items may fall in it
-    }
-    cur.running += __builtin_amdgcn_readlane(incl, 63);
+// The eviction logit of unit (b, h) of a one-token step, as a scalar load of
+// the aligned dword that holds it (an exact upcast for bf16).
+__device__ __forceinline__ float scalar_logit(const LogitSrc& ls, int b, int h) {
+  const int64_t e = (int64_t)b * ls.sb + (int64_t)h * ls.sh + ls.off;
+  if (ls.bf16) {
+    const int64_t byte = e * 2;
+    const unsigned w = (unsigned)scalar_load((const int32_t*)((const uint8_t*)ls.base + (byte & ~(int64_t)3)));
+    return __uint_as_float(((byte & 2) ? (w >> 16) : (w & 0xffffu)) << 16);
   }
-  return false;
+  return __int_as_float(scalar_load((const int32_t*)ls.base + e));
+}
+
+// The k-th item of a work-group in whole-unit mode: a whole unit, the next
+// of its range of the unit order; false past the range.  FUSED: also the
+// state the unit's append needs, read before this kernel writes any of it
+// (only the work-group that owns a unit writes its state, after its items'
+// setup).
+template <bool FUSED>
+__device__ __forceinline__ bool whole_item(const Dev& p, const Share& s, int k, const LogitSrc& logit, Item& it) {
+  const int i = s.w0 + k;
+  if (i >= s.w1) return false;
+  const int u = scalar_load(p.order + i);
+  const int n = scalar_load(p.n + u);
+  it.u = u;
+  it.nblk = (n + 15) >> 4;
+  it.tail = n & 15;
+  it.jb = 0;
+  it.je = it.nblk;
+  it.pidx = -1;
+  it.plan_cnt = 0;
+  it.q = 0;
+  it.rs = -1;
+  it.tblk = -1;
+  it.alpha = 0;
+  if constexpr (FUSED) {
+    const int q = scalar_load(p.pos + u);
+    const int rs = scalar_load(p.ring + (int64_t)u * p.R + q % p.R);
+    const int slot = rs >= 0 ? rs : n;
+    it.q = q;
+    it.rs = rs;
+    // the slot's block exists unless the token starts a new one
+    it.tblk = (rs >= 0 || (n & 15) != 0) ? scalar_load(p.btab + (int64_t)u * p.max_blocks + (slot >> 4)) : -1;
+    const int b = u / p.Hkv;
+    it.alpha = scalar_logit(logit, b, u - b * p.Hkv) > 0.0f ? 1 : 0;  // NaN compares false
+  }
+  return true;
 }
 
 template <int ES, int D>
@@ -838,10 +870,6 @@ __device__ __forceinline__ void attend_block(const Frag<ES, D>& f, const u32x4 (
 // operand of channel tile j is therefore 8 bytes of block A next to 8 bytes
 // of block B, and it is loaded straight into that order.  For fp32 the pair
 // is two blocks computed one after the other.
-#ifndef DMS_PF_LAZY
-#define DMS_PF_LAZY 1
-#endif
-
 template <int ES, int D>
 struct PairFrag {
   Frag<ES, D> a, b;
@@ -936,7 +964,6 @@ __device__ __forceinline__ void softmax_pv_masked(const PairFrag<2, D>& f, const
 #pragma unroll
   for (int r = 0; r < 8; ++r) pr[r] = exp2_fast(fmaf(s[r], sl2e, -mref));
   const float psum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-#if DMS_PF_LAZY
   // Rescale only when some column's running max moved (after the first
   // blocks it rarely does).  An unmoved max gives alpha = 1 exactly; a
   // column with no key yet has o = l = 0, which any alpha leaves at 0.
@@ -947,12 +974,6 @@ __device__ __forceinline__ void softmax_pv_masked(const PairFrag<2, D>& f, const
     for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
   }
   a.l += psum;
-#else
-  const float alpha = exp2_fast(a.m - mref);
-  a.l = a.l * alpha + psum;
-#pragma unroll
-  for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
-#endif
   a.m = mn;
   unsigned hi[4], lo[4];
 #pragma unroll
@@ -983,22 +1004,37 @@ __device__ __forceinline__ void attend_pair(const PairFrag<ES, D>& f, const u32x
   }
 }
 
-// Split-K decode attention.  A work item is a run of one (sequence, KV
-// head)'s blocks, processed by one work-group of 4 waves: wave w takes the
-// run's blocks w, w+4, w+8, ... so the work-group streams one contiguous run.
-// The waves' softmax states are merged through LDS; a unit held by a single
-// work item writes its output there, otherwise the merged partial goes to
+// Decode attention.  A work item is a run of one (sequence, KV head)'s
+// blocks, processed by one work-group of 4 waves: wave w takes the run's
+// blocks w, w+4, w+8, ... so the work-group streams one contiguous run.  The
+// waves' softmax states are merged through LDS; an item that is its whole
+// unit writes the output there, otherwise the merged partial goes to
 // reduce_kernel.
 //
 // The loads do not stop at item boundaries.  While a wave computes item A it
 // already holds the block ids of its next item B, and the loads that run past
 // A's last block fetch B's first two blocks; the LDS merge of A overlaps
 // them.
-template <int ES, int D>
+//
+// FUSED (the decode step in whole-unit mode): each work-group also appends
+// the new token of every unit it owns.  The attention reads the cache as it
+// was before the step, without the slot of the token that retires now, and
+// takes the new token from the step's input rows; the append's stores land
+// in slots no one reads during the launch.  So the visible set is the one
+// after the append, Vis(q) = Vis(q - 1) - {q - w - 1 if marked} + {q}, with
+// no ordering between work-groups.
+template <int ES, int D, bool FUSED>
 struct AttnShared {
+  // staging buffers of the per-item inputs (Q, and the new K/V row when
+  // FUSED): the next item's are stored while the current one streams; the
+  // fused append reads the current item's after the merge, so a third
+  // buffer keeps them from being overwritten meanwhile
+  static constexpr int kBufs = FUSED ? 3 : 2;
+  static constexpr int kRowPieces = 2 * D * ES / 16;  // 16-byte pieces of the K row then the V row
   f32x4 o[kWavesPerWG][Geo<ES, D>::kTiles][64];
   float m[kWavesPerWG][16], l[kWavesPerWG][16];
-  u32x4 q[2][Geo<ES, D>::kChunks][64];  // Q fragments of the current and the next item
+  u32x4 q[kBufs][Geo<ES, D>::kChunks][64];  // Q fragments
+  u32x4 row[FUSED ? kBufs : 1][kRowPieces];  // the new token's K then V row (FUSED)
 };
 
 // One work item as one wave sees it.  Block ids are read through the scalar
@@ -1014,12 +1050,11 @@ struct WaveItem {
   int cnt;       // this wave's blocks: the unit's blocks j0 + 4i, i < cnt
   int vs;        // visit stride: the wave's i-th load is its block (i * vs) mod cnt
   int pf0, pf1;  // pool ids of the first two blocks visited (pool block 0 if absent)
+  int rj;        // FUSED: logical block of the retiring slot (masked out), else -1
+  uint32_t rbit; // its bit in that block's mask
+  int q, rs, tblk, alpha;  // FUSED: the unit's append (Item)
+  int n;         // the unit's live slots before the step
 };
-
-// A load of a uniform address that no kernel writes while this one runs, read
-// through the scalar cache (constant address space).
-typedef const __attribute__((address_space(4))) int32_t const_i32;
-__device__ __forceinline__ int scalar_load(const int32_t* a) { return *(const_i32*)(uintptr_t)a; }
 
 __device__ __forceinline__ int padded3(int c) { return (c + 2) / 3 * 3; }
 
@@ -1055,28 +1090,32 @@ __device__ __forceinline__ int wave_item_id(const int32_t* __restrict__ btab, in
   return scalar_load(btab + (int64_t)w.u * max_blocks + j);
 }
 
-// Sets up item `it` for this wave; the first wave of the unit's first item
-// also records the unit's item range for reduce_kernel.
+// Sets up item `it` for this wave; in split mode the first wave of a unit's
+// first item also records the unit's item range for reduce_kernel.
 __device__ __forceinline__ void wave_item_setup(const Dev& p, const int32_t* __restrict__ btab, int wave, int lane,
                                                 const Item& it, WaveItem& w) {
-  // k < items <= max_splits <= 2^11 and nblk <= 2^20: the products fit 32 bits unsigned
-  const int jb = (int)((unsigned)it.k * (unsigned)it.nblk / (unsigned)it.items);
-  const int je = (int)((unsigned)(it.k + 1) * (unsigned)it.nblk / (unsigned)it.items);
   // readfirstlane: all of these are uniform, and must live in scalar
-  // registers (the division is expanded with vector instructions), or the
-  // block-id loads computed from them would be vector loads
+  // registers, or the block-id loads computed from them would be vector loads
+  const int je = min(it.je, it.nblk);  // plan blocks past the live ones (an empty unit's) load nothing
   w.u = __builtin_amdgcn_readfirstlane(it.u);
   w.nblk = __builtin_amdgcn_readfirstlane(it.nblk);
   w.tail = __builtin_amdgcn_readfirstlane(it.tail);
-  w.pidx = __builtin_amdgcn_readfirstlane(it.items == 1 ? -1 : it.base + it.k);
-  w.j0 = __builtin_amdgcn_readfirstlane(jb + wave);
-  w.cnt = __builtin_amdgcn_readfirstlane(max(0, (je - jb - wave + kWavesPerWG - 1) / kWavesPerWG));
+  w.pidx = __builtin_amdgcn_readfirstlane(it.pidx);
+  w.j0 = __builtin_amdgcn_readfirstlane(it.jb + wave);
+  w.cnt = __builtin_amdgcn_readfirstlane(max(0, (je - it.jb - wave + kWavesPerWG - 1) / kWavesPerWG));
   w.vs = visit_stride(w.cnt);
   w.pf0 = w.cnt > 0 ? wave_item_id(btab, p.max_blocks, w, 0) : 0;
   w.pf1 = w.cnt > 1 ? wave_item_id(btab, p.max_blocks, w, 1) : 0;
-  if (it.k == 0 && it.nblk > 0 && wave == 0 && lane == 0) {
-    p.plan[2 * it.u] = it.base;
-    p.plan[2 * it.u + 1] = it.items;
+  w.rj = __builtin_amdgcn_readfirstlane(it.rs >= 0 ? (it.rs >> 4) : -1);
+  w.rbit = 1u << (it.rs & 15);
+  w.q = __builtin_amdgcn_readfirstlane(it.q);
+  w.rs = __builtin_amdgcn_readfirstlane(it.rs);
+  w.tblk = __builtin_amdgcn_readfirstlane(it.tblk);
+  w.alpha = __builtin_amdgcn_readfirstlane(it.alpha);
+  w.n = __builtin_amdgcn_readfirstlane(it.nblk > 0 ? (it.nblk - 1) * 16 + (it.tail ? it.tail : 16) : 0);
+  if (it.plan_cnt > 0 && wave == 0 && lane == 0) {
+    p.plan[2 * it.u] = it.pidx < 0 ? 0 : it.pidx;
+    p.plan[2 * it.u + 1] = it.plan_cnt;
   }
 }
 
@@ -1092,32 +1131,45 @@ __device__ __forceinline__ void wave_item_none(WaveItem& w) {
   w.vs = 0;
   w.pf0 = 0;
   w.pf1 = 0;
+  w.rj = -1;
+  w.rbit = 0;
+  w.q = 0;
+  w.rs = -1;
+  w.tblk = -1;
+  w.alpha = 0;
+  w.n = 0;
 }
 
 // Live-slot mask of this wave's i-th visited block of item w.  Live slots are
 // always the dense prefix [0, n) of the unit's slots (an append reuses the
 // slot it retires or takes slot n; prefill assigns 0 .. n-1), so only the
-// unit's last block can be partly filled.
+// unit's last block can be partly filled.  FUSED: the retiring slot is
+// masked out as well.
+template <bool FUSED>
 __device__ __forceinline__ uint32_t wave_item_mask(const WaveItem& w, int i) {
   const int j = w.j0 + kWavesPerWG * visit_pos(w, i);
-  return (j == w.nblk - 1 && w.tail != 0) ? ((1u << w.tail) - 1u) : 0xffffu;
+  uint32_t m = (j == w.nblk - 1 && w.tail != 0) ? ((1u << w.tail) - 1u) : 0xffffu;
+  if constexpr (FUSED) m &= (j == w.rj) ? ~w.rbit : 0xffffffffu;
+  return m;
 }
 
-// Q fragment (B operand of S = K Q^T): head g = lane % 16 of the item's
-// group, the channels this lane's K fragment elements carry.  It goes through
-// LDS: wave w loads chunks w, w+4, ... of the next item's fragment while the
-// current item streams, stores them before the merge, and every wave reads
-// the whole fragment after it.  No wait for a K/V load is ever also a wait
-// for Q, nor the other way round.
-template <int ES, int D>
+// Per-item inputs, staged through LDS: wave w loads chunks w, w+4, ... of the
+// next item's Q fragment (B operand of S = K Q^T: head g = lane % 16 of the
+// item's group, the channels this lane's K fragment elements carry) while
+// the current item streams, and, when FUSED, the pieces of the new token's
+// K and V rows.  The pieces are stored before the merge and read after it.
+// No wait for a K/V load is ever also a wait for these, nor the other way
+// round.
+template <int ES, int D, bool FUSED>
 struct QPart {
   static constexpr int kN = (Geo<ES, D>::kChunks + kWavesPerWG - 1) / kWavesPerWG;
   u32x4 v[kN];
+  u32x4 row;  // FUSED: piece min(lane, kRowPieces - 1) of the new K row then V row
 };
 
-template <int ES, int D>
-__device__ __forceinline__ void load_q_part(const Dev& p, const uint8_t* __restrict__ q, int u, int lane,
-                                            int wave, QPart<ES, D>& part) {
+template <int ES, int D, bool FUSED>
+__device__ __forceinline__ void load_q_part(const Dev& p, const uint8_t* __restrict__ q, const StepIn& in, int u,
+                                            int lane, int wave, QPart<ES, D, FUSED>& part) {
   using G = Geo<ES, D>;
   const int b = u / p.Hkv, h = u - b * p.Hkv;
   const int g = lane & 15;
@@ -1125,58 +1177,79 @@ __device__ __forceinline__ void load_q_part(const Dev& p, const uint8_t* __restr
   // an independent softmax, and those columns are never written out.
   const uint8_t* qrow = q + ((int64_t)b * p.Hq + h * p.G + (g < p.G ? g : 0)) * D * ES;
 #pragma unroll
-  for (int j = 0; j < QPart<ES, D>::kN; ++j) {
+  for (int j = 0; j < QPart<ES, D, FUSED>::kN; ++j) {
     const int c = min(wave + kWavesPerWG * j, G::kChunks - 1);
     part.v[j] = *(const u32x4*)(qrow + (c * 4 * G::kE + G::kE * (lane >> 4)) * ES);
   }
+  if constexpr (FUSED) {
+    constexpr int kRowPieces = AttnShared<ES, D, FUSED>::kRowPieces;
+    constexpr int kHalf = kRowPieces / 2;
+    const int r = min(lane, kRowPieces - 1);
+    const uint8_t* src = r < kHalf ? in.k + (int64_t)u * D * ES + r * 16 : in.v + (int64_t)u * D * ES + (r - kHalf) * 16;
+    part.row = *(const u32x4*)src;
+    if (r < kHalf) clear_channel<ES>(part.row, r, in.zero_ch);
+  }
 }
 
-template <int ES, int D>
-__device__ __forceinline__ void store_q_part(AttnShared<ES, D>& sh, int buf, int lane, int wave,
-                                             const QPart<ES, D>& part) {
+template <int ES, int D, bool FUSED>
+__device__ __forceinline__ void store_q_part(AttnShared<ES, D, FUSED>& sh, int buf, int lane, int wave,
+                                             const QPart<ES, D, FUSED>& part) {
   // Clamped like the load: waves past the last chunk store that chunk again,
   // with the same values (an unconditional store keeps the load waits exact).
 #pragma unroll
-  for (int j = 0; j < QPart<ES, D>::kN; ++j)
+  for (int j = 0; j < QPart<ES, D, FUSED>::kN; ++j)
     sh.q[buf][min(wave + kWavesPerWG * j, Geo<ES, D>::kChunks - 1)][lane] = part.v[j];
+  // every wave stores the same row pieces
+  if constexpr (FUSED) sh.row[buf][min(lane, AttnShared<ES, D, FUSED>::kRowPieces - 1)] = part.row;
 }
 
-template <int ES, int D>
-__device__ __forceinline__ void read_q(const AttnShared<ES, D>& sh, int buf, int lane,
+template <int ES, int D, bool FUSED>
+__device__ __forceinline__ void read_q(const AttnShared<ES, D, FUSED>& sh, int buf, int lane,
                                        u32x4 (&qf)[Geo<ES, D>::kChunks]) {
 #pragma unroll
   for (int c = 0; c < Geo<ES, D>::kChunks; ++c) qf[c] = sh.q[buf][c][lane];
 }
 
-// Item `item` in whole-unit mode: the unit at that position of the unit
-// order, whole.  Every unit holds at least its newest token whenever an
-// attention is allowed, so no unit is skipped and no plan is needed.  (A unit
-// left empty by an exhausted pool becomes an item with no blocks, for which
-// merge_item writes nothing.)
-__device__ __forceinline__ bool whole_item(const Dev& p, int item, Item& it) {
-  if (item >= p.U) return false;
-  it.u = p.ordered ? scalar_load(p.order + item) : item;
-  const int n = scalar_load(p.n + it.u);
-  it.nblk = (n + 15) >> 4;
-  it.tail = n & 15;
-  it.base = item;
-  it.items = 1;
-  it.k = 0;
-  return true;
+__device__ __forceinline__ float sum_over_groups(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
 }
 
-// The item lookup: direct in whole-unit mode, else the LDS plan, or for very
-// many units a scan of n[].
-struct Planner {
-  bool whole, lds;
-  long long tot;
-  PlanCursor cur;
-};
+// Raw score <q_g, k_new> of the new token for head g = lane % 16 (every lane
+// of the head gets it): each lane multiplies the channels of its Q fragment
+// with the same channels of the staged K row, then the four lane groups add.
+template <int ES, int D>
+__device__ __forceinline__ float new_token_score(const u32x4* krow, const u32x4 (&qf)[Geo<ES, D>::kChunks],
+                                                 int lane) {
+  using G = Geo<ES, D>;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) {
+    const u32x4 kk = krow[c * 4 + (lane >> 4)];  // channels c * 4E + E * (lane / 16) + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (ES == 2) {
+        acc = fmaf(bf16_lo_to_f32(qf[c][e]), bf16_lo_to_f32(kk[e]), acc);
+        acc = fmaf(bf16_hi_to_f32(qf[c][e]), bf16_hi_to_f32(kk[e]), acc);
+      } else {
+        acc = fmaf(__uint_as_float(qf[c][e]), __uint_as_float(kk[e]), acc);
+      }
+    }
+  }
+  return sum_over_groups(acc);
+}
 
-__device__ __forceinline__ bool find_item(const Dev& p, const PlanLds& pl, Planner& pn, int item, int lane,
-                                          Item& it) {
-  if (pn.whole) return whole_item(p, item, it);
-  return pn.lds ? plan_lookup_lds(p, pl, p.U, item, lane, it) : plan_find(p, lane, pn.tot, item, it, pn.cur);
+// Channels 16 j + 4 (lane / 16) + r (r < 4) of the staged V row, as fp32.
+template <int ES, int D>
+__device__ __forceinline__ f32x4 new_token_values(const u32x4* vrow_pieces, int j, int lane) {
+  const uint8_t* vrow = (const uint8_t*)vrow_pieces;
+  const int ch = 16 * j + 4 * (lane >> 4);
+  if constexpr (ES == 2) {
+    const u32x2 w = *(const u32x2*)(vrow + ch * 2);
+    return f32x4{bf16_lo_to_f32(w[0]), bf16_hi_to_f32(w[0]), bf16_lo_to_f32(w[1]), bf16_hi_to_f32(w[1])};
+  } else {
+    return *(const f32x4*)(vrow + ch * 4);
+  }
 }
 
 // Computes this wave's blocks of item A.  The wave reads one stream of
@@ -1186,7 +1259,7 @@ __device__ __forceinline__ bool find_item(const Dev& p, const PlanLds& pl, Plann
 // there.  Padding slots, and stream positions past B, load pool block 0 (any
 // valid address does) and are not computed.  When A has no blocks, buffers 0
 // and 1 were filled before B was known and are loaded again here.
-template <int ES, int D, typename Early>
+template <int ES, int D, bool FUSED, typename Early>
 __device__ __forceinline__ void run_item(const Dev& p, Frag<ES, D>& f0, Frag<ES, D>& f1, Frag<ES, D>& f2,
                                          const WaveItem& A, const WaveItem& B,
                                          const u32x4 (&qf)[Geo<ES, D>::kChunks], int lane, Acc<D>& acc,
@@ -1220,11 +1293,11 @@ __device__ __forceinline__ void run_item(const Dev& p, Frag<ES, D>& f0, Frag<ES,
       n4 = wave_item_id(btab, p.max_blocks, A, i + 7);
     }
     fetch(f2, b2);
-    attend_block<ES, D>(f0, qf, wave_item_mask(A, i), lane, sl2e, acc);
+    attend_block<ES, D>(f0, qf, wave_item_mask<FUSED>(A, i), lane, sl2e, acc);
     fetch(f0, b3);
-    if (i + 1 < cnt) attend_block<ES, D>(f1, qf, wave_item_mask(A, i + 1), lane, sl2e, acc);
+    if (i + 1 < cnt) attend_block<ES, D>(f1, qf, wave_item_mask<FUSED>(A, i + 1), lane, sl2e, acc);
     fetch(f1, b4);
-    if (i + 2 < cnt) attend_block<ES, D>(f2, qf, wave_item_mask(A, i + 2), lane, sl2e, acc);
+    if (i + 2 < cnt) attend_block<ES, D>(f2, qf, wave_item_mask<FUSED>(A, i + 2), lane, sl2e, acc);
   };
   // The first group is peeled: it is the one that waits for the item's Q
   // (loaded after blocks 0 and 1), and keeping that wait out of the loop
@@ -1244,17 +1317,19 @@ __device__ __forceinline__ void run_item(const Dev& p, Frag<ES, D>& f0, Frag<ES,
 }
 
 // Merges the four waves' states of item `it` through LDS and writes the
-// output (single-item unit) or the item's partial.  Contains two work-group
-// barriers; LDS stores made before the call (the next item's Q) are visible to
-// every wave on return.
-template <int ES, int D>
+// output (an item that is its whole unit) or the item's partial.  FUSED: the
+// new token (staged in buffer `buf`) joins the merge as one more key.
+// Contains two work-group barriers; LDS stores made before the call (the next
+// item's staged inputs) are visible to every wave on return.
+template <int ES, int D, bool FUSED>
 __device__ __forceinline__ void merge_item(const Dev& p, float* __restrict__ out, const WaveItem& it,
-                                           const Acc<D>& acc, int lane, int wave, AttnShared<ES, D>& sh) {
+                                           const Acc<D>& acc, int lane, int wave, AttnShared<ES, D, FUSED>& sh,
+                                           int buf, const u32x4 (&qf)[Geo<ES, D>::kChunks]) {
   using G = Geo<ES, D>;
   constexpr int kW = kWavesPerWG;
   constexpr int kTilesPerWave = (G::kTiles + kW - 1) / kW;
-  if (it.nblk == 0) {  // a unit with no live token (uniform): nothing to write
-    __syncthreads();    // but the next item's Q must still be visible on return
+  if (!FUSED && it.nblk == 0) {  // a unit with no live token (uniform): nothing to write
+    __syncthreads();             // but the next item's Q must still be visible on return
     return;
   }
   const int u = it.u;
@@ -1276,6 +1351,13 @@ __device__ __forceinline__ void merge_item(const Dev& p, float* __restrict__ out
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kW; ++w) M = fmaxf(M, sh.m[w][g]);
+  // wave w finishes tiles w * kTilesPerWave ...
+  const int j0 = wave * kTilesPerWave;
+  float sn = -INFINITY;
+  if constexpr (FUSED) {
+    sn = new_token_score<ES, D>(&sh.row[buf][0], qf, lane) * p.scale_log2e;
+    M = fmaxf(M, sn);
+  }
   const float Mr = (M == -INFINITY) ? 0.f : M;
   float wt[kW];
   float L = 0.f;
@@ -1284,8 +1366,6 @@ __device__ __forceinline__ void merge_item(const Dev& p, float* __restrict__ out
     wt[w] = exp2_fast(sh.m[w][g] - Mr);
     L += wt[w] * sh.l[w][g];
   }
-  // wave w finishes tiles w * kTilesPerWave ...
-  const int j0 = wave * kTilesPerWave;
   f32x4 O[kTilesPerWave];
 #pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) {
@@ -1294,6 +1374,14 @@ __device__ __forceinline__ void merge_item(const Dev& p, float* __restrict__ out
 #pragma unroll
       for (int w = 0; w < kW; ++w) O[t] += wt[w] * sh.o[w][j0 + t][lane];
     }
+  }
+  if constexpr (FUSED) {
+    const float wn = exp2_fast(sn - Mr);
+    L += wn;
+#pragma unroll
+    for (int t = 0; t < kTilesPerWave; ++t)
+      if (j0 + t < G::kTiles)
+        O[t] += wn * new_token_values<ES, D>(&sh.row[buf][AttnShared<ES, D, FUSED>::kRowPieces / 2], j0 + t, lane);
   }
   __syncthreads();  // the LDS of this item may be overwritten after this
   if (it.pidx < 0) {
@@ -1320,52 +1408,77 @@ __device__ __forceinline__ void merge_item(const Dev& p, float* __restrict__ out
   }
 }
 
-// Persistent launch: one work-group per resident slot; work-group b takes
-// items b, b + G, b + 2G, ... (G = grid size).  The plan makes items of about
-// equal size (in whole-unit mode each unit is one item, found without a
-// plan), so the static assignment is balanced, and the next item is known in
-// advance: its block ids are read while the item before it is computed.
+// Persistent launch: one work-group per resident slot.  Whole-unit mode:
+// work-group g takes the units of its range of the unit order, each as one
+// item (the host deals the units so that the ranges carry about equal live
+// blocks).  Split mode: it takes its equal share of all plan blocks, cut at
+// unit boundaries (SplitPlan).  Either way each work-group knows its next item
+// in advance: its block ids are read while the item before it is computed.
 //
 // The loop is written so that the compiler's load-counter waits stay exact:
 // every load is unconditional (an absent next item is an empty one on unit
 // 0), block ids come through the scalar cache, and values loaded before an
 // item's block loop are consumed right after its first group of loads.  A
 // wait for one value then never drains the K/V blocks in flight behind it.
-template <int ES, int D>
+template <int ES, int D, bool FUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2 : 1))) void attention_kernel(
-    Dev p, const int32_t* __restrict__ btab, const uint8_t* __restrict__ q, float* __restrict__ out) {
+    Dev p, const int32_t* __restrict__ btab, const uint8_t* __restrict__ q, float* __restrict__ out, StepIn in) {
   using G = Geo<ES, D>;
-  __shared__ AttnShared<ES, D> sh;
-  __shared__ PlanLds pl;
+  __shared__ AttnShared<ES, D, FUSED> sh;
+  // the fused step runs in whole-unit mode only: no split plan
+  __shared__ typename std::conditional<FUSED, int, SplitPlan>::type pl;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  Planner pn;
-  pn.whole = p.whole_units != 0;
-  pn.lds = p.U <= kPlanLdsUnits;
-  pn.tot = 0;
-  if (!pn.whole) {
-    if (pn.lds)
-      plan_build_lds(p, pl);
-    else
-      pn.tot = plan_blocks(p, lane);
+  Share s;
+  s.g = blockIdx.x;
+  s.R = 1;
+  s.T = 1;
+  s.b0 = 0;
+  s.b1 = 0;
+  s.u0 = 0;
+  s.w0 = 0;
+  s.w1 = 0;
+  bool split = false;
+  if constexpr (!FUSED) {
+    split = p.split != 0;
+    if (split) {
+      split_plan_build(p, pl);
+      const uint32_t T = __builtin_amdgcn_readfirstlane(pl.P[p.U]);
+      const int R = (int)min((uint32_t)p.split_wgs, (T + kMinSplitBlocks - 1) / kMinSplitBlocks);
+      if (s.g >= R) return;  // uniform over the work-group
+      s.R = R;
+      s.T = T;
+      s.b0 = (uint32_t)((uint64_t)s.g * T / (uint64_t)R);
+      s.b1 = (uint32_t)((uint64_t)(s.g + 1) * T / (uint64_t)R);
+      s.u0 = split_unit_at(pl, p.U, s.b0, lane);
+    }
   }
+  if (!split) {
+    s.w0 = scalar_load(p.wg_range + s.g);
+    s.w1 = scalar_load(p.wg_range + s.g + 1);
+  }
+  auto find_item = [&](int k, Item& it) -> bool {
+    if constexpr (!FUSED) {
+      if (split) return split_item(p, pl, s, k, it);
+    }
+    return whole_item<FUSED>(p, s, k, in.logit, it);
+  };
 
-  const int grid = (int)gridDim.x;
-  int item = blockIdx.x;
+  int k = 0;
   WaveItem W0, W1;
-  QPart<ES, D> q0;
+  QPart<ES, D, FUSED> q0;
   {
     Item it;
-    if (!find_item(p, pl, pn, item, lane, it)) return;  // uniform over the work-group
+    if (!find_item(k, it)) return;  // uniform over the work-group
     // Q first: it is stored to LDS below, and a wait for it must not also
     // wait for the first blocks (loads complete in issue order)
-    load_q_part<ES, D>(p, q, it.u, lane, wave, q0);
+    load_q_part<ES, D, FUSED>(p, q, in, it.u, lane, wave, q0);
     wave_item_setup(p, btab, wave, lane, it, W0);
   }
   bool has_next;
   {
     Item it;
-    has_next = find_item(p, pl, pn, item + grid, lane, it);
+    has_next = find_item(k + 1, it);
     if (has_next)
       wave_item_setup(p, btab, wave, lane, it, W1);
     else
@@ -1374,32 +1487,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
   Frag<ES, D> f0, f1, f2;
   load_frag<ES, D>(f0, p.pool + (int64_t)W0.pf0 * p.block_bytes, lane);
   load_frag<ES, D>(f1, p.pool + (int64_t)W0.pf1 * p.block_bytes, lane);
-  store_q_part<ES, D>(sh, 0, lane, wave, q0);
+  store_q_part<ES, D, FUSED>(sh, 0, lane, wave, q0);
   __syncthreads();
   u32x4 qf[G::kChunks];
-  read_q<ES, D>(sh, 0, lane, qf);
+  read_q<ES, D, FUSED>(sh, 0, lane, qf);
+  constexpr int kBufs = AttnShared<ES, D, FUSED>::kBufs;
   int qbuf = 0;
+  unsigned long long live = 0;  // FUSED: live tokens after the appends (wave 0)
 
   // W0 is the item being computed, W1 the next one (both held in scalar
   // registers, so moving W1 into W0 waits for no load).
   for (;;) {
-    QPart<ES, D> qn;
-    load_q_part<ES, D>(p, q, W1.u, lane, wave, qn);  // W1's Q, stored to LDS early in W0's block loop
+    const int nbuf = qbuf + 1 == kBufs ? 0 : qbuf + 1;
+    QPart<ES, D, FUSED> qn;
+    load_q_part<ES, D, FUSED>(p, q, in, W1.u, lane, wave, qn);  // W1's inputs, stored to LDS early in W0's block loop
     Acc<D> acc;  // set by run_item
-    run_item<ES, D>(p, f0, f1, f2, W0, W1, qf, lane, acc,
-                    [&]() { store_q_part<ES, D>(sh, qbuf ^ 1, lane, wave, qn); });
-    merge_item<ES, D>(p, out, W0, acc, lane, wave, sh);
+    run_item<ES, D, FUSED>(p, f0, f1, f2, W0, W1, qf, lane, acc,
+                           [&]() { store_q_part<ES, D, FUSED>(sh, nbuf, lane, wave, qn); });
+    merge_item<ES, D, FUSED>(p, out, W0, acc, lane, wave, sh, qbuf, qf);
+    if constexpr (FUSED) {
+      // the new token's row is in buffer qbuf, which the next item's staging
+      // (buffer nbuf, then the one after) leaves alone until this wave has
+      // passed the next merge's barriers
+      if (wave == 0) {
+        const uint8_t* krow = (const uint8_t*)&sh.row[qbuf][0];
+        live += store_token<ES, D>(p, W0.u, lane, krow, krow + D * ES, W0.alpha != 0, W0.q, W0.rs, W0.n,
+                                   W0.tblk, -1);
+      }
+    }
     if (!has_next) break;
-    qbuf ^= 1;
-    read_q<ES, D>(sh, qbuf, lane, qf);
+    qbuf = nbuf;
+    read_q<ES, D, FUSED>(sh, qbuf, lane, qf);
     W0 = W1;
-    item += grid;
+    ++k;
     Item it;
-    has_next = find_item(p, pl, pn, item + grid, lane, it);
+    has_next = find_item(k + 1, it);
     if (has_next)
       wave_item_setup(p, btab, wave, lane, it, W1);
     else
       wave_item_none(W1);
+  }
+  if constexpr (FUSED) {
+    if (wave == 0 && lane == 0) atomicAdd(&p.ctr->live_token_steps, live);
   }
 }
 
@@ -1455,10 +1584,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(Dev p, float* __restrict__ 
 // w owns kPfCols tiles of 16 queries, one query per MFMA column (where the
 // decode packs the group's heads), and streams the same key blocks as the
 // other waves.
-#ifndef DMS_PF_COLS
-#define DMS_PF_COLS 3
-#endif
-constexpr int kPfCols = DMS_PF_COLS;
+constexpr int kPfCols = 3;
 constexpr int kPfTile = 16 * kPfCols * kWavesPerWG;
 
 // Fragment (the cache block order) of 16 consecutive dense rows row0 ..
@@ -1963,28 +2089,17 @@ __global__ __launch_bounds__(256) void soft_forward_kernel(SoftArgs a, const uin
   }
 }
 
-#ifndef DMS_SOFT_QCOLS
-#define DMS_SOFT_QCOLS 1
-#endif
-#ifndef DMS_SOFT_DQ_WG
-#define DMS_SOFT_DQ_WG 4
-#endif
-#ifndef DMS_SOFT_DKV_WG
-#define DMS_SOFT_DKV_WG 4
-#endif
 // Waves per work-group of the backward kernels.  The waves of a work-group
 // share every staged step, so more waves re-read the streamed operands less
 // often; measured on the 32B-shaped training layer, 8 waves made dq slower
 // and dkv no faster than 4.
-constexpr int kSoftQWaves = DMS_SOFT_DQ_WG;
-constexpr int kSoftKWaves = DMS_SOFT_DKV_WG;
-constexpr int kSoftQCols = DMS_SOFT_QCOLS;               // query tiles of 16 per wave (dQ)
+constexpr int kSoftQWaves = 4;
+constexpr int kSoftKWaves = 4;
+constexpr int kSoftQCols = 1;              // query tiles of 16 per wave (dQ)
 constexpr int kSoftQTile = 16 * kSoftQCols * kSoftQWaves;  // queries per work-group (dQ)
-#ifndef DMS_SOFT_DKV_KT
-#define DMS_SOFT_DKV_KT 1
-#endif
-constexpr int kSoftKT = DMS_SOFT_DKV_KT;                    // key tiles of 16 per wave (dK, dV)
+constexpr int kSoftKT = 1;                   // key tiles of 16 per wave (dK, dV)
 constexpr int kSoftKTile = 16 * kSoftKT * kSoftKWaves;      // keys per work-group (dK, dV)
+constexpr int kSoftDqWavesPerEu = 2;  // waves per SIMD soft_dq_kernel's registers are sized for
 
 // Backward, query-stationary: dq = scale * dS k with dS = P (dP - delta), P
 // recomputed from the forward's lse, dP = dO v^T.  Each wave holds
@@ -2027,11 +2142,8 @@ struct SoftQStage {
   float bias[32];
 };
 
-#ifndef DMS_SOFT_DQ_WAVES
-#define DMS_SOFT_DQ_WAVES 2
-#endif
 template <int D>
-__global__ __launch_bounds__(64 * kSoftQWaves) __attribute__((amdgpu_waves_per_eu(DMS_SOFT_DQ_WAVES))) void soft_dq_kernel(
+__global__ __launch_bounds__(64 * kSoftQWaves) __attribute__((amdgpu_waves_per_eu(kSoftDqWavesPerEu))) void soft_dq_kernel(
     SoftArgs a, const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const uint8_t* __restrict__ kt, const uint8_t* __restrict__ dO, const float* __restrict__ bias2,
     const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dq) {
@@ -2665,21 +2777,15 @@ hipError_t launch_prefill(const Dev& p, int dtype, int d, const void* k, const v
 }
 
 template <int ES, int D>
-static hipError_t attention_t(const Dev& p, const void* q, float* out, int64_t grid_wgs, hipStream_t s,
-                              hipEvent_t start, hipEvent_t stop) {
-  // whole_units: no unit is split, so there is nothing for reduce_kernel
-  const dim3 grid((unsigned)grid_wgs), block(64 * kWavesPerWG);
+static hipError_t attention_t(const Dev& p, const void* q, float* out, hipStream_t s, hipEvent_t start,
+                              hipEvent_t stop) {
+  // whole-unit mode: no unit is split, so there is nothing for reduce_kernel
+  const dim3 grid((unsigned)p.grid), block(64 * kWavesPerWG);
   const dim3 rgrid((p.U + kWavesPerWG - 1) / kWavesPerWG);
-  if (!start && !stop) {
-    const hipError_t e = launch(attention_kernel<ES, D>, grid, block, s, p, (const int32_t*)p.btab,
-                                (const uint8_t*)q, out);
-    if (e != hipSuccess || p.whole_units) return e;
-    return launch(reduce_kernel<D>, rgrid, block, s, p, out);
-  }
-  // timed: start with the attention launch, stop with the call's last launch
-  const hipError_t e = launch_timed(attention_kernel<ES, D>, grid, block, s, start, p.whole_units ? stop : nullptr,
-                                    p, (const int32_t*)p.btab, (const uint8_t*)q, out);
-  if (e != hipSuccess || p.whole_units) return e;
+  const StepIn none{};
+  const hipError_t e = launch_timed(attention_kernel<ES, D, false>, grid, block, s, start, p.split ? nullptr : stop,
+                                    p, (const int32_t*)p.btab, (const uint8_t*)q, out, none);
+  if (e != hipSuccess || !p.split) return e;
   return launch_timed(reduce_kernel<D>, rgrid, block, s, nullptr, stop, p, out);
 }
 
@@ -2706,9 +2812,7 @@ hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* 
 // two work-groups stay resident per CU.  Three tiles beyond, so that more
 // columns share every loaded block.  (Measured on the 32B-shaped layer, G =
 // 5: one tile was faster for chunks of 1, three tiles for 4 and 12.)
-#ifndef DMS_CHUNK_SMALL_COLS
-#define DMS_CHUNK_SMALL_COLS 16
-#endif
+constexpr int kChunkSmallCols = 16;
 
 template <int ES, int D, int NC>
 static hipError_t chunk_attention_t(const Dev& p, const void* q, const void* k, const void* v, const LogitSrc& logit,
@@ -2721,7 +2825,7 @@ static hipError_t chunk_attention_t(const Dev& p, const void* q, const void* k, 
 template <int ES, int D>
 static hipError_t decode_chunk_t(const Dev& p, const void* q, const void* k, const void* v, const LogitSrc& logit,
                                  int zero_ch, int chunk, float* out, hipStream_t s) {
-  const hipError_t e = chunk * p.G <= DMS_CHUNK_SMALL_COLS
+  const hipError_t e = chunk * p.G <= kChunkSmallCols
                            ? chunk_attention_t<ES, D, 1>(p, q, k, v, logit, zero_ch, chunk, out, s)
                            : chunk_attention_t<ES, D, 3>(p, q, k, v, logit, zero_ch, chunk, out, s);
   if (e != hipSuccess) return e;
@@ -2827,14 +2931,20 @@ hipError_t launch_soft_backward(const SoftArgs& a, int d, const void* q, const v
                                         (uint8_t*)ws, s);
 }
 
-template <int ES, int D>
-static int resident_t(int num_cus) {
+template <typename K>
+static int resident_of(K kernel, int num_cus) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attention_kernel<ES, D>, 64 * kWavesPerWG, 0) !=
-          hipSuccess ||
-      per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kWavesPerWG, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
   return per_cu * num_cus;
+}
+
+// The launch size serves both attention kernels (the fused step and the
+// attention alone): the smaller of their resident counts.
+template <int ES, int D>
+static int resident_t(int num_cus) {
+  return std::min(resident_of(attention_kernel<ES, D, false>, num_cus),
+                  resident_of(attention_kernel<ES, D, true>, num_cus));
 }
 
 int attention_resident_wgs(int dtype, int d, int num_cus) {
@@ -2842,13 +2952,35 @@ int attention_resident_wgs(int dtype, int d, int num_cus) {
   return d == 128 ? resident_t<4, 128>(num_cus) : resident_t<4, 64>(num_cus);
 }
 
-hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out, int64_t grid_wgs,
-                            hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+hipError_t launch_attention(const Dev& p, int dtype, int d, const void* q, float* out, hipStream_t s,
+                            hipEvent_t start, hipEvent_t stop) {
   if (dtype == 1)
-    return d == 128 ? attention_t<2, 128>(p, q, out, grid_wgs, s, start, stop)
-                    : attention_t<2, 64>(p, q, out, grid_wgs, s, start, stop);
-  return d == 128 ? attention_t<4, 128>(p, q, out, grid_wgs, s, start, stop)
-                  : attention_t<4, 64>(p, q, out, grid_wgs, s, start, stop);
+    return d == 128 ? attention_t<2, 128>(p, q, out, s, start, stop) : attention_t<2, 64>(p, q, out, s, start, stop);
+  return d == 128 ? attention_t<4, 128>(p, q, out, s, start, stop) : attention_t<4, 64>(p, q, out, s, start, stop);
+}
+
+template <int ES, int D>
+static hipError_t decode_step_t(const Dev& p, const void* q, const StepIn& in, float* out, hipStream_t s,
+                                hipEvent_t start, hipEvent_t stop) {
+  const dim3 block(64 * kWavesPerWG);
+  if (!p.split)
+    return launch_timed(attention_kernel<ES, D, true>, dim3((unsigned)p.grid), block, s, start, stop, p,
+                        (const int32_t*)p.btab, (const uint8_t*)q, out, in);
+  // split mode: the append, then the attention and the split merge
+  const int blocks = (p.U + kWavesPerWG - 1) / kWavesPerWG;
+  const hipError_t e = launch_timed(append_kernel<ES, D>, dim3(blocks), block, s, start, nullptr, p, in.k, in.v,
+                                    in.logit, (int)in.zero_ch);
+  if (e != hipSuccess) return e;
+  return attention_t<ES, D>(p, q, out, s, nullptr, stop);
+}
+
+hipError_t launch_decode_step(const Dev& p, int dtype, int d, const void* q, const StepIn& in, float* out,
+                              hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  if (dtype == 1)
+    return d == 128 ? decode_step_t<2, 128>(p, q, in, out, s, start, stop)
+                    : decode_step_t<2, 64>(p, q, in, out, s, start, stop);
+  return d == 128 ? decode_step_t<4, 128>(p, q, in, out, s, start, stop)
+                  : decode_step_t<4, 64>(p, q, in, out, s, start, stop);
 }
 
 }  // namespace dms

@@ -20,24 +20,18 @@ struct dms_cache {
   uint8_t* ws;
   int device;
   int num_cus;
-  int target_items;
-  int64_t grid_wgs;
+  int grid;   // attention work-groups per launch (resident at once)
+  bool split; // the attention's mode: split by live blocks, or whole units
   std::vector<int32_t> len;  // host mirror of each sequence's length
   // True from a successful prefill until the next append or reset: the cache
   // then holds the prompt's visible tokens with slots in position order, which
   // dms_prefill_attention relies on.
   bool prompt_fresh = false;
   int prompt_zero_ch = -1;  // the key channel that prefill stored as 0, or -1
-  // The attention's unit order (in the workspace; identity after create and
-  // reset).  Set after a prefill with unequal prompt lengths, see balance_units.
-  bool ordered = false;
-  std::vector<int32_t> order;  // host copy, alive while the upload may still read it
+  // Host copies of the whole-unit layout last uploaded (order, wg_range),
+  // alive while the upload may still read them.
+  std::vector<int32_t> order, wg_range;
 };
-
-// Split-plan target in quarters of the resident work-group count.
-#ifndef DMS_SPLIT_ITEMS_PER_RESIDENT
-#define DMS_SPLIT_ITEMS_PER_RESIDENT 4
-#endif
 
 namespace {
 
@@ -56,7 +50,7 @@ bool valid_config(const dms_config* c) {
   if (c->window < 0) return false;
   if (c->block_tokens != dms::kBlockTokens) return false;
   if (c->max_tokens < 1 || c->max_tokens > (1 << 24)) return false;
-  if (c->max_splits < 0 || c->max_splits > 1024) return false;
+  if (c->split_wgs < 0 || c->split_wgs > 65535) return false;
   if (c->pool_blocks < 1 || c->pool_blocks > 0x7fffffffLL) return false;
   if (c->dtype != DMS_F32 && c->dtype != DMS_BF16) return false;
   if (!isfinite(c->scale) || c->scale < 0.0f) return false;
@@ -73,17 +67,12 @@ void make_layout(const dms_config* c, dms::Layout& L) {
   L.R = std::min(c->window, c->max_tokens) + 1;
   L.max_tokens = c->max_tokens;
   L.max_blocks = (c->max_tokens + dms::kBlockTokens - 1) / dms::kBlockTokens;
-  // at least enough work items per unit to keep each within kMaxItemBlocks
-  L.max_splits = std::max(c->max_splits == 0 ? 32 : c->max_splits,
-                          (L.max_blocks + dms::kMaxItemBlocks - 1) / dms::kMaxItemBlocks);
   L.U = c->batch * c->num_kv_heads;
   L.pool_blocks = c->pool_blocks;
   L.block_bytes = 2LL * dms::kBlockTokens * L.d * L.esize;
   L.item_floats = 32 + L.G * L.d;
-  // A plan never has more than target + 2U + pool_blocks / kMaxItemBlocks
-  // items (target <= kMaxTargetItems), nor more than max_splits per unit.
-  L.max_items = std::min<int64_t>((int64_t)L.U * L.max_splits,
-                                  dms::kMaxTargetItems + 2LL * L.U + L.pool_blocks / dms::kMaxItemBlocks);
+  // split mode writes the partial of work-group g's piece of unit u to slot u + g
+  L.max_items = (int64_t)L.U + dms::kMaxAttnWGs;
   int64_t o = 0;
   L.off_pool = o;
   o = align_up(o + L.pool_blocks * L.block_bytes, kAlign);
@@ -103,6 +92,8 @@ void make_layout(const dms_config* c, dms::Layout& L) {
   o = align_up(o + (int64_t)L.U * 8, kAlign);
   L.off_order = o;
   o = align_up(o + (int64_t)L.U * 4, kAlign);
+  L.off_wgrange = o;
+  o = align_up(o + (int64_t)(dms::kMaxAttnWGs + 1) * 4, kAlign);
   L.off_ctr = o;
   o = align_up(o + (int64_t)sizeof(dms::Counters), kAlign);
   L.off_part = o;
@@ -122,6 +113,7 @@ dms::Dev make_dev(const dms_cache* c) {
   p.pos = (int32_t*)(c->ws + L.off_pos);
   p.plan = (int32_t*)(c->ws + L.off_plan);
   p.order = (int32_t*)(c->ws + L.off_order);
+  p.wg_range = (int32_t*)(c->ws + L.off_wgrange);
   p.ctr = (dms::Counters*)(c->ws + L.off_ctr);
   p.part = (float*)(c->ws + L.off_part);
   p.B = L.B;
@@ -131,12 +123,11 @@ dms::Dev make_dev(const dms_cache* c) {
   p.R = L.R;
   p.max_tokens = L.max_tokens;
   p.max_blocks = L.max_blocks;
-  p.max_splits = L.max_splits;
   p.U = L.U;
   p.item_floats = L.item_floats;
-  p.target_items = c->target_items;
-  p.whole_units = c->L.U >= c->target_items ? 1 : 0;
-  p.ordered = c->ordered ? 1 : 0;
+  p.grid = c->grid;
+  p.split = c->split ? 1 : 0;
+  p.split_wgs = c->cfg.split_wgs >= 2 ? std::min(c->cfg.split_wgs, c->grid) : c->grid;
   p.pool_blocks = L.pool_blocks;
   p.block_bytes = L.block_bytes;
   const float scale = c->cfg.scale == 0.0f ? 1.0f / sqrtf((float)L.d) : c->cfg.scale;
@@ -185,6 +176,15 @@ int soft_args(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d, int32_t 
   return DMS_OK;
 }
 
+// The attention's mode until dms_cache_balance decides from the live counts:
+// split_wgs 1 forces whole units, >= 2 forces the split; otherwise whole units
+// when every work-group can have one.
+bool default_split(const dms_cache* c) {
+  if (c->cfg.split_wgs == 1) return false;
+  if (c->cfg.split_wgs >= 2) return true;
+  return c->L.U < c->grid && c->L.U <= dms::kPlanLdsUnits;
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,17 +216,17 @@ int dms_cache_create(const dms_config* cfg, void* d_workspace, size_t workspace_
   c->device = dev;
   c->num_cus = prop.multiProcessorCount;
   // Persistent attention grid: as many 4-wave work-groups as fit at once.
-  // The split plan aims at one work item per resident work-group.  With at
-  // least as many units as that, every unit is one item (whole-unit mode):
-  // the kernel builds no plan (item i is the unit at position i of the unit
-  // order), no partials are written and the split-merge launch is skipped.  With
-  // fewer, units are split in proportion to their blocks.  (Measured on 512
-  // equal units and 512 work-groups: one item per unit 193.5 us per call,
-  // two 199 us.)
-  const int resident = dms::attention_resident_wgs(cfg->dtype, L.d, c->num_cus);
-  c->target_items = std::min(dms::kMaxTargetItems, std::max(8, resident * DMS_SPLIT_ITEMS_PER_RESIDENT / 4));
-  c->grid_wgs = std::min<int64_t>(resident, std::min<int64_t>(L.max_items, (int64_t)c->target_items + 2LL * L.U +
-                                                                              L.pool_blocks / dms::kMaxItemBlocks));
+  // Whole-unit mode when there are at least as many units as work-groups
+  // (each work-group takes whole units: no plan, no partials, no split
+  // merge, and the decode step fuses the append into the same launch), split
+  // mode with fewer units (the live blocks in equal shares).
+  // dms_cache_balance re-decides from the live counts.
+  c->grid = std::max(1, std::min(dms::kMaxAttnWGs, dms::attention_resident_wgs(cfg->dtype, L.d, c->num_cus)));
+  if (cfg->split_wgs >= 2 && L.U > dms::kPlanLdsUnits) {
+    delete c;
+    return DMS_ERR_ARG;  // split mode plans at most kPlanLdsUnits units
+  }
+  c->split = default_split(c);
   c->len.assign(L.B, 0);
   const int st = hip_status(dms::launch_init(make_dev(c), (hipStream_t)stream));
   if (st != DMS_OK) {
@@ -250,7 +250,7 @@ int dms_cache_reset(dms_cache* c, void* stream) {
   if (st == DMS_OK) {
     std::fill(c->len.begin(), c->len.end(), 0);
     c->prompt_fresh = false;
-    c->ordered = false;
+    c->split = default_split(c);
   }
   return st;
 }
@@ -292,37 +292,61 @@ static int channel_logits(const dms_cache* c, const void* d_k, const void* d_q, 
   return DMS_OK;
 }
 
-// With one work item per unit, work-group g of the G resident ones takes
-// units order[g], order[g + G], order[g + 2G], ...  After a prefill with
-// unequal prompt lengths the host orders the units by their sequence's
-// length, longest first, and deals them out in alternating directions (round
-// k: slot g gets the (kG + g)-th largest unit for even k, the (kG + G-1-g)-th
-// for odd k), so that every work-group's sum of lengths is about the mean.
-// The live counts of a sequence's heads follow its length, so this balances
-// the attention's load.  Appends keep the order valid (all lengths grow by
-// one).  Equal lengths keep the index order.
-static int balance_units(dms_cache* c, void* stream) {
+// Whole-unit mode: deals the units to the work-groups longest processing
+// time first (heaviest unit to the least loaded work-group) by weight wt[u],
+// and uploads the layout (order, wg_range) to the workspace.  Returns the
+// heaviest work-group's load.
+static int64_t deal_units(dms_cache* c, const std::vector<int64_t>& wt, void* stream, int* status) {
+  const int U = c->L.U, Gn = c->grid;
+  std::vector<int32_t> s(U);
+  for (int u = 0; u < U; ++u) s[u] = u;
+  std::stable_sort(s.begin(), s.end(), [&](int32_t a, int32_t b) { return wt[a] > wt[b]; });
+  // min-heap of (load, work-group)
+  std::vector<std::pair<int64_t, int32_t>> heap;
+  heap.reserve(Gn);
+  for (int g = 0; g < Gn; ++g) heap.push_back({0, g});
+  auto cmp = [](const std::pair<int64_t, int32_t>& a, const std::pair<int64_t, int32_t>& b) {
+    return a.first != b.first ? a.first > b.first : a.second > b.second;
+  };
+  std::make_heap(heap.begin(), heap.end(), cmp);
+  std::vector<std::vector<int32_t>> lists(Gn);
+  for (int32_t u : s) {
+    std::pop_heap(heap.begin(), heap.end(), cmp);
+    heap.back().first += wt[u];
+    lists[heap.back().second].push_back(u);
+    std::push_heap(heap.begin(), heap.end(), cmp);
+  }
+  int64_t worst = 0;
+  for (const auto& h : heap) worst = std::max(worst, h.first);
+  c->order.clear();
+  c->wg_range.assign(1, 0);
+  for (int g = 0; g < Gn; ++g) {
+    c->order.insert(c->order.end(), lists[g].begin(), lists[g].end());
+    c->wg_range.push_back((int32_t)c->order.size());
+  }
   const dms::Layout& L = c->L;
-  c->ordered = false;
-  if (L.U < c->target_items) return DMS_OK;  // units are split and balanced by blocks instead
+  *status = (hipMemcpyAsync(c->ws + L.off_order, c->order.data(), (size_t)U * 4, hipMemcpyHostToDevice,
+                            (hipStream_t)stream) != hipSuccess ||
+             hipMemcpyAsync(c->ws + L.off_wgrange, c->wg_range.data(), (size_t)(Gn + 1) * 4,
+                            hipMemcpyHostToDevice, (hipStream_t)stream) != hipSuccess)
+                ? DMS_ERR_HIP
+                : DMS_OK;
+  return worst;
+}
+
+// After a prefill with unequal prompt lengths, whole-unit mode deals the
+// units by their sequence's length (the live counts of a sequence's heads
+// grow with it; they are not known on the host).  Appends keep the layout
+// valid.  Equal lengths keep the default layout.
+static int balance_by_length(dms_cache* c, void* stream) {
+  if (c->split) return DMS_OK;
   const auto mm = std::minmax_element(c->len.begin(), c->len.end());
   if (*mm.first == *mm.second) return DMS_OK;
-  std::vector<int32_t> s(L.U);
-  for (int u = 0; u < L.U; ++u) s[u] = u;
-  std::stable_sort(s.begin(), s.end(),
-                   [&](int32_t a, int32_t b) { return c->len[a / L.Hkv] > c->len[b / L.Hkv]; });
-  const int64_t G = c->grid_wgs;
-  c->order.assign(L.U, 0);
-  for (int64_t k0 = 0; k0 < L.U; k0 += G) {
-    const int64_t r = std::min<int64_t>(G, L.U - k0);
-    const bool rev = ((k0 / G) & 1) != 0;
-    for (int64_t g = 0; g < r; ++g) c->order[k0 + g] = s[k0 + (rev ? r - 1 - g : g)];
-  }
-  if (hipMemcpyAsync(c->ws + L.off_order, c->order.data(), (size_t)L.U * 4, hipMemcpyHostToDevice,
-                     (hipStream_t)stream) != hipSuccess)
-    return DMS_ERR_HIP;
-  c->ordered = true;
-  return DMS_OK;
+  std::vector<int64_t> wt(c->L.U);
+  for (int u = 0; u < c->L.U; ++u) wt[u] = c->len[u / c->L.Hkv];
+  int st = DMS_OK;
+  deal_units(c, wt, stream, &st);
+  return st;
 }
 
 static int prefill_common(dms_cache* c, const void* d_k, const void* d_v, const dms::LogitSrc& ls, int zero_ch,
@@ -341,7 +365,7 @@ static int prefill_common(dms_cache* c, const void* d_k, const void* d_v, const 
     for (int b = 0; b < c->L.B; ++b) c->len[b] = h_lengths[b];
     c->prompt_fresh = true;
     c->prompt_zero_ch = zero_ch;
-    st = balance_units(c, stream);
+    st = balance_by_length(c, stream);
   }
   return st;
 }
@@ -443,8 +467,7 @@ int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, void* stre
   if (st != DMS_OK) return st;
   for (int32_t x : c->len)
     if (x < 1) return DMS_ERR_STATE;
-  return hip_status(dms::launch_attention(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_out, c->grid_wgs,
-                                          (hipStream_t)stream));
+  return hip_status(dms::launch_attention(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_out, (hipStream_t)stream));
 }
 
 int dms_decode_attention_timed(dms_cache* c, const void* d_q, float* d_out, void* start_event, void* stop_event,
@@ -454,8 +477,74 @@ int dms_decode_attention_timed(dms_cache* c, const void* d_q, float* d_out, void
   if (st != DMS_OK) return st;
   for (int32_t x : c->len)
     if (x < 1) return DMS_ERR_STATE;
-  return hip_status(dms::launch_attention(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_out, c->grid_wgs,
-                                          (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event));
+  return hip_status(dms::launch_attention(make_dev(c), c->cfg.dtype, c->L.d, d_q, d_out, (hipStream_t)stream,
+                                          (hipEvent_t)start_event, (hipEvent_t)stop_event));
+}
+
+static int step_common(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, const dms::LogitSrc& ls,
+                       int zero_ch, float* d_out, void* stream, void* start_event, void* stop_event) {
+  int st = check_device(c);
+  if (st != DMS_OK) return st;
+  for (int32_t x : c->len)
+    if (x + 1 > c->L.max_tokens) return DMS_ERR_CAPACITY;
+  const dms::StepIn in{(const uint8_t*)d_k, (const uint8_t*)d_v, ls, zero_ch};
+  st = hip_status(dms::launch_decode_step(make_dev(c), c->cfg.dtype, c->L.d, d_q, in, d_out, (hipStream_t)stream,
+                                          (hipEvent_t)start_event, (hipEvent_t)stop_event));
+  if (st == DMS_OK) {
+    for (auto& x : c->len) ++x;
+    c->prompt_fresh = false;
+  }
+  return st;
+}
+
+int dms_decode_step(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, const float* d_logit,
+                    float* d_out, void* stream) {
+  if (!c || !d_q || !d_k || !d_v || !d_logit || !d_out) return DMS_ERR_ARG;
+  return step_common(c, d_q, d_k, d_v, array_logits(c, d_logit, 1), -1, d_out, stream, nullptr, nullptr);
+}
+
+int dms_decode_step_timed(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, const float* d_logit,
+                          float* d_out, void* start_event, void* stop_event, void* stream) {
+  if (!c || !d_q || !d_k || !d_v || !d_logit || !d_out || !start_event || !stop_event) return DMS_ERR_ARG;
+  return step_common(c, d_q, d_k, d_v, array_logits(c, d_logit, 1), -1, d_out, stream, start_event, stop_event);
+}
+
+int dms_decode_step_channel(dms_cache* c, const void* d_q, const void* d_k, const void* d_v, int32_t source,
+                            int32_t channel, int32_t zero_channel, float* d_out, void* stream) {
+  if (!c || !d_q || !d_k || !d_v || !d_out) return DMS_ERR_ARG;
+  dms::LogitSrc ls{};
+  const int st = channel_logits(c, d_k, d_q, source, channel, zero_channel, 1, &ls);
+  if (st != DMS_OK) return st;
+  return step_common(c, d_q, d_k, d_v, ls, zero_channel ? channel : -1, d_out, stream, nullptr, nullptr);
+}
+
+int dms_cache_balance(dms_cache* c, void* stream) {
+  if (!c) return DMS_ERR_ARG;
+  int st = check_device(c);
+  if (st != DMS_OK) return st;
+  const dms::Layout& L = c->L;
+  if (c->cfg.split_wgs >= 2) return DMS_OK;  // split mode forced: nothing to plan on the host
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DMS_ERR_HIP;
+  std::vector<int32_t> n(L.U);
+  if (hipMemcpy(n.data(), c->ws + L.off_n, (size_t)L.U * 4, hipMemcpyDeviceToHost) != hipSuccess) return DMS_ERR_HIP;
+  // plan blocks, as the attention counts them (a unit with no live token counts one)
+  std::vector<int64_t> nb(L.U);
+  int64_t total = 0;
+  for (int u = 0; u < L.U; ++u) {
+    nb[u] = std::max<int64_t>(1, (n[u] + 15) / 16);
+    total += nb[u];
+  }
+  const bool can_split = c->cfg.split_wgs == 0 && L.U <= dms::kPlanLdsUnits;
+  if (can_split && L.U < c->grid) {  // some work-group would have no unit
+    c->split = true;
+    return DMS_OK;
+  }
+  const int64_t worst = deal_units(c, nb, stream, &st);
+  if (st != DMS_OK) return st;
+  // Whole units while the heaviest work-group carries at most 1/16 (plus one
+  // block) above the mean; beyond that the split's equal shares win.
+  c->split = can_split && 16 * worst * c->grid > 17 * total + 16LL * c->grid;
+  return DMS_OK;
 }
 
 int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream) {

@@ -49,7 +49,7 @@ class dms_config(ctypes.Structure):
         ("window", ctypes.c_int32),
         ("block_tokens", ctypes.c_int32),
         ("max_tokens", ctypes.c_int32),
-        ("max_splits", ctypes.c_int32),
+        ("split_wgs", ctypes.c_int32),
         ("pool_blocks", ctypes.c_int64),
         ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
@@ -98,6 +98,10 @@ def _load():
         "dms_prefill_compress_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, P(i32), i32, vp]),
         "dms_decode_attention": (ctypes.c_int, [vp, vp, vp, vp]),
         "dms_decode_attention_timed": (ctypes.c_int, [vp, vp, vp, vp, vp, vp]),
+        "dms_decode_step": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp]),
+        "dms_decode_step_timed": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "dms_decode_step_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
+        "dms_cache_balance": (ctypes.c_int, [vp, vp]),
         "dms_prefill_attention": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, vp]),
         "dms_decode_chunk": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp, vp]),
         "dms_decode_chunk_channel": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]),
@@ -134,9 +138,9 @@ def _i32p(a: Optional[np.ndarray]):
 
 
 def make_config(batch, num_q_heads, num_kv_heads, head_dim, window, max_tokens, pool_blocks,
-                dtype=DMS_BF16, max_splits=0, scale=0.0, block_tokens=16) -> dms_config:
+                dtype=DMS_BF16, split_wgs=0, scale=0.0, block_tokens=16) -> dms_config:
     return dms_config(batch, num_q_heads, num_kv_heads, head_dim, window, block_tokens, max_tokens,
-                      max_splits, pool_blocks, dtype, scale)
+                      split_wgs, pool_blocks, dtype, scale)
 
 
 def dms_status_str(status: int) -> str:
@@ -208,6 +212,26 @@ def dms_decode_attention(h: int, d_q: int, d_out: int, stream: int = 0):
 def dms_decode_attention_timed(h: int, d_q: int, d_out: int, start_event: int, stop_event: int, stream: int = 0):
     _check(lib.dms_decode_attention_timed(h, d_q, d_out, start_event, stop_event, stream),
            "dms_decode_attention_timed")
+
+
+def dms_decode_step(h: int, d_q: int, d_k: int, d_v: int, d_logit: int, d_out: int, stream: int = 0):
+    _check(lib.dms_decode_step(h, d_q, d_k, d_v, d_logit, d_out, stream), "dms_decode_step")
+
+
+def dms_decode_step_timed(h: int, d_q: int, d_k: int, d_v: int, d_logit: int, d_out: int, start_event: int,
+                          stop_event: int, stream: int = 0):
+    _check(lib.dms_decode_step_timed(h, d_q, d_k, d_v, d_logit, d_out, start_event, stop_event, stream),
+           "dms_decode_step_timed")
+
+
+def dms_decode_step_channel(h: int, d_q: int, d_k: int, d_v: int, source: int, channel: int, zero_channel: bool,
+                            d_out: int, stream: int = 0):
+    _check(lib.dms_decode_step_channel(h, d_q, d_k, d_v, int(source), int(channel), int(bool(zero_channel)), d_out,
+                                       stream), "dms_decode_step_channel")
+
+
+def dms_cache_balance(h: int, stream: int = 0):
+    _check(lib.dms_cache_balance(h, stream), "dms_cache_balance")
 
 
 _hip = None
@@ -420,13 +444,13 @@ class Cache:
     the library by pointer."""
 
     def __init__(self, batch, num_q_heads, num_kv_heads, head_dim, window, max_tokens, pool_blocks,
-                 dtype="bf16", max_splits=0, scale=0.0):
+                 dtype="bf16", split_wgs=0, scale=0.0):
         import torch
         self._torch = torch
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.cfg = make_config(batch, num_q_heads, num_kv_heads, head_dim, window, max_tokens, pool_blocks,
-                               DMS_BF16 if dtype == "bf16" else DMS_F32, max_splits, scale)
+                               DMS_BF16 if dtype == "bf16" else DMS_F32, split_wgs, scale)
         self.B, self.Hq, self.Hkv, self.d = batch, num_q_heads, num_kv_heads, head_dim
         self.window, self.max_tokens = window, max_tokens
         self.ring_size = min(window, max_tokens) + 1
@@ -537,6 +561,41 @@ class Cache:
         po = self._chk(out, (self.B, self.Hq, self.d), self._torch.float32, "out")
         dms_decode_attention_timed(self.handle, pq, po, timer.start.value, timer.stop.value, self._stream())
         return out
+
+    def _step_args(self, q, k, v, out):
+        pq = self._chk(q, (self.B, self.Hq, self.d), self.tdtype, "q")
+        pk = self._chk(k, (self.B, self.Hkv, self.d), self.tdtype, "k")
+        pv = self._chk(v, (self.B, self.Hkv, self.d), self.tdtype, "v")
+        if out is None:
+            out = self._torch.empty((self.B, self.Hq, self.d), dtype=self._torch.float32, device=q.device)
+        po = self._chk(out, (self.B, self.Hq, self.d), self._torch.float32, "out")
+        return pq, pk, pv, out, po
+
+    def step(self, q, k, v, logit, out=None):
+        """One decode step (append + attention, dms_decode_step): q [B, Hq, d],
+        k, v [B, Hkv, d], logit [B, Hkv] fp32; returns (or fills) out."""
+        pq, pk, pv, out, po = self._step_args(q, k, v, out)
+        pl = self._chk(logit, (self.B, self.Hkv), self._torch.float32, "logit")
+        dms_decode_step(self.handle, pq, pk, pv, pl, po, self._stream())
+        return out
+
+    def step_timed(self, q, k, v, logit, timer: "KernelTimer", out=None):
+        """step, with its kernels timed into `timer` (elapsed_ms)."""
+        pq, pk, pv, out, po = self._step_args(q, k, v, out)
+        pl = self._chk(logit, (self.B, self.Hkv), self._torch.float32, "logit")
+        dms_decode_step_timed(self.handle, pq, pk, pv, pl, po, timer.start.value, timer.stop.value, self._stream())
+        return out
+
+    def step_channel(self, q, k, v, source="k", channel=0, zero=False, out=None):
+        """step with the eviction logit read from channel `channel` of the key
+        row (source "k") or of the group's first query head (source "q")."""
+        pq, pk, pv, out, po = self._step_args(q, k, v, out)
+        dms_decode_step_channel(self.handle, pq, pk, pv, self._SOURCES[source], channel, zero, po, self._stream())
+        return out
+
+    def balance(self):
+        """Re-plan the attention's work split from the live counts (synchronises)."""
+        dms_cache_balance(self.handle, self._stream())
 
     def stats(self) -> dict:
         return dms_cache_stats(self.handle, self._stream())

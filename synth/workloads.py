@@ -45,6 +45,9 @@ class Workload:
     mu_before: List[float] = field(default_factory=lambda: [0.0])
     mu_after: Optional[List[float]] = None
     pos_threshold: int = synth.MAX_POS
+    # per KV head logit mean (the same at every position and layer); when set
+    # it replaces mu_before / mu_after: each head reaches its own compression
+    head_mu: Optional[List[float]] = None
     description: str = ""
 
     @property
@@ -61,13 +64,21 @@ class Workload:
         return int(self.prompt_lengths().max()) + self.decode_steps
 
     def layer_mu(self, layer: int):
+        """Logit means (below, at or above pos_threshold): scalars, or one
+        value per KV head when head_mu is set."""
+        if self.head_mu is not None:
+            hm = np.asarray(self.head_mu, dtype=np.float64)
+            return hm, hm
         before = self.mu_before[layer if len(self.mu_before) > 1 else 0]
         after = before if self.mu_after is None else self.mu_after[layer if len(self.mu_after) > 1 else 0]
         return before, after
 
-    def marked_prob(self, layer: int, pos: np.ndarray) -> np.ndarray:
-        """P(logit > 0) at each position under the Gaussian model of the logit."""
+    def marked_prob(self, layer: int, pos: np.ndarray, head: int = 0) -> np.ndarray:
+        """P(logit > 0) at each position of KV head `head` under the Gaussian
+        model of the logit."""
         before, after = self.layer_mu(layer)
+        if self.head_mu is not None:
+            before = after = float(self.head_mu[head])
         nd = NormalDist()
         pb = 1.0 - nd.cdf(-before) if np.isfinite(before) else 0.0
         pa = 1.0 - nd.cdf(-after) if np.isfinite(after) else 0.0
@@ -78,20 +89,24 @@ class Workload:
         position of every sequence, times `slack`, in 16-token blocks, plus
         one partly filled block per (sequence, KV head)."""
         total = 0
+        heads = range(self.num_kv_heads) if self.head_mu is not None else [0]
+        per_head = self.num_kv_heads // len(heads)
         for P in np.unique(self.prompt_lengths()):
             count = int(np.sum(self.prompt_lengths() == P))
             q = int(P) + self.decode_steps - 1
-            per_unit = int(np.ceil(slack * self.expected_live(layer, q) / 16.0)) + 2
-            total += per_unit * count * self.num_kv_heads
+            for h in heads:
+                per_unit = int(np.ceil(slack * self.expected_live(layer, q, h) / 16.0)) + 2
+                total += per_unit * count * per_head
         return total
 
-    def expected_live(self, layer: int, q: int) -> float:
-        """E|Vis(q)| under independent marks: unmarked tokens plus the window."""
+    def expected_live(self, layer: int, q: int, head: int = 0) -> float:
+        """E|Vis(q)| of KV head `head` under independent marks: unmarked
+        tokens plus the window."""
         if q < self.pos_threshold:  # one marking rate over positions 0..q: closed form
-            p = float(self.marked_prob(layer, np.array([0]))[0])
+            p = float(self.marked_prob(layer, np.array([0]), head)[0])
             return (q + 1) * (1.0 - p) + min(self.window + 1, q + 1) * p
         pos = np.arange(q + 1)
-        p = self.marked_prob(layer, pos)
+        p = self.marked_prob(layer, pos, head)
         in_window = pos >= q - self.window
         return float(np.sum(1.0 - p) + np.sum(p[in_window]))
 
@@ -142,6 +157,31 @@ def qwen_32b_dense() -> Workload:
     w.mu_before, w.mu_after, w.pos_threshold = [-8.0], None, synth.MAX_POS
     w.description = ("Qwen-R1-32B-shaped layer as above with every eviction logit below 0: nothing is "
                      "evicted (CR 1), 64 chains x 32768 tokens of dense KV")
+    return w
+
+
+def head_skew_crs(num_kv_heads: int = 8):
+    """Per-KV-head compression ratios spread over [2, 16] with arithmetic mean
+    8: CR_h = 2 + 14 (h / (H - 1))^1.4 (the exponent puts the mean at 8.0 for
+    8 heads).  The CR-2 head keeps about 2.5 times the layer's mean live
+    tokens, the CR-16 head about a third of it."""
+    H = num_kv_heads
+    return [2.0 + 14.0 * (h / (H - 1)) ** 1.4 for h in range(H)]
+
+
+def qwen_32b_head_skew() -> Workload:
+    """The Qwen-R1-32B-shaped layer with per-head compression: KV head h
+    marks a fraction 1 - 1/CR_h of its tokens at every position, CR_h from
+    head_skew_crs (2 ... 16, mean 8), the same for every sequence (a head's
+    rate is a property of the head).  Live counts per (sequence, KV head)
+    then differ by up to 7x within the layer."""
+    w = qwen_32b()
+    w.name = "qwen-r1-32b-layer-head-skew"
+    w.seed = 1007
+    w.mu_before, w.mu_after, w.pos_threshold = [0.0], None, synth.MAX_POS
+    w.head_mu = [mu_for_cr(c) for c in head_skew_crs(w.num_kv_heads)]
+    w.description = ("Qwen-R1-32B-shaped layer (64 chains x 32768 tokens, 40 Q / 8 KV heads, d 128, bf16, w 256) "
+                     "with per-KV-head CR 2 ... 16 (arithmetic mean 8): live tokens per head differ up to 7x")
     return w
 
 
@@ -239,4 +279,5 @@ def qwen_32b_train() -> TrainWorkload:
                     "Logistic noise")
 
 
-ALL = {w().name: w for w in (tiny, llama_1b, qwen_7b, qwen_32b, qwen_32b_dense, qwen_32b_hyperscale, full_32b)}
+ALL = {w().name: w for w in (tiny, llama_1b, qwen_7b, qwen_32b, qwen_32b_dense, qwen_32b_head_skew,
+                              qwen_32b_hyperscale, full_32b)}

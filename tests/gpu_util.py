@@ -29,14 +29,14 @@ def tdtype(wl: Workload):
     return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
 
-def make_cache(wl: Workload, layer: int = 0, pool_blocks: Optional[int] = None, max_splits: int = 0,
+def make_cache(wl: Workload, layer: int = 0, pool_blocks: Optional[int] = None, split_wgs: int = 0,
                max_tokens: Optional[int] = None, window: Optional[int] = None):
     from learned_kv_cache_dms_amd import dms
     return dms.Cache(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                      wl.window if window is None else window,
                      wl.max_tokens() if max_tokens is None else max_tokens,
                      wl.pool_blocks(layer) if pool_blocks is None else pool_blocks,
-                     dtype=wl.dtype, max_splits=max_splits)
+                     dtype=wl.dtype, split_wgs=split_wgs)
 
 
 def device_prompt(wl: Workload, layer: int, lengths: np.ndarray):
@@ -136,15 +136,20 @@ def check_unit_step(cache, wl: Workload, ud: UnitData, t: int, out_gpu: torch.Te
 
 
 def run_decode(wl: Workload, steps: int, units: Sequence[Tuple[int, int]], tol: float, layer: int = 0,
-               check_every: int = 1, cache=None, host_data: Optional[Dict] = None) -> CompareStats:
-    """Prefill + `steps` decode steps on the GPU, checking `units` against the oracle."""
+               check_every: int = 1, cache=None, host_data: Optional[Dict] = None, mode: str = "calls",
+               balance: bool = False) -> CompareStats:
+    """Prefill + `steps` decode steps on the GPU, checking `units` against the
+    oracle.  mode "calls": dms_append_step then dms_decode_attention; "step":
+    dms_decode_step.  balance: dms_cache_balance after the prompt (and every
+    64 steps)."""
     lengths = wl.prompt_lengths()
     if cache is None:
         cache = make_cache(wl, layer)
-    log(f"[{wl.name}] device prompt {tuple(lengths[:4])}... B={wl.batch}")
-    K, V, Lg = device_prompt(wl, layer, lengths)
-    cache.prefill(K, V, Lg, lengths)
-    del K, V, Lg
+    log(f"[{wl.name}] device prompt {tuple(lengths[:4])}... B={wl.batch} mode={mode} balance={balance}")
+    if int(lengths.max()) > 0:
+        K, V, Lg = device_prompt(wl, layer, lengths)
+        cache.prefill(K, V, Lg, lengths)
+        del K, V, Lg
     if host_data is None:
         host_data = {}
         for (b, h) in units:
@@ -152,9 +157,14 @@ def run_decode(wl: Workload, steps: int, units: Sequence[Tuple[int, int]], tol: 
     st = CompareStats()
     pos = torch.tensor(lengths, dtype=torch.int32, device="cuda")
     for t in range(steps):
+        if balance and t % 64 == 0:
+            cache.balance()
         q, k, v, lg = device_step(wl, layer, pos + t)
-        cache.append(k, v, lg)
-        out = cache.attend(q)
+        if mode == "step":
+            out = cache.step(q, k, v, lg)
+        else:
+            cache.append(k, v, lg)
+            out = cache.attend(q)
         if t % check_every == 0 or t == steps - 1:
             torch.cuda.synchronize()
             for key in units:

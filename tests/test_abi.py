@@ -53,7 +53,7 @@ def test_workspace_bytes_valid_and_monotone():
 @pytest.mark.parametrize("bad", [
     dict(num_q_heads=7), dict(num_q_heads=40, num_kv_heads=2), dict(head_dim=96), dict(window=-1),
     dict(block_tokens=8), dict(max_tokens=0), dict(pool_blocks=0), dict(dtype=5), dict(batch=0),
-    dict(scale=float("nan")), dict(max_splits=-1),
+    dict(scale=float("nan")), dict(split_wgs=-1),
 ])
 def test_workspace_bytes_rejects_invalid(bad):
     from learned_kv_cache_dms_amd import dms

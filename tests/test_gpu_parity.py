@@ -75,13 +75,13 @@ def test_small_shapes_every_unit(wl):
 
 @gpu
 def test_split_invariance():
-    """One work item per unit versus the default split plan (fp32)."""
+    """Whole units versus the default split by live blocks (fp32)."""
     import gpu_util as U
     wl = _small("f32-split", dtype="f32", batch=2, prompt_len=700, decode_steps=4, mu_before=[-0.5],
                 window=16)
     outs = []
-    for max_splits in (1, 0):
-        c = U.make_cache(wl, max_splits=max_splits)
+    for split_wgs in (1, 0):
+        c = U.make_cache(wl, split_wgs=split_wgs)
         lengths = wl.prompt_lengths()
         K, V, Lg = U.device_prompt(wl, 0, lengths)
         c.prefill(K, V, Lg, lengths)
@@ -96,15 +96,15 @@ def test_split_invariance():
 @pytest.mark.parametrize("blocks", [28, 308], ids=["7-per-wave", "77-per-wave"])
 def test_visit_order_strides(blocks):
     """Each of the attention's four waves walks its blocks of an item at a
-    stride coprime to their count: 7, else 11, else 13.  One item per unit
-    (max_splits 1) and nothing evicted (logits far below 0), so at the first
+    stride coprime to their count: 7, else 11, else 13.  Whole units
+    (split_wgs 1) and nothing evicted (logits far below 0), so at the first
     step every wave holds exactly blocks / 4 blocks: 7 (stride 11) or 77
     (stride 13).  Every unit, every step, against the oracle."""
     import gpu_util as U
     wl = _small(f"f32-d64-{blocks}-blocks", dtype="f32", head_dim=64, batch=2, num_q_heads=4, num_kv_heads=2,
                 window=8, decode_steps=3, prompt_len=blocks * 16 - 1, mu_before=[-8.0])
     units = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
-    st = U.run_decode(wl, wl.decode_steps, units, TOL["f32"], cache=U.make_cache(wl, max_splits=1))
+    st = U.run_decode(wl, wl.decode_steps, units, TOL["f32"], cache=U.make_cache(wl, split_wgs=1))
     assert st.checks == len(units) * wl.decode_steps
 
 
@@ -126,10 +126,10 @@ def test_whole_units_long_runs():
 @gpu
 @pytest.mark.parametrize("batch", [512, 520], ids=["4096-units", "4160-units"])
 def test_many_units(batch):
-    """As many (sequence, KV head) units as the attention's work-group-wide
-    plan in LDS holds (4096), and more: then each item is found by scanning
-    the live counts.  Ragged prompts of 1-120 tokens; sampled units, the
-    first and the last among them, checked at every step."""
+    """As many (sequence, KV head) units as the split mode plans for (4096),
+    and more (whole units only).  Ragged prompts of 1-120 tokens, dealt to
+    the work-groups by length; sampled units, the first and the last among
+    them, checked at every step."""
     import gpu_util as U
     wl = _small(f"bf16-d64-{batch}x8-units", head_dim=64, batch=batch, num_q_heads=16, num_kv_heads=8, window=8,
                 decode_steps=6, lengths_range=(1, 120))
