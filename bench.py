@@ -51,6 +51,8 @@ HBM_PEAK_GBPS = 8000.0
 # MI355X Infinity Cache (MALL): a step whose live KV fits in it is reported as
 # cache-resident, its rate is not an HBM rate
 MALL_BYTES = 256 * 2**20
+# live KV read between two visits of one cache when the bench rotates caches
+ROTATE_BYTES = 2**30
 # MI355X dense bf16 matrix-core peak (no sparsity)
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 KERNEL_SRCS = [os.path.join(ROOT, "learned_kv_cache_dms_amd", "csrc", f) for f in ("dms_kernels.hip", "dms_runtime.cpp")]
@@ -66,10 +68,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed counter summary, or
-    None when it is missing or was taken on another version of the kernels."""
-    path = os.path.join(ROOT, "profiles", f"attention_traffic_{workload}.md")
+def measured_traffic(workload: str, path_kind: str = "calls"):
+    """HBM bytes per timed call (the fused step, or the attention) from the
+    committed counter summary, or None when it is missing or was taken on
+    another version of the kernels."""
+    name = "decode_step_traffic" if path_kind == "step" else "attention_traffic"
+    path = os.path.join(ROOT, "profiles", f"{name}_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -462,8 +466,10 @@ def bench_chunk(args):
 
 def bench_full_step(args):
     """A multi-layer decode step: one cache per layer, every timed step runs
-    dms_append_step + dms_decode_attention for every layer in order (as a
-    model would).  Tokens/s = batch / (time of one step over all layers)."""
+    the decode step of every layer in order (as a model would): one
+    dms_decode_step per layer (--path step) or dms_append_step +
+    dms_decode_attention (--path calls).  Each layer's cache is balanced once
+    after its prompt.  Tokens/s = batch / (time of one step over all layers)."""
     import torch
     from learned_kv_cache_dms_amd import dms
     from synth import device as dsynth
@@ -489,6 +495,7 @@ def bench_full_step(args):
         dsynth.fill(Vd, wl.seed, synth.STREAM_V, l, 0)
         dsynth.logits(Ld, wl.seed, l, 0, mb, ma, wl.pos_threshold)
         c.prefill(Kd, Vd, Ld, lengths)
+        c.balance()
         del Kd, Vd, Ld
         caches.append(c)
         if l % 16 == 15:
@@ -509,12 +516,28 @@ def bench_full_step(args):
             dsynth.logits(lgs[t, l], wl.seed, l, 0, mb, ma, wl.pos_threshold, pos_base=base + t)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
+    def layer_step(t, l, timer=None):
+        c = caches[l]
+        if args.path == "step":
+            if timer is None:
+                c.step(qs[t, l], ks[t, l], vs[t, l], lgs[t, l], out)
+            else:
+                c.step_timed(qs[t, l], ks[t, l], vs[t, l], lgs[t, l], timer, out)
+        else:
+            c.append(ks[t, l], vs[t, l], lgs[t, l])
+            if timer is None:
+                c.attend(qs[t, l], out)
+            else:
+                c.attend_timed(qs[t, l], timer, out)
+
     for t in range(W):
         for l in range(NL):
-            caches[l].append(ks[t, l], vs[t, l], lgs[t, l])
-            caches[l].attend(qs[t, l], out)
+            layer_step(t, l)
     st0 = [c.stats() for c in caches]
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K * NL)]
+    # every layer call of every N-th step timed by kernel-stamped events
+    N = max(1, args.event_every)
+    sampled = list(range(0, K, N))
+    ev = {(i, l): dms.KernelTimer() for i in sampled for l in range(NL)}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -522,10 +545,7 @@ def bench_full_step(args):
     for i in range(K):
         t = W + i
         for l in range(NL):
-            caches[l].append(ks[t, l], vs[t, l], lgs[t, l])
-            ev[i * NL + l][0].record()
-            caches[l].attend(qs[t, l], out)
-            ev[i * NL + l][1].record()
+            layer_step(t, l, ev.get((i, l)))
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -533,7 +553,10 @@ def bench_full_step(args):
     if any(x["sticky_error"] for x in st1):
         raise SystemExit("device error during the run")
     total_ms = start.elapsed_time(end)
-    attn_s = sum(a.elapsed_time(b) for a, b in ev) / 1e3          # all attention calls
+    attn_s = sum(tm.elapsed_ms() for tm in ev.values()) / 1e3 * K / len(sampled)  # timed calls, scaled to K steps
+    for tm in ev.values():
+        tm.close()
+    split_layers = sum(1 for c in caches if c.split_mode())
     live_tokens = sum(b["live_token_steps"] - a["live_token_steps"] for a, b in zip(st0, st1)) / K
     live_bytes = live_tokens * 2 * d * esize                        # per step, all layers
     step_s = total_ms / K / 1e3
@@ -549,16 +572,239 @@ def bench_full_step(args):
                    "decode_steps": S},
         "live_kv_gbps": round(achieved, 1), "live_kv_gbps_per_step": round(live_bytes / step_s / 1e9, 1),
         "pct_peak_hbm": round(100 * achieved / HBM_PEAK_GBPS, 2),
-        "attention_ms_per_layer": round(attn_s / (K * NL) * 1e3, 5),
+        "timed_kernels_ms_per_layer": round(attn_s / (K * NL) * 1e3, 5),
+        "path": args.path, "layers_in_split_mode": split_layers,
         "live_bytes_per_step": round(live_bytes), "realized_cr": round(seen / live_now, 3),
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "dms_decode_attention = attention_kernel (+ reduce_kernel when a unit is split)",
+                     "kernel": ("dms_decode_step per layer (fused append + attention launch in whole-unit mode)"
+                                if args.path == "step" else
+                                "dms_decode_attention per layer = attention_kernel (+ reduce_kernel in split mode)"),
                      "algorithmic_bytes_per_launch": round(live_bytes / NL)},
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
+
+
+def _mu_json(mu):
+    import numpy as np
+    a = np.asarray(mu, dtype=np.float64)
+    return round(float(a), 4) if a.ndim == 0 else [round(float(x), 4) for x in a]
+
+
+def bench_decode(args):
+    """The decode step of a one-layer workload: every timed step is one
+    dms_decode_step (--path step: the append fused into the attention launch
+    in whole-unit mode) or dms_append_step + dms_decode_attention (--path
+    calls), on every sequence.  After the prompt's compression the cache is
+    balanced once (dms_cache_balance).  A step whose live KV would fit in the
+    MALL rotates over k independent caches (k x live bytes >= 1 GB), so that
+    every step reads its cache from HBM; the same workload without rotation is
+    reported beside it as the cache-resident figure."""
+    import math
+
+    import torch
+
+    from learned_kv_cache_dms_amd import dms
+    from synth import device as dsynth
+    from synth import synth, workloads
+
+    wl0 = workloads.ALL[args.workload]()
+    W, K = args.warmup, args.steps
+    B, Hq, Hkv, d = wl0.batch, wl0.num_q_heads, wl0.num_kv_heads, wl0.head_dim
+    tdt = torch.bfloat16 if wl0.dtype == "bf16" else torch.float32
+    esize = 2 if wl0.dtype == "bf16" else 4
+    lengths = wl0.prompt_lengths()
+    max_len = int(lengths.max())
+    # expected live bytes of a step, for the rotation count
+    est_bytes = sum(wl0.expected_live(0, int(lengths[b]) + wl0.decode_steps // 2, h)
+                    for b in range(B) for h in range(Hkv)) * 2 * d * esize
+    rot = args.rotate if args.rotate > 0 else (1 if est_bytes >= MALL_BYTES else
+                                               int(math.ceil(ROTATE_BYTES / est_bytes)))
+    S = W + K
+    local_steps = -(-S // rot)  # steps each cache takes
+    wl = dataclasses.replace(wl0, decode_steps=local_steps)
+    src, ch = args.logit_source, args.logit_channel
+    G = Hq // Hkv
+    if src != "array" and args.path != "calls":
+        raise SystemExit("--logit-source k|q is timed with --path calls")
+    print(f"# workload {wl.name}: prompt {max_len}, {W}+{K} steps over {rot} cache(s), pool {wl.pool_blocks(0)} "
+          f"blocks each, path {args.path}", file=sys.stderr, flush=True)
+    mb, ma = wl.layer_mu(0)
+    Kd = torch.empty((B, Hkv, max_len, d), dtype=tdt, device="cuda")
+    Vd = torch.empty_like(Kd)
+    Ld = torch.empty((B, Hkv, max_len), dtype=torch.float32, device="cuda")
+    dsynth.fill(Kd, wl.seed, synth.STREAM_K, 0, 0)
+    dsynth.fill(Vd, wl.seed, synth.STREAM_V, 0, 0)
+    dsynth.logits(Ld, wl.seed, 0, 0, mb, ma, wl.pos_threshold)
+    if src == "k":
+        Kd[..., ch] = Ld.to(tdt)
+    Qp = None
+    if src == "q":
+        Qp = torch.zeros((B, Hq, max_len, d), dtype=tdt, device="cuda")
+        Qp[:, ::G, :, ch] = Ld.to(tdt)
+    caches = []
+    for r in range(rot):
+        c = dms.Cache(B, Hq, Hkv, d, wl.window, wl.max_tokens(), wl.pool_blocks(0), dtype=wl.dtype)
+        if src == "array":
+            c.prefill(Kd, Vd, Ld, lengths)
+        elif src == "k":
+            c.prefill_channel(Kd, Vd, lengths, source="k", channel=ch, zero=True)
+        else:
+            c.prefill_channel(Kd, Vd, lengths, source="q", channel=ch, q=Qp)
+        c.balance()
+        caches.append(c)
+    torch.cuda.synchronize()
+    # The dense prompt stays in torch's cache: returning 17 GB to the HIP runtime
+    # (empty_cache) was measured to lower HBM streaming rates by 4-5% for the
+    # rest of the process on this platform.
+    del Kd, Vd, Ld, Qp
+
+    qs = torch.empty((local_steps, B, Hq, d), dtype=tdt, device="cuda")
+    ks = torch.empty((local_steps, B, Hkv, d), dtype=tdt, device="cuda")
+    vs = torch.empty_like(ks)
+    lgs = torch.empty((local_steps, B, Hkv), dtype=torch.float32, device="cuda")
+    base = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    for t in range(local_steps):
+        pb = base + t
+        dsynth.fill(qs[t], wl.seed, synth.STREAM_Q, 0, 0, pos_base=pb)
+        dsynth.fill(ks[t], wl.seed, synth.STREAM_K, 0, 0, pos_base=pb)
+        dsynth.fill(vs[t], wl.seed, synth.STREAM_V, 0, 0, pos_base=pb)
+        dsynth.logits(lgs[t], wl.seed, 0, 0, mb, ma, wl.pos_threshold, pos_base=pb)
+    if src == "k":
+        ks[..., ch] = lgs.to(tdt)
+    elif src == "q":
+        qs[:, :, ::G, ch] = lgs.to(tdt)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(s, timer=None):
+        c, t = caches[s % rot], s // rot
+        if args.path == "step":
+            if timer is None:
+                c.step(qs[t], ks[t], vs[t], lgs[t], out)
+            else:
+                c.step_timed(qs[t], ks[t], vs[t], lgs[t], timer, out)
+            return
+        if src == "array":
+            c.append(ks[t], vs[t], lgs[t])
+        else:
+            c.append_channel(ks[t], vs[t], source=src, channel=ch, zero=(src == "k"),
+                             q=qs[t] if src == "q" else None)
+        if timer is None:
+            c.attend(qs[t], out)
+        else:
+            c.attend_timed(qs[t], timer, out)
+
+    for s in range(W):
+        step(s)
+    st0 = [c.stats() for c in caches]
+
+    # Every N-th step of the timed region is timed by a pair of HIP events that
+    # the runtime stamps with the start and the end of that call's own kernels
+    # (the step's launches, or the attention's with --path calls); the steps in
+    # between run exactly as the sampled ones.  (Event pairs recorded around
+    # the call instead read 1-10 us more than the kernels themselves.)
+    N = max(1, args.event_every)
+    sampled = list(range(0, K, N))
+    ev = {i: dms.KernelTimer() for i in sampled}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(W + i, ev.get(i))
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st1 = [c.stats() for c in caches]
+    if any(x["sticky_error"] != 0 for x in st1):
+        raise SystemExit(f"device error during the run: {st1}")
+
+    total_ms = start.elapsed_time(end)
+    kern_ms = [ev[i].elapsed_ms() for i in sampled]
+    kern_avg_s = sum(kern_ms) / len(kern_ms) / 1e3
+    period_ms = [dms.KernelTimer.between(ev[a], ev[b]) / (b - a) for a, b in zip(sampled, sampled[1:])]
+    for tm in ev.values():
+        tm.close()
+    live_tokens = sum(b["live_token_steps"] - a["live_token_steps"] for a, b in zip(st0, st1)) / K
+    live_bytes = live_tokens * 2 * d * esize   # per step: the K/V rows of every visible token
+    step_s = total_ms / K / 1e3
+    achieved = live_bytes / kern_avg_s / 1e9
+    traffic = measured_traffic(wl.name, args.path) if rot == 1 else None
+    seen = sum(x["seen_tokens"] for x in st1)
+    live_now = sum(x["live_tokens"] for x in st1)
+    kernel = ("dms_decode_step = attention_kernel<fused> (the append inside the attention launch; split mode: "
+              "append_kernel + attention_kernel + reduce_kernel)" if args.path == "step" else
+              "dms_decode_attention = attention_kernel (+ reduce_kernel in split mode)")
+    res = {
+        "metric": METRIC,
+        "value": round(B / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(total_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+            "context": max_len, "window": wl.window, "block_tokens": 16,
+            "decode_steps": S, "logit_mean": [_mu_json(mb), _mu_json(ma)], "logit_mean_switch": wl.pos_threshold,
+            "logit_source": {"array": "array", "k": f"key channel {ch} (stored zeroed)",
+                             "q": f"query channel {ch} of each group's first head"}[src],
+            "path": args.path, "caches_rotated": rot,
+        },
+        "live_kv_gbps": round(achieved, 1),
+        "live_kv_gbps_per_step": round(live_bytes / step_s / 1e9, 1),
+        "pct_peak_hbm": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "timed_kernels_ms": round(kern_avg_s * 1e3, 5),
+        "timed_kernels_ms_median": round(statistics.median(kern_ms), 5),
+        "timed_calls": len(kern_ms),
+        "ms_per_step_median": round(statistics.median(period_ms), 5) if period_ms else None,
+        "cache_resident": bool(rot == 1 and live_bytes < MALL_BYTES),
+        "attention_mode": "split" if caches[0].split_mode() else "whole units",
+        "live_tokens_per_step": round(live_tokens, 1),
+        "realized_cr": round(seen / live_now, 3),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "kernel": kernel,
+            "algorithmic_bytes_per_launch": round(live_bytes),
+        },
+        "cpu_baseline": None,
+    }
+    for c in caches:
+        c.close()
+    del caches
+    if rot > 1 and not args.no_resident:
+        res["cache_resident_run"] = resident_figure(args, wl0)
+    if not args.no_cpu_baseline and src == "array":
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps, args.cpu_units)
+    print(json.dumps(res), flush=True)
+
+
+def resident_figure(args, wl0):
+    """The same decode steps on one cache (its live KV stays in the MALL)."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", wl0.name, "--steps", str(args.steps),
+           "--warmup", str(args.warmup), "--rotate", "1", "--path", args.path, "--no-cpu-baseline",
+           "--event-every", str(args.event_every)]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True, timeout=600)
+    if r.returncode != 0:
+        return None
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    return {"value": line["value"], "ms_per_step": line["ms_per_step"], "live_kv_gbps": line["live_kv_gbps"],
+            "note": "one cache, its live KV resident in the 256 MB MALL: not an HBM rate"}
 
 
 def main():
@@ -585,6 +831,13 @@ def main():
                     help="run the hyper-scaling harness (vanilla budget, DMS frontier, end-to-end runs)")
     ap.add_argument("--soft-attention", action="store_true",
                     help="training-time relaxed attention forward + backward on the 32B-shaped training layer")
+    ap.add_argument("--path", choices=("step", "calls"), default="step",
+                    help="decode bench: dms_decode_step (step) or dms_append_step + dms_decode_attention (calls)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="decode bench: independent caches used in turn (0: enough for 1 GB of live KV "
+                         "when one step's live KV would fit in the MALL, else 1)")
+    ap.add_argument("--no-resident", action="store_true",
+                    help="skip the cache-resident (one cache) figure that goes with a rotated run")
     ap.add_argument("--prefill-attention", action="store_true",
                     help="time dms_prefill_attention on the workload's prompt instead of the decode step "
                          "(use small --steps / --warmup: one call is a whole prompt)")
@@ -614,169 +867,13 @@ def main():
         bench_chunk(args)
         return
 
-    from learned_kv_cache_dms_amd import dms
-    from synth import device as dsynth
-    from synth import synth, workloads
+    from synth import workloads
 
     wl0 = workloads.ALL[args.workload]()
     if wl0.num_layers != 1:
         bench_full_step(args)
         return
-    W, K = args.warmup, args.steps
-    wl = dataclasses.replace(wl0, decode_steps=W + K)
-    B, Hq, Hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
-    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    esize = 2 if wl.dtype == "bf16" else 4
-    lengths = wl.prompt_lengths()
-
-    cache = dms.Cache(B, Hq, Hkv, d, wl.window, wl.max_tokens(), wl.pool_blocks(0), dtype=wl.dtype)
-    print(f"# workload {wl.name}: prompt {int(lengths.max())}, {W}+{K} steps, pool {wl.pool_blocks(0)} blocks",
-          file=sys.stderr, flush=True)
-    max_len = int(lengths.max())
-    Kd = torch.empty((B, Hkv, max_len, d), dtype=tdt, device="cuda")
-    Vd = torch.empty_like(Kd)
-    Ld = torch.empty((B, Hkv, max_len), dtype=torch.float32, device="cuda")
-    mb, ma = wl.layer_mu(0)
-    dsynth.fill(Kd, wl.seed, synth.STREAM_K, 0, 0)
-    dsynth.fill(Vd, wl.seed, synth.STREAM_V, 0, 0)
-    dsynth.logits(Ld, wl.seed, 0, 0, mb, ma, wl.pos_threshold)
-    src, ch = args.logit_source, args.logit_channel
-    G = Hq // Hkv
-    if src == "array":
-        cache.prefill(Kd, Vd, Ld, lengths)
-    elif src == "k":
-        Kd[..., ch] = Ld.to(tdt)
-        cache.prefill_channel(Kd, Vd, lengths, source="k", channel=ch, zero=True)
-    else:
-        Qp = torch.zeros((B, Hq, max_len, d), dtype=tdt, device="cuda")
-        Qp[:, ::G, :, ch] = Ld.to(tdt)
-        cache.prefill_channel(Kd, Vd, lengths, source="q", channel=ch, q=Qp)
-        del Qp
-    torch.cuda.synchronize()
-    # The dense prompt stays in torch's cache: returning 17 GB to the HIP runtime
-    # (empty_cache) was measured to lower HBM streaming rates by 4-5% for the
-    # rest of the process on this platform.
-    del Kd, Vd, Ld
-
-    S = W + K
-    qs = torch.empty((S, B, Hq, d), dtype=tdt, device="cuda")
-    ks = torch.empty((S, B, Hkv, d), dtype=tdt, device="cuda")
-    vs = torch.empty_like(ks)
-    lgs = torch.empty((S, B, Hkv), dtype=torch.float32, device="cuda")
-    base = torch.tensor(lengths, dtype=torch.int32, device="cuda")
-    for t in range(S):
-        pb = base + t
-        dsynth.fill(qs[t], wl.seed, synth.STREAM_Q, 0, 0, pos_base=pb)
-        dsynth.fill(ks[t], wl.seed, synth.STREAM_K, 0, 0, pos_base=pb)
-        dsynth.fill(vs[t], wl.seed, synth.STREAM_V, 0, 0, pos_base=pb)
-        dsynth.logits(lgs[t], wl.seed, 0, 0, mb, ma, wl.pos_threshold, pos_base=pb)
-    if src == "k":
-        ks[..., ch] = lgs.to(tdt)
-    elif src == "q":
-        qs[:, :, ::G, ch] = lgs.to(tdt)
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
-    torch.cuda.synchronize()
-
-    if src == "array":
-        def append(t):
-            cache.append(ks[t], vs[t], lgs[t])
-    else:
-        def append(t):
-            cache.append_channel(ks[t], vs[t], source=src, channel=ch, zero=(src == "k"),
-                                 q=qs[t] if src == "q" else None)
-
-    for t in range(W):
-        append(t)
-        cache.attend(qs[t], out)
-    st0 = cache.stats()
-
-    # Every N-th attention call of the timed region is timed by a pair of HIP
-    # events that the runtime stamps with the start and the end of the call's
-    # own kernels (dms_decode_attention_timed); the calls in between run
-    # exactly as the sampled ones.  (Event pairs recorded around the call
-    # instead read 1-10 us more than the kernels themselves.)
-    N = max(1, args.event_every)
-    sampled = list(range(0, K, N))
-    ev = {i: dms.KernelTimer() for i in sampled}
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(K):
-        t = W + i
-        append(t)
-        if i in ev:
-            cache.attend_timed(qs[t], ev[i], out)
-        else:
-            cache.attend(qs[t], out)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    st1 = cache.stats()
-    if st1["sticky_error"] != 0:
-        raise SystemExit(f"device error during the run: {st1}")
-
-    total_ms = start.elapsed_time(end)
-    attn_ms = [ev[i].elapsed_ms() for i in sampled]
-    attn_avg_s = sum(attn_ms) / len(attn_ms) / 1e3
-    # step period from one sampled attention end to the next, per step
-    period_ms = [dms.KernelTimer.between(ev[a], ev[b]) / (b - a) for a, b in zip(sampled, sampled[1:])]
-    for tm in ev.values():
-        tm.close()
-    live_tokens = (st1["live_token_steps"] - st0["live_token_steps"]) / K   # per step, all units
-    live_bytes = live_tokens * 2 * d * esize
-    step_s = total_ms / K / 1e3
-    tokens_per_s = B / step_s
-    achieved = live_bytes / attn_avg_s / 1e9
-    traffic = measured_traffic(wl.name)
-    seen = st1["seen_tokens"] / (B * Hkv)
-
-    res = {
-        "metric": METRIC,
-        "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(total_ms / K, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.dtype,
-        "data": "synthetic",
-        "config": {
-            "workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
-            "context": int(lengths.max()), "window": wl.window, "block_tokens": 16,
-            "decode_steps": S, "logit_mean": [round(mb, 4), round(ma, 4)], "logit_mean_switch": wl.pos_threshold,
-            "logit_source": {"array": "array", "k": f"key channel {ch} (stored zeroed)",
-                             "q": f"query channel {ch} of each group's first head"}[src],
-        },
-        "live_kv_gbps": round(achieved, 1),
-        "live_kv_gbps_per_step": round(live_bytes / step_s / 1e9, 1),
-        "pct_peak_hbm": round(100 * achieved / HBM_PEAK_GBPS, 2),
-        "attention_ms": round(attn_avg_s * 1e3, 5),
-        "attention_ms_median": round(statistics.median(attn_ms), 5),
-        "attention_calls_timed": len(attn_ms),
-        "ms_per_step_median": round(statistics.median(period_ms), 5) if period_ms else None,
-        "cache_resident": bool(live_bytes < MALL_BYTES),
-        "live_tokens_per_step": round(live_tokens, 1),
-        "realized_cr": round(seen * B * Hkv / st1["live_tokens"], 3),
-        "wall_s_timed": round(wall, 4),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None if traffic is None else round(traffic),
-            "kernel": "dms_decode_attention = attention_kernel (+ reduce_kernel when a unit is split)",
-            "algorithmic_bytes_per_launch": round(live_bytes),
-        },
-        "cpu_baseline": None,
-    }
-    if not args.no_cpu_baseline and src == "array":
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps, args.cpu_units)
-    print(json.dumps(res), flush=True)
+    bench_decode(args)
 
 
 if __name__ == "__main__":

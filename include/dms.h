@@ -102,7 +102,9 @@ typedef struct {
   int64_t live_token_steps; /* sum, over dms_append_step calls, of live_tokens right after
                                the call: the visible K/V rows the following attention reads */
   int32_t sticky_error;     /* 0, or the first device-detected dms_status */
-  int32_t reserved;
+  int32_t split_mode;       /* 1 when the decode attention currently splits the live blocks
+                               in equal shares, 0 when it gives each (sequence, KV head)
+                               whole to one work-group (see dms_cache_balance) */
 } dms_stats;
 
 /* Bytes of device workspace the cache needs for `cfg`, or 0 if cfg is invalid.

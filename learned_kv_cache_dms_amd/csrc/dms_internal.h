@@ -17,7 +17,7 @@ constexpr int kMinSplitBlocks = 8;  // split mode: fewest blocks per work-group 
 // Device-side counters (one 64-byte line).
 struct Counters {
   unsigned long long bump;              // next free pool block (may overshoot on exhaustion)
-  unsigned long long live_token_steps;  // sum of live tokens after each append call
+  unsigned long long live_token_steps;  // sum of live tokens after each append (fused steps: in wg_live)
   int sticky_error;                     // first device-detected dms_status, else 0
   int pad[11];
 };
@@ -32,7 +32,7 @@ struct Layout {
   int32_t item_floats;  // floats per attention partial: m[16], l[16], o[G][d]
   int64_t max_items;    // partial slots: U + kMaxAttnWGs (split mode uses slots u + g)
   int64_t off_pool, off_btab, off_blkpos, off_blkmask, off_ring, off_n, off_pos, off_plan, off_order,
-      off_wgrange, off_ctr, off_part, total;
+      off_wgrange, off_wglive, off_ctr, off_part, total;
 };
 
 // Device pointers derived from a Layout and the workspace base, passed by
@@ -48,6 +48,7 @@ struct Dev {
   int32_t* plan;       // [U][2] split mode: first partial slot and item count of each unit
   int32_t* order;      // [U] whole-unit mode: the units, work-group by work-group
   int32_t* wg_range;   // [grid + 1] whole-unit mode: work-group g takes order[wg_range[g] .. wg_range[g+1])
+  unsigned long long* wg_live;  // [kMaxAttnWGs] fused steps: live tokens summed by work-group g
   Counters* ctr;
   float* part;         // [max_items][item_floats] attention partials
   int32_t B, Hq, Hkv, G, R, max_tokens, max_blocks, U, item_floats;

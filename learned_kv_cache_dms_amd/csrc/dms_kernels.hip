@@ -190,6 +190,7 @@ __global__ void init_kernel(Dev p) {
     p.order[g * per + min(g, extra) + k] = (int32_t)i;
   }
   for (int64_t g = tid; g <= p.grid; g += stride) p.wg_range[g] = (int32_t)(g * per + min<int64_t>(g, extra));
+  for (int64_t g = tid; g < kMaxAttnWGs; g += stride) p.wg_live[g] = 0;
   if (tid == 0) {
     p.ctr->bump = 0;
     p.ctr->live_token_steps = 0;
@@ -293,10 +294,10 @@ __device__ __forceinline__ unsigned store_token(const Dev& p, int u, int lane, c
       write_row<ES, D>(dst, t, krow, vrow, lane, zero_ch);
     if (lane == 0) {
       p.blk_pos[(int64_t)blk * 16 + t] = q;
-      if (fresh)
-        p.blk_mask[blk] = 1u;
-      else if (rs < 0)
-        p.blk_mask[blk] |= 1u << t;
+      // live slots are the dense prefix [0, n): taking slot n leaves slots
+      // 0 .. t of its block live (no read of the old mask); a reused slot
+      // was live already
+      if (rs < 0) p.blk_mask[blk] = (2u << t) - 1u;
       ring[r] = alpha ? slot : -1;
       if (rs < 0) p.n[u] = n + 1;
     }
@@ -598,11 +599,6 @@ struct Item {
   int jb, je;     // plan blocks of the unit covered by this item
   int pidx;       // partial slot of the item, or -1 when it is the whole unit
   int plan_cnt;   // split mode, the unit's first item: the unit's item count, else 0
-  // fused decode step only (whole-unit mode): the token appended to the unit
-  int q;          // its position
-  int rs;         // slot of position q - w - 1 if that token was marked (it retires now), else -1
-  int tblk;       // pool block of the slot the token goes to, -1 when a fresh block is claimed
-  int alpha;      // its eviction decision
 };
 
 __device__ __forceinline__ uint32_t wave_incl_scan_u(uint32_t x, int lane) {
@@ -719,10 +715,6 @@ __device__ __forceinline__ bool split_item(const Dev& p, const SplitPlan& pl, co
   // floor(g T / R) <= pe - 1
   const int glast = (int)(((uint64_t)pe * (uint64_t)s.R - 1ull) / s.T);
   it.plan_cnt = it.jb == 0 ? glast - s.g + 1 : 0;
-  it.q = 0;
-  it.rs = -1;
-  it.tblk = -1;
-  it.alpha = 0;
   return true;
 }
 
@@ -744,12 +736,8 @@ __device__ __forceinline__ float scalar_logit(const LogitSrc& ls, int b, int h) 
 }
 
 // The k-th item of a work-group in whole-unit mode: a whole unit, the next
-// of its range of the unit order; false past the range.  FUSED: also the
-// state the unit's append needs, read before this kernel writes any of it
-// (only the work-group that owns a unit writes its state, after its items'
-// setup).
-template <bool FUSED>
-__device__ __forceinline__ bool whole_item(const Dev& p, const Share& s, int k, const LogitSrc& logit, Item& it) {
+// of its range of the unit order; false past the range.
+__device__ __forceinline__ bool whole_item(const Dev& p, const Share& s, int k, Item& it) {
   const int i = s.w0 + k;
   if (i >= s.w1) return false;
   const int u = scalar_load(p.order + i);
@@ -761,21 +749,6 @@ __device__ __forceinline__ bool whole_item(const Dev& p, const Share& s, int k, 
   it.je = it.nblk;
   it.pidx = -1;
   it.plan_cnt = 0;
-  it.q = 0;
-  it.rs = -1;
-  it.tblk = -1;
-  it.alpha = 0;
-  if constexpr (FUSED) {
-    const int q = scalar_load(p.pos + u);
-    const int rs = scalar_load(p.ring + (int64_t)u * p.R + q % p.R);
-    const int slot = rs >= 0 ? rs : n;
-    it.q = q;
-    it.rs = rs;
-    // the slot's block exists unless the token starts a new one
-    it.tblk = (rs >= 0 || (n & 15) != 0) ? scalar_load(p.btab + (int64_t)u * p.max_blocks + (slot >> 4)) : -1;
-    const int b = u / p.Hkv;
-    it.alpha = scalar_logit(logit, b, u - b * p.Hkv) > 0.0f ? 1 : 0;  // NaN compares false
-  }
   return true;
 }
 
@@ -1050,10 +1023,14 @@ struct WaveItem {
   int cnt;       // this wave's blocks: the unit's blocks j0 + 4i, i < cnt
   int vs;        // visit stride: the wave's i-th load is its block (i * vs) mod cnt
   int pf0, pf1;  // pool ids of the first two blocks visited (pool block 0 if absent)
-  int rj;        // FUSED: logical block of the retiring slot (masked out), else -1
-  uint32_t rbit; // its bit in that block's mask
-  int q, rs, tblk, alpha;  // FUSED: the unit's append (Item)
   int n;         // the unit's live slots before the step
+  // FUSED: the token appended to the unit (wave_item_step)
+  int q;         // its position
+  int rs;        // slot of position q - w - 1 if that token was marked (it retires now), else -1
+  int rj;        // logical block of the retiring slot (masked out), else -1
+  uint32_t rbit; // its bit in that block's mask
+  int tblk;      // pool block of the slot the token goes to, -1 when it starts a new block
+  int alpha;     // its eviction decision
 };
 
 __device__ __forceinline__ int padded3(int c) { return (c + 2) / 3 * 3; }
@@ -1106,13 +1083,13 @@ __device__ __forceinline__ void wave_item_setup(const Dev& p, const int32_t* __r
   w.vs = visit_stride(w.cnt);
   w.pf0 = w.cnt > 0 ? wave_item_id(btab, p.max_blocks, w, 0) : 0;
   w.pf1 = w.cnt > 1 ? wave_item_id(btab, p.max_blocks, w, 1) : 0;
-  w.rj = __builtin_amdgcn_readfirstlane(it.rs >= 0 ? (it.rs >> 4) : -1);
-  w.rbit = 1u << (it.rs & 15);
-  w.q = __builtin_amdgcn_readfirstlane(it.q);
-  w.rs = __builtin_amdgcn_readfirstlane(it.rs);
-  w.tblk = __builtin_amdgcn_readfirstlane(it.tblk);
-  w.alpha = __builtin_amdgcn_readfirstlane(it.alpha);
   w.n = __builtin_amdgcn_readfirstlane(it.nblk > 0 ? (it.nblk - 1) * 16 + (it.tail ? it.tail : 16) : 0);
+  w.q = 0;
+  w.rs = -1;
+  w.rj = -1;
+  w.rbit = 0;
+  w.tblk = -1;
+  w.alpha = 0;
   if (it.plan_cnt > 0 && wave == 0 && lane == 0) {
     p.plan[2 * it.u] = it.pidx < 0 ? 0 : it.pidx;
     p.plan[2 * it.u + 1] = it.plan_cnt;
@@ -1131,13 +1108,32 @@ __device__ __forceinline__ void wave_item_none(WaveItem& w) {
   w.vs = 0;
   w.pf0 = 0;
   w.pf1 = 0;
-  w.rj = -1;
-  w.rbit = 0;
+  w.n = 0;
   w.q = 0;
   w.rs = -1;
+  w.rj = -1;
+  w.rbit = 0;
   w.tblk = -1;
   w.alpha = 0;
-  w.n = 0;
+}
+
+// FUSED: reads what the step's append to item w's unit needs: the new
+// token's position q, the slot that retires with it (ring entry q mod R), the
+// pool block of the slot the token goes to and its decision.  Each wave reads
+// them one item ahead (the first item's after its first block loads are
+// issued, so that those do not wait for this chain of dependent loads);
+// only wave 0 of the work-group that owns the unit writes the unit's state,
+// after every wave has passed a barrier that follows these reads.
+__device__ __forceinline__ void wave_item_step(const Dev& p, const LogitSrc& logit, WaveItem& w) {
+  w.q = scalar_load(p.pos + w.u);
+  w.rs = scalar_load(p.ring + (int64_t)w.u * p.R + w.q % p.R);
+  w.rj = w.rs >= 0 ? (w.rs >> 4) : -1;
+  w.rbit = 1u << (w.rs & 15);
+  const int slot = w.rs >= 0 ? w.rs : w.n;
+  // the slot's block exists unless the token starts a new one
+  w.tblk = (w.rs >= 0 || (w.n & 15) != 0) ? scalar_load(p.btab + (int64_t)w.u * p.max_blocks + (slot >> 4)) : -1;
+  const int b = w.u / p.Hkv;
+  w.alpha = scalar_logit(logit, b, w.u - b * p.Hkv) > 0.0f ? 1 : 0;  // NaN compares false
 }
 
 // Live-slot mask of this wave's i-th visited block of item w.  Live slots are
@@ -1186,21 +1182,28 @@ __device__ __forceinline__ void load_q_part(const Dev& p, const uint8_t* __restr
     constexpr int kHalf = kRowPieces / 2;
     const int r = min(lane, kRowPieces - 1);
     const uint8_t* src = r < kHalf ? in.k + (int64_t)u * D * ES + r * 16 : in.v + (int64_t)u * D * ES + (r - kHalf) * 16;
-    part.row = *(const u32x4*)src;
-    if (r < kHalf) clear_channel<ES>(part.row, r, in.zero_ch);
+    part.row = *(const u32x4*)src;  // the key channel is cleared when stored (store_q_part)
   }
 }
 
 template <int ES, int D, bool FUSED>
 __device__ __forceinline__ void store_q_part(AttnShared<ES, D, FUSED>& sh, int buf, int lane, int wave,
-                                             const QPart<ES, D, FUSED>& part) {
+                                             const QPart<ES, D, FUSED>& part, int zero_ch) {
   // Clamped like the load: waves past the last chunk store that chunk again,
   // with the same values (an unconditional store keeps the load waits exact).
 #pragma unroll
   for (int j = 0; j < QPart<ES, D, FUSED>::kN; ++j)
     sh.q[buf][min(wave + kWavesPerWG * j, Geo<ES, D>::kChunks - 1)][lane] = part.v[j];
-  // every wave stores the same row pieces
-  if constexpr (FUSED) sh.row[buf][min(lane, AttnShared<ES, D, FUSED>::kRowPieces - 1)] = part.row;
+  if constexpr (FUSED) {
+    // every wave stores the same row pieces; the key row with channel
+    // zero_ch cleared (here, where the loaded value is consumed anyway: a
+    // change of it right after its load would wait for every load before it)
+    constexpr int kRowPieces = AttnShared<ES, D, FUSED>::kRowPieces;
+    const int r = min(lane, kRowPieces - 1);
+    u32x4 v = part.row;
+    if (r < kRowPieces / 2) clear_channel<ES>(v, r, zero_ch);
+    sh.row[buf][r] = v;
+  }
 }
 
 template <int ES, int D, bool FUSED>
@@ -1461,7 +1464,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
     if constexpr (!FUSED) {
       if (split) return split_item(p, pl, s, k, it);
     }
-    return whole_item<FUSED>(p, s, k, in.logit, it);
+    return whole_item(p, s, k, it);
   };
 
   int k = 0;
@@ -1487,13 +1490,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
   Frag<ES, D> f0, f1, f2;
   load_frag<ES, D>(f0, p.pool + (int64_t)W0.pf0 * p.block_bytes, lane);
   load_frag<ES, D>(f1, p.pool + (int64_t)W0.pf1 * p.block_bytes, lane);
-  store_q_part<ES, D, FUSED>(sh, 0, lane, wave, q0);
+  unsigned long long live = 0;  // FUSED: live tokens after this work-group's appends (wave 0)
+  if constexpr (FUSED) {
+    // after the first block loads: their addresses do not depend on these
+    __builtin_amdgcn_sched_barrier(0);
+    wave_item_step(p, in.logit, W0);
+    if (has_next) wave_item_step(p, in.logit, W1);
+    // this work-group's running sum of live tokens, continued below
+    live = (unsigned long long)(uint32_t)scalar_load((const int32_t*)(p.wg_live + s.g)) |
+           ((unsigned long long)(uint32_t)scalar_load((const int32_t*)(p.wg_live + s.g) + 1) << 32);
+  }
+  store_q_part<ES, D, FUSED>(sh, 0, lane, wave, q0, in.zero_ch);
   __syncthreads();
   u32x4 qf[G::kChunks];
   read_q<ES, D, FUSED>(sh, 0, lane, qf);
   constexpr int kBufs = AttnShared<ES, D, FUSED>::kBufs;
   int qbuf = 0;
-  unsigned long long live = 0;  // FUSED: live tokens after the appends (wave 0)
 
   // W0 is the item being computed, W1 the next one (both held in scalar
   // registers, so moving W1 into W0 waits for no load).
@@ -1502,13 +1514,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
     QPart<ES, D, FUSED> qn;
     load_q_part<ES, D, FUSED>(p, q, in, W1.u, lane, wave, qn);  // W1's inputs, stored to LDS early in W0's block loop
     Acc<D> acc;  // set by run_item
-    run_item<ES, D, FUSED>(p, f0, f1, f2, W0, W1, qf, lane, acc,
-                           [&]() { store_q_part<ES, D, FUSED>(sh, nbuf, lane, wave, qn); });
+    run_item<ES, D, FUSED>(p, f0, f1, f2, W0, W1, qf, lane, acc, [&]() {
+      store_q_part<ES, D, FUSED>(sh, nbuf, lane, wave, qn, in.zero_ch);
+    });
     merge_item<ES, D, FUSED>(p, out, W0, acc, lane, wave, sh, qbuf, qf);
     if constexpr (FUSED) {
-      // the new token's row is in buffer qbuf, which the next item's staging
-      // (buffer nbuf, then the one after) leaves alone until this wave has
-      // passed the next merge's barriers
+      // The append, by wave 0 after the merge: the new row (staged in buffer
+      // qbuf, which the staging of the next two items leaves alone) goes to a
+      // slot this launch never reads, the retiring one (masked) or slot n
+      // (past the live prefix).  (Done inside the block stream instead, right
+      // after the item's first blocks, the call took 197 against 191 us.)
       if (wave == 0) {
         const uint8_t* krow = (const uint8_t*)&sh.row[qbuf][0];
         live += store_token<ES, D>(p, W0.u, lane, krow, krow + D * ES, W0.alpha != 0, W0.q, W0.rs, W0.n,
@@ -1522,13 +1537,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
     ++k;
     Item it;
     has_next = find_item(k + 1, it);
-    if (has_next)
+    if (has_next) {
       wave_item_setup(p, btab, wave, lane, it, W1);
-    else
+      if constexpr (FUSED) wave_item_step(p, in.logit, W1);
+    } else {
       wave_item_none(W1);
+    }
   }
   if constexpr (FUSED) {
-    if (wave == 0 && lane == 0) atomicAdd(&p.ctr->live_token_steps, live);
+    // one slot per work-group, written only by it: no contended atomic
+    if (wave == 0 && lane == 0) p.wg_live[s.g] = live;
   }
 }
 

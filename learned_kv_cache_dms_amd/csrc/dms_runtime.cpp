@@ -94,6 +94,8 @@ void make_layout(const dms_config* c, dms::Layout& L) {
   o = align_up(o + (int64_t)L.U * 4, kAlign);
   L.off_wgrange = o;
   o = align_up(o + (int64_t)(dms::kMaxAttnWGs + 1) * 4, kAlign);
+  L.off_wglive = o;
+  o = align_up(o + (int64_t)dms::kMaxAttnWGs * 8, kAlign);
   L.off_ctr = o;
   o = align_up(o + (int64_t)sizeof(dms::Counters), kAlign);
   L.off_part = o;
@@ -114,6 +116,7 @@ dms::Dev make_dev(const dms_cache* c) {
   p.plan = (int32_t*)(c->ws + L.off_plan);
   p.order = (int32_t*)(c->ws + L.off_order);
   p.wg_range = (int32_t*)(c->ws + L.off_wgrange);
+  p.wg_live = (unsigned long long*)(c->ws + L.off_wglive);
   p.ctr = (dms::Counters*)(c->ws + L.off_ctr);
   p.part = (float*)(c->ws + L.off_part);
   p.B = L.B;
@@ -555,7 +558,9 @@ int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream) {
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DMS_ERR_HIP;
   dms::Counters ctr;
   std::vector<int32_t> n(L.U), pos(L.U);
+  std::vector<unsigned long long> wg_live(c->grid);
   if (hipMemcpy(&ctr, c->ws + L.off_ctr, sizeof(ctr), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(wg_live.data(), c->ws + L.off_wglive, wg_live.size() * 8, hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemcpy(n.data(), c->ws + L.off_n, (size_t)L.U * 4, hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemcpy(pos.data(), c->ws + L.off_pos, (size_t)L.U * 4, hipMemcpyDeviceToHost) != hipSuccess)
     return DMS_ERR_HIP;
@@ -566,7 +571,9 @@ int dms_cache_stats(dms_cache* c, dms_stats* out, void* stream) {
   }
   out->allocated_blocks = (int64_t)std::min<unsigned long long>(ctr.bump, (unsigned long long)L.pool_blocks);
   out->live_token_steps = (int64_t)ctr.live_token_steps;
+  for (unsigned long long x : wg_live) out->live_token_steps += (int64_t)x;
   out->sticky_error = ctr.sticky_error;
+  out->split_mode = c->split ? 1 : 0;
   return DMS_OK;
 }
 

@@ -63,7 +63,7 @@ class dms_stats(ctypes.Structure):
         ("allocated_blocks", ctypes.c_int64),
         ("live_token_steps", ctypes.c_int64),
         ("sticky_error", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("split_mode", ctypes.c_int32),
     ]
 
 
@@ -596,6 +596,10 @@ class Cache:
     def balance(self):
         """Re-plan the attention's work split from the live counts (synchronises)."""
         dms_cache_balance(self.handle, self._stream())
+
+    def split_mode(self) -> bool:
+        """True when the attention splits the live blocks in equal shares."""
+        return bool(self.stats()["split_mode"])
 
     def stats(self) -> dict:
         return dms_cache_stats(self.handle, self._stream())
