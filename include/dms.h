@@ -227,8 +227,9 @@ DMS_API int dms_decode_attention(dms_cache* c, const void* d_q, float* d_out, vo
    work-group that attends a (sequence, KV head) also appends its token, and
    the attention reads the cache as it stood before the step without the
    retiring token, plus the new token from d_k / d_v, which is exactly the
-   visible set after the append.  In split mode it is the append, the
-   attention and the split merge.  Unlike the two calls, a sequence may be
+   visible set after the append.  In split mode it is two launches: that
+   attention, split over work-groups, then the split merge, which also
+   appends.  Unlike the two calls, a sequence may be
    empty before the step (its output is then the new token's value row).
    When the pool is exhausted (sticky DMS_ERR_OUT_OF_BLOCKS) the token that
    found no block is not stored but is still attended in this step.

@@ -998,16 +998,16 @@ __device__ __forceinline__ void attend_pair(const PairFrag<ES, D>& f, const u32x
 // no ordering between work-groups.
 template <int ES, int D, bool FUSED>
 struct AttnShared {
-  // staging buffers of the per-item inputs (Q, and the new K/V row when
-  // FUSED): the next item's are stored while the current one streams; the
-  // fused append reads the current item's after the merge, so a third
-  // buffer keeps them from being overwritten meanwhile
-  static constexpr int kBufs = FUSED ? 3 : 2;
+  // staging buffers of the per-item inputs: the next item's are stored
+  // while the current one streams.  The fused append reads the current
+  // item's new row after the merge, so the rows have a third buffer that
+  // keeps them from being overwritten meanwhile.
+  static constexpr int kRowBufs = 3;
   static constexpr int kRowPieces = 2 * D * ES / 16;  // 16-byte pieces of the K row then the V row
   f32x4 o[kWavesPerWG][Geo<ES, D>::kTiles][64];
   float m[kWavesPerWG][16], l[kWavesPerWG][16];
-  u32x4 q[kBufs][Geo<ES, D>::kChunks][64];  // Q fragments
-  u32x4 row[FUSED ? kBufs : 1][kRowPieces];  // the new token's K then V row (FUSED)
+  u32x4 q[2][Geo<ES, D>::kChunks][64];           // Q fragments
+  u32x4 row[FUSED ? kRowBufs : 1][kRowPieces];  // the new token's K then V row (FUSED)
 };
 
 // One work item as one wave sees it.  Block ids are read through the scalar
@@ -1024,6 +1024,7 @@ struct WaveItem {
   int vs;        // visit stride: the wave's i-th load is its block (i * vs) mod cnt
   int pf0, pf1;  // pool ids of the first two blocks visited (pool block 0 if absent)
   int n;         // the unit's live slots before the step
+  int first;     // 1 when the item begins at the unit's first block (it takes the new token when FUSED)
   // FUSED: the token appended to the unit (wave_item_step)
   int q;         // its position
   int rs;        // slot of position q - w - 1 if that token was marked (it retires now), else -1
@@ -1084,6 +1085,7 @@ __device__ __forceinline__ void wave_item_setup(const Dev& p, const int32_t* __r
   w.pf0 = w.cnt > 0 ? wave_item_id(btab, p.max_blocks, w, 0) : 0;
   w.pf1 = w.cnt > 1 ? wave_item_id(btab, p.max_blocks, w, 1) : 0;
   w.n = __builtin_amdgcn_readfirstlane(it.nblk > 0 ? (it.nblk - 1) * 16 + (it.tail ? it.tail : 16) : 0);
+  w.first = __builtin_amdgcn_readfirstlane(it.jb == 0 ? 1 : 0);
   w.q = 0;
   w.rs = -1;
   w.rj = -1;
@@ -1109,6 +1111,7 @@ __device__ __forceinline__ void wave_item_none(WaveItem& w) {
   w.pf0 = 0;
   w.pf1 = 0;
   w.n = 0;
+  w.first = 0;
   w.q = 0;
   w.rs = -1;
   w.rj = -1;
@@ -1187,7 +1190,7 @@ __device__ __forceinline__ void load_q_part(const Dev& p, const uint8_t* __restr
 }
 
 template <int ES, int D, bool FUSED>
-__device__ __forceinline__ void store_q_part(AttnShared<ES, D, FUSED>& sh, int buf, int lane, int wave,
+__device__ __forceinline__ void store_q_part(AttnShared<ES, D, FUSED>& sh, int buf, int rbuf, int lane, int wave,
                                              const QPart<ES, D, FUSED>& part, int zero_ch) {
   // Clamped like the load: waves past the last chunk store that chunk again,
   // with the same values (an unconditional store keeps the load waits exact).
@@ -1202,7 +1205,7 @@ __device__ __forceinline__ void store_q_part(AttnShared<ES, D, FUSED>& sh, int b
     const int r = min(lane, kRowPieces - 1);
     u32x4 v = part.row;
     if (r < kRowPieces / 2) clear_channel<ES>(v, r, zero_ch);
-    sh.row[buf][r] = v;
+    sh.row[rbuf][r] = v;
   }
 }
 
@@ -1321,7 +1324,7 @@ __device__ __forceinline__ void run_item(const Dev& p, Frag<ES, D>& f0, Frag<ES,
 
 // Merges the four waves' states of item `it` through LDS and writes the
 // output (an item that is its whole unit) or the item's partial.  FUSED: the
-// new token (staged in buffer `buf`) joins the merge as one more key.
+// new token (staged in row buffer `buf`) joins the merge as one more key.
 // Contains two work-group barriers; LDS stores made before the call (the next
 // item's staged inputs) are visible to every wave on return.
 template <int ES, int D, bool FUSED>
@@ -1356,10 +1359,12 @@ __device__ __forceinline__ void merge_item(const Dev& p, float* __restrict__ out
   for (int w = 0; w < kW; ++w) M = fmaxf(M, sh.m[w][g]);
   // wave w finishes tiles w * kTilesPerWave ...
   const int j0 = wave * kTilesPerWave;
-  float sn = -INFINITY;
+  float sn = -INFINITY;  // the new token's score: only the unit's first item takes it
   if constexpr (FUSED) {
-    sn = new_token_score<ES, D>(&sh.row[buf][0], qf, lane) * p.scale_log2e;
-    M = fmaxf(M, sn);
+    if (it.first) {
+      sn = new_token_score<ES, D>(&sh.row[buf][0], qf, lane) * p.scale_log2e;
+      M = fmaxf(M, sn);
+    }
   }
   const float Mr = (M == -INFINITY) ? 0.f : M;
   float wt[kW];
@@ -1379,7 +1384,7 @@ __device__ __forceinline__ void merge_item(const Dev& p, float* __restrict__ out
     }
   }
   if constexpr (FUSED) {
-    const float wn = exp2_fast(sn - Mr);
+    const float wn = exp2_fast(sn - Mr);  // 0 for an item without the new token
     L += wn;
 #pragma unroll
     for (int t = 0; t < kTilesPerWave; ++t)
@@ -1423,13 +1428,19 @@ __device__ __forceinline__ void merge_item(const Dev& p, float* __restrict__ out
 // 0), block ids come through the scalar cache, and values loaded before an
 // item's block loop are consumed right after its first group of loads.  A
 // wait for one value then never drains the K/V blocks in flight behind it.
-template <int ES, int D, bool FUSED>
+// What an attention launch does: kAttend, the attention alone (whole units
+// or split, as p.split says); kStepWhole, a decode step in whole-unit mode
+// (the append inside); kStepSplit, a decode step in split mode (reduce_kernel
+// appends).  The whole-unit step carries no split plan.
+constexpr int kAttend = 0, kStepWhole = 1, kStepSplit = 2;
+
+template <int ES, int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2 : 1))) void attention_kernel(
     Dev p, const int32_t* __restrict__ btab, const uint8_t* __restrict__ q, float* __restrict__ out, StepIn in) {
   using G = Geo<ES, D>;
+  constexpr bool FUSED = MODE != kAttend;
   __shared__ AttnShared<ES, D, FUSED> sh;
-  // the fused step runs in whole-unit mode only: no split plan
-  __shared__ typename std::conditional<FUSED, int, SplitPlan>::type pl;
+  __shared__ typename std::conditional<MODE == kStepWhole, int, SplitPlan>::type pl;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Share s;
@@ -1441,9 +1452,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
   s.u0 = 0;
   s.w0 = 0;
   s.w1 = 0;
-  bool split = false;
-  if constexpr (!FUSED) {
-    split = p.split != 0;
+  const bool split = MODE == kStepSplit || (MODE == kAttend && p.split != 0);
+  if constexpr (MODE != kStepWhole) {
     if (split) {
       split_plan_build(p, pl);
       const uint32_t T = __builtin_amdgcn_readfirstlane(pl.P[p.U]);
@@ -1461,7 +1471,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
     s.w1 = scalar_load(p.wg_range + s.g + 1);
   }
   auto find_item = [&](int k, Item& it) -> bool {
-    if constexpr (!FUSED) {
+    if constexpr (MODE != kStepWhole) {
       if (split) return split_item(p, pl, s, k, it);
     }
     return whole_item(p, s, k, it);
@@ -1500,38 +1510,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
     live = (unsigned long long)(uint32_t)scalar_load((const int32_t*)(p.wg_live + s.g)) |
            ((unsigned long long)(uint32_t)scalar_load((const int32_t*)(p.wg_live + s.g) + 1) << 32);
   }
-  store_q_part<ES, D, FUSED>(sh, 0, lane, wave, q0, in.zero_ch);
+  store_q_part<ES, D, FUSED>(sh, 0, 0, lane, wave, q0, in.zero_ch);
   __syncthreads();
   u32x4 qf[G::kChunks];
   read_q<ES, D, FUSED>(sh, 0, lane, qf);
-  constexpr int kBufs = AttnShared<ES, D, FUSED>::kBufs;
-  int qbuf = 0;
+  int qbuf = 0, rbuf = 0;  // staging buffers of the current item (Q: 2, rows: 3)
 
   // W0 is the item being computed, W1 the next one (both held in scalar
   // registers, so moving W1 into W0 waits for no load).
   for (;;) {
-    const int nbuf = qbuf + 1 == kBufs ? 0 : qbuf + 1;
+    const int nrbuf = rbuf + 1 == AttnShared<ES, D, FUSED>::kRowBufs ? 0 : rbuf + 1;
     QPart<ES, D, FUSED> qn;
     load_q_part<ES, D, FUSED>(p, q, in, W1.u, lane, wave, qn);  // W1's inputs, stored to LDS early in W0's block loop
     Acc<D> acc;  // set by run_item
     run_item<ES, D, FUSED>(p, f0, f1, f2, W0, W1, qf, lane, acc, [&]() {
-      store_q_part<ES, D, FUSED>(sh, nbuf, lane, wave, qn, in.zero_ch);
+      store_q_part<ES, D, FUSED>(sh, qbuf ^ 1, nrbuf, lane, wave, qn, in.zero_ch);
     });
-    merge_item<ES, D, FUSED>(p, out, W0, acc, lane, wave, sh, qbuf, qf);
+    merge_item<ES, D, FUSED>(p, out, W0, acc, lane, wave, sh, rbuf, qf);
     if constexpr (FUSED) {
-      // The append, by wave 0 after the merge: the new row (staged in buffer
-      // qbuf, which the staging of the next two items leaves alone) goes to a
+      // The append, by wave 0 after the merge: the new row (staged in row
+      // buffer rbuf, which the staging of the next two items leaves alone) goes to a
       // slot this launch never reads, the retiring one (masked) or slot n
       // (past the live prefix).  (Done inside the block stream instead, right
       // after the item's first blocks, the call took 197 against 191 us.)
-      if (wave == 0) {
-        const uint8_t* krow = (const uint8_t*)&sh.row[qbuf][0];
+      // In split mode several work-groups read a unit's state, so the split
+      // merge that follows appends instead.
+      if (MODE == kStepWhole && wave == 0) {
+        const uint8_t* krow = (const uint8_t*)&sh.row[rbuf][0];
         live += store_token<ES, D>(p, W0.u, lane, krow, krow + D * ES, W0.alpha != 0, W0.q, W0.rs, W0.n,
                                    W0.tblk, -1);
       }
     }
     if (!has_next) break;
-    qbuf = nbuf;
+    qbuf ^= 1;
+    rbuf = nrbuf;
     read_q<ES, D, FUSED>(sh, qbuf, lane, qf);
     W0 = W1;
     ++k;
@@ -1550,40 +1562,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ES == 2 ? 2
   }
 }
 
-// Split reduce: one wave per (sequence, KV head) whose attention was split
-// into several work items; merges their (m, l, o) partials by log-sum-exp:
-//   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  o = sum_s 2^(m_s - M) o_s / L.
-// Lane l handles head l % 16 and the channels 16j + 4(l/16) + r.
+// Split merge: one wave per (sequence, KV head) whose attention was split
+// into several work items; merges their (m, l, o) partials by log-sum-exp,
+//   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  o = sum_s 2^(m_s - M) o_s / L,
+// in one online pass: the partials are loaded four items at a time (all
+// loads of a group before any use), each group's max updates M and rescales
+// what was summed so far.  Lane l handles head l % 16 and the channels
+// 16j + 4(l/16) + r.
 template <int D>
-__global__ __launch_bounds__(256) void reduce_kernel(Dev p, float* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int u = blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
-  if (u >= p.U) return;
-  const int n = p.n[u], base = p.plan[2 * u], items = p.plan[2 * u + 1];
-  if (n == 0) return;
+__device__ __forceinline__ void merge_partials(const Dev& p, int u, int lane, float* __restrict__ out) {
+  const int base = p.plan[2 * u], items = p.plan[2 * u + 1];
   const int g = lane & 15;
   if (items <= 1 || g >= p.G) return;
-  const int b = u / p.Hkv, h = u - b * p.Hkv;
+  constexpr int kJ = D / 16, kU = 4;
   const int IF = p.item_floats;
   const float* pb = p.part + (int64_t)base * IF;
-  float M = -INFINITY;
-  for (int s = 0; s < items; ++s) M = fmaxf(M, pb[(int64_t)s * IF + g]);
-  const float Mr = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
-  f32x4 O[D / 16];
+  const int c0 = 4 * (lane >> 4);
+  float M = -INFINITY, L = 0.f;
+  f32x4 O[kJ];
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < items; ++s) {
-    const float* ps = pb + (int64_t)s * IF;
-    const float ws = exp2_fast(ps[g] - Mr);
-    L += ws * ps[16 + g];
+  for (int j = 0; j < kJ; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < items; s0 += kU) {
+    float ms[kU], ls[kU];
+    f32x4 os[kU][kJ];
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) O[j] += ws * *(const f32x4*)(ps + 32 + g * D + 16 * j + 4 * (lane >> 4));
+    for (int k = 0; k < kU; ++k) {
+      const float* ps = pb + (int64_t)min(s0 + k, items - 1) * IF;  // clamped: past the end weighs 0
+      ms[k] = ps[g];
+      ls[k] = ps[16 + g];
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) os[k][j] = *(const f32x4*)(ps + 32 + g * D + 16 * j + c0);
+    }
+    float mg = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kU; ++k)
+      if (s0 + k < items) mg = fmaxf(mg, ms[k]);
+    const float Mn = fmaxf(M, mg);
+    const float Mr = (Mn == -INFINITY) ? 0.f : Mn;
+    const float a = exp2_fast(M - Mr);  // 0 before the first finite max
+    L *= a;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) O[j] *= a;
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const float w = (s0 + k < items) ? exp2_fast(ms[k] - Mr) : 0.f;
+      L += w * ls[k];
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) O[j] += w * os[k][j];
+    }
+    M = Mn;
   }
+  const int b = u / p.Hkv, h = u - b * p.Hkv;
   const float inv = 1.0f / L;
-  float* orow = out + ((int64_t)b * p.Hq + h * p.G + g) * D + 4 * (lane >> 4);
+  float* orow = out + ((int64_t)b * p.Hq + h * p.G + g) * D + c0;
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j) *(f32x4*)(orow + 16 * j) = O[j] * inv;
+  for (int j = 0; j < kJ; ++j) *(f32x4*)(orow + 16 * j) = O[j] * inv;
+}
+
+// After a split attention: one wave per (sequence, KV head) merges its
+// partials (when it was cut).  STEP (a decode step in split mode): the wave
+// then appends the unit's new token, which the attention has already taken
+// from the step's input rows; the unit's state is written only now, so every
+// work-group of the attention read the state from before the step.
+template <int ES, int D, bool STEP>
+__global__ __launch_bounds__(256) void reduce_kernel(Dev p, float* __restrict__ out, StepIn in) {
+  const int lane = threadIdx.x & 63;
+  const int u = blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
+  unsigned long long live = 0;
+  if (u < p.U) {
+    merge_partials<D>(p, u, lane, out);
+    if constexpr (STEP) {
+      const int b = u / p.Hkv;
+      live = append_token<ES, D>(p, u, lane, in.k + (int64_t)u * D * ES, in.v + (int64_t)u * D * ES,
+                                 load_logit(in.logit, b, u - b * p.Hkv, 0), in.zero_ch);
+    }
+  }
+  if constexpr (STEP) add_live_token_steps(p, live);
 }
 
 // ---------------------------------------------------------------------------
@@ -2801,10 +2855,10 @@ static hipError_t attention_t(const Dev& p, const void* q, float* out, hipStream
   const dim3 grid((unsigned)p.grid), block(64 * kWavesPerWG);
   const dim3 rgrid((p.U + kWavesPerWG - 1) / kWavesPerWG);
   const StepIn none{};
-  const hipError_t e = launch_timed(attention_kernel<ES, D, false>, grid, block, s, start, p.split ? nullptr : stop,
+  const hipError_t e = launch_timed(attention_kernel<ES, D, kAttend>, grid, block, s, start, p.split ? nullptr : stop,
                                     p, (const int32_t*)p.btab, (const uint8_t*)q, out, none);
   if (e != hipSuccess || !p.split) return e;
-  return launch_timed(reduce_kernel<D>, rgrid, block, s, nullptr, stop, p, out);
+  return launch_timed(reduce_kernel<ES, D, false>, rgrid, block, s, nullptr, stop, p, out, none);
 }
 
 template <int ES, int D>
@@ -2957,12 +3011,13 @@ static int resident_of(K kernel, int num_cus) {
   return per_cu * num_cus;
 }
 
-// The launch size serves both attention kernels (the fused step and the
-// attention alone): the smaller of their resident counts.
+// The launch size serves every attention kernel (the attention alone and the
+// two decode steps): the smallest of their resident counts.
 template <int ES, int D>
 static int resident_t(int num_cus) {
-  return std::min(resident_of(attention_kernel<ES, D, false>, num_cus),
-                  resident_of(attention_kernel<ES, D, true>, num_cus));
+  return std::min({resident_of(attention_kernel<ES, D, kAttend>, num_cus),
+                   resident_of(attention_kernel<ES, D, kStepWhole>, num_cus),
+                   resident_of(attention_kernel<ES, D, kStepSplit>, num_cus)});
 }
 
 int attention_resident_wgs(int dtype, int d, int num_cus) {
@@ -2981,15 +3036,16 @@ template <int ES, int D>
 static hipError_t decode_step_t(const Dev& p, const void* q, const StepIn& in, float* out, hipStream_t s,
                                 hipEvent_t start, hipEvent_t stop) {
   const dim3 block(64 * kWavesPerWG);
+  // whole-unit mode: one launch (the append inside); split mode: the
+  // attention, then the split merge with the appends
   if (!p.split)
-    return launch_timed(attention_kernel<ES, D, true>, dim3((unsigned)p.grid), block, s, start, stop, p,
+    return launch_timed(attention_kernel<ES, D, kStepWhole>, dim3((unsigned)p.grid), block, s, start, stop, p,
                         (const int32_t*)p.btab, (const uint8_t*)q, out, in);
-  // split mode: the append, then the attention and the split merge
-  const int blocks = (p.U + kWavesPerWG - 1) / kWavesPerWG;
-  const hipError_t e = launch_timed(append_kernel<ES, D>, dim3(blocks), block, s, start, nullptr, p, in.k, in.v,
-                                    in.logit, (int)in.zero_ch);
+  const hipError_t e = launch_timed(attention_kernel<ES, D, kStepSplit>, dim3((unsigned)p.grid), block, s, start,
+                                    nullptr, p, (const int32_t*)p.btab, (const uint8_t*)q, out, in);
   if (e != hipSuccess) return e;
-  return attention_t<ES, D>(p, q, out, s, nullptr, stop);
+  const dim3 rgrid((p.U + kWavesPerWG - 1) / kWavesPerWG);
+  return launch_timed(reduce_kernel<ES, D, true>, rgrid, block, s, nullptr, stop, p, out, in);
 }
 
 hipError_t launch_decode_step(const Dev& p, int dtype, int d, const void* q, const StepIn& in, float* out,
