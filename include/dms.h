@@ -73,7 +73,8 @@ typedef enum {
   DMS_ERR_CAPACITY = -4,      /* a sequence would exceed max_tokens */
   DMS_ERR_STATE = -5,         /* call not valid in the cache's current state */
   DMS_ERR_HIP = -6,           /* a HIP runtime call or kernel launch failed */
-  DMS_ERR_DEVICE = -7         /* current device is not gfx950 */
+  DMS_ERR_DEVICE = -7,        /* current device is not gfx950 */
+  DMS_ERR_TOO_LARGE = -8      /* the call needs more scratch than the built-in buffer holds */
 } dms_status;
 
 typedef struct {
@@ -356,6 +357,29 @@ DMS_API int dms_soft_attention_forward(int32_t B, int32_t Hq, int32_t Hkv, int32
    shapes). */
 DMS_API size_t dms_soft_attention_forward_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
                                                           int32_t d);
+
+/* Async.  dms_soft_attention_forward for callers that cannot allocate
+   device memory (code under HIP graph capture, serving loops, harnesses that
+   forbid hipMalloc): the same computation and results, with its scratch (the
+   forward's workspace) in a buffer built into the library instead of a
+   caller workspace.  The buffer holds dms_soft_attention_forward_noalloc_max_bytes()
+   = 64 MiB per GPU, kept from the first call on that GPU until the process
+   ends; its address is looked up on that first call (the only setup, no
+   allocation).  Calls on one GPU share it: calls that overlap in time on
+   one GPU (different streams without ordering, or different host threads)
+   race, and must be ordered by the caller.  Nothing in the buffer carries
+   over from one call to the next.
+   Errors: as dms_soft_attention_forward; DMS_ERR_TOO_LARGE when
+   dms_soft_attention_forward_workspace_bytes of the shape exceeds the
+   buffer (nothing is enqueued); DMS_ERR_HIP if the buffer's address cannot
+   be found. */
+DMS_API int dms_soft_attention_forward_noalloc(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d,
+                                               int32_t window, float gamma, float tau, float scale, const void* d_q,
+                                               const void* d_k, const void* d_v, const float* d_logit,
+                                               const float* d_noise, float* d_out, float* d_lse, void* stream);
+
+/* Bytes of the buffer built into dms_soft_attention_forward_noalloc. */
+DMS_API size_t dms_soft_attention_forward_noalloc_max_bytes(void);
 
 /* Bytes of device workspace dms_soft_attention_backward needs (0 for bad
    shapes): copies of q, dout and k in a transposed operand layout, the row

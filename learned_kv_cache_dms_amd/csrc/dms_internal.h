@@ -122,6 +122,11 @@ int64_t soft_forward_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
 hipError_t launch_soft_forward(const SoftArgs& a, int d, const void* q, const void* k, const void* v,
                                const float* logit, const float* noise, float* out, float* lse, void* ws,
                                hipStream_t s);
+// The relaxed forward's built-in scratch (for the allocation-free entry
+// point): its size, and its device address on device `dev`, which must be
+// current (looked up the first time, then kept; null on failure).
+int64_t soft_scratch_bytes();
+void* soft_scratch_address(int dev);
 // Backward from dout (bf16, like out): dq, dk, dv (fp32, like q, k, v) and
 // dlogit (fp32, like logit); ws holds soft_backward_workspace_bytes.
 int64_t soft_backward_workspace_bytes(int B, int Hq, int Hkv, int T, int d);

@@ -51,6 +51,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <tuple>
 #include <utility>
@@ -2957,6 +2959,32 @@ hipError_t launch_soft_forward(const SoftArgs& a, int d, const void* q, const vo
                                hipStream_t s) {
   return d == 128 ? soft_forward_t<128>(a, q, k, v, logit, noise, out, lse, (uint8_t*)ws, s)
                   : soft_forward_t<64>(a, q, k, v, logit, noise, out, lse, (uint8_t*)ws, s);
+}
+
+// Allocation-free relaxed forward: its scratch (v's transposed copy and the
+// keys' biases, soft_forward_workspace_bytes) lives in this file-scope device
+// array instead of a caller workspace.  Host code never passes the array's
+// name to a kernel (there it is a host-side stand-in): its address on each
+// device is looked up once, with that device current, and kept.
+constexpr int64_t kSoftScratchBytes = 64ll << 20;
+static __device__ __align__(256) uint8_t scratch[kSoftScratchBytes];
+
+int64_t soft_scratch_bytes() { return kSoftScratchBytes; }
+
+void* soft_scratch_address(int dev) {
+  constexpr int kMaxDevices = 256;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  static std::mutex mu;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = ptrs[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(mu);
+  ptr = ptrs[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    ptrs[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
 }
 
 template <int D>

@@ -638,6 +638,26 @@ int dms_soft_attention_forward(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, in
                                              (hipStream_t)stream));
 }
 
+int dms_soft_attention_forward_noalloc(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d, int32_t window,
+                                       float gamma, float tau, float scale, const void* d_q, const void* d_k,
+                                       const void* d_v, const float* d_logit, const float* d_noise, float* d_out,
+                                       float* d_lse, void* stream) {
+  if (!d_q || !d_k || !d_v || !d_logit || !d_noise || !d_out || !d_lse) return DMS_ERR_ARG;
+  dms::SoftArgs a;
+  int st = soft_args(B, Hq, Hkv, T, d, window, gamma, tau, scale, &a);
+  if (st != DMS_OK) return st;
+  if (dms::soft_forward_workspace_bytes(B, Hq, Hkv, T, d) > dms::soft_scratch_bytes()) return DMS_ERR_TOO_LARGE;
+  int dev;
+  st = current_gfx950_device(&dev);
+  if (st != DMS_OK) return st;
+  void* ws = dms::soft_scratch_address(dev);
+  if (!ws) return DMS_ERR_HIP;
+  return hip_status(
+      dms::launch_soft_forward(a, d, d_q, d_k, d_v, d_logit, d_noise, d_out, d_lse, ws, (hipStream_t)stream));
+}
+
+size_t dms_soft_attention_forward_noalloc_max_bytes(void) { return (size_t)dms::soft_scratch_bytes(); }
+
 size_t dms_soft_attention_backward_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d) {
   if (!soft_shapes_ok(B, Hq, Hkv, T, d)) return 0;
   return (size_t)dms::soft_backward_workspace_bytes(B, Hq, Hkv, T, d);
@@ -674,6 +694,7 @@ const char* dms_status_str(int status) {
     case DMS_ERR_STATE: return "DMS_ERR_STATE: call not valid in the cache's current state";
     case DMS_ERR_HIP: return "DMS_ERR_HIP: HIP runtime or launch failure";
     case DMS_ERR_DEVICE: return "DMS_ERR_DEVICE: current device is not gfx950";
+    case DMS_ERR_TOO_LARGE: return "DMS_ERR_TOO_LARGE: the call needs more scratch than the built-in buffer holds";
     default: return "unknown dms status";
   }
 }

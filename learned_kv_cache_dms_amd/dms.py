@@ -29,6 +29,7 @@ DMS_ERR_CAPACITY = -4
 DMS_ERR_STATE = -5
 DMS_ERR_HIP = -6
 DMS_ERR_DEVICE = -7
+DMS_ERR_TOO_LARGE = -8
 
 DMS_LOGIT_FROM_K = 0
 DMS_LOGIT_FROM_Q = 1
@@ -111,6 +112,9 @@ def _load():
         "dms_soft_attention_forward": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                                       ctypes.c_float, ctypes.c_float] + [vp] * 8 + [sz, vp]),
         "dms_soft_attention_forward_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "dms_soft_attention_forward_noalloc": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, ctypes.c_float,
+                                                              ctypes.c_float, ctypes.c_float] + [vp] * 7 + [vp]),
+        "dms_soft_attention_forward_noalloc_max_bytes": (sz, []),
         "dms_soft_attention_backward_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "dms_soft_attention_backward": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                                        ctypes.c_float, ctypes.c_float] + [vp] * 13 + [sz, vp]),
@@ -326,6 +330,17 @@ def dms_soft_attention_forward(B, Hq, Hkv, T, d, window, gamma, tau, scale, d_q,
                                           d_workspace, int(workspace_bytes), stream), "dms_soft_attention_forward")
 
 
+def dms_soft_attention_forward_noalloc(B, Hq, Hkv, T, d, window, gamma, tau, scale, d_q, d_k, d_v, d_logit,
+                                       d_noise, d_out, d_lse, stream: int = 0):
+    _check(lib.dms_soft_attention_forward_noalloc(int(B), int(Hq), int(Hkv), int(T), int(d), int(window),
+                                                  float(gamma), float(tau), float(scale), d_q, d_k, d_v, d_logit,
+                                                  d_noise, d_out, d_lse, stream), "dms_soft_attention_forward_noalloc")
+
+
+def dms_soft_attention_forward_noalloc_max_bytes() -> int:
+    return int(lib.dms_soft_attention_forward_noalloc_max_bytes())
+
+
 def dms_soft_attention_backward_workspace_bytes(B, Hq, Hkv, T, d) -> int:
     return int(lib.dms_soft_attention_backward_workspace_bytes(int(B), int(Hq), int(Hkv), int(T), int(d)))
 
@@ -369,6 +384,21 @@ def soft_attention_forward(q, k, v, logit, noise, window, gamma=0.0, tau=1.0, sc
     dms_soft_attention_forward(B, Hq, Hkv, T, d, window, gamma, tau, scale, q.data_ptr(), k.data_ptr(),
                                v.data_ptr(), logit.data_ptr(), noise.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                workspace.data_ptr(), workspace.numel(), torch.cuda.current_stream().cuda_stream)
+    return out, lse
+
+
+def soft_attention_forward_noalloc(q, k, v, logit, noise, window, out, lse, gamma=0.0, tau=1.0, scale=0.0):
+    """dms_soft_attention_forward_noalloc on torch tensors: the caller passes
+    out [B, Hq, T, d] and lse [B, Hq, T] (fp32); the library allocates
+    nothing."""
+    import torch
+    B, Hq, Hkv, T, d = _soft_check(q, k, v, logit, noise)
+    for t, shape, name in ((out, (B, Hq, T, d), "out"), (lse, (B, Hq, T), "lse")):
+        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name}: expected contiguous float32 {shape} on the GPU")
+    dms_soft_attention_forward_noalloc(B, Hq, Hkv, T, d, window, gamma, tau, scale, q.data_ptr(), k.data_ptr(),
+                                       v.data_ptr(), logit.data_ptr(), noise.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr(), torch.cuda.current_stream().cuda_stream)
     return out, lse
 
 
