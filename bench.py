@@ -55,12 +55,16 @@ MALL_BYTES = 256 * 2**20
 ROTATE_BYTES = 2**30
 # MI355X dense bf16 matrix-core peak (no sparsity)
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-KERNEL_SRCS = [os.path.join(ROOT, "learned_kv_cache_dms_amd", "csrc", f) for f in ("dms_kernels.hip", "dms_runtime.cpp")]
+# the sources that decide a decode call's HBM traffic: the decode kernels, the
+# device helpers they share and the runtime that plans their launches
+KERNEL_SRCS = [os.path.join(ROOT, "learned_kv_cache_dms_amd", "csrc", f)
+               for f in ("dms_device.h", "dms_decode.hip", "dms_runtime.cpp")]
 
 
 def kernel_source_hash() -> str:
-    """First 16 hex digits of the SHA-256 of the kernels and of the runtime
-    that plans their launches (both decide the traffic of a call)."""
+    """First 16 hex digits of the SHA-256 of the decode kernels, their shared
+    device helpers and the runtime that plans their launches (together they
+    decide the traffic of a decode call)."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
         with open(path, "rb") as f:
@@ -92,6 +96,42 @@ def calib_copy(nbytes: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calib_copy_bytes": nbytes, "launches": 5}), flush=True)
+
+
+def calib_read(nbytes: int, reps: int = 20):
+    """The HBM read ceiling: a plain streaming read (synth's read_kernel, 16
+    bytes per lane, nontemporal, four loads in flight per thread) of nbytes,
+    run back to back; for each grid size the mean time per launch over
+    `reps` launches bracketed by one event pair, and the best single launch
+    (an event pair each).  One JSON line per grid size."""
+    import torch
+    from synth import device as dsynth
+    n = nbytes // 16 * 16
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    for grid in (512, 1024, 2048, 4096):
+        sink = torch.empty(grid, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            dsynth.stream_read(src, grid, sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            dsynth.stream_read(src, grid, sink)
+        b.record()
+        torch.cuda.synchronize()
+        mean_s = a.elapsed_time(b) / reps / 1e3
+        single = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dsynth.stream_read(src, grid, sink)
+            e1.record()
+            single.append((e0, e1))
+        torch.cuda.synchronize()
+        best_s = min(x.elapsed_time(y) for x, y in single) / 1e3
+        print(json.dumps({"calib_read_bytes": n, "grid": grid, "launches": reps,
+                          "mean_us": round(mean_s * 1e6, 2), "mean_gbps": round(n / mean_s / 1e9, 1),
+                          "best_us": round(best_s * 1e6, 2), "best_gbps": round(n / best_s / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(wl, steps_per_unit: int, n_units: int):
@@ -816,7 +856,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=24)
     ap.add_argument("--cpu-steps", type=int, default=256)
-    ap.add_argument("--calib-copy-bytes", type=int, default=0)
+    ap.add_argument("--calib-copy-bytes", type=int, default=0,
+                    help="plain copy of this many bytes (to scale the HBM byte counters)")
+    ap.add_argument("--calib-read-bytes", type=int, default=0,
+                    help="plain streaming read of this many bytes: the HBM read ceiling")
     ap.add_argument("--event-every", type=int, default=8,
                     help="decode bench: time every N-th attention call of the timed region with its own "
                          "kernel-stamped event pair (roofline.achieved is their mean)")
@@ -853,6 +896,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calib_copy_bytes:
         calib_copy(args.calib_copy_bytes)
+        return
+    if args.calib_read_bytes:
+        calib_read(args.calib_read_bytes)
         return
     if args.prefill_attention:
         bench_prefill_attention(args)

@@ -59,10 +59,14 @@ def _run(cmd):
         raise RuntimeError(f"build failed ({r.returncode}): {' '.join(cmd)}")
 
 
+# the kernels by subsystem, and the host runtime behind the C ABI
+DMS_SOURCES = ("dms_decode.hip", "dms_prompt.hip", "dms_soft.hip", "dms_runtime.cpp")
+
+
 def build_dms(out: str = LIB, extra=()):
     tmp = out + ".tmp"
     _run([hipcc(), *COMMON, *DMS_DEVICE, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-          os.path.join(CSRC, "dms_kernels.hip"), os.path.join(CSRC, "dms_runtime.cpp"), "-o", tmp])
+          *[os.path.join(CSRC, f) for f in DMS_SOURCES], "-o", tmp])
     os.replace(tmp, out)
     return out
 

@@ -1,5 +1,6 @@
 // Internal layout of the DMS cache workspace and the launch interface between
-// the host runtime (dms_runtime.cpp) and the kernels (dms_kernels.hip).
+// the host runtime (dms_runtime.cpp) and the kernels (dms_decode.hip,
+// dms_prompt.hip, dms_soft.hip).
 #pragma once
 
 #include <hip/hip_runtime_api.h>

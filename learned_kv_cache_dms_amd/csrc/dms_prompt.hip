@@ -1,0 +1,511 @@
+// DMS attention of several queries per sequence for gfx950 (MI355X):
+//   * prefill_attention_kernel: every prompt query over its own visible set,
+//     from the compressed cache (positions below q - w) and the dense prompt
+//     (the window), right after the prompt's compression;
+//   * chunk_attention_kernel + append_chunk_kernel: the queries of a chunk of
+//     tokens over the cache as it stands plus the chunk's own rows, then the
+//     chunk's appends in order.
+#include "dms_device.h"
+
+namespace dms {
+// ---------------------------------------------------------------------------
+// attention of the prompt's own queries, after the prompt's compression
+// ---------------------------------------------------------------------------
+
+// Query q attends Vis(q) = { j < q - w : j unmarked } + [q - w, q] (every
+// token of the last w + 1 positions is visible, marked or not).  The first
+// part is exactly the cache slots whose position is below q - w: right after
+// the compression the cache holds every unmarked prompt token, and the marked
+// tokens it still holds sit at positions >= P - 1 - w >= q - w; its slots are
+// in position order.  The second part is read from the dense prompt.  The two
+// parts are disjoint and the decisions themselves are never needed.
+//
+
+// Fragment (the cache block order) of 16 consecutive dense rows row0 ..
+// row0 + 15 of one (sequence, KV head), rows clamped to `last` (the clamped
+// rows are masked out by the caller; they only have to be finite).
+template <int ES, int D>
+__device__ __forceinline__ void load_frag_dense(Frag<ES, D>& f, const uint8_t* __restrict__ K,
+                                                const uint8_t* __restrict__ V, int row0, int last, int lane,
+                                                int zero_ch = -1) {
+  using G = Geo<ES, D>;
+  // K: lane l carries row l % 16, 16-byte piece 4c + l / 16 of the row
+  // (key channel zero_ch, when >= 0, is read as 0, as the cache stores it)
+  const uint8_t* krow = K + (int64_t)min(row0 + (lane & 15), last) * D * ES;
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) {
+    f.k[c] = *(const u32x4*)(krow + c * 64 + 16 * (lane >> 4));
+    clear_channel<ES>(f.k[c], 4 * c + (lane >> 4), zero_ch);
+  }
+  // V: lane l carries rows 4 (l / 16) + e, channel 16 (c kNJ + jj) + l % 16
+  const uint8_t* vrow[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vrow[e] = V + (int64_t)min(row0 + 4 * (lane >> 4) + e, last) * D * ES;
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) {
+    u32x4 val = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int jj = 0; jj < G::kNJ; ++jj) {
+      const int ch = 16 * (c * G::kNJ + jj) + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (ES == 2) {
+          const unsigned x = *(const uint16_t*)(vrow[e] + ch * 2);
+          val[jj * 2 + (e >> 1)] |= x << (16 * (e & 1));
+        } else {
+          val[e] = *(const uint32_t*)(vrow[e] + ch * 4);
+        }
+      }
+    }
+    f.v[c] = val;
+  }
+}
+
+// Grid (ceil(max_len_used / kPfTile), Hq, B).
+template <int ES, int D>
+__global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uint8_t* __restrict__ q,
+                                                                const uint8_t* __restrict__ k,
+                                                                const uint8_t* __restrict__ v, int32_t max_len,
+                                                                int zero_ch, float* __restrict__ out) {
+  using G = Geo<ES, D>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.z, hq = blockIdx.y;
+  const int h = hq / p.G, u = b * p.Hkv + h;
+  const int P = __builtin_amdgcn_readfirstlane(p.pos[u]);
+  const int q0 = blockIdx.x * kPfTile;
+  if (q0 >= P) return;
+  const int w = p.R - 1;
+  const int qmax = min(q0 + kPfTile, P) - 1;
+  const int64_t unit_rows = ((int64_t)b * p.Hkv + h) * max_len;
+  const uint8_t* Ku = k + unit_rows * D * ES;
+  const uint8_t* Vu = v + unit_rows * D * ES;
+  const uint8_t* Qh = q + ((int64_t)b * p.Hq + hq) * max_len * D * ES;
+
+  int qc[kPfCols];
+  u32x4 qf[kPfCols][G::kChunks];
+  Acc<D> acc[kPfCols];
+#pragma unroll
+  for (int t = 0; t < kPfCols; ++t) {
+    qc[t] = q0 + 16 * (kPfCols * wave + t) + (lane & 15);
+    const uint8_t* qrow = Qh + (int64_t)min(qc[t], P - 1) * D * ES;
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) qf[t][c] = *(const u32x4*)(qrow + c * 64 + 16 * (lane >> 4));
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) acc[t].o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[t].m = -INFINITY;
+    acc[t].l = 0.f;
+  }
+  const int tb = 4 * (lane >> 4);
+
+  // Far part: the cache blocks whose first slot lies below qmax - w (slot
+  // positions increase, so they are a prefix); counted with one round of
+  // independent loads of the blocks' first positions.
+  const int n = __builtin_amdgcn_readfirstlane(p.n[u]);
+  const int nb = (n + 15) >> 4;
+  const int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
+  const int lim = qmax - w;
+  // nfar: blocks whose first slot lies below qmax - w.  nfull: blocks j whose
+  // next block starts at or below q0 - w; all 16 slots of such a block lie
+  // below q0 - w, so every key in it is far for every query of the tile.
+  // Slot positions increase, so both are prefixes; one round of independent
+  // loads of the blocks' first positions counts them.
+  int nfar = 0, nlow = 0;
+  for (int j0 = 0; j0 < nb; j0 += 64) {
+    const int j = j0 + lane;
+    int c = 0, d2 = 0;
+    if (j < nb) {
+      const int first = p.blk_pos[(int64_t)bt[j] * 16];
+      c = first < lim ? 1 : 0;
+      d2 = first <= q0 - w ? 1 : 0;
+    }
+    nfar += wave_sum_i(c);
+    nlow += wave_sum_i(d2);
+  }
+  nfar = __builtin_amdgcn_readfirstlane(nfar);
+  const int nfull = min(max(__builtin_amdgcn_readfirstlane(nlow) - 1, 0), nfar);
+  auto blk_at = [&](int j, int jmax) { return __builtin_amdgcn_readfirstlane(bt[min(j, jmax)]); };
+  if (nfull > 0) {
+    // Whole blocks, in pairs, one pair loaded ahead of the one computed.
+    // Loads are unconditional: an index past the last whole block re-reads
+    // it, and its keys are masked out.  The scheduling barriers keep each
+    // pair's loads issued ahead of the previous pair's arithmetic (left alone,
+    // the scheduler sinks them next to their use, exposing their latency).
+    const int npair = (nfull + 1) >> 1;
+    auto fetch = [&](PairFrag<ES, D>& f, int i) {
+      const int ba = blk_at(2 * i, nfull - 1), bb = blk_at(2 * i + 1, nfull - 1);
+      load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
+    };
+    auto compute = [&](const PairFrag<ES, D>& f, int i) {
+      const uint32_t mb = 2 * i + 1 < nfull ? 0xffffu : 0u;
+      if constexpr (ES == 2) {
+        // column t + 1's score products issued before column t's softmax
+        f32x4 SA[2], SB[2];
+        score_pair<D>(f, qf[0], SA[0], SB[0]);
+#pragma unroll
+        for (int t = 0; t < kPfCols; ++t) {
+          if (t + 1 < kPfCols) score_pair<D>(f, qf[t + 1], SA[(t + 1) & 1], SB[(t + 1) & 1]);
+          softmax_pv_masked<D>(f, SA[t & 1], SB[t & 1], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < kPfCols; ++t) attend_pair<ES, D>(f, qf[t], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
+      }
+    };
+    PairFrag<ES, D> f0, f1;
+    fetch(f0, 0);
+    for (int i = 0; i < npair; i += 2) {
+      fetch(f1, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f0, i);
+      if (i + 1 >= npair) break;
+      fetch(f0, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f1, i + 1);
+    }
+  }
+  // The far blocks that straddle q - w for some query of the tile: masked
+  // per slot position (a key is far for query q when its position is < q - w).
+  for (int j = nfull; j < nfar; j += 2) {
+    const int ba = blk_at(j, nfar - 1), bb = blk_at(j + 1, nfar - 1);
+    PairFrag<ES, D> f;
+    load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
+    const int4 pa = *(const int4*)(p.blk_pos + (int64_t)ba * 16 + tb);
+    const int4 pb = *(const int4*)(p.blk_pos + (int64_t)bb * 16 + tb);
+    const int lva = n - 16 * j, lvb = j + 1 < nfar ? n - 16 * (j + 1) : 0;  // live slots
+#pragma unroll
+    for (int t = 0; t < kPfCols; ++t) {
+      const int lt = qc[t] - w;
+      uint32_t ma = 0, mb = 0;
+      const int xa[4] = {pa.x, pa.y, pa.z, pa.w}, xb[4] = {pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (tb + r < lva && xa[r] < lt) ma |= 1u << (tb + r);
+        if (tb + r < lvb && xb[r] < lt) mb |= 1u << (tb + r);
+      }
+      attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
+    }
+  }
+
+  // Near part: dense rows max(0, q0 - w) .. qmax, all visible within the
+  // window, 32 rows per softmax step.
+  auto near_mask = [&](int r0, int t) -> uint32_t {
+    uint32_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pos = r0 + tb + r;
+      if (pos <= qc[t] && pos >= qc[t] - w && pos < P) m |= 1u << (tb + r);
+    }
+    return m;
+  };
+  for (int r0 = max(0, q0 - w); r0 <= qmax; r0 += 32) {
+    Frag<ES, D> fa, fb;
+    load_frag_dense<ES, D>(fa, Ku, Vu, r0, P - 1, lane, zero_ch);
+    load_frag_dense<ES, D>(fb, Ku, Vu, r0 + 16, P - 1, lane, zero_ch);
+    PairFrag<ES, D> f;
+    make_pair<ES, D>(f, fa, fb);
+#pragma unroll
+    for (int t = 0; t < kPfCols; ++t)
+      attend_pair<ES, D>(f, qf[t], near_mask(r0, t), near_mask(r0 + 16, t), lane, p.scale_log2e, acc[t]);
+  }
+
+#pragma unroll
+  for (int t = 0; t < kPfCols; ++t) {
+    // each lane's l sums its own 4 keys of every block: add the 4 lane groups
+    // of the column (all share the column's running max)
+    float lt = acc[t].l + __shfl_xor(acc[t].l, 16);
+    lt = lt + __shfl_xor(lt, 32);
+    if (qc[t] >= P) continue;
+    const float inv = 1.0f / lt;
+    float* orow = out + (((int64_t)b * p.Hq + hq) * max_len + qc[t]) * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(orow + 16 * j) = acc[t].o[j] * inv;
+  }
+}
+
+// `chunk` consecutive tokens per unit, in order, as that many append_kernel
+// launches would: k, v [U, chunk, d]; the logit of token j from `logit` at
+// position j.
+template <int ES, int D>
+__global__ __launch_bounds__(256) void append_chunk_kernel(Dev p, const uint8_t* __restrict__ k,
+                                                           const uint8_t* __restrict__ v, LogitSrc logit,
+                                                           int zero_ch, int chunk) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x * kWavesPerWG + wave;
+  unsigned long long live = 0;
+  if (u < p.U) {
+    const int b = u / p.Hkv, h = u - b * p.Hkv;
+    for (int j = 0; j < chunk; ++j) {
+      const int64_t row = (int64_t)u * chunk + j;
+      live += append_token<ES, D>(p, u, lane, k + row * D * ES, v + row * D * ES, load_logit(logit, b, h, j),
+                                  zero_ch);
+    }
+  }
+  add_live_token_steps(p, live);
+}
+
+// ---------------------------------------------------------------------------
+// decode of a chunk of consecutive tokens: attention, then the appends
+// ---------------------------------------------------------------------------
+
+// Chunk query j (position q0 + j, q0 = the unit's length before the chunk)
+// attends Vis(q0 + j), read before any token of the chunk is appended:
+//  - every cached token that is not a pending marked one (an unmarked token
+//    stays visible for good);
+//  - a pending marked token (a slot held by the ring) while its position is
+//    >= q0 + j - w;
+//  - chunk row i <= j when it is unmarked or i >= j - w.
+// Marked tokens that left the cache before the chunk are invisible to every
+// chunk query too, so this is exactly the visible set of each step.  The
+// pending slots come from the ring into a per-block bitmap in LDS.
+//
+// Work-group = 4 waves = one (sequence, KV head) unit and kPfTile columns;
+// column c = j G + g carries query head h G + g of chunk position j, so the
+// group's heads share every loaded block as in the decode kernel.
+constexpr int kChunkMaxBlocks = 8192;
+
+// NC tiles of 16 columns per wave.  Grid (U, ceil(chunk G / (64 NC))).
+// q [B, Hq, chunk, d]; k, v [B, Hkv,
+// chunk, d]; logit [B, Hkv, chunk]; out [B, Hq, chunk, d].
+//
+// The work-group's columns need 1 to 4 waves of NC tiles each.  When
+// they fit in one or two waves, the idle waves split the key stream instead
+// (4 or 2 ways: wave w takes every nsplit-th pair of blocks and of chunk
+// rows), and the waves of one tile group merge their softmax states through
+// LDS at the end, tile by tile.
+template <int ES, int D, int NC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && ES == 2 ? 2 : 1))) void chunk_attention_kernel(Dev p, const uint8_t* __restrict__ q,
+                                                              const uint8_t* __restrict__ k,
+                                                              const uint8_t* __restrict__ v, LogitSrc logit,
+                                                              int zero_ch, int chunk, float* __restrict__ out) {
+  using G = Geo<ES, D>;
+  __shared__ uint32_t pend[kChunkMaxBlocks];
+  __shared__ f32x4 mo[kWavesPerWG - 1][G::kTiles][64];
+  __shared__ float mm[kWavesPerWG - 1][64], ml[kWavesPerWG - 1][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x;
+  const int b = u / p.Hkv, h = u - b * p.Hkv;
+  const int n = __builtin_amdgcn_readfirstlane(p.n[u]);
+  const int nb = (n + 15) >> 4;
+  const int q0 = __builtin_amdgcn_readfirstlane(p.pos[u]);
+  const int w = p.R - 1;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) pend[i] = 0u;
+  __syncthreads();
+  const int32_t* ring = p.ring + (int64_t)u * p.R;
+  for (int r = threadIdx.x; r < p.R; r += blockDim.x) {
+    const int sl = ring[r];
+    if (sl >= 0 && sl < n) atomicOr(&pend[sl >> 4], 1u << (sl & 15));
+  }
+  __syncthreads();
+
+  const int ncol = chunk * p.G;
+  const int cwg = blockIdx.y * (16 * NC * kWavesPerWG);
+  const int wg_cols = min((16 * NC * kWavesPerWG), ncol - cwg);
+  const int need = (wg_cols + 16 * NC - 1) / (16 * NC);  // waves with columns
+  const int nsplit = need == 1 ? 4 : (need == 2 ? 2 : 1);
+  const int tg = wave / nsplit, sp = wave - tg * nsplit;
+  if (tg >= need) return;  // only when nsplit == 1: no barrier follows for this work-group
+  const int c0 = cwg + 16 * NC * tg;
+  const int tb = 4 * (lane >> 4);
+  int qj[NC], qg[NC];
+  u32x4 qf[NC][G::kChunks];
+  Acc<D> acc[NC];
+#pragma unroll
+  for (int t = 0; t < NC; ++t) {
+    const int col = min(c0 + 16 * t + (lane & 15), ncol - 1);
+    qj[t] = col / p.G;
+    qg[t] = col - qj[t] * p.G;
+    const uint8_t* qrow = q + (((int64_t)b * p.Hq + h * p.G + qg[t]) * chunk + qj[t]) * D * ES;
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) qf[t][c] = *(const u32x4*)(qrow + c * 64 + 16 * (lane >> 4));
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) acc[t].o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[t].m = -INFINITY;
+    acc[t].l = 0.f;
+  }
+
+  // Cached tokens: this wave's pairs of blocks i = sp, sp + nsplit, ...,
+  // one pair loaded ahead of the one computed.  Loads are unconditional
+  // (clamped indices; a pair past the wave's last is masked out).
+  const int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
+  const int npair = (nb + 1) >> 1;
+  const int cnt = sp < npair ? (npair - sp + nsplit - 1) / nsplit : 0;
+  if (cnt > 0) {
+    struct Meta {
+      int4 pa, pb;
+      uint32_t wa, wb;
+    };
+    auto fetch = [&](PairFrag<ES, D>& f, Meta& m, int kk) {
+      const int i = min(sp + nsplit * kk, npair - 1);
+      const int ja = 2 * i, jb = min(2 * i + 1, nb - 1);
+      const int ba = __builtin_amdgcn_readfirstlane(bt[ja]), bb = __builtin_amdgcn_readfirstlane(bt[jb]);
+      load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
+      m.pa = *(const int4*)(p.blk_pos + (int64_t)ba * 16 + tb);
+      m.pb = *(const int4*)(p.blk_pos + (int64_t)bb * 16 + tb);
+      m.wa = pend[ja];
+      m.wb = pend[jb];
+    };
+    auto compute = [&](const PairFrag<ES, D>& f, const Meta& m, int kk) {
+      const int i = sp + nsplit * kk;
+      const bool ok = i < npair;
+      const int ja = 2 * i;
+      const int lva = ok ? n - 16 * ja : 0, lvb = ok && ja + 1 < nb ? n - 16 * (ja + 1) : 0;
+      const int xa[4] = {m.pa.x, m.pa.y, m.pa.z, m.pa.w}, xb[4] = {m.pb.x, m.pb.y, m.pb.z, m.pb.w};
+#pragma unroll
+      for (int t = 0; t < NC; ++t) {
+        const int lt = q0 + qj[t] - w;  // a pending token is visible from position >= lt
+        uint32_t ma = 0, mb = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int bit = tb + r;
+          if (bit < lva && (!((m.wa >> bit) & 1u) || xa[r] >= lt)) ma |= 1u << bit;
+          if (bit < lvb && (!((m.wb >> bit) & 1u) || xb[r] >= lt)) mb |= 1u << bit;
+        }
+        attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
+      }
+    };
+    PairFrag<ES, D> f0, f1;
+    Meta m0, m1;
+    fetch(f0, m0, 0);
+    for (int kk = 0; kk < cnt; kk += 2) {
+      fetch(f1, m1, kk + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f0, m0, kk);
+      if (kk + 1 >= cnt) break;
+      fetch(f0, m0, kk + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f1, m1, kk + 1);
+    }
+  }
+
+  // The chunk's own rows, 32 per step, every nsplit-th step for this wave.
+  const uint8_t* Ku = k + (int64_t)u * chunk * D * ES;
+  const uint8_t* Vu = v + (int64_t)u * chunk * D * ES;
+  for (int r0 = 32 * sp; r0 < chunk; r0 += 32 * nsplit) {
+    Frag<ES, D> fa, fb;
+    load_frag_dense<ES, D>(fa, Ku, Vu, r0, chunk - 1, lane, zero_ch);
+    load_frag_dense<ES, D>(fb, Ku, Vu, r0 + 16, chunk - 1, lane, zero_ch);
+    PairFrag<ES, D> f;
+    make_pair<ES, D>(f, fa, fb);
+    bool unmarked_a[4], unmarked_b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      unmarked_a[r] = !(load_logit(logit, b, h, min(r0 + tb + r, chunk - 1)) > 0.0f);
+      unmarked_b[r] = !(load_logit(logit, b, h, min(r0 + 16 + tb + r, chunk - 1)) > 0.0f);
+    }
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+      uint32_t ma = 0, mb = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ia = r0 + tb + r, ib = r0 + 16 + tb + r;
+        if (ia <= qj[t] && (unmarked_a[r] || ia >= qj[t] - w)) ma |= 1u << (tb + r);
+        if (ib <= qj[t] && (unmarked_b[r] || ib >= qj[t] - w)) mb |= 1u << (tb + r);
+      }
+      attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
+    }
+  }
+
+  // Merge the split waves' states (per lane: same column, same lane group),
+  // then normalise and write.  nsplit is uniform over the work-group, so every
+  // wave takes the same barriers.
+#pragma unroll
+  for (int t = 0; t < NC; ++t) {
+    if (nsplit > 1) {
+      if (sp > 0) {
+        const int slot = (tg * nsplit + sp) - tg - 1;  // the split waves' LDS slots: 0 .. 4 - need - 1
+#pragma unroll
+        for (int j = 0; j < G::kTiles; ++j) mo[slot][j][lane] = acc[t].o[j];
+        mm[slot][lane] = acc[t].m;
+        ml[slot][lane] = acc[t].l;
+      }
+      __syncthreads();
+      if (sp == 0) {
+        float M = acc[t].m;
+        for (int x = 1; x < nsplit; ++x) M = fmaxf(M, mm[tg * (nsplit - 1) + x - 1][lane]);
+        const float Mr = M == -INFINITY ? 0.f : M;
+        const float w0 = exp2_fast(acc[t].m - Mr);
+        float L = acc[t].l * w0;
+#pragma unroll
+        for (int j = 0; j < G::kTiles; ++j) acc[t].o[j] *= w0;
+        for (int x = 1; x < nsplit; ++x) {
+          const int slot = tg * (nsplit - 1) + x - 1;
+          const float wx = exp2_fast(mm[slot][lane] - Mr);
+          L += ml[slot][lane] * wx;
+#pragma unroll
+          for (int j = 0; j < G::kTiles; ++j) acc[t].o[j] += mo[slot][j][lane] * wx;
+        }
+        acc[t].l = L;
+      }
+      __syncthreads();
+    }
+    float lt = acc[t].l + __shfl_xor(acc[t].l, 16);
+    lt = lt + __shfl_xor(lt, 32);
+    if (sp != 0 || c0 + 16 * t + (lane & 15) >= ncol) continue;
+    const float inv = 1.0f / lt;
+    float* orow = out + (((int64_t)b * p.Hq + h * p.G + qg[t]) * chunk + qj[t]) * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) *(f32x4*)(orow + 16 * j) = acc[t].o[j] * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+template <int ES, int D>
+static hipError_t prefill_attention_t(const Dev& p, const void* q, const void* k, const void* v, int32_t max_len,
+                                      int32_t max_prompt, int zero_ch, float* out, hipStream_t s) {
+  const dim3 grid((unsigned)((max_prompt + kPfTile - 1) / kPfTile), (unsigned)p.Hq, (unsigned)p.B);
+  return launch(prefill_attention_kernel<ES, D>, grid, dim3(64 * kWavesPerWG), s, p, (const uint8_t*)q,
+                (const uint8_t*)k, (const uint8_t*)v, max_len, zero_ch, out);
+}
+
+hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,
+                                    int32_t max_len, int32_t max_prompt, int zero_ch, float* out, hipStream_t s) {
+  if (max_prompt < 1) return hipSuccess;
+  if (dtype == 1)
+    return d == 128 ? prefill_attention_t<2, 128>(p, q, k, v, max_len, max_prompt, zero_ch, out, s)
+                    : prefill_attention_t<2, 64>(p, q, k, v, max_len, max_prompt, zero_ch, out, s);
+  return d == 128 ? prefill_attention_t<4, 128>(p, q, k, v, max_len, max_prompt, zero_ch, out, s)
+                  : prefill_attention_t<4, 64>(p, q, k, v, max_len, max_prompt, zero_ch, out, s);
+}
+
+// Columns per wave of the chunk attention: one tile when the chunk's columns
+// (chunk x G) fit in it; every wave then streams a quarter of the keys, and
+// two work-groups stay resident per CU.  Three tiles beyond, so that more
+// columns share every loaded block.  (Measured on the 32B-shaped layer, G =
+// 5: one tile was faster for chunks of 1, three tiles for 4 and 12.)
+constexpr int kChunkSmallCols = 16;
+
+template <int ES, int D, int NC>
+static hipError_t chunk_attention_t(const Dev& p, const void* q, const void* k, const void* v, const LogitSrc& logit,
+                                    int zero_ch, int chunk, float* out, hipStream_t s) {
+  const int ytiles = (chunk * p.G + 64 * NC - 1) / (64 * NC);
+  return launch(chunk_attention_kernel<ES, D, NC>, dim3((unsigned)p.U, (unsigned)ytiles), dim3(64 * kWavesPerWG), s,
+                p, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, logit, zero_ch, chunk, out);
+}
+
+template <int ES, int D>
+static hipError_t decode_chunk_t(const Dev& p, const void* q, const void* k, const void* v, const LogitSrc& logit,
+                                 int zero_ch, int chunk, float* out, hipStream_t s) {
+  const hipError_t e = chunk * p.G <= kChunkSmallCols
+                           ? chunk_attention_t<ES, D, 1>(p, q, k, v, logit, zero_ch, chunk, out, s)
+                           : chunk_attention_t<ES, D, 3>(p, q, k, v, logit, zero_ch, chunk, out, s);
+  if (e != hipSuccess) return e;
+  const int blocks = (p.U + kWavesPerWG - 1) / kWavesPerWG;
+  return launch(append_chunk_kernel<ES, D>, dim3(blocks), dim3(64 * kWavesPerWG), s, p, (const uint8_t*)k,
+                (const uint8_t*)v, logit, zero_ch, chunk);
+}
+
+hipError_t launch_decode_chunk(const Dev& p, int dtype, int d, const void* q, const void* k, const void* v,
+                               const LogitSrc& logit, int zero_ch, int chunk, float* out, hipStream_t s) {
+  if (dtype == 1)
+    return d == 128 ? decode_chunk_t<2, 128>(p, q, k, v, logit, zero_ch, chunk, out, s)
+                    : decode_chunk_t<2, 64>(p, q, k, v, logit, zero_ch, chunk, out, s);
+  return d == 128 ? decode_chunk_t<4, 128>(p, q, k, v, logit, zero_ch, chunk, out, s)
+                  : decode_chunk_t<4, 64>(p, q, k, v, logit, zero_ch, chunk, out, s);
+}
+
+int chunk_max_blocks() { return kChunkMaxBlocks; }
+
+}  // namespace dms

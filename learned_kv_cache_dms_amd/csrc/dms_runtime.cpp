@@ -1,7 +1,7 @@
 // Host runtime behind the C ABI in include/dms.h: argument and state
 // validation, workspace layout, launch geometry, status mapping, and the
 // host side of stats / export.  All device work is the kernels in
-// dms_kernels.hip; nothing here computes any part of the decode path.
+// dms_*.hip; nothing here computes any part of the decode path.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

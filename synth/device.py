@@ -35,6 +35,8 @@ def _load():
     lib.synth_logits.restype = ctypes.c_int
     dp = ctypes.POINTER(ctypes.c_double)
     lib.synth_logits.argtypes = [vp, u64, i32, i32, i32, i32, vp, i32, i32, dp, dp, i32, vp]
+    lib.synth_read.restype = ctypes.c_int
+    lib.synth_read.argtypes = [vp, ctypes.c_int64, i32, vp, vp]
     return lib
 
 
@@ -83,3 +85,11 @@ def logits(out, seed: int, layer: int, b0: int, mu_before, mu_after=None, pos_th
     if rc != 0:
         raise RuntimeError(f"synth_logits failed ({rc})")
     return out
+
+
+def stream_read(src, grid: int, sink):
+    """One plain streaming read of the uint8 cuda tensor `src` (length a
+    multiple of 16) by `grid` work-groups; sink: uint32 cuda tensor [grid]."""
+    rc = lib.synth_read(src.data_ptr(), src.numel(), int(grid), sink.data_ptr(), _stream())
+    if rc != 0:
+        raise RuntimeError(f"synth_read failed ({rc})")

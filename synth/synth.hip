@@ -1,6 +1,8 @@
 // Device twin of synth/synth.py: the same counter-based values, bit for bit,
 // generated in HBM so large synthetic workloads need no host round trip.
 // Holds no arithmetic of the decode path.  See synth.py for the definition.
+// Also a plain streaming read (read_kernel) with which the bench measures the
+// HBM read ceiling that the decode attention is compared with.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -85,6 +87,36 @@ int grid_for(int64_t total) {
   return (int)(g < 1 ? 1 : g);
 }
 
+// Reads n16 16-byte words as a decode attention reads its blocks (16 bytes
+// per lane, nontemporal, four loads in flight per thread, the grid striding
+// over the buffer) and folds them by XOR into one word per work-group, so
+// that no load can be dropped; nothing else.
+typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned int))));
+
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                   uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  const uint32_t fold = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  __shared__ uint32_t part[256];
+  part[threadIdx.x] = fold;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t x = 0;
+    for (int t = 0; t < 256; ++t) x ^= part[t];
+    sink[blockIdx.x] = x;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -122,6 +154,15 @@ int synth_logits(float* d_out, uint64_t seed, int layer, int b0, int nb, int hea
   void* args[] = {&s, &d_out, &mu, &pos_threshold, (void*)&total};
   return hipLaunchKernel((const void*)logit_kernel, dim3(grid_for(total)), dim3(256), args, 0,
                          (hipStream_t)hip_stream) == hipSuccess ? 0 : -6;
+}
+
+// Streams n_bytes (a multiple of 16) of d_src once with `grid` work-groups;
+// d_sink receives `grid` words.
+__attribute__((visibility("default"))) int synth_read(const void* d_src, int64_t n_bytes, int grid,
+                                                      uint32_t* d_sink, hipStream_t stream) {
+  if (!d_src || !d_sink || n_bytes <= 0 || n_bytes % 16 != 0 || grid < 1) return -1;
+  hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, stream, (const u32x4*)d_src, n_bytes / 16, d_sink);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
 }  // extern "C"

@@ -91,3 +91,11 @@ def test_logistic_noise_distribution_and_addressing():
     full = synth.logistic_noise(11, 0, np.arange(4), 4, np.arange(25000))
     assert np.array_equal(part[0, 0], full[2, 3, 100:200])
     assert np.all(np.isfinite(g))
+
+
+def test_device_library_exports():
+    """The device twin's library loads and exports its entry points (no GPU
+    call is made)."""
+    from synth import device
+    for name in ("synth_fill", "synth_logits", "synth_read"):
+        assert hasattr(device.lib, name), name
