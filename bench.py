@@ -693,7 +693,8 @@ def bench_decode(args):
             c.prefill_channel(Kd, Vd, lengths, source="k", channel=ch, zero=True)
         else:
             c.prefill_channel(Kd, Vd, lengths, source="q", channel=ch, q=Qp)
-        c.balance()
+        if not args.no_balance:
+            c.balance()
         caches.append(c)
     torch.cuda.synchronize()
     # The dense prompt stays in torch's cache: returning 17 GB to the HIP runtime
@@ -797,7 +798,7 @@ def bench_decode(args):
             "decode_steps": S, "logit_mean": [_mu_json(mb), _mu_json(ma)], "logit_mean_switch": wl.pos_threshold,
             "logit_source": {"array": "array", "k": f"key channel {ch} (stored zeroed)",
                              "q": f"query channel {ch} of each group's first head"}[src],
-            "path": args.path, "caches_rotated": rot,
+            "path": args.path, "caches_rotated": rot, "balanced": not args.no_balance,
         },
         "live_kv_gbps": round(achieved, 1),
         "live_kv_gbps_per_step": round(live_bytes / step_s / 1e9, 1),
@@ -879,6 +880,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=0,
                     help="decode bench: independent caches used in turn (0: enough for 1 GB of live KV "
                          "when one step's live KV would fit in the MALL, else 1)")
+    ap.add_argument("--no-balance", action="store_true",
+                    help="decode bench: keep the cache's default work split (skip dms_cache_balance after the prompt)")
     ap.add_argument("--no-resident", action="store_true",
                     help="skip the cache-resident (one cache) figure that goes with a rotated run")
     ap.add_argument("--prefill-attention", action="store_true",
