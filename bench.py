@@ -2,24 +2,31 @@
 """Benchmark of the DMS decode hot path on one MI355X.
 
 One step = one decode step of every sequence of the workload through the C
-ABI: dms_append_step (decide, retire, store) then dms_decode_attention
-(attention over the visible tokens; a split merge when a unit is split).
-Inputs are synthetic, generated in HBM before the timed region.  The default
-workload is the Qwen-R1-32B-shaped layer: 64 chains at 32768 tokens, 40 query
-/ 8 KV heads, head_dim 128, bf16, w = 256, logit mean for CR 4 below position
-10240 and CR 12 beyond (overall about 8).
+ABI: dms_decode_step (decide, retire, store, then attention over the visible
+tokens; in whole-unit mode a single launch, in split mode the attention and
+the split merge that also appends).  `--path calls` times dms_append_step +
+dms_decode_attention instead.  Inputs are synthetic, generated in HBM before
+the timed region; after the prompt's compression dms_cache_balance plans the
+attention's work split.  The default workload is the Qwen-R1-32B-shaped
+layer: 64 chains at 32768 tokens, 40 query / 8 KV heads, head_dim 128, bf16,
+w = 256, logit mean for CR 4 below position 10240 and CR 12 beyond (overall
+about 8).
 
-Prints one JSON line.  `value` is decode-attention tokens per second (batch
-sequences per step); the live-KV bandwidth of the attention launch is in
-`roofline`, timed on every 8th attention call of the timed region with HIP
-events that the runtime stamps at the call's own kernels
-(dms_decode_attention_timed: attention_kernel; reduce_kernel too when some
-unit is split, which never happens at 512 units on 512 resident work-groups).  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same workload.
+Prints one JSON line.  `value` is decode tokens per second (batch sequences
+per step); the live-KV bandwidth of the step's kernels is in `roofline`,
+timed on every 8th step of the timed region with HIP events that the runtime
+stamps at the call's own kernels (dms_decode_step_timed).  A workload whose
+live KV per step would fit in the MALL rotates over enough independent caches
+that every step reads HBM, and reports the one-cache figure beside it.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --workload qwen-r1-32b-layer-dense --no-cpu-baseline
         # the dense baseline (nothing evicted, CR 1) through the same kernels
+    python bench.py --workload qwen-r1-32b-layer-head-skew [--no-balance]
+        # per-head compression 2 ... 16 (split mode after balancing)
+    python bench.py --workload qwen-r1-7b-layer | llama-3.2-1b-layer
+        # MALL-sized layers, caches rotated
     python bench.py --prefill-attention --steps 5 --warmup 1
         # attention of every prompt query (after the prompt's compression)
     python bench.py --chunk 16 --steps 30 --warmup 3
@@ -28,7 +35,10 @@ CPU oracle on a bounded sample of the same workload.
         # the whole 64-layer step (256 chains, prompts of 1K-32K tokens)
     python bench.py --hyper-scaling
         # KV budgets of a vanilla generation spent on longer / more DMS chains
-    python bench.py --calib-copy-bytes N    # plain copy kernel, for counter scaling
+    python bench.py --soft-attention
+        # training-time relaxed attention, forward + backward
+    python bench.py --calib-copy-bytes N    # plain copy, for scaling the HBM byte counters
+    python bench.py --calib-read-bytes N    # plain streaming read: the HBM read ceiling
 """
 from __future__ import annotations
 
