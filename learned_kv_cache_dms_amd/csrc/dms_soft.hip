@@ -169,18 +169,16 @@ __device__ __forceinline__ void load_pairT(u32x4 (&f)[D / 16], const uint8_t* __
   for (int j = 0; j < D / 16; ++j) f[j] = *(const u32x4*)(a + j * 1024);
 }
 
-// 8 fp32 values in the pair order as bf16 hi and lo parts (x = hi + lo to
-// about 2^-17 relative), the B operand of a product over the pair's rows.
-__device__ __forceinline__ void split_pair(const float (&x)[8], bf16x8& H, bf16x8& L) {
-  unsigned hi[4], lo[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hi[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-    lo[i] = pack_bf16x2(x[2 * i] - bf16_lo_to_f32(hi[i]), x[2 * i + 1] - bf16_hi_to_f32(hi[i]));
-  }
-  const u32x4 hv = {hi[0], hi[1], hi[2], hi[3]}, lv = {lo[0], lo[1], lo[2], lo[3]};
-  H = __builtin_bit_cast(bf16x8, hv);
-  L = __builtin_bit_cast(bf16x8, lv);
+// 8 fp32 values in the pair order rounded to bf16 (nearest even, 2^-8
+// relative at most), the B operand of a product over the pair's rows.  The
+// backward's gradient products take P and dS this way: their error is at
+// most 2^-8 of the sum of the terms' magnitudes (e.g. of P^T |dO| for dV).
+// Measured on the 32B-shaped training layer, keeping a lo part as well (x =
+// hi + lo to about 2^-17) made the backward 15 % slower.
+__device__ __forceinline__ bf16x8 round_pair(const float (&x)[8]) {
+  const u32x4 v = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                   pack_bf16x2(x[6], x[7])};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, f32x4 c) {
@@ -306,11 +304,11 @@ __global__ __launch_bounds__(256) void soft_forward_kernel(SoftArgs a, const uin
 }
 
 // Waves per work-group of the backward kernels.  The waves of a work-group
-// share every staged step, so more waves re-read the streamed operands less
+// share every staged step, so more waves stage the streamed operands less
 // often; measured on the 32B-shaped training layer, 8 waves made dq slower
-// and dkv no faster than 4.
+// and dkv about 4 % faster than 4.
 constexpr int kSoftQWaves = 4;
-constexpr int kSoftKWaves = 4;
+constexpr int kSoftKWaves = 8;
 constexpr int kSoftQCols = 1;              // query tiles of 16 per wave (dQ)
 constexpr int kSoftQTile = 16 * kSoftQCols * kSoftQWaves;  // queries per work-group (dQ)
 constexpr int kSoftKT = 1;                   // key tiles of 16 per wave (dK, dV)
@@ -321,10 +319,10 @@ constexpr int kSoftDqWavesPerEu = 2;  // waves per SIMD soft_dq_kernel's registe
 // recomputed from the forward's lse, dP = dO v^T.  Each wave holds
 // kSoftQCols tiles of 16 queries (columns) and streams the causal keys in
 // pairs of 16-row blocks: S^T = k q^T and dP^T = v dO^T with the keys as rows,
-// then dq^T += k^T dS^T with k^T from its pairT copy.  The 4 waves share each
-// key pair: the work-group stages k and v rows (operand order), k^T and the
-// keys' bias in LDS, double-buffered as in soft_dkv_kernel.  Grid (ceil(T /
-// kSoftQTile), Hq, B).
+// then dq^T += k^T dS^T with k^T from its pairT copy (dS rounded to bf16).
+// The 4 waves share each key pair: the work-group stages k and v rows
+// (operand order), k^T and the keys' bias in LDS, double-buffered as in
+// soft_dkv_kernel.  Grid (ceil(T / kSoftQTile), Hq, B).
 // Pieces of one staged operand this thread moves (32 rows of D bf16 = 4 D
 // pieces, NTH threads): row operands in fragment order, piece (blk * D / 32 +
 // c) * 64 + l = row 16 blk + l % 16, bytes 64 c + 16 (l / 16); pairT
@@ -473,13 +471,11 @@ __global__ __launch_bounds__(64 * kSoftQWaves) __attribute__((amdgpu_waves_per_e
           ds[r] = exp2_fast(fmaf(sv, a.scale_log2e, badd) - lse2[t]) * (dp - dl[t]);
         }
       }
-      bf16x8 DH, DL;
-      split_pair(ds, DH, DL);
+      const bf16x8 DS = round_pair(ds);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const bf16x8 KT = __builtin_bit_cast(bf16x8, S.op[2][j * 64 + lane]);
-        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KT, DH, acc[t][j], 0, 0, 0);
-        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KT, DL, acc[t][j], 0, 0, 0);
+        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KT, DS, acc[t][j], 0, 0, 0);
       }
     }
     if (s + 1 < nsteps) lds_store(st[(s + 1) & 1], pre, prb);
@@ -499,7 +495,8 @@ __global__ __launch_bounds__(64 * kSoftQWaves) __attribute__((amdgpu_waves_per_e
 // q and dlogit = -sigmoid(x) / tau * (sum of dS over the far queries).  S =
 // q k^T and dP = dO v^T with the queries as rows (k, v rows stay in
 // registers); dv^T += dO^T P and dk^T += q^T dS with dO^T, q^T from their
-// pairT copies.  The 4 waves share each step's 32 queries: the work-group
+// pairT copies (P and dS rounded to bf16).  The kSoftKWaves waves share
+// each step's 32 queries: the work-group
 // stages q and dO (rows and pairT, in operand order) and the rows' lse and
 // delta in LDS, double-buffered, the next step's loads in flight during the
 // current step's products.  No atomics: every key has one owner.  Grid
@@ -622,7 +619,7 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
     }
     const f32x4 la = *(const f32x4*)&S.lse2[tb], lb = *(const f32x4*)&S.lse2[16 + tb];
     const f32x4 da = *(const f32x4*)&S.delta[tb], db = *(const f32x4*)&S.delta[16 + tb];
-    bf16x8 PH[KT], PL[KT], DH[KT], DL[KT];
+    bf16x8 PB16[KT], DS16[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = SA, PA = SA, PB = SA;
@@ -660,8 +657,8 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
           if (qi - key[kt] > w) far_ds[kt] += ds[r];
         }
       }
-      split_pair(pr, PH[kt], PL[kt]);
-      split_pair(ds, DH[kt], DL[kt]);
+      PB16[kt] = round_pair(pr);
+      DS16[kt] = round_pair(ds);
     }
     // Raised issue priority over the gradient products, so that another
     // wave's softmax arithmetic on the same SIMD does not delay their issue
@@ -673,10 +670,8 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
       const bf16x8 QT = __builtin_bit_cast(bf16x8, S.op[2][j * 64 + lane]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        av[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PH[kt], av[kt][j], 0, 0, 0);
-        av[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PL[kt], av[kt][j], 0, 0, 0);
-        ak[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DH[kt], ak[kt][j], 0, 0, 0);
-        ak[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DL[kt], ak[kt][j], 0, 0, 0);
+        av[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(OT, PB16[kt], av[kt][j], 0, 0, 0);
+        ak[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(QT, DS16[kt], ak[kt][j], 0, 0, 0);
       }
     }
     __builtin_amdgcn_s_setprio(0);

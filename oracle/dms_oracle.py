@@ -309,13 +309,18 @@ def soft_attention(Q, K, V, logit, noise, w: int, gamma: float, tau: float,
 
 
 def soft_attention_grads(Q, K, V, logit, noise, dO, w: int, gamma: float, tau: float,
-                         scale: Optional[float] = None) -> Dict:
+                         scale: Optional[float] = None, magnitudes: bool = False) -> Dict:
     """Gradients of sum(dO * out) of ``soft_attention`` with respect to Q,
     K, V and the logits (the noise, gamma and tau are constants), written out
     from the chain rule: P = softmax(S), dP = dO V^T, dS = P (dP - rowsum(dO
     out)), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO, and for the bias
     -softplus(x) of the far keys, dlogit_i = -sigmoid(x_i) / tau * sum of dS
-    over the far (query, head) pairs of key i.  All float64."""
+    over the far (query, head) pairs of key i.  All float64.
+
+    With ``magnitudes``, also the same sums over the terms' absolute values,
+    dq_mag = scale |dS| |K|, dk_mag = scale |dS|^T |Q| and dv_mag = P^T |dO|:
+    an implementation that rounds each P or dS entry of these products by a
+    relative e is off by at most e times them (test tolerances)."""
     B, Hq, T, d = Q.shape
     Hkv = K.shape[1]
     G = Hq // Hkv
@@ -325,6 +330,8 @@ def soft_attention_grads(Q, K, V, logit, noise, dO, w: int, gamma: float, tau: f
     dK = np.zeros((B, Hkv, T, d))
     dV = np.zeros((B, Hkv, T, d))
     dlogit = np.zeros((B, Hkv, T))
+    if magnitudes:
+        mag = {"dq_mag": np.zeros_like(dQ), "dk_mag": np.zeros_like(dK), "dv_mag": np.zeros_like(dV)}
     for b in range(B):
         for h in range(Hkv):
             x = soft_decision_arg(logit[b, h], noise[b, h], gamma, tau)
@@ -344,9 +351,16 @@ def soft_attention_grads(Q, K, V, logit, noise, dO, w: int, gamma: float, tau: f
                 dK[b, h] += scale * (dS.T @ Qh)
                 dV[b, h] += P.T @ dOh
                 dlogit[b, h] += np.sum(np.where(far, dS, 0.0), axis=0)
+                if magnitudes:
+                    mag["dq_mag"][b, hq] = scale * (np.abs(dS) @ np.abs(Kh))
+                    mag["dk_mag"][b, h] += scale * (np.abs(dS).T @ np.abs(Qh))
+                    mag["dv_mag"][b, h] += P.T @ np.abs(dOh)
             sig = 1.0 / (1.0 + np.exp(-x))
             dlogit[b, h] *= -sig / tau
-    return {"dq": dQ, "dk": dK, "dv": dV, "dlogit": dlogit}
+    res = {"dq": dQ, "dk": dK, "dv": dV, "dlogit": dlogit}
+    if magnitudes:
+        res.update(mag)
+    return res
 
 
 # ----------------------------------------------------------------------------

@@ -548,6 +548,45 @@ def pin_soft_attention_grads_are_autograd(O):
         np.testing.assert_allclose(g["dlogit"], lg.grad.numpy(), rtol=0, atol=1e-11)
 
 
+def pin_soft_attention_grad_magnitudes(O):
+    """The magnitude sums (used to bound a rounded P or dS in the GPU's
+    gradient products) against torch: dS is the autograd gradient of the loss
+    at the masked scores and P their softmax; dv_mag = P^T |dO|, dk_mag =
+    scale |dS|^T |Q|, dq_mag = scale |dS| |K|, summed over each group's heads."""
+    Q, K, V, logit, noise, dO = _soft_inputs(55)
+    B, Hq, T, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    for w, gamma, tau in ((2, 0.0, 1.0), (0, 1.0, 0.5)):
+        g = O.soft_attention_grads(Q, K, V, logit, noise, dO, w, gamma, tau, magnitudes=True)
+        pos = torch.arange(T)
+        far = (pos[:, None] - pos[None, :]) > w
+        causal = pos[None, :] <= pos[:, None]
+        x = (torch.tensor(logit, dtype=torch.float64) + gamma + torch.tensor(noise, dtype=torch.float64)) / tau
+        bias = torch.log(1.0 - torch.sigmoid(x))
+        q, k, v, do = (torch.tensor(a, dtype=torch.float64) for a in (Q, K, V, dO))
+        for b in range(B):
+            dk_ref = torch.zeros((Hkv, T, d), dtype=torch.float64)
+            dv_ref = torch.zeros((Hkv, T, d), dtype=torch.float64)
+            for hq in range(Hq):
+                h = hq // G
+                mask = torch.where(causal, torch.where(far, bias[b, h][None, :], torch.zeros(())),
+                                   torch.tensor(-float("inf")))
+                s = (scale * (q[b, hq] @ k[b, h].T) + mask).detach().requires_grad_()
+                P = torch.softmax(s, dim=1)
+                ((P @ v[b, h]) * do[b, hq]).sum().backward()
+                dS = s.grad
+                np.testing.assert_allclose(g["dq_mag"][b, hq], (scale * dS.abs() @ k[b, h].abs()).numpy(),
+                                           rtol=0, atol=1e-12)
+                dk_ref[h] += scale * dS.abs().T @ q[b, hq].abs()
+                dv_ref[h] += P.detach().T @ do[b, hq].abs()
+            np.testing.assert_allclose(g["dk_mag"][b], dk_ref.numpy(), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(g["dv_mag"][b], dv_ref.numpy(), rtol=0, atol=1e-12)
+        for key in ("dq", "dk", "dv"):
+            assert np.all(np.abs(g[key]) <= g[key + "_mag"] + 1e-12), key
+
+
 ALL_PINS = [
     pin_golden_visibility,
     pin_fifo_simulation,
@@ -575,4 +614,5 @@ ALL_PINS = [
     pin_soft_attention_hard_limit,
     pin_soft_attention_lse,
     pin_soft_attention_grads_are_autograd,
+    pin_soft_attention_grad_magnitudes,
 ]

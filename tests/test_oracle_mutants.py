@@ -145,8 +145,8 @@ def _soft_arg_without_noise(logit, noise, gamma, tau):
     return (np.asarray(logit, np.float64) + gamma) / tau
 
 
-def _soft_grads_dlogit_sign(Q, K, V, logit, noise, dO, w, gamma, tau, scale=None):
-    g = real.__dict__["_orig_soft_attention_grads"](Q, K, V, logit, noise, dO, w, gamma, tau, scale)
+def _soft_grads_dlogit_sign(Q, K, V, logit, noise, dO, w, gamma, tau, scale=None, magnitudes=False):
+    g = real.__dict__["_orig_soft_attention_grads"](Q, K, V, logit, noise, dO, w, gamma, tau, scale, magnitudes)
     g["dlogit"] = -g["dlogit"]
     return g
 
