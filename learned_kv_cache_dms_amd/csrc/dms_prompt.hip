@@ -61,32 +61,45 @@ __device__ __forceinline__ void load_frag_dense(Frag<ES, D>& f, const uint8_t* _
   }
 }
 
-// Grid (ceil(max_len_used / kPfTile), Hq, B).
+// Column tiles per wave of the prompt attention for rows of ES-byte elements:
+// fp32 rows at d = 128 take twice the registers of bf16 ones, and three tiles
+// of them spill (93 registers); two do not.
+template <int ES, int D>
+constexpr int pf_cols() {
+  return ES == 4 && D == 128 ? 2 : kPfCols;
+}
+template <int ES, int D>
+constexpr int pf_tile() {
+  return 16 * pf_cols<ES, D>() * kWavesPerWG;
+}
+
+// Grid (ceil(max_len_used / pf_tile<ES, D>()), Hq, B).
 template <int ES, int D>
 __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uint8_t* __restrict__ q,
                                                                 const uint8_t* __restrict__ k,
                                                                 const uint8_t* __restrict__ v, int32_t max_len,
                                                                 int zero_ch, float* __restrict__ out) {
   using G = Geo<ES, D>;
+  constexpr int NCOL = pf_cols<ES, D>(), TILE = pf_tile<ES, D>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.z, hq = blockIdx.y;
   const int h = hq / p.G, u = b * p.Hkv + h;
   const int P = __builtin_amdgcn_readfirstlane(p.pos[u]);
-  const int q0 = blockIdx.x * kPfTile;
+  const int q0 = blockIdx.x * TILE;
   if (q0 >= P) return;
   const int w = p.R - 1;
-  const int qmax = min(q0 + kPfTile, P) - 1;
+  const int qmax = min(q0 + TILE, P) - 1;
   const int64_t unit_rows = ((int64_t)b * p.Hkv + h) * max_len;
   const uint8_t* Ku = k + unit_rows * D * ES;
   const uint8_t* Vu = v + unit_rows * D * ES;
   const uint8_t* Qh = q + ((int64_t)b * p.Hq + hq) * max_len * D * ES;
 
-  int qc[kPfCols];
-  u32x4 qf[kPfCols][G::kChunks];
-  Acc<D> acc[kPfCols];
+  int qc[NCOL];
+  u32x4 qf[NCOL][G::kChunks];
+  Acc<D> acc[NCOL];
 #pragma unroll
-  for (int t = 0; t < kPfCols; ++t) {
-    qc[t] = q0 + 16 * (kPfCols * wave + t) + (lane & 15);
+  for (int t = 0; t < NCOL; ++t) {
+    qc[t] = q0 + 16 * (NCOL * wave + t) + (lane & 15);
     const uint8_t* qrow = Qh + (int64_t)min(qc[t], P - 1) * D * ES;
 #pragma unroll
     for (int c = 0; c < G::kChunks; ++c) qf[t][c] = *(const u32x4*)(qrow + c * 64 + 16 * (lane >> 4));
@@ -142,13 +155,13 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
         f32x4 SA[2], SB[2];
         score_pair<D>(f, qf[0], SA[0], SB[0]);
 #pragma unroll
-        for (int t = 0; t < kPfCols; ++t) {
-          if (t + 1 < kPfCols) score_pair<D>(f, qf[t + 1], SA[(t + 1) & 1], SB[(t + 1) & 1]);
+        for (int t = 0; t < NCOL; ++t) {
+          if (t + 1 < NCOL) score_pair<D>(f, qf[t + 1], SA[(t + 1) & 1], SB[(t + 1) & 1]);
           softmax_pv_masked<D>(f, SA[t & 1], SB[t & 1], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < kPfCols; ++t) attend_pair<ES, D>(f, qf[t], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
+        for (int t = 0; t < NCOL; ++t) attend_pair<ES, D>(f, qf[t], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
       }
     };
     PairFrag<ES, D> f0, f1;
@@ -173,7 +186,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
     const int4 pb = *(const int4*)(p.blk_pos + (int64_t)bb * 16 + tb);
     const int lva = n - 16 * j, lvb = j + 1 < nfar ? n - 16 * (j + 1) : 0;  // live slots
 #pragma unroll
-    for (int t = 0; t < kPfCols; ++t) {
+    for (int t = 0; t < NCOL; ++t) {
       const int lt = qc[t] - w;
       uint32_t ma = 0, mb = 0;
       const int xa[4] = {pa.x, pa.y, pa.z, pa.w}, xb[4] = {pb.x, pb.y, pb.z, pb.w};
@@ -204,12 +217,12 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
     PairFrag<ES, D> f;
     make_pair<ES, D>(f, fa, fb);
 #pragma unroll
-    for (int t = 0; t < kPfCols; ++t)
+    for (int t = 0; t < NCOL; ++t)
       attend_pair<ES, D>(f, qf[t], near_mask(r0, t), near_mask(r0 + 16, t), lane, p.scale_log2e, acc[t]);
   }
 
 #pragma unroll
-  for (int t = 0; t < kPfCols; ++t) {
+  for (int t = 0; t < NCOL; ++t) {
     // each lane's l sums its own 4 keys of every block: add the 4 lane groups
     // of the column (all share the column's running max)
     float lt = acc[t].l + __shfl_xor(acc[t].l, 16);
@@ -455,7 +468,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
 template <int ES, int D>
 static hipError_t prefill_attention_t(const Dev& p, const void* q, const void* k, const void* v, int32_t max_len,
                                       int32_t max_prompt, int zero_ch, float* out, hipStream_t s) {
-  const dim3 grid((unsigned)((max_prompt + kPfTile - 1) / kPfTile), (unsigned)p.Hq, (unsigned)p.B);
+  constexpr int TILE = pf_tile<ES, D>();
+  const dim3 grid((unsigned)((max_prompt + TILE - 1) / TILE), (unsigned)p.Hq, (unsigned)p.B);
   return launch(prefill_attention_kernel<ES, D>, grid, dim3(64 * kWavesPerWG), s, p, (const uint8_t*)q,
                 (const uint8_t*)k, (const uint8_t*)v, max_len, zero_ch, out);
 }
@@ -474,8 +488,13 @@ hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* 
 // (chunk x G) fit in it; every wave then streams a quarter of the keys, and
 // two work-groups stay resident per CU.  Three tiles beyond, so that more
 // columns share every loaded block.  (Measured on the 32B-shaped layer, G =
-// 5: one tile was faster for chunks of 1, three tiles for 4 and 12.)
+// 5: one tile was faster for chunks of 1, three tiles for 4 and 12.)  fp32
+// rows at d = 128 take two tiles: three spill.
 constexpr int kChunkSmallCols = 16;
+template <int ES, int D>
+constexpr int chunk_cols() {
+  return ES == 4 && D == 128 ? 2 : 3;
+}
 
 template <int ES, int D, int NC>
 static hipError_t chunk_attention_t(const Dev& p, const void* q, const void* k, const void* v, const LogitSrc& logit,
@@ -490,7 +509,7 @@ static hipError_t decode_chunk_t(const Dev& p, const void* q, const void* k, con
                                  int zero_ch, int chunk, float* out, hipStream_t s) {
   const hipError_t e = chunk * p.G <= kChunkSmallCols
                            ? chunk_attention_t<ES, D, 1>(p, q, k, v, logit, zero_ch, chunk, out, s)
-                           : chunk_attention_t<ES, D, 3>(p, q, k, v, logit, zero_ch, chunk, out, s);
+                           : chunk_attention_t<ES, D, chunk_cols<ES, D>()>(p, q, k, v, logit, zero_ch, chunk, out, s);
   if (e != hipSuccess) return e;
   const int blocks = (p.U + kWavesPerWG - 1) / kWavesPerWG;
   return launch(append_chunk_kernel<ES, D>, dim3(blocks), dim3(64 * kWavesPerWG), s, p, (const uint8_t*)k,
