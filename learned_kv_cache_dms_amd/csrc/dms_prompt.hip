@@ -61,6 +61,70 @@ __device__ __forceinline__ void load_frag_dense(Frag<ES, D>& f, const uint8_t* _
   }
 }
 
+// Softmax step and P.V of a pair of blocks for the prompt attention (the
+// masks as softmax_pv_masked).  Two differences from the decode's step, both
+// for this compute-bound kernel:
+//  - the weights enter P.V as bf16 (nearest even), one product per tile: an
+//    output element is off by at most 2^-8 of sum_i p_i |v_i| / sum_i p_i
+//    (the sum l stays fp32).  A lo part as well (about 2^-17) cost 22 % of
+//    the kernel's time on the 32B-shaped layer;
+//  - a column's reference max moves only when a score exceeds it by more
+//    than 2^kPromptSlack in the exp2 domain, so the accumulators are rescaled
+//    a few times per column rather than whenever its max creeps up; the
+//    weights exp2(s - m) stay below 2^kPromptSlack and o / l is unchanged.
+constexpr float kPromptSlack = 8.0f;
+template <int D>
+__device__ __forceinline__ void softmax_pv_prompt(const PairFrag<2, D>& f, const f32x4& SA, const f32x4& SB,
+                                                  uint32_t ma, uint32_t mb, int lane, float sl2e, Acc<D>& a) {
+  using G = Geo<2, D>;
+  const int tb = 4 * (lane >> 4);
+  float s[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s[r] = ((ma >> (tb + r)) & 1u) ? SA[r] : -INFINITY;
+    s[4 + r] = ((mb >> (tb + r)) & 1u) ? SB[r] : -INFINITY;
+  }
+  const float bm = max_over_groups(
+      fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))));
+  const float bm2 = bm * sl2e;  // the scale is > 0
+  // a column with no key yet has m = -inf and o = l = 0: its first finite
+  // score moves the reference, and alpha = 0 leaves o and l at 0; the other
+  // columns keep theirs (alpha = 1, also when m is still -inf)
+  const bool grow = bm2 > a.m + kPromptSlack;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const float mn = grow ? bm2 : a.m;
+    const float alpha = grow ? exp2_fast(a.m - mn) : 1.0f;
+    a.l *= alpha;
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) a.o[j] *= alpha;
+    a.m = mn;
+  }
+  const float mref = (a.m == -INFINITY) ? 0.f : a.m;
+  float pr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) pr[r] = exp2_fast(fmaf(s[r], sl2e, -mref));
+  a.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+  const u32x4 pv = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]), pack_bf16x2(pr[4], pr[5]),
+                    pack_bf16x2(pr[6], pr[7])};
+  const bf16x8 PB = __builtin_bit_cast(bf16x8, pv);
+#pragma unroll
+  for (int j = 0; j < G::kTiles; ++j)
+    a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.v[j]), PB, a.o[j], 0, 0, 0);
+}
+
+// attend_pair with the prompt attention's softmax step for bf16 rows.
+template <int ES, int D>
+__device__ __forceinline__ void attend_pair_prompt(const PairFrag<ES, D>& f, const u32x4 (&qf)[Geo<ES, D>::kChunks],
+                                                   uint32_t ma, uint32_t mb, int lane, float sl2e, Acc<D>& a) {
+  if constexpr (ES != 2) {
+    attend_pair<ES, D>(f, qf, ma, mb, lane, sl2e, a);
+  } else {
+    f32x4 SA, SB;
+    score_pair<D>(f, qf, SA, SB);
+    softmax_pv_prompt<D>(f, SA, SB, ma, mb, lane, sl2e, a);
+  }
+}
+
 // Column tiles per wave of the prompt attention for rows of ES-byte elements:
 // fp32 rows at d = 128 take twice the registers of bf16 ones, and three tiles
 // of them spill (93 registers); two do not.
@@ -157,11 +221,11 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
 #pragma unroll
         for (int t = 0; t < NCOL; ++t) {
           if (t + 1 < NCOL) score_pair<D>(f, qf[t + 1], SA[(t + 1) & 1], SB[(t + 1) & 1]);
-          softmax_pv_masked<D>(f, SA[t & 1], SB[t & 1], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
+          softmax_pv_prompt<D>(f, SA[t & 1], SB[t & 1], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < NCOL; ++t) attend_pair<ES, D>(f, qf[t], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
+        for (int t = 0; t < NCOL; ++t) attend_pair_prompt<ES, D>(f, qf[t], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
       }
     };
     PairFrag<ES, D> f0, f1;
@@ -195,7 +259,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
         if (tb + r < lva && xa[r] < lt) ma |= 1u << (tb + r);
         if (tb + r < lvb && xb[r] < lt) mb |= 1u << (tb + r);
       }
-      attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
+      attend_pair_prompt<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
     }
   }
 
@@ -218,7 +282,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
     make_pair<ES, D>(f, fa, fb);
 #pragma unroll
     for (int t = 0; t < NCOL; ++t)
-      attend_pair<ES, D>(f, qf[t], near_mask(r0, t), near_mask(r0 + 16, t), lane, p.scale_log2e, acc[t]);
+      attend_pair_prompt<ES, D>(f, qf[t], near_mask(r0, t), near_mask(r0 + 16, t), lane, p.scale_log2e, acc[t]);
   }
 
 #pragma unroll
@@ -276,7 +340,8 @@ __global__ __launch_bounds__(256) void append_chunk_kernel(Dev p, const uint8_t*
 // group's heads share every loaded block as in the decode kernel.
 constexpr int kChunkMaxBlocks = 8192;
 
-// NC tiles of 16 columns per wave.  Grid (U, ceil(chunk G / (64 NC))).
+// NC tiles of 16 columns per wave.  One work-group per (unit, group of 64 NC
+// columns), ceil(chunk G / (64 NC)) groups per unit; grid 8 ceil(items / 8).
 // q [B, Hq, chunk, d]; k, v [B, Hkv,
 // chunk, d]; logit [B, Hkv, chunk]; out [B, Hq, chunk, d].
 //
@@ -295,7 +360,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
   __shared__ f32x4 mo[kWavesPerWG - 1][G::kTiles][64];
   __shared__ float mm[kWavesPerWG - 1][64], ml[kWavesPerWG - 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int u = blockIdx.x;
+  // Work item (unit, column group) of this work-group.  Work-group i runs on
+  // XCD i mod 8; the items are dealt so that each XCD takes a run of
+  // consecutive items: the column groups of a unit one after another (its
+  // blocks are then re-read from that XCD's L2) and neighbouring units, whose
+  // blocks the prefill allocated next to each other.  (Measured on the
+  // 32B-shaped layer against one work-group per item in unit order: 1-5 %
+  // faster for chunks of 4 to 64.)
+  const int ytiles = (chunk * p.G + 64 * NC - 1) / (64 * NC);
+  const int items = p.U * ytiles, per_xcd = (items + 7) / 8;
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (item >= items) return;  // before any barrier
+  const int u = item / ytiles, ytile = item - u * ytiles;
   const int b = u / p.Hkv, h = u - b * p.Hkv;
   const int n = __builtin_amdgcn_readfirstlane(p.n[u]);
   const int nb = (n + 15) >> 4;
@@ -311,7 +387,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
   __syncthreads();
 
   const int ncol = chunk * p.G;
-  const int cwg = blockIdx.y * (16 * NC * kWavesPerWG);
+  const int cwg = ytile * (16 * NC * kWavesPerWG);
   const int wg_cols = min((16 * NC * kWavesPerWG), ncol - cwg);
   const int need = (wg_cols + 16 * NC - 1) / (16 * NC);  // waves with columns
   const int nsplit = need == 1 ? 4 : (need == 2 ? 2 : 1);
@@ -500,7 +576,8 @@ template <int ES, int D, int NC>
 static hipError_t chunk_attention_t(const Dev& p, const void* q, const void* k, const void* v, const LogitSrc& logit,
                                     int zero_ch, int chunk, float* out, hipStream_t s) {
   const int ytiles = (chunk * p.G + 64 * NC - 1) / (64 * NC);
-  return launch(chunk_attention_kernel<ES, D, NC>, dim3((unsigned)p.U, (unsigned)ytiles), dim3(64 * kWavesPerWG), s,
+  const int items = p.U * ytiles;
+  return launch(chunk_attention_kernel<ES, D, NC>, dim3((unsigned)(8 * ((items + 7) / 8))), dim3(64 * kWavesPerWG), s,
                 p, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, logit, zero_ch, chunk, out);
 }
 

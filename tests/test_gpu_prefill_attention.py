@@ -1,6 +1,14 @@
 """GPU parity of dms_prefill_attention (every prompt query attends its own
 visible set) against the oracle's ``prefill_attention``: every output row at
-small and medium sizes, sampled rows at the full Qwen-R1-32B-shaped layer."""
+small and medium sizes, sampled rows at the full Qwen-R1-32B-shaped layer.
+
+Tolerances: fp32 rows 1e-5 absolute.  For bf16 rows the kernel feeds the
+softmax weights p_i to P.V rounded to bf16 (nearest even, 2^-8 relative) and
+keeps their sum in fp32, so an output element is off by at most 2^-8 sum_i
+softmax_i |v_i| from the rounding, plus n 2^-24 of the same sum for the fp32
+accumulation of n keys, plus 1e-4 for the rest of the fp32 arithmetic (the
+decode path's bound).  sum_i softmax_i |v_i| is the oracle's attention with
+|V| as the values."""
 import numpy as np
 import pytest
 import torch
@@ -10,6 +18,19 @@ from synth import synth
 gpu = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 1e-4}
+ROUND = 2.0 ** -8   # bf16 rounding of one weight, relative
+U32 = 2.0 ** -24    # fp32 unit roundoff
+
+
+def excess(got, want, mag, n_keys, dtype):
+    """max |got - want| / allowed over the elements (at most 1 passes):
+    allowed = TOL for fp32 rows; (ROUND + n_keys U32) mag + TOL for bf16
+    rows, mag = sum_i softmax_i |v_i| of each element."""
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    if dtype == "f32":
+        return float(np.max(np.abs(got - want))) / TOL["f32"]
+    return float(np.max(np.abs(got - want) / ((ROUND + n_keys * U32) * mag + TOL["bf16"])))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -40,18 +61,21 @@ def _run(B, Hq, Hkv, d, dtype, w, P, mu, seed):
     T = int(P.max())
     Q, K, V, lg = _host_prompt(seed, B, Hq, Hkv, T, d, dtype, mu)
     ref = O.prefill_attention(Q, K, V, lg, P, w)
+    mag = O.prefill_attention(Q, K, np.abs(V), lg, P, w) if dtype == "bf16" else None
     cache = dms.Cache(B, Hq, Hkv, d, w, T + 1, B * Hkv * (T // 16 + 2), dtype=dtype)
     Qd, Kd, Vd = _dev(Q, dtype), _dev(K, dtype), _dev(V, dtype)
     cache.prefill(Kd, Vd, torch.from_numpy(lg).cuda(), P)
     out = torch.full((B, Hq, T, d), 7.0, dtype=torch.float32, device="cuda")
     cache.prefill_attention(Qd, Kd, Vd, out)
     got = out.double().cpu().numpy()
-    err = 0.0
+    err = ratio = 0.0
     for b in range(B):
-        e = float(np.max(np.abs(got[b, :, :P[b]] - ref[b, :, :P[b]]))) if P[b] > 0 else 0.0
-        err = max(err, e)
+        if P[b] > 0:
+            sl = (b, slice(None), slice(0, P[b]))
+            err = max(err, float(np.max(np.abs(got[sl] - ref[sl]))), 0.0 if np.all(np.isfinite(got[sl])) else np.inf)
+            ratio = max(ratio, excess(got[sl], ref[sl], mag[sl] if mag is not None else None, P[b], dtype))
         assert np.all(got[b, :, P[b]:] == 7.0), "rows past the prompt were written"
-    return err
+    return err, ratio
 
 
 CASES = [
@@ -72,9 +96,9 @@ CASES = [
 def test_prefill_attention_every_row(case):
     name, B, Hq, Hkv, d, dtype, w, P, mu = case
     print(f"[{name}] B={B} Hq={Hq} Hkv={Hkv} d={d} w={w} P={P} mu={mu}", flush=True)
-    err = _run(B, Hq, Hkv, d, dtype, w, P, mu, seed=5000 + d + w)
-    print(f"[{name}] max_err={err:.3e}", flush=True)
-    assert err <= TOL[dtype], (name, err)
+    err, ratio = _run(B, Hq, Hkv, d, dtype, w, P, mu, seed=5000 + d + w)
+    print(f"[{name}] max_err={err:.3e} (fraction of the bound {ratio:.2f})", flush=True)
+    assert ratio <= 1.0, (name, err, ratio)
 
 
 @gpu
@@ -94,6 +118,7 @@ def test_prefill_attention_after_channel_prefill(source, zero):
     lg = O.logits_from_channel(K if source == "k" else Q, ch, 1 if source == "k" else G)
     Kc = O.without_channel(K, ch) if zero else K
     ref = O.prefill_attention(Q, Kc, V, lg, P, w)
+    mag = O.prefill_attention(Q, Kc, np.abs(V), lg, P, w)
     cache = dms.Cache(B, Hq, Hkv, d, w, T + 1, B * Hkv * (T // 16 + 2), dtype=dtype)
     Qd, Kd, Vd = _dev(Q, dtype), _dev(K, dtype), _dev(V, dtype)
     cache.prefill_channel(Kd, Vd, P, source=source, channel=ch, zero=zero, q=Qd if source == "q" else None)
@@ -101,8 +126,9 @@ def test_prefill_attention_after_channel_prefill(source, zero):
     cache.prefill_attention(Qd, Kd, Vd, out)
     got = out.double().cpu().numpy()
     for b in range(B):
-        err = float(np.max(np.abs(got[b, :, :P[b]] - ref[b, :, :P[b]])))
-        assert err <= TOL[dtype], (source, b, err)
+        sl = (b, slice(None), slice(0, P[b]))
+        ratio = excess(got[sl], ref[sl], mag[sl], P[b], dtype)
+        assert ratio <= 1.0, (source, b, ratio)
 
 
 @gpu
@@ -142,10 +168,12 @@ def test_prefill_attention_full_size_sampled_rows():
         qv = synth.tensor(wl.seed, synth.STREAM_Q, 0, [b], [hq], [qpos], d, wl.dtype)[0, 0]
         vis = O.visible(O.eviction_decision(lg), qpos, wl.window)
         ref = O.attend(qv, Kh[vis], Vh[vis], scale)[0]
+        mag = O.attend(qv, Kh[vis], np.abs(Vh[vis]), scale)[0]
         got = out[b, hq, qpos].double().cpu().numpy()
         err = float(np.max(np.abs(got - ref)))
-        print(f"  (b={b}, hq={hq}, q={qpos}) |Vis|={len(vis)} err={err:.2e}", flush=True)
-        assert err <= TOL["bf16"], (b, hq, qpos, err)
+        ratio = excess(got, ref, mag, len(vis), "bf16")
+        print(f"  (b={b}, hq={hq}, q={qpos}) |Vis|={len(vis)} err={err:.2e} ({ratio:.2f} of the bound)", flush=True)
+        assert ratio <= 1.0, (b, hq, qpos, err, ratio)
 
 
 @gpu

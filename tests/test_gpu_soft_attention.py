@@ -168,7 +168,13 @@ def test_soft_attention_hard_limit_equals_prompt_attention():
     torch.cuda.synchronize()
     err = float((out - hard).abs().max())
     print(f"[hard limit] max |soft - prompt attention| = {err:.2e}", flush=True)
-    assert err <= TOL
+    # each is within its own bound of the hard attention: the prompt
+    # attention's for bf16-rounded weights, and this forward's TOL
+    from oracle import dms_oracle as O
+    import test_gpu_prefill_attention as PA
+    mag = O.prefill_attention(Q, K, np.abs(V), lg, [T] * B, w)
+    allowed = (PA.ROUND + T * PA.U32) * mag + PA.TOL["bf16"] + TOL
+    assert np.all(np.abs(hard.double().cpu().numpy() - out.double().cpu().numpy()) <= allowed)
     assert float(grads["dlogit"].abs().max()) == 0.0
 
 
