@@ -333,11 +333,16 @@ __global__ __launch_bounds__(256) void append_chunk_kernel(Dev p, const uint8_t*
 //  - chunk row i <= j when it is unmarked or i >= j - w.
 // Marked tokens that left the cache before the chunk are invisible to every
 // chunk query too, so this is exactly the visible set of each step.  The
-// pending slots come from the ring into a per-block bitmap in LDS.
+// pending slots come from the ring into a per-block bitmap in LDS: bit s of
+// word i is slot 16 i + s, and bit 16 flags a block holding a pending token
+// at a position below q0 + chunk - 1 - w, which some chunk query cannot see.
+// A pair of full blocks without that flag is visible to every column whole,
+// so its per-column masks are skipped (at most chunk such tokens exist,
+// against thousands of blocks).
 //
-// Work-group = 4 waves = one (sequence, KV head) unit and kPfTile columns;
-// column c = j G + g carries query head h G + g of chunk position j, so the
-// group's heads share every loaded block as in the decode kernel.
+// Work-group = 4 waves = one (sequence, KV head) unit and up to 64 NC
+// columns; column c = j G + g carries query head h G + g of chunk position j,
+// so the group's heads share every loaded block as in the decode kernel.
 constexpr int kChunkMaxBlocks = 8192;
 
 // NC tiles of 16 columns per wave.  One work-group per (unit, group of 64 NC
@@ -380,9 +385,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
   for (int i = threadIdx.x; i < nb; i += blockDim.x) pend[i] = 0u;
   __syncthreads();
   const int32_t* ring = p.ring + (int64_t)u * p.R;
+  const int hide_lim = q0 + chunk - 1 - w;
   for (int r = threadIdx.x; r < p.R; r += blockDim.x) {
     const int sl = ring[r];
-    if (sl >= 0 && sl < n) atomicOr(&pend[sl >> 4], 1u << (sl & 15));
+    if (sl >= 0 && sl < n) {
+      const int blk = p.btab[(int64_t)u * p.max_blocks + (sl >> 4)];
+      const int pos = p.blk_pos[(int64_t)blk * 16 + (sl & 15)];
+      atomicOr(&pend[sl >> 4], (1u << (sl & 15)) | (pos < hide_lim ? 0x10000u : 0u));
+    }
   }
   __syncthreads();
 
@@ -424,9 +434,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
       uint32_t wa, wb;
     };
     auto fetch = [&](PairFrag<ES, D>& f, Meta& m, int kk) {
-      const int i = min(sp + nsplit * kk, npair - 1);
+      // The block ids through the scalar cache (an index the compiler can
+      // see is uniform): a vector load here, its value needed at once for
+      // the addresses, made the wave wait for every load in flight, the
+      // prefetched pair's included (measured: C = 16 0.469 -> 0.408 ms).
+      const int i = __builtin_amdgcn_readfirstlane(min(sp + nsplit * kk, npair - 1));
       const int ja = 2 * i, jb = min(2 * i + 1, nb - 1);
-      const int ba = __builtin_amdgcn_readfirstlane(bt[ja]), bb = __builtin_amdgcn_readfirstlane(bt[jb]);
+      const int ba = scalar_load(bt + ja), bb = scalar_load(bt + jb);
       load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
       m.pa = *(const int4*)(p.blk_pos + (int64_t)ba * 16 + tb);
       m.pb = *(const int4*)(p.blk_pos + (int64_t)bb * 16 + tb);
@@ -439,17 +453,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
       const int ja = 2 * i;
       const int lva = ok ? n - 16 * ja : 0, lvb = ok && ja + 1 < nb ? n - 16 * (ja + 1) : 0;
       const int xa[4] = {m.pa.x, m.pa.y, m.pa.z, m.pa.w}, xb[4] = {m.pb.x, m.pb.y, m.pb.z, m.pb.w};
+      // full blocks, no token hidden from any column: masks all ones
+      const bool plain =
+          __builtin_amdgcn_readfirstlane((lva >= 16 && lvb >= 16 && !((m.wa | m.wb) & 0x10000u)) ? 1 : 0) != 0;
+      // (bf16) column t + 1's score products are issued before column t's
+      // softmax, so that they run during its VALU work
+      f32x4 SA[2], SB[2];
+      if constexpr (ES == 2) score_pair<D>(f, qf[0], SA[0], SB[0]);
 #pragma unroll
       for (int t = 0; t < NC; ++t) {
         const int lt = q0 + qj[t] - w;  // a pending token is visible from position >= lt
-        uint32_t ma = 0, mb = 0;
+        uint32_t ma = 0xffffu, mb = 0xffffu;
+        if (!plain) {
+          ma = mb = 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int bit = tb + r;
-          if (bit < lva && (!((m.wa >> bit) & 1u) || xa[r] >= lt)) ma |= 1u << bit;
-          if (bit < lvb && (!((m.wb >> bit) & 1u) || xb[r] >= lt)) mb |= 1u << bit;
+          for (int r = 0; r < 4; ++r) {
+            const int bit = tb + r;
+            if (bit < lva && (!((m.wa >> bit) & 1u) || xa[r] >= lt)) ma |= 1u << bit;
+            if (bit < lvb && (!((m.wb >> bit) & 1u) || xb[r] >= lt)) mb |= 1u << bit;
+          }
         }
-        attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
+        if constexpr (ES == 2) {
+          if (t + 1 < NC) score_pair<D>(f, qf[t + 1], SA[(t + 1) & 1], SB[(t + 1) & 1]);
+          softmax_pv_masked<D>(f, SA[t & 1], SB[t & 1], ma, mb, lane, p.scale_log2e, acc[t]);
+        } else {
+          attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
+        }
       }
     };
     PairFrag<ES, D> f0, f1;
@@ -560,13 +589,15 @@ hipError_t launch_prefill_attention(const Dev& p, int dtype, int d, const void* 
                   : prefill_attention_t<4, 64>(p, q, k, v, max_len, max_prompt, zero_ch, out, s);
 }
 
-// Columns per wave of the chunk attention: one tile when the chunk's columns
-// (chunk x G) fit in it; every wave then streams a quarter of the keys, and
-// two work-groups stay resident per CU.  Three tiles beyond, so that more
-// columns share every loaded block.  (Measured on the 32B-shaped layer, G =
-// 5: one tile was faster for chunks of 1, three tiles for 4 and 12.)  fp32
-// rows at d = 128 take two tiles: three spill.
-constexpr int kChunkSmallCols = 16;
+// Column tiles per wave of the chunk attention, by the chunk's tiles of 16
+// columns (chunk x G): one tile when they fit in it (every wave then streams
+// a quarter of the keys, and two work-groups stay resident per CU); as many
+// tiles as the columns need, up to 4, so that no wave computes a padding
+// tile and one wave holds every column of the pairs it loads; 3 beyond (5
+// tiles at d = 128 spill).  Measured on the 32B-shaped layer (G = 5), against
+// 3 tiles whenever more than one was needed: 2 tiles at C = 4 0.249 -> 0.237
+// ms, 4 tiles at C = 12 0.383 -> 0.281 ms.  fp32 rows: two tiles at d = 128
+// (three spill), three at d = 64.
 template <int ES, int D>
 constexpr int chunk_cols() {
   return ES == 4 && D == 128 ? 2 : 3;
@@ -584,9 +615,14 @@ static hipError_t chunk_attention_t(const Dev& p, const void* q, const void* k, 
 template <int ES, int D>
 static hipError_t decode_chunk_t(const Dev& p, const void* q, const void* k, const void* v, const LogitSrc& logit,
                                  int zero_ch, int chunk, float* out, hipStream_t s) {
-  const hipError_t e = chunk * p.G <= kChunkSmallCols
-                           ? chunk_attention_t<ES, D, 1>(p, q, k, v, logit, zero_ch, chunk, out, s)
-                           : chunk_attention_t<ES, D, chunk_cols<ES, D>()>(p, q, k, v, logit, zero_ch, chunk, out, s);
+  const int tiles = (chunk * p.G + 15) / 16;
+  hipError_t e;
+  if (tiles <= 1) e = chunk_attention_t<ES, D, 1>(p, q, k, v, logit, zero_ch, chunk, out, s);
+  else if constexpr (ES == 4) e = chunk_attention_t<ES, D, chunk_cols<ES, D>()>(p, q, k, v, logit, zero_ch, chunk, out, s);
+  else if (tiles == 2) e = chunk_attention_t<ES, D, 2>(p, q, k, v, logit, zero_ch, chunk, out, s);
+  else if (tiles == 3) e = chunk_attention_t<ES, D, 3>(p, q, k, v, logit, zero_ch, chunk, out, s);
+  else if (tiles == 4) e = chunk_attention_t<ES, D, 4>(p, q, k, v, logit, zero_ch, chunk, out, s);
+  else e = chunk_attention_t<ES, D, 3>(p, q, k, v, logit, zero_ch, chunk, out, s);
   if (e != hipSuccess) return e;
   const int blocks = (p.U + kWavesPerWG - 1) / kWavesPerWG;
   return launch(append_chunk_kernel<ES, D>, dim3(blocks), dim3(64 * kWavesPerWG), s, p, (const uint8_t*)k,

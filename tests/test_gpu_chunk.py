@@ -47,6 +47,10 @@ CASES = [
     ("bf16-d128-g16-two-column-tiles", 1, 16, 1, 128, "bf16", 12, [70], 0.8, [16, 13, 1]),
     ("f32-d128-g5-w-ge-context", 1, 10, 2, 128, "f32", 400, [60], 0.5, [20, 31]),
     ("bf16-d128-g5-empty-prompt", 2, 10, 2, 128, "bf16", 6, [0, 0], 0.6, [3, 25]),
+    # 2, 3 and 4 column tiles per wave (G = 4 at d = 64, G = 5 at d = 128),
+    # prompts long enough for many pairs of full blocks, a short window
+    ("bf16-d64-g4-two-three-tiles", 2, 8, 2, 64, "bf16", 10, [120, 77], 0.7, [6, 12, 8, 1]),
+    ("bf16-d128-g5-three-four-tiles", 2, 10, 2, 128, "bf16", 20, [300, 150], 0.9, [8, 12, 16, 4]),
 ]
 
 
