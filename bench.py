@@ -787,7 +787,7 @@ def bench_decode(args):
     seen = sum(x["seen_tokens"] for x in st1)
     live_now = sum(x["live_tokens"] for x in st1)
     kernel = ("dms_decode_step = attention_kernel<fused> (the append inside the attention launch; split mode: "
-              "append_kernel + attention_kernel + reduce_kernel)" if args.path == "step" else
+              "attention_kernel<split step> + reduce_kernel<step>, the merge and the appends)" if args.path == "step" else
               "dms_decode_attention = attention_kernel (+ reduce_kernel in split mode)")
     res = {
         "metric": METRIC,
