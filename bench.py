@@ -696,7 +696,8 @@ def bench_decode(args):
         Qp[:, ::G, :, ch] = Ld.to(tdt)
     caches = []
     for r in range(rot):
-        c = dms.Cache(B, Hq, Hkv, d, wl.window, wl.max_tokens(), wl.pool_blocks(0), dtype=wl.dtype)
+        c = dms.Cache(B, Hq, Hkv, d, wl.window, wl.max_tokens(), wl.pool_blocks(0), dtype=wl.dtype,
+                      split_wgs=args.split_wgs)
         if src == "array":
             c.prefill(Kd, Vd, Ld, lengths)
         elif src == "k":
@@ -892,6 +893,9 @@ def main():
                          "when one step's live KV would fit in the MALL, else 1)")
     ap.add_argument("--no-balance", action="store_true",
                     help="decode bench: keep the cache's default work split (skip dms_cache_balance after the prompt)")
+    ap.add_argument("--split-wgs", type=int, default=0,
+                    help="decode bench: dms_config.split_wgs (0 = the library's choice, 1 = whole units, "
+                         ">= 2 = split over that many work-groups at most)")
     ap.add_argument("--no-resident", action="store_true",
                     help="skip the cache-resident (one cache) figure that goes with a rotated run")
     ap.add_argument("--prefill-attention", action="store_true",

@@ -86,10 +86,11 @@ typedef struct {
   int32_t block_tokens; /* tokens per cache block; must be 16 */
   int32_t max_tokens;   /* per sequence, prompt plus decode steps, 1 .. 2^24 */
   int32_t split_wgs;    /* how the decode attention shares its work among work-groups:
-                           0 automatic (see dms_cache_balance); 1 every (sequence, KV
-                           head) whole to one work-group; n >= 2 always split the
-                           live blocks in equal shares over min(n, resident)
-                           work-groups (requires batch * num_kv_heads <= 4096) */
+                           0 automatic (see dms_cache_balance; a split goes over one
+                           work-group per CU); 1 every (sequence, KV head) whole to
+                           one work-group; n >= 2 always split the live blocks in
+                           equal shares over min(n, resident) work-groups (requires
+                           batch * num_kv_heads <= 4096) */
   int64_t pool_blocks;  /* blocks in the shared pool, 1 .. 2^31-1; one block holds
                            16 tokens of K and V of one (sequence, KV head) */
   dms_dtype dtype;      /* element type of Q, K, V; outputs are always fp32 */

@@ -130,7 +130,15 @@ dms::Dev make_dev(const dms_cache* c) {
   p.item_floats = L.item_floats;
   p.grid = c->grid;
   p.split = c->split ? 1 : 0;
-  p.split_wgs = c->cfg.split_wgs >= 2 ? std::min(c->cfg.split_wgs, c->grid) : c->grid;
+  // Split mode shares the live blocks over at most one work-group per CU by
+  // default: with two per CU (the resident grid) every work-group streams
+  // half as many blocks and a cut unit has twice the pieces to merge, and on
+  // the layers whose steps are latency-bound that was slower (Llama-3.2-1B-
+  // shaped step 0.0266 against 0.0201 ms, Qwen-R1-7B-shaped 0.0443 against
+  // 0.0403 ms) while the bandwidth-bound head-skew step was unchanged
+  // (0.2842 against 0.2848 ms).  Widths between one and two per CU load
+  // some CUs twice and were slower than either.
+  p.split_wgs = c->cfg.split_wgs >= 2 ? std::min(c->cfg.split_wgs, c->grid) : std::min(c->grid, c->num_cus);
   p.pool_blocks = L.pool_blocks;
   p.block_bytes = L.block_bytes;
   const float scale = c->cfg.scale == 0.0f ? 1.0f / sqrtf((float)L.d) : c->cfg.scale;
