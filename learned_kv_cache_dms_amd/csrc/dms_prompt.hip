@@ -61,21 +61,26 @@ __device__ __forceinline__ void load_frag_dense(Frag<ES, D>& f, const uint8_t* _
   }
 }
 
-// Softmax step and P.V of a pair of blocks for the prompt attention (the
-// masks as softmax_pv_masked).  Two differences from the decode's step, both
-// for this compute-bound kernel:
-//  - the weights enter P.V as bf16 (nearest even), one product per tile: an
-//    output element is off by at most 2^-8 of sum_i p_i |v_i| / sum_i p_i
-//    (the sum l stays fp32).  A lo part as well (about 2^-17) cost 22 % of
-//    the kernel's time on the 32B-shaped layer;
-//  - a column's reference max moves only when a score exceeds it by more
-//    than 2^kPromptSlack in the exp2 domain, so the accumulators are rescaled
-//    a few times per column rather than whenever its max creeps up; the
-//    weights exp2(s - m) stay below 2^kPromptSlack and o / l is unchanged.
+// Softmax step and P.V of a pair of blocks for the compute-bound attention
+// of several queries per sequence (the masks as softmax_pv_masked).  A
+// column's reference max moves only when a score exceeds it by more than
+// 2^kPromptSlack in the exp2 domain, so the accumulators are rescaled a few
+// times per column rather than whenever its max creeps up; the weights
+// exp2(s - m) stay below 2^kPromptSlack and o / l is unchanged.  (A state
+// kept this way and one kept by softmax_pv_masked are the same kind: o and l
+// relative to the reference m.)  HILO: the weights enter P.V as bf16 hi + lo
+// pairs (about 2^-17, as the decode kernels); else as bf16 (nearest even), one
+// product per tile: an output element is then off by at most 2^-8 of
+// sum_i p_i |v_i| / sum_i p_i (the sum l stays fp32).
+//  - prompt attention: bf16 weights; hi + lo cost 22 % of the kernel's time on
+//    the 32B-shaped layer (276.8 against 220.2 ms with both changes);
+//  - chunk attention: hi + lo, so that a chunk's outputs match the one-token
+//    steps' to their precision; the stale max took C = 16 from 0.390 to
+//    0.372 ms and C = 64 from 1.170 to 1.141 ms.
 constexpr float kPromptSlack = 8.0f;
-template <int D>
-__device__ __forceinline__ void softmax_pv_prompt(const PairFrag<2, D>& f, const f32x4& SA, const f32x4& SB,
-                                                  uint32_t ma, uint32_t mb, int lane, float sl2e, Acc<D>& a) {
+template <int D, bool HILO>
+__device__ __forceinline__ void softmax_pv_stale(const PairFrag<2, D>& f, const f32x4& SA, const f32x4& SB,
+                                                 uint32_t ma, uint32_t mb, int lane, float sl2e, Acc<D>& a) {
   using G = Geo<2, D>;
   const int tb = 4 * (lane >> 4);
   float s[8];
@@ -104,12 +109,29 @@ __device__ __forceinline__ void softmax_pv_prompt(const PairFrag<2, D>& f, const
 #pragma unroll
   for (int r = 0; r < 8; ++r) pr[r] = exp2_fast(fmaf(s[r], sl2e, -mref));
   a.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-  const u32x4 pv = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]), pack_bf16x2(pr[4], pr[5]),
-                    pack_bf16x2(pr[6], pr[7])};
-  const bf16x8 PB = __builtin_bit_cast(bf16x8, pv);
+  unsigned hi[4];
 #pragma unroll
-  for (int j = 0; j < G::kTiles; ++j)
-    a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.v[j]), PB, a.o[j], 0, 0, 0);
+  for (int i = 0; i < 4; ++i) hi[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
+  const u32x4 hv = {hi[0], hi[1], hi[2], hi[3]};
+  const bf16x8 PH = __builtin_bit_cast(bf16x8, hv);
+  if constexpr (HILO) {
+    unsigned lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lo[i] = pack_bf16x2(pr[2 * i] - bf16_lo_to_f32(hi[i]), pr[2 * i + 1] - bf16_hi_to_f32(hi[i]));
+    const u32x4 lv = {lo[0], lo[1], lo[2], lo[3]};
+    const bf16x8 PL = __builtin_bit_cast(bf16x8, lv);
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j) {
+      const bf16x8 A = __builtin_bit_cast(bf16x8, f.v[j]);
+      a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PH, a.o[j], 0, 0, 0);
+      a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, PL, a.o[j], 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < G::kTiles; ++j)
+      a.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.v[j]), PH, a.o[j], 0, 0, 0);
+  }
 }
 
 // attend_pair with the prompt attention's softmax step for bf16 rows.
@@ -121,7 +143,7 @@ __device__ __forceinline__ void attend_pair_prompt(const PairFrag<ES, D>& f, con
   } else {
     f32x4 SA, SB;
     score_pair<D>(f, qf, SA, SB);
-    softmax_pv_prompt<D>(f, SA, SB, ma, mb, lane, sl2e, a);
+    softmax_pv_stale<D, false>(f, SA, SB, ma, mb, lane, sl2e, a);
   }
 }
 
@@ -221,7 +243,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
 #pragma unroll
         for (int t = 0; t < NCOL; ++t) {
           if (t + 1 < NCOL) score_pair<D>(f, qf[t + 1], SA[(t + 1) & 1], SB[(t + 1) & 1]);
-          softmax_pv_prompt<D>(f, SA[t & 1], SB[t & 1], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
+          softmax_pv_stale<D, false>(f, SA[t & 1], SB[t & 1], 0xffffu, mb, lane, p.scale_log2e, acc[t]);
         }
       } else {
 #pragma unroll
@@ -475,7 +497,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
         }
         if constexpr (ES == 2) {
           if (t + 1 < NC) score_pair<D>(f, qf[t + 1], SA[(t + 1) & 1], SB[(t + 1) & 1]);
-          softmax_pv_masked<D>(f, SA[t & 1], SB[t & 1], ma, mb, lane, p.scale_log2e, acc[t]);
+          softmax_pv_stale<D, true>(f, SA[t & 1], SB[t & 1], ma, mb, lane, p.scale_log2e, acc[t]);
         } else {
           attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
         }
