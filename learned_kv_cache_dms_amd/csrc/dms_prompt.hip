@@ -47,14 +47,20 @@ __device__ __forceinline__ void load_frag_dense(Frag<ES, D>& f, const uint8_t* _
 #pragma unroll
     for (int jj = 0; jj < G::kNJ; ++jj) {
       const int ch = 16 * (c * G::kNJ + jj) + (lane & 15);
+      if constexpr (ES == 2) {
+        // two 16-bit loads per register, joined as a vector (one v_perm_b32
+        // instead of a shift and an or)
+        typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (ES == 2) {
-          const unsigned x = *(const uint16_t*)(vrow[e] + ch * 2);
-          val[jj * 2 + (e >> 1)] |= x << (16 * (e & 1));
-        } else {
-          val[e] = *(const uint32_t*)(vrow[e] + ch * 4);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          u16x2 t;
+          t.x = *(const uint16_t*)(vrow[2 * h2] + ch * 2);
+          t.y = *(const uint16_t*)(vrow[2 * h2 + 1] + ch * 2);
+          val[jj * 2 + h2] = __builtin_bit_cast(uint32_t, t);
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = *(const uint32_t*)(vrow[e] + ch * 4);
       }
     }
     f.v[c] = val;
@@ -425,7 +431,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
   const int nb = (n + 15) >> 4;
   const int q0 = __builtin_amdgcn_readfirstlane(p.pos[u]);
   const int w = p.R - 1;
+  // the first and last block holding a pending token hidden from some column
+  __shared__ int hid_lo, hid_hi;
   for (int i = threadIdx.x; i < nb; i += blockDim.x) pend[i] = 0u;
+  if (threadIdx.x == 0) {
+    hid_lo = 1 << 30;
+    hid_hi = -1;
+  }
   __syncthreads();
   const int32_t* ring = p.ring + (int64_t)u * p.R;
   const int hide_lim = q0 + chunk - 1 - w;
@@ -434,7 +446,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
     if (sl >= 0 && sl < n) {
       const int blk = p.btab[(int64_t)u * p.max_blocks + (sl >> 4)];
       const int pos = p.blk_pos[(int64_t)blk * 16 + (sl & 15)];
-      atomicOr(&pend[sl >> 4], (1u << (sl & 15)) | (pos < hide_lim ? 0x10000u : 0u));
+      const bool hidden = pos < hide_lim;
+      atomicOr(&pend[sl >> 4], (1u << (sl & 15)) | (hidden ? 0x10000u : 0u));
+      if (hidden) {
+        atomicMin(&hid_lo, sl >> 4);
+        atomicMax(&hid_hi, sl >> 4);
+      }
     }
   }
   __syncthreads();
@@ -465,76 +482,94 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
     acc[t].l = 0.f;
   }
 
-  // Cached tokens: this wave's pairs of blocks i = sp, sp + nsplit, ...,
-  // one pair loaded ahead of the one computed.  Loads are unconditional
-  // (clamped indices; a pair past the wave's last is masked out).
+  // Cached tokens, in pairs of blocks.  The pairs of two full blocks with no
+  // token hidden from any column ("plain": every key visible to every
+  // column) go through their own loop and a softmax without masks; the rest
+  // (the pairs of the hidden tokens' blocks, one contiguous range, and a last
+  // pair that is not two full blocks) through the masked one.  Each wave
+  // takes every nsplit-th pair of each list, from its sp-th on.  (One loop
+  // for both, the masks all ones for plain pairs: C = 16 0.359 -> 0.342 ms,
+  // C = 64 1.101 -> 0.976 ms on the 32B-shaped layer with the split.)
   const int32_t* bt = p.btab + (int64_t)u * p.max_blocks;
   const int npair = (nb + 1) >> 1;
-  const int cnt = sp < npair ? (npair - sp + nsplit - 1) / nsplit : 0;
-  if (cnt > 0) {
-    struct Meta {
-      int4 pa, pb;
-      uint32_t wa, wb;
+  const int plast = npair - ((n & 31) != 0 ? 1 : 0);  // pairs [0, plast) hold two full blocks
+  const int hlo = __builtin_amdgcn_readfirstlane(hid_lo), hhi = __builtin_amdgcn_readfirstlane(hid_hi);
+  const int mlo = hhi >= 0 ? min(hlo >> 1, plast) : plast;       // masked pairs [mlo, mhi) ...
+  const int mhi = hhi >= 0 ? min((hhi >> 1) + 1, plast) : plast;  // ... and [plast, npair)
+  const int nplain = plast - (mhi - mlo), nmasked = npair - nplain;
+  auto load_blocks = [&](PairFrag<ES, D>& f, int i) {
+    // The block ids through the scalar cache (an index the compiler can
+    // see is uniform): a vector load here, its value needed at once for
+    // the addresses, made the wave wait for every load in flight, the
+    // prefetched pair's included (measured: C = 16 0.469 -> 0.408 ms).
+    const int ja = 2 * i, jb = min(2 * i + 1, nb - 1);
+    const int ba = scalar_load(bt + ja), bb = scalar_load(bt + jb);
+    load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
+    return int2{ba, bb};
+  };
+  const int cnt_plain = sp < nplain ? (nplain - sp + nsplit - 1) / nsplit : 0;
+  if (cnt_plain > 0) {
+    // plain pair kk of this wave: index sp + nsplit kk of the plain list
+    auto pair_id = [&](int kk) {
+      const int x = __builtin_amdgcn_readfirstlane(min(sp + nsplit * kk, nplain - 1));
+      return x < mlo ? x : x + (mhi - mlo);
     };
-    auto fetch = [&](PairFrag<ES, D>& f, Meta& m, int kk) {
-      // The block ids through the scalar cache (an index the compiler can
-      // see is uniform): a vector load here, its value needed at once for
-      // the addresses, made the wave wait for every load in flight, the
-      // prefetched pair's included (measured: C = 16 0.469 -> 0.408 ms).
-      const int i = __builtin_amdgcn_readfirstlane(min(sp + nsplit * kk, npair - 1));
-      const int ja = 2 * i, jb = min(2 * i + 1, nb - 1);
-      const int ba = scalar_load(bt + ja), bb = scalar_load(bt + jb);
-      load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
-      m.pa = *(const int4*)(p.blk_pos + (int64_t)ba * 16 + tb);
-      m.pb = *(const int4*)(p.blk_pos + (int64_t)bb * 16 + tb);
-      m.wa = pend[ja];
-      m.wb = pend[jb];
-    };
-    auto compute = [&](const PairFrag<ES, D>& f, const Meta& m, int kk) {
-      const int i = sp + nsplit * kk;
-      const bool ok = i < npair;
-      const int ja = 2 * i;
-      const int lva = ok ? n - 16 * ja : 0, lvb = ok && ja + 1 < nb ? n - 16 * (ja + 1) : 0;
-      const int xa[4] = {m.pa.x, m.pa.y, m.pa.z, m.pa.w}, xb[4] = {m.pb.x, m.pb.y, m.pb.z, m.pb.w};
-      // full blocks, no token hidden from any column: masks all ones
-      const bool plain =
-          __builtin_amdgcn_readfirstlane((lva >= 16 && lvb >= 16 && !((m.wa | m.wb) & 0x10000u)) ? 1 : 0) != 0;
-      // (bf16) column t + 1's score products are issued before column t's
-      // softmax, so that they run during its VALU work
-      f32x4 SA[2], SB[2];
-      if constexpr (ES == 2) score_pair<D>(f, qf[0], SA[0], SB[0]);
+    auto compute = [&](const PairFrag<ES, D>& f) {
+      if constexpr (ES == 2) {
+        // column t + 1's score products are issued before column t's softmax
+        f32x4 SA[2], SB[2];
+        score_pair<D>(f, qf[0], SA[0], SB[0]);
 #pragma unroll
-      for (int t = 0; t < NC; ++t) {
-        const int lt = q0 + qj[t] - w;  // a pending token is visible from position >= lt
-        uint32_t ma = 0xffffu, mb = 0xffffu;
-        if (!plain) {
-          ma = mb = 0;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int bit = tb + r;
-            if (bit < lva && (!((m.wa >> bit) & 1u) || xa[r] >= lt)) ma |= 1u << bit;
-            if (bit < lvb && (!((m.wb >> bit) & 1u) || xb[r] >= lt)) mb |= 1u << bit;
-          }
-        }
-        if constexpr (ES == 2) {
+        for (int t = 0; t < NC; ++t) {
           if (t + 1 < NC) score_pair<D>(f, qf[t + 1], SA[(t + 1) & 1], SB[(t + 1) & 1]);
-          softmax_pv_stale<D, true>(f, SA[t & 1], SB[t & 1], ma, mb, lane, p.scale_log2e, acc[t]);
-        } else {
-          attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
+          softmax_pv_stale<D, true, false>(f, SA[t & 1], SB[t & 1], 0xffffu, 0xffffu, lane, p.scale_log2e, acc[t]);
         }
+      } else {
+#pragma unroll
+        for (int t = 0; t < NC; ++t) attend_pair<ES, D>(f, qf[t], 0xffffu, 0xffffu, lane, p.scale_log2e, acc[t]);
       }
     };
+    // one pair loaded ahead of the one computed (the load past the wave's
+    // last pair re-reads it and goes unused)
     PairFrag<ES, D> f0, f1;
-    Meta m0, m1;
-    fetch(f0, m0, 0);
-    for (int kk = 0; kk < cnt; kk += 2) {
-      fetch(f1, m1, kk + 1);
+    load_blocks(f0, pair_id(0));
+    for (int kk = 0; kk < cnt_plain; kk += 2) {
+      load_blocks(f1, pair_id(kk + 1));
       __builtin_amdgcn_sched_barrier(0);
-      compute(f0, m0, kk);
-      if (kk + 1 >= cnt) break;
-      fetch(f0, m0, kk + 2);
+      compute(f0);
+      if (kk + 1 >= cnt_plain) break;
+      load_blocks(f0, pair_id(kk + 2));
       __builtin_amdgcn_sched_barrier(0);
-      compute(f1, m1, kk + 1);
+      compute(f1);
+    }
+  }
+  for (int x = sp; x < nmasked; x += nsplit) {
+    const int i = x < mhi - mlo ? mlo + x : plast + (x - (mhi - mlo));
+    PairFrag<ES, D> f;
+    const int2 bl = load_blocks(f, i);
+    const int4 pa = *(const int4*)(p.blk_pos + (int64_t)bl.x * 16 + tb);
+    const int4 pb = *(const int4*)(p.blk_pos + (int64_t)bl.y * 16 + tb);
+    const int ja = 2 * i;
+    const uint32_t wa = pend[ja], wb = pend[min(ja + 1, nb - 1)];
+    const int lva = n - 16 * ja, lvb = ja + 1 < nb ? n - 16 * (ja + 1) : 0;  // live slots
+    const int xa[4] = {pa.x, pa.y, pa.z, pa.w}, xb[4] = {pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+      const int lt = q0 + qj[t] - w;  // a pending token is visible from position >= lt
+      uint32_t ma = 0, mb = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int bit = tb + r;
+        if (bit < lva && (!((wa >> bit) & 1u) || xa[r] >= lt)) ma |= 1u << bit;
+        if (bit < lvb && (!((wb >> bit) & 1u) || xb[r] >= lt)) mb |= 1u << bit;
+      }
+      if constexpr (ES == 2) {
+        f32x4 SA, SB;
+        score_pair<D>(f, qf[t], SA, SB);
+        softmax_pv_stale<D, true>(f, SA, SB, ma, mb, lane, p.scale_log2e, acc[t]);
+      } else {
+        attend_pair<ES, D>(f, qf[t], ma, mb, lane, p.scale_log2e, acc[t]);
+      }
     }
   }
 
