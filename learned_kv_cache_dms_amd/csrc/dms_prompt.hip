@@ -177,7 +177,7 @@ constexpr int pf_tile() {
   return 16 * pf_cols<ES, D>() * kWavesPerWG;
 }
 
-// Grid (ceil(max_len_used / pf_tile<ES, D>()), Hq, B).
+// Grid (ceil(max_len_used / pf_tile<ES, D>()), Hq, B), read as one list of work items.
 template <int ES, int D>
 __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uint8_t* __restrict__ q,
                                                                 const uint8_t* __restrict__ k,
@@ -186,10 +186,21 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
   using G = Geo<ES, D>;
   constexpr int NCOL = pf_cols<ES, D>(), TILE = pf_tile<ES, D>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.z, hq = blockIdx.y;
+  // Work item (sequence, query head, query tile) of this work-group.  Work-group
+  // i runs on XCD i mod 8; each XCD takes a contiguous run of the items, which
+  // are in unit order, so that a unit's blocks are read into one XCD's L2 by
+  // the query tiles of all its heads; within a (sequence, query head) the
+  // last query tiles (the longest far parts) go first.  (Against the grid's
+  // own order on the 32B-shaped layer: 172.6 -> 168.6 ms; tiles in ascending
+  // order 169.5.)
+  const int ntile = gridDim.x, nitems = ntile * gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + ntile * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int xcd = lin & 7, base = nitems >> 3, rem = nitems & 7;
+  const int item = xcd * base + min(xcd, rem) + (lin >> 3);
+  const int tile = ntile - 1 - item % ntile, hq = (item / ntile) % gridDim.y, b = item / (ntile * gridDim.y);
   const int h = hq / p.G, u = b * p.Hkv + h;
   const int P = __builtin_amdgcn_readfirstlane(p.pos[u]);
-  const int q0 = blockIdx.x * TILE;
+  const int q0 = tile * TILE;
   if (q0 >= P) return;
   const int w = p.R - 1;
   const int qmax = min(q0 + TILE, P) - 1;
