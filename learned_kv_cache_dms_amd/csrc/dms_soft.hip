@@ -331,9 +331,11 @@ __global__ __launch_bounds__(256) void soft_forward_kernel(SoftArgs a, const uin
 
 // Waves per work-group of the backward kernels.  The waves of a work-group
 // share every staged step, so more waves stage the streamed operands less
-// often; measured on the 32B-shaped training layer, 8 waves made dq slower
-// and dkv about 4 % faster than 4.
-constexpr int kSoftQWaves = 4;
+// often; measured on the 32B-shaped training layer, 8 waves made dkv about
+// 4 % faster than 4 (and 4 waves, or 2 key tiles per wave at 4 waves, 12-16 %
+// slower in the XCD-aware order), and dq 3 % faster once the work items were
+// dealt XCD-aware (3.48 against 3.60 ms; before, 8 waves had made it slower).
+constexpr int kSoftQWaves = 8;
 constexpr int kSoftKWaves = 8;
 constexpr int kSoftQCols = 1;              // query tiles of 16 per wave (dQ)
 constexpr int kSoftQTile = 16 * kSoftQCols * kSoftQWaves;  // queries per work-group (dQ)
@@ -346,7 +348,7 @@ constexpr int kSoftDqWavesPerEu = 2;  // waves per SIMD soft_dq_kernel's registe
 // kSoftQCols tiles of 16 queries (columns) and streams the causal keys in
 // pairs of 16-row blocks: S^T = k q^T and dP^T = v dO^T with the keys as rows,
 // then dq^T += k^T dS^T with k^T from its pairT copy (dS rounded to bf16).
-// The 4 waves share each key pair: the work-group stages k and v rows
+// The kSoftQWaves waves share each key pair: the work-group stages k and v rows
 // (operand order), k^T and the keys' bias in LDS, double-buffered as in
 // soft_dkv_kernel.  Grid (ceil(T / kSoftQTile), Hq, B), read as one list of
 // work items (xcd_item), the last query tiles of a (sequence, head) first.
