@@ -410,28 +410,34 @@ struct PairFrag<2, D> {
   u32x4 v[Geo<2, D>::kTiles];  // tile 2c + jj: {A keys tb..tb+3, B keys tb..tb+3} of channel 16(2c+jj) + l%16
 };
 
-// Loads blocks A and B of the pool (fragment order) as a pair.
-// Plain loads, without the non-temporal hint of the decode path's block loads
-// (load_frag): the prompt and chunk kernels, its users, re-read every block
-// from several waves of a work-group and from other work-groups, and the hint
-// cost them the cache hits (prompt attention 196.7 -> 172.5 ms, chunk C = 16
-// 0.346 -> 0.334 ms on the 32B-shaped layer without it).
-template <int ES, int D>
+// Loads blocks A and B of the pool (fragment order) as a pair.  kStream: with
+// the non-temporal hint, for a stream that reads each block about once;
+// false: plain loads, for kernels whose waves and work-groups re-read the
+// same blocks close together.  Measured on the 32B-shaped layer: the prompt
+// attention 196.7 -> 172.5 ms with plain loads; the chunk attention faster
+// with the hint at C = 1, 4, 8, 12 and 64 (3-10 %), and with plain loads at
+// C = 16 (0.343 -> 0.325 ms), where two groups of column tiles in a
+// work-group each read every pair.
+template <int ES, int D, bool kStream = true>
 __device__ __forceinline__ void load_pair(PairFrag<ES, D>& f, const uint8_t* blka, const uint8_t* blkb, int lane) {
   using G = Geo<ES, D>;
+  auto ld = [](const auto* ptr) {
+    if constexpr (kStream) return __builtin_nontemporal_load(ptr);
+    else return *ptr;
+  };
   if constexpr (ES == 2) {
     const uint8_t* a = blka + lane * 16;
     const uint8_t* b = blkb + lane * 16;
 #pragma unroll
-    for (int c = 0; c < G::kChunks; ++c) f.ka[c] = *(const u32x4*)(a + c * 1024);
+    for (int c = 0; c < G::kChunks; ++c) f.ka[c] = ld((const u32x4*)(a + c * 1024));
 #pragma unroll
-    for (int c = 0; c < G::kChunks; ++c) f.kb[c] = *(const u32x4*)(b + c * 1024);
+    for (int c = 0; c < G::kChunks; ++c) f.kb[c] = ld((const u32x4*)(b + c * 1024));
 #pragma unroll
     for (int c = 0; c < G::kChunks; ++c) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
-        const u32x2 x = *(const u32x2*)(a + G::kHalf + c * 1024 + jj * 8);
-        const u32x2 y = *(const u32x2*)(b + G::kHalf + c * 1024 + jj * 8);
+        const u32x2 x = ld((const u32x2*)(a + G::kHalf + c * 1024 + jj * 8));
+        const u32x2 y = ld((const u32x2*)(b + G::kHalf + c * 1024 + jj * 8));
         f.v[2 * c + jj] = u32x4{x[0], x[1], y[0], y[1]};
       }
     }

@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
     const int npair = nfull >> 1;
     auto fetch = [&](PairFrag<ES, D>& f, int i) {
       const int ba = blk_at(2 * i, nfull - 1), bb = blk_at(2 * i + 1, nfull - 1);
-      load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
+      load_pair<ES, D, false>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
     };
     auto compute = [&](const PairFrag<ES, D>& f, int i) {
       if constexpr (ES == 2) {
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(Dev p, const uin
   for (int j = nfull; j < nfar; j += 2) {
     const int ba = blk_at(j, nfar - 1), bb = blk_at(j + 1, nfar - 1);
     PairFrag<ES, D> f;
-    load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
+    load_pair<ES, D, false>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
     const int4 pa = *(const int4*)(p.blk_pos + (int64_t)ba * 16 + tb);
     const int4 pb = *(const int4*)(p.blk_pos + (int64_t)bb * 16 + tb);
     const int lva = n - 16 * j, lvb = j + 1 < nfar ? n - 16 * (j + 1) : 0;  // live slots
@@ -414,8 +414,9 @@ constexpr int kChunkMaxBlocks = 8192;
 // they fit in one or two waves, the idle waves split the key stream instead
 // (4 or 2 ways: wave w takes every nsplit-th pair of blocks and of chunk
 // rows), and the waves of one tile group merge their softmax states through
-// LDS at the end, tile by tile.
-template <int ES, int D, int NC>
+// LDS at the end, tile by tile.  CACHED: the cache blocks are loaded without
+// the streaming hint (load_pair).
+template <int ES, int D, int NC, bool CACHED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && ES == 2 ? 2 : 1))) void chunk_attention_kernel(Dev p, const uint8_t* __restrict__ q,
                                                               const uint8_t* __restrict__ k,
                                                               const uint8_t* __restrict__ v, LogitSrc logit,
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
     // prefetched pair's included (measured: C = 16 0.469 -> 0.408 ms).
     const int ja = 2 * i, jb = min(2 * i + 1, nb - 1);
     const int ba = scalar_load(bt + ja), bb = scalar_load(bt + jb);
-    load_pair<ES, D>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
+    load_pair<ES, D, !CACHED>(f, p.pool + (int64_t)ba * p.block_bytes, p.pool + (int64_t)bb * p.block_bytes, lane);
     return int2{ba, bb};
   };
   const int cnt_plain = sp < nplain ? (nplain - sp + nsplit - 1) / nsplit : 0;
@@ -692,12 +693,12 @@ constexpr int chunk_cols() {
   return ES == 4 && D == 128 ? 2 : 3;
 }
 
-template <int ES, int D, int NC>
+template <int ES, int D, int NC, bool CACHED = false>
 static hipError_t chunk_attention_t(const Dev& p, const void* q, const void* k, const void* v, const LogitSrc& logit,
                                     int zero_ch, int chunk, float* out, hipStream_t s) {
   const int ytiles = (chunk * p.G + 64 * NC - 1) / (64 * NC);
   const int items = p.U * ytiles;
-  return launch(chunk_attention_kernel<ES, D, NC>, dim3((unsigned)(8 * ((items + 7) / 8))), dim3(64 * kWavesPerWG), s,
+  return launch(chunk_attention_kernel<ES, D, NC, CACHED>, dim3((unsigned)(8 * ((items + 7) / 8))), dim3(64 * kWavesPerWG), s,
                 p, (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, logit, zero_ch, chunk, out);
 }
 
@@ -711,6 +712,9 @@ static hipError_t decode_chunk_t(const Dev& p, const void* q, const void* k, con
   else if (tiles == 2) e = chunk_attention_t<ES, D, 2>(p, q, k, v, logit, zero_ch, chunk, out, s);
   else if (tiles == 3) e = chunk_attention_t<ES, D, 3>(p, q, k, v, logit, zero_ch, chunk, out, s);
   else if (tiles == 4) e = chunk_attention_t<ES, D, 4>(p, q, k, v, logit, zero_ch, chunk, out, s);
+  // two groups of three column tiles, each reading every pair of the
+  // work-group's unit: plain loads (see load_pair)
+  else if (tiles <= 6) e = chunk_attention_t<ES, D, 3, true>(p, q, k, v, logit, zero_ch, chunk, out, s);
   else e = chunk_attention_t<ES, D, 3>(p, q, k, v, logit, zero_ch, chunk, out, s);
   if (e != hipSuccess) return e;
   const int blocks = (p.U + kWavesPerWG - 1) / kWavesPerWG;
