@@ -497,8 +497,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NC == 1 && 
   // Cached tokens, in pairs of blocks.  The pairs of two full blocks with no
   // token hidden from any column ("plain": every key visible to every
   // column) go through their own loop and a softmax without masks; the rest
-  // (the pairs of the hidden tokens' blocks, one contiguous range, and a last
-  // pair that is not two full blocks) through the masked one.  Each wave
+  // (every pair from the first to the last block holding a hidden token, a
+  // short range near the tail of the cache, since pending tokens take the
+  // tail's slots or slots freed by recent retirements; and a last pair that
+  // is not two full blocks) through the masked one.  Each wave
   // takes every nsplit-th pair of each list, from its sp-th on.  (One loop
   // for both, the masks all ones for plain pairs: C = 16 0.359 -> 0.342 ms,
   // C = 64 1.101 -> 0.976 ms on the 32B-shaped layer with the split.)
