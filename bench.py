@@ -144,10 +144,10 @@ def calib_read(nbytes: int, reps: int = 20):
                           "best_us": round(best_s * 1e6, 2), "best_gbps": round(n / best_s / 1e9, 1)}), flush=True)
 
 
-def cpu_baseline(wl, steps_per_unit: int, n_units: int):
-    """The oracle, as it is, on a sample of the workload's (sequence, KV head)
-    units: `steps_per_unit` decode steps each at full context.  Input
-    generation is outside the timed part."""
+def cpu_baseline(wl, steps_per_unit: int, n_units: int, layers: int = 1):
+    """The oracle, as it is, on a sample of the workload's (layer, sequence,
+    KV head) units over its first `layers` layers: `steps_per_unit` decode
+    steps each at full context.  Input generation is outside the timed part."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -156,37 +156,88 @@ def cpu_baseline(wl, steps_per_unit: int, n_units: int):
 
     rng = np.random.default_rng(wl.seed + 17)
     U = wl.batch * wl.num_kv_heads
-    units = sorted(rng.choice(U, size=min(n_units, U), replace=False).tolist())
+    units = sorted(rng.choice(U * layers, size=min(n_units, U * layers), replace=False).tolist())
     lengths = wl.prompt_lengths()
     G = wl.group
     elapsed = 0.0
     live = 0  # live tokens attended over the sampled steps
-    for u in units:
+    for lu in units:
+        layer, u = divmod(lu, U)
         b, h = divmod(u, wl.num_kv_heads)
         P = int(lengths[b])
         pos = np.arange(P + steps_per_unit)
-        K = synth.tensor(wl.seed, synth.STREAM_K, 0, [b], [h], pos, wl.head_dim, wl.dtype)[0, 0]
-        V = synth.tensor(wl.seed, synth.STREAM_V, 0, [b], [h], pos, wl.head_dim, wl.dtype)[0, 0]
-        lg = synth.logits(wl.seed, 0, [b], [h], pos, *wl.layer_mu(0), wl.pos_threshold)[0, 0]
-        Q = synth.tensor(wl.seed, synth.STREAM_Q, 0, [b], list(range(h * G, (h + 1) * G)),
+        K = synth.tensor(wl.seed, synth.STREAM_K, layer, [b], [h], pos, wl.head_dim, wl.dtype)[0, 0]
+        V = synth.tensor(wl.seed, synth.STREAM_V, layer, [b], [h], pos, wl.head_dim, wl.dtype)[0, 0]
+        lg = synth.logits(wl.seed, layer, [b], [h], pos, *wl.layer_mu(layer), wl.pos_threshold)[0, 0]
+        Q = synth.tensor(wl.seed, synth.STREAM_Q, layer, [b], list(range(h * G, (h + 1) * G)),
                          np.arange(P, P + steps_per_unit), wl.head_dim, wl.dtype)[0].transpose(1, 0, 2)
         t0 = time.perf_counter()
         recs = O.decode_unit(Q, K, V, lg, P, steps_per_unit, wl.window, O.default_scale(wl.head_dim))
         elapsed += time.perf_counter() - t0
         live += sum(len(r.visible) for r in recs)
     per_unit_step = elapsed / (len(units) * steps_per_unit)
-    step_s = per_unit_step * U                      # a full decode step of the workload
+    step_s = per_unit_step * U * layers             # a full decode step of the workload
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
         "value": wl.batch / step_s,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{len(units)} of {U} (sequence, KV head) units x {steps_per_unit} decode steps at full "
-                  f"context ({elapsed:.1f} s of oracle time), scaled to all units",
+        "sample": f"{len(units)} of {U * layers} ({'layer, ' if layers > 1 else ''}sequence, KV head) units x "
+                  f"{steps_per_unit} decode steps at full context ({elapsed:.1f} s of oracle time), "
+                  f"scaled to all units",
         "seconds_per_step": step_s,
         # the live K/V bytes of the workload's dtype attended per second, as the metric counts them
         "live_kv_gbps": live * 2 * wl.head_dim * (2 if wl.dtype == "bf16" else 4) / elapsed / 1e9,
+        "host_cores_available": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
+    }
+
+
+def cpu_baseline_prompt(wl, n_units: int, n_queries: int):
+    """The oracle's prompt attention (each query over its visible set, the
+    oracle's own visible + attend) on sampled (sequence, KV head) units and
+    sampled prompt queries of each, every query head of the group: algorithmic
+    TFLOP/s at 4 d flops per visible (query, key) pair and head."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import dms_oracle as O
+    from synth import synth
+
+    rng = np.random.default_rng(wl.seed + 23)
+    U = wl.batch * wl.num_kv_heads
+    units = sorted(rng.choice(U, size=min(n_units, U), replace=False).tolist())
+    lengths = wl.prompt_lengths()
+    G, d = wl.group, wl.head_dim
+    scale = O.default_scale(d)
+    elapsed, pairs, nq = 0.0, 0, 0
+    for u in units:
+        b, h = divmod(u, wl.num_kv_heads)
+        P = int(lengths[b])
+        pos = np.arange(P)
+        K = synth.tensor(wl.seed, synth.STREAM_K, 0, [b], [h], pos, d, wl.dtype)[0, 0]
+        V = synth.tensor(wl.seed, synth.STREAM_V, 0, [b], [h], pos, d, wl.dtype)[0, 0]
+        lg = synth.logits(wl.seed, 0, [b], [h], pos, *wl.layer_mu(0), wl.pos_threshold)[0, 0]
+        qs = np.sort(rng.choice(P, size=min(n_queries, P), replace=False))
+        Q = synth.tensor(wl.seed, synth.STREAM_Q, 0, [b], list(range(h * G, (h + 1) * G)), qs, d,
+                         wl.dtype)[0]                       # [G, n, d]
+        alpha = O.eviction_decision(lg)
+        t0 = time.perf_counter()
+        for i, q in enumerate(qs):
+            vis = O.visible(alpha, int(q), wl.window)
+            O.attend(Q[:, i], K[vis], V[vis], scale)
+            pairs += len(vis) * G
+        elapsed += time.perf_counter() - t0
+        nq += len(qs)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": 4.0 * d * pairs / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{nq} prompt queries (x {G} query heads) from {len(units)} of {U} (sequence, KV head) "
+                  f"units, {pairs} visible (query, key) pairs ({elapsed:.1f} s of oracle time)",
         "host_cores_available": len(os.sched_getaffinity(0)),
         "cpu_model": cpu_model(),
     }
@@ -280,6 +331,8 @@ def bench_prefill_attention(args):
                      "algorithmic_flops_per_launch": flops},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prompt(wl, 8, 512)
     print(json.dumps(res), flush=True)
 
 
@@ -511,6 +564,12 @@ def bench_chunk(args):
                      "algorithmic_bytes_per_launch": round(kv_bytes)},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        # a chunk of C tokens computes what C decode steps do: the oracle's
+        # step-by-step decode is the baseline, in tokens/s
+        cpu = cpu_baseline(wl0, args.cpu_steps, args.cpu_units)
+        cpu["sample"] += f" (a chunk of {C} tokens = {C} decode steps)"
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
@@ -634,6 +693,10 @@ def bench_full_step(args):
                      "algorithmic_bytes_per_launch": round(live_bytes / NL)},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        # (layer, sequence, KV head) units drawn from every layer, scaled to all
+        # layers' units: the oracle's time for one decode step of the model
+        res["cpu_baseline"] = cpu_baseline(wl0, args.cpu_steps, args.cpu_units, layers=NL)
     print(json.dumps(res), flush=True)
 
 
