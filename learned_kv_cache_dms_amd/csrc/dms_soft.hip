@@ -335,13 +335,15 @@ __global__ __launch_bounds__(256) void soft_forward_kernel(SoftArgs a, const uin
 // 4 % faster than 4 (and 4 waves, or 2 key tiles per wave at 4 waves, 12-16 %
 // slower in the XCD-aware order), and dq 3 % faster once the work items were
 // dealt XCD-aware (3.48 against 3.60 ms; before, 8 waves had made it slower).
-constexpr int kSoftQWaves = 8;
+// dq then took 12 waves (three per SIMD, which its registers allow): the
+// backward 2 % faster again (3.52 against 3.59 ms).
+constexpr int kSoftQWaves = 12;
 constexpr int kSoftKWaves = 8;
 constexpr int kSoftQCols = 1;              // query tiles of 16 per wave (dQ)
 constexpr int kSoftQTile = 16 * kSoftQCols * kSoftQWaves;  // queries per work-group (dQ)
 constexpr int kSoftKT = 1;                   // key tiles of 16 per wave (dK, dV)
 constexpr int kSoftKTile = 16 * kSoftKT * kSoftKWaves;      // keys per work-group (dK, dV)
-constexpr int kSoftDqWavesPerEu = 2;  // waves per SIMD soft_dq_kernel's registers are sized for
+constexpr int kSoftDqWavesPerEu = 3;  // waves per SIMD soft_dq_kernel's registers are sized for
 
 // Backward, query-stationary: dq = scale * dS k with dS = P (dP - delta), P
 // recomputed from the forward's lse, dP = dO v^T.  Each wave holds
@@ -570,15 +572,19 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
   const int nsteps = a.G * per_head;
   const Pc pcs(tid);
 
-  // Step state (hq, q0), advanced without divisions.
+  // Step state (hq, q0), advanced without divisions: the query steps from
+  // the last one down to kbase, the G query heads of each step one after
+  // another.  Every work-group of a unit walks the same sequence of steps
+  // (each stops at its own kbase), so the work-groups of a unit that run at
+  // once read each staged step from the XCD's L2 together.
   struct Pos {
     int hq, q0;
   };
+  const int hq0 = h * a.G, qtop = 32 * ((T - 1) / 32);
   auto next = [&](Pos p) -> Pos {
-    p.q0 += 32;
-    if (p.q0 >= T) {
-      p.q0 = kbase;
-      ++p.hq;
+    if (++p.hq == hq0 + a.G) {
+      p.hq = hq0;
+      p.q0 -= 32;
     }
     return p;
   };
@@ -632,7 +638,7 @@ __global__ __launch_bounds__(64 * kSoftKWaves) void soft_dkv_kernel(SoftArgs a, 
 
   u32x4 pre[4][NP];
   float prx = 0.f;
-  Pos cur{h * a.G, kbase};
+  Pos cur{hq0, qtop};
   gload(pre, prx, cur);
   lds_store(st[0], pre, prx);
   __syncthreads();
