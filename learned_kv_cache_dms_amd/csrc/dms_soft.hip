@@ -336,14 +336,19 @@ __global__ __launch_bounds__(256) void soft_forward_kernel(SoftArgs a, const uin
 // slower in the XCD-aware order), and dq 3 % faster once the work items were
 // dealt XCD-aware (3.48 against 3.60 ms; before, 8 waves had made it slower).
 // dq then took 12 waves (three per SIMD, which its registers allow): the
-// backward 2 % faster again (3.52 against 3.59 ms).
-constexpr int kSoftQWaves = 12;
+// backward 2 % faster again (3.52 against 3.59 ms).  With the staged key
+// fragments read one channel chunk at a time (48 registers fewer), two query
+// tiles per dq wave fit the registers of two waves per SIMD: each staged
+// fragment then feeds twice the products, and the backward went from 3.49 to
+// 3.36 ms against the twelve-wave, one-tile dq (the chunked reads alone
+// changed nothing).
+constexpr int kSoftQWaves = 8;
 constexpr int kSoftKWaves = 8;
-constexpr int kSoftQCols = 1;              // query tiles of 16 per wave (dQ)
+constexpr int kSoftQCols = 2;              // query tiles of 16 per wave (dQ)
 constexpr int kSoftQTile = 16 * kSoftQCols * kSoftQWaves;  // queries per work-group (dQ)
 constexpr int kSoftKT = 1;                   // key tiles of 16 per wave (dK, dV)
 constexpr int kSoftKTile = 16 * kSoftKT * kSoftKWaves;      // keys per work-group (dK, dV)
-constexpr int kSoftDqWavesPerEu = 3;  // waves per SIMD soft_dq_kernel's registers are sized for
+constexpr int kSoftDqWavesPerEu = 2;  // waves per SIMD soft_dq_kernel's registers are sized for
 
 // Backward, query-stationary: dq = scale * dS k with dS = P (dP - delta), P
 // recomputed from the forward's lse, dP = dO v^T.  Each wave holds
@@ -464,32 +469,31 @@ __global__ __launch_bounds__(64 * kSoftQWaves) __attribute__((amdgpu_waves_per_e
     const int r0 = 32 * s;
     // every key of the pair is past the window of every query of the wave
     const bool far = r0 + 31 + w < cw0;
-    u32x4 ka[NCH], kb[NCH], va[NCH], vb[NCH];
+    const f32x4 ba = *(const f32x4*)&S.bias[tb], bb = *(const f32x4*)&S.bias[16 + tb];
+    f32x4 SA[kSoftQCols], SB[kSoftQCols], PA[kSoftQCols], PB[kSoftQCols];
+#pragma unroll
+    for (int t = 0; t < kSoftQCols; ++t) SA[t] = SB[t] = PA[t] = PB[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      ka[c] = S.op[0][c * 64 + lane];
-      kb[c] = S.op[0][(NCH + c) * 64 + lane];
-      va[c] = S.op[1][c * 64 + lane];
-      vb[c] = S.op[1][(NCH + c) * 64 + lane];
+      const u32x4 ka = S.op[0][c * 64 + lane], kb = S.op[0][(NCH + c) * 64 + lane];
+      const u32x4 va = S.op[1][c * 64 + lane], vb = S.op[1][(NCH + c) * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < kSoftQCols; ++t) {
+        SA[t] = mfma_bf16(ka, qf[t][c], SA[t]);
+        SB[t] = mfma_bf16(kb, qf[t][c], SB[t]);
+        PA[t] = mfma_bf16(va, of[t][c], PA[t]);
+        PB[t] = mfma_bf16(vb, of[t][c], PB[t]);
+      }
     }
-    const f32x4 ba = *(const f32x4*)&S.bias[tb], bb = *(const f32x4*)&S.bias[16 + tb];
 #pragma unroll
     for (int t = 0; t < kSoftQCols; ++t) {
-      f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = SA, PA = SA, PB = SA;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        SA = mfma_bf16(ka[c], qf[t][c], SA);
-        SB = mfma_bf16(kb[c], qf[t][c], SB);
-        PA = mfma_bf16(va[c], of[t][c], PA);
-        PB = mfma_bf16(vb[c], of[t][c], PB);
-      }
       float ds[8];
       if (far) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const float kb2 = r < 4 ? ba[r] : bb[r - 4];
-          const float sv = r < 4 ? SA[r] : SB[r - 4];
-          const float dp = r < 4 ? PA[r] : PB[r - 4];
+          const float sv = r < 4 ? SA[t][r] : SB[t][r - 4];
+          const float dp = r < 4 ? PA[t][r] : PB[t][r - 4];
           ds[r] = exp2_fast(fmaf(sv, a.scale_log2e, kb2 - lse2[t])) * (dp - dl[t]);
         }
       } else {
@@ -498,8 +502,8 @@ __global__ __launch_bounds__(64 * kSoftQWaves) __attribute__((amdgpu_waves_per_e
           const int i = r0 + (r >> 2) * 16 + tb + (r & 3);
           const float kb2 = r < 4 ? ba[r] : bb[r - 4];
           const float badd = i > qc[t] ? -INFINITY : (qc[t] - i > w ? kb2 : 0.f);
-          const float sv = r < 4 ? SA[r] : SB[r - 4];
-          const float dp = r < 4 ? PA[r] : PB[r - 4];
+          const float sv = r < 4 ? SA[t][r] : SB[t][r - 4];
+          const float dp = r < 4 ? PA[t][r] : PB[t][r - 4];
           ds[r] = exp2_fast(fmaf(sv, a.scale_log2e, badd) - lse2[t]) * (dp - dl[t]);
         }
       }
