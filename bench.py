@@ -144,10 +144,12 @@ def calib_read(nbytes: int, reps: int = 20):
                           "best_us": round(best_s * 1e6, 2), "best_gbps": round(n / best_s / 1e9, 1)}), flush=True)
 
 
-def cpu_baseline(wl, steps_per_unit: int, n_units: int, layers: int = 1):
+def cpu_baseline(wl, steps_per_unit: int, n_units: int, layers: int = 1, budget_s: float = 20.0):
     """The oracle, as it is, on a sample of the workload's (layer, sequence,
     KV head) units over its first `layers` layers: `steps_per_unit` decode
-    steps each at full context.  Input generation is outside the timed part."""
+    steps each at full context, for up to `n_units` units or until the
+    oracle has run `budget_s` seconds (at least one unit).  Input generation
+    is outside the timed part."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -156,12 +158,17 @@ def cpu_baseline(wl, steps_per_unit: int, n_units: int, layers: int = 1):
 
     rng = np.random.default_rng(wl.seed + 17)
     U = wl.batch * wl.num_kv_heads
-    units = sorted(rng.choice(U * layers, size=min(n_units, U * layers), replace=False).tolist())
+    # in the sample's random order, so that a budget cut keeps it unbiased
+    units = rng.choice(U * layers, size=min(n_units, U * layers), replace=False).tolist()
     lengths = wl.prompt_lengths()
     G = wl.group
     elapsed = 0.0
     live = 0  # live tokens attended over the sampled steps
+    done = 0
     for lu in units:
+        if done and elapsed >= budget_s:
+            break
+        done += 1
         layer, u = divmod(lu, U)
         b, h = divmod(u, wl.num_kv_heads)
         P = int(lengths[b])
@@ -175,6 +182,7 @@ def cpu_baseline(wl, steps_per_unit: int, n_units: int, layers: int = 1):
         recs = O.decode_unit(Q, K, V, lg, P, steps_per_unit, wl.window, O.default_scale(wl.head_dim))
         elapsed += time.perf_counter() - t0
         live += sum(len(r.visible) for r in recs)
+    units = units[:done]
     per_unit_step = elapsed / (len(units) * steps_per_unit)
     step_s = per_unit_step * U * layers             # a full decode step of the workload
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -567,7 +575,7 @@ def bench_chunk(args):
     if not args.no_cpu_baseline:
         # a chunk of C tokens computes what C decode steps do: the oracle's
         # step-by-step decode is the baseline, in tokens/s
-        cpu = cpu_baseline(wl0, args.cpu_steps, args.cpu_units)
+        cpu = cpu_baseline(wl0, args.cpu_steps, args.cpu_units, budget_s=args.cpu_seconds)
         cpu["sample"] += f" (a chunk of {C} tokens = {C} decode steps)"
         res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
@@ -696,7 +704,7 @@ def bench_full_step(args):
     if not args.no_cpu_baseline:
         # (layer, sequence, KV head) units drawn from every layer, scaled to all
         # layers' units: the oracle's time for one decode step of the model
-        res["cpu_baseline"] = cpu_baseline(wl0, args.cpu_steps, args.cpu_units, layers=NL)
+        res["cpu_baseline"] = cpu_baseline(wl0, args.cpu_steps, args.cpu_units, layers=NL, budget_s=args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
@@ -904,7 +912,7 @@ def bench_decode(args):
     if rot > 1 and not args.no_resident:
         res["cache_resident_run"] = resident_figure(args, wl0)
     if not args.no_cpu_baseline and src == "array":
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps, args.cpu_units)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps, args.cpu_units, budget_s=args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
@@ -931,6 +939,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=24)
     ap.add_argument("--cpu-steps", type=int, default=256)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="the oracle baseline stops taking units after this many seconds of oracle time")
     ap.add_argument("--calib-copy-bytes", type=int, default=0,
                     help="plain copy of this many bytes (to scale the HBM byte counters)")
     ap.add_argument("--calib-read-bytes", type=int, default=0,
