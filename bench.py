@@ -855,7 +855,8 @@ def bench_decode(args):
     live_bytes = live_tokens * 2 * d * esize   # per step: the K/V rows of every visible token
     step_s = total_ms / K / 1e3
     achieved = live_bytes / kern_avg_s / 1e9
-    traffic = measured_traffic(wl.name, args.path) if rot == 1 else None
+    # per call; the same whichever of the rotated caches a call reads
+    traffic = measured_traffic(wl.name, args.path)
     seen = sum(x["seen_tokens"] for x in st1)
     live_now = sum(x["live_tokens"] for x in st1)
     kernel = ("dms_decode_step = attention_kernel<fused> (the append inside the attention launch; split mode: "
