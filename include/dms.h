@@ -266,11 +266,13 @@ DMS_API int dms_decode_step_channel(dms_cache* c, const void* d_q, const void* d
    can land at its own compression ratio), so the live blocks per (sequence,
    KV head) can differ several-fold.  Whole-unit mode deals the (sequence, KV
    head)s to the work-groups longest first by live blocks; when the heaviest
-   work-group would still carry more than 1/16 above the mean (or there are
-   fewer (sequence, KV head)s than work-groups), the attention switches to
-   split mode, which gives every work-group an equal share of the live
-   blocks and merges the pieces of a split (sequence, KV head) in a second
-   launch.  The plan stays in force until the next dms_cache_balance, reset
+   work-group would still carry more than 1/16 above the mean, the attention
+   switches to split mode, which gives every work-group an equal share of the
+   live blocks and merges the pieces of a split (sequence, KV head) in a
+   second launch.  With fewer (sequence, KV head)s than work-groups, each
+   gets a work-group of its own unless the heaviest one, streamed by one
+   work-group alone, is estimated to take longer than the split with its
+   fixed costs (the estimate's rates are MI355X measurements).  The plan stays in force until the next dms_cache_balance, reset
    or prompt compression; calls stay correct whatever the plan, only their
    speed depends on it.  With split_wgs != 0 the mode is fixed (1: whole
    units, dealt as above; >= 2: split, nothing to do).  Call after a prompt's

@@ -162,7 +162,8 @@ def _skew_small(batch, steps=6):
 @pytest.mark.parametrize("batch,mode", [(8, "calls"), (8, "step"), (160, "step"), (160, "calls")])
 def test_balance_head_skew(batch, mode):
     """Per-head CR 2 ... 16: dms_cache_balance picks split mode for 64 units
-    (fewer than the work-groups) and deals 1280 units whole or split by how
+    (fewer than the work-groups; the CR-2 head's units, one work-group each,
+    would take longer than the split) and deals 1280 units whole or split by how
     evenly they pack; every plan gives the oracle's results.  Sampled units
     (every KV head) at every step."""
     import gpu_util as U
@@ -171,6 +172,23 @@ def test_balance_head_skew(batch, mode):
     units = [(int(rng.integers(0, batch)), h) for h in range(wl.num_kv_heads)]
     st = U.run_decode(wl, wl.decode_steps, units, _tol(wl), mode=mode, balance=True)
     assert st.checks == len(units) * wl.decode_steps
+
+
+@gpu
+def test_balance_mode_for_few_units():
+    """With fewer (sequence, KV head)s than work-groups, dms_cache_balance
+    gives each its own work-group when the units are alike (the
+    Llama-3.2-1B-shaped layer: 64 units of about 80 live blocks) and splits
+    when one head keeps several times the others' tokens (per-head CR 2 ...
+    16, 64 units); both plans give the oracle's results."""
+    import gpu_util as U
+    for wl, want in ((W.llama_1b(), 0), (_skew_small(8), 1)):
+        wl = dataclasses.replace(wl, decode_steps=3)
+        c = U.make_cache(wl)
+        units = [(0, h) for h in range(wl.num_kv_heads)]
+        st = U.run_decode(wl, wl.decode_steps, units, _tol(wl), mode="step", balance=True, cache=c)
+        assert st.checks == len(units) * wl.decode_steps
+        assert c.stats()["split_mode"] == want, wl.name
 
 
 @gpu
