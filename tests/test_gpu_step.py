@@ -178,11 +178,13 @@ def test_balance_head_skew(batch, mode):
 def test_balance_mode_for_few_units():
     """With fewer (sequence, KV head)s than work-groups, dms_cache_balance
     gives each its own work-group when the units are alike (the
-    Llama-3.2-1B-shaped layer: 64 units of about 80 live blocks) and splits
-    when one head keeps several times the others' tokens (per-head CR 2 ...
-    16, 64 units); both plans give the oracle's results."""
+    Llama-3.2-1B-shaped layer: 64 units of about 80 live blocks; the
+    Qwen-R1-7B-shaped layer: 128 units of about 143, both at full size, as
+    the bench times them) and splits when one head keeps several times the
+    others' tokens (per-head CR 2 ... 16, 64 units); every plan gives the
+    oracle's results."""
     import gpu_util as U
-    for wl, want in ((W.llama_1b(), 0), (_skew_small(8), 1)):
+    for wl, want in ((W.llama_1b(), 0), (W.qwen_7b(), 0), (_skew_small(8), 1)):
         wl = dataclasses.replace(wl, decode_steps=3)
         c = U.make_cache(wl)
         units = [(0, h) for h in range(wl.num_kv_heads)]
